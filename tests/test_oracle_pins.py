@@ -1,0 +1,396 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+constants and entry counts the pages and workloads state, closed forms,
+library routines it must reduce to, invariants, and an independent brute-force
+formulation on tiny inputs.  Each pin is chosen so that a plausible slip (a
+dropped term, a sign, an index off by one, a transposed operand) fails it."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import lca_inputs as li
+from oracle import attention as att
+from oracle import compress as cmp
+from oracle import dense, indexer, numerics, pipeline
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold():
+    with open(os.path.join(GOLD, "page_constants.json")) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# constants and entry counts
+# --------------------------------------------------------------------------
+
+def test_presets_match_page_constants():
+    g = _gold()
+    for cfg in li.CONFIGS.values():
+        assert cfg.m == g["csa_stride_m"]["value"]
+        assert cfg.w == g["csa_overlapping_streams"]["value"] * cfg.m
+        assert cfg.m2 == cfg.w2 == g["hca_ratio"]["value"]
+        assert cfg.W == g["swa_window"]["value"]
+    assert li.PRO_1M_DECODE.k == g["topk_pro"]["value"]
+    assert li.FLASH_DECODE.k == li.FLASH_PREFILL.k == g["topk_flash"]["value"]
+    assert li.PRO_1M_DECODE.H == g["pro_query_heads"]["value"]
+    assert li.PRO_1M_DECODE.D == g["pro_head_dim"]["value"]
+    assert li.FLASH_DECODE.H == g["flash_query_heads"]["value"]
+    assert li.PRO_1M_DECODE.lens[0] == g["context"]["value"]
+
+
+def test_entry_counts_match_workloads():
+    for case in _gold()["workload_entry_counts"]["cases"]:
+        L = case["tokens"]
+        assert cmp.n_entries(L, 4, 8) == case["csa"]
+        assert cmp.n_entries(L, 128, 128) == case["hca"]
+
+
+def test_entry_count_matches_enumeration():
+    # brute force: count windows [j*m, j*m+w) that fit inside L tokens
+    for L in range(0, 300):
+        for m, w in ((4, 8), (128, 128), (1, 1), (2, 4), (3, 3)):
+            brute = sum(1 for j in range(L + 1) if j * m + w <= L)
+            assert cmp.n_entries(L, m, w) == brute
+
+
+def test_visibility_boundary():
+    # an entry becomes visible exactly when the query reaches its last token
+    for j in range(20):
+        last = j * 4 + 7
+        assert cmp.n_visible(last, 4, 8) == j + 1
+        assert cmp.n_visible(last - 1, 4, 8) == j
+        lastH = j * 128 + 127
+        assert cmp.n_visible(lastH, 128, 128) == j + 1
+        assert cmp.n_visible(lastH - 1, 128, 128) == j
+
+
+# --------------------------------------------------------------------------
+# pooling + norm closed forms
+# --------------------------------------------------------------------------
+
+def test_constant_stream_closed_form():
+    rng = np.random.default_rng(1)
+    L, C = 64, 16
+    x = np.ones((L, C))
+    z = rng.standard_normal((L, C))
+    e = cmp.compress(x, z, 4, 8, norm=False)
+    assert np.all(e == 1.0) or np.max(np.abs(e - 1.0)) < 1e-15   # weights sum to one
+    en = cmp.compress(x, z, 4, 8, norm=True, eps=1e-6)
+    assert np.max(np.abs(en - 1.0 / math.sqrt(1.0 + 1e-6))) < 1e-15
+
+
+def test_constant_logits_give_window_mean():
+    rng = np.random.default_rng(2)
+    L, C = 300, 8
+    x = rng.standard_normal((L, C))
+    z = np.full((L, C), 0.37)
+    for m, w in ((4, 8), (128, 128)):
+        e = cmp.compress(x, z, m, w, norm=False)
+        for j in range(e.shape[0]):
+            assert np.allclose(e[j], x[j * m:j * m + w].mean(axis=0), rtol=0, atol=1e-14)
+        en = cmp.compress(x, z, m, w, norm=True, eps=1e-6)
+        mean = np.stack([x[j * m:j * m + w].mean(axis=0) for j in range(e.shape[0])])
+        ref = mean / np.sqrt((mean ** 2).mean(axis=1, keepdims=True) + 1e-6)
+        assert np.allclose(en, ref, rtol=0, atol=1e-13)
+
+
+def test_dominant_logit_picks_its_token_per_channel():
+    # channel c puts a +60 logit on token (c mod w) of each window -> the entry
+    # equals that token in that channel (per-channel softmax, right direction)
+    rng = np.random.default_rng(3)
+    L, C, m, w = 64, 16, 4, 8
+    x = rng.standard_normal((L, C))
+    z = rng.standard_normal((L, C)) * 0.1
+    tol = w * math.exp(-59.0) * np.max(np.abs(x))
+    for j in range(cmp.n_entries(L, m, w)):
+        zz = z.copy()
+        for c in range(C):
+            zz[j * m + (c % w), c] = 60.0
+        e = cmp.compress(x, zz, m, w, norm=False, entries=[j])[0]
+        for c in range(C):
+            assert abs(e[c] - x[j * m + (c % w), c]) <= tol
+
+
+def test_per_token_logits_broadcast():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((40, 6))
+    zt = rng.standard_normal(40)
+    a = cmp.compress(x, zt, 4, 8, norm=True)
+    b = cmp.compress(x, np.repeat(zt[:, None], 6, axis=1), 4, 8, norm=True)
+    assert np.array_equal(a, b)
+
+
+def test_overlapping_windows_share_tokens():
+    # "two overlapping streams": token t (t >= 4) feeds entries t//4 - 1 and t//4
+    rng = np.random.default_rng(5)
+    L, C = 40, 4
+    x = rng.standard_normal((L, C))
+    z = rng.standard_normal((L, C))
+    base = cmp.compress(x, z, 4, 8, norm=False)
+    for t in range(L):
+        x2 = x.copy()
+        x2[t] += 1.0
+        changed = np.nonzero(np.any(cmp.compress(x2, z, 4, 8, norm=False) != base, axis=1))[0]
+        expect = [j for j in (t // 4 - 1, t // 4) if 0 <= j < base.shape[0]]
+        assert list(changed) == expect
+
+
+def test_rmsnorm_mean_square():
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((50, 64)) * rng.uniform(0.01, 10, size=(50, 1))
+    eps = 1e-6
+    y = cmp.rmsnorm(v, eps)
+    ms = (v ** 2).mean(axis=1)
+    assert np.allclose((y ** 2).mean(axis=1), ms / (ms + eps), rtol=1e-13, atol=0)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(7)
+    x32 = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                          np.float32([1.00390625, 1.01171875, -3.0078125, 0.0, 1e-3])])
+    ours = numerics.round_bf16(x32.astype(np.float64))
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+# --------------------------------------------------------------------------
+# indexer and top-k
+# --------------------------------------------------------------------------
+
+def test_indexer_single_head_is_relu_dot():
+    rng = np.random.default_rng(8)
+    keys = rng.standard_normal((200, 16))
+    p = rng.standard_normal((1, 16))
+    s = indexer.scores(p, [1.0], keys)
+    brute = [max(0.0, sum(float(p[0, t]) * float(keys[j, t]) for t in range(16))) for j in range(200)]
+    assert np.allclose(s, brute, rtol=0, atol=1e-12)
+
+
+def test_indexer_head_weights_and_signs():
+    rng = np.random.default_rng(9)
+    keys = rng.standard_normal((50, 8))
+    p = rng.standard_normal((3, 8))
+    om = np.array([0.5, -2.0, 1.5])
+    s = indexer.scores(p, om, keys)
+    for j in range(50):
+        ref = 0.0
+        for r in range(3):
+            d = float(np.dot(p[r], keys[j]))
+            ref += om[r] * (d if d > 0 else 0.0)
+        assert abs(s[j] - ref) < 1e-12
+    # one-hot head weights isolate one head
+    s1 = indexer.scores(p, [0.0, 1.0, 0.0], keys)
+    assert np.allclose(s1, np.maximum(keys @ p[1], 0.0))
+
+
+def test_topk_bruteforce_with_ties():
+    rng = np.random.default_rng(10)
+    for trial in range(50):
+        n = int(rng.integers(1, 60))
+        s = rng.integers(-3, 4, size=n).astype(np.float64)   # many exact ties
+        k = int(rng.integers(1, 70))
+        got = list(indexer.topk(s, k))
+        ref = sorted(range(n), key=lambda j: (-s[j], j))[:k]
+        assert got == ref
+
+
+# --------------------------------------------------------------------------
+# attention: reductions to textbook attention, sink, merge
+# --------------------------------------------------------------------------
+
+def _sdpa(qhat, keys, scale):
+    q = torch.from_numpy(qhat)[None]       # [1, H, D] as (batch, L=H rows, D)
+    k = torch.from_numpy(keys)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, k, scale=scale)
+    return o[0].numpy()
+
+
+@pytest.mark.parametrize("branch", ["csa", "hca", "swa"])
+def test_window_one_reduces_to_dense_causal_attention(branch):
+    """m = w = 1 (one token per entry), k >= N, no sink, one branch alone: the
+    method is dense causal attention over RMS-normalised tokens."""
+    rng = np.random.default_rng(11)
+    L, H, D = 37, 3, 16
+    x = numerics.round_bf16(rng.standard_normal((L, D)))
+    z = rng.standard_normal((L, D))
+    q = rng.standard_normal((H, D))
+    eps, scale = 1e-6, 1.0 / math.sqrt(D)
+    qhat = att.normalize_query(q, eps, "bf16")
+    for i in (0, 5, L - 1):
+        keys_ref = att.normalize_tokens(x[:i + 1], eps, "bf16")
+        if branch == "swa":
+            cfg = li.TINY.with_(W=L + 5, D=D, dtype="bf16")
+            keys = pipeline.window_keys(x, i, cfg)
+        else:
+            ent = numerics.round_bf16(cmp.compress(x, z, 1, 1, True, eps))
+            nv = cmp.n_visible(i, 1, 1)
+            if branch == "csa":
+                s = indexer.scores(rng.standard_normal((2, D)), [1.0, 1.0], ent[:nv])
+                sel = indexer.topk(s, 10 * L)
+                assert sorted(sel) == list(range(i + 1))
+                keys = ent[sel]
+            else:
+                keys = ent[:nv]
+        o, lse = att.partial(qhat, keys, scale)
+        o_ref = _sdpa(qhat, keys_ref, scale)
+        assert np.allclose(np.sort(keys, axis=0), np.sort(keys_ref, axis=0))
+        assert np.allclose(o, o_ref, rtol=0, atol=1e-12)
+        o2, _ = att.merge([(o, lse)], None)
+        assert np.allclose(o2, o_ref, rtol=0, atol=1e-12)
+
+
+def test_sink_closed_forms():
+    rng = np.random.default_rng(12)
+    H, D = 4, 8
+    key = rng.standard_normal((1, D))
+    qhat = rng.standard_normal((H, D))
+    scale = 0.3
+    o, _, _ = att.attend(qhat, key, scale, sigma=np.full(H, -np.inf))
+    assert np.allclose(o, np.repeat(key, H, axis=0), atol=1e-15)
+    o, _, _ = att.attend(qhat, key, scale, sigma=np.full(H, 60.0))
+    assert np.max(np.abs(o)) < 1e-20
+    lg = scale * (qhat @ key[0])
+    o, _, ps = att.attend(qhat, key, scale, sigma=lg)      # sink logit == key logit
+    assert np.allclose(o, 0.5 * np.repeat(key, H, axis=0), atol=1e-15)
+    assert np.allclose(ps, 0.5)
+    # the same through partial + merge
+    part = att.partial(qhat, key, scale)
+    om, _ = att.merge([part], lg)
+    assert np.allclose(om, 0.5 * np.repeat(key, H, axis=0), atol=1e-15)
+
+
+def test_probabilities_sum_to_one():
+    rng = np.random.default_rng(13)
+    qhat = rng.standard_normal((5, 16))
+    keys = rng.standard_normal((30, 16))
+    sig = rng.standard_normal(5)
+    _, prob, ps = att.attend(qhat, keys, 0.25, sig)
+    assert np.allclose(prob.sum(axis=1) + ps, 1.0, atol=1e-14)
+    assert np.all(prob >= 0) and np.all(ps > 0)
+
+
+def test_merge_of_any_partition_equals_one_softmax():
+    rng = np.random.default_rng(14)
+    H, D, n = 6, 12, 40
+    qhat = rng.standard_normal((H, D))
+    keys = rng.standard_normal((n, D)) * 3
+    sig = rng.standard_normal(H)
+    ref, _, _ = att.attend(qhat, keys, 0.7, sig)
+    for trial in range(20):
+        lab = rng.integers(0, 4, size=n)                       # some parts may be empty
+        parts = [att.partial(qhat, keys[lab == p], 0.7) for p in range(4)]
+        o, _ = att.merge(parts, sig)
+        assert np.allclose(o, ref, rtol=0, atol=1e-12)
+    empty = att.partial(qhat, keys[:0], 0.7)
+    assert np.all(empty[1] == -np.inf) and np.all(empty[0] == 0)
+
+
+def test_attention_order_invariance():
+    rng = np.random.default_rng(15)
+    qhat = rng.standard_normal((4, 16))
+    keys = rng.standard_normal((25, 16))
+    o1, l1 = att.partial(qhat, keys, 0.25)
+    perm = rng.permutation(25)
+    o2, l2 = att.partial(qhat, keys[perm], 0.25)
+    assert np.allclose(o1, o2, atol=1e-14) and np.allclose(l1, l2, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# whole-step pins on tiny inputs
+# --------------------------------------------------------------------------
+
+def _tiny_cfg(dtype="bf16", **kw):
+    base = dict(H=3, D=8, HI=2, dI=4, k=5, m2=16, w2=16, W=12)
+    base.update(kw)
+    return li.small("pin", 900, (70, 45), tq=1, dtype=dtype, **base)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gather_oracle_equals_dense_bruteforce(dtype):
+    cfg = _tiny_cfg(dtype)
+    raw = li.make_raw(cfg)
+    caches, _ = pipeline.run(raw, cfg)
+    off = raw["tok_off"]
+    for b in range(cfg.B):
+        L = cfg.lens[b]
+        sl = lambda k: pipeline.seq_slice(raw[k], off, b)  # noqa: E731
+        for i in (L - 1, L - 9, 20, 7, 0):
+            r = pipeline.query_step(caches[b], sl("x"), raw["q"][b], raw["p"][b], raw["omega"][b],
+                                    raw["sigma"], i, cfg)
+            od, chosen = dense.query(sl("x"), sl("a"), sl("g"), sl("u"), sl("c"), raw["q"][b],
+                                     raw["p"][b], raw["omega"][b], raw["sigma"], i, cfg)
+            assert set(int(j) for j in r["sel"]) == chosen
+            assert np.allclose(r["out_raw"] if dtype == "f32" else r["out"], np.array(od),
+                               rtol=0, atol=1e-12 if dtype == "f32" else 1e-2)
+            assert np.array_equal(r["out"], numerics.round_to(np.array(od), dtype)) or \
+                np.max(np.abs(r["out"] - np.array(od))) <= 2.0 ** -7 * np.max(np.abs(od))
+
+
+def test_causality_nan_poison():
+    """Raw inputs after the query position cannot reach its output."""
+    cfg = _tiny_cfg("f32")
+    raw = li.make_raw(cfg)
+    caches, res = pipeline.run(raw, cfg)
+    off = raw["tok_off"]
+    b = 0
+    L = cfg.lens[b]
+    for i in (L - 1, 50, 31, 16, 15, 3):
+        ref = pipeline.query_step(caches[b], pipeline.seq_slice(raw["x"], off, b), raw["q"][0],
+                                  raw["p"][0], raw["omega"][0], raw["sigma"], i, cfg)
+        pois = {k: v.copy() for k, v in raw.items()}
+        for key in ("x", "a", "g", "u", "c"):
+            pois[key][int(off[b]) + i + 1:int(off[b + 1])] = np.nan
+        sl = lambda k: pipeline.seq_slice(pois[k], off, b)  # noqa: E731
+        pc = pipeline.build_seq_caches(sl("x"), sl("a"), sl("g"), sl("u"), sl("c"), cfg)
+        got = pipeline.query_step(pc, sl("x"), raw["q"][0], raw["p"][0], raw["omega"][0],
+                                  raw["sigma"], i, cfg)
+        assert np.all(np.isfinite(got["out"]))
+        assert np.array_equal(got["out"], ref["out"])
+
+
+def test_selected_set_matters():
+    """Attending over a different visible set changes the output (the checks
+    that compare outputs can see a wrong selection)."""
+    cfg = _tiny_cfg("f32", k=3)
+    raw = li.make_raw(cfg)
+    caches, res = pipeline.run(raw, cfg)
+    r = res[(0, 0)]
+    off = raw["tok_off"]
+    nv = len(r["scores"])
+    other = [j for j in range(nv) if j not in set(r["sel"].tolist())][:3]
+    alt = pipeline.query_step(caches[0], pipeline.seq_slice(raw["x"], off, 0), raw["q"][0], raw["p"][0],
+                              raw["omega"][0], raw["sigma"], cfg.lens[0] - 1, cfg, idx=other)
+    assert np.max(np.abs(alt["out"] - r["out"])) > 1e-3
+
+
+def test_empty_branches():
+    """A query before the first complete window has no CSA/HCA entries; the
+    window always holds the query token itself."""
+    cfg = _tiny_cfg("f32")
+    raw = li.make_raw(cfg)
+    caches, _ = pipeline.run(raw, cfg)
+    x0 = pipeline.seq_slice(raw["x"], raw["tok_off"], 0)
+    r = pipeline.query_step(caches[0], x0, raw["q"][0], raw["p"][0], raw["omega"][0], raw["sigma"], 0, cfg)
+    assert len(r["sel"]) == 0
+    assert np.all(r["csa"][1] == -np.inf) and np.all(r["hca"][1] == -np.inf)
+    assert np.all(np.isfinite(r["out"]))
+    # with a single window token the output is that normalised token times its
+    # softmax weight against the sink
+    key = att.normalize_tokens(x0[:1], cfg.eps, cfg.dtype)[0]
+    lg = cfg.scale * (r["qhat"] @ key)
+    wgt = 1.0 / (1.0 + np.exp(raw["sigma"] - lg))
+    assert np.allclose(r["out_raw"], wgt[:, None] * key[None, :], atol=1e-13)
+
+
+def test_generator_is_seeded_and_rounded():
+    a = li.make_raw(_tiny_cfg("bf16"))
+    b = li.make_raw(_tiny_cfg("bf16"))
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+    assert np.array_equal(numerics.round_bf16(a["x"].astype(np.float64)), a["x"].astype(np.float64))
+    assert abs(float(np.mean(a["x"]))) < 0.05 and abs(float(np.std(a["x"])) - 1) < 0.05
