@@ -1,0 +1,222 @@
+/*
+ * lca.h -- C-ABI of the MI355X (gfx950) hybrid compressed attention library.
+ *
+ * DeepSeek-V4's attention stack, as the pages describe it ("Why DeepSeek V4
+ * Stands Apart", Core Architectural Innovations; "DeepSeek-V4" spec sheet,
+ * Design overview, Core block, Inference efficiency): the KV stream is
+ * compressed into overlapping entries every 4 tokens (CSA) and into one entry
+ * per 128 tokens (HCA); a lightning indexer scores the CSA entries and each
+ * query attends to its top-k of them, to every HCA entry, to the most recent
+ * 128 raw tokens and to an attention sink.  One KV head is shared by all query
+ * heads, and a compressed entry is both key and value.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *   never allocates, frees or keeps a buffer, and keeps no state between calls
+ *   except in the caller's workspace (see lca_csa_index_topk).
+ * - `stream` is a hipStream_t passed as void*; every call is asynchronous on it.
+ * - Every argument is validated on the host before anything is launched; a
+ *   failed call launches nothing and returns a negative code.  Device faults
+ *   surface at the caller's next synchronisation (HIP semantics); with the
+ *   environment variable LCA_SYNC=1 every call synchronises its stream and
+ *   reports a device error as LCA_ERR_HIP.
+ * - Element type: LCA_BF16 (bfloat16 storage, fp32 arithmetic) or LCA_F32.
+ *   Indexer head weights, sink logits, partial outputs and scores are fp32.
+ * - Sequences are packed: rows of sequence b live at [off[b], off[b+1]) of a
+ *   tensor; offsets are device int64 arrays of length B+1.
+ * - Row-major layouts; "[a, b, c]" lists dimensions from slowest to fastest.
+ * - Thread safety: concurrent calls are safe when they use different
+ *   workspaces and outputs.
+ */
+#ifndef LCA_H_
+#define LCA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum lca_status {
+  LCA_OK = 0,
+  LCA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent sizes */
+  LCA_ERR_UNSUPPORTED = -2, /* a shape or type this build has no kernel for */
+  LCA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  LCA_ERR_HIP = -4          /* the HIP runtime reported an error */
+};
+
+enum lca_dtype { LCA_F32 = 0, LCA_BF16 = 1 };
+
+/* Static text for a status code. */
+const char* lca_strerror(int status);
+/* Text describing the last failure on the calling thread ("" if none). */
+const char* lca_last_error(void);
+/* Library version, major*10000 + minor*100 + patch. */
+int lca_version(void);
+
+/* ------------------------------------------------------------------------
+ * a1. KV compression
+ *
+ * "Why DeepSeek V4 Stands Apart", Core Architectural Innovations (CSA
+ * compresses KV entries 4x; HCA compresses 128:1) and "DeepSeek-V4", Design
+ * overview (every 4 tokens into two overlapping streams; m' = 128) and
+ * Provenance 17 (RMSNorm on compressed KV entries).
+ *
+ * Entry j of sequence b pools the raw rows t = j*m .. j*m+w-1 of that
+ * sequence:  e[j, c] = sum_t softmax_t(z[t, c]) * src[t, c]  (softmax over the
+ * w tokens of the window, separately per channel c; with per_channel = 0 the
+ * same logit z[t] serves every channel).  With rmsnorm = 1 the entry is then
+ * divided by sqrt(mean_c e[j, c]^2 + eps).  The result is rounded to the
+ * storage type.  Only complete windows exist: a sequence of L tokens has
+ * N(L) = L < w ? 0 : (L - w) / m + 1 entries.  CSA: m = 4, w = 8; HCA:
+ * m = w = 128.
+ *
+ * A call writes, for every sequence b and every stream, the entries
+ * N(done_len[b]) .. N(L_b) - 1, L_b = tok_off[b+1] - tok_off[b]: all of them
+ * for a cache build (done_len = NULL), the ones the newest tokens complete for
+ * a decode step or a prefill chunk.  Only the raw rows inside those windows
+ * are read.
+ * ---------------------------------------------------------------------- */
+typedef struct lca_compress_stream {
+  const void* src;        /* [T, C] raw rows, packed by tok_off                      */
+  const void* logits;     /* [T, C] if per_channel else [T]; same element type       */
+  void* out;              /* [sum_b N(L_b), C] entries, packed by ent_off             */
+  const int64_t* ent_off; /* device [B+1]: first row of sequence b in `out`           */
+  int32_t C;              /* channels: multiple of 8 (bf16) / 4 (f32), at most 1024   */
+  int32_t m;              /* stride (>= 1)                                            */
+  int32_t w;              /* window (>= m)                                            */
+  int32_t per_channel;    /* 1: logits [T, C]; 0: logits [T]                          */
+  int32_t rmsnorm;        /* 1: RMS-normalise each entry over its C channels          */
+  int32_t max_entries;    /* host bound on entries written per sequence (>= 0)        */
+} lca_compress_stream;
+
+/* Compress up to 4 streams in one launch.
+ *   streams  host array of n_streams (1..4) descriptors
+ *   tok_off  device int64 [B+1]
+ *   done_len device int64 [B] or NULL (0 for every sequence)
+ *   eps      RMSNorm epsilon (1e-6 in this build's workloads)
+ * Returns LCA_OK or an error; the caller must make ent_off leave room for
+ * N(L_b) rows per sequence and max_entries >= N(L_b) - N(done_len[b]). */
+int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int64_t* tok_off,
+                    const int64_t* done_len, int B, float eps, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a2 + a3. Lightning-indexer scores and exact top-k over the CSA entries
+ *
+ * "DeepSeek-V4", Design overview and Inference efficiency (V3.2's lightning
+ * indexer on the compressed entries); "Why DeepSeek V4 Stands Apart", Core
+ * Architectural Innovations (top-1024 for Pro, top-512 for Flash).
+ *
+ * For query row r = b*Tq + t at position i = q_pos[b*Tq + t], entry j of
+ * sequence b is a candidate iff its window ends at or before i
+ * (j*m + w - 1 <= i).  Its score is
+ *     s_j = sum_h omega[r, h] * max(0, p[r, h, :] . ikey[csa_off[b] + j, :]).
+ * idx[r, 0..k) receives the k candidates of largest score, ties broken toward
+ * the smaller j, as local entry indices (0-based within the sequence).  When a
+ * query has fewer than k candidates all are selected and the rest of its row is
+ * -1.  The order of a row is deterministic (candidates above the k-th score's
+ * top bits in index order, then the rest in index order) but is not a ranking.
+ *
+ *   p        [B*Tq, H_I, d_I]  indexer queries (dtype)
+ *   omega    [B*Tq, H_I]       fp32 head weights
+ *   ikey     [sum_b N, d_I]    indexer keys (dtype), packed by csa_off
+ *   q_pos    device int32 [B*Tq]
+ *   max_entries  host bound on the candidates of any query (>= 1)
+ *   scores   optional fp32 [B*Tq, max_entries] output of every candidate's
+ *            score (entry j at column j); NULL to keep them in the workspace
+ *   ws       device workspace of at least lca_csa_index_topk_workspace()
+ *            bytes.  It must be ZERO-FILLED before its first use; every call
+ *            that returns LCA_OK leaves it zero-filled again.  Calls that
+ *            share a workspace must be ordered on one stream.
+ * Supported: H_I * d_I <= 1024, d_I multiple of 8, k in [1, 4096],
+ * entries per sequence < 2^24. */
+size_t lca_csa_index_topk_workspace(int n_rows, int64_t max_entries, int k);
+int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                       const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
+                       int64_t max_entries, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
+                       int dtype, void* stream);
+
+/* The two halves of lca_csa_index_topk, one kernel each, same arguments and
+ * workspace: lca_csa_index_score (a2) writes the scores and the selection
+ * histogram into the workspace (and into `scores` when it is not NULL);
+ * lca_csa_topk_select (a3) must follow on the same stream with the same
+ * arguments and workspace (and the same `scores` pointer). */
+int lca_csa_index_score(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                        const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
+                        int64_t max_entries, float* scores, void* ws, size_t ws_bytes, int dtype,
+                        void* stream);
+int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                        int64_t max_entries, int32_t* idx, const float* scores, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * Attention partials (a4, a5)
+ *
+ * Shared-KV multi-query attention ("DeepSeek-V4", Inference efficiency): all H
+ * query heads attend to the same keys, and a compressed entry is key and value.
+ * Every query head is RMS-normalised over D in the kernel (RMSNorm on queries,
+ * "DeepSeek-V4" Provenance 17) and rounded to the storage type; logits are
+ * scale * qhat . key.  The key list of a query is cut into n_split parts; part
+ * s writes the softmax-normalised output and natural-log log-sum-exp of its
+ * keys:
+ *     o_part[s, r, h, :]  fp32, [n_split, B*Tq, H, D]
+ *     lse[s, r, h]        fp32, [n_split, B*Tq, H]
+ * An empty part writes o = 0 and lse = -inf.  lca_swa_merge combines parts.
+ * Supported: D in {64, 128, 256, 512}; any H (H a multiple of 16 uses the
+ * matrix cores for bf16); 1 <= n_split <= 256.
+ * ---------------------------------------------------------------------- */
+
+/* a4. Sparse attention over the selected CSA entries ("Why DeepSeek V4
+ * Stands Apart", Core Architectural Innovations: attention over the top-k
+ * compressed entries of each query).
+ *   q       [B*Tq, H, D] raw queries (dtype)
+ *   kv_csa  [sum_b N, D] compressed, normalised KV entries, packed by csa_off
+ *   idx     int32 [B*Tq, k] local entry indices, -1 = unused slot           */
+int lca_csa_sparse_attn(const void* q, const void* kv_csa, const int64_t* csa_off, const int32_t* idx,
+                        int B, int Tq, int H, int D, int k, float scale, float eps, int n_split,
+                        float* o_part, float* lse, int dtype, void* stream);
+
+/* a5. Dense attention over every visible HCA entry ("Why DeepSeek V4 Stands
+ * Apart", Core Architectural Innovations: dense attention over the 128:1
+ * compressed representation).  Entry j of sequence b is visible to the query
+ * at position i iff j*m2 + w2 - 1 <= i.
+ *   kv_hca  [sum_b N2, D] packed by hca_off; q_pos device int32 [B*Tq]
+ *   max_entries  host bound on the visible entries of any query            */
+int lca_hca_attn(const void* q, const void* kv_hca, const int64_t* hca_off, const int32_t* q_pos,
+                 int B, int Tq, int H, int D, int m2, int w2, int64_t max_entries, float scale, float eps,
+                 int n_split, float* o_part, float* lse, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a6. Sliding window + sink + merge
+ *
+ * "Why DeepSeek V4 Stands Apart", Core Architectural Innovations (window of
+ * the most recent 128 tokens); "DeepSeek-V4", Core block (attention sinks).
+ * For query row r at position i of sequence b: attends to the raw rows
+ * max(0, i-W+1) .. i of x (each RMS-normalised over D and rounded to the
+ * storage type on load), then combines that window with every partial of
+ * `parts` and the sink logit sink[h] (zero value; NULL = no sink) into one
+ * softmax:
+ *     lse = log(sum_p exp(lse_p) + exp(sink))
+ *     out = sum_p exp(lse_p - lse) * o_p        (rounded to dtype)
+ * W = 0 skips the window.  ws: at least lca_swa_merge_workspace() bytes.
+ *   x       [T, D] raw KV rows, packed by tok_off (device int64 [B+1])
+ *   out     [B*Tq, H, D] (dtype)
+ * ---------------------------------------------------------------------- */
+typedef struct lca_partial {
+  const float* o;   /* [n_split, B*Tq, H, D] */
+  const float* lse; /* [n_split, B*Tq, H]    */
+  int32_t n_split;
+} lca_partial;
+
+size_t lca_swa_merge_workspace(int n_rows, int H, int D);
+int lca_swa_merge(const void* q, const void* x, const int64_t* tok_off, const int32_t* q_pos,
+                  const float* sink, const lca_partial* parts, int n_parts, int B, int Tq, int H, int D,
+                  int W, float scale, float eps, void* out, void* ws, size_t ws_bytes, int dtype,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCA_H_ */

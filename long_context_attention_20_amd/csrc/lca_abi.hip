@@ -1,0 +1,274 @@
+// extern "C" entry points of liblca: host-side validation, then launches.
+// Every check runs before anything is enqueued; a failing call enqueues nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <cmath>
+#include <string>
+
+#include "lca_common.h"
+
+namespace lca {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+// launchers (lca_compress.hip, lca_indexer.hip, lca_attention.hip)
+int launch_compress(const lca_compress_stream* streams, int n, const int64_t* tok_off, const int64_t* done_len,
+                    int B, float eps, int dtype, hipStream_t stream);
+size_t index_topk_workspace(int rows, int64_t maxN, int k);
+int launch_index_score(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                       const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
+                       float* scores, void* ws, int dtype, hipStream_t stream);
+int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                       int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
+int launch_attention(int src, const void* q, const void* kv, const int64_t* off, const int32_t* idx,
+                     const int32_t* q_pos, int B, int Tq, int H, int D, int k, int m2, int w2, int W,
+                     float scale, float eps, int n_split, float* o_part, float* lse, int dtype,
+                     hipStream_t stream);
+int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, const float* win_lse,
+                 const float* sink, int rows, int H, int D, void* out, int dtype, hipStream_t stream);
+
+static bool sync_mode() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("LCA_SYNC");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+static int finish(int rc, hipStream_t stream, const char* what) {
+  if (rc != LCA_OK) {
+    if (rc == LCA_ERR_HIP) set_error("%s: launch failed: %s", what, hipGetErrorString(hipGetLastError()));
+    return rc;
+  }
+  if (sync_mode()) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) {
+      set_error("%s: %s", what, hipGetErrorString(e));
+      return LCA_ERR_HIP;
+    }
+  }
+  g_last_error.clear();
+  return LCA_OK;
+}
+
+#define LCA_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) {                   \
+      set_error(__VA_ARGS__);        \
+      return (code);                 \
+    }                                \
+  } while (0)
+
+static bool valid_dtype(int d) { return d == LCA_F32 || d == LCA_BF16; }
+static bool valid_head_dim(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
+
+}  // namespace lca
+
+using namespace lca;
+
+extern "C" {
+
+const char* lca_strerror(int status) {
+  switch (status) {
+    case LCA_OK: return "ok";
+    case LCA_ERR_INVALID_ARG: return "invalid argument";
+    case LCA_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case LCA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LCA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* lca_last_error(void) { return g_last_error.c_str(); }
+
+int lca_version(void) { return 100; }
+
+int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int64_t* tok_off,
+                    const int64_t* done_len, int B, float eps, int dtype, void* stream) {
+  LCA_REQUIRE(streams != nullptr, LCA_ERR_INVALID_ARG, "kv_compress: streams is NULL");
+  LCA_REQUIRE(n_streams >= 1 && n_streams <= 4, LCA_ERR_INVALID_ARG, "kv_compress: n_streams=%d not in [1,4]",
+              n_streams);
+  LCA_REQUIRE(tok_off != nullptr, LCA_ERR_INVALID_ARG, "kv_compress: tok_off is NULL");
+  LCA_REQUIRE(B >= 1, LCA_ERR_INVALID_ARG, "kv_compress: B=%d", B);
+  LCA_REQUIRE(valid_dtype(dtype), LCA_ERR_INVALID_ARG, "kv_compress: dtype=%d", dtype);
+  LCA_REQUIRE(std::isfinite(eps) && eps >= 0.f, LCA_ERR_INVALID_ARG, "kv_compress: eps must be finite and >= 0");
+  const int VE = dtype == LCA_BF16 ? 8 : 4;
+  for (int k = 0; k < n_streams; ++k) {
+    const lca_compress_stream& s = streams[k];
+    LCA_REQUIRE(s.src && s.logits && s.out && s.ent_off, LCA_ERR_INVALID_ARG,
+                "kv_compress: stream %d has a NULL pointer", k);
+    LCA_REQUIRE(s.C > 0 && s.C <= 1024 && s.C % VE == 0, LCA_ERR_INVALID_ARG,
+                "kv_compress: stream %d: C=%d must be a positive multiple of %d, at most 1024", k, s.C, VE);
+    const int lanes = s.C / VE;
+    const bool lanes_ok = (lanes <= 64 && (64 % lanes) == 0) || (lanes % 64 == 0 && lanes / 64 <= (VE == 8 ? 2 : 4));
+    LCA_REQUIRE(lanes_ok, LCA_ERR_UNSUPPORTED, "kv_compress: stream %d: C=%d is not a supported width", k, s.C);
+    LCA_REQUIRE(s.m >= 1 && s.w >= s.m && s.w <= 4096, LCA_ERR_INVALID_ARG,
+                "kv_compress: stream %d: need 1 <= m <= w <= 4096 (m=%d, w=%d)", k, s.m, s.w);
+    LCA_REQUIRE(s.per_channel == 0 || s.per_channel == 1, LCA_ERR_INVALID_ARG, "kv_compress: per_channel");
+    LCA_REQUIRE(s.rmsnorm == 0 || s.rmsnorm == 1, LCA_ERR_INVALID_ARG, "kv_compress: rmsnorm");
+    LCA_REQUIRE(s.max_entries >= 0, LCA_ERR_INVALID_ARG, "kv_compress: max_entries < 0");
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_compress(streams, n_streams, tok_off, done_len, B, eps, dtype, st), st, "kv_compress");
+}
+
+size_t lca_csa_index_topk_workspace(int n_rows, int64_t max_entries, int k) {
+  if (n_rows < 1 || max_entries < 1 || k < 1) return 0;
+  return index_topk_workspace(n_rows, max_entries, k);
+}
+
+static int check_index(const char* what, bool need_inputs, const void* p, const float* omega, const void* ikey,
+                       const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m,
+                       int w, int64_t max_entries, void* ws, size_t ws_bytes, int dtype) {
+  if (need_inputs) {
+    LCA_REQUIRE(p && omega && ikey, LCA_ERR_INVALID_ARG, "%s: a required pointer is NULL", what);
+    LCA_REQUIRE(H_I >= 1 && H_I <= 16 && d_I >= 8 && d_I % 8 == 0 && H_I * d_I <= 1024, LCA_ERR_UNSUPPORTED,
+                "%s: H_I=%d d_I=%d unsupported", what, H_I, d_I);
+    LCA_REQUIRE(valid_dtype(dtype), LCA_ERR_INVALID_ARG, "%s: dtype=%d", what, dtype);
+  }
+  LCA_REQUIRE(csa_off && q_pos, LCA_ERR_INVALID_ARG, "%s: a required pointer is NULL", what);
+  LCA_REQUIRE(B >= 1 && Tq >= 1, LCA_ERR_INVALID_ARG, "%s: B=%d Tq=%d", what, B, Tq);
+  LCA_REQUIRE((int64_t)B * Tq <= 65535, LCA_ERR_UNSUPPORTED, "%s: B*Tq must be <= 65535", what);
+  LCA_REQUIRE(k >= 1 && k <= 4096, LCA_ERR_UNSUPPORTED, "%s: k=%d not in [1,4096]", what, k);
+  LCA_REQUIRE(m >= 1 && w >= 1, LCA_ERR_INVALID_ARG, "%s: m=%d w=%d", what, m, w);
+  LCA_REQUIRE(max_entries >= 1 && max_entries < (1 << 24), LCA_ERR_UNSUPPORTED,
+              "%s: max_entries=%lld not in [1, 2^24)", what, (long long)max_entries);
+  const size_t need = index_topk_workspace(B * Tq, max_entries, k);
+  LCA_REQUIRE(ws != nullptr && ws_bytes >= need, LCA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given",
+              what, need, ws ? ws_bytes : (size_t)0);
+  return LCA_OK;
+}
+
+int lca_csa_index_score(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                        const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
+                        int64_t max_entries, float* scores, void* ws, size_t ws_bytes, int dtype, void* stream) {
+  int rc = check_index("csa_index_score", true, p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w,
+                       max_entries, ws, ws_bytes, dtype);
+  if (rc != LCA_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_index_score(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries, scores, ws,
+                                   dtype, st),
+                st, "csa_index_score");
+}
+
+int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                        int64_t max_entries, int32_t* idx, const float* scores, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc = check_index("csa_topk_select", false, nullptr, nullptr, nullptr, csa_off, q_pos, B, Tq, 1, 8, k, m, w,
+                       max_entries, ws, ws_bytes, LCA_BF16);
+  if (rc != LCA_OK) return rc;
+  LCA_REQUIRE(idx != nullptr, LCA_ERR_INVALID_ARG, "csa_topk_select: idx is NULL");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_topk_select(csa_off, q_pos, B, Tq, k, m, w, max_entries, idx, scores, ws, st), st,
+                "csa_topk_select");
+}
+
+int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                       const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
+                       int64_t max_entries, int32_t* idx, float* scores, void* ws, size_t ws_bytes, int dtype,
+                       void* stream) {
+  LCA_REQUIRE(idx != nullptr, LCA_ERR_INVALID_ARG, "csa_index_topk: idx is NULL");
+  int rc = lca_csa_index_score(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries, scores, ws,
+                               ws_bytes, dtype, stream);
+  if (rc != LCA_OK) return rc;
+  return lca_csa_topk_select(csa_off, q_pos, B, Tq, k, m, w, max_entries, idx, scores, ws, ws_bytes, stream);
+}
+
+static int check_attn(const char* what, const void* q, const void* kv, const void* off, const void* lst,
+                      int B, int Tq, int H, int D, float scale, float eps, int n_split, const float* o,
+                      const float* lse, int dtype) {
+  LCA_REQUIRE(q && kv && off && lst && o && lse, LCA_ERR_INVALID_ARG, "%s: a required pointer is NULL", what);
+  LCA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1, LCA_ERR_INVALID_ARG, "%s: B=%d Tq=%d H=%d", what, B, Tq, H);
+  LCA_REQUIRE((int64_t)B * Tq <= 65535 && H <= 65535, LCA_ERR_UNSUPPORTED, "%s: B*Tq and H must be <= 65535",
+              what);
+  LCA_REQUIRE(valid_head_dim(D), LCA_ERR_UNSUPPORTED, "%s: D=%d not in {64,128,256,512}", what, D);
+  LCA_REQUIRE(n_split >= 1 && n_split <= 256, LCA_ERR_INVALID_ARG, "%s: n_split=%d not in [1,256]", what,
+              n_split);
+  LCA_REQUIRE(std::isfinite(scale) && scale > 0.f, LCA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", what);
+  LCA_REQUIRE(std::isfinite(eps) && eps >= 0.f, LCA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", what);
+  LCA_REQUIRE(valid_dtype(dtype), LCA_ERR_INVALID_ARG, "%s: dtype=%d", what, dtype);
+  return LCA_OK;
+}
+
+int lca_csa_sparse_attn(const void* q, const void* kv_csa, const int64_t* csa_off, const int32_t* idx, int B,
+                        int Tq, int H, int D, int k, float scale, float eps, int n_split, float* o_part,
+                        float* lse, int dtype, void* stream) {
+  int rc = check_attn("csa_sparse_attn", q, kv_csa, csa_off, idx, B, Tq, H, D, scale, eps, n_split, o_part, lse,
+                      dtype);
+  if (rc != LCA_OK) return rc;
+  LCA_REQUIRE(k >= 1 && k <= 65536, LCA_ERR_INVALID_ARG, "csa_sparse_attn: k=%d", k);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // q_pos is not used by the gathered source; pass idx to keep the pointer valid
+  return finish(launch_attention(1, q, kv_csa, csa_off, idx, reinterpret_cast<const int32_t*>(idx), B, Tq, H, D,
+                                 k, 1, 1, 0, scale, eps, n_split, o_part, lse, dtype, st),
+                st, "csa_sparse_attn");
+}
+
+int lca_hca_attn(const void* q, const void* kv_hca, const int64_t* hca_off, const int32_t* q_pos, int B, int Tq,
+                 int H, int D, int m2, int w2, int64_t max_entries, float scale, float eps, int n_split,
+                 float* o_part, float* lse, int dtype, void* stream) {
+  int rc = check_attn("hca_attn", q, kv_hca, hca_off, q_pos, B, Tq, H, D, scale, eps, n_split, o_part, lse, dtype);
+  if (rc != LCA_OK) return rc;
+  LCA_REQUIRE(m2 >= 1 && w2 >= 1, LCA_ERR_INVALID_ARG, "hca_attn: m2=%d w2=%d", m2, w2);
+  LCA_REQUIRE(max_entries >= 0, LCA_ERR_INVALID_ARG, "hca_attn: max_entries < 0");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_attention(0, q, kv_hca, hca_off, nullptr, q_pos, B, Tq, H, D, 0, m2, w2, 0, scale, eps,
+                                 n_split, o_part, lse, dtype, st),
+                st, "hca_attn");
+}
+
+size_t lca_swa_merge_workspace(int n_rows, int H, int D) {
+  if (n_rows < 1 || H < 1 || D < 1) return 0;
+  const size_t o = ((size_t)n_rows * H * D * 4 + 255) & ~(size_t)255;
+  return o + (size_t)n_rows * H * 4;
+}
+
+int lca_swa_merge(const void* q, const void* x, const int64_t* tok_off, const int32_t* q_pos, const float* sink,
+                  const lca_partial* parts, int n_parts, int B, int Tq, int H, int D, int W, float scale, float eps,
+                  void* out, void* ws, size_t ws_bytes, int dtype, void* stream) {
+  LCA_REQUIRE(out != nullptr, LCA_ERR_INVALID_ARG, "swa_merge: out is NULL");
+  LCA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1, LCA_ERR_INVALID_ARG, "swa_merge: B=%d Tq=%d H=%d", B, Tq, H);
+  LCA_REQUIRE((int64_t)B * Tq <= 65535 && H <= 65535, LCA_ERR_UNSUPPORTED, "swa_merge: B*Tq and H must be <= 65535");
+  LCA_REQUIRE(valid_head_dim(D), LCA_ERR_UNSUPPORTED, "swa_merge: D=%d not in {64,128,256,512}", D);
+  LCA_REQUIRE(valid_dtype(dtype), LCA_ERR_INVALID_ARG, "swa_merge: dtype=%d", dtype);
+  LCA_REQUIRE(W >= 0, LCA_ERR_INVALID_ARG, "swa_merge: W=%d", W);
+  LCA_REQUIRE(n_parts >= 0 && n_parts <= 7, LCA_ERR_UNSUPPORTED, "swa_merge: n_parts=%d not in [0,7]", n_parts);
+  LCA_REQUIRE(n_parts == 0 || parts != nullptr, LCA_ERR_INVALID_ARG, "swa_merge: parts is NULL");
+  for (int p = 0; p < n_parts; ++p)
+    LCA_REQUIRE(parts[p].o && parts[p].lse && parts[p].n_split >= 1 && parts[p].n_split <= 256,
+                LCA_ERR_INVALID_ARG, "swa_merge: part %d is invalid", p);
+  LCA_REQUIRE(std::isfinite(scale) && scale > 0.f, LCA_ERR_INVALID_ARG, "swa_merge: scale");
+  LCA_REQUIRE(std::isfinite(eps) && eps >= 0.f, LCA_ERR_INVALID_ARG, "swa_merge: eps");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int rows = B * Tq;
+  float* wo = nullptr;
+  float* wl = nullptr;
+  if (W > 0) {
+    LCA_REQUIRE(q && x && tok_off && q_pos, LCA_ERR_INVALID_ARG, "swa_merge: q, x, tok_off and q_pos are required");
+    const size_t need = lca_swa_merge_workspace(rows, H, D);
+    LCA_REQUIRE(ws != nullptr && ws_bytes >= need, LCA_ERR_WORKSPACE,
+                "swa_merge: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    wo = reinterpret_cast<float*>(ws);
+    wl = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (((size_t)rows * H * D * 4 + 255) & ~(size_t)255));
+    int rc = launch_attention(2, q, x, tok_off, nullptr, q_pos, B, Tq, H, D, 0, 1, 1, W, scale, eps, 1, wo, wl,
+                              dtype, st);
+    if (rc != LCA_OK) return finish(rc, st, "swa_merge(window)");
+  }
+  LCA_REQUIRE(n_parts > 0 || W > 0 || sink != nullptr, LCA_ERR_INVALID_ARG, "swa_merge: nothing to merge");
+  return finish(launch_merge(parts, n_parts, wo, wl, sink, rows, H, D, out, dtype, st), st, "swa_merge");
+}
+
+}  // extern "C"

@@ -1,0 +1,203 @@
+"""Torch-tensor front end of liblca: argument marshalling only.
+
+Every function here takes device tensors, checks their dtype/device/layout,
+and calls the C entry point of the same name on the current torch stream.
+All arithmetic runs in the HIP kernels of liblca.so.
+"""
+from typing import Optional, Sequence
+
+import ctypes
+import torch
+
+from ._lib import (LCA_BF16, LCA_F32, CompressStream, Partial, check, lib)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LCA_BF16
+    if t.dtype == torch.float32:
+        return LCA_F32
+    raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("liblca takes device tensors")
+        if not t.is_contiguous():
+            raise ValueError("liblca takes contiguous tensors")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _i64(t: torch.Tensor, what: str):
+    if t.dtype != torch.int64:
+        raise TypeError(f"{what} must be int64")
+
+
+def _i32(t: torch.Tensor, what: str):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{what} must be int32")
+
+
+# ---------------------------------------------------------------- a1
+
+def kv_compress(streams: Sequence[dict], tok_off: torch.Tensor, done_len: Optional[torch.Tensor] = None,
+                eps: float = 1e-6):
+    """streams: dicts with src, logits, out, ent_off (tensors) and m, w,
+    rmsnorm, max_entries (ints); per_channel is taken from the logits' rank."""
+    if not 1 <= len(streams) <= 4:
+        raise ValueError("1..4 streams per call")
+    _i64(tok_off, "tok_off")
+    B = tok_off.numel() - 1
+    arr = (CompressStream * len(streams))()
+    dt = None
+    keep = []
+    for i, s in enumerate(streams):
+        src, lg, out, eo = s["src"], s["logits"], s["out"], s["ent_off"]
+        _dev(src, lg, out, eo)
+        _i64(eo, "ent_off")
+        d = _dtype_code(src)
+        if dt is None:
+            dt = d
+        if d != dt or _dtype_code(lg) != d or _dtype_code(out) != d:
+            raise TypeError("one element type per call")
+        C = src.shape[-1]
+        pc = 1 if lg.dim() == 2 else 0
+        arr[i] = CompressStream(src.data_ptr(), lg.data_ptr(), out.data_ptr(), eo.data_ptr(), C, int(s["m"]),
+                                int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]))
+        keep.append(s)
+    _dev(tok_off, done_len)
+    if done_len is not None:
+        _i64(done_len, "done_len")
+    check(lib.lca_kv_compress(arr, len(streams), _ptr(tok_off), _ptr(done_len), B, float(eps), dt, _stream()),
+          "kv_compress")
+
+
+# ---------------------------------------------------------------- a2 + a3
+
+def csa_index_topk_workspace(n_rows: int, max_entries: int, k: int) -> int:
+    return int(lib.lca_csa_index_topk_workspace(n_rows, max_entries, k))
+
+
+def csa_index_topk(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws: torch.Tensor,
+                   idx: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None):
+    """p [B*Tq, H_I, d_I], omega [B*Tq, H_I] fp32, ikey [N, d_I], csa_off
+    int64 [B+1], q_pos int32 [B, Tq].  Returns idx int32 [B*Tq, k]."""
+    _dev(p, omega, ikey, csa_off, q_pos, ws, idx, scores)
+    _i64(csa_off, "csa_off")
+    _i32(q_pos, "q_pos")
+    B = csa_off.numel() - 1
+    rows = q_pos.numel()
+    Tq = rows // B
+    HI, dI = p.shape[-2], p.shape[-1]
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=p.device)
+    check(lib.lca_csa_index_topk(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B, Tq, HI, dI, k, m,
+                                 w, int(max_entries), _ptr(idx), _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _dtype_code(p), _stream()), "csa_index_topk")
+    return idx
+
+
+def csa_index_score(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws: torch.Tensor,
+                    scores: Optional[torch.Tensor] = None):
+    """First half of csa_index_topk (scores + selection histogram)."""
+    _dev(p, omega, ikey, csa_off, q_pos, ws, scores)
+    B = csa_off.numel() - 1
+    rows = q_pos.numel()
+    check(lib.lca_csa_index_score(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B, rows // B,
+                                  p.shape[-2], p.shape[-1], k, m, w, int(max_entries), _ptr(scores), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _dtype_code(p), _stream()), "csa_index_score")
+
+
+def csa_topk_select(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws: torch.Tensor,
+                    idx: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None):
+    """Second half of csa_index_topk: exact top-k from the scored workspace."""
+    _dev(csa_off, q_pos, ws, idx, scores)
+    B = csa_off.numel() - 1
+    rows = q_pos.numel()
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=q_pos.device)
+    check(lib.lca_csa_topk_select(_ptr(csa_off), _ptr(q_pos), B, rows // B, k, m, w, int(max_entries), _ptr(idx),
+                                  _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+          "csa_topk_select")
+    return idx
+
+
+# ---------------------------------------------------------------- a4 / a5
+
+def _parts_out(rows, H, D, n_split, device, o_part, lse):
+    if o_part is None:
+        o_part = torch.empty((n_split, rows, H, D), dtype=torch.float32, device=device)
+    if lse is None:
+        lse = torch.empty((n_split, rows, H), dtype=torch.float32, device=device)
+    return o_part, lse
+
+
+def csa_sparse_attn(q, kv_csa, csa_off, idx, scale: float, eps: float, n_split: int,
+                    o_part=None, lse=None):
+    """q [B*Tq, H, D] raw; idx int32 [B*Tq, k].  Returns (o_part, lse)."""
+    _dev(q, kv_csa, csa_off, idx, o_part, lse)
+    _i64(csa_off, "csa_off")
+    _i32(idx, "idx")
+    B = csa_off.numel() - 1
+    rows, H, D = q.shape
+    Tq = rows // B
+    k = idx.shape[-1]
+    o_part, lse = _parts_out(rows, H, D, n_split, q.device, o_part, lse)
+    check(lib.lca_csa_sparse_attn(_ptr(q), _ptr(kv_csa), _ptr(csa_off), _ptr(idx), B, Tq, H, D, k, float(scale),
+                                  float(eps), n_split, _ptr(o_part), _ptr(lse), _dtype_code(q), _stream()),
+          "csa_sparse_attn")
+    return o_part, lse
+
+
+def hca_attn(q, kv_hca, hca_off, q_pos, m2: int, w2: int, max_entries: int, scale: float, eps: float,
+             n_split: int, o_part=None, lse=None):
+    _dev(q, kv_hca, hca_off, q_pos, o_part, lse)
+    _i64(hca_off, "hca_off")
+    _i32(q_pos, "q_pos")
+    B = hca_off.numel() - 1
+    rows, H, D = q.shape
+    Tq = rows // B
+    o_part, lse = _parts_out(rows, H, D, n_split, q.device, o_part, lse)
+    check(lib.lca_hca_attn(_ptr(q), _ptr(kv_hca), _ptr(hca_off), _ptr(q_pos), B, Tq, H, D, m2, w2, int(max_entries),
+                           float(scale), float(eps), n_split, _ptr(o_part), _ptr(lse), _dtype_code(q), _stream()),
+          "hca_attn")
+    return o_part, lse
+
+
+# ---------------------------------------------------------------- a6
+
+def swa_merge_workspace(n_rows: int, H: int, D: int) -> int:
+    return int(lib.lca_swa_merge_workspace(n_rows, H, D))
+
+
+def swa_merge(q, x, tok_off, q_pos, sink, parts, W: int, scale: float, eps: float, ws: torch.Tensor,
+              out=None):
+    """parts: list of (o_part, lse) pairs.  Returns out [B*Tq, H, D] (q's dtype)."""
+    _dev(q, x, tok_off, q_pos, sink, ws, out)
+    _i64(tok_off, "tok_off")
+    _i32(q_pos, "q_pos")
+    B = tok_off.numel() - 1
+    rows, H, D = q.shape
+    Tq = rows // B
+    arr = (Partial * max(1, len(parts)))()
+    for i, (o, l) in enumerate(parts):
+        _dev(o, l)
+        arr[i] = Partial(o.data_ptr(), l.data_ptr(), o.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    if sink is not None and sink.dtype != torch.float32:
+        raise TypeError("sink must be float32")
+    check(lib.lca_swa_merge(_ptr(q), _ptr(x), _ptr(tok_off), _ptr(q_pos), _ptr(sink), arr, len(parts), B, Tq, H, D,
+                            W, float(scale), float(eps), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                            _dtype_code(q), _stream()), "swa_merge")
+    return out

@@ -1,0 +1,142 @@
+"""One layer of hybrid compressed attention driven through liblca.
+
+Holds the static shape of a layer (heads, head dim, indexer shape, top-k,
+strides and windows), the caller's caches as device tensors with their host
+and device offsets, and reusable workspaces.  It only sizes buffers and
+sequences the C entry points; every step runs in the HIP kernels.
+
+Decode / prefill step (one call per step):
+    kv_compress (entries completed by the new tokens)
+    csa_index_topk -> csa_sparse_attn
+    hca_attn                       (independent of the indexer)
+    swa_merge (window + sink + merge of every partial)
+"""
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import ops
+
+
+def n_windows(L: int, m: int, w: int) -> int:
+    """Complete windows of length w at stride m in L tokens (host-side sizing)."""
+    return 0 if L < w else (L - w) // m + 1
+
+
+@dataclass
+class Caches:
+    lens: List[int]          # tokens per sequence covered by the caches
+    csa_off: torch.Tensor    # int64 [B+1]
+    hca_off: torch.Tensor
+    kv_csa: torch.Tensor     # [sum N_csa, D]
+    ikey: torch.Tensor       # [sum N_csa, dI]
+    kv_hca: torch.Tensor     # [sum N_hca, D]
+    csa_off_h: np.ndarray
+    hca_off_h: np.ndarray
+
+
+def _offsets(counts) -> np.ndarray:
+    o = np.zeros(len(counts) + 1, dtype=np.int64)
+    o[1:] = np.cumsum(np.asarray(counts, dtype=np.int64))
+    return o
+
+
+class HybridAttention:
+    def __init__(self, H: int, D: int, HI: int, dI: int, k: int, m: int = 4, w: int = 8, m2: int = 128,
+                 w2: int = 128, W: int = 128, eps: float = 1e-6, scale: Optional[float] = None,
+                 split_csa: Optional[int] = None, split_hca: Optional[int] = None):
+        self.H, self.D, self.HI, self.dI, self.k = H, D, HI, dI, k
+        self.m, self.w, self.m2, self.w2, self.W, self.eps = m, w, m2, w2, W, eps
+        self.scale = float(scale) if scale is not None else 1.0 / float(np.sqrt(D))
+        self.split_csa, self.split_hca = split_csa, split_hca
+        self._ws: Dict[str, torch.Tensor] = {}
+
+    # -------------------------------------------------------------- buffers
+    def _workspace(self, name: str, nbytes: int, device, zero: bool) -> torch.Tensor:
+        t = self._ws.get(name)
+        if t is None or t.numel() < nbytes or t.device != torch.device(device):
+            t = (torch.zeros if zero else torch.empty)(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._ws[name] = t
+        return t
+
+    def alloc_caches(self, lens: Sequence[int], device, dtype) -> Caches:
+        lens = [int(v) for v in lens]
+        co = _offsets([n_windows(L, self.m, self.w) for L in lens])
+        ho = _offsets([n_windows(L, self.m2, self.w2) for L in lens])
+        return Caches(
+            lens=lens,
+            csa_off=torch.from_numpy(co).to(device), hca_off=torch.from_numpy(ho).to(device),
+            # at least one row each, so that empty caches still have an address
+            kv_csa=torch.empty((max(1, int(co[-1])), self.D), dtype=dtype, device=device),
+            ikey=torch.empty((max(1, int(co[-1])), self.dI), dtype=dtype, device=device),
+            kv_hca=torch.empty((max(1, int(ho[-1])), self.D), dtype=dtype, device=device),
+            csa_off_h=co, hca_off_h=ho)
+
+    # -------------------------------------------------------------- a1
+    def compress(self, caches: Caches, raw: dict, tok_off: torch.Tensor,
+                 done_len: Optional[torch.Tensor] = None, done_len_h: Optional[Sequence[int]] = None):
+        """Write the entries of every sequence completed after done_len tokens
+        (all of them when done_len is None)."""
+        lens = caches.lens
+        done = [0] * len(lens) if done_len_h is None else [int(v) for v in done_len_h]
+        new_csa = max(n_windows(L, self.m, self.w) - n_windows(d, self.m, self.w) for L, d in zip(lens, done))
+        new_hca = max(n_windows(L, self.m2, self.w2) - n_windows(d, self.m2, self.w2) for L, d in zip(lens, done))
+        streams = []
+        if new_csa > 0:
+            streams.append(dict(src=raw["x"], logits=raw["a"], out=caches.kv_csa, ent_off=caches.csa_off,
+                                m=self.m, w=self.w, rmsnorm=1, max_entries=new_csa))
+            streams.append(dict(src=raw["u"], logits=raw["c"], out=caches.ikey, ent_off=caches.csa_off,
+                                m=self.m, w=self.w, rmsnorm=0, max_entries=new_csa))
+        if new_hca > 0:
+            streams.append(dict(src=raw["x"], logits=raw["g"], out=caches.kv_hca, ent_off=caches.hca_off,
+                                m=self.m2, w=self.w2, rmsnorm=1, max_entries=new_hca))
+        # streams of one launch share the number of 16-byte vectors per lane
+        groups: Dict[int, list] = {}
+        for s in streams:
+            lanes = s["src"].shape[-1] // (8 if s["src"].dtype == torch.bfloat16 else 4)
+            groups.setdefault(1 if lanes <= 64 else lanes // 64, []).append(s)
+        for g in groups.values():
+            ops.kv_compress(g, tok_off, done_len, self.eps)
+
+    # -------------------------------------------------------------- a2-a6
+    def index_workspace(self, rows: int, max_entries: int, device) -> torch.Tensor:
+        nbytes = ops.csa_index_topk_workspace(rows, max(1, max_entries), self.k)
+        return self._workspace(f"idx{rows}_{max_entries}", nbytes, device, zero=True)
+
+    def default_splits(self, rows: int, n_keys: int) -> int:
+        hg = (self.H + 63) // 64
+        tiles = max(1, (n_keys + 31) // 32)
+        want = max(1, -(-256 // (rows * hg)))
+        return int(max(1, min(want, tiles // 4 if tiles >= 4 else 1, 256)))
+
+    def step(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, q: torch.Tensor, p: torch.Tensor,
+             omega: torch.Tensor, sigma: Optional[torch.Tensor], q_pos: torch.Tensor, q_pos_h: np.ndarray,
+             mode: str = "A", keep: bool = False):
+        """Attention output for every query row (after the caches hold every
+        entry the query positions can see).  mode "A": one softmax over the
+        selected CSA entries, the visible HCA entries, the window and the sink;
+        "B": returns (csa-layer output, hca-layer output)."""
+        rows = q.shape[0]
+        dev = q.device
+        qmax = int(np.max(q_pos_h)) + 1
+        max_csa = max(1, n_windows(qmax, self.m, self.w))
+        max_hca = n_windows(qmax, self.m2, self.w2)
+        ws = self.index_workspace(rows, max_csa, dev)
+        idx = ops.csa_index_topk(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w, max_csa, ws)
+        sc = self.split_csa or self.default_splits(rows, self.k)
+        sh = self.split_hca or self.default_splits(rows, max_hca)
+        csa = ops.csa_sparse_attn(q, caches.kv_csa, caches.csa_off, idx, self.scale, self.eps, sc)
+        hca = ops.hca_attn(q, caches.kv_hca, caches.hca_off, q_pos, self.m2, self.w2, max_hca, self.scale, self.eps,
+                           sh)
+        wsm = self._workspace(f"swa{rows}", ops.swa_merge_workspace(rows, self.H, self.D), dev, zero=False)
+        if mode == "A":
+            out = ops.swa_merge(q, x, tok_off, q_pos, sigma, [csa, hca], self.W, self.scale, self.eps, wsm)
+        else:
+            o1 = ops.swa_merge(q, x, tok_off, q_pos, sigma, [csa], self.W, self.scale, self.eps, wsm)
+            o2 = ops.swa_merge(q, x, tok_off, q_pos, sigma, [hca], self.W, self.scale, self.eps, wsm)
+            out = (o1, o2)
+        if keep:
+            return out, dict(idx=idx, csa=csa, hca=hca)
+        return out

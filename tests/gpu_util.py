@@ -1,0 +1,111 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the
+HIP path through the C-ABI, and compare against the oracle."""
+import numpy as np
+import torch
+
+import lca_inputs as li
+from oracle import attention as oatt
+from oracle import indexer as oidx
+from oracle import pipeline as opipe
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}     # max-abs output tolerance
+REL = {"bf16": 1e-2, "f32": 1e-5}     # extra: relative Frobenius error
+U32 = 2.0 ** -24
+
+
+def tdtype(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def to_device(raw, cfg, dev="cuda"):
+    dt = tdtype(cfg)
+    d = {}
+    for k in ("x", "a", "g", "u", "c", "q", "p"):
+        d[k] = torch.from_numpy(np.ascontiguousarray(raw[k])).to(dev).to(dt)
+    d["omega"] = torch.from_numpy(raw["omega"]).to(dev).contiguous()
+    d["sigma"] = torch.from_numpy(raw["sigma"]).to(dev).contiguous()
+    d["tok_off"] = torch.from_numpy(raw["tok_off"]).to(dev)
+    d["q_pos"] = torch.from_numpy(np.ascontiguousarray(raw["q_pos"].reshape(-1))).to(dev)
+    return d
+
+
+def layer_for(cfg, **kw):
+    from long_context_attention_20_amd import HybridAttention
+    return HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps, **kw)
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def seq_caches(caches, b):
+    co, ho = caches.csa_off_h, caches.hca_off_h
+    return opipe.SeqCaches(f64(caches.kv_csa[co[b]:co[b + 1]]), f64(caches.ikey[co[b]:co[b + 1]]),
+                           f64(caches.kv_hca[ho[b]:ho[b + 1]]))
+
+
+def run_gpu(cfg, raw, dev="cuda", mode="A", **kw):
+    d = to_device(raw, cfg, dev)
+    layer = layer_for(cfg, **kw)
+    caches = layer.alloc_caches(cfg.lens, dev, tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    out, inter = layer.step(caches, d["x"], d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"],
+                            raw["q_pos"].reshape(-1), mode=mode, keep=True)
+    torch.cuda.synchronize()
+    return d, layer, caches, out, inter
+
+
+def merge_splits(o_part, lse):
+    """GPU split partials of one row -> (o [H, D], lse [H]) via the oracle merge."""
+    parts = [(f64(o_part[s]), f64(lse[s])) for s in range(o_part.shape[0])]
+    return oatt.merge(parts, None)
+
+
+def score_bound(p, omega, keys):
+    """A-priori bound on |fp32 score - exact score| for every key."""
+    p = np.asarray(p, np.float64)
+    om = np.abs(np.asarray(omega, np.float64))
+    mag = np.abs(keys) @ np.abs(p).T            # [N, HI]
+    n = p.shape[1] + p.shape[0] + 4
+    return 2.0 * n * U32 * (mag @ om) + 1e-30
+
+
+def check_topk(sel_gpu, s_gpu, s_ref, bound, k):
+    """Set checks for one query row.  Returns the number of accepted near-tie
+    differences."""
+    nv = len(s_ref)
+    sel = np.asarray(sel_gpu)
+    assert np.all(sel[sel >= 0] < nv), "selected an invisible entry"
+    chosen = sel[sel >= 0]
+    assert len(set(chosen.tolist())) == len(chosen), "duplicate index"
+    if nv <= k:
+        assert sorted(chosen.tolist()) == list(range(nv))
+        assert np.all(sel[nv:] == -1)
+        return 0
+    assert len(chosen) == k
+    # exact self-consistency with the GPU's own fp32 scores
+    self_ref = set(oidx.topk(np.asarray(s_gpu[:nv], np.float64), k).tolist())
+    assert set(chosen.tolist()) == self_ref, "selection is not the exact top-k of the GPU scores"
+    # GPU scores against the oracle
+    err = np.abs(np.asarray(s_gpu[:nv], np.float64) - s_ref)
+    assert np.all(err <= bound), f"score error {np.max(err / bound):.2f}x the fp32 bound"
+    ref = oidx.topk(s_ref, k)
+    kth = s_ref[ref[-1]]
+    diff = set(chosen.tolist()) ^ set(ref.tolist())
+    for j in diff:
+        assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + bound[j], \
+            f"entry {j}: score {s_ref[j]} vs k-th {kth}: not a tie"
+    return len(diff)
+
+
+def assert_close(got, ref, dtype, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    assert err <= TOL[dtype], f"{what}: max-abs {err:.3e} > {TOL[dtype]}"
+    nrm = np.linalg.norm(ref)
+    if nrm > 0:
+        rel = np.linalg.norm(got - ref) / nrm
+        assert rel <= REL[dtype], f"{what}: relative error {rel:.3e} > {REL[dtype]}"
+    return err
