@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Decode throughput of one hybrid compressed attention layer on one MI355X.
+
+Metric: decode query-tokens/s per layer at a 1M-token Pro-shaped context, and
+the fraction of peak HBM bandwidth it corresponds to.
+
+A step is one pass of the whole hot path for one query token per sequence:
+  kv_compress (the CSA, indexer-key and HCA entries the new token completes)
+  -> csa_index_score -> csa_topk_select -> csa_sparse_attn
+  -> hca_attn -> swa_merge (window + sink + merge)
+over caches resident in HBM.  To keep the 256 MB Infinity Cache from serving
+the caches, steps rotate over R layers, each with its own raw streams and
+caches (R * per-step bytes >= 2 x 256 MB).
+
+Timed regions (HIP events on the launch stream, synchronised on both sides):
+  1. the step replayed as HIP graphs (headline value), then
+  2. the same steps launched directly, with events bracketing the dominant
+     kernel's launch in every step (its average duration gives the roofline).
+cpu_baseline: the float64 oracle on the host, same workload, bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X
+MFMA_BF16_PEAK = 2.5e15    # dense bf16 FLOP/s, MI355X
+MALL_BYTES = 256 << 20
+
+
+def n_windows(L, m, w):
+    return 0 if L < w else (L - w) // m + 1
+
+
+def step_bytes(cfg):
+    """Algorithmic HBM bytes of one decode step: what the method must move."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    tot = 0
+    for L in cfg.lens:
+        ncsa = n_windows(L, cfg.m, cfg.w)
+        nh = n_windows(L, cfg.m2, cfg.w2)
+        kk = min(cfg.k, ncsa)
+        tot += ncsa * cfg.dI * e                        # indexer keys
+        tot += kk * (cfg.D * e + 4)                     # selected entries + indices
+        tot += min(cfg.W, L) * cfg.D * e                # window rows
+        tot += nh * cfg.D * e                           # HCA entries
+        tot += cfg.H * cfg.D * 2 * e + cfg.H * 4        # q, out, sink
+    return tot
+
+
+def kernel_cost(cfg, name):
+    """(bytes, flops) that one launch of a step's kernel must move / do."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    by = fl = 0
+    for L in cfg.lens:
+        ncsa = n_windows(L, cfg.m, cfg.w)
+        nh = n_windows(L, cfg.m2, cfg.w2)
+        kk = min(cfg.k, ncsa)
+        if name == "csa_index_score":
+            by += ncsa * cfg.dI * e
+            fl += 2 * ncsa * cfg.dI * cfg.HI
+        elif name == "csa_topk_select":
+            by += ncsa * 4 + kk * 4
+        elif name == "csa_sparse_attn":
+            by += kk * cfg.D * e + cfg.H * cfg.D * e
+            fl += 4 * cfg.H * cfg.D * kk
+        elif name == "hca_attn":
+            by += nh * cfg.D * e + cfg.H * cfg.D * e
+            fl += 4 * cfg.H * cfg.D * nh
+        elif name == "swa_merge":
+            nwin = min(cfg.W, L)
+            by += nwin * cfg.D * e + cfg.H * cfg.D * 2 * e
+            fl += 4 * cfg.H * cfg.D * nwin
+        elif name == "kv_compress":
+            by += (2 * cfg.w * cfg.D + 2 * cfg.w * cfg.dI + 2 * cfg.w2 * cfg.D) * e + (2 * cfg.D + cfg.dI) * e
+    return by, fl
+
+
+class LayerState:
+    """One layer's inputs and caches, all resident on the GPU."""
+
+    def __init__(self, cfg, layer, attn, dev):
+        import torch
+        import lca_inputs as li
+        raw = li.make_raw_torch(cfg, layer, dev)
+        self.raw = raw
+        self.caches = attn.alloc_caches(cfg.lens, dev, raw["x"].dtype)
+        attn.compress(self.caches, raw, raw["tok_off"])                     # cache build
+        self.q, self.p, self.omega, self.sigma = raw["q"], raw["p"], raw["omega"], raw["sigma"]
+        self.q_pos = raw["q_pos"].reshape(-1).contiguous()
+        self.tok_off = raw["tok_off"]
+        self.done = torch.tensor([L - 1 for L in cfg.lens], dtype=torch.int64, device=dev)
+        self.streams = []
+        c, dv = self.caches, cfg
+        for src, lg, out, off, m, w, norm in ((raw["x"], raw["a"], c.kv_csa, c.csa_off, dv.m, dv.w, 1),
+                                              (raw["u"], raw["c"], c.ikey, c.csa_off, dv.m, dv.w, 0),
+                                              (raw["x"], raw["g"], c.kv_hca, c.hca_off, dv.m2, dv.w2, 1)):
+            new = max(n_windows(L, m, w) - n_windows(L - 1, m, w) for L in cfg.lens)
+            if new > 0:
+                self.streams.append(dict(src=src, logits=lg, out=out, ent_off=off, m=m, w=w, rmsnorm=norm,
+                                         max_entries=new))
+
+
+class Runner:
+    def __init__(self, cfg, R, dev):
+        import torch
+        from long_context_attention_20_amd import HybridAttention, ops
+        self.torch, self.ops = torch, ops
+        self.cfg = cfg
+        a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps)
+        self.attn = a
+        self.layers = [LayerState(cfg, r, a, dev) for r in range(R)]
+        rows = cfg.B * cfg.tq
+        qmax = max(cfg.lens)
+        self.max_csa = max(1, n_windows(qmax, cfg.m, cfg.w))
+        self.max_hca = n_windows(qmax, cfg.m2, cfg.w2)
+        self.ws_idx = a.index_workspace(rows, self.max_csa, dev)
+        self.ws_swa = torch.empty(ops.swa_merge_workspace(rows, cfg.H, cfg.D), dtype=torch.uint8, device=dev)
+        self.sc = a.default_splits(rows, cfg.k)
+        self.sh = a.default_splits(rows, self.max_hca)
+        f32 = torch.float32
+        self.idx = torch.empty((rows, cfg.k), dtype=torch.int32, device=dev)
+        self.csa = (torch.empty((self.sc, rows, cfg.H, cfg.D), dtype=f32, device=dev),
+                    torch.empty((self.sc, rows, cfg.H), dtype=f32, device=dev))
+        self.hca = (torch.empty((self.sh, rows, cfg.H, cfg.D), dtype=f32, device=dev),
+                    torch.empty((self.sh, rows, cfg.H), dtype=f32, device=dev))
+        self.out = torch.empty((rows, cfg.H, cfg.D), dtype=self.layers[0].q.dtype, device=dev)
+        self.names = ["kv_compress", "csa_index_score", "csa_topk_select", "csa_sparse_attn", "hca_attn",
+                      "swa_merge"]
+
+    def calls(self, L):
+        cfg, ops, a, c = self.cfg, self.ops, self.attn, L.caches
+        return [
+            lambda: ops.kv_compress(L.streams, L.tok_off, L.done, cfg.eps),
+            lambda: ops.csa_index_score(L.p, L.omega, c.ikey, c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, self.max_csa,
+                                        self.ws_idx),
+            lambda: ops.csa_topk_select(c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, self.max_csa, self.ws_idx,
+                                        idx=self.idx),
+            lambda: ops.csa_sparse_attn(L.q, c.kv_csa, c.csa_off, self.idx, a.scale, cfg.eps, self.sc, *self.csa),
+            lambda: ops.hca_attn(L.q, c.kv_hca, c.hca_off, L.q_pos, cfg.m2, cfg.w2, self.max_hca, a.scale, cfg.eps,
+                                 self.sh, *self.hca),
+            lambda: ops.swa_merge(L.q, L.raw["x"], L.tok_off, L.q_pos, L.sigma, [self.csa, self.hca], cfg.W, a.scale,
+                                  cfg.eps, self.ws_swa, out=self.out),
+        ]
+
+    def step(self, L, probe=None):
+        for i, f in enumerate(self.calls(L)):
+            if probe is not None and i == probe[0]:
+                probe[1].record()
+                f()
+                probe[2].record()
+            else:
+                f()
+
+
+def cpu_baseline(cfg, state, budget_s):
+    """The oracle (float64, numpy) on this host: one decode step per query of
+    layer 0 -- append the completed entries, score, select, attend, merge --
+    on caches it builds itself from the same raw inputs (build not timed)."""
+    from oracle import compress as ocmp
+    from oracle import numerics as onum
+    from oracle import pipeline as opipe
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    raw = state.raw
+    b = 0
+    L = cfg.lens[b]
+    off = raw["tok_off"].cpu().numpy()
+    def host(t):
+        return t[int(off[b]):int(off[b + 1])].float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    x, a, g, u, c = host(raw["x"]), host(raw["a"]), host(raw["g"]), host(raw["u"]), host(raw["c"])
+    caches = opipe.build_seq_caches(x, a, g, u, c, cfg)
+    build_s = time.perf_counter() - t0
+    q = raw["q"][0].float().cpu().numpy().astype(np.float64)
+    p = raw["p"][0].float().cpu().numpy().astype(np.float64)
+    om = raw["omega"][0].cpu().numpy().astype(np.float64)
+    sg = raw["sigma"].cpu().numpy().astype(np.float64)
+    i = L - 1
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        # append: the entries the newest token completes
+        for m, w, src, lg, norm, name in ((cfg.m, cfg.w, x, a, True, "kv_csa"), (cfg.m, cfg.w, u, c, False, "ikey"),
+                                          (cfg.m2, cfg.w2, x, g, True, "kv_hca")):
+            new = range(ocmp.n_entries(L - 1, m, w), ocmp.n_entries(L, m, w))
+            if len(new):
+                getattr(caches, name)[list(new)] = onum.round_to(ocmp.compress(src, lg, m, w, norm, cfg.eps, new),
+                                                                 cfg.dtype)
+        opipe.query_step(caches, x, q, p, om, sg, i, cfg)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    return {"value": n / el, "unit": "q-tok/s/layer", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} decode steps of sequence 0 (1 query at position {i}) of layer 0, float64 numpy oracle "
+                      f"(append + indexer + top-k + sparse + HCA + window + sink + merge) on caches it built "
+                      f"itself in {build_s:.1f} s (not timed); {el:.1f} s timed",
+            "seconds": round(el, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--config", default="pro_1m_decode")
+    ap.add_argument("--layers", type=int, default=0, help="layers to rotate over (0: enough to exceed 2x MALL)")
+    ap.add_argument("--graph", type=int, default=1, help="1: headline from HIP graph replay")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        sys.exit(2)
+
+    import torch
+    import lca_inputs as li
+    cfg = li.CONFIGS[args.config]
+    if cfg.tq != 1:
+        raise SystemExit("bench.py measures decode workloads (one query token per sequence)")
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    sb = step_bytes(cfg)
+    R = args.layers or max(1, -(-2 * MALL_BYTES // sb))
+    t0 = time.perf_counter()
+    run = Runner(cfg, R, dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    print(f"[bench] {cfg.name}: {R} layers built in {setup_s:.1f} s; {sb / 1e6:.2f} MB/step; "
+          f"splits csa={run.sc} hca={run.sh}", file=sys.stderr, flush=True)
+
+    # warm-up, and per-kernel event timing to find the dominant kernel
+    s = torch.cuda.current_stream()
+    per = np.zeros(len(run.names))
+    cnt = 0
+    for w in range(max(args.warmup, 2 * R)):
+        L = run.layers[w % R]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in run.names]
+        for i, f in enumerate(run.calls(L)):
+            evs[i][0].record()
+            f()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        if w >= R:
+            per += [a.elapsed_time(b) for a, b in evs]
+            cnt += 1
+    per /= max(1, cnt)
+    dom = int(np.argmax(per))
+    print("[bench] per-kernel ms (isolated): " + ", ".join(f"{n}={t:.4f}" for n, t in zip(run.names, per)),
+          file=sys.stderr, flush=True)
+
+    K = args.steps
+    ms_graph = None
+    if args.graph:
+        graphs = []
+        for L in run.layers:
+            for _ in range(2):
+                run.step(L)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run.step(L)
+            graphs.append(g)
+        for w in range(args.warmup):
+            graphs[w % R].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for it in range(K):
+            graphs[it % R].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / K
+
+    # stream launches, dominant kernel bracketed by events in every step
+    for w in range(args.warmup):
+        run.step(run.layers[w % R])
+    torch.cuda.synchronize()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for it in range(K):
+        run.step(run.layers[it % R], probe=(dom, kev[it][0], kev[it][1]))
+    e1.record()
+    torch.cuda.synchronize()
+    ms_stream = e0.elapsed_time(e1) / K
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+
+    ms = ms_graph if ms_graph is not None else ms_stream
+    value = cfg.B / (ms / 1e3)
+    name = run.names[dom]
+    kb, kf = kernel_cost(cfg, name)
+    if name in ("hca_attn", "csa_sparse_attn", "swa_merge") and kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
+        roof = {"bound": "mfma", "achieved": kf / (k_ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kb / (k_ms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = name
+    roof["kernel_ms"] = k_ms
+    roof["bytes_per_launch"] = kb
+    roof["flops_per_launch"] = kf
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(cfg, run.layers[0], args.cpu_seconds)
+
+    res = {
+        "metric": "decode query-tokens/s per layer at 1M ctx (Pro shape); % of HBM peak BW",
+        "value": value,
+        "unit": "q-tok/s/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1), generated on the GPU)",
+        "config": {"workload": cfg.name, "sequences": cfg.B, "context": list(cfg.lens) if cfg.B <= 8 else
+                   f"{cfg.B} seqs, mean {int(np.mean(cfg.lens))}", "q_heads": cfg.H, "head_dim": cfg.D,
+                   "indexer": f"{cfg.HI}x{cfg.dI}", "topk": cfg.k, "m": cfg.m, "m2": cfg.m2, "window": cfg.W,
+                   "layers_rotated": R, "timing": "hip-graph replay" if ms_graph is not None else "stream"},
+        "hbm_frac_of_peak": sb / (ms / 1e3) / HBM_PEAK,
+        "bytes_per_step": sb,
+        "ms_per_step_stream": ms_stream,
+        "kernel_ms_isolated": {n: float(t) for n, t in zip(run.names, per)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -6,6 +6,10 @@ there is no fallback: loading fails loudly when it is missing.
 import ctypes
 import os
 
+# torch first: torch ships its own HIP runtime with the same soname as the
+# system one; loading it first makes liblca bind to that single runtime.
+import torch  # noqa: F401
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblca.so")
 

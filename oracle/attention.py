@@ -66,7 +66,8 @@ def merge(parts, sigma=None):
     stack = np.stack(lses, axis=0)                    # [P, H]
     mx = np.max(stack, axis=0)
     safe = np.where(np.isfinite(mx), mx, 0.0)
-    tot = safe + np.log(np.sum(np.exp(stack - safe), axis=0))
+    with np.errstate(divide="ignore"):                # all parts empty -> log(0) = -inf
+        tot = safe + np.log(np.sum(np.exp(stack - safe), axis=0))
     tot = np.where(np.isfinite(mx), tot, -np.inf)
     o = np.zeros((H, D))
     for o_p, l_p in parts:

@@ -60,9 +60,11 @@ def test_kv_compress(case):
                 err = np.max(np.abs(got - ref))
                 assert err <= TOL[cfg.dtype], f"{name}[{b}] max-abs {err}"
                 if cfg.dtype == "bf16":
-                    # at most one bf16 step apart
-                    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
-                    assert np.all(np.abs(got - ref) <= ulp), f"{name}[{b}] beyond one bf16 step"
+                    # one bf16 step of the value, plus the fp32 rounding of a
+                    # pooled sum of O(1) terms (values near zero cancel)
+                    lim = np.abs(ref) * 2.0 ** -7 + 1e-5
+                    bad = np.abs(got - ref) > lim
+                    assert not np.any(bad), f"{name}[{b}]: {int(bad.sum())} values beyond one bf16 step"
                 eq += int(np.sum(got == ref))
                 tot += got.size
     if tot and cfg.dtype == "bf16":
