@@ -75,11 +75,13 @@ def kernel_cost(cfg, name):
         elif name == "hca_attn":
             by += nh * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * nh
-        elif name == "swa_merge":
+        elif name == "swa_attn":
             nwin = min(cfg.W, L)
-            by += nwin * cfg.D * e + cfg.H * cfg.D * 2 * e
+            by += nwin * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * nwin
-        elif name == "kv_compress":
+        elif name == "swa_merge":
+            by += cfg.H * cfg.D * e + cfg.H * 4                # output + sink
+        elif name == "kv_compress":                            # the entries one token completes
             by += (2 * cfg.w * cfg.D + 2 * cfg.w * cfg.dI + 2 * cfg.w2 * cfg.D) * e + (2 * cfg.D + cfg.dI) * e
     return by, fl
 
@@ -97,61 +99,55 @@ class LayerState:
         self.q, self.p, self.omega, self.sigma = raw["q"], raw["p"], raw["omega"], raw["sigma"]
         self.q_pos = raw["q_pos"].reshape(-1).contiguous()
         self.tok_off = raw["tok_off"]
-        self.done = torch.tensor([L - 1 for L in cfg.lens], dtype=torch.int64, device=dev)
-        self.streams = []
-        c, dv = self.caches, cfg
-        for src, lg, out, off, m, w, norm in ((raw["x"], raw["a"], c.kv_csa, c.csa_off, dv.m, dv.w, 1),
-                                              (raw["u"], raw["c"], c.ikey, c.csa_off, dv.m, dv.w, 0),
-                                              (raw["x"], raw["g"], c.kv_hca, c.hca_off, dv.m2, dv.w2, 1)):
-            new = max(n_windows(L, m, w) - n_windows(L - 1, m, w) for L in cfg.lens)
-            if new > 0:
-                self.streams.append(dict(src=src, logits=lg, out=out, ent_off=off, m=m, w=w, rmsnorm=norm,
-                                         max_entries=new))
+        self.done_h = [L - 1 for L in cfg.lens]
+        self.done = torch.tensor(self.done_h, dtype=torch.int64, device=dev)
 
 
 class Runner:
-    def __init__(self, cfg, R, dev):
+    def __init__(self, cfg, R, dev, split_csa=0, split_hca=0):
         import torch
         from long_context_attention_20_amd import HybridAttention, ops
         self.torch, self.ops = torch, ops
         self.cfg = cfg
-        a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps)
+        a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
+                            split_csa=split_csa or None, split_hca=split_hca or None)
         self.attn = a
         self.layers = [LayerState(cfg, r, a, dev) for r in range(R)]
         rows = cfg.B * cfg.tq
         qmax = max(cfg.lens)
-        self.max_csa = max(1, n_windows(qmax, cfg.m, cfg.w))
-        self.max_hca = n_windows(qmax, cfg.m2, cfg.w2)
-        self.ws_idx = a.index_workspace(rows, self.max_csa, dev)
-        self.ws_swa = torch.empty(ops.swa_merge_workspace(rows, cfg.H, cfg.D), dtype=torch.uint8, device=dev)
-        self.sc = a.default_splits(rows, cfg.k)
-        self.sh = a.default_splits(rows, self.max_hca)
-        f32 = torch.float32
-        self.idx = torch.empty((rows, cfg.k), dtype=torch.int32, device=dev)
-        self.csa = (torch.empty((self.sc, rows, cfg.H, cfg.D), dtype=f32, device=dev),
-                    torch.empty((self.sc, rows, cfg.H), dtype=f32, device=dev))
-        self.hca = (torch.empty((self.sh, rows, cfg.H, cfg.D), dtype=f32, device=dev),
-                    torch.empty((self.sh, rows, cfg.H), dtype=f32, device=dev))
-        self.out = torch.empty((rows, cfg.H, cfg.D), dtype=self.layers[0].q.dtype, device=dev)
-        self.names = ["kv_compress", "csa_index_score", "csa_topk_select", "csa_sparse_attn", "hca_attn",
-                      "swa_merge"]
+        self.bufs = a.decode_buffers(rows, n_windows(qmax, cfg.m, cfg.w), n_windows(qmax, cfg.m2, cfg.w2), dev,
+                                     self.layers[0].q.dtype)
+        self.sc, self.sh = self.bufs["sc"], self.bufs["sh"]
+        self.side = torch.cuda.Stream()
+        self.names = ["kv_compress(csa,idx)", "kv_compress(hca)", "csa_index_score", "csa_topk_select",
+                      "csa_sparse_attn", "hca_attn", "swa_attn", "swa_merge"]
+
+    def step(self, L, side=True):
+        """The whole decode step; the HCA and window branches on the side stream."""
+        return self.attn.decode_step(L.caches, L.raw, L.tok_off, L.q, L.p, L.omega, L.sigma, L.q_pos, self.bufs,
+                                     done_len=L.done, done_h=L.done_h, side=self.side if side else None)
 
     def calls(self, L):
-        cfg, ops, a, c = self.cfg, self.ops, self.attn, L.caches
+        """The same step as a sequence of single-kernel calls (one stream)."""
+        cfg, ops, a, c, bf = self.cfg, self.ops, self.attn, L.caches, self.bufs
+        st_c = a.compress_streams(c, L.raw, L.done_h, ("csa", "idx"))
+        st_h = a.compress_streams(c, L.raw, L.done_h, ("hca",))
         return [
-            lambda: ops.kv_compress(L.streams, L.tok_off, L.done, cfg.eps),
-            lambda: ops.csa_index_score(L.p, L.omega, c.ikey, c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, self.max_csa,
-                                        self.ws_idx),
-            lambda: ops.csa_topk_select(c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, self.max_csa, self.ws_idx,
-                                        idx=self.idx),
-            lambda: ops.csa_sparse_attn(L.q, c.kv_csa, c.csa_off, self.idx, a.scale, cfg.eps, self.sc, *self.csa),
-            lambda: ops.hca_attn(L.q, c.kv_hca, c.hca_off, L.q_pos, cfg.m2, cfg.w2, self.max_hca, a.scale, cfg.eps,
-                                 self.sh, *self.hca),
-            lambda: ops.swa_merge(L.q, L.raw["x"], L.tok_off, L.q_pos, L.sigma, [self.csa, self.hca], cfg.W, a.scale,
-                                  cfg.eps, self.ws_swa, out=self.out),
+            lambda: st_c and ops.kv_compress(st_c, L.tok_off, L.done, cfg.eps),
+            lambda: st_h and ops.kv_compress(st_h, L.tok_off, L.done, cfg.eps),
+            lambda: ops.csa_index_score(L.p, L.omega, c.ikey, c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, bf["max_csa"],
+                                        bf["ws_idx"]),
+            lambda: ops.csa_topk_select(c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, bf["max_csa"], bf["ws_idx"],
+                                        idx=bf["idx"]),
+            lambda: ops.csa_sparse_attn(L.q, c.kv_csa, c.csa_off, bf["idx"], a.scale, cfg.eps, bf["sc"], *bf["csa"]),
+            lambda: ops.hca_attn(L.q, c.kv_hca, c.hca_off, L.q_pos, cfg.m2, cfg.w2, bf["max_hca"], a.scale, cfg.eps,
+                                 bf["sh"], *bf["hca"]),
+            lambda: ops.swa_attn(L.q, L.raw["x"], L.tok_off, L.q_pos, cfg.W, a.scale, cfg.eps, *bf["swa"]),
+            lambda: ops.swa_merge(L.q, None, None, None, L.sigma, [bf["csa"], bf["hca"], bf["swa"]], 0, a.scale,
+                                  cfg.eps, None, out=bf["out"]),
         ]
 
-    def step(self, L, probe=None):
+    def step_calls(self, L, probe=None):
         for i, f in enumerate(self.calls(L)):
             if probe is not None and i == probe[0]:
                 probe[1].record()
@@ -220,6 +216,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="layers to rotate over (0: enough to exceed 2x MALL)")
     ap.add_argument("--graph", type=int, default=1, help="1: headline from HIP graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
+    ap.add_argument("--split-csa", type=int, default=0, help="entry splits of the sparse attention (0: default)")
+    ap.add_argument("--split-hca", type=int, default=0, help="entry splits of the HCA attention (0: default)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
@@ -236,7 +234,7 @@ def main():
     sb = step_bytes(cfg)
     R = args.layers or max(1, -(-2 * MALL_BYTES // sb))
     t0 = time.perf_counter()
-    run = Runner(cfg, R, dev)
+    run = Runner(cfg, R, dev, args.split_csa, args.split_hca)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     print(f"[bench] {cfg.name}: {R} layers built in {setup_s:.1f} s; {sb / 1e6:.2f} MB/step; "
@@ -267,8 +265,12 @@ def main():
     if args.graph:
         graphs = []
         for L in run.layers:
-            for _ in range(2):
-                run.step(L)
+            s2 = torch.cuda.Stream()
+            s2.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s2):
+                for _ in range(2):
+                    run.step(L)
+            torch.cuda.current_stream().wait_stream(s2)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -287,13 +289,13 @@ def main():
 
     # stream launches, dominant kernel bracketed by events in every step
     for w in range(args.warmup):
-        run.step(run.layers[w % R])
+        run.step_calls(run.layers[w % R])
     torch.cuda.synchronize()
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for it in range(K):
-        run.step(run.layers[it % R], probe=(dom, kev[it][0], kev[it][1]))
+        run.step_calls(run.layers[it % R], probe=(dom, kev[it][0], kev[it][1]))
     e1.record()
     torch.cuda.synchronize()
     ms_stream = e0.elapsed_time(e1) / K
@@ -302,8 +304,10 @@ def main():
     ms = ms_graph if ms_graph is not None else ms_stream
     value = cfg.B / (ms / 1e3)
     name = run.names[dom]
-    kb, kf = kernel_cost(cfg, name)
-    if name in ("hca_attn", "csa_sparse_attn", "swa_merge") and kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
+    kb, kf = kernel_cost(cfg, name.split("(")[0])
+    if name.startswith("kv_compress"):  # split between the two launches
+        kb = kb // 2
+    if name in ("hca_attn", "csa_sparse_attn", "swa_attn") and kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
         roof = {"bound": "mfma", "achieved": kf / (k_ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
                 "unit": "TFLOP/s"}
     else:

@@ -204,6 +204,14 @@ int lca_hca_attn(const void* q, const void* kv_hca, const int64_t* hca_off, cons
  *   x       [T, D] raw KV rows, packed by tok_off (device int64 [B+1])
  *   out     [B*Tq, H, D] (dtype)
  * ---------------------------------------------------------------------- */
+/* The window branch alone, as a partial: attends to the raw rows
+ * max(0, i-W+1) .. i of x (RMS-normalised over D and rounded to the storage
+ * type on load) and writes o_part [1, B*Tq, H, D] and lse [1, B*Tq, H] (one
+ * split), so that it can run beside the other branches and be merged by
+ * lca_swa_merge with W = 0.  W >= 1. */
+int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int32_t* q_pos, int B, int Tq, int H,
+                 int D, int W, float scale, float eps, float* o_part, float* lse, int dtype, void* stream);
+
 typedef struct lca_partial {
   const float* o;   /* [n_split, B*Tq, H, D] */
   const float* lse; /* [n_split, B*Tq, H]    */

@@ -24,7 +24,7 @@ LCA_BF16 = 1
 EXPORTS = [
     "lca_strerror", "lca_last_error", "lca_version", "lca_kv_compress",
     "lca_csa_index_topk_workspace", "lca_csa_index_topk", "lca_csa_index_score", "lca_csa_topk_select", "lca_csa_sparse_attn", "lca_hca_attn",
-    "lca_swa_merge_workspace", "lca_swa_merge",
+    "lca_swa_attn", "lca_swa_merge_workspace", "lca_swa_merge",
 ]
 
 
@@ -72,6 +72,8 @@ def _load():
     L.lca_csa_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, i32, vp, vp, i32, vp]
     L.lca_hca_attn.restype = i32
     L.lca_hca_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, f32, f32, i32, vp, vp, i32, vp]
+    L.lca_swa_attn.restype = i32
+    L.lca_swa_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp, i32, vp]
     L.lca_swa_merge_workspace.restype = sz
     L.lca_swa_merge_workspace.argtypes = [i32, i32, i32]
     L.lca_swa_merge.restype = i32

@@ -230,6 +230,17 @@ int lca_hca_attn(const void* q, const void* kv_hca, const int64_t* hca_off, cons
                 st, "hca_attn");
 }
 
+int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int32_t* q_pos, int B, int Tq, int H,
+                 int D, int W, float scale, float eps, float* o_part, float* lse, int dtype, void* stream) {
+  int rc = check_attn("swa_attn", q, x, tok_off, q_pos, B, Tq, H, D, scale, eps, 1, o_part, lse, dtype);
+  if (rc != LCA_OK) return rc;
+  LCA_REQUIRE(W >= 1, LCA_ERR_INVALID_ARG, "swa_attn: W=%d must be >= 1", W);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_attention(2, q, x, tok_off, nullptr, q_pos, B, Tq, H, D, 0, 1, 1, W, scale, eps, 1, o_part,
+                                 lse, dtype, st),
+                st, "swa_attn");
+}
+
 size_t lca_swa_merge_workspace(int n_rows, int H, int D) {
   if (n_rows < 1 || H < 1 || D < 1) return 0;
   const size_t o = ((size_t)n_rows * H * D * 4 + 255) & ~(size_t)255;
@@ -247,9 +258,13 @@ int lca_swa_merge(const void* q, const void* x, const int64_t* tok_off, const in
   LCA_REQUIRE(W >= 0, LCA_ERR_INVALID_ARG, "swa_merge: W=%d", W);
   LCA_REQUIRE(n_parts >= 0 && n_parts <= 7, LCA_ERR_UNSUPPORTED, "swa_merge: n_parts=%d not in [0,7]", n_parts);
   LCA_REQUIRE(n_parts == 0 || parts != nullptr, LCA_ERR_INVALID_ARG, "swa_merge: parts is NULL");
-  for (int p = 0; p < n_parts; ++p)
+  int slots = W > 0 ? 1 : 0;
+  for (int p = 0; p < n_parts; ++p) {
     LCA_REQUIRE(parts[p].o && parts[p].lse && parts[p].n_split >= 1 && parts[p].n_split <= 256,
                 LCA_ERR_INVALID_ARG, "swa_merge: part %d is invalid", p);
+    slots += parts[p].n_split;
+  }
+  LCA_REQUIRE(slots <= 512, LCA_ERR_UNSUPPORTED, "swa_merge: %d partial slots, at most 512", slots);
   LCA_REQUIRE(std::isfinite(scale) && scale > 0.f, LCA_ERR_INVALID_ARG, "swa_merge: scale");
   LCA_REQUIRE(std::isfinite(eps) && eps >= 0.f, LCA_ERR_INVALID_ARG, "swa_merge: eps");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

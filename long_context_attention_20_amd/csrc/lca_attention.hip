@@ -14,13 +14,16 @@
 // A compressed entry is key and value (K = V).
 //
 // Matrix-core path (bf16, H a multiple of 16): a block holds one query row and
-// 64 heads (4 waves x 16 heads).  A wave keeps its 16 normalised query heads in
-// registers as the B operand of S^T = K . Qhat^T (v_mfma_f32_16x16x32_bf16:
-// 16 entries x 16 heads x 32 dims per instruction), runs the online softmax on
-// the S^T accumulator (lane = head, 8 entries per lane), and accumulates
+// 64 heads.  A wave keeps normalised query heads in registers as the B operand
+// of S^T = K . Qhat^T (v_mfma_f32_16x16x32_bf16: 16 entries x 16 heads x 32
+// dims per instruction), runs the online softmax on the S^T accumulator
+// (lane = head, 8 entries per lane), and accumulates
 // O^T = V^T . P^T, whose B operand is the S^T accumulator itself once rounded
 // to bf16 (the contraction index is permuted identically in A and B).  The
-// 32-entry KV tile sits in LDS (rows padded to avoid bank conflicts); the next
+// 32-entry KV tile sits in LDS once, row-major (rows padded against bank
+// conflicts): S^T reads it with 16-byte row reads, and the V^T operand of
+// O^T comes from the same rows through ds_read_b64_tr_b16, whose 16-lane
+// transpose hands lane i column i of a 4-row x 16-column block.  The next
 // tile's global loads are in flight while the current tile is computed.
 #include "lca_common.h"
 
@@ -77,28 +80,68 @@ __device__ __forceinline__ int64_t attn_row(const AttnParams& a, int r, int64_t 
 
 // ============================================================ matrix cores
 
-constexpr int kTile = 32;  // keys per tile
+constexpr int kTile = 32;       // keys per tile
+constexpr int kIdxLds = 4096;   // gathered indices staged per block
 
 template <int D>
 struct MfmaCfg {
-  static constexpr int KS = D / 32;           // k-steps of S (32 dims each)
-  static constexpr int DB = D / 16;           // 16-dim blocks of O
-  static constexpr int PITCH = D + 8;         // bf16 elements per LDS row
-  static constexpr int VPR = D / 8;           // 16-byte vectors per row
+  static constexpr int KS = D / 32;                // k-steps of S (32 dims each)
+  static constexpr int DB = D / 16;                // 16-dim blocks of O
+  static constexpr int PITCH = D + 8;              // bf16 elements per LDS row
+  static constexpr int VPR = D / 8;                // 16-byte vectors per row
   static constexpr int LOADS = kTile * VPR / 256;  // per thread per tile
+  static constexpr int KB = KS < 4 ? KS : 4;       // k-steps per operand batch
+  static constexpr int OB = DB < 4 ? DB : 4;       // dim blocks per operand batch
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_mfma(AttnParams a) {
-  using Cfg = MfmaCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * Cfg::PITCH];
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+
+__device__ __forceinline__ uint4 pack_tr(const s4_t lo, const s4_t hi) {
+  uint4 v;
+  v.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  v.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  v.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  v.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return v;
+}
+
+// Block: 4 waves, 32 query heads of one query row.  Wave w owns heads
+// 16*(w%2) .. +15 and the dim half (w/2) of D: it computes the S^T partial over
+// its half of D, adds its partner's half through LDS (same order in both, so
+// both hold identical logits), runs the online softmax and accumulates O^T
+// for its D/2 dims.  Halving the per-wave query and accumulator state lets
+// two or three independent blocks share a CU, so that the latency-bound
+// phases of one block (staging, exchange, softmax) overlap the matrix-core
+// phases of another.
+constexpr int kAttnThreads = 256;
+constexpr int kAttnHeads = 32;      // query heads per block
+
+template <int D, int SRC>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnParams a) {
+  constexpr int DH = D / 2;                 // dims per wave
+  constexpr int KS = DH / 32;               // k-steps of the S partial
+  constexpr int DB = DH / 16;               // 16-dim blocks of O per wave
+  constexpr int PITCH = D + 8;              // bf16 elements per LDS row
+  constexpr int VPR = D / 8;                // 16-byte vectors per row
+  constexpr int LOADS = (kTile * VPR + kAttnThreads - 1) / kAttnThreads;
+  constexpr bool PARTIAL = kTile * VPR < kAttnThreads;  // some threads stage nothing
+  constexpr int KB = KS < 2 ? KS : 2;       // k-steps per operand batch
+  constexpr int OB = DB < 4 ? DB : 4;       // dim blocks per operand batch
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * PITCH];
+  __shared__ int32_t sidx[SRC == SRC_GATHER ? kIdxLds : 1];
+  __shared__ float sx[4][8][64];            // S partial exchange
+  __shared__ float qss[4][16];              // query sum-of-squares exchange
+  __shared__ uint32_t tile_valid;
   const int r = blockIdx.z;
   const int split = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int h0 = blockIdx.y * 64 + wave * 16;
-  const bool wave_on = h0 < a.H;  // H is a multiple of 16
+  const int hq = wave & 1, dh = wave >> 1;
+  const int h0 = blockIdx.y * kAttnHeads + hq * 16;
+  const bool wave_on = h0 < a.H;  // H is a multiple of 16; uniform per wave pair
   const int h = h0 + c16;
+  const int d0 = dh * DH;         // first dim of this wave
 
   int64_t first, nseq;
   const int64_t n = attn_keys(a, r, &first, &nseq);
@@ -106,107 +149,195 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnParams a) {
   const int64_t tps = (ntiles + a.n_split - 1) / a.n_split;
   const int64_t tb = (int64_t)split * tps;
   const int64_t te = min(ntiles, tb + tps);
+  const int64_t kbase = tb * kTile;
 
-  // --- normalised query heads in registers (B operand of S^T)
-  bf16x8_t qb[Cfg::KS];
-  if (wave_on) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h) * D;
-    uint4 raw[Cfg::KS];
+  if (SRC == SRC_GATHER) {
+    const int64_t cnt = min((te - tb) * kTile, n - kbase);
+    for (int i = threadIdx.x; i < cnt; i += kAttnThreads) {
+      const int32_t j = a.idx[(int64_t)r * a.k + kbase + i];
+      sidx[i] = (j < 0 || j >= nseq) ? -1 : j;
+    }
+  }
+
+
+  // --- tile staging: loads are unconditional (invalid keys read a clamped
+  // valid row) and masked when stored
+  uint4 stage[LOADS];
+  uint32_t okbits = 0;
+  const uint16_t* kvp = reinterpret_cast<const uint16_t*>(a.kv);
+  auto load_tile = [&](int64_t t) {
+    okbits = 0;
+#pragma unroll
+    for (int v = 0; v < LOADS; ++v) {
+      const int id = threadIdx.x + kAttnThreads * v;
+      const int row = id / VPR, vec = id % VPR;
+      if (PARTIAL && row >= kTile) break;
+      const int64_t key = t * kTile + row;
+      bool ok = key < n;
+      int64_t off;
+      if (SRC == SRC_GATHER) {
+        const int32_t j = ok ? sidx[key - kbase] : -1;
+        ok = j >= 0;
+        off = ok ? j : 0;
+      } else {
+        off = ok ? key : 0;
+      }
+      okbits |= (ok ? 1u : 0u) << v;
+      stage[v] = *reinterpret_cast<const uint4*>(kvp + (first + off) * D + vec * 8);
+    }
+  };
+  auto store_tile = [&]() {
+    uint32_t mask = 0;
+#pragma unroll
+    for (int v = 0; v < LOADS; ++v) {
+      const int id = threadIdx.x + kAttnThreads * v;
+      const int row = id / VPR, vec = id % VPR;
+      if (PARTIAL && row >= kTile) break;
+      const bool ok = (okbits >> v) & 1u;
+      *reinterpret_cast<uint4*>(&tile[row * PITCH + vec * 8]) = ok ? stage[v] : make_uint4(0, 0, 0, 0);
+      if (vec == 0 && ok) mask |= 1u << row;
+    }
+    if (threadIdx.x == 0) tile_valid = 0;
+    __syncthreads();
+    if (mask) atomicOr(&tile_valid, mask);
+    if (SRC == SRC_WINDOW) {
+      // RMS-normalise each row over D in place: TPR threads per row
+      __syncthreads();
+      constexpr int TPR = VPR < 16 ? VPR : 16;
+      constexpr int PER = D / TPR;                     // elements per thread, a multiple of 8
+      constexpr int RPP = kAttnThreads / TPR;          // rows per pass
+      const int part = threadIdx.x % TPR;
+#pragma unroll
+      for (int row0 = 0; row0 < kTile; row0 += RPP) {
+        const int row = row0 + threadIdx.x / TPR;
+        uint4* rp = reinterpret_cast<uint4*>(&tile[(row < kTile ? row : 0) * PITCH + part * PER]);
+        uint4 vals[PER / 8];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER / 8; ++i) {
+          vals[i] = rp[i];
+          float f[8];
+          BF16::unpack(vals[i], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+        }
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+        if (row < kTile) {
+#pragma unroll
+          for (int i = 0; i < PER / 8; ++i) {
+            float f[8];
+            BF16::unpack(vals[i], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] *= inv;
+            rp[i] = BF16::pack(f);
+          }
+        }
+      }
+    }
+  };
+
+  // dense and window keys do not depend on staged indices: request the first
+  // tile before the query loads
+  if (SRC != SRC_GATHER && tb < te && nseq > 0) load_tile(tb);
+
+  // --- normalised query: this wave's heads, its half of D (B operand of S^T)
+  bf16x8_t qb[KS];
+  uint4 qraw[KS];
+  {
     float ss = 0.f;
+    if (wave_on) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h) * D + d0;
 #pragma unroll
-    for (int ks = 0; ks < Cfg::KS; ++ks) {
-      raw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32 + g * 8);
-      float f[8];
-      BF16::unpack(raw[ks], f);
+      for (int ks = 0; ks < KS; ++ks) {
+        qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32 + g * 8);
+        float f[8];
+        BF16::unpack(qraw[ks], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+        for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+      }
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
+    if (g == 0) qss[wave][c16] = ss;
+  }
+  __syncthreads();  // sidx and qss ready
+  if (wave_on) {
+    const float ss = qss[hq][c16] + qss[hq + 2][c16];
     const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-    for (int ks = 0; ks < Cfg::KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       float f[8];
-      BF16::unpack(raw[ks], f);
+      BF16::unpack(qraw[ks], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= inv;
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
 
-  f32x4 O[Cfg::DB];
+  f32x4 O[DB];
 #pragma unroll
-  for (int d = 0; d < Cfg::DB; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < DB; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
-
-  // --- tile staging: thread -> (row, 16-byte vector) pairs
-  uint4 stage[Cfg::LOADS];
-  auto load_tile = [&](int64_t t) {
-#pragma unroll
-    for (int v = 0; v < Cfg::LOADS; ++v) {
-      const int id = threadIdx.x + 256 * v;
-      const int row = id / Cfg::VPR, vec = id % Cfg::VPR;
-      const int64_t key = t * kTile + row;
-      int64_t grow = -1;
-      if (key < n) grow = attn_row(a, r, first, nseq, key);
-      stage[v] = grow >= 0 ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.kv) + grow * D + vec * 8)
-                           : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&]() {
-    if (a.src == SRC_WINDOW) {
-      // RMS-normalise every row over D; a row spans VPR consecutive lanes
-#pragma unroll
-      for (int v = 0; v < Cfg::LOADS; ++v) {
-        float f[8];
-        BF16::unpack(stage[v], f);
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-        ss = wave_sum(ss, Cfg::VPR < 64 ? Cfg::VPR : 64);
-        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] *= inv;
-        stage[v] = BF16::pack(f);
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < Cfg::LOADS; ++v) {
-      const int id = threadIdx.x + 256 * v;
-      const int row = id / Cfg::VPR, vec = id % Cfg::VPR;
-      *reinterpret_cast<uint4*>(&tile[row * Cfg::PITCH + vec * 8]) = stage[v];
-    }
-  };
-
-  if (tb < te) load_tile(tb);
-  for (int64_t t = tb; t < te; ++t) {
+  if (SRC == SRC_GATHER && tb < te && nseq > 0) load_tile(tb);
+  for (int64_t t = tb; t < te && nseq > 0; ++t) {
     store_tile();
     __syncthreads();
     if (t + 1 < te) load_tile(t + 1);
+    // ---- S^T partial over this wave's dims, entries 0-15 (s0) and 16-31 (s1)
+    f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
     if (wave_on) {
-      // S^T for entries 0-15 and 16-31 of the tile
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow0 = &tile[c16 * PITCH + d0 + g * 8];
+      const uint16_t* krow1 = krow0 + 16 * PITCH;
+      uint4 kbuf[2][KB][2];
 #pragma unroll
-      for (int ks = 0; ks < Cfg::KS; ++ks) {
-        const uint4 k0 = *reinterpret_cast<const uint4*>(&tile[c16 * Cfg::PITCH + ks * 32 + g * 8]);
-        const uint4 k1 = *reinterpret_cast<const uint4*>(&tile[(16 + c16) * Cfg::PITCH + ks * 32 + g * 8]);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qb[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qb[ks], s1, 0, 0, 0);
+      for (int j = 0; j < KB; ++j) {
+        kbuf[0][j][0] = *reinterpret_cast<const uint4*>(krow0 + j * 32);
+        kbuf[0][j][1] = *reinterpret_cast<const uint4*>(krow1 + j * 32);
       }
-      // lane (c16 = head, g): s0[i] -> entry 4g+i, s1[i] -> entry 16+4g+i
+#pragma unroll
+      for (int bi = 0; bi < KS / KB; ++bi) {
+        const int cur = bi & 1;
+        if (bi + 1 < KS / KB) {
+#pragma unroll
+          for (int j = 0; j < KB; ++j) {
+            kbuf[cur ^ 1][j][0] = *reinterpret_cast<const uint4*>(krow0 + ((bi + 1) * KB + j) * 32);
+            kbuf[cur ^ 1][j][1] = *reinterpret_cast<const uint4*>(krow1 + ((bi + 1) * KB + j) * 32);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          const int ks = bi * KB + j;
+          if (j & 1) {
+            s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kbuf[cur][j][0]), qb[ks], s0b, 0, 0, 0);
+            s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kbuf[cur][j][1]), qb[ks], s1b, 0, 0, 0);
+          } else {
+            s0a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kbuf[cur][j][0]), qb[ks], s0a, 0, 0, 0);
+            s1a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kbuf[cur][j][1]), qb[ks], s1a, 0, 0, 0);
+          }
+        }
+      }
+    }
+    const f32x4 p0 = s0a + s0b, p1 = s1a + s1b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sx[wave][i][lane] = p0[i];
+      sx[wave][4 + i][lane] = p1[i];
+    }
+    __syncthreads();
+    if (wave_on) {
+      const int wlo = hq;       // dims [0, D/2)
+      const int whi = hq + 2;   // dims [D/2, D)
       float lg[8];
-      const int64_t kb = t * kTile;
+      const uint32_t vm = tile_valid;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t e0 = kb + 4 * g + i, e1 = kb + 16 + 4 * g + i;
-        bool v0 = e0 < n, v1 = e1 < n;
-        if (a.src == SRC_GATHER) {
-          v0 = v0 && attn_row(a, r, first, nseq, e0) >= 0;
-          v1 = v1 && attn_row(a, r, first, nseq, e1) >= 0;
-        }
-        lg[i] = v0 ? s0[i] * sl2 : -INFINITY;
-        lg[4 + i] = v1 ? s1[i] * sl2 : -INFINITY;
+        const float s0 = sx[wlo][i][lane] + sx[whi][i][lane];
+        const float s1 = sx[wlo][4 + i][lane] + sx[whi][4 + i][lane];
+        lg[i] = ((vm >> (4 * g + i)) & 1u) ? s0 * sl2 : -INFINITY;
+        lg[4 + i] = ((vm >> (16 + 4 * g + i)) & 1u) ? s1 * sl2 : -INFINITY;
       }
       float tmax = lg[0];
 #pragma unroll
@@ -214,7 +345,7 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnParams a) {
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float m_new = fmaxf(m_run, tmax);
-      if (m_new != -INFINITY) {
+      if (m_new != -INFINITY) {  // uniform: masks do not depend on the head
         const float alpha = exp2f(m_run - m_new);
         float p[8], psum = 0.f;
 #pragma unroll
@@ -224,25 +355,44 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnParams a) {
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) O[db] = O[db] * alpha;
+        }
         uint4 pb;
         pb.x = pack_bf16x2(p[0], p[1]);
         pb.y = pack_bf16x2(p[2], p[3]);
         pb.z = pack_bf16x2(p[4], p[5]);
         pb.w = pack_bf16x2(p[6], p[7]);
         const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, pb);
-        // V^T operand rows for this lane group: entries 4g..4g+3, 16+4g..16+4g+3
-        const uint16_t* r0 = &tile[(4 * g) * Cfg::PITCH];
-        const uint16_t* r1 = &tile[(16 + 4 * g) * Cfg::PITCH];
+        // ---- O^T += V^T . P^T over this wave's dims; the V^T operand of lane
+        // c16 in group g holds entries 4g..4g+3 and 16+4g..16+4g+3 at dim
+        // d0 + 16*db + c16: it addresses row 4g + c16/4 (and 16 + ...) at
+        // columns d0 + 16*db + 4*(c16%4); the transpose read returns its column.
+        const uint16_t* trow0 = &tile[(4 * g + (c16 >> 2)) * PITCH + d0 + 4 * (c16 & 3)];
+        const uint16_t* trow1 = trow0 + 16 * PITCH;
+        s4_t vbuf[2][OB][2];
 #pragma unroll
-        for (int db = 0; db < Cfg::DB; ++db) {
-          const int col = db * 16 + c16;
-          uint4 vv;
-          vv.x = (uint32_t)r0[col] | ((uint32_t)r0[Cfg::PITCH + col] << 16);
-          vv.y = (uint32_t)r0[2 * Cfg::PITCH + col] | ((uint32_t)r0[3 * Cfg::PITCH + col] << 16);
-          vv.z = (uint32_t)r1[col] | ((uint32_t)r1[Cfg::PITCH + col] << 16);
-          vv.w = (uint32_t)r1[2 * Cfg::PITCH + col] | ((uint32_t)r1[3 * Cfg::PITCH + col] << 16);
-          O[db] = O[db] * alpha;
-          O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pt, O[db], 0, 0, 0);
+        for (int j = 0; j < OB; ++j) {
+          vbuf[0][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow0 + j * 16));
+          vbuf[0][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow1 + j * 16));
+        }
+#pragma unroll
+        for (int bi = 0; bi < DB / OB; ++bi) {
+          const int cur = bi & 1;
+          if (bi + 1 < DB / OB) {
+#pragma unroll
+            for (int j = 0; j < OB; ++j) {
+              vbuf[cur ^ 1][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow0 + ((bi + 1) * OB + j) * 16));
+              vbuf[cur ^ 1][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow1 + ((bi + 1) * OB + j) * 16));
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < OB; ++j) {
+            const int db = bi * OB + j;
+            O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, pack_tr(vbuf[cur][j][0], vbuf[cur][j][1])), pt, O[db], 0, 0, 0);
+          }
         }
       }
     }
@@ -253,14 +403,14 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnParams a) {
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  float* op = a.o_part + (((int64_t)split * a.rows + r) * a.H + h) * D;
-  // lane (head c16, g) holds dims 16*db + 4g .. +3
+  float* op = a.o_part + (((int64_t)split * a.rows + r) * a.H + h) * D + d0;
+  // lane (head c16, g) holds dims d0 + 16*db + 4g .. +3
 #pragma unroll
-  for (int db = 0; db < Cfg::DB; ++db) {
+  for (int db = 0; db < DB; ++db) {
     float4 v = make_float4(O[db][0] * inv, O[db][1] * inv, O[db][2] * inv, O[db][3] * inv);
     *reinterpret_cast<float4*>(op + db * 16 + 4 * g) = v;
   }
-  if (g == 0) {
+  if (g == 0 && dh == 0) {
     const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     a.lse[((int64_t)split * a.rows + r) * a.H + h] = lse;
   }
@@ -335,71 +485,97 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
 
 // ============================================================ merge
 // out[r, h, :] = sum_s exp(lse_s - lse) * o_s,  lse = log(sum_s exp(lse_s) + exp(sink_h)).
-// One wavefront per (row, head); a lane owns D/64 dims.
+// A block owns HPB (row, head) pairs; D/4 threads per pair, 4 dims each.  The
+// slot weights of a pair are computed once into LDS.
 constexpr int kMaxParts = 8;
+constexpr int kMaxSlots = 512;
 struct MergeParams {
   const float* o[kMaxParts];
   const float* lse[kMaxParts];
   int n_split[kMaxParts];
   int n_parts;
+  int n_slots;
   const float* sink;
   int rows, H, D;
   void* out;
 };
 
-template <typename ET, int DPL>
+template <typename ET>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t rh = (int64_t)blockIdx.x * 4 + wave;
-  if (rh >= (int64_t)a.rows * a.H) return;
-  const int h = (int)(rh % a.H);
-  float mx = a.sink ? a.sink[h] : -INFINITY;
-  for (int p = 0; p < a.n_parts; ++p)
-    for (int s = 0; s < a.n_split[p]; ++s) mx = fmaxf(mx, a.lse[p][(int64_t)s * a.rows * a.H + rh]);
-  float den = 0.f;
-  if (mx != -INFINITY) {
-    if (a.sink) den = expf(a.sink[h] - mx);
-    for (int p = 0; p < a.n_parts; ++p)
-      for (int s = 0; s < a.n_split[p]; ++s) {
-        const float l = a.lse[p][(int64_t)s * a.rows * a.H + rh];
-        if (l != -INFINITY) den += expf(l - mx);
+  __shared__ float wts[16][kMaxSlots];
+  __shared__ const float* sl[kMaxSlots];   // lse of slot
+  __shared__ const float* so[kMaxSlots];   // o of slot
+  const int TPH = a.D / 4;                 // threads per (row, head)
+  const int HPB = 256 / TPH;
+  const int RL = TPH < 64 ? TPH : 64;      // reducer lanes per pair
+  const int hl = threadIdx.x / TPH, t = threadIdx.x % TPH;
+  const int64_t RH = (int64_t)a.rows * a.H;
+  const int64_t rh = (int64_t)blockIdx.x * HPB + hl;
+  for (int sidx = threadIdx.x; sidx < a.n_slots; sidx += blockDim.x) {
+    int p = 0, s = sidx;
+    while (s >= a.n_split[p]) { s -= a.n_split[p]; ++p; }
+    sl[sidx] = a.lse[p] + (int64_t)s * RH;
+    so[sidx] = a.o[p] + (int64_t)s * RH * a.D;
+  }
+  __syncthreads();
+  const bool on = rh < RH;
+  // weights exp(lse_s - lse) of every slot, by the first RL lanes of the pair
+  if (t < RL) {
+    float mx = -INFINITY;
+    const int h = (int)((on ? rh : 0) % a.H);
+    if (on)
+      for (int sidx = t; sidx < a.n_slots; sidx += RL) {
+        const float l = sl[sidx][rh];
+        wts[hl][sidx] = l;
+        mx = fmaxf(mx, l);
+      }
+    mx = wave_max(mx, RL);
+    if (on && a.sink) mx = fmaxf(mx, a.sink[h]);
+    float den = 0.f;
+    if (on && mx != -INFINITY)
+      for (int sidx = t; sidx < a.n_slots; sidx += RL) {
+        const float l = wts[hl][sidx];
+        den += l == -INFINITY ? 0.f : expf(l - mx);
+      }
+    den = wave_sum(den, RL);
+    if (on && a.sink && mx != -INFINITY) den += expf(a.sink[h] - mx);
+    const float lse = mx != -INFINITY ? mx + logf(den) : -INFINITY;
+    if (on)
+      for (int sidx = t; sidx < a.n_slots; sidx += RL) {
+        const float l = wts[hl][sidx];
+        wts[hl][sidx] = (l != -INFINITY && lse != -INFINITY) ? expf(l - lse) : 0.f;
       }
   }
-  const float lse = mx != -INFINITY ? mx + logf(den) : -INFINITY;
-  float acc[DPL];
+  __syncthreads();
+  if (!on) return;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int64_t off = rh * a.D + 4 * t;
+  constexpr int U = 8;
+  int sidx = 0;
+  for (; sidx + U <= a.n_slots; sidx += U) {
+    float4 v[U];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  if (lse != -INFINITY) {
-    for (int p = 0; p < a.n_parts; ++p)
-      for (int s = 0; s < a.n_split[p]; ++s) {
-        const int64_t base = (int64_t)s * a.rows * a.H + rh;
-        const float l = a.lse[p][base];
-        if (l == -INFINITY) continue;
-        const float wgt = expf(l - lse);
-        const float* op = a.o[p] + base * a.D + lane * DPL;
-        if constexpr (DPL % 4 == 0) {
+    for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float4*>(so[sidx + u] + off);
 #pragma unroll
-          for (int i = 0; i < DPL; i += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(op + i);
-            acc[i] = fmaf(wgt, v.x, acc[i]); acc[i + 1] = fmaf(wgt, v.y, acc[i + 1]);
-            acc[i + 2] = fmaf(wgt, v.z, acc[i + 2]); acc[i + 3] = fmaf(wgt, v.w, acc[i + 3]);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wgt, op[i], acc[i]);
-        }
-      }
-  }
-  if constexpr (ET::kBytes == 2 && DPL == 8) {
-    stg16(a.out, (rh * a.D + lane * 8) * 2, BF16::pack(acc));
-  } else {
-    for (int i = 0; i < DPL; ++i) {
-      const int64_t o = rh * a.D + lane * DPL + i;
-      if (ET::kBytes == 2)
-        reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(acc[i]);
-      else
-        reinterpret_cast<float*>(a.out)[o] = acc[i];
+    for (int u = 0; u < U; ++u) {
+      const float wgt = wts[hl][sidx + u];
+      acc[0] = fmaf(wgt, v[u].x, acc[0]); acc[1] = fmaf(wgt, v[u].y, acc[1]);
+      acc[2] = fmaf(wgt, v[u].z, acc[2]); acc[3] = fmaf(wgt, v[u].w, acc[3]);
     }
+  }
+  for (; sidx < a.n_slots; ++sidx) {
+    const float4 v = *reinterpret_cast<const float4*>(so[sidx] + off);
+    const float wgt = wts[hl][sidx];
+    acc[0] = fmaf(wgt, v.x, acc[0]); acc[1] = fmaf(wgt, v.y, acc[1]);
+    acc[2] = fmaf(wgt, v.z, acc[2]); acc[3] = fmaf(wgt, v.w, acc[3]);
+  }
+  if constexpr (ET::kBytes == 2) {
+    uint2 v;
+    v.x = pack_bf16x2(acc[0], acc[1]);
+    v.y = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = v;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
 }
 
@@ -416,14 +592,25 @@ int launch_attention(int src, const void* q, const void* kv, const int64_t* off,
   a.o_part = o_part; a.lse = lse;
   const int rows = B * Tq;
   if (dtype == LCA_BF16 && H % 16 == 0) {
-    dim3 grid((unsigned)n_split, (unsigned)((H + 63) / 64), (unsigned)rows);
+    if (src == SRC_GATHER && (int64_t)((k + kTile - 1) / kTile + n_split - 1) / n_split * kTile > kIdxLds) {
+      set_error("attention: n_split=%d leaves more than %d gathered slots per block (k=%d)", n_split, kIdxLds, k);
+      return LCA_ERR_UNSUPPORTED;
+    }
+    dim3 grid((unsigned)n_split, (unsigned)((H + kAttnHeads - 1) / kAttnHeads), (unsigned)rows);
+#define LCA_ATTN(DD)                                                                                             \
+  switch (src) {                                                                                                 \
+    case SRC_DENSE: hipLaunchKernelGGL((attn_mfma<DD, SRC_DENSE>), grid, dim3(kAttnThreads), 0, stream, a); break;       \
+    case SRC_GATHER: hipLaunchKernelGGL((attn_mfma<DD, SRC_GATHER>), grid, dim3(kAttnThreads), 0, stream, a); break;     \
+    default: hipLaunchKernelGGL((attn_mfma<DD, SRC_WINDOW>), grid, dim3(kAttnThreads), 0, stream, a); break;             \
+  }
     switch (D) {
-      case 64: hipLaunchKernelGGL((attn_mfma<64>), grid, dim3(256), 0, stream, a); break;
-      case 128: hipLaunchKernelGGL((attn_mfma<128>), grid, dim3(256), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL((attn_mfma<256>), grid, dim3(256), 0, stream, a); break;
-      case 512: hipLaunchKernelGGL((attn_mfma<512>), grid, dim3(256), 0, stream, a); break;
+      case 64: LCA_ATTN(64) break;
+      case 128: LCA_ATTN(128) break;
+      case 256: LCA_ATTN(256) break;
+      case 512: LCA_ATTN(512) break;
       default: set_error("attention: D=%d not supported", D); return LCA_ERR_UNSUPPORTED;
     }
+#undef LCA_ATTN
   } else {
     dim3 grid((unsigned)n_split, (unsigned)H, (unsigned)rows);
 #define LCA_VALU(ETy)                                                                      \
@@ -443,25 +630,25 @@ int launch_attention(int src, const void* q, const void* kv, const int64_t* off,
 int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, const float* win_lse,
                  const float* sink, int rows, int H, int D, void* out, int dtype, hipStream_t stream) {
   MergeParams a{};
-  int np = 0;
+  int np = 0, ns = 0;
   for (int p = 0; p < n_parts; ++p) {
-    a.o[np] = parts[p].o; a.lse[np] = parts[p].lse; a.n_split[np] = parts[p].n_split; ++np;
+    a.o[np] = parts[p].o; a.lse[np] = parts[p].lse; a.n_split[np] = parts[p].n_split; ns += parts[p].n_split; ++np;
   }
-  if (win_o) { a.o[np] = win_o; a.lse[np] = win_lse; a.n_split[np] = 1; ++np; }
+  if (win_o) { a.o[np] = win_o; a.lse[np] = win_lse; a.n_split[np] = 1; ns += 1; ++np; }
+  if (ns > kMaxSlots) {
+    set_error("merge: %d partial slots, at most %d", ns, kMaxSlots);
+    return LCA_ERR_UNSUPPORTED;
+  }
   a.n_parts = np;
+  a.n_slots = ns;
   a.sink = sink; a.rows = rows; a.H = H; a.D = D; a.out = out;
-  const int64_t waves = (int64_t)rows * H;
-  dim3 grid((unsigned)((waves + 3) / 4));
-#define LCA_MERGE(ETy)                                                                           \
-  switch (D) {                                                                                   \
-    case 64: hipLaunchKernelGGL((merge_kernel<ETy, 1>), grid, dim3(256), 0, stream, a); break;  \
-    case 128: hipLaunchKernelGGL((merge_kernel<ETy, 2>), grid, dim3(256), 0, stream, a); break; \
-    case 256: hipLaunchKernelGGL((merge_kernel<ETy, 4>), grid, dim3(256), 0, stream, a); break; \
-    case 512: hipLaunchKernelGGL((merge_kernel<ETy, 8>), grid, dim3(256), 0, stream, a); break; \
-    default: set_error("merge: D=%d not supported", D); return LCA_ERR_UNSUPPORTED;            \
-  }
-  if (dtype == LCA_BF16) { LCA_MERGE(BF16) } else { LCA_MERGE(F32) }
-#undef LCA_MERGE
+  const int HPB = 256 / (D / 4);
+  const int64_t pairs = (int64_t)rows * H;
+  dim3 grid((unsigned)((pairs + HPB - 1) / HPB));
+  if (dtype == LCA_BF16)
+    hipLaunchKernelGGL((merge_kernel<BF16>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<F32>), grid, dim3(256), 0, stream, a);
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 

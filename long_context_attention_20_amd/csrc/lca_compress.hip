@@ -26,7 +26,7 @@
 
 namespace lca {
 
-constexpr int kCompressThreads = 256;
+constexpr int kCompressThreads = 512;
 constexpr int kRunEntries = 16;  // entries per row group in small-window mode
 
 struct CompressStreamDev {
@@ -262,22 +262,43 @@ __device__ void compress_large(const CompressStreamDev& s, const CompressParams&
       lds[(rg * 3 + 2) * C + c] = st[v].sn[e];
     }
   __syncthreads();
+  // combine the row groups' states, one channel per thread; pooled value -> LDS
+  float* pooled = lds + RG * 3 * C;
+  for (int c = threadIdx.x; c < C; c += kCompressThreads) {
+    float M = -INFINITY;
+    for (int r = 0; r < RG; ++r) M = fmaxf(M, lds[(r * 3 + 0) * C + c]);
+    float se = 0.f, sn = 0.f;
+    for (int r = 0; r < RG; ++r) {
+      const float m = lds[(r * 3 + 0) * C + c];
+      const float f = m == -INFINITY ? 0.f : __expf(m - M);
+      se = fmaf(lds[(r * 3 + 1) * C + c], f, se);
+      sn = fmaf(lds[(r * 3 + 2) * C + c], f, sn);
+    }
+    pooled[c] = sn / se;
+  }
+  __syncthreads();
   if (rg != 0) return;
-  for (int r = 1; r < RG; ++r) {
-    PoolState<VE> o[NV];
+  float e[NV][VE];
+  float ss = 0.f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int k = 0; k < VE; ++k) {
+      e[v][k] = pooled[rc.ch0[v] + k];
+      ss = fmaf(e[v][k], e[v][k], ss);
+    }
+  if (s.rmsnorm) {
+    ss = wave_sum(ss, G);
+    const float inv = 1.0f / sqrtf(ss / (float)C + P.eps);
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const int c = rc.ch0[v] + e;
-        o[v].mx[e] = lds[(r * 3 + 0) * C + c];
-        o[v].se[e] = lds[(r * 3 + 1) * C + c];
-        o[v].sn[e] = lds[(r * 3 + 2) * C + c];
-      }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) st[v].merge(o[v]);
+      for (int k = 0; k < VE; ++k) e[v][k] *= inv;
   }
-  finish_entry<ET, NV>(s, P.eps, G, st, rc.ch0, s.ent_off[b] + j, true);
+  const int64_t rb = (int64_t)C * ET::kBytes;
+  const int64_t out_row = s.ent_off[b] + j;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) stg16(s.out, out_row * rb + (int64_t)rc.ch0[v] * ET::kBytes, ET::pack(e[v]));
 }
 
 template <typename ET, int NV>
@@ -333,7 +354,7 @@ int launch_compress(const lca_compress_stream* streams, int n, const int64_t* to
     d.block_begin = (int)blocks;
     blocks += (int64_t)d.bps * B;
     if (!d.small) {
-      size_t need = (size_t)RG * 3 * in.C * sizeof(float);
+      size_t need = ((size_t)RG * 3 + 1) * in.C * sizeof(float);
       if (need > lds_bytes) lds_bytes = need;
     }
   }

@@ -16,13 +16,17 @@
 // 2048-bin histogram of the top 11 bits of an order-preserving integer key of
 // every score (LDS, then one global atomic per non-empty bin).
 //
-// Kernel 2 (select): every block derives the threshold bin T from the
-// histogram (the highest bin whose suffix count reaches k), keeps the entries
-// of its chunk above T and the candidates inside T, each in index order, in a
-// private workspace region.  The last block of a row (atomic ticket) gathers
-// them, radix-selects the missing candidates exactly on (low 21 key bits,
-// inverted index) -- a total order, so ties go to the smaller index -- writes
-// the row and zeroes the histogram and ticket for the next call.
+// Kernel 2 (filter): every block derives the threshold bin T from the
+// histogram (the highest bin whose suffix count reaches k), and appends the
+// entries of its chunk above T to a per-row "selected" list and those inside T
+// (the candidates) to a per-row candidate list, reserving space with one
+// 64-bit atomic per block.  No block waits for another.
+//
+// Kernel 3 (finalize, one block per row): radix-selects the missing
+// candidates exactly on (low 21 key bits, inverted index) -- a total order,
+// so ties go to the smaller index -- marks every chosen entry in an LDS
+// bitmap and writes the row in ascending index order (deterministic whatever
+// order the lists were filled in), then zeroes the histogram and counters.
 #include "lca_common.h"
 
 namespace lca {
@@ -41,21 +45,14 @@ struct IndexParams {
   const int32_t* q_pos;
   int Tq, HI, dI, k, m, w;
   int64_t max_entries;
-  int chunk;           // entries per score block
-  float* scores;       // [rows][max_entries]
-  uint32_t* hist;      // [rows][kHistBins]
-  // select
-  uint32_t* ticket;    // [rows]
-  uint32_t* nsel;      // [rows][nblk]
-  uint32_t* ncand;     // [rows][nblk]
-  int32_t* sel;        // [rows][nblk][selcap]
-  uint64_t* cand;      // [rows][nblk][kSelChunk]
-  uint64_t* cand_all;  // [rows][max_entries]
-  int nblk;
-  int selcap;
-  int32_t* idx;        // [rows][k]
+  int chunk;                // entries per score block
+  float* scores;            // [rows][max_entries]
+  uint32_t* hist;           // [rows][kHistBins]
+  unsigned long long* ctr;  // [rows]: selected count | candidate count << 32
+  int32_t* sel;             // [rows][k]
+  uint64_t* cand;           // [rows][max_entries]
+  int32_t* idx;             // [rows][k]
 };
-
 __device__ __forceinline__ int64_t row_visible(const IndexParams& a, int r, int64_t n_seq) {
   const int i = a.q_pos[r];
   int64_t nv = n_windows((int64_t)i + 1, a.m, a.w);
@@ -115,7 +112,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
 
   const uint16_t* K = reinterpret_cast<const uint16_t*>(a.ikey) + e_base * a.dI;
   float* S = a.scores + (int64_t)r * a.max_entries;
-  constexpr int U = 4;  // tiles in flight per wave
+  constexpr int U = 8;  // tiles in flight per wave
   const int64_t ntile = (c1 - c0 + 15) / 16;
   for (int64_t t0 = wave * U; t0 < ntile; t0 += 4 * U) {
     uint4 kv[U][KS];
@@ -188,7 +185,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
 
 // ------------------------------------------------------------------ select
 
-// Exclusive prefix sum over the block (256 threads); returns the total in *tot.
+// Exclusive prefix sum over the block; returns the total in *tot.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tot, uint32_t* sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -209,34 +206,29 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tot, u
   return before + x - v;
 }
 
-// Highest bin T with suffix count >= need over a histogram in LDS; returns T
-// and the count strictly above T.
-__device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint32_t* sm, int* T_out,
-                               uint32_t* above_out) {
-  const int per = nbins / kSelThreads;
-  // thread t owns bins [t*per, (t+1)*per); suffix order = descending bins
+// Highest bin T with suffix count >= need over a histogram in LDS (nbins a
+// multiple of blockDim.x); writes T and the count strictly above T.
+__device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint32_t* sm, uint32_t* rev,
+                               int* T_out, uint32_t* above_out) {
+  const int nt = blockDim.x;
+  const int per = nbins / nt;
   const int t = threadIdx.x;
   uint32_t mine = 0;
   for (int i = 0; i < per; ++i) mine += h[t * per + i];
-  // exclusive scan in reversed thread order
-  const int rt = kSelThreads - 1 - t;
-  // do a scan where the "earlier" threads are those with higher bins
-  uint32_t tot;
-  // emulate by scanning over reversed index via LDS
-  __shared__ uint32_t rev[kSelThreads];
+  // scan in descending-bin order: thread t' = nt-1-t holds this thread's count
+  const int rt = nt - 1 - t;
   rev[rt] = mine;
   __syncthreads();
-  uint32_t v = rev[t];
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan(rev[t], &tot, sm);  // bins above thread rt's range
   __syncthreads();
-  uint32_t ex = block_excl_scan(v, &tot, sm);  // ex = sum of rev[0..t) = bins above thread (kSelThreads-1-t)'s range
   rev[t] = ex;
   __syncthreads();
-  uint32_t above_mine = rev[rt];  // count in bins above my range
-  __syncthreads();
+  const uint32_t above_mine = rev[rt];
   if (above_mine < need && above_mine + mine >= need) {
     uint32_t acc = above_mine;
     for (int i = per - 1; i >= 0; --i) {
-      uint32_t c = h[t * per + i];
+      const uint32_t c = h[t * per + i];
       if (acc + c >= need) {
         *T_out = t * per + i;
         *above_out = acc;
@@ -248,187 +240,218 @@ __device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kSelThreads) void topk_select(IndexParams a) {
-  __shared__ uint32_t sh[4096];
-  __shared__ uint32_t sm[8];
+__global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
+  __shared__ uint32_t sh[kHistBins];
+  __shared__ uint32_t sm[8], rev[kSelThreads];
   __shared__ int s_T;
-  __shared__ uint32_t s_above, s_flag;
+  __shared__ uint32_t s_above;
+  __shared__ unsigned long long s_base;
   const int r = blockIdx.y;
   const int cb = blockIdx.x;
   const int b = r / a.Tq;
   const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - a.csa_off[b]);
-  int32_t* out = a.idx + (int64_t)r * a.k;
-  if (nv <= a.k) {
-    if (cb == 0)
-      for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = t < nv ? t : -1;
-    return;
-  }
-  const int nblk = (int)((nv + kSelChunk - 1) / kSelChunk);
-  if (cb >= nblk) return;
+  if (nv <= a.k) return;  // the finalize kernel takes every visible entry
+  const int64_t c0 = (int64_t)cb * kSelChunk;
+  if (c0 >= nv) return;
 
-  // threshold bin from the histogram
-  const uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sh[i] = gh[i];
+  // histogram and this chunk's scores, all loads in flight together
+  const uint4* gh = reinterpret_cast<const uint4*>(a.hist + (int64_t)r * kHistBins);
+  const float* S = a.scores + (int64_t)r * a.max_entries;
+  constexpr int HV = kHistBins / 4 / kSelThreads;  // uint4 per thread
+  uint4 hv[HV];
+#pragma unroll
+  for (int i = 0; i < HV; ++i) hv[i] = gh[threadIdx.x + i * kSelThreads];
+  const int64_t e0 = c0 + (int64_t)threadIdx.x * kSelPerThread;
+  float sv[kSelPerThread];
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i) {
+    const int64_t e = e0 + i;
+    sv[i] = S[e < nv ? e : nv - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < HV; ++i) reinterpret_cast<uint4*>(sh)[threadIdx.x + i * kSelThreads] = hv[i];
   if (threadIdx.x == 0) { s_T = 0; s_above = 0; }
   __syncthreads();
-  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, &s_T, &s_above);
+  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, rev, &s_T, &s_above);
   const uint32_t T = (uint32_t)s_T;
-  const uint32_t above = s_above;
 
-  // filter this chunk, index order: thread t owns kSelPerThread consecutive entries
-  const float* S = a.scores + (int64_t)r * a.max_entries;
-  const int64_t e0 = (int64_t)cb * kSelChunk + (int64_t)threadIdx.x * kSelPerThread;
   uint32_t keys[kSelPerThread];
   uint32_t ns = 0, nc = 0;
 #pragma unroll
   for (int i = 0; i < kSelPerThread; ++i) {
-    const int64_t e = e0 + i;
-    uint32_t key = 0;
-    if (e < nv) key = score_key(S[e]);
-    keys[i] = key;
-    const uint32_t bin = key >> 21;
-    if (e < nv) {
-      ns += bin > T;
-      nc += bin == T;
-    }
+    const bool in = e0 + i < nv;
+    keys[i] = score_key(sv[i]);
+    const uint32_t bin = keys[i] >> 21;
+    ns += (in && bin > T) ? 1u : 0u;
+    nc += (in && bin == T) ? 1u : 0u;
   }
-  uint32_t tot_s, tot_c;
-  uint32_t ps = block_excl_scan(ns, &tot_s, sm);
-  uint32_t pc = block_excl_scan(nc, &tot_c, sm);
-  int32_t* selr = a.sel + ((int64_t)r * a.nblk + cb) * a.selcap;
-  uint64_t* candr = a.cand + ((int64_t)r * a.nblk + cb) * kSelChunk;
+  uint32_t tot;
+  const uint32_t pos = block_excl_scan(ns | (nc << 16), &tot, sm);  // both counts < 2^16
+  if (threadIdx.x == 0)
+    s_base = atomicAdd(&a.ctr[r], (unsigned long long)(tot & 0xFFFFu) | ((unsigned long long)(tot >> 16) << 32));
+  __syncthreads();
+  uint32_t ps = (uint32_t)(s_base & 0xFFFFFFFFull) + (pos & 0xFFFFu);
+  uint32_t pc = (uint32_t)(s_base >> 32) + (pos >> 16);
+  int32_t* selr = a.sel + (int64_t)r * a.k;
+  uint64_t* candr = a.cand + (int64_t)r * a.max_entries;
 #pragma unroll
   for (int i = 0; i < kSelPerThread; ++i) {
     const int64_t e = e0 + i;
     if (e >= nv) continue;
     const uint32_t bin = keys[i] >> 21;
     if (bin > T) {
-      if (ps < (uint32_t)a.selcap) selr[ps] = (int32_t)e;
+      if (ps < (uint32_t)a.k) selr[ps] = (int32_t)e;
       ++ps;
-    } else if (bin == T)
-      candr[pc++] = ((uint64_t)(keys[i] & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
+    } else if (bin == T) {
+      if (pc < (uint32_t)a.max_entries)
+        candr[pc] = ((uint64_t)(keys[i] & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
+      ++pc;
+    }
   }
-  if (threadIdx.x == 0) {
-    a.nsel[(int64_t)r * a.nblk + cb] = tot_s;
-    a.ncand[(int64_t)r * a.nblk + cb] = tot_c;
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t prev = atomicAdd(&a.ticket[r], 1u);
-    s_flag = (prev == (uint32_t)nblk - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!s_flag) return;
-  __threadfence();
+}
 
-  // ---- last block of the row: gather selected and candidates in index order
-  uint32_t sel_base = 0, cand_base = 0;
-  uint64_t* call = a.cand_all + (int64_t)r * a.max_entries;
-  for (int blk0 = 0; blk0 < nblk; blk0 += kSelThreads) {
-    const int blk = blk0 + threadIdx.x;
-    uint32_t cs = 0, cc = 0;
-    if (blk < nblk) {
-      cs = __atomic_load_n(&a.nsel[(int64_t)r * a.nblk + blk], __ATOMIC_RELAXED);
-      cc = __atomic_load_n(&a.ncand[(int64_t)r * a.nblk + blk], __ATOMIC_RELAXED);
-    }
-    uint32_t ts, tc;
-    uint32_t os = block_excl_scan(cs, &ts, sm) + sel_base;
-    uint32_t oc = block_excl_scan(cc, &tc, sm) + cand_base;
-    if (blk < nblk) {
-      const int32_t* src = a.sel + ((int64_t)r * a.nblk + blk) * a.selcap;
-      for (uint32_t i = 0; i < cs && i < (uint32_t)a.selcap && os + i < (uint32_t)a.k; ++i) out[os + i] = src[i];
-      const uint64_t* srcc = a.cand + ((int64_t)r * a.nblk + blk) * kSelChunk;
-      for (uint32_t i = 0; i < cc; ++i) call[oc + i] = srcc[i];
-    }
-    sel_base += ts;
-    cand_base += tc;
+constexpr int kFinThreads = 1024;
+constexpr int kCandLds = 8192;                   // candidates kept in LDS
+constexpr int kBitmapWords = 8192;               // 262144 entries
+
+__global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
+  __shared__ uint32_t sh[4096];
+  __shared__ uint32_t sm[16], rev[kFinThreads];
+  __shared__ uint64_t lds_cand[kCandLds];
+  __shared__ uint32_t bitmap[kBitmapWords];
+  __shared__ int s_T;
+  __shared__ uint32_t s_above;
+  __shared__ uint32_t s_fill;
+  const int r = blockIdx.x;
+  const int b = r / a.Tq;
+  const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - a.csa_off[b]);
+  int32_t* out = a.idx + (int64_t)r * a.k;
+  if (nv <= a.k) {
+    for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = t < nv ? t : -1;
+    return;
   }
-  __threadfence_block();
+  const unsigned long long cnt = a.ctr[r];
+  const uint32_t n_sel = (uint32_t)(cnt & 0xFFFFFFFFull);
+  const uint32_t ncands = (uint32_t)(cnt >> 32);
+  // the threshold bin of the filter kernel, recomputed from the same histogram
+  const uint32_t* gh = a.hist + (int64_t)r * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sh[i] = gh[i];
+  if (threadIdx.x == 0) { s_T = 0; s_above = 0; }
   __syncthreads();
-  const uint32_t ncands = cand_base;
-  // consistent histogram: above < k <= above + ncands
-  if (above >= (uint32_t)a.k || above + ncands < (uint32_t)a.k) {
+  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, rev, &s_T, &s_above);
+  const uint32_t above = s_above;
+  const bool consistent = n_sel == above && above < (uint32_t)a.k && above + ncands >= (uint32_t)a.k &&
+                          ncands <= (uint32_t)a.max_entries;
+  const bool use_bitmap = nv <= (int64_t)kBitmapWords * 32;
+  if (!consistent) {
     for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = -1;
-    goto cleanup;
-  }
-  {
-  uint32_t need = (uint32_t)a.k - above;
-
-  // radix select of the need-th largest packed value (all distinct)
-  uint64_t prefix = 0, mask = 0;
-  const int shifts[4] = {34, 23, 12, 0};
-  const int widths[4] = {11, 11, 11, 12};
-  for (int pass = 0; pass < 4; ++pass) {
-    const int sft = shifts[pass], nb = 1 << widths[pass];
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) sh[i] = 0;
+  } else {
+    // candidates into LDS when they fit
+    const bool in_lds = ncands <= (uint32_t)kCandLds;
+    const uint64_t* cg = a.cand + (int64_t)r * a.max_entries;
+    if (in_lds)
+      for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) lds_cand[i] = cg[i];
+    const uint64_t* cl = in_lds ? lds_cand : cg;
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) {
-      const uint64_t v = call[i];
-      if ((v & mask) == prefix) atomicAdd(&sh[(uint32_t)(v >> sft) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) { s_T = 0; s_above = 0; }
-    __syncthreads();
-    find_threshold(sh, nb, need, sm, &s_T, &s_above);
-    prefix |= (uint64_t)s_T << sft;
-    mask |= (uint64_t)(nb - 1) << sft;
-    need -= s_above;
-  }
-  const uint64_t vstar = prefix;  // exactly (k - above) candidates are >= vstar
-
-  // write the chosen candidates in list (index) order
-  uint32_t wbase = above;
-  for (uint32_t c0 = 0; c0 < ncands; c0 += kSelThreads * 8) {
-    uint32_t cnt = 0;
-    uint64_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t ci = c0 + threadIdx.x * 8 + i;
-      v[i] = ci < ncands ? call[ci] : 0;
-      cnt += (ci < ncands && v[i] >= vstar);
-    }
-    uint32_t tot;
-    uint32_t o = block_excl_scan(cnt, &tot, sm) + wbase;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t ci = c0 + threadIdx.x * 8 + i;
-      if (ci < ncands && v[i] >= vstar) {
-        if (o < (uint32_t)a.k) out[o] = (int32_t)(0xFFFFFFu - (uint32_t)(v[i] & 0xFFFFFFu));
-        ++o;
+    // radix select of the need-th largest packed value (all distinct)
+    uint32_t need = (uint32_t)a.k - above;
+    uint64_t prefix = 0, mask = 0;
+    const int shifts[4] = {34, 23, 12, 0};
+    const int widths[4] = {11, 11, 11, 12};
+    if (need < ncands) {
+      for (int pass = 0; pass < 4; ++pass) {
+        const int sft = shifts[pass], nb = 1 << widths[pass];
+        for (int i = threadIdx.x; i < nb; i += blockDim.x) sh[i] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) {
+          const uint64_t v = cl[i];
+          if ((v & mask) == prefix) atomicAdd(&sh[(uint32_t)(v >> sft) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) { s_T = 0; s_above = 0; }
+        __syncthreads();
+        find_threshold(sh, nb, need, sm, rev, &s_T, &s_above);
+        prefix |= (uint64_t)s_T << sft;
+        mask |= (uint64_t)(nb - 1) << sft;
+        need -= s_above;
+        // every value left in the chosen bucket is needed: its lower bound
+        // (prefix with zero low bits) is the threshold
+        if (sh[s_T] == need) break;
       }
     }
-    wbase += tot;
+    const uint64_t vstar = prefix;  // need < ncands: exactly (k - above) values >= vstar; else 0 (all)
+    const int32_t* selr = a.sel + (int64_t)r * a.k;
+    if (use_bitmap) {
+      // ascending index order through a bitmap of the chosen entries
+      for (int i = threadIdx.x; i < kBitmapWords; i += blockDim.x) bitmap[i] = 0;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) {
+        const uint32_t e = (uint32_t)selr[i];
+        atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+      }
+      for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) {
+        const uint64_t v = cl[i];
+        if (v >= vstar) {
+          const uint32_t e = 0xFFFFFFu - (uint32_t)(v & 0xFFFFFFu);
+          atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+        }
+      }
+      __syncthreads();
+      constexpr int WPT = kBitmapWords / kFinThreads;  // words per thread
+      uint32_t wv[WPT], c = 0;
+#pragma unroll
+      for (int i = 0; i < WPT; ++i) {
+        wv[i] = bitmap[threadIdx.x * WPT + i];
+        c += __popc(wv[i]);
+      }
+      uint32_t tot;
+      uint32_t o = block_excl_scan(c, &tot, sm);
+#pragma unroll
+      for (int i = 0; i < WPT; ++i) {
+        uint32_t w = wv[i];
+        while (w) {
+          const int bit = __ffs(w) - 1;
+          w &= w - 1;
+          if (o < (uint32_t)a.k) out[o] = (int32_t)((threadIdx.x * WPT + i) * 32 + bit);
+          ++o;
+        }
+      }
+    } else {
+      // large rows: selected entries in list order, then the chosen candidates
+      if (threadIdx.x == 0) s_fill = 0;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) out[i] = selr[i];
+      for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) {
+        const uint64_t v = cl[i];
+        if (v >= vstar) {
+          const uint32_t o = above + atomicAdd(&s_fill, 1u);
+          if (o < (uint32_t)a.k) out[o] = (int32_t)(0xFFFFFFu - (uint32_t)(v & 0xFFFFFFu));
+        }
+      }
+    }
   }
-  }
-cleanup:
   // leave the workspace clean for the next call
   uint32_t* ghw = a.hist + (int64_t)r * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) ghw[i] = 0;
-  if (threadIdx.x == 0) a.ticket[r] = 0;
+  if (threadIdx.x == 0) a.ctr[r] = 0;
 }
 
 // ------------------------------------------------------------------ host
 
 struct IndexWs {
-  size_t scores, hist, ticket, nsel, ncand, sel, cand, cand_all, total;
+  size_t scores, hist, ctr, sel, cand, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static IndexWs index_ws_layout(int rows, int64_t maxN, int k) {
   IndexWs w{};
-  const int64_t nblk = (maxN + kSelChunk - 1) / kSelChunk;
-  const int64_t selcap = k < kSelChunk ? k : kSelChunk;
   size_t o = 0;
   w.hist = o;     o = align256(o + (size_t)rows * kHistBins * 4);
-  w.ticket = o;   o = align256(o + (size_t)rows * 4);
+  w.ctr = o;      o = align256(o + (size_t)rows * 8);
   w.scores = o;   o = align256(o + (size_t)rows * maxN * 4);
-  w.nsel = o;     o = align256(o + (size_t)rows * nblk * 4);
-  w.ncand = o;    o = align256(o + (size_t)rows * nblk * 4);
-  w.sel = o;      o = align256(o + (size_t)rows * nblk * selcap * 4);
-  w.cand = o;     o = align256(o + (size_t)rows * nblk * kSelChunk * 8);
-  w.cand_all = o; o = align256(o + (size_t)rows * maxN * 8);
+  w.sel = o;      o = align256(o + (size_t)rows * k * 4);
+  w.cand = o;     o = align256(o + (size_t)rows * maxN * 8);
   w.total = o;
   return w;
 }
@@ -446,14 +469,9 @@ static IndexParams make_params(const void* p, const float* omega, const void* ik
   a.Tq = Tq; a.HI = HI; a.dI = dI; a.k = k; a.m = m; a.w = w; a.max_entries = maxN;
   a.scores = scores ? const_cast<float*>(scores) : reinterpret_cast<float*>(base + L.scores);
   a.hist = reinterpret_cast<uint32_t*>(base + L.hist);
-  a.ticket = reinterpret_cast<uint32_t*>(base + L.ticket);
-  a.nsel = reinterpret_cast<uint32_t*>(base + L.nsel);
-  a.ncand = reinterpret_cast<uint32_t*>(base + L.ncand);
+  a.ctr = reinterpret_cast<unsigned long long*>(base + L.ctr);
   a.sel = reinterpret_cast<int32_t*>(base + L.sel);
   a.cand = reinterpret_cast<uint64_t*>(base + L.cand);
-  a.cand_all = reinterpret_cast<uint64_t*>(base + L.cand_all);
-  a.nblk = (int)((maxN + kSelChunk - 1) / kSelChunk);
-  a.selcap = k < kSelChunk ? k : kSelChunk;
   a.idx = idx;
   // score blocks: aim for >= 2 blocks per CU at decode
   int64_t chunk = 512;
@@ -488,8 +506,9 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream) {
   IndexParams a = make_params(nullptr, nullptr, nullptr, csa_off, q_pos, B, Tq, 1, 8, k, m, w, maxN, idx, scores, ws);
-  dim3 g2((unsigned)a.nblk, (unsigned)(B * Tq));
-  hipLaunchKernelGGL(topk_select, g2, dim3(kSelThreads), 0, stream, a);
+  const int nblk = (int)((maxN + kSelChunk - 1) / kSelChunk);
+  hipLaunchKernelGGL(topk_filter, dim3((unsigned)nblk, (unsigned)(B * Tq)), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(topk_finalize, dim3((unsigned)(B * Tq)), dim3(kFinThreads), 0, stream, a);
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 

@@ -176,19 +176,37 @@ def hca_attn(q, kv_hca, hca_off, q_pos, m2: int, w2: int, max_entries: int, scal
 
 # ---------------------------------------------------------------- a6
 
+def swa_attn(q, x, tok_off, q_pos, W: int, scale: float, eps: float, o_part=None, lse=None):
+    """The window branch as a one-split partial (o_part [1, rows, H, D], lse)."""
+    _dev(q, x, tok_off, q_pos, o_part, lse)
+    _i64(tok_off, "tok_off")
+    _i32(q_pos, "q_pos")
+    B = tok_off.numel() - 1
+    rows, H, D = q.shape
+    o_part, lse = _parts_out(rows, H, D, 1, q.device, o_part, lse)
+    check(lib.lca_swa_attn(_ptr(q), _ptr(x), _ptr(tok_off), _ptr(q_pos), B, rows // B, H, D, W, float(scale),
+                           float(eps), _ptr(o_part), _ptr(lse), _dtype_code(q), _stream()), "swa_attn")
+    return o_part, lse
+
+
 def swa_merge_workspace(n_rows: int, H: int, D: int) -> int:
     return int(lib.lca_swa_merge_workspace(n_rows, H, D))
 
 
 def swa_merge(q, x, tok_off, q_pos, sink, parts, W: int, scale: float, eps: float, ws: torch.Tensor,
               out=None):
-    """parts: list of (o_part, lse) pairs.  Returns out [B*Tq, H, D] (q's dtype)."""
+    """parts: list of (o_part, lse) pairs.  Returns out [B*Tq, H, D] (q's dtype).
+    With W = 0 only the partials and the sink are merged (x, tok_off, q_pos
+    and ws may be None)."""
     _dev(q, x, tok_off, q_pos, sink, ws, out)
-    _i64(tok_off, "tok_off")
-    _i32(q_pos, "q_pos")
-    B = tok_off.numel() - 1
     rows, H, D = q.shape
-    Tq = rows // B
+    if W > 0:
+        _i64(tok_off, "tok_off")
+        _i32(q_pos, "q_pos")
+        B = tok_off.numel() - 1
+        Tq = rows // B
+    else:
+        B, Tq = rows, 1
     arr = (Partial * max(1, len(parts)))()
     for i, (o, l) in enumerate(parts):
         _dev(o, l)
@@ -198,6 +216,7 @@ def swa_merge(q, x, tok_off, q_pos, sink, parts, W: int, scale: float, eps: floa
     if sink is not None and sink.dtype != torch.float32:
         raise TypeError("sink must be float32")
     check(lib.lca_swa_merge(_ptr(q), _ptr(x), _ptr(tok_off), _ptr(q_pos), _ptr(sink), arr, len(parts), B, Tq, H, D,
-                            W, float(scale), float(eps), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                            _dtype_code(q), _stream()), "swa_merge")
+                            W, float(scale), float(eps), _ptr(out), _ptr(ws),
+                            0 if ws is None else ws.numel() * ws.element_size(), _dtype_code(q), _stream()),
+          "swa_merge")
     return out

@@ -75,23 +75,30 @@ class HybridAttention:
             csa_off_h=co, hca_off_h=ho)
 
     # -------------------------------------------------------------- a1
-    def compress(self, caches: Caches, raw: dict, tok_off: torch.Tensor,
-                 done_len: Optional[torch.Tensor] = None, done_len_h: Optional[Sequence[int]] = None):
-        """Write the entries of every sequence completed after done_len tokens
-        (all of them when done_len is None)."""
+    def compress_streams(self, caches: Caches, raw: dict, done_h: Sequence[int], which=("csa", "idx", "hca")):
+        """Descriptors of the entries completed after done_h[b] tokens."""
         lens = caches.lens
-        done = [0] * len(lens) if done_len_h is None else [int(v) for v in done_len_h]
-        new_csa = max(n_windows(L, self.m, self.w) - n_windows(d, self.m, self.w) for L, d in zip(lens, done))
-        new_hca = max(n_windows(L, self.m2, self.w2) - n_windows(d, self.m2, self.w2) for L, d in zip(lens, done))
+        new_csa = max(n_windows(L, self.m, self.w) - n_windows(d, self.m, self.w) for L, d in zip(lens, done_h))
+        new_hca = max(n_windows(L, self.m2, self.w2) - n_windows(d, self.m2, self.w2) for L, d in zip(lens, done_h))
         streams = []
-        if new_csa > 0:
+        if new_csa > 0 and "csa" in which:
             streams.append(dict(src=raw["x"], logits=raw["a"], out=caches.kv_csa, ent_off=caches.csa_off,
                                 m=self.m, w=self.w, rmsnorm=1, max_entries=new_csa))
+        if new_csa > 0 and "idx" in which:
             streams.append(dict(src=raw["u"], logits=raw["c"], out=caches.ikey, ent_off=caches.csa_off,
                                 m=self.m, w=self.w, rmsnorm=0, max_entries=new_csa))
-        if new_hca > 0:
+        if new_hca > 0 and "hca" in which:
             streams.append(dict(src=raw["x"], logits=raw["g"], out=caches.kv_hca, ent_off=caches.hca_off,
                                 m=self.m2, w=self.w2, rmsnorm=1, max_entries=new_hca))
+        return streams
+
+    def compress(self, caches: Caches, raw: dict, tok_off: torch.Tensor,
+                 done_len: Optional[torch.Tensor] = None, done_len_h: Optional[Sequence[int]] = None,
+                 which=("csa", "idx", "hca")):
+        """Write the entries of every sequence completed after done_len tokens
+        (all of them when done_len is None)."""
+        done = [0] * len(caches.lens) if done_len_h is None else [int(v) for v in done_len_h]
+        streams = self.compress_streams(caches, raw, done, which)
         # streams of one launch share the number of 16-byte vectors per lane
         groups: Dict[int, list] = {}
         for s in streams:
@@ -140,3 +147,64 @@ class HybridAttention:
         if keep:
             return out, dict(idx=idx, csa=csa, hca=hca)
         return out
+
+    # -------------------------------------------------------------- whole step
+    def decode_buffers(self, rows: int, max_csa: int, max_hca: int, device, dtype):
+        """Preallocated outputs of decode_step (so that the step can be
+        captured in a HIP graph and replayed)."""
+        f32 = torch.float32
+        sc = self.split_csa or self.default_splits(rows, self.k)
+        sh = self.split_hca or self.default_splits(rows, max_hca)
+        return dict(
+            sc=sc, sh=sh, max_csa=max(1, max_csa), max_hca=max_hca,
+            ws_idx=self.index_workspace(rows, max(1, max_csa), device),
+            idx=torch.empty((rows, self.k), dtype=torch.int32, device=device),
+            csa=(torch.empty((sc, rows, self.H, self.D), dtype=f32, device=device),
+                 torch.empty((sc, rows, self.H), dtype=f32, device=device)),
+            hca=(torch.empty((sh, rows, self.H, self.D), dtype=f32, device=device),
+                 torch.empty((sh, rows, self.H), dtype=f32, device=device)),
+            swa=(torch.empty((1, rows, self.H, self.D), dtype=f32, device=device),
+                 torch.empty((1, rows, self.H), dtype=f32, device=device)),
+            out=torch.empty((rows, self.H, self.D), dtype=dtype, device=device))
+
+    def decode_step(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos,
+                    bufs: dict, done_len: Optional[torch.Tensor] = None, done_h: Optional[Sequence[int]] = None,
+                    side: Optional["torch.cuda.Stream"] = None):
+        """One decode (or prefill-chunk) step of mode A: append the entries the
+        new tokens complete (when done_len is given), then the CSA branch
+        (indexer, top-k, sparse attention) on the current stream and, when a
+        side stream is given, the HCA and window branches on it, joined before
+        the merge."""
+        main = torch.cuda.current_stream()
+        if side is not None:
+            fork = torch.cuda.Event()
+            fork.record(main)
+            side.wait_event(fork)
+        # ---- HCA + window branch
+        with torch.cuda.stream(side if side is not None else main):
+            if done_len is not None:
+                st = self.compress_streams(caches, raw, done_h, ("hca",))
+                if st:
+                    ops.kv_compress(st, tok_off, done_len, self.eps)
+            ops.hca_attn(q, caches.kv_hca, caches.hca_off, q_pos, self.m2, self.w2, bufs["max_hca"], self.scale,
+                         self.eps, bufs["sh"], *bufs["hca"])
+            ops.swa_attn(q, raw["x"], tok_off, q_pos, self.W, self.scale, self.eps, *bufs["swa"])
+            if side is not None:
+                join = torch.cuda.Event()
+                join.record(side)
+        # ---- CSA branch
+        if done_len is not None:
+            st = self.compress_streams(caches, raw, done_h, ("csa", "idx"))
+            if st:
+                ops.kv_compress(st, tok_off, done_len, self.eps)
+        ops.csa_index_score(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"],
+                            bufs["ws_idx"])
+        ops.csa_topk_select(caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"], bufs["ws_idx"],
+                            idx=bufs["idx"])
+        ops.csa_sparse_attn(q, caches.kv_csa, caches.csa_off, bufs["idx"], self.scale, self.eps, bufs["sc"],
+                            *bufs["csa"])
+        if side is not None:
+            main.wait_event(join)
+        ops.swa_merge(q, None, None, None, sigma, [bufs["csa"], bufs["hca"], bufs["swa"]], 0, self.scale, self.eps,
+                      None, out=bufs["out"])
+        return bufs["out"]

@@ -271,3 +271,74 @@ def test_index_permutation_invariance():
         a, _ = merge_splits(o1[0][:, r], o1[1][:, r])
         bb, _ = merge_splits(o2[0][:, r], o2[1][:, r])
         assert_close(bb, a, cfg.dtype, "permuted idx")
+
+
+def _decode_setup(cfg, raw):
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    full = (caches.kv_csa.clone(), caches.ikey.clone(), caches.kv_hca.clone())
+    done_h = [L - 1 for L in cfg.lens]
+    # wipe the entries the newest token completes; decode_step appends them again
+    for b, L in enumerate(cfg.lens):
+        for t, off, m, w in ((caches.kv_csa, caches.csa_off_h, cfg.m, cfg.w), (caches.ikey, caches.csa_off_h, cfg.m, cfg.w),
+                             (caches.kv_hca, caches.hca_off_h, cfg.m2, cfg.w2)):
+            n0, n1 = ocmp.n_entries(L - 1, m, w), ocmp.n_entries(L, m, w)
+            t[int(off[b]) + n0:int(off[b]) + n1] = 0
+    done = torch.tensor(done_h, dtype=torch.int64, device="cuda")
+    qmax = int(raw["q_pos"].max()) + 1
+    bufs = layer.decode_buffers(cfg.B, ocmp.n_entries(qmax, cfg.m, cfg.w), ocmp.n_entries(qmax, cfg.m2, cfg.w2),
+                                "cuda", tdtype(cfg))
+    return d, layer, caches, full, done, done_h, bufs
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_decode_step_with_append(overlap):
+    """decode_step: append of the completed entries, both branches (optionally
+    on two streams) and the merge, against the oracle from raw inputs."""
+    cfg = li.small("decode", 108, (4001, 2600, 777), H=64, D=512, k=256)
+    raw = li.make_raw(cfg)
+    d, layer, caches, full, done, done_h, bufs = _decode_setup(cfg, raw)
+    side = torch.cuda.Stream() if overlap else None
+    out = layer.decode_step(caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs,
+                            done_len=done, done_h=done_h, side=side)
+    torch.cuda.synchronize()
+    assert torch.equal(caches.kv_csa, full[0]) and torch.equal(caches.ikey, full[1]) and torch.equal(caches.kv_hca, full[2])
+    _, ores = opipe.run(raw, cfg)
+    idx_h = bufs["idx"].cpu().numpy()
+    out_h = f64(out)
+    for b in range(cfg.B):
+        res = ores[(b, 0)]
+        assert set(idx_h[b][idx_h[b] >= 0].tolist()) == set(res["sel"].tolist())
+        assert np.all(np.diff(idx_h[b][idx_h[b] >= 0]) > 0), "selection not in ascending index order"
+        assert_close(out_h[b], res["out"], cfg.dtype, f"decode row {b}")
+
+
+def test_decode_step_graph_replay():
+    """The two-stream step captured in a HIP graph: every replay equals the
+    eager step (eager work and synchronisation between replays)."""
+    cfg = li.small("graph", 109, (3000, 1500), H=64, D=512, k=256)
+    raw = li.make_raw(cfg)
+    d, layer, caches, full, done, done_h, bufs = _decode_setup(cfg, raw)
+    side = torch.cuda.Stream()
+    args = (caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs)
+    eager = layer.decode_step(*args, done_len=done, done_h=done_h, side=side).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.decode_step(*args, done_len=done, done_h=done_h, side=side)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        layer.decode_step(*args, done_len=done, done_h=done_h, side=side)
+    for rep in range(4):
+        bufs["out"].zero_()
+        bufs["idx"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["out"], eager), f"replay {rep} differs from the eager step"
+        _ = (d["q"].float() * 2).sum().item()   # unrelated eager work between replays
