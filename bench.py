@@ -240,25 +240,33 @@ def main():
     print(f"[bench] {cfg.name}: {R} layers built in {setup_s:.1f} s; {sb / 1e6:.2f} MB/step; "
           f"splits csa={run.sc} hca={run.sh}", file=sys.stderr, flush=True)
 
-    # warm-up, and per-kernel event timing to find the dominant kernel
+    # per-kernel durations: each single-kernel call captured R times (one per
+    # rotated layer) in a HIP graph, replayed, timed with events on its stream
     s = torch.cuda.current_stream()
+    for w in range(2 * R):
+        run.step_calls(run.layers[w % R])
+    torch.cuda.synchronize()
     per = np.zeros(len(run.names))
-    cnt = 0
-    for w in range(max(args.warmup, 2 * R)):
-        L = run.layers[w % R]
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in run.names]
-        for i, f in enumerate(run.calls(L)):
-            evs[i][0].record()
-            f()
-            evs[i][1].record()
+    reps = 8
+    for i in range(len(run.names)):
+        calls = [run.calls(L)[i] for L in run.layers]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in calls:
+                f()
+        g.replay()
         torch.cuda.synchronize()
-        if w >= R:
-            per += [a.elapsed_time(b) for a, b in evs]
-            cnt += 1
-    per /= max(1, cnt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per[i] = e0.elapsed_time(e1) / (reps * R)
+        del g
     dom = int(np.argmax(per))
-    print("[bench] per-kernel ms (isolated): " + ", ".join(f"{n}={t:.4f}" for n, t in zip(run.names, per)),
-          file=sys.stderr, flush=True)
+    print("[bench] per-kernel ms (graph, rotated layers): " +
+          ", ".join(f"{n}={t:.4f}" for n, t in zip(run.names, per)), file=sys.stderr, flush=True)
 
     K = args.steps
     ms_graph = None
@@ -287,19 +295,18 @@ def main():
         torch.cuda.synchronize()
         ms_graph = e0.elapsed_time(e1) / K
 
-    # stream launches, dominant kernel bracketed by events in every step
+    # the same steps as direct single-kernel launches on one stream
     for w in range(args.warmup):
         run.step_calls(run.layers[w % R])
     torch.cuda.synchronize()
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for it in range(K):
-        run.step_calls(run.layers[it % R], probe=(dom, kev[it][0], kev[it][1]))
+        run.step_calls(run.layers[it % R])
     e1.record()
     torch.cuda.synchronize()
     ms_stream = e0.elapsed_time(e1) / K
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+    k_ms = float(per[dom])
 
     ms = ms_graph if ms_graph is not None else ms_stream
     value = cfg.B / (ms / 1e3)
@@ -343,7 +350,7 @@ def main():
         "hbm_frac_of_peak": sb / (ms / 1e3) / HBM_PEAK,
         "bytes_per_step": sb,
         "ms_per_step_stream": ms_stream,
-        "kernel_ms_isolated": {n: float(t) for n, t in zip(run.names, per)},
+        "kernel_ms": {n: float(t) for n, t in zip(run.names, per)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -500,82 +500,113 @@ struct MergeParams {
   void* out;
 };
 
-template <typename ET>
+// One block per (row, head): 256 threads = 4 slot groups x 64 lanes; a lane
+// owns D/64 dims (float4 or narrower), a slot group a quarter of the slots,
+// and the groups meet in LDS.  All of a thread's loads are issued together.
+constexpr int kMergeGroups = 4;
+constexpr int kMergeSlotsPerGroup = kMaxSlots / kMergeGroups;
+
+template <typename ET, int DPL>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
-  __shared__ float wts[16][kMaxSlots];
-  __shared__ const float* sl[kMaxSlots];   // lse of slot
-  __shared__ const float* so[kMaxSlots];   // o of slot
-  const int TPH = a.D / 4;                 // threads per (row, head)
-  const int HPB = 256 / TPH;
-  const int RL = TPH < 64 ? TPH : 64;      // reducer lanes per pair
-  const int hl = threadIdx.x / TPH, t = threadIdx.x % TPH;
+  __shared__ float wts[kMaxSlots];
+  __shared__ float red[kMergeGroups][64 * DPL];
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int64_t RH = (int64_t)a.rows * a.H;
-  const int64_t rh = (int64_t)blockIdx.x * HPB + hl;
-  for (int sidx = threadIdx.x; sidx < a.n_slots; sidx += blockDim.x) {
+  const int64_t rh = blockIdx.x;
+  const int h = (int)(rh % a.H);
+  // slot pointers (cheap: at most kMaxParts parts)
+  auto slot_ptr = [&](int sidx, const float** lse_p, const float** o_p) {
     int p = 0, s = sidx;
     while (s >= a.n_split[p]) { s -= a.n_split[p]; ++p; }
-    sl[sidx] = a.lse[p] + (int64_t)s * RH;
-    so[sidx] = a.o[p] + (int64_t)s * RH * a.D;
-  }
-  __syncthreads();
-  const bool on = rh < RH;
-  // weights exp(lse_s - lse) of every slot, by the first RL lanes of the pair
-  if (t < RL) {
+    *lse_p = a.lse[p] + (int64_t)s * RH + rh;
+    *o_p = a.o[p] + ((int64_t)s * RH + rh) * a.D;
+  };
+  // weights, by wave 0
+  if (grp == 0) {
+    float l_loc[kMaxSlots / 64];
     float mx = -INFINITY;
-    const int h = (int)((on ? rh : 0) % a.H);
-    if (on)
-      for (int sidx = t; sidx < a.n_slots; sidx += RL) {
-        const float l = sl[sidx][rh];
-        wts[hl][sidx] = l;
-        mx = fmaxf(mx, l);
+#pragma unroll
+    for (int i = 0; i < kMaxSlots / 64; ++i) {
+      const int sidx = lane + 64 * i;
+      l_loc[i] = -INFINITY;
+      if (sidx < a.n_slots) {
+        const float* lp; const float* op;
+        slot_ptr(sidx, &lp, &op);
+        l_loc[i] = *lp;
       }
-    mx = wave_max(mx, RL);
-    if (on && a.sink) mx = fmaxf(mx, a.sink[h]);
+      mx = fmaxf(mx, l_loc[i]);
+    }
+    mx = wave_max(mx, 64);
+    if (a.sink) mx = fmaxf(mx, a.sink[h]);
     float den = 0.f;
-    if (on && mx != -INFINITY)
-      for (int sidx = t; sidx < a.n_slots; sidx += RL) {
-        const float l = wts[hl][sidx];
-        den += l == -INFINITY ? 0.f : expf(l - mx);
-      }
-    den = wave_sum(den, RL);
-    if (on && a.sink && mx != -INFINITY) den += expf(a.sink[h] - mx);
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < kMaxSlots / 64; ++i) den += l_loc[i] == -INFINITY ? 0.f : expf(l_loc[i] - mx);
+    }
+    den = wave_sum(den, 64);
+    if (a.sink && mx != -INFINITY) den += expf(a.sink[h] - mx);
     const float lse = mx != -INFINITY ? mx + logf(den) : -INFINITY;
-    if (on)
-      for (int sidx = t; sidx < a.n_slots; sidx += RL) {
-        const float l = wts[hl][sidx];
-        wts[hl][sidx] = (l != -INFINITY && lse != -INFINITY) ? expf(l - lse) : 0.f;
-      }
-  }
-  __syncthreads();
-  if (!on) return;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const int64_t off = rh * a.D + 4 * t;
-  constexpr int U = 8;
-  int sidx = 0;
-  for (; sidx + U <= a.n_slots; sidx += U) {
-    float4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float4*>(so[sidx + u] + off);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float wgt = wts[hl][sidx + u];
-      acc[0] = fmaf(wgt, v[u].x, acc[0]); acc[1] = fmaf(wgt, v[u].y, acc[1]);
-      acc[2] = fmaf(wgt, v[u].z, acc[2]); acc[3] = fmaf(wgt, v[u].w, acc[3]);
+    for (int i = 0; i < kMaxSlots / 64; ++i) {
+      const int sidx = lane + 64 * i;
+      if (sidx < a.n_slots) wts[sidx] = (l_loc[i] != -INFINITY && lse != -INFINITY) ? expf(l_loc[i] - lse) : 0.f;
     }
   }
-  for (; sidx < a.n_slots; ++sidx) {
-    const float4 v = *reinterpret_cast<const float4*>(so[sidx] + off);
-    const float wgt = wts[hl][sidx];
-    acc[0] = fmaf(wgt, v.x, acc[0]); acc[1] = fmaf(wgt, v.y, acc[1]);
-    acc[2] = fmaf(wgt, v.z, acc[2]); acc[3] = fmaf(wgt, v.w, acc[3]);
+  // this group's slots: grp, grp + 4, ...
+  const int nmine = (a.n_slots - grp + kMergeGroups - 1) / kMergeGroups;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  constexpr int U = 16;
+  for (int base = 0; base < nmine; base += U) {
+    float v[U][DPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u;
+      const int sidx = grp + kMergeGroups * (j < nmine ? j : 0);
+      const float* lp; const float* op;
+      slot_ptr(sidx, &lp, &op);
+      if constexpr (DPL == 8) {
+        const float4 x0 = *reinterpret_cast<const float4*>(op + lane * 8);
+        const float4 x1 = *reinterpret_cast<const float4*>(op + lane * 8 + 4);
+        v[u][0] = x0.x; v[u][1] = x0.y; v[u][2] = x0.z; v[u][3] = x0.w;
+        v[u][4] = x1.x; v[u][5] = x1.y; v[u][6] = x1.z; v[u][7] = x1.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) v[u][i] = op[lane * DPL + i];
+      }
+    }
+    if (base == 0) __syncthreads();  // weights ready (every thread reaches this once)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u;
+      if (j >= nmine) break;
+      const float wgt = wts[grp + kMergeGroups * j];
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wgt, v[u][i], acc[i]);
+    }
   }
+  if (nmine <= 0) __syncthreads();
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) red[grp][lane * DPL + i] = acc[i];
+  __syncthreads();
+  if (grp != 0) return;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    float sum = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < kMergeGroups; ++g2) sum += red[g2][lane * DPL + i];
+    acc[i] = sum;
+  }
+  const int64_t off = rh * a.D + lane * DPL;
   if constexpr (ET::kBytes == 2) {
-    uint2 v;
-    v.x = pack_bf16x2(acc[0], acc[1]);
-    v.y = pack_bf16x2(acc[2], acc[3]);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = v;
+    if constexpr (DPL == 8) {
+      stg16(a.out, off * 2, BF16::pack(acc));
+    } else {
+      for (int i = 0; i < DPL; ++i) reinterpret_cast<uint16_t*>(a.out)[off + i] = (uint16_t)f32_to_bf16_bits(acc[i]);
+    }
   } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    for (int i = 0; i < DPL; ++i) reinterpret_cast<float*>(a.out)[off + i] = acc[i];
   }
 }
 
@@ -642,13 +673,17 @@ int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, cons
   a.n_parts = np;
   a.n_slots = ns;
   a.sink = sink; a.rows = rows; a.H = H; a.D = D; a.out = out;
-  const int HPB = 256 / (D / 4);
-  const int64_t pairs = (int64_t)rows * H;
-  dim3 grid((unsigned)((pairs + HPB - 1) / HPB));
-  if (dtype == LCA_BF16)
-    hipLaunchKernelGGL((merge_kernel<BF16>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((merge_kernel<F32>), grid, dim3(256), 0, stream, a);
+  dim3 grid((unsigned)((int64_t)rows * H));
+#define LCA_MERGE(ETy)                                                                            \
+  switch (D) {                                                                                    \
+    case 64: hipLaunchKernelGGL((merge_kernel<ETy, 1>), grid, dim3(256), 0, stream, a); break;   \
+    case 128: hipLaunchKernelGGL((merge_kernel<ETy, 2>), grid, dim3(256), 0, stream, a); break;  \
+    case 256: hipLaunchKernelGGL((merge_kernel<ETy, 4>), grid, dim3(256), 0, stream, a); break;  \
+    case 512: hipLaunchKernelGGL((merge_kernel<ETy, 8>), grid, dim3(256), 0, stream, a); break;  \
+    default: set_error("merge: D=%d not supported", D); return LCA_ERR_UNSUPPORTED;             \
+  }
+  if (dtype == LCA_BF16) { LCA_MERGE(BF16) } else { LCA_MERGE(F32) }
+#undef LCA_MERGE
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 

@@ -28,6 +28,7 @@ namespace lca {
 
 constexpr int kCompressThreads = 512;
 constexpr int kRunEntries = 16;  // entries per row group in small-window mode
+constexpr int kPrefetchM = 4;    // small-window strides up to this use the prefetching walk
 
 struct CompressStreamDev {
   const void* src;
@@ -168,6 +169,75 @@ __device__ void compress_small(const CompressStreamDev& s, const CompressParams&
   const bool two = (s.w == 2 * s.m);
 
   PoolState<VE> prev[NV], cur[NV];
+  if constexpr (NV == 1) if (m <= kPrefetchM) {
+    // raw rows of the next segment are requested before the current one is
+    // pooled, so a run costs one memory round trip per segment at most and a
+    // single entry (decode append) costs one in all
+    struct Raw {
+      uint4 x[kPrefetchM][NV], z[kPrefetchM][NV];
+      float zs[kPrefetchM];
+    };
+    auto fetch = [&](int64_t q, Raw& r) {
+      const int64_t tb = q * m;
+#pragma unroll
+      for (int t = 0; t < kPrefetchM; ++t) {
+        if (t < m) {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            r.x[t][v] = ldg16(rc.src, (tb + t) * rc.row_bytes + (int64_t)rc.ch0[v] * ET::kBytes);
+            if (rc.per_channel) r.z[t][v] = ldg16(rc.lg, (tb + t) * rc.row_bytes + (int64_t)rc.ch0[v] * ET::kBytes);
+          }
+          if (!rc.per_channel) r.zs[t] = ET::load1(rc.lg, tb + t);
+        }
+      }
+    };
+    auto pool = [&](const Raw& r, PoolState<VE>(&st)[NV]) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) st[v].reset();
+#pragma unroll
+      for (int t = 0; t < kPrefetchM; ++t) {
+        if (t < m) {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            float x[VE], z[VE];
+            ET::unpack(r.x[t][v], x);
+            if (rc.per_channel) {
+              ET::unpack(r.z[t][v], z);
+            } else {
+#pragma unroll
+              for (int e = 0; e < VE; ++e) z[e] = r.zs[t];
+            }
+            st[v].add(z, x);
+          }
+        }
+      }
+    };
+    const int64_t q_end = two ? j1 + 1 : j1;  // last segment + 1
+    Raw ra, rb;
+    fetch(j0, ra);
+    if (j0 + 1 < q_end) fetch(j0 + 1, rb);
+    if (two) {
+      pool(ra, prev);
+      ra = rb;
+      if (j0 + 2 < q_end) fetch(j0 + 2, rb);
+    }
+    // ra holds the segment pooled next, rb the one after it (in flight)
+    for (int64_t j = j0; j < j1; ++j) {
+      pool(ra, cur);
+      ra = rb;
+      const int64_t nq = (two ? j + 1 : j) + 2;
+      if (nq < q_end) fetch(nq, rb);
+      if (two) {
+        PoolState<VE> e[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) { e[v] = prev[v]; e[v].merge(cur[v]); prev[v] = cur[v]; }
+        finish_entry<ET, NV>(s, P.eps, G, e, rc.ch0, ent_base + j, true);
+      } else {
+        finish_entry<ET, NV>(s, P.eps, G, cur, rc.ch0, ent_base + j, true);
+      }
+    }
+    return;
+  }
   auto segment = [&](int64_t q, PoolState<VE>(&st)[NV]) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) st[v].reset();

@@ -47,7 +47,8 @@ struct IndexParams {
   int64_t max_entries;
   int chunk;                // entries per score block
   float* scores;            // [rows][max_entries]
-  uint32_t* hist;           // [rows][kHistBins]
+  uint32_t* hist;           // [rows][nstripe][kHistBins]
+  int nstripe;              // histogram copies (score blocks spread their atomics)
   unsigned long long* ctr;  // [rows]: selected count | candidate count << 32
   int32_t* sel;             // [rows][k]
   uint64_t* cand;           // [rows][max_entries]
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
     }
   }
   __syncthreads();
-  if (do_hist) hist_flush(lh, a.hist + (int64_t)r * kHistBins);
+  if (do_hist) hist_flush(lh, a.hist + ((int64_t)r * a.nstripe + blockIdx.x % a.nstripe) * kHistBins);
 }
 
 // Generic path (fp32, or bf16 shapes the matrix-core kernel does not take):
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
     if (do_hist) hist_add(lh, s);
   }
   __syncthreads();
-  if (do_hist) hist_flush(lh, a.hist + (int64_t)r * kHistBins);
+  if (do_hist) hist_flush(lh, a.hist + ((int64_t)r * a.nstripe + blockIdx.x % a.nstripe) * kHistBins);
 }
 
 // ------------------------------------------------------------------ select
@@ -254,13 +255,27 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
   const int64_t c0 = (int64_t)cb * kSelChunk;
   if (c0 >= nv) return;
 
-  // histogram and this chunk's scores, all loads in flight together
-  const uint4* gh = reinterpret_cast<const uint4*>(a.hist + (int64_t)r * kHistBins);
+  // histogram (summed over its stripes) and this chunk's scores, all loads in
+  // flight together
+  const uint4* gh = reinterpret_cast<const uint4*>(a.hist + (int64_t)r * a.nstripe * kHistBins);
   const float* S = a.scores + (int64_t)r * a.max_entries;
   constexpr int HV = kHistBins / 4 / kSelThreads;  // uint4 per thread
+  constexpr int kMaxStripes = 8;
+  uint4 hs[kMaxStripes][HV];
+#pragma unroll
+  for (int st = 0; st < kMaxStripes; ++st)
+#pragma unroll
+    for (int i = 0; i < HV; ++i)
+      hs[st][i] = st < a.nstripe ? gh[st * (kHistBins / 4) + threadIdx.x + i * kSelThreads] : make_uint4(0, 0, 0, 0);
   uint4 hv[HV];
 #pragma unroll
-  for (int i = 0; i < HV; ++i) hv[i] = gh[threadIdx.x + i * kSelThreads];
+  for (int i = 0; i < HV; ++i) {
+    hv[i] = hs[0][i];
+#pragma unroll
+    for (int st = 1; st < kMaxStripes; ++st) {
+      hv[i].x += hs[st][i].x; hv[i].y += hs[st][i].y; hv[i].z += hs[st][i].z; hv[i].w += hs[st][i].w;
+    }
+  }
   const int64_t e0 = c0 + (int64_t)threadIdx.x * kSelPerThread;
   float sv[kSelPerThread];
 #pragma unroll
@@ -334,8 +349,12 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
   const uint32_t n_sel = (uint32_t)(cnt & 0xFFFFFFFFull);
   const uint32_t ncands = (uint32_t)(cnt >> 32);
   // the threshold bin of the filter kernel, recomputed from the same histogram
-  const uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sh[i] = gh[i];
+  const uint32_t* gh = a.hist + (int64_t)r * a.nstripe * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) {
+    uint32_t c = 0;
+    for (int st = 0; st < a.nstripe; ++st) c += gh[st * kHistBins + i];
+    sh[i] = c;
+  }
   if (threadIdx.x == 0) { s_T = 0; s_above = 0; }
   __syncthreads();
   find_threshold(sh, kHistBins, (uint32_t)a.k, sm, rev, &s_T, &s_above);
@@ -431,8 +450,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
     }
   }
   // leave the workspace clean for the next call
-  uint32_t* ghw = a.hist + (int64_t)r * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) ghw[i] = 0;
+  uint32_t* ghw = a.hist + (int64_t)r * a.nstripe * kHistBins;
+  for (int i = threadIdx.x; i < a.nstripe * kHistBins; i += blockDim.x) ghw[i] = 0;
   if (threadIdx.x == 0) a.ctr[r] = 0;
 }
 
@@ -444,10 +463,21 @@ struct IndexWs {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// entries per score block (>= 2 blocks per CU at decode) and histogram stripes
+static int64_t score_chunk(int rows, int64_t maxN) {
+  int64_t chunk = 512;
+  while (chunk < 8192 && ((maxN + chunk - 1) / chunk) * (int64_t)rows > 4096) chunk *= 2;
+  return chunk;
+}
+static int hist_stripes(int rows, int64_t maxN) {
+  const int64_t blocks = (maxN + score_chunk(rows, maxN) - 1) / score_chunk(rows, maxN);
+  return blocks >= 8 ? 8 : (int)blocks;
+}
+
 static IndexWs index_ws_layout(int rows, int64_t maxN, int k) {
   IndexWs w{};
   size_t o = 0;
-  w.hist = o;     o = align256(o + (size_t)rows * kHistBins * 4);
+  w.hist = o;     o = align256(o + (size_t)rows * hist_stripes(rows, maxN) * kHistBins * 4);
   w.ctr = o;      o = align256(o + (size_t)rows * 8);
   w.scores = o;   o = align256(o + (size_t)rows * maxN * 4);
   w.sel = o;      o = align256(o + (size_t)rows * k * 4);
@@ -473,10 +503,8 @@ static IndexParams make_params(const void* p, const float* omega, const void* ik
   a.sel = reinterpret_cast<int32_t*>(base + L.sel);
   a.cand = reinterpret_cast<uint64_t*>(base + L.cand);
   a.idx = idx;
-  // score blocks: aim for >= 2 blocks per CU at decode
-  int64_t chunk = 512;
-  while (chunk < 8192 && ((maxN + chunk - 1) / chunk) * (int64_t)rows > 4096) chunk *= 2;
-  a.chunk = (int)chunk;
+  a.chunk = (int)score_chunk(rows, maxN);
+  a.nstripe = hist_stripes(rows, maxN);
   return a;
 }
 

@@ -1,0 +1,121 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (decode_step: append of the entries the new token completes,
+CSA branch on the current stream, HCA and window branches on a side stream,
+merge).  Inputs are drawn on the GPU with a seeded generator and copied back
+for the oracle, which checks sampled compressed entries, every selected set
+of the checked rows (scores recomputed in float64 from the GPU-stored indexer
+keys), and every head of the checked rows' outputs, stage-wise and end to end.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lca_inputs as li
+from oracle import attention as oatt
+from oracle import compress as ocmp
+from oracle import indexer as oidx
+from oracle import numerics as onum
+
+from gpu_util import assert_close, check_topk, f64, layer_for, score_bound
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _host(t):
+    return t.float().cpu().numpy()
+
+
+def _run(cfg):
+    raw = li.make_raw_torch(cfg, 0, "cuda")
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", raw["x"].dtype)
+    layer.compress(caches, raw, raw["tok_off"])
+    q_pos = raw["q_pos"].reshape(-1).contiguous()
+    done_h = [L - 1 for L in cfg.lens]
+    done = torch.tensor(done_h, dtype=torch.int64, device="cuda")
+    qmax = max(cfg.lens)
+    bufs = layer.decode_buffers(cfg.B, ocmp.n_entries(qmax, cfg.m, cfg.w), ocmp.n_entries(qmax, cfg.m2, cfg.w2),
+                                "cuda", raw["x"].dtype)
+    out = layer.decode_step(caches, raw, raw["tok_off"], raw["q"], raw["p"], raw["omega"], raw["sigma"], q_pos, bufs,
+                            done_len=done, done_h=done_h, side=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    return raw, layer, caches, bufs, out
+
+
+def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
+    off = raw["tok_off"].cpu().numpy()
+    idx_h = bufs["idx"].cpu().numpy()
+    out_h = f64(out)
+    for b in rows:
+        L = cfg.lens[b]
+        s0, s1 = int(off[b]), int(off[b + 1])
+        print(f"[{cfg.name}] sequence {b}: {L} tokens", flush=True)
+        x, a, g = _host(raw["x"][s0:s1]), _host(raw["a"][s0:s1]), _host(raw["g"][s0:s1])
+        u, c = _host(raw["u"][s0:s1]), _host(raw["c"][s0:s1])
+        co, ho = caches.csa_off_h, caches.hca_off_h
+        kv_csa = f64(caches.kv_csa[co[b]:co[b + 1]])
+        ikey = f64(caches.ikey[co[b]:co[b + 1]])
+        kv_hca = f64(caches.kv_hca[ho[b]:ho[b + 1]])
+        ncsa, nhca = ocmp.n_entries(L, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m2, cfg.w2)
+        # ---- a1 on sampled entries (and the appended last ones)
+        ent = sorted(set(rng.choice(ncsa, size=min(48, ncsa), replace=False).tolist()) | {ncsa - 1})
+        for got, src, lg, norm in ((kv_csa, x, a, True), (ikey, u, c, False)):
+            ref = onum.round_to(ocmp.compress(src, lg, cfg.m, cfg.w, norm, cfg.eps, ent), cfg.dtype)
+            assert np.max(np.abs(got[ent] - ref)) <= 2e-2
+        entj = sorted(set(rng.choice(nhca, size=min(16, nhca), replace=False).tolist()) | {nhca - 1})
+        ref = onum.round_to(ocmp.compress(x, g, cfg.m2, cfg.w2, True, cfg.eps, entj), cfg.dtype)
+        assert np.max(np.abs(kv_hca[entj] - ref)) <= 2e-2
+        # ---- a2/a3: every visible entry scored in float64 from the GPU-stored keys
+        i = L - 1
+        p = f64(raw["p"][b])
+        om = raw["omega"][b].cpu().numpy().astype(np.float64)
+        s_ref = oidx.scores(p, om, ikey)
+        bound = score_bound(p, om, ikey)
+        sel = idx_h[b]
+        chosen = sel[sel >= 0]
+        assert len(chosen) == min(cfg.k, ncsa)
+        assert np.all(np.diff(chosen) > 0)
+        ref_sel = oidx.topk(s_ref, cfg.k)
+        kth = s_ref[ref_sel[-1]]
+        diff = set(chosen.tolist()) ^ set(ref_sel.tolist())
+        for j in diff:
+            assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + bound[j], f"entry {j} is not a near tie"
+        print(f"  top-{cfg.k}: {len(diff)} near-tie differences", flush=True)
+        # ---- a4-a6 stage-wise (GPU caches and selection), all heads
+        qhat = oatt.normalize_query(f64(raw["q"][b]), cfg.eps, cfg.dtype)
+        csa = oatt.partial(qhat, kv_csa[chosen], cfg.scale)
+        hca = oatt.partial(qhat, kv_hca[:nhca], cfg.scale)
+        win = oatt.normalize_tokens(x[max(0, i - cfg.W + 1):i + 1].astype(np.float64), cfg.eps, cfg.dtype)
+        swa = oatt.partial(qhat, win, cfg.scale)
+        sig = raw["sigma"].cpu().numpy().astype(np.float64)
+        o_ref, _ = oatt.merge([csa, hca, swa], sig)
+        assert_close(out_h[b], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"{cfg.name} row {b}")
+        # ---- end to end: oracle keys from raw inputs, if the selected sets agree
+        if not diff:
+            ikey_o = onum.round_to(ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps), cfg.dtype)
+            sel_o = oidx.topk(oidx.scores(p, om, ikey_o), cfg.k)
+            kv_sel = onum.round_to(ocmp.compress(x, a, cfg.m, cfg.w, True, cfg.eps, sorted(sel_o)), cfg.dtype)
+            kv_h = onum.round_to(ocmp.compress(x, g, cfg.m2, cfg.w2, True, cfg.eps), cfg.dtype)
+            o_e2e, _ = oatt.merge([oatt.partial(qhat, kv_sel, cfg.scale), oatt.partial(qhat, kv_h, cfg.scale), swa], sig)
+            assert_close(out_h[b], onum.round_to(o_e2e, cfg.dtype), cfg.dtype, f"{cfg.name} row {b} e2e")
+
+
+def test_flash_decode_full():
+    cfg = li.FLASH_DECODE
+    raw, layer, caches, bufs, out = _run(cfg)
+    _check_rows(cfg, raw, caches, bufs, out, [0, 5], np.random.default_rng(1))
+
+
+def test_pro_1m_decode_full():
+    cfg = li.PRO_1M_DECODE
+    raw, layer, caches, bufs, out = _run(cfg)
+    _check_rows(cfg, raw, caches, bufs, out, [0], np.random.default_rng(2))
+
+
+def test_pro_varlen_full():
+    cfg = li.PRO_VARLEN
+    raw, layer, caches, bufs, out = _run(cfg)
+    lens = np.asarray(cfg.lens)
+    rows = [int(np.argmin(lens)), int(np.argmax(lens)), 17]
+    _check_rows(cfg, raw, caches, bufs, out, rows, np.random.default_rng(3))
+    assert torch.isfinite(out.float()).all()
