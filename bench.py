@@ -5,17 +5,23 @@ Metric: decode query-tokens/s per layer at a 1M-token Pro-shaped context, and
 the fraction of peak HBM bandwidth it corresponds to.
 
 A step is one pass of the whole hot path for one query token per sequence:
-  kv_compress (the CSA, indexer-key and HCA entries the new token completes)
-  -> csa_index_score -> csa_topk_select -> csa_sparse_attn
-  -> hca_attn -> swa_merge (window + sink + merge)
-over caches resident in HBM.  To keep the 256 MB Infinity Cache from serving
+  csa_index_score_append (the CSA, indexer-key and HCA entries the new token
+    completes, and the index scores, in one launch)
+  -> csa_topk_select -> hybrid_attn (CSA sparse + HCA dense + window
+  partials, one launch) -> swa_merge (sink + merge)
+on one stream, over caches resident in HBM.  To keep the 256 MB Infinity Cache from serving
 the caches, steps rotate over R layers, each with its own raw streams and
 caches (R * per-step bytes >= 2 x 256 MB).
 
 Timed regions (HIP events on the launch stream, synchronised on both sides):
-  1. the step replayed as HIP graphs (headline value), then
-  2. the same steps launched directly, with events bracketing the dominant
-     kernel's launch in every step (its average duration gives the roofline).
+  1. per kernel: one HIP graph of that kernel's launch for each of the R
+     rotated layers, replayed 8 times (the top-k kernels, which consume the
+     histogram the score kernel builds, are timed with it and the score
+     kernel's time subtracted); the dominant kernel's average launch
+     duration gives the roofline;
+  2. the headline: the W warmup steps and then the K timed steps, each set
+     captured as one HIP graph of consecutive layer steps and replayed once;
+  3. the same K steps launched directly (host launch cost included).
 cpu_baseline: the float64 oracle on the host, same workload, bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
@@ -79,10 +85,16 @@ def kernel_cost(cfg, name):
             nwin = min(cfg.W, L)
             by += nwin * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * nwin
+        elif name == "hybrid_attn":
+            nwin = min(cfg.W, L)
+            by += (kk + nh + nwin) * cfg.D * e + cfg.H * cfg.D * e + kk * 4
+            fl += 4 * cfg.H * cfg.D * (kk + nh + nwin)
         elif name == "swa_merge":
             by += cfg.H * cfg.D * e + cfg.H * 4                # output + sink
-        elif name == "kv_compress":                            # the entries one token completes
+        elif name == "csa_index_score_append":                 # scores + the entries one token completes
+            by += ncsa * cfg.dI * e
             by += (2 * cfg.w * cfg.D + 2 * cfg.w * cfg.dI + 2 * cfg.w2 * cfg.D) * e + (2 * cfg.D + cfg.dI) * e
+            fl += 2 * ncsa * cfg.dI * cfg.HI
     return by, fl
 
 
@@ -117,44 +129,45 @@ class Runner:
         qmax = max(cfg.lens)
         self.bufs = a.decode_buffers(rows, n_windows(qmax, cfg.m, cfg.w), n_windows(qmax, cfg.m2, cfg.w2), dev,
                                      self.layers[0].q.dtype)
-        self.sc, self.sh = self.bufs["sc"], self.bufs["sh"]
-        self.side = torch.cuda.Stream()
-        self.names = ["kv_compress(csa,idx)", "kv_compress(hca)", "csa_index_score", "csa_topk_select",
-                      "csa_sparse_attn", "hca_attn", "swa_attn", "swa_merge"]
+        self.sc, self.sh, self.sw = self.bufs["sc"], self.bufs["sh"], self.bufs["sw"]
+        self.names = ["csa_index_score_append", "csa_topk_select", "hybrid_attn", "swa_merge"]
+        # the top-k kernels consume and clear the histogram the score kernel
+        # builds, so they are timed together with it (score subtracted)
+        self.timed = ["csa_index_score_append", "csa_index_score_append+csa_topk_select", "hybrid_attn",
+                      "swa_merge"]
 
-    def step(self, L, side=True):
-        """The whole decode step; the HCA and window branches on the side stream."""
+    def step(self, L):
+        """The whole decode step (four calls on the current stream)."""
         return self.attn.decode_step(L.caches, L.raw, L.tok_off, L.q, L.p, L.omega, L.sigma, L.q_pos, self.bufs,
-                                     done_len=L.done, done_h=L.done_h, side=self.side if side else None)
+                                     done_len=L.done, done_h=L.done_h)
 
     def calls(self, L):
-        """The same step as a sequence of single-kernel calls (one stream)."""
+        """The same step as a sequence of single-kernel calls."""
         cfg, ops, a, c, bf = self.cfg, self.ops, self.attn, L.caches, self.bufs
-        st_c = a.compress_streams(c, L.raw, L.done_h, ("csa", "idx"))
-        st_h = a.compress_streams(c, L.raw, L.done_h, ("hca",))
+        st = a.compress_streams(c, L.raw, L.done_h)
+        idx_st = [x for x in st if x["out"] is c.ikey][0]
+        kv_st = [x for x in st if x["out"] is not c.ikey]
+        srcs = a.attn_sources(c, L.raw["x"], L.tok_off, bf["idx"], bf)
+        parts = [bf["csa"], bf["hca"], bf["swa"]][:len(srcs)]
         return [
-            lambda: st_c and ops.kv_compress(st_c, L.tok_off, L.done, cfg.eps),
-            lambda: st_h and ops.kv_compress(st_h, L.tok_off, L.done, cfg.eps),
-            lambda: ops.csa_index_score(L.p, L.omega, c.ikey, c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, bf["max_csa"],
-                                        bf["ws_idx"]),
+            lambda: ops.csa_index_score_append(L.p, L.omega, c.ikey, c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w,
+                                               bf["max_csa"], bf["ws_idx"], idx_st, kv_st, L.tok_off, L.done,
+                                               cfg.eps),
             lambda: ops.csa_topk_select(c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, bf["max_csa"], bf["ws_idx"],
                                         idx=bf["idx"]),
-            lambda: ops.csa_sparse_attn(L.q, c.kv_csa, c.csa_off, bf["idx"], a.scale, cfg.eps, bf["sc"], *bf["csa"]),
-            lambda: ops.hca_attn(L.q, c.kv_hca, c.hca_off, L.q_pos, cfg.m2, cfg.w2, bf["max_hca"], a.scale, cfg.eps,
-                                 bf["sh"], *bf["hca"]),
-            lambda: ops.swa_attn(L.q, L.raw["x"], L.tok_off, L.q_pos, cfg.W, a.scale, cfg.eps, *bf["swa"]),
-            lambda: ops.swa_merge(L.q, None, None, None, L.sigma, [bf["csa"], bf["hca"], bf["swa"]], 0, a.scale,
-                                  cfg.eps, None, out=bf["out"]),
+            lambda: ops.hybrid_attn(L.q, L.q_pos, srcs, a.scale, cfg.eps),
+            lambda: ops.swa_merge(L.q, None, None, None, L.sigma, parts, 0, a.scale, cfg.eps, None, out=bf["out"]),
         ]
 
-    def step_calls(self, L, probe=None):
-        for i, f in enumerate(self.calls(L)):
-            if probe is not None and i == probe[0]:
-                probe[1].record()
-                f()
-                probe[2].record()
-            else:
-                f()
+    def timed_call(self, L, name):
+        """The call (or pair of calls) timed as `name`."""
+        fs = dict(zip(self.names, self.calls(L)))
+        parts = [fs[n] for n in name.split("+")]
+        return lambda: [f() for f in parts]
+
+    def step_calls(self, L):
+        for f in self.calls(L):
+            f()
 
 
 def cpu_baseline(cfg, state, budget_s):
@@ -238,7 +251,7 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     print(f"[bench] {cfg.name}: {R} layers built in {setup_s:.1f} s; {sb / 1e6:.2f} MB/step; "
-          f"splits csa={run.sc} hca={run.sh}", file=sys.stderr, flush=True)
+          f"splits csa={run.sc} hca={run.sh} window={run.sw}", file=sys.stderr, flush=True)
 
     # per-kernel durations: each single-kernel call captured R times (one per
     # rotated layer) in a HIP graph, replayed, timed with events on its stream
@@ -246,10 +259,10 @@ def main():
     for w in range(2 * R):
         run.step_calls(run.layers[w % R])
     torch.cuda.synchronize()
-    per = np.zeros(len(run.names))
+    tper = np.zeros(len(run.timed))
     reps = 8
-    for i in range(len(run.names)):
-        calls = [run.calls(L)[i] for L in run.layers]
+    for i, tname in enumerate(run.timed):
+        calls = [run.timed_call(L, tname) for L in run.layers]
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for f in calls:
@@ -262,8 +275,10 @@ def main():
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        per[i] = e0.elapsed_time(e1) / (reps * R)
+        tper[i] = e0.elapsed_time(e1) / (reps * R)
         del g
+    tt = dict(zip(run.timed, tper))
+    per = np.array([tt[n] if n in tt else tt[run.names[0] + "+" + n] - tt[run.names[0]] for n in run.names])
     dom = int(np.argmax(per))
     print("[bench] per-kernel ms (graph, rotated layers): " +
           ", ".join(f"{n}={t:.4f}" for n, t in zip(run.names, per)), file=sys.stderr, flush=True)
@@ -271,29 +286,32 @@ def main():
     K = args.steps
     ms_graph = None
     if args.graph:
-        graphs = []
-        for L in run.layers:
-            s2 = torch.cuda.Stream()
-            s2.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s2):
-                for _ in range(2):
-                    run.step(L)
-            torch.cuda.current_stream().wait_stream(s2)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        # the warmup steps and the K timed steps each captured as one graph of
+        # consecutive layer steps (as the layers of one forward pass run), so
+        # that host-side launch cost is paid once per graph, not per step
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            for L in run.layers:
                 run.step(L)
-            graphs.append(g)
-        for w in range(args.warmup):
-            graphs[w % R].replay()
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        gw, gk = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw):
+            for w in range(args.warmup):
+                run.step(run.layers[w % R])
+        with torch.cuda.graph(gk):
+            for it in range(K):
+                run.step(run.layers[it % R])
+        gw.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for it in range(K):
-            graphs[it % R].replay()
+        gk.replay()
         e1.record()
         torch.cuda.synchronize()
         ms_graph = e0.elapsed_time(e1) / K
+        del gw, gk
 
     # the same steps as direct single-kernel launches on one stream
     for w in range(args.warmup):
@@ -312,9 +330,7 @@ def main():
     value = cfg.B / (ms / 1e3)
     name = run.names[dom]
     kb, kf = kernel_cost(cfg, name.split("(")[0])
-    if name.startswith("kv_compress"):  # split between the two launches
-        kb = kb // 2
-    if name in ("hca_attn", "csa_sparse_attn", "swa_attn") and kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
+    if name == "hybrid_attn" and kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
         roof = {"bound": "mfma", "achieved": kf / (k_ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
                 "unit": "TFLOP/s"}
     else:

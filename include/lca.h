@@ -147,6 +147,32 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
                         const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
                         int64_t max_entries, float* scores, void* ws, size_t ws_bytes, int dtype,
                         void* stream);
+/* a1 + a2 for one decode step: the compression of the entries the newest
+ * tokens complete and the index scores, in one launch.  Equivalent to
+ *     lca_kv_compress({idx_stream} + kv_streams, tok_off, done_len, ...)
+ *     lca_csa_index_score(..., Tq = 1, ...)
+ * (one query row per sequence): the new indexer keys are pooled, stored and
+ * scored by blocks of their own, the entries that existed before by the
+ * scoring blocks, and the kv_streams (entries only the attention reads, such
+ * as the CSA and HCA KV entries) by further blocks of the same launch; no
+ * block reads what another writes.  The caches written are bit-identical to
+ * lca_kv_compress's; the new entries' scores agree within rounding order.
+ * Falls back to those two calls where the fused launch does not apply: fp32,
+ * d_I not in {32, 64, 128, 256}, an indexer window other than w = m or
+ * w = 2m <= 16, kv streams wider than 512 bf16 channels.
+ *   idx_stream  the indexer-key stream: out == ikey, ent_off == csa_off,
+ *               C == d_I, same m and w
+ *   kv_streams  0 to 4 further streams sharing one vector width
+ *   tok_off, done_len  as lca_kv_compress (done_len required)
+ * Other arguments as lca_csa_index_score with Tq = 1; the workspace must be
+ * clean (as left by lca_csa_topk_select). */
+int lca_csa_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                               const int32_t* q_pos, int B, int H_I, int d_I, int k, int m, int w,
+                               int64_t max_entries, const lca_compress_stream* idx_stream,
+                               const lca_compress_stream* kv_streams, int n_kv, const int64_t* tok_off,
+                               const int64_t* done_len, float eps, float* scores, void* ws, size_t ws_bytes,
+                               int dtype, void* stream);
+
 int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                         int64_t max_entries, int32_t* idx, const float* scores, void* ws, size_t ws_bytes,
                         void* stream);
@@ -211,6 +237,40 @@ int lca_hca_attn(const void* q, const void* kv_hca, const int64_t* hca_off, cons
  * lca_swa_merge with W = 0.  W >= 1. */
 int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int32_t* q_pos, int B, int Tq, int H,
                  int D, int W, float scale, float eps, float* o_part, float* lse, int dtype, void* stream);
+
+/* All three attention branches of a step in one launch.  Each source writes
+ * its own partials, exactly as the single-branch calls above would with the
+ * same n_split, so lca_swa_merge (W = 0) combines them:
+ *   LCA_SRC_DENSE   HCA entries of kv (packed by off) visible under m2, w2
+ *                   (as lca_hca_attn)
+ *   LCA_SRC_GATHER  the k entries of kv listed in idx [B*Tq, k], -1 = unused
+ *                   (as lca_csa_sparse_attn)
+ *   LCA_SRC_WINDOW  raw rows max(0, i-W+1) .. i of kv packed by off, each
+ *                   RMS-normalised over D on load (as lca_swa_attn, any
+ *                   n_split)
+ * The sources share q [B*Tq, H, D], q_pos (device int32 [B*Tq]; read by the
+ * DENSE and WINDOW sources), scale and eps.  One launch costs one kernel
+ * start and lets the branches' blocks share the machine.  The bf16
+ * matrix-core path (H a multiple of 16) stages at most 2048 gathered slots
+ * per split: ceil(ceil(k/32) / n_split) * 32 <= 2048, else
+ * LCA_ERR_UNSUPPORTED.  1 <= n_src <= 3; 1 <= n_split <= 256 per source. */
+enum { LCA_SRC_DENSE = 0, LCA_SRC_GATHER = 1, LCA_SRC_WINDOW = 2 };
+
+typedef struct lca_attn_source {
+  int32_t kind;          /* LCA_SRC_* */
+  const void* kv;        /* cache rows (DENSE, GATHER) or raw rows (WINDOW), dtype */
+  const int64_t* off;    /* device int64 [B+1]: row offsets of kv per sequence */
+  const int32_t* idx;    /* GATHER: device int32 [B*Tq, k]; else NULL */
+  int32_t k;             /* GATHER slots per row */
+  int32_t m2, w2;        /* DENSE: stride and window of the entries */
+  int32_t W;             /* WINDOW: window length, >= 1 */
+  int32_t n_split;       /* key-range parts */
+  float* o_part;         /* fp32 [n_split, B*Tq, H, D] */
+  float* lse;            /* fp32 [n_split, B*Tq, H] */
+} lca_attn_source;
+
+int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
+                    int H, int D, float scale, float eps, int dtype, void* stream);
 
 typedef struct lca_partial {
   const float* o;   /* [n_split, B*Tq, H, D] */

@@ -23,9 +23,11 @@ LCA_BF16 = 1
 
 EXPORTS = [
     "lca_strerror", "lca_last_error", "lca_version", "lca_kv_compress",
-    "lca_csa_index_topk_workspace", "lca_csa_index_topk", "lca_csa_index_score", "lca_csa_topk_select", "lca_csa_sparse_attn", "lca_hca_attn",
-    "lca_swa_attn", "lca_swa_merge_workspace", "lca_swa_merge",
+    "lca_csa_index_topk_workspace", "lca_csa_index_topk", "lca_csa_index_score", "lca_csa_index_score_append",
+    "lca_csa_topk_select", "lca_csa_sparse_attn", "lca_hca_attn",
+    "lca_swa_attn", "lca_hybrid_attn", "lca_swa_merge_workspace", "lca_swa_merge",
 ]
+LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_WINDOW = 0, 1, 2
 
 
 class CompressStream(ctypes.Structure):
@@ -38,6 +40,14 @@ class CompressStream(ctypes.Structure):
 
 class Partial(ctypes.Structure):
     _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("n_split", ctypes.c_int32)]
+
+
+class AttnSource(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("kv", ctypes.c_void_p), ("off", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+        ("k", ctypes.c_int32), ("m2", ctypes.c_int32), ("w2", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("n_split", ctypes.c_int32), ("o_part", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+    ]
 
 
 class LCAError(RuntimeError):
@@ -66,6 +76,10 @@ def _load():
                                      i32, vp]
     L.lca_csa_index_score.restype = i32
     L.lca_csa_index_score.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, sz, i32, vp]
+    L.lca_csa_index_score_append.restype = i32
+    L.lca_csa_index_score_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+                                             ctypes.POINTER(CompressStream), ctypes.POINTER(CompressStream), i32,
+                                             vp, vp, f32, vp, vp, sz, i32, vp]
     L.lca_csa_topk_select.restype = i32
     L.lca_csa_topk_select.argtypes = [vp, vp, i32, i32, i32, i32, i32, i64, vp, vp, vp, sz, vp]
     L.lca_csa_sparse_attn.restype = i32
@@ -74,6 +88,8 @@ def _load():
     L.lca_hca_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, f32, f32, i32, vp, vp, i32, vp]
     L.lca_swa_attn.restype = i32
     L.lca_swa_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp, i32, vp]
+    L.lca_hybrid_attn.restype = i32
+    L.lca_hybrid_attn.argtypes = [ctypes.POINTER(AttnSource), i32, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp]
     L.lca_swa_merge_workspace.restype = sz
     L.lca_swa_merge_workspace.argtypes = [i32, i32, i32]
     L.lca_swa_merge.restype = i32

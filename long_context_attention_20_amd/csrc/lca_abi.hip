@@ -29,12 +29,23 @@ size_t index_topk_workspace(int rows, int64_t maxN, int k);
 int launch_index_score(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
                        const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
                        float* scores, void* ws, int dtype, hipStream_t stream);
+int launch_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                              const int32_t* q_pos, int B, int HI, int dI, int k, int m, int w, int64_t maxN,
+                              const lca_compress_stream* idx_stream, const lca_compress_stream* kv_streams, int n_kv,
+                              const int64_t* tok_off, const int64_t* done_len, float eps, float* scores, void* ws,
+                              int dtype, hipStream_t stream);
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
-int launch_attention(int src, const void* q, const void* kv, const int64_t* off, const int32_t* idx,
-                     const int32_t* q_pos, int B, int Tq, int H, int D, int k, int m2, int w2, int W,
-                     float scale, float eps, int n_split, float* o_part, float* lse, int dtype,
-                     hipStream_t stream);
+int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
+                     int H, int D, float scale, float eps, int dtype, hipStream_t stream);
+
+static lca_attn_source make_source(int kind, const void* kv, const int64_t* off, const int32_t* idx, int k, int m2,
+                                   int w2, int W, int n_split, float* o_part, float* lse) {
+  lca_attn_source s{};
+  s.kind = kind; s.kv = kv; s.off = off; s.idx = idx; s.k = k; s.m2 = m2; s.w2 = w2; s.W = W;
+  s.n_split = n_split; s.o_part = o_part; s.lse = lse;
+  return s;
+}
 int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, const float* win_lse,
                  const float* sink, int rows, int H, int D, void* out, int dtype, hipStream_t stream);
 
@@ -96,15 +107,7 @@ const char* lca_last_error(void) { return g_last_error.c_str(); }
 
 int lca_version(void) { return 100; }
 
-int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int64_t* tok_off,
-                    const int64_t* done_len, int B, float eps, int dtype, void* stream) {
-  LCA_REQUIRE(streams != nullptr, LCA_ERR_INVALID_ARG, "kv_compress: streams is NULL");
-  LCA_REQUIRE(n_streams >= 1 && n_streams <= 4, LCA_ERR_INVALID_ARG, "kv_compress: n_streams=%d not in [1,4]",
-              n_streams);
-  LCA_REQUIRE(tok_off != nullptr, LCA_ERR_INVALID_ARG, "kv_compress: tok_off is NULL");
-  LCA_REQUIRE(B >= 1, LCA_ERR_INVALID_ARG, "kv_compress: B=%d", B);
-  LCA_REQUIRE(valid_dtype(dtype), LCA_ERR_INVALID_ARG, "kv_compress: dtype=%d", dtype);
-  LCA_REQUIRE(std::isfinite(eps) && eps >= 0.f, LCA_ERR_INVALID_ARG, "kv_compress: eps must be finite and >= 0");
+static int check_streams(const lca_compress_stream* streams, int n_streams, int dtype) {
   const int VE = dtype == LCA_BF16 ? 8 : 4;
   for (int k = 0; k < n_streams; ++k) {
     const lca_compress_stream& s = streams[k];
@@ -121,6 +124,20 @@ int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int
     LCA_REQUIRE(s.rmsnorm == 0 || s.rmsnorm == 1, LCA_ERR_INVALID_ARG, "kv_compress: rmsnorm");
     LCA_REQUIRE(s.max_entries >= 0, LCA_ERR_INVALID_ARG, "kv_compress: max_entries < 0");
   }
+  return LCA_OK;
+}
+
+int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int64_t* tok_off,
+                    const int64_t* done_len, int B, float eps, int dtype, void* stream) {
+  LCA_REQUIRE(streams != nullptr, LCA_ERR_INVALID_ARG, "kv_compress: streams is NULL");
+  LCA_REQUIRE(n_streams >= 1 && n_streams <= 4, LCA_ERR_INVALID_ARG, "kv_compress: n_streams=%d not in [1,4]",
+              n_streams);
+  LCA_REQUIRE(tok_off != nullptr, LCA_ERR_INVALID_ARG, "kv_compress: tok_off is NULL");
+  LCA_REQUIRE(B >= 1, LCA_ERR_INVALID_ARG, "kv_compress: B=%d", B);
+  LCA_REQUIRE(valid_dtype(dtype), LCA_ERR_INVALID_ARG, "kv_compress: dtype=%d", dtype);
+  LCA_REQUIRE(std::isfinite(eps) && eps >= 0.f, LCA_ERR_INVALID_ARG, "kv_compress: eps must be finite and >= 0");
+  int rc = check_streams(streams, n_streams, dtype);
+  if (rc != LCA_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return finish(launch_compress(streams, n_streams, tok_off, done_len, B, eps, dtype, st), st, "kv_compress");
 }
@@ -162,6 +179,35 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
   return finish(launch_index_score(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries, scores, ws,
                                    dtype, st),
                 st, "csa_index_score");
+}
+
+int lca_csa_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                               const int32_t* q_pos, int B, int H_I, int d_I, int k, int m, int w,
+                               int64_t max_entries, const lca_compress_stream* idx_stream,
+                               const lca_compress_stream* kv_streams, int n_kv, const int64_t* tok_off,
+                               const int64_t* done_len, float eps, float* scores, void* ws, size_t ws_bytes,
+                               int dtype, void* stream) {
+  int rc = check_index("csa_index_score_append", true, p, omega, ikey, csa_off, q_pos, B, 1, H_I, d_I, k, m, w,
+                       max_entries, ws, ws_bytes, dtype);
+  if (rc != LCA_OK) return rc;
+  LCA_REQUIRE(idx_stream != nullptr && tok_off != nullptr && done_len != nullptr, LCA_ERR_INVALID_ARG,
+              "csa_index_score_append: idx_stream, tok_off and done_len are required");
+  LCA_REQUIRE(n_kv >= 0 && n_kv <= 4 && (n_kv == 0 || kv_streams != nullptr), LCA_ERR_INVALID_ARG,
+              "csa_index_score_append: n_kv=%d not in [0,4] (or kv_streams is NULL)", n_kv);
+  LCA_REQUIRE(idx_stream->out == ikey && idx_stream->ent_off == csa_off && idx_stream->C == d_I &&
+                  idx_stream->m == m && idx_stream->w == w,
+              LCA_ERR_INVALID_ARG,
+              "csa_index_score_append: idx_stream must write ikey, packed by csa_off, with C = d_I, m and w");
+  LCA_REQUIRE(std::isfinite(eps) && eps >= 0.f, LCA_ERR_INVALID_ARG,
+              "csa_index_score_append: eps must be finite and >= 0");
+  rc = check_streams(idx_stream, 1, dtype);
+  if (rc == LCA_OK && n_kv > 0) rc = check_streams(kv_streams, n_kv, dtype);
+  if (rc != LCA_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_index_score_append(p, omega, ikey, csa_off, q_pos, B, H_I, d_I, k, m, w, max_entries,
+                                          idx_stream, kv_streams, n_kv, tok_off, done_len, eps, scores, ws, dtype,
+                                          st),
+                st, "csa_index_score_append");
 }
 
 int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
@@ -211,10 +257,9 @@ int lca_csa_sparse_attn(const void* q, const void* kv_csa, const int64_t* csa_of
   if (rc != LCA_OK) return rc;
   LCA_REQUIRE(k >= 1 && k <= 65536, LCA_ERR_INVALID_ARG, "csa_sparse_attn: k=%d", k);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // q_pos is not used by the gathered source; pass idx to keep the pointer valid
-  return finish(launch_attention(1, q, kv_csa, csa_off, idx, reinterpret_cast<const int32_t*>(idx), B, Tq, H, D,
-                                 k, 1, 1, 0, scale, eps, n_split, o_part, lse, dtype, st),
-                st, "csa_sparse_attn");
+  const lca_attn_source src = make_source(LCA_SRC_GATHER, kv_csa, csa_off, idx, k, 1, 1, 0, n_split, o_part, lse);
+  // q_pos is not read by the gathered source
+  return finish(launch_attention(&src, 1, q, nullptr, B, Tq, H, D, scale, eps, dtype, st), st, "csa_sparse_attn");
 }
 
 int lca_hca_attn(const void* q, const void* kv_hca, const int64_t* hca_off, const int32_t* q_pos, int B, int Tq,
@@ -225,9 +270,9 @@ int lca_hca_attn(const void* q, const void* kv_hca, const int64_t* hca_off, cons
   LCA_REQUIRE(m2 >= 1 && w2 >= 1, LCA_ERR_INVALID_ARG, "hca_attn: m2=%d w2=%d", m2, w2);
   LCA_REQUIRE(max_entries >= 0, LCA_ERR_INVALID_ARG, "hca_attn: max_entries < 0");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  return finish(launch_attention(0, q, kv_hca, hca_off, nullptr, q_pos, B, Tq, H, D, 0, m2, w2, 0, scale, eps,
-                                 n_split, o_part, lse, dtype, st),
-                st, "hca_attn");
+  const lca_attn_source src = make_source(LCA_SRC_DENSE, kv_hca, hca_off, nullptr, 0, m2, w2, 0, n_split, o_part,
+                                          lse);
+  return finish(launch_attention(&src, 1, q, q_pos, B, Tq, H, D, scale, eps, dtype, st), st, "hca_attn");
 }
 
 int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int32_t* q_pos, int B, int Tq, int H,
@@ -236,9 +281,33 @@ int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int
   if (rc != LCA_OK) return rc;
   LCA_REQUIRE(W >= 1, LCA_ERR_INVALID_ARG, "swa_attn: W=%d must be >= 1", W);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  return finish(launch_attention(2, q, x, tok_off, nullptr, q_pos, B, Tq, H, D, 0, 1, 1, W, scale, eps, 1, o_part,
-                                 lse, dtype, st),
-                st, "swa_attn");
+  const lca_attn_source src = make_source(LCA_SRC_WINDOW, x, tok_off, nullptr, 0, 1, 1, W, 1, o_part, lse);
+  return finish(launch_attention(&src, 1, q, q_pos, B, Tq, H, D, scale, eps, dtype, st), st, "swa_attn");
+}
+
+int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
+                    int H, int D, float scale, float eps, int dtype, void* stream) {
+  LCA_REQUIRE(srcs != nullptr && n_src >= 1 && n_src <= 3, LCA_ERR_INVALID_ARG,
+              "hybrid_attn: n_src=%d not in [1,3] (or srcs is NULL)", n_src);
+  bool need_pos = false;
+  for (int i = 0; i < n_src; ++i) {
+    const lca_attn_source& x = srcs[i];
+    LCA_REQUIRE(x.kind == LCA_SRC_DENSE || x.kind == LCA_SRC_GATHER || x.kind == LCA_SRC_WINDOW,
+                LCA_ERR_INVALID_ARG, "hybrid_attn: source %d has kind %d", i, x.kind);
+    int rc = check_attn("hybrid_attn", q, x.kv, x.off, x.kind == LCA_SRC_GATHER ? (const void*)x.idx : q, B, Tq, H,
+                        D, scale, eps, x.n_split, x.o_part, x.lse, dtype);
+    if (rc != LCA_OK) return rc;
+    if (x.kind == LCA_SRC_GATHER)
+      LCA_REQUIRE(x.k >= 1 && x.k <= 65536, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: k=%d", i, x.k);
+    if (x.kind == LCA_SRC_DENSE)
+      LCA_REQUIRE(x.m2 >= 1 && x.w2 >= 1, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: m2=%d w2=%d", i, x.m2, x.w2);
+    if (x.kind == LCA_SRC_WINDOW)
+      LCA_REQUIRE(x.W >= 1, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: W=%d must be >= 1", i, x.W);
+    need_pos = need_pos || x.kind != LCA_SRC_GATHER;
+  }
+  LCA_REQUIRE(!need_pos || q_pos != nullptr, LCA_ERR_INVALID_ARG, "hybrid_attn: q_pos is NULL");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_attention(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype, st), st, "hybrid_attn");
 }
 
 size_t lca_swa_merge_workspace(int n_rows, int H, int D) {
@@ -278,8 +347,8 @@ int lca_swa_merge(const void* q, const void* x, const int64_t* tok_off, const in
                 "swa_merge: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     wo = reinterpret_cast<float*>(ws);
     wl = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (((size_t)rows * H * D * 4 + 255) & ~(size_t)255));
-    int rc = launch_attention(2, q, x, tok_off, nullptr, q_pos, B, Tq, H, D, 0, 1, 1, W, scale, eps, 1, wo, wl,
-                              dtype, st);
+    const lca_attn_source src = make_source(LCA_SRC_WINDOW, x, tok_off, nullptr, 0, 1, 1, W, 1, wo, wl);
+    int rc = launch_attention(&src, 1, q, q_pos, B, Tq, H, D, scale, eps, dtype, st);
     if (rc != LCA_OK) return finish(rc, st, "swa_merge(window)");
   }
   LCA_REQUIRE(n_parts > 0 || W > 0 || sink != nullptr, LCA_ERR_INVALID_ARG, "swa_merge: nothing to merge");

@@ -31,38 +31,60 @@ namespace lca {
 
 enum { SRC_DENSE = 0, SRC_GATHER = 1, SRC_WINDOW = 2 };
 
-struct AttnParams {
-  const void* q;        // [rows, H, D]
-  const void* kv;       // cache rows or raw rows
+// One key source of a launch; its splits take blockIdx.x in
+// [block_begin, block_begin + n_split).
+struct AttnSrc {
+  const void* kv;       // cache rows (DENSE, GATHER) or raw rows (WINDOW)
   const int64_t* off;   // [B+1] row offsets of kv
   const int32_t* idx;   // GATHER: [rows, k]
-  const int32_t* q_pos; // [rows]
-  int src;
-  int Tq, H, D;
+  int kind;             // SRC_*
   int k;                // GATHER slots per row
   int m2, w2;           // DENSE visibility
   int W;                // WINDOW length
-  float scale, eps;
   int n_split;
-  int rows;
+  int block_begin;
   float* o_part;        // [n_split, rows, H, D]
   float* lse;           // [n_split, rows, H]
 };
 
-// Number of keys of query row r and its first raw row (WINDOW) -------------
-__device__ __forceinline__ int64_t attn_keys(const AttnParams& a, int r, int64_t* first, int64_t* nseq_out) {
+constexpr int kMaxSrc = 3;
+
+struct AttnParams {
+  const void* q;        // [rows, H, D]
+  const int32_t* q_pos; // [rows]
+  int Tq, H, D, rows;
+  float scale, eps;
+  int n_src;
+  int n_x;              // splits of all sources (blocks per row and head block)
+  int n_hb;             // head blocks per row (matrix-core path)
+  AttnSrc s[kMaxSrc];
+};
+
+// Source of split column bx (uniform) and the split inside it.
+__device__ __forceinline__ int attn_source(const AttnParams& a, int bx, int* split) {
+  int si = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxSrc; ++k)
+    if (k < a.n_src && bx >= a.s[k].block_begin) si = k;
+  *split = bx - a.s[si].block_begin;
+  return si;
+}
+
+// Number of keys of query row r and its first row in kv -------------------
+__device__ __forceinline__ int64_t attn_keys(const AttnParams& a, const AttnSrc& s, int r, int64_t* first,
+                                             int64_t* nseq_out) {
   const int b = r / a.Tq;
-  const int64_t base = a.off[b];
-  const int64_t nseq = a.off[b + 1] - base;
+  const int64_t base = s.off[b];
+  const int64_t nseq = s.off[b + 1] - base;
   *first = base;
   *nseq_out = nseq;
-  if (a.src == SRC_GATHER) return a.k;
+  if (s.kind == SRC_GATHER) return s.k;
   const int64_t i = a.q_pos[r];
-  if (a.src == SRC_DENSE) {
-    int64_t n = n_windows(i + 1, a.m2, a.w2);
+  if (s.kind == SRC_DENSE) {
+    int64_t n = n_windows(i + 1, s.m2, s.w2);
     return n < nseq ? n : nseq;
   }
-  int64_t lo = i - a.W + 1;
+  int64_t lo = i - s.W + 1;
   if (lo < 0) lo = 0;
   int64_t hi = i < nseq - 1 ? i : nseq - 1;
   *first = base + lo;
@@ -70,9 +92,9 @@ __device__ __forceinline__ int64_t attn_keys(const AttnParams& a, int r, int64_t
 }
 
 // Global row of key t (or -1 when the slot is unused or out of range).
-__device__ __forceinline__ int64_t attn_row(const AttnParams& a, int r, int64_t first, int64_t nseq, int64_t t) {
-  if (a.src == SRC_GATHER) {
-    const int32_t j = a.idx[(int64_t)r * a.k + t];
+__device__ __forceinline__ int64_t attn_row(const AttnSrc& s, int r, int64_t first, int64_t nseq, int64_t t) {
+  if (s.kind == SRC_GATHER) {
+    const int32_t j = s.idx[(int64_t)r * s.k + t];
     return (j < 0 || j >= nseq) ? -1 : first + j;
   }
   return first + t;
@@ -81,18 +103,7 @@ __device__ __forceinline__ int64_t attn_row(const AttnParams& a, int r, int64_t 
 // ============================================================ matrix cores
 
 constexpr int kTile = 32;       // keys per tile
-constexpr int kIdxLds = 4096;   // gathered indices staged per block
-
-template <int D>
-struct MfmaCfg {
-  static constexpr int KS = D / 32;                // k-steps of S (32 dims each)
-  static constexpr int DB = D / 16;                // 16-dim blocks of O
-  static constexpr int PITCH = D + 8;              // bf16 elements per LDS row
-  static constexpr int VPR = D / 8;                // 16-byte vectors per row
-  static constexpr int LOADS = kTile * VPR / 256;  // per thread per tile
-  static constexpr int KB = KS < 4 ? KS : 4;       // k-steps per operand batch
-  static constexpr int OB = DB < 4 ? DB : 4;       // dim blocks per operand batch
-};
+constexpr int kIdxLds = 2048;   // gathered indices staged per block
 
 typedef short s4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4_t lds_s4_t;
@@ -106,76 +117,93 @@ __device__ __forceinline__ uint4 pack_tr(const s4_t lo, const s4_t hi) {
   return v;
 }
 
-// Block: 4 waves, 32 query heads of one query row.  Wave w owns heads
-// 16*(w%2) .. +15 and the dim half (w/2) of D: it computes the S^T partial over
-// its half of D, adds its partner's half through LDS (same order in both, so
-// both hold identical logits), runs the online softmax and accumulates O^T
-// for its D/2 dims.  Halving the per-wave query and accumulator state lets
-// two or three independent blocks share a CU, so that the latency-bound
-// phases of one block (staging, exchange, softmax) overlap the matrix-core
-// phases of another.
-constexpr int kAttnThreads = 256;
+// Block: 8 waves = 2 teams x 4 waves, 32 query heads of one query row, one
+// key source (chosen per block).  Team t takes the tiles t, t+2, ... of the
+// block's key range; in a team, wave w owns heads 16*(w%2) .. +15 and the dim
+// half (w/2) of D: it computes the S^T partial over its half of D, adds its
+// partner's half through LDS (same order in both, so both hold identical
+// logits), runs the online softmax and accumulates O^T for its D/2 dims.  At
+// the end the two teams' softmax states meet in LDS, so a block emits one
+// partial for twice the keys of one team.
+//
+// A round costs two block barriers: tiles are double-buffered per team (a
+// buffer is rewritten two rounds after it was read, with both barriers of the
+// round between), the key-validity mask comes from a ballot, and window rows
+// are RMS-normalised in registers before they are stored (a wave's loads of
+// one tile hold whole rows).
+constexpr int kAttnThreads = 512;
+constexpr int kTeamThreads = 256;
 constexpr int kAttnHeads = 32;      // query heads per block
 
-template <int D, int SRC>
+template <int D>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnParams a) {
   constexpr int DH = D / 2;                 // dims per wave
   constexpr int KS = DH / 32;               // k-steps of the S partial
   constexpr int DB = DH / 16;               // 16-dim blocks of O per wave
   constexpr int PITCH = D + 8;              // bf16 elements per LDS row
-  constexpr int VPR = D / 8;                // 16-byte vectors per row
-  constexpr int LOADS = (kTile * VPR + kAttnThreads - 1) / kAttnThreads;
-  constexpr bool PARTIAL = kTile * VPR < kAttnThreads;  // some threads stage nothing
+  constexpr int VPR = D / 8;                // 16-byte vectors per row (a divisor of 64)
+  constexpr int LOADS = kTile * VPR / kTeamThreads;
+  static_assert(LOADS * kTeamThreads == kTile * VPR, "a tile must split evenly over a team");
   constexpr int KB = KS < 2 ? KS : 2;       // k-steps per operand batch
   constexpr int OB = DB < 4 ? DB : 4;       // dim blocks per operand batch
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * PITCH];
-  __shared__ int32_t sidx[SRC == SRC_GATHER ? kIdxLds : 1];
-  __shared__ float sx[4][8][64];            // S partial exchange
-  __shared__ float qss[4][16];              // query sum-of-squares exchange
-  __shared__ uint32_t tile_valid;
-  const int r = blockIdx.z;
-  const int split = blockIdx.x;
+  constexpr int TILE_ELEMS = kTile * PITCH;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][TILE_ELEMS];  // [team][buffer]
+  __shared__ int32_t sidx[kIdxLds];
+  __shared__ float sx[2][4][8][64];         // S partial exchange, per team
+  __shared__ float qss[2][4][16];           // query sum-of-squares exchange, per team
+  // 1-D grid, XCD-aware: workgroups go to the 8 XCDs round-robin by linear
+  // id, so the n_hb head blocks of one (row, split) unit take ids 8 apart and
+  // share an XCD's L2 for the keys they all read
+  const int xcd = blockIdx.x & 7;
+  const int jj = blockIdx.x >> 3;
+  const int hb = jj % a.n_hb;
+  const int unit = (jj / a.n_hb) * 8 + xcd;
+  if (unit >= a.rows * a.n_x) return;  // padding of the last group (uniform)
+  const int r = unit / a.n_x;
+  int split;
+  const int si = attn_source(a, unit % a.n_x, &split);
+  const AttnSrc& S = a.s[si];
+  const int kind = S.kind;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int team = wave >> 2, wt = wave & 3;
+  const int tt = threadIdx.x & (kTeamThreads - 1);  // thread index inside the team
   const int c16 = lane & 15, g = lane >> 4;
-  const int hq = wave & 1, dh = wave >> 1;
-  const int h0 = blockIdx.y * kAttnHeads + hq * 16;
+  const int hq = wt & 1, dh = wt >> 1;
+  const int hbase = hb * kAttnHeads;
+  const int h0 = hbase + hq * 16;
   const bool wave_on = h0 < a.H;  // H is a multiple of 16; uniform per wave pair
   const int h = h0 + c16;
   const int d0 = dh * DH;         // first dim of this wave
 
   int64_t first, nseq;
-  const int64_t n = attn_keys(a, r, &first, &nseq);
+  const int64_t n = attn_keys(a, S, r, &first, &nseq);
   const int64_t ntiles = (n + kTile - 1) / kTile;
-  const int64_t tps = (ntiles + a.n_split - 1) / a.n_split;
+  const int64_t tps = (ntiles + S.n_split - 1) / S.n_split;
   const int64_t tb = (int64_t)split * tps;
   const int64_t te = min(ntiles, tb + tps);
   const int64_t kbase = tb * kTile;
+  const int64_t rounds = (te > tb && nseq > 0) ? (te - tb + 1) / 2 : 0;  // uniform over the block
 
-  if (SRC == SRC_GATHER) {
-    const int64_t cnt = min((te - tb) * kTile, n - kbase);
-    for (int i = threadIdx.x; i < cnt; i += kAttnThreads) {
-      const int32_t j = a.idx[(int64_t)r * a.k + kbase + i];
-      sidx[i] = (j < 0 || j >= nseq) ? -1 : j;
-    }
-  }
-
-
-  // --- tile staging: loads are unconditional (invalid keys read a clamped
-  // valid row) and masked when stored
+  // --- tile staging (per team): loads are unconditional (invalid keys read a
+  // clamped valid row) and zeroed when stored
   uint4 stage[LOADS];
   uint32_t okbits = 0;
-  const uint16_t* kvp = reinterpret_cast<const uint16_t*>(a.kv);
+  const uint16_t* kvp = reinterpret_cast<const uint16_t*>(S.kv);
+  auto key_ok = [&](int64_t key) -> bool {
+    if (key >= n) return false;
+    return kind != SRC_GATHER || sidx[key - kbase] >= 0;
+  };
   auto load_tile = [&](int64_t t) {
     okbits = 0;
+    if (t >= te) return;
 #pragma unroll
     for (int v = 0; v < LOADS; ++v) {
-      const int id = threadIdx.x + kAttnThreads * v;
+      const int id = tt + kTeamThreads * v;
       const int row = id / VPR, vec = id % VPR;
-      if (PARTIAL && row >= kTile) break;
       const int64_t key = t * kTile + row;
       bool ok = key < n;
       int64_t off;
-      if (SRC == SRC_GATHER) {
+      if (kind == SRC_GATHER) {
         const int32_t j = ok ? sidx[key - kbase] : -1;
         ok = j >= 0;
         off = ok ? j : 0;
@@ -186,72 +214,55 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       stage[v] = *reinterpret_cast<const uint4*>(kvp + (first + off) * D + vec * 8);
     }
   };
-  auto store_tile = [&]() {
-    uint32_t mask = 0;
+  auto store_tile = [&](uint16_t* tile) {
+    if (kind == SRC_WINDOW) {
+      // RMS-normalise each row over D: the VPR lanes holding a row are
+      // consecutive lanes of one wave
 #pragma unroll
-    for (int v = 0; v < LOADS; ++v) {
-      const int id = threadIdx.x + kAttnThreads * v;
-      const int row = id / VPR, vec = id % VPR;
-      if (PARTIAL && row >= kTile) break;
-      const bool ok = (okbits >> v) & 1u;
-      *reinterpret_cast<uint4*>(&tile[row * PITCH + vec * 8]) = ok ? stage[v] : make_uint4(0, 0, 0, 0);
-      if (vec == 0 && ok) mask |= 1u << row;
-    }
-    if (threadIdx.x == 0) tile_valid = 0;
-    __syncthreads();
-    if (mask) atomicOr(&tile_valid, mask);
-    if (SRC == SRC_WINDOW) {
-      // RMS-normalise each row over D in place: TPR threads per row
-      __syncthreads();
-      constexpr int TPR = VPR < 16 ? VPR : 16;
-      constexpr int PER = D / TPR;                     // elements per thread, a multiple of 8
-      constexpr int RPP = kAttnThreads / TPR;          // rows per pass
-      const int part = threadIdx.x % TPR;
-#pragma unroll
-      for (int row0 = 0; row0 < kTile; row0 += RPP) {
-        const int row = row0 + threadIdx.x / TPR;
-        uint4* rp = reinterpret_cast<uint4*>(&tile[(row < kTile ? row : 0) * PITCH + part * PER]);
-        uint4 vals[PER / 8];
+      for (int v = 0; v < LOADS; ++v) {
+        float f[8];
+        BF16::unpack(stage[v], f);
         float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < PER / 8; ++i) {
-          vals[i] = rp[i];
-          float f[8];
-          BF16::unpack(vals[i], f);
+        for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+        ss = lane_group_sum<VPR>(ss);
+        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-        }
-#pragma unroll
-        for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
-        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-        if (row < kTile) {
-#pragma unroll
-          for (int i = 0; i < PER / 8; ++i) {
-            float f[8];
-            BF16::unpack(vals[i], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] *= inv;
-            rp[i] = BF16::pack(f);
-          }
-        }
+        for (int e = 0; e < 8; ++e) f[e] *= inv;
+        stage[v] = BF16::pack(f);
       }
+    }
+#pragma unroll
+    for (int v = 0; v < LOADS; ++v) {
+      const int id = tt + kTeamThreads * v;
+      const int row = id / VPR, vec = id % VPR;
+      const bool ok = (okbits >> v) & 1u;
+      *reinterpret_cast<uint4*>(&tile[row * PITCH + vec * 8]) = ok ? stage[v] : make_uint4(0, 0, 0, 0);
     }
   };
 
-  // dense and window keys do not depend on staged indices: request the first
-  // tile before the query loads
-  if (SRC != SRC_GATHER && tb < te && nseq > 0) load_tile(tb);
-
-  // --- normalised query: this wave's heads, its half of D (B operand of S^T)
-  bf16x8_t qb[KS];
+  // --- prologue: the query (and, for gathered keys, the block's indices) in
+  // one memory round trip; dense and window keys do not depend on staged
+  // indices, so their first tile is requested first
+  if (kind != SRC_GATHER && rounds > 0) load_tile(tb + team);
   uint4 qraw[KS];
+  if (wave_on) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h) * D + d0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32 + g * 8);
+  }
+  if (kind == SRC_GATHER && rounds > 0) {
+    const int64_t cnt = min((te - tb) * kTile, n - kbase);
+    for (int i = threadIdx.x; i < cnt; i += kAttnThreads) {
+      const int32_t j = S.idx[(int64_t)r * S.k + kbase + i];
+      sidx[i] = (j < 0 || j >= nseq) ? -1 : j;
+    }
+  }
   {
     float ss = 0.f;
     if (wave_on) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h) * D + d0;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32 + g * 8);
         float f[8];
         BF16::unpack(qraw[ks], f);
 #pragma unroll
@@ -260,12 +271,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    if (g == 0) qss[wave][c16] = ss;
+    if (g == 0) qss[team][wt][c16] = ss;
   }
   __syncthreads();  // sidx and qss ready
+  if (kind == SRC_GATHER && rounds > 0) load_tile(tb + team);
+  bf16x8_t qb[KS];
   if (wave_on) {
-    const float ss = qss[hq][c16] + qss[hq + 2][c16];
-    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+    const float ss = qss[team][hq][c16] + qss[team][hq + 2][c16];
+    const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float f[8];
@@ -281,14 +294,19 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   for (int d = 0; d < DB; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
-  if (SRC == SRC_GATHER && tb < te && nseq > 0) load_tile(tb);
-  for (int64_t t = tb; t < te && nseq > 0; ++t) {
-    store_tile();
-    __syncthreads();
-    if (t + 1 < te) load_tile(t + 1);
+
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    const int64_t t = tb + 2 * rd + team;   // this team's tile (may be past te)
+    const bool active = t < te;
+    uint16_t* tile = tiles[team][rd & 1];
+    store_tile(tile);
+    // validity of the tile's 32 keys, one per lane of the low half-wave
+    const uint64_t vm = __ballot(lane < kTile && active && key_ok(t * kTile + lane));
+    __syncthreads();  // A: tile in LDS
+    load_tile(t + 2);
     // ---- S^T partial over this wave's dims, entries 0-15 (s0) and 16-31 (s1)
     f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
-    if (wave_on) {
+    if (wave_on && active) {
       const uint16_t* krow0 = &tile[c16 * PITCH + d0 + g * 8];
       const uint16_t* krow1 = krow0 + 16 * PITCH;
       uint4 kbuf[2][KB][2];
@@ -323,19 +341,16 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     const f32x4 p0 = s0a + s0b, p1 = s1a + s1b;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sx[wave][i][lane] = p0[i];
-      sx[wave][4 + i][lane] = p1[i];
+      sx[team][wt][i][lane] = p0[i];
+      sx[team][wt][4 + i][lane] = p1[i];
     }
-    __syncthreads();
-    if (wave_on) {
-      const int wlo = hq;       // dims [0, D/2)
-      const int whi = hq + 2;   // dims [D/2, D)
+    __syncthreads();  // B: S partials exchanged
+    if (wave_on && active) {
       float lg[8];
-      const uint32_t vm = tile_valid;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float s0 = sx[wlo][i][lane] + sx[whi][i][lane];
-        const float s1 = sx[wlo][4 + i][lane] + sx[whi][4 + i][lane];
+        const float s0 = sx[team][hq][i][lane] + sx[team][hq + 2][i][lane];
+        const float s1 = sx[team][hq][4 + i][lane] + sx[team][hq + 2][4 + i][lane];
         lg[i] = ((vm >> (4 * g + i)) & 1u) ? s0 * sl2 : -INFINITY;
         lg[4 + i] = ((vm >> (16 + 4 * g + i)) & 1u) ? s1 * sl2 : -INFINITY;
       }
@@ -344,17 +359,20 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, lg[i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      if (m_new != -INFINITY) {  // uniform: masks do not depend on the head
-        const float alpha = exp2f(m_run - m_new);
+      if (tmax != -INFINITY) {  // uniform: masks do not depend on the head
+        // the reference max moves only when a logit exceeds it by more than
+        // 8 (log2 units): p <= 256, and the rescale of O is rare
+        const bool move = tmax > m_run + 8.0f;  // true on the first valid tile
+        const float alpha = move ? exp2f(m_run - tmax) : 1.0f;
+        const float m_ref = move ? tmax : m_run;
         float p[8], psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          p[i] = exp2f(lg[i] - m_new);
+          p[i] = exp2f(lg[i] - m_ref);
           psum += p[i];
         }
         l_run = l_run * alpha + psum;
-        m_run = m_new;
+        m_run = m_ref;
         if (__ballot(alpha != 1.0f)) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) O[db] = O[db] * alpha;
@@ -396,23 +414,58 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
         }
       }
     }
-    __syncthreads();
   }
 
-  if (!wave_on) return;
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  float* op = a.o_part + (((int64_t)split * a.rows + r) * a.H + h) * D + d0;
-  // lane (head c16, g) holds dims d0 + 16*db + 4g .. +3
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    float4 v = make_float4(O[db][0] * inv, O[db][1] * inv, O[db][2] * inv, O[db][3] * inv);
-    *reinterpret_cast<float4*>(op + db * 16 + 4 * g) = v;
+  // --- epilogue: the teams' softmax states meet in LDS; each wave writes its
+  // O scaled by its team's weight into a per-team [head][dim] buffer (in the
+  // free tile memory), and the block stores the sum of the two as one
+  // contiguous run of 32 heads x D floats
+  __shared__ float st_m[2][2][16], st_l[2][2][16];
+  __syncthreads();  // every wave has left the last round: tiles and sx are free
+  {
+    float lg = l_run + __shfl_xor(l_run, 16, 64);
+    lg += __shfl_xor(lg, 32, 64);
+    if (dh == 0 && g == 0) {
+      st_m[team][hq][c16] = m_run;
+      st_l[team][hq][c16] = lg;
+    }
   }
-  if (g == 0 && dh == 0) {
-    const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    a.lse[((int64_t)split * a.rows + r) * a.H + h] = lse;
+  __syncthreads();
+  constexpr int XP = D + 4;  // floats per head row of the exchange buffers
+  static_assert(2 * kAttnHeads * XP * 4 <= 4 * TILE_ELEMS * 2, "epilogue buffers exceed the tile memory");
+  float* ox = reinterpret_cast<float*>(&tiles[0][0][0]);  // [team][32 heads][XP]
+  auto head_state = [&](int hh, float* M, float* f0, float* f1, float* lsum) {
+    const int q2 = hh >> 4, c = hh & 15;
+    const float m0 = st_m[0][q2][c], m1 = st_m[1][q2][c];
+    *M = fmaxf(m0, m1);
+    *f0 = *M == -INFINITY ? 0.f : exp2f(m0 - *M);
+    *f1 = *M == -INFINITY ? 0.f : exp2f(m1 - *M);
+    *lsum = st_l[0][q2][c] * *f0 + st_l[1][q2][c] * *f1;
+  };
+  {
+    float M, f0, f1, lsum;
+    head_state(hq * 16 + c16, &M, &f0, &f1, &lsum);
+    const float w = lsum > 0.f ? (team ? f1 : f0) / lsum : 0.f;
+    float* xp = ox + (team * kAttnHeads + hq * 16 + c16) * XP + d0 + 4 * g;
+    // lane (head c16, g) holds dims d0 + 16*db + 4g .. +3
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<float4*>(xp + db * 16) = make_float4(O[db][0] * w, O[db][1] * w, O[db][2] * w, O[db][3] * w);
+  }
+  __syncthreads();
+  const int nh = min(kAttnHeads, a.H - hbase);
+  float* op = S.o_part + (((int64_t)split * a.rows + r) * a.H + hbase) * D;
+  for (int i = threadIdx.x; i < nh * (D / 4); i += kAttnThreads) {
+    const int hh = i / (D / 4), d = (i % (D / 4)) * 4;
+    const float4 u = *reinterpret_cast<const float4*>(ox + hh * XP + d);
+    const float4 v = *reinterpret_cast<const float4*>(ox + (kAttnHeads + hh) * XP + d);
+    *reinterpret_cast<float4*>(op + (int64_t)i * 4) = make_float4(u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w);
+  }
+  if (threadIdx.x < nh) {
+    float M, f0, f1, lsum;
+    head_state(threadIdx.x, &M, &f0, &f1, &lsum);
+    S.lse[((int64_t)split * a.rows + r) * a.H + hbase + threadIdx.x] =
+        lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
 }
 
@@ -423,12 +476,13 @@ template <typename ET, int DPL>
 __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
   const int r = blockIdx.z;
   const int h = blockIdx.y;
-  const int split = blockIdx.x;
+  int split;
+  const AttnSrc& S = a.s[attn_source(a, blockIdx.x, &split)];
   const int lane = threadIdx.x;
   const int D = a.D;
   int64_t first, nseq;
-  const int64_t n = attn_keys(a, r, &first, &nseq);
-  const int64_t per = (n + a.n_split - 1) / a.n_split;
+  const int64_t n = attn_keys(a, S, r, &first, &nseq);
+  const int64_t per = (n + S.n_split - 1) / S.n_split;
   const int64_t kb = (int64_t)split * per;
   const int64_t ke = min(n, kb + per);
 
@@ -450,16 +504,16 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
   for (int i = 0; i < DPL; ++i) o[i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   for (int64_t t = kb; t < ke; ++t) {
-    const int64_t row = attn_row(a, r, first, nseq, t);
+    const int64_t row = attn_row(S, r, first, nseq, t);
     if (row < 0) continue;
     float kv[DPL];
     float dot = 0.f, ss = 0.f;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
-      kv[i] = ET::load1(a.kv, row * D + lane * DPL + i);
+      kv[i] = ET::load1(S.kv, row * D + lane * DPL + i);
       ss = fmaf(kv[i], kv[i], ss);
     }
-    if (a.src == SRC_WINDOW) {
+    if (S.kind == SRC_WINDOW) {
       ss = wave_sum(ss, 64);
       const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
@@ -477,10 +531,10 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
     for (int i = 0; i < DPL; ++i) o[i] = fmaf(o[i], alpha, p * kv[i]);
   }
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  float* op = a.o_part + (((int64_t)split * a.rows + r) * a.H + h) * D;
+  float* op = S.o_part + (((int64_t)split * a.rows + r) * a.H + h) * D;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) op[lane * DPL + i] = o[i] * inv;
-  if (lane == 0) a.lse[((int64_t)split * a.rows + r) * a.H + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+  if (lane == 0) S.lse[((int64_t)split * a.rows + r) * a.H + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
 }
 
 // ============================================================ merge
@@ -500,97 +554,95 @@ struct MergeParams {
   void* out;
 };
 
-// One block per (row, head): 256 threads = 4 slot groups x 64 lanes; a lane
-// owns D/64 dims (float4 or narrower), a slot group a quarter of the slots,
-// and the groups meet in LDS.  All of a thread's loads are issued together.
+// One block per (row, head, 256-dim part): 256 threads = 4 slot groups x 64
+// lanes; a lane owns 4 consecutive dims (or fewer for D = 64), a slot group
+// every fourth slot.  The slots' addresses are resolved once, one thread per
+// slot, into LDS; then every wave loads all the slots' lse values and its own
+// slots' partials in one batch (one memory round trip), computes the slot
+// weights itself, and the groups' sums meet in LDS.
 constexpr int kMergeGroups = 4;
-constexpr int kMergeSlotsPerGroup = kMaxSlots / kMergeGroups;
+constexpr int kMergeSlotsPerWave = 32;  // partial loads in flight per lane and batch
 
 template <typename ET, int DPL>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
-  __shared__ float wts[kMaxSlots];
   __shared__ float red[kMergeGroups][64 * DPL];
+  __shared__ const float* s_o[kMaxSlots];
+  __shared__ const float* s_l[kMaxSlots];
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int64_t RH = (int64_t)a.rows * a.H;
-  const int64_t rh = blockIdx.x;
+  const int parts_d = (a.D + 64 * DPL - 1) / (64 * DPL);
+  const int64_t rh = blockIdx.x / parts_d;
+  const int dpart = (blockIdx.x % parts_d) * 64 * DPL;
   const int h = (int)(rh % a.H);
-  // slot pointers (cheap: at most kMaxParts parts)
-  auto slot_ptr = [&](int sidx, const float** lse_p, const float** o_p) {
-    int p = 0, s = sidx;
-    while (s >= a.n_split[p]) { s -= a.n_split[p]; ++p; }
-    *lse_p = a.lse[p] + (int64_t)s * RH + rh;
-    *o_p = a.o[p] + ((int64_t)s * RH + rh) * a.D;
-  };
-  // weights, by wave 0
-  if (grp == 0) {
-    float l_loc[kMaxSlots / 64];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kMaxSlots / 64; ++i) {
-      const int sidx = lane + 64 * i;
-      l_loc[i] = -INFINITY;
-      if (sidx < a.n_slots) {
-        const float* lp; const float* op;
-        slot_ptr(sidx, &lp, &op);
-        l_loc[i] = *lp;
-      }
-      mx = fmaxf(mx, l_loc[i]);
-    }
-    mx = wave_max(mx, 64);
-    if (a.sink) mx = fmaxf(mx, a.sink[h]);
-    float den = 0.f;
-    if (mx != -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < kMaxSlots / 64; ++i) den += l_loc[i] == -INFINITY ? 0.f : expf(l_loc[i] - mx);
-    }
-    den = wave_sum(den, 64);
-    if (a.sink && mx != -INFINITY) den += expf(a.sink[h] - mx);
-    const float lse = mx != -INFINITY ? mx + logf(den) : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kMaxSlots / 64; ++i) {
-      const int sidx = lane + 64 * i;
-      if (sidx < a.n_slots) wts[sidx] = (l_loc[i] != -INFINITY && lse != -INFINITY) ? expf(l_loc[i] - lse) : 0.f;
-    }
+  for (int i = threadIdx.x; i < a.n_slots; i += blockDim.x) {
+    int p = 0, t = i;
+    while (p + 1 < a.n_parts && t >= a.n_split[p]) { t -= a.n_split[p]; ++p; }
+    s_o[i] = a.o[p] + ((int64_t)t * RH + rh) * a.D + dpart;
+    s_l[i] = a.lse[p] + (int64_t)t * RH + rh;
   }
-  // this group's slots: grp, grp + 4, ...
+  __syncthreads();
   const int nmine = (a.n_slots - grp + kMergeGroups - 1) / kMergeGroups;
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  constexpr int U = 16;
-  for (int base = 0; base < nmine; base += U) {
-    float v[U][DPL];
+  float lse_tot = -INFINITY;
+  for (int base = 0; base == 0 || base < nmine; base += kMergeSlotsPerWave) {
+    // lse of every slot (lane l: slots l, l + 64, ...; first batch only) and
+    // this group's partials, all in flight together
+    float l_loc[kMaxSlots / 64];
+    if (base == 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + u;
-      const int sidx = grp + kMergeGroups * (j < nmine ? j : 0);
-      const float* lp; const float* op;
-      slot_ptr(sidx, &lp, &op);
-      if constexpr (DPL == 8) {
-        const float4 x0 = *reinterpret_cast<const float4*>(op + lane * 8);
-        const float4 x1 = *reinterpret_cast<const float4*>(op + lane * 8 + 4);
-        v[u][0] = x0.x; v[u][1] = x0.y; v[u][2] = x0.z; v[u][3] = x0.w;
-        v[u][4] = x1.x; v[u][5] = x1.y; v[u][6] = x1.z; v[u][7] = x1.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) v[u][i] = op[lane * DPL + i];
+      for (int i = 0; i < kMaxSlots / 64; ++i) {
+        const int sidx = lane + 64 * i;
+        l_loc[i] = sidx < a.n_slots ? *s_l[sidx] : -INFINITY;
       }
     }
-    if (base == 0) __syncthreads();  // weights ready (every thread reaches this once)
+    float v[kMergeSlotsPerWave][DPL];
+    float lw[kMergeSlotsPerWave];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kMergeSlotsPerWave; ++u) {
       const int j = base + u;
-      if (j >= nmine) break;
-      const float wgt = wts[grp + kMergeGroups * j];
+      const bool ok = j < nmine;
+      const int sidx = ok ? grp + kMergeGroups * j : 0;
+      lw[u] = ok ? *s_l[sidx] : -INFINITY;
+      const float* op = (ok ? s_o[sidx] : s_o[0]) + lane * DPL;
+      if constexpr (DPL == 4) {
+        const float4 x = ok ? *reinterpret_cast<const float4*>(op) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) v[u][i] = ok ? op[i] : 0.f;
+      }
+    }
+    if (base == 0) {
+      // total log-sum-exp over every slot and the sink (each wave alike)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kMaxSlots / 64; ++i) mx = fmaxf(mx, l_loc[i]);
+      mx = wave_max(mx, 64);
+      if (a.sink) mx = fmaxf(mx, a.sink[h]);
+      float den = 0.f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < kMaxSlots / 64; ++i) den += l_loc[i] == -INFINITY ? 0.f : expf(l_loc[i] - mx);
+      }
+      den = wave_sum(den, 64);
+      if (a.sink && mx != -INFINITY) den += expf(a.sink[h] - mx);
+      lse_tot = mx != -INFINITY ? mx + logf(den) : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeSlotsPerWave; ++u) {
+      const bool use = lw[u] != -INFINITY && lse_tot != -INFINITY;
+      const float wgt = use ? expf(lw[u] - lse_tot) : 0.f;
 #pragma unroll
       for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wgt, v[u][i], acc[i]);
     }
   }
-  if (nmine <= 0) __syncthreads();
 #pragma unroll
   for (int i = 0; i < DPL; ++i) red[grp][lane * DPL + i] = acc[i];
   __syncthreads();
-  if (grp != 0) return;
+  const int d0 = dpart + lane * DPL;
+  if (grp != 0 || d0 >= a.D) return;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
     float sum = 0.f;
@@ -598,10 +650,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
     for (int g2 = 0; g2 < kMergeGroups; ++g2) sum += red[g2][lane * DPL + i];
     acc[i] = sum;
   }
-  const int64_t off = rh * a.D + lane * DPL;
+  const int64_t off = rh * a.D + d0;
   if constexpr (ET::kBytes == 2) {
-    if constexpr (DPL == 8) {
-      stg16(a.out, off * 2, BF16::pack(acc));
+    if constexpr (DPL == 4) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[0], acc[1]);
+      pk.y = pack_bf16x2(acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = pk;
     } else {
       for (int i = 0; i < DPL; ++i) reinterpret_cast<uint16_t*>(a.out)[off + i] = (uint16_t)f32_to_bf16_bits(acc[i]);
     }
@@ -612,38 +667,52 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
 
 // ============================================================ host
 
-int launch_attention(int src, const void* q, const void* kv, const int64_t* off, const int32_t* idx,
-                     const int32_t* q_pos, int B, int Tq, int H, int D, int k, int m2, int w2, int W,
-                     float scale, float eps, int n_split, float* o_part, float* lse, int dtype,
-                     hipStream_t stream) {
+int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
+                     int H, int D, float scale, float eps, int dtype, hipStream_t stream) {
+  if (n_src < 1 || n_src > kMaxSrc) {
+    set_error("attention: %d key sources, 1 to %d supported", n_src, kMaxSrc);
+    return LCA_ERR_UNSUPPORTED;
+  }
   AttnParams a{};
-  a.q = q; a.kv = kv; a.off = off; a.idx = idx; a.q_pos = q_pos; a.src = src;
-  a.Tq = Tq; a.H = H; a.D = D; a.k = k; a.m2 = m2; a.w2 = w2; a.W = W;
-  a.scale = scale; a.eps = eps; a.n_split = n_split; a.rows = B * Tq;
-  a.o_part = o_part; a.lse = lse;
-  const int rows = B * Tq;
-  if (dtype == LCA_BF16 && H % 16 == 0) {
-    if (src == SRC_GATHER && (int64_t)((k + kTile - 1) / kTile + n_split - 1) / n_split * kTile > kIdxLds) {
-      set_error("attention: n_split=%d leaves more than %d gathered slots per block (k=%d)", n_split, kIdxLds, k);
+  a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
+  a.scale = scale; a.eps = eps; a.n_src = n_src;
+  const bool mfma = dtype == LCA_BF16 && H % 16 == 0;
+  int blocks = 0;
+  for (int i = 0; i < n_src; ++i) {
+    const lca_attn_source& in = srcs[i];
+    AttnSrc& d = a.s[i];
+    d.kv = in.kv; d.off = in.off; d.idx = in.idx; d.kind = in.kind; d.k = in.k; d.m2 = in.m2; d.w2 = in.w2;
+    d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse;
+    d.block_begin = blocks;
+    blocks += in.n_split;
+    if (mfma && in.kind == SRC_GATHER &&
+        (int64_t)((in.k + kTile - 1) / kTile + in.n_split - 1) / in.n_split * kTile > kIdxLds) {
+      set_error("attention: n_split=%d leaves more than %d gathered slots per block (k=%d)", in.n_split, kIdxLds,
+                in.k);
       return LCA_ERR_UNSUPPORTED;
     }
-    dim3 grid((unsigned)n_split, (unsigned)((H + kAttnHeads - 1) / kAttnHeads), (unsigned)rows);
-#define LCA_ATTN(DD)                                                                                             \
-  switch (src) {                                                                                                 \
-    case SRC_DENSE: hipLaunchKernelGGL((attn_mfma<DD, SRC_DENSE>), grid, dim3(kAttnThreads), 0, stream, a); break;       \
-    case SRC_GATHER: hipLaunchKernelGGL((attn_mfma<DD, SRC_GATHER>), grid, dim3(kAttnThreads), 0, stream, a); break;     \
-    default: hipLaunchKernelGGL((attn_mfma<DD, SRC_WINDOW>), grid, dim3(kAttnThreads), 0, stream, a); break;             \
   }
+  const int rows = B * Tq;
+  a.n_x = blocks;
+  a.n_hb = (H + kAttnHeads - 1) / kAttnHeads;
+  if (mfma) {
+    // units of (row, split) in groups of 8 (one per XCD), each with n_hb head blocks
+    const int64_t units = (int64_t)rows * blocks;
+    const int64_t nblk = (units + 7) / 8 * 8 * a.n_hb;
+    if (nblk > 0x7FFFFFFF) {
+      set_error("attention: %lld blocks exceed the grid limit", (long long)nblk);
+      return LCA_ERR_UNSUPPORTED;
+    }
+    dim3 grid((unsigned)nblk);
     switch (D) {
-      case 64: LCA_ATTN(64) break;
-      case 128: LCA_ATTN(128) break;
-      case 256: LCA_ATTN(256) break;
-      case 512: LCA_ATTN(512) break;
+      case 64: hipLaunchKernelGGL((attn_mfma<64>), grid, dim3(kAttnThreads), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL((attn_mfma<128>), grid, dim3(kAttnThreads), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL((attn_mfma<256>), grid, dim3(kAttnThreads), 0, stream, a); break;
+      case 512: hipLaunchKernelGGL((attn_mfma<512>), grid, dim3(kAttnThreads), 0, stream, a); break;
       default: set_error("attention: D=%d not supported", D); return LCA_ERR_UNSUPPORTED;
     }
-#undef LCA_ATTN
   } else {
-    dim3 grid((unsigned)n_split, (unsigned)H, (unsigned)rows);
+    dim3 grid((unsigned)blocks, (unsigned)H, (unsigned)rows);
 #define LCA_VALU(ETy)                                                                      \
   switch (D) {                                                                             \
     case 64: hipLaunchKernelGGL((attn_valu<ETy, 1>), grid, dim3(64), 0, stream, a); break; \
@@ -673,13 +742,19 @@ int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, cons
   a.n_parts = np;
   a.n_slots = ns;
   a.sink = sink; a.rows = rows; a.H = H; a.D = D; a.out = out;
-  dim3 grid((unsigned)((int64_t)rows * H));
+  // (row, head) pairs x 256-dim parts
+  const int64_t nblk = (int64_t)rows * H * (D > 256 ? D / 256 : 1);
+  if (nblk > 0x7FFFFFFF) {
+    set_error("merge: %lld blocks exceed the grid limit", (long long)nblk);
+    return LCA_ERR_UNSUPPORTED;
+  }
+  dim3 grid((unsigned)nblk);
 #define LCA_MERGE(ETy)                                                                            \
   switch (D) {                                                                                    \
     case 64: hipLaunchKernelGGL((merge_kernel<ETy, 1>), grid, dim3(256), 0, stream, a); break;   \
     case 128: hipLaunchKernelGGL((merge_kernel<ETy, 2>), grid, dim3(256), 0, stream, a); break;  \
-    case 256: hipLaunchKernelGGL((merge_kernel<ETy, 4>), grid, dim3(256), 0, stream, a); break;  \
-    case 512: hipLaunchKernelGGL((merge_kernel<ETy, 8>), grid, dim3(256), 0, stream, a); break;  \
+    case 256:                                                                                     \
+    case 512: hipLaunchKernelGGL((merge_kernel<ETy, 4>), grid, dim3(256), 0, stream, a); break;  \
     default: set_error("merge: D=%d not supported", D); return LCA_ERR_UNSUPPORTED;             \
   }
   if (dtype == LCA_BF16) { LCA_MERGE(BF16) } else { LCA_MERGE(F32) }

@@ -19,14 +19,16 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round to nearest even (finite inputs).
+// Round to nearest even: gfx950 converts a pair in one instruction
+// (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f32_to_bf16_bits(f) << 16); }
 
@@ -85,6 +87,52 @@ __device__ __forceinline__ float wave_sum(float v, int width) {
 __device__ __forceinline__ float wave_max(float v, int width) {
   for (int o = width >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f32(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 4 .. 64); every lane of
+// a group gets the same total.  Quad permutes, the half-row and row mirrors
+// (DPP, no LDS traffic), then lane reads across 16-lane rows.  Every lane of
+// the wave must be active.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group of 4 to 64 lanes");
+  v += dpp_f32<0xB1>(v);                          // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);                          // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v += dpp_f32<0x141>(v);   // row_half_mirror
+  if constexpr (N >= 16) v += dpp_f32<0x140>(v);  // row_mirror
+  if constexpr (N == 32) {
+    const float lo = readlane_f32(v, 0) + readlane_f32(v, 16);
+    const float hi = readlane_f32(v, 32) + readlane_f32(v, 48);
+    v = (threadIdx.x & 32) ? hi : lo;
+  } else if constexpr (N == 64) {
+    v = (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+  }
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps with
+// DPP row shifts inside each 16-lane row, then the row broadcasts of lanes 15
+// and 31 into the rows above them.  Every lane of the wave must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_u32<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_u32<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_u32<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_u32<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_u32<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
 }
 
 // ---------------------------------------------------------------- windows

@@ -27,7 +27,7 @@
 // so ties go to the smaller index -- marks every chosen entry in an LDS
 // bitmap and writes the row in ascending index order (deterministic whatever
 // order the lists were filled in), then zeroes the histogram and counters.
-#include "lca_common.h"
+#include "lca_compress.h"
 
 namespace lca {
 
@@ -75,17 +75,17 @@ __device__ __forceinline__ void hist_flush(const uint32_t* lh, uint32_t* gh) {
   }
 }
 
-// bf16, matrix cores.  KS = dI / 32 k-steps.
+// bf16, matrix cores.  KS = dI / 32 k-steps.  Block (cx, r) scores the
+// entries [cx*chunk, min((cx+1)*chunk, lim)) of row r; lh: kHistBins words
+// of LDS.
 template <int KS>
-__global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
-  __shared__ uint32_t lh[kHistBins];
-  const int r = blockIdx.y;
+__device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, int cx, int64_t lim, uint32_t* lh) {
   const int b = r / a.Tq;
   const int64_t e_base = a.csa_off[b];
   const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - e_base);
-  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
-  if (c0 >= nv) return;
-  const int64_t c1 = min(c0 + a.chunk, nv);
+  const int64_t c0 = (int64_t)cx * a.chunk;
+  const int64_t c1 = min(min(c0 + a.chunk, nv), lim);
+  if (c0 >= c1) return;
   const bool do_hist = nv > a.k;
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0;
 
@@ -115,7 +115,8 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
   float* S = a.scores + (int64_t)r * a.max_entries;
   constexpr int U = 8;  // tiles in flight per wave
   const int64_t ntile = (c1 - c0 + 15) / 16;
-  for (int64_t t0 = wave * U; t0 < ntile; t0 += 4 * U) {
+  const int nw = (int)(blockDim.x >> 6);
+  for (int64_t t0 = wave * U; t0 < ntile; t0 += nw * U) {
     uint4 kv[U][KS];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -145,7 +146,146 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
     }
   }
   __syncthreads();
-  if (do_hist) hist_flush(lh, a.hist + ((int64_t)r * a.nstripe + blockIdx.x % a.nstripe) * kHistBins);
+  if (do_hist) hist_flush(lh, a.hist + ((int64_t)r * a.nstripe + cx % a.nstripe) * kHistBins);
+}
+
+template <int KS>
+__global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
+  __shared__ uint32_t lh[kHistBins];
+  score_chunk_mfma<KS>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
+}
+
+// ------------------------------------------------------------------ score + append
+// One decode launch that also appends the entries the new token completes:
+//   blocks [0, ncb):             the compression blocks of the other streams
+//                                (KV entries that only the attention reads);
+//   blocks [ncb, ncb + B):       per sequence, pool each new indexer key,
+//                                store it, and score it against the row's
+//                                indexer query (adding it to the histogram);
+//   blocks [ncb + B, ... + nsb): scores of the entries that existed before
+//                                the token (as index_score_mfma).
+// Blocks are dispatched in index order, so the few long compression blocks
+// start first and overlap the scoring.  No block reads what another block of
+// the launch writes.
+struct AppendIdx {
+  CompressStreamDev s;      // the indexer-key stream (out is the key cache)
+  const int64_t* tok_off;
+  const int64_t* done_len;
+  int ncb;                  // compression blocks
+  int nsb;                  // score blocks
+  int nsx;                  // score blocks per row
+  int B;
+  float eps;
+};
+
+// Sum over aligned groups of n lanes, n in {4, 8, 16, 32} (uniform).
+__device__ __forceinline__ float group_sum_n(float v, int n) {
+  switch (n) {
+    case 4: return lane_group_sum<4>(v);
+    case 8: return lane_group_sum<8>(v);
+    case 16: return lane_group_sum<16>(v);
+    default: return lane_group_sum<32>(v);
+  }
+}
+
+__device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int b) {
+  constexpr int VE = 8;                    // bf16 channels per 16-byte vector
+  const CompressStreamDev& s = ap.s;
+  const int G = s.C / VE;                  // lanes per entry (4 .. 32)
+  const int RG = (int)blockDim.x / G;
+  const int rg = threadIdx.x / G, li = threadIdx.x % G;
+  const int r = b;                         // one query row per sequence
+  const int64_t t0 = ap.tok_off[b];
+  const int64_t e_base = a.csa_off[b];
+  const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - e_base);
+  // every entry the tokens complete is appended (as the compression kernel
+  // does); the visible ones are scored
+  const int64_t n_hi = n_windows(ap.tok_off[b + 1] - t0, s.m, s.w);
+  const int64_t n_lo = n_windows(ap.done_len[b], s.m, s.w);
+  const bool do_hist = nv > a.k;
+  const int64_t rb = (int64_t)s.C * 2;
+  const char* src = reinterpret_cast<const char*>(s.src) + t0 * rb;
+  const char* lg = reinterpret_cast<const char*>(s.logits) + (s.per_channel ? t0 * rb : t0 * 2);
+  const int ch0 = li * VE;
+  // indexer query of this row for this lane's channels, all heads
+  const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p) + (int64_t)r * a.HI * a.dI;
+  for (int64_t j0 = n_lo; j0 < n_hi; j0 += RG) {
+    const int64_t j = j0 + rg;
+    const bool on = j < n_hi;              // uniform over a row group
+    // the same arithmetic, in the same order, as the small-window walk of
+    // the compression kernel: each m-token segment pooled on its own, two
+    // adjacent segments merged when w = 2m
+    const int64_t tb = (on ? j : n_lo) * s.m;
+    PoolState<VE> st[2];
+    const int nseg = s.w == s.m ? 1 : 2;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      st[q].reset();
+      if (q >= nseg) continue;
+      for (int t = q * s.m; t < (q + 1) * s.m; ++t) {
+        float x[VE], z[VE];
+        BF16::unpack(ldg16(src, (tb + t) * rb + ch0 * 2), x);
+        if (s.per_channel) {
+          BF16::unpack(ldg16(lg, (tb + t) * rb + ch0 * 2), z);
+        } else {
+          const float zs = BF16::load1(lg, tb + t);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) z[e] = zs;
+        }
+        st[q].add(z, x);
+      }
+    }
+    if (nseg == 2) st[0].merge(st[1]);
+    float key[VE];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      key[e] = st[0].sn[e] / st[0].se[e];
+      ss = fmaf(key[e], key[e], ss);
+    }
+    if (s.rmsnorm) {
+      ss = wave_sum(ss, G);
+      const float inv = 1.0f / sqrtf(ss / (float)s.C + ap.eps);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) key[e] *= inv;
+    }
+    const uint4 kq = BF16::pack(key);
+    if (on) stg16(s.out, (e_base + j) * rb + ch0 * 2, kq);
+    BF16::unpack(kq, key);                 // the stored (rounded) key is the one scored
+    float score = 0.f;
+    for (int h = 0; h < a.HI; ++h) {
+      float pv[VE];
+      BF16::unpack(*reinterpret_cast<const uint4*>(P + h * a.dI + ch0), pv);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) d = fmaf(pv[e], key[e], d);
+      d = group_sum_n(d, G);
+      score = fmaf(a.omega[(int64_t)r * a.HI + h], fmaxf(d, 0.f), score);
+    }
+    if (on && j < nv && li == 0) {
+      a.scores[(int64_t)r * a.max_entries + j] = score;
+      if (do_hist)
+        atomicAdd(&a.hist[((int64_t)r * a.nstripe + (int)(j % a.nstripe)) * kHistBins + (score_key(score) >> 21)], 1u);
+    }
+  }
+}
+
+template <int KS>
+__global__ __launch_bounds__(kIdxThreads) void index_score_append(IndexParams a, AppendIdx ap, CompressParams cp) {
+  extern __shared__ uint32_t dyn[];  // max(histogram, compression) words
+  const int blk = blockIdx.x;
+  if (blk < ap.ncb) {
+    // 8-token batches and no prefetching keep the register budget of the
+    // scoring blocks
+    compress_block<BF16, 1, 8, false>(cp, blk, reinterpret_cast<float*>(dyn));
+  } else if (blk < ap.ncb + ap.B) {
+    append_and_score(a, ap, blk - ap.ncb);
+  } else {
+    const int sb = blk - ap.ncb - ap.B;
+    const int r = sb / ap.nsx, cx = sb % ap.nsx;
+    const int b = r / a.Tq;
+    score_chunk_mfma<KS>(a, r, cx, n_windows(ap.done_len[b], a.m, a.w), dyn);
+  }
 }
 
 // Generic path (fp32, or bf16 shapes the matrix-core kernel does not take):
@@ -186,46 +326,40 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
 
 // ------------------------------------------------------------------ select
 
-// Exclusive prefix sum over the block; returns the total in *tot.
+// Exclusive prefix sum over the block; returns the total in *tot.  sm holds
+// one word per wave; the block may reuse it once this returns.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tot, uint32_t* sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sm[wave] = x;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) sm[wave] = inc;
   __syncthreads();
   uint32_t before = 0, all = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) before += sm[w];
-    all += sm[w];
+  const int nw = (int)(blockDim.x >> 6);
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t c = sm[w];
+    before += w < wave ? c : 0u;
+    all += c;
   }
   __syncthreads();
   *tot = all;
-  return before + x - v;
+  return before + inc - v;
 }
 
-// Highest bin T with suffix count >= need over a histogram in LDS (nbins a
-// multiple of blockDim.x); writes T and the count strictly above T.
-__device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint32_t* sm, uint32_t* rev,
-                               int* T_out, uint32_t* above_out) {
-  const int nt = blockDim.x;
-  const int per = nbins / nt;
+// Highest bin T whose suffix count reaches need, over a histogram in LDS
+// (nbins a multiple of blockDim.x).  Writes T, the count strictly above T and
+// the count of bin T (0, 0, 0 when the histogram holds fewer than need).
+// The results are visible to the block on return; the histogram is no longer
+// read, so the block may overwrite it.
+__device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint32_t* sm, int* T_out,
+                               uint32_t* above_out, uint32_t* cnt_out) {
+  const int per = nbins / (int)blockDim.x;
   const int t = threadIdx.x;
   uint32_t mine = 0;
   for (int i = 0; i < per; ++i) mine += h[t * per + i];
-  // scan in descending-bin order: thread t' = nt-1-t holds this thread's count
-  const int rt = nt - 1 - t;
-  rev[rt] = mine;
-  __syncthreads();
+  if (t == 0) { *T_out = 0; *above_out = 0; *cnt_out = 0; }
   uint32_t tot;
-  const uint32_t ex = block_excl_scan(rev[t], &tot, sm);  // bins above thread rt's range
-  __syncthreads();
-  rev[t] = ex;
-  __syncthreads();
-  const uint32_t above_mine = rev[rt];
+  const uint32_t ex = block_excl_scan(mine, &tot, sm);
+  const uint32_t above_mine = tot - ex - mine;  // bins of the threads after this one
   if (above_mine < need && above_mine + mine >= need) {
     uint32_t acc = above_mine;
     for (int i = per - 1; i >= 0; --i) {
@@ -233,6 +367,7 @@ __device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint
       if (acc + c >= need) {
         *T_out = t * per + i;
         *above_out = acc;
+        *cnt_out = c;
         break;
       }
       acc += c;
@@ -243,9 +378,9 @@ __device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint
 
 __global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
   __shared__ uint32_t sh[kHistBins];
-  __shared__ uint32_t sm[8], rev[kSelThreads];
+  __shared__ uint32_t sm[kSelThreads / 64];
   __shared__ int s_T;
-  __shared__ uint32_t s_above;
+  __shared__ uint32_t s_above, s_cnt;
   __shared__ unsigned long long s_base;
   const int r = blockIdx.y;
   const int cb = blockIdx.x;
@@ -285,9 +420,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
   }
 #pragma unroll
   for (int i = 0; i < HV; ++i) reinterpret_cast<uint4*>(sh)[threadIdx.x + i * kSelThreads] = hv[i];
-  if (threadIdx.x == 0) { s_T = 0; s_above = 0; }
   __syncthreads();
-  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, rev, &s_T, &s_above);
+  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, &s_T, &s_above, &s_cnt);
   const uint32_t T = (uint32_t)s_T;
 
   uint32_t keys[kSelPerThread];
@@ -331,11 +465,11 @@ constexpr int kBitmapWords = 8192;               // 262144 entries
 
 __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
   __shared__ uint32_t sh[4096];
-  __shared__ uint32_t sm[16], rev[kFinThreads];
+  __shared__ uint32_t sm[kFinThreads / 64];
   __shared__ uint64_t lds_cand[kCandLds];
   __shared__ uint32_t bitmap[kBitmapWords];
   __shared__ int s_T;
-  __shared__ uint32_t s_above;
+  __shared__ uint32_t s_above, s_cnt;
   __shared__ uint32_t s_fill;
   const int r = blockIdx.x;
   const int b = r / a.Tq;
@@ -348,20 +482,37 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
   const unsigned long long cnt = a.ctr[r];
   const uint32_t n_sel = (uint32_t)(cnt & 0xFFFFFFFFull);
   const uint32_t ncands = (uint32_t)(cnt >> 32);
-  // the threshold bin of the filter kernel, recomputed from the same histogram
-  const uint32_t* gh = a.hist + (int64_t)r * a.nstripe * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) {
-    uint32_t c = 0;
-    for (int st = 0; st < a.nstripe; ++st) c += gh[st * kHistBins + i];
-    sh[i] = c;
+  // the threshold bin of the filter kernel, recomputed from the same
+  // histogram (every stripe's loads in flight together); the histogram and
+  // the counters are then cleared for the next call right away
+  uint32_t* gh = a.hist + (int64_t)r * a.nstripe * kHistBins;
+  {
+    constexpr int kMaxStripes = 8;
+    constexpr int HB = kHistBins / kFinThreads;
+    uint32_t c[HB][kMaxStripes];
+#pragma unroll
+    for (int j = 0; j < HB; ++j)
+#pragma unroll
+      for (int st = 0; st < kMaxStripes; ++st)
+        c[j][st] = st < a.nstripe ? gh[st * kHistBins + threadIdx.x + j * kFinThreads] : 0u;
+#pragma unroll
+    for (int j = 0; j < HB; ++j) {
+      uint32_t sum = 0;
+#pragma unroll
+      for (int st = 0; st < kMaxStripes; ++st) sum += c[j][st];
+      sh[threadIdx.x + j * kFinThreads] = sum;
+    }
   }
-  if (threadIdx.x == 0) { s_T = 0; s_above = 0; }
+  for (int i = threadIdx.x; i < a.nstripe * kHistBins; i += blockDim.x) gh[i] = 0;
+  if (threadIdx.x == 0) a.ctr[r] = 0;
+  const bool use_bitmap = nv <= (int64_t)kBitmapWords * 32;
+  if (use_bitmap)
+    for (int i = threadIdx.x; i < kBitmapWords; i += blockDim.x) bitmap[i] = 0;
   __syncthreads();
-  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, rev, &s_T, &s_above);
+  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, &s_T, &s_above, &s_cnt);
   const uint32_t above = s_above;
   const bool consistent = n_sel == above && above < (uint32_t)a.k && above + ncands >= (uint32_t)a.k &&
                           ncands <= (uint32_t)a.max_entries;
-  const bool use_bitmap = nv <= (int64_t)kBitmapWords * 32;
   if (!consistent) {
     for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = -1;
   } else {
@@ -387,23 +538,21 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
           if ((v & mask) == prefix) atomicAdd(&sh[(uint32_t)(v >> sft) & (uint32_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        if (threadIdx.x == 0) { s_T = 0; s_above = 0; }
-        __syncthreads();
-        find_threshold(sh, nb, need, sm, rev, &s_T, &s_above);
+        find_threshold(sh, nb, need, sm, &s_T, &s_above, &s_cnt);
         prefix |= (uint64_t)s_T << sft;
         mask |= (uint64_t)(nb - 1) << sft;
         need -= s_above;
         // every value left in the chosen bucket is needed: its lower bound
         // (prefix with zero low bits) is the threshold
-        if (sh[s_T] == need) break;
+        const bool done = s_cnt == need;
+        __syncthreads();  // s_T, s_above and s_cnt are rewritten by the next pass
+        if (done) break;
       }
     }
     const uint64_t vstar = prefix;  // need < ncands: exactly (k - above) values >= vstar; else 0 (all)
     const int32_t* selr = a.sel + (int64_t)r * a.k;
     if (use_bitmap) {
       // ascending index order through a bitmap of the chosen entries
-      for (int i = threadIdx.x; i < kBitmapWords; i += blockDim.x) bitmap[i] = 0;
-      __syncthreads();
       for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) {
         const uint32_t e = (uint32_t)selr[i];
         atomicOr(&bitmap[e >> 5], 1u << (e & 31));
@@ -449,10 +598,6 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
       }
     }
   }
-  // leave the workspace clean for the next call
-  uint32_t* ghw = a.hist + (int64_t)r * a.nstripe * kHistBins;
-  for (int i = threadIdx.x; i < a.nstripe * kHistBins; i += blockDim.x) ghw[i] = 0;
-  if (threadIdx.x == 0) a.ctr[r] = 0;
 }
 
 // ------------------------------------------------------------------ host
@@ -527,6 +672,70 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
     hipLaunchKernelGGL((index_score_valu<BF16>), g1, dim3(kIdxThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL((index_score_valu<F32>), g1, dim3(kIdxThreads), 0, stream, a);
+  }
+  return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+}
+
+int launch_compress(const lca_compress_stream* streams, int n, const int64_t* tok_off, const int64_t* done_len,
+                    int B, float eps, int dtype, hipStream_t stream);
+
+int launch_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                              const int32_t* q_pos, int B, int HI, int dI, int k, int m, int w, int64_t maxN,
+                              const lca_compress_stream* idx_stream, const lca_compress_stream* kv_streams, int n_kv,
+                              const int64_t* tok_off, const int64_t* done_len, float eps, float* scores, void* ws,
+                              int dtype, hipStream_t stream) {
+  // the fused launch: bf16 matrix-core scores, one query row per sequence,
+  // KV streams of at most 512 bf16 channels; anything else runs as the two
+  // launches it stands for
+  const bool fused = dtype == LCA_BF16 && HI <= 16 && (dI == 32 || dI == 64 || dI == 128 || dI == 256) &&
+                     idx_stream->C == dI && idx_stream->m == m && idx_stream->w == w &&
+                     (w == m || w == 2 * m) && w <= 16;
+  CompressParams cp{};
+  int64_t cblocks = 0;
+  size_t clds = 0;
+  int nv = 1;
+  if (fused && n_kv > 0) {
+    const int rc = setup_compress(kv_streams, n_kv, tok_off, done_len, B, eps, dtype, kIdxThreads, &cp, &cblocks,
+                                  &clds, &nv);
+    if (rc != LCA_OK) return rc;
+  }
+  if (!fused || nv != 1) {
+    lca_compress_stream all[5];
+    int n = 0;
+    all[n++] = *idx_stream;
+    for (int i = 0; i < n_kv; ++i) all[n++] = kv_streams[i];
+    // streams of one compression launch share the vector width: the indexer
+    // keys go first, alone when they differ
+    int rc = launch_compress(all, 1, tok_off, done_len, B, eps, dtype, stream);
+    if (rc == LCA_OK && n_kv > 0) rc = launch_compress(all + 1, n_kv, tok_off, done_len, B, eps, dtype, stream);
+    if (rc != LCA_OK) return rc;
+    return launch_index_score(p, omega, ikey, csa_off, q_pos, B, 1, HI, dI, k, m, w, maxN, scores, ws, dtype, stream);
+  }
+  IndexParams a = make_params(p, omega, ikey, csa_off, q_pos, B, 1, HI, dI, k, m, w, maxN, nullptr, scores, ws);
+  AppendIdx ap{};
+  const lca_compress_stream& in = *idx_stream;
+  ap.s.src = in.src; ap.s.logits = in.logits; ap.s.out = in.out; ap.s.ent_off = in.ent_off;
+  ap.s.C = in.C; ap.s.m = in.m; ap.s.w = in.w; ap.s.per_channel = in.per_channel; ap.s.rmsnorm = in.rmsnorm;
+  ap.s.max_entries = in.max_entries;
+  ap.tok_off = tok_off;
+  ap.done_len = done_len;
+  ap.nsx = (int)((maxN + a.chunk - 1) / a.chunk);
+  ap.nsb = ap.nsx * B;
+  ap.ncb = (int)cblocks;
+  ap.B = B;
+  ap.eps = eps;
+  const int64_t blocks = (int64_t)ap.nsb + B + cblocks;
+  if (blocks > 0x7FFFFFFF) {
+    set_error("csa_index_score_append: grid too large (%lld blocks)", (long long)blocks);
+    return LCA_ERR_UNSUPPORTED;
+  }
+  const size_t lds = clds > kHistBins * 4 ? clds : kHistBins * 4;
+  dim3 grid((unsigned)blocks);
+  switch (dI / 32) {
+    case 1: hipLaunchKernelGGL((index_score_append<1>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
+    case 2: hipLaunchKernelGGL((index_score_append<2>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
+    case 4: hipLaunchKernelGGL((index_score_append<4>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
+    default: hipLaunchKernelGGL((index_score_append<8>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
   }
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }

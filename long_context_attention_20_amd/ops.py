@@ -9,7 +9,8 @@ from typing import Optional, Sequence
 import ctypes
 import torch
 
-from ._lib import (LCA_BF16, LCA_F32, CompressStream, Partial, check, lib)
+from ._lib import (LCA_BF16, LCA_F32, LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_WINDOW, AttnSource, CompressStream,
+                   Partial, check, lib)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -50,17 +51,10 @@ def _i32(t: torch.Tensor, what: str):
 
 # ---------------------------------------------------------------- a1
 
-def kv_compress(streams: Sequence[dict], tok_off: torch.Tensor, done_len: Optional[torch.Tensor] = None,
-                eps: float = 1e-6):
-    """streams: dicts with src, logits, out, ent_off (tensors) and m, w,
-    rmsnorm, max_entries (ints); per_channel is taken from the logits' rank."""
-    if not 1 <= len(streams) <= 4:
-        raise ValueError("1..4 streams per call")
-    _i64(tok_off, "tok_off")
-    B = tok_off.numel() - 1
-    arr = (CompressStream * len(streams))()
+def _stream_array(streams: Sequence[dict]):
+    """ctypes array of lca_compress_stream and the common element type."""
+    arr = (CompressStream * max(1, len(streams)))()
     dt = None
-    keep = []
     for i, s in enumerate(streams):
         src, lg, out, eo = s["src"], s["logits"], s["out"], s["ent_off"]
         _dev(src, lg, out, eo)
@@ -74,7 +68,18 @@ def kv_compress(streams: Sequence[dict], tok_off: torch.Tensor, done_len: Option
         pc = 1 if lg.dim() == 2 else 0
         arr[i] = CompressStream(src.data_ptr(), lg.data_ptr(), out.data_ptr(), eo.data_ptr(), C, int(s["m"]),
                                 int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]))
-        keep.append(s)
+    return arr, dt
+
+
+def kv_compress(streams: Sequence[dict], tok_off: torch.Tensor, done_len: Optional[torch.Tensor] = None,
+                eps: float = 1e-6):
+    """streams: dicts with src, logits, out, ent_off (tensors) and m, w,
+    rmsnorm, max_entries (ints); per_channel is taken from the logits' rank."""
+    if not 1 <= len(streams) <= 4:
+        raise ValueError("1..4 streams per call")
+    _i64(tok_off, "tok_off")
+    B = tok_off.numel() - 1
+    arr, dt = _stream_array(streams)
     _dev(tok_off, done_len)
     if done_len is not None:
         _i64(done_len, "done_len")
@@ -116,6 +121,29 @@ def csa_index_score(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: int, max_
     check(lib.lca_csa_index_score(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B, rows // B,
                                   p.shape[-2], p.shape[-1], k, m, w, int(max_entries), _ptr(scores), _ptr(ws),
                                   ws.numel() * ws.element_size(), _dtype_code(p), _stream()), "csa_index_score")
+
+
+def csa_index_score_append(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: int, max_entries: int,
+                           ws: torch.Tensor, idx_stream: dict, kv_streams: Sequence[dict], tok_off: torch.Tensor,
+                           done_len: torch.Tensor, eps: float = 1e-6, scores: Optional[torch.Tensor] = None):
+    """kv_compress of the indexer-key stream and kv_streams (entries completed
+    after done_len tokens) and csa_index_score for one query row per
+    sequence, in one launch."""
+    _dev(p, omega, ikey, csa_off, q_pos, ws, scores, tok_off, done_len)
+    _i64(tok_off, "tok_off")
+    _i64(done_len, "done_len")
+    B = csa_off.numel() - 1
+    if q_pos.numel() != B:
+        raise ValueError("one query row per sequence")
+    if len(kv_streams) > 4:
+        raise ValueError("0..4 kv streams per call")
+    ia, _ = _stream_array([idx_stream])
+    ka, _ = _stream_array(kv_streams)
+    check(lib.lca_csa_index_score_append(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B,
+                                         p.shape[-2], p.shape[-1], k, m, w, int(max_entries), ia, ka,
+                                         len(kv_streams), _ptr(tok_off), _ptr(done_len), float(eps), _ptr(scores),
+                                         _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(p), _stream()),
+          "csa_index_score_append")
 
 
 def csa_topk_select(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws: torch.Tensor,
@@ -187,6 +215,48 @@ def swa_attn(q, x, tok_off, q_pos, W: int, scale: float, eps: float, o_part=None
     check(lib.lca_swa_attn(_ptr(q), _ptr(x), _ptr(tok_off), _ptr(q_pos), B, rows // B, H, D, W, float(scale),
                            float(eps), _ptr(o_part), _ptr(lse), _dtype_code(q), _stream()), "swa_attn")
     return o_part, lse
+
+
+_KINDS = {"dense": LCA_SRC_DENSE, "gather": LCA_SRC_GATHER, "window": LCA_SRC_WINDOW}
+
+
+def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
+    """The attention branches of a step in one launch.  sources: dicts with
+    kind ("gather", "dense" or "window"), kv, off and n_split, plus idx
+    (gather), m2 and w2 (dense), W (window), and optionally o_part / lse.
+    Returns one (o_part, lse) pair per source, as the single-branch calls."""
+    if not 1 <= len(sources) <= 3:
+        raise ValueError("1..3 sources per call")
+    _dev(q, q_pos)
+    if q_pos is not None:
+        _i32(q_pos, "q_pos")
+    rows, H, D = q.shape
+    arr = (AttnSource * len(sources))()
+    outs = []
+    B = None
+    for i, s in enumerate(sources):
+        kind = _KINDS[s["kind"]]
+        kv, off, idx = s["kv"], s["off"], s.get("idx")
+        _dev(kv, off, idx)
+        _i64(off, "off")
+        if B is None:
+            B = off.numel() - 1
+        elif off.numel() - 1 != B:
+            raise ValueError("every source needs the same number of sequences")
+        k = 0
+        if kind == LCA_SRC_GATHER:
+            _i32(idx, "idx")
+            k = idx.shape[-1]
+        ns = int(s["n_split"])
+        o_part, lse = _parts_out(rows, H, D, ns, q.device, s.get("o_part"), s.get("lse"))
+        _dev(o_part, lse)
+        arr[i] = AttnSource(kind, kv.data_ptr(), off.data_ptr(), None if idx is None else idx.data_ptr(), k,
+                            int(s.get("m2", 1)), int(s.get("w2", 1)), int(s.get("W", 0)), ns, o_part.data_ptr(),
+                            lse.data_ptr())
+        outs.append((o_part, lse))
+    check(lib.lca_hybrid_attn(arr, len(sources), _ptr(q), _ptr(q_pos), B, rows // B, H, D, float(scale), float(eps),
+                              _dtype_code(q), _stream()), "hybrid_attn")
+    return outs
 
 
 def swa_merge_workspace(n_rows: int, H: int, D: int) -> int:

@@ -5,11 +5,14 @@ strides and windows), the caller's caches as device tensors with their host
 and device offsets, and reusable workspaces.  It only sizes buffers and
 sequences the C entry points; every step runs in the HIP kernels.
 
-Decode / prefill step (one call per step):
-    kv_compress (entries completed by the new tokens)
-    csa_index_topk -> csa_sparse_attn
-    hca_attn                       (independent of the indexer)
-    swa_merge (window + sink + merge of every partial)
+Decode step (one query row per sequence), four calls on one stream:
+    csa_index_score_append  the CSA, indexer-key and HCA entries the new token
+                            completes, and the index scores (one launch)
+    csa_topk_select         exact top-k
+    hybrid_attn             CSA sparse + HCA dense + window partials (one launch)
+    swa_merge               sink + merge of every partial
+Prefill chunks (several rows per sequence) run kv_compress and
+csa_index_score as separate launches.
 """
 from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
@@ -107,16 +110,41 @@ class HybridAttention:
         for g in groups.values():
             ops.kv_compress(g, tok_off, done_len, self.eps)
 
+    def _append(self, caches: Caches, raw: dict, tok_off, done_len, done_h, which=("csa", "idx", "hca")):
+        """Launch the compression of the entries completed after done_h tokens
+        (one launch when the streams share a vector width)."""
+        streams = self.compress_streams(caches, raw, done_h, which)
+        groups: Dict[int, list] = {}
+        for s in streams:
+            lanes = s["src"].shape[-1] // (8 if s["src"].dtype == torch.bfloat16 else 4)
+            groups.setdefault(1 if lanes <= 64 else lanes // 64, []).append(s)
+        for g in groups.values():
+            ops.kv_compress(g, tok_off, done_len, self.eps)
+
     # -------------------------------------------------------------- a2-a6
     def index_workspace(self, rows: int, max_entries: int, device) -> torch.Tensor:
         nbytes = ops.csa_index_topk_workspace(rows, max(1, max_entries), self.k)
         return self._workspace(f"idx{rows}_{max_entries}", nbytes, device, zero=True)
 
     def default_splits(self, rows: int, n_keys: int) -> int:
-        hg = (self.H + 63) // 64
+        """Splits of one source launched on its own: about one block per
+        compute unit, at least two tiles for each of a block's two streams."""
+        hg = (self.H + 31) // 32
         tiles = max(1, (n_keys + 31) // 32)
         want = max(1, -(-256 // (rows * hg)))
         return int(max(1, min(want, tiles // 4 if tiles >= 4 else 1, 256)))
+
+    def fused_splits(self, rows: int, n_csa: int, n_hca: int, n_win: int):
+        """Splits of the three sources of one fused launch: the blocks of all
+        sources take about the same number of 32-key tiles (an even number,
+        one per team and round), chosen so that one wave of blocks (one per
+        compute unit) covers the launch when the rows allow it."""
+        hg = (self.H + 31) // 32
+        tiles = [max(1, (n + 31) // 32) for n in (n_csa, n_hca, n_win)]
+        budget = max(3, 256 // max(1, rows * hg))
+        per = -(-sum(tiles) // budget)
+        per = min(32, max(2, per + (per & 1)))
+        return tuple(int(min(256, max(1, -(-t // per)))) for t in tiles)
 
     def step(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, q: torch.Tensor, p: torch.Tensor,
              omega: torch.Tensor, sigma: Optional[torch.Tensor], q_pos: torch.Tensor, q_pos_h: np.ndarray,
@@ -153,58 +181,72 @@ class HybridAttention:
         """Preallocated outputs of decode_step (so that the step can be
         captured in a HIP graph and replayed)."""
         f32 = torch.float32
-        sc = self.split_csa or self.default_splits(rows, self.k)
-        sh = self.split_hca or self.default_splits(rows, max_hca)
+        sc, sh, sw = self.fused_splits(rows, min(self.k, max(1, max_csa)), max_hca, self.W)
+        sc = self.split_csa or sc
+        sh = self.split_hca or sh
+        part = lambda n: (torch.empty((n, rows, self.H, self.D), dtype=f32, device=device),
+                          torch.empty((n, rows, self.H), dtype=f32, device=device))
         return dict(
-            sc=sc, sh=sh, max_csa=max(1, max_csa), max_hca=max_hca,
+            sc=sc, sh=sh, sw=sw, max_csa=max(1, max_csa), max_hca=max_hca,
             ws_idx=self.index_workspace(rows, max(1, max_csa), device),
             idx=torch.empty((rows, self.k), dtype=torch.int32, device=device),
-            csa=(torch.empty((sc, rows, self.H, self.D), dtype=f32, device=device),
-                 torch.empty((sc, rows, self.H), dtype=f32, device=device)),
-            hca=(torch.empty((sh, rows, self.H, self.D), dtype=f32, device=device),
-                 torch.empty((sh, rows, self.H), dtype=f32, device=device)),
-            swa=(torch.empty((1, rows, self.H, self.D), dtype=f32, device=device),
-                 torch.empty((1, rows, self.H), dtype=f32, device=device)),
+            csa=part(sc), hca=part(sh), swa=part(sw),
             out=torch.empty((rows, self.H, self.D), dtype=dtype, device=device))
+
+    def attn_sources(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, idx: torch.Tensor, bufs: dict):
+        """The three key sources of the fused attention launch."""
+        src = [dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=bufs["sc"],
+                    o_part=bufs["csa"][0], lse=bufs["csa"][1])]
+        if bufs["max_hca"] > 0:
+            src.append(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2,
+                            n_split=bufs["sh"], o_part=bufs["hca"][0], lse=bufs["hca"][1]))
+        if self.W > 0:
+            src.append(dict(kind="window", kv=x, off=tok_off, W=self.W, n_split=bufs["sw"], o_part=bufs["swa"][0],
+                            lse=bufs["swa"][1]))
+        return src
 
     def decode_step(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos,
                     bufs: dict, done_len: Optional[torch.Tensor] = None, done_h: Optional[Sequence[int]] = None,
                     side: Optional["torch.cuda.Stream"] = None):
         """One decode (or prefill-chunk) step of mode A: append the entries the
-        new tokens complete (when done_len is given), then the CSA branch
-        (indexer, top-k, sparse attention) on the current stream and, when a
-        side stream is given, the HCA and window branches on it, joined before
-        the merge."""
+        new tokens complete (when done_len is given), score and select the CSA
+        entries, attend to the selected CSA entries, the visible HCA entries
+        and the window in one launch, and merge the partials with the sink.
+        With one query row per sequence the appends ride in the scoring
+        launch.  With a side stream the HCA append runs there instead, beside
+        the indexer (the join costs a cross-queue wait in a graph)."""
         main = torch.cuda.current_stream()
-        if side is not None:
-            fork = torch.cuda.Event()
-            fork.record(main)
-            side.wait_event(fork)
-        # ---- HCA + window branch
-        with torch.cuda.stream(side if side is not None else main):
-            if done_len is not None:
-                st = self.compress_streams(caches, raw, done_h, ("hca",))
-                if st:
-                    ops.kv_compress(st, tok_off, done_len, self.eps)
-            ops.hca_attn(q, caches.kv_hca, caches.hca_off, q_pos, self.m2, self.w2, bufs["max_hca"], self.scale,
-                         self.eps, bufs["sh"], *bufs["hca"])
-            ops.swa_attn(q, raw["x"], tok_off, q_pos, self.W, self.scale, self.eps, *bufs["swa"])
-            if side is not None:
-                join = torch.cuda.Event()
-                join.record(side)
-        # ---- CSA branch
+        join = None
+        scored = False
         if done_len is not None:
-            st = self.compress_streams(caches, raw, done_h, ("csa", "idx"))
-            if st:
-                ops.kv_compress(st, tok_off, done_len, self.eps)
-        ops.csa_index_score(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"],
-                            bufs["ws_idx"])
+            if side is not None:
+                fork = torch.cuda.Event()
+                fork.record(main)
+                side.wait_event(fork)
+                with torch.cuda.stream(side):
+                    self._append(caches, raw, tok_off, done_len, done_h, ("hca",))
+                    join = torch.cuda.Event()
+                    join.record(side)
+                self._append(caches, raw, tok_off, done_len, done_h, ("csa", "idx"))
+            else:
+                streams = self.compress_streams(caches, raw, done_h)
+                idx_st = [st for st in streams if st["out"] is caches.ikey]
+                kv_st = [st for st in streams if st["out"] is not caches.ikey]
+                if idx_st and q.shape[0] == len(caches.lens):
+                    ops.csa_index_score_append(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w,
+                                               bufs["max_csa"], bufs["ws_idx"], idx_st[0], kv_st, tok_off, done_len,
+                                               self.eps)
+                    scored = True
+                else:
+                    self._append(caches, raw, tok_off, done_len, done_h)
+        if not scored:
+            ops.csa_index_score(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w,
+                                bufs["max_csa"], bufs["ws_idx"])
         ops.csa_topk_select(caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"], bufs["ws_idx"],
                             idx=bufs["idx"])
-        ops.csa_sparse_attn(q, caches.kv_csa, caches.csa_off, bufs["idx"], self.scale, self.eps, bufs["sc"],
-                            *bufs["csa"])
-        if side is not None:
+        if join is not None:
             main.wait_event(join)
-        ops.swa_merge(q, None, None, None, sigma, [bufs["csa"], bufs["hca"], bufs["swa"]], 0, self.scale, self.eps,
-                      None, out=bufs["out"])
+        srcs = self.attn_sources(caches, raw["x"], tok_off, bufs["idx"], bufs)
+        parts = ops.hybrid_attn(q, q_pos, srcs, self.scale, self.eps)
+        ops.swa_merge(q, None, None, None, sigma, parts, 0, self.scale, self.eps, None, out=bufs["out"])
         return bufs["out"]

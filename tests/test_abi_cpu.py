@@ -120,3 +120,69 @@ def test_swa_merge_rejects(L):
     parts[0] = L.Partial(256, 0, 1)
     assert f(P, P, P, P, P, parts, 1, 1, 1, 64, 512, 128, 0.04, 1e-6, P, P, need, 1, None) == L.LCA_ERR_INVALID_ARG
     assert f(P, P, P, P, None, None, 0, 1, 1, 64, 512, 0, 0.04, 1e-6, P, None, 0, 1, None) == L.LCA_ERR_INVALID_ARG
+
+
+def test_hybrid_attn_rejects(L):
+    lib = L.lib
+    P = ctypes.c_void_p(256)
+    src = (L.AttnSource * 3)()
+
+    def fill(i, kind=L.LCA_SRC_GATHER, kv=256, off=256, idx=256, k=512, m2=128, w2=128, W=128, ns=4, o=256, l=256):
+        src[i] = L.AttnSource(kind, kv, off, idx, k, m2, w2, W, ns, o, l)
+
+    def call(n=1, q=P, qp=P, H=64, D=512, dt=1):
+        return lib.lca_hybrid_attn(src, n, q, qp, 1, 1, H, D, 0.04, 1e-6, dt, None)
+    for i in range(3):
+        fill(i)
+    assert lib.lca_hybrid_attn(None, 1, P, P, 1, 1, 64, 512, 0.04, 1e-6, 1, None) == L.LCA_ERR_INVALID_ARG
+    assert call(n=0) == L.LCA_ERR_INVALID_ARG
+    assert call(n=4) == L.LCA_ERR_INVALID_ARG
+    fill(1, kind=7)
+    assert call(n=2) == L.LCA_ERR_INVALID_ARG                  # unknown kind
+    fill(1, kind=L.LCA_SRC_DENSE, m2=0)
+    assert call(n=2) == L.LCA_ERR_INVALID_ARG                  # m2
+    fill(1, kind=L.LCA_SRC_WINDOW, W=0)
+    assert call(n=2) == L.LCA_ERR_INVALID_ARG                  # W
+    fill(1, kind=L.LCA_SRC_WINDOW)
+    assert call(n=2, qp=None) == L.LCA_ERR_INVALID_ARG         # window needs q_pos
+    fill(0, idx=0)
+    assert call() == L.LCA_ERR_INVALID_ARG                     # gather needs idx
+    fill(0, k=0)
+    assert call() == L.LCA_ERR_INVALID_ARG
+    fill(0, ns=0)
+    assert call() == L.LCA_ERR_INVALID_ARG
+    fill(0, o=0)
+    assert call() == L.LCA_ERR_INVALID_ARG
+    fill(0)
+    assert call(D=96) == L.LCA_ERR_UNSUPPORTED
+    fill(0, k=65536, ns=1)                                     # more gathered slots per split than LDS holds
+    assert call() == L.LCA_ERR_UNSUPPORTED
+    assert b"gathered slots" in lib.lca_last_error()
+
+
+def test_index_score_append_rejects(L):
+    lib = L.lib
+    P = ctypes.c_void_p(256)
+    need = lib.lca_csa_index_topk_workspace(1, 1000, 512)
+    idx = (L.CompressStream * 1)()
+    idx[0] = L.CompressStream(256, 256, 256, 256, 64, 4, 8, 1, 0, 1)   # out == ikey, ent_off == csa_off
+    kv = (L.CompressStream * 2)()
+    kv[0] = L.CompressStream(512, 512, 512, 512, 512, 4, 8, 1, 1, 1)
+    kv[1] = L.CompressStream(512, 512, 512, 768, 512, 128, 128, 1, 1, 1)
+
+    def call(idx_s=idx, kv_s=kv, n_kv=2, done=P, dI=64, ws_bytes=need, eps=1e-6):
+        return lib.lca_csa_index_score_append(P, P, P, P, P, 1, 4, dI, 512, 4, 8, 1000, idx_s, kv_s, n_kv, P, done,
+                                              eps, None, P, ws_bytes, 1, None)
+    assert call(idx_s=None) == L.LCA_ERR_INVALID_ARG
+    assert call(done=None) == L.LCA_ERR_INVALID_ARG
+    assert call(n_kv=5) == L.LCA_ERR_INVALID_ARG
+    assert call(kv_s=None) == L.LCA_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == L.LCA_ERR_WORKSPACE
+    assert call(eps=-1.0) == L.LCA_ERR_INVALID_ARG
+    idx[0] = L.CompressStream(256, 256, 512, 256, 64, 4, 8, 1, 0, 1)    # writes somewhere other than ikey
+    assert call() == L.LCA_ERR_INVALID_ARG
+    idx[0] = L.CompressStream(256, 256, 256, 256, 32, 4, 8, 1, 0, 1)    # C != d_I
+    assert call() == L.LCA_ERR_INVALID_ARG
+    idx[0] = L.CompressStream(256, 256, 256, 256, 64, 4, 8, 1, 0, 1)
+    kv[1] = L.CompressStream(512, 512, 512, 768, 500, 128, 128, 1, 1, 1)  # C % 8
+    assert call() == L.LCA_ERR_INVALID_ARG

@@ -1,7 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (decode_step: append of the entries the new token completes,
-CSA branch on the current stream, HCA and window branches on a side stream,
-merge).  Inputs are drawn on the GPU with a seeded generator and copied back
+benchmark times (decode_step: the CSA and indexer-key appends, index score
+and top-k on the current stream beside the HCA append on a side stream, one
+launch of the CSA, HCA and window attention partials, merge).  Inputs are drawn on the GPU with a seeded generator and copied back
 for the oracle, which checks sampled compressed entries, every selected set
 of the checked rows (scores recomputed in float64 from the GPU-stored indexer
 keys), and every head of the checked rows' outputs, stage-wise and end to end.

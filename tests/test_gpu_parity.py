@@ -293,16 +293,16 @@ def _decode_setup(cfg, raw):
     return d, layer, caches, full, done, done_h, bufs
 
 
-@pytest.mark.parametrize("overlap", [False, True])
-def test_decode_step_with_append(overlap):
-    """decode_step: append of the completed entries, both branches (optionally
-    on two streams) and the merge, against the oracle from raw inputs."""
+@pytest.mark.parametrize("side", [False, True])
+def test_decode_step_with_append(side):
+    """decode_step: append of the completed entries (the HCA append on a
+    side stream, optionally), selection, the fused attention launch and the
+    merge, against the oracle from raw inputs."""
     cfg = li.small("decode", 108, (4001, 2600, 777), H=64, D=512, k=256)
     raw = li.make_raw(cfg)
     d, layer, caches, full, done, done_h, bufs = _decode_setup(cfg, raw)
-    side = torch.cuda.Stream() if overlap else None
     out = layer.decode_step(caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs,
-                            done_len=done, done_h=done_h, side=side)
+                            done_len=done, done_h=done_h, side=torch.cuda.Stream() if side else None)
     torch.cuda.synchronize()
     assert torch.equal(caches.kv_csa, full[0]) and torch.equal(caches.ikey, full[1]) and torch.equal(caches.kv_hca, full[2])
     _, ores = opipe.run(raw, cfg)
@@ -316,13 +316,14 @@ def test_decode_step_with_append(overlap):
 
 
 def test_decode_step_graph_replay():
-    """The two-stream step captured in a HIP graph: every replay equals the
-    eager step (eager work and synchronisation between replays)."""
+    """The step (HCA append on a side stream) captured in a HIP graph: every
+    replay equals the eager step (eager work and synchronisation between
+    replays)."""
     cfg = li.small("graph", 109, (3000, 1500), H=64, D=512, k=256)
     raw = li.make_raw(cfg)
     d, layer, caches, full, done, done_h, bufs = _decode_setup(cfg, raw)
-    side = torch.cuda.Stream()
     args = (caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs)
+    side = torch.cuda.Stream()
     eager = layer.decode_step(*args, done_len=done, done_h=done_h, side=side).clone()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -342,3 +343,104 @@ def test_decode_step_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(bufs["out"], eager), f"replay {rep} differs from the eager step"
         _ = (d["q"].float() * 2).sum().item()   # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("case", ["flash_ragged", "bf16_h4"])
+def test_hybrid_attn_equals_single_branches(case):
+    """One fused launch of the three sources writes exactly the partials of
+    the three single-branch calls with the same splits, and its merge matches
+    the oracle's union softmax."""
+    from long_context_attention_20_amd import ops
+    cfg = CASES[case]
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    q_pos = d["q_pos"]
+    qmax = int(raw["q_pos"].max()) + 1
+    max_csa = max(1, ocmp.n_entries(qmax, cfg.m, cfg.w))
+    max_hca = ocmp.n_entries(qmax, cfg.m2, cfg.w2)
+    ws = layer.index_workspace(q_pos.numel(), max_csa, "cuda")
+    idx = ops.csa_index_topk(d["p"], d["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws)
+    sc, sh, sw = 3, 5, 2
+    srcs = [dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=sc),
+            dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=cfg.m2, w2=cfg.w2, n_split=sh),
+            dict(kind="window", kv=d["x"], off=d["tok_off"], W=cfg.W, n_split=sw)]
+    fused = ops.hybrid_attn(d["q"], q_pos, srcs, cfg.scale, cfg.eps)
+    csa = ops.csa_sparse_attn(d["q"], caches.kv_csa, caches.csa_off, idx, cfg.scale, cfg.eps, sc)
+    hca = ops.hca_attn(d["q"], caches.kv_hca, caches.hca_off, q_pos, cfg.m2, cfg.w2, max_hca, cfg.scale, cfg.eps, sh)
+    win1 = ops.swa_attn(d["q"], d["x"], d["tok_off"], q_pos, cfg.W, cfg.scale, cfg.eps)
+    torch.cuda.synchronize()
+    for (fo, fl), (so, sl), what in zip(fused[:2], (csa, hca), ("csa", "hca")):
+        assert torch.equal(fo, so) and torch.equal(fl, sl), f"fused {what} partials differ from the single call"
+    # the window in two splits merges to the one-split window partial
+    wo, wl = fused[2]
+    for r in range(q_pos.numel()):
+        a, la = merge_splits(wo[:, r], wl[:, r])
+        bb, lb = merge_splits(win1[0][:, r], win1[1][:, r])
+        assert_close(a, bb, cfg.dtype, f"window splits row {r}")
+    wsm = layer._workspace("m", ops.swa_merge_workspace(q_pos.numel(), cfg.H, cfg.D), "cuda", zero=False)
+    out = ops.swa_merge(d["q"], None, None, None, d["sigma"], fused, 0, cfg.scale, cfg.eps, wsm)
+    torch.cuda.synchronize()
+    _, ores = opipe.run(raw, cfg)
+    out_h = f64(out)
+    idx_h = idx.cpu().numpy()
+    rows = [(b, t) for b in range(cfg.B) for t in range(cfg.tq)]
+    for r, key in enumerate(rows):
+        res = ores[key]
+        if set(idx_h[r][idx_h[r] >= 0].tolist()) != set(res["sel"].tolist()):
+            continue  # near-tie selections are covered by the index tests
+        assert_close(out_h[r], res["out"], cfg.dtype, f"{case} row {key}")
+
+
+@pytest.mark.parametrize("rmsnorm_idx", [0, 1])
+def test_index_score_append_equals_separate(rmsnorm_idx):
+    """csa_index_score_append (appends + scores in one launch) writes the
+    caches bit-identically to kv_compress and the scores of csa_index_score
+    within rounding order; the selections agree except at near-ties."""
+    from long_context_attention_20_amd import ops
+    cfg = li.small("append", 110, (4001, 2600, 777, 4096), H=64, D=512, k=256)
+    raw = li.make_raw(cfg)
+    d, layer, caches, full, done, done_h, bufs = _decode_setup(cfg, raw)
+    streams = layer.compress_streams(caches, d, done_h)
+    idx_st = [s for s in streams if s["out"] is caches.ikey][0]
+    idx_st = dict(idx_st, rmsnorm=rmsnorm_idx)
+    kv_st = [s for s in streams if s["out"] is not caches.ikey]
+    ws1 = layer.index_workspace(cfg.B, bufs["max_csa"], "cuda")
+    ops.csa_index_score_append(d["p"], d["omega"], caches.ikey, caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w,
+                               bufs["max_csa"], ws1, idx_st, kv_st, d["tok_off"], done, cfg.eps)
+    idx1 = ops.csa_topk_select(caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w, bufs["max_csa"], ws1)
+    torch.cuda.synchronize()
+    fused_caches = (caches.kv_csa.clone(), caches.ikey.clone(), caches.kv_hca.clone())
+    # the separate launches from the same wiped state
+    for b, L in enumerate(cfg.lens):
+        for t, off, m, w in ((caches.kv_csa, caches.csa_off_h, cfg.m, cfg.w),
+                             (caches.ikey, caches.csa_off_h, cfg.m, cfg.w),
+                             (caches.kv_hca, caches.hca_off_h, cfg.m2, cfg.w2)):
+            n0, n1 = ocmp.n_entries(L - 1, m, w), ocmp.n_entries(L, m, w)
+            t[int(off[b]) + n0:int(off[b]) + n1] = 0
+    ops.kv_compress([idx_st], d["tok_off"], done, cfg.eps)
+    ops.kv_compress(kv_st, d["tok_off"], done, cfg.eps)
+    ws2 = layer.index_workspace(cfg.B, bufs["max_csa"], "cuda")
+    ops.csa_index_score(d["p"], d["omega"], caches.ikey, caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w,
+                        bufs["max_csa"], ws2)
+    idx2 = ops.csa_topk_select(caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w, bufs["max_csa"], ws2)
+    torch.cuda.synchronize()
+    for got, ref, name in zip(fused_caches, (caches.kv_csa, caches.ikey, caches.kv_hca), ("kv_csa", "ikey", "kv_hca")):
+        assert torch.equal(got, ref), f"{name}: fused append differs from kv_compress"
+    if rmsnorm_idx == 0:
+        assert torch.equal(fused_caches[1], full[1])
+    for b in range(cfg.B):
+        a1 = set(idx1[b][idx1[b] >= 0].tolist())
+        a2 = set(idx2[b][idx2[b] >= 0].tolist())
+        # scores of the appended entry differ at most by rounding order: any
+        # difference in the sets must be a near-tie, checked against the oracle
+        if a1 != a2:
+            co = caches.csa_off_h
+            keys = f64(caches.ikey[int(co[b]):int(co[b + 1])])
+            s_ref = oidx.scores(f64(d["p"][b]), d["omega"][b].cpu().numpy().astype(np.float64), keys)
+            kth = np.sort(s_ref)[::-1][cfg.k - 1]
+            bound = score_bound(f64(d["p"][b]), d["omega"][b].cpu().numpy().astype(np.float64), keys)
+            for j in a1 ^ a2:
+                assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + 2 * bound[j], f"row {b}: {j} not a near tie"
