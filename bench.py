@@ -20,7 +20,11 @@ Timed regions (HIP events on the launch stream, synchronised on both sides):
      kernel's time subtracted); the dominant kernel's average launch
      duration gives the roofline;
   2. the headline: the W warmup steps and then the K timed steps, each set
-     captured as one HIP graph of consecutive layer steps and replayed once;
+     captured as one HIP graph of consecutive layer steps and replayed once.
+     With one sequence the K steps are K consecutive decode positions, each
+     appending what its token completes (so appends are amortized as they
+     occur); also reported: the step at the last position, where the token
+     completes a CSA, an indexer and an HCA entry at once;
   3. the same K steps launched directly (host launch cost included).
 cpu_baseline: the float64 oracle on the host, same workload, bounded sample.
 
@@ -38,6 +42,38 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X
+
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and, in a run
+# of its own, WRITE_SIZE on this benchmark (the summary and the commands are
+# in profiles/hbm_traffic_pro_1m_decode.md), each scaled by what the counter
+# reads for a plain 256 MiB device copy (FETCH_SIZE reports half the bytes the
+# copy reads: x2; WRITE_SIZE all it writes: x1).  A figure holds for the
+# kernel source it was taken on: the SHA-1 of the files the kernel is built
+# from; any change makes the reported traffic null until it is measured again.
+TRAFFIC = {
+    ("pro_1m_decode", "hybrid_attn"): {
+        "files": ["long_context_attention_20_amd/csrc/lca_attention.hip",
+                  "long_context_attention_20_amd/csrc/lca_common.h"],
+        "sha1": "ea06c7832f3964482b5f65ee0bc1a60a0eac6b37",
+        "fetch_kib": 5305.5, "write_kib": 12825.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+}
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the counter runs, or None when
+    none was taken on the current source."""
+    import hashlib
+    t = TRAFFIC.get((workload, kernel))
+    if t is None:
+        return None
+    h = hashlib.sha1()
+    for f in t["files"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != t["sha1"]:
+        return None
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 FLOP/s, MI355X
 MALL_BYTES = 256 << 20
 
@@ -115,6 +151,21 @@ class LayerState:
         self.done = torch.tensor(self.done_h, dtype=torch.int64, device=dev)
 
 
+class Position:
+    """A decode step of a one-sequence workload at token position p: the
+    sequence is read as its first p + 1 tokens, so the step appends exactly
+    the entries token p completes and the query sees positions 0 .. p."""
+
+    def __init__(self, p, dev):
+        import torch
+        self.p = p
+        self.tok_off = torch.tensor([0, p + 1], dtype=torch.int64, device=dev)
+        self.q_pos = torch.tensor([p], dtype=torch.int32, device=dev)
+        self.done = torch.tensor([p], dtype=torch.int64, device=dev)
+        self.done_h = [p]
+        self.lens_h = [p + 1]
+
+
 class Runner:
     def __init__(self, cfg, R, dev, split_csa=0, split_hca=0):
         import torch
@@ -131,15 +182,20 @@ class Runner:
                                      self.layers[0].q.dtype)
         self.sc, self.sh, self.sw = self.bufs["sc"], self.bufs["sh"], self.bufs["sw"]
         self.names = ["csa_index_score_append", "csa_topk_select", "hybrid_attn", "swa_merge"]
+        self.launches = {"csa_topk_select": 2}  # kernels per call (default 1)
         # the top-k kernels consume and clear the histogram the score kernel
         # builds, so they are timed together with it (score subtracted)
         self.timed = ["csa_index_score_append", "csa_index_score_append+csa_topk_select", "hybrid_attn",
                       "swa_merge"]
 
-    def step(self, L):
-        """The whole decode step (four calls on the current stream)."""
-        return self.attn.decode_step(L.caches, L.raw, L.tok_off, L.q, L.p, L.omega, L.sigma, L.q_pos, self.bufs,
-                                     done_len=L.done, done_h=L.done_h)
+    def step(self, L, pos=None):
+        """The whole decode step (four calls on the current stream), at the
+        last position of every sequence or at `pos` (one sequence)."""
+        if pos is None:
+            return self.attn.decode_step(L.caches, L.raw, L.tok_off, L.q, L.p, L.omega, L.sigma, L.q_pos, self.bufs,
+                                         done_len=L.done, done_h=L.done_h)
+        return self.attn.decode_step(L.caches, L.raw, pos.tok_off, L.q, L.p, L.omega, L.sigma, pos.q_pos, self.bufs,
+                                     done_len=pos.done, done_h=pos.done_h, lens_h=pos.lens_h)
 
     def calls(self, L):
         """The same step as a sequence of single-kernel calls."""
@@ -231,6 +287,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
     ap.add_argument("--split-csa", type=int, default=0, help="entry splits of the sparse attention (0: default)")
     ap.add_argument("--split-hca", type=int, default=0, help="entry splits of the HCA attention (0: default)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB 10 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
@@ -238,6 +296,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 10}))
+        return
     import lca_inputs as li
     cfg = li.CONFIGS[args.config]
     if cfg.tq != 1:
@@ -279,12 +346,21 @@ def main():
         del g
     tt = dict(zip(run.timed, tper))
     per = np.array([tt[n] if n in tt else tt[run.names[0] + "+" + n] - tt[run.names[0]] for n in run.names])
-    dom = int(np.argmax(per))
+    # the dominant kernel: the longest single launch
+    dom = int(np.argmax([t / run.launches.get(n, 1) for n, t in zip(run.names, per)]))
     print("[bench] per-kernel ms (graph, rotated layers): " +
           ", ".join(f"{n}={t:.4f}" for n, t in zip(run.names, per)), file=sys.stderr, flush=True)
 
     K = args.steps
-    ms_graph = None
+    # one sequence: the K timed steps are K consecutive decode positions
+    # L-K .. L-1 (each appends what its token completes: a CSA and an indexer
+    # entry every 4th step, an HCA entry every 128th); several sequences: every
+    # step is the last position (all three appends each step)
+    consecutive = cfg.B == 1 and cfg.lens[0] > K + args.warmup + 2 * cfg.w2
+    pos_t = [Position(cfg.lens[0] - K + it, dev) for it in range(K)] if consecutive else [None] * K
+    pos_w = [Position(cfg.lens[0] - K - args.warmup + w, dev) for w in range(args.warmup)] if consecutive \
+        else [None] * args.warmup
+    ms_graph = ms_last = None
     if args.graph:
         # the warmup steps and the K timed steps each captured as one graph of
         # consecutive layer steps (as the layers of one forward pass run), so
@@ -296,12 +372,15 @@ def main():
                 run.step(L)
         torch.cuda.current_stream().wait_stream(s2)
         torch.cuda.synchronize()
-        gw, gk = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        gw, gk, gl = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(gw):
             for w in range(args.warmup):
-                run.step(run.layers[w % R])
+                run.step(run.layers[w % R], pos_w[w])
         with torch.cuda.graph(gk):
             for it in range(K):
+                run.step(run.layers[it % R], pos_t[it])
+        with torch.cuda.graph(gl):  # the last position: every append in every step
+            for it in range(2 * R):
                 run.step(run.layers[it % R])
         gw.replay()
         torch.cuda.synchronize()
@@ -311,16 +390,23 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms_graph = e0.elapsed_time(e1) / K
-        del gw, gk
+        gl.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        gl.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_last = e0.elapsed_time(e1) / (2 * R)
+        del gw, gk, gl
 
-    # the same steps as direct single-kernel launches on one stream
+    # the same steps launched directly on one stream
     for w in range(args.warmup):
-        run.step_calls(run.layers[w % R])
+        run.step(run.layers[w % R], pos_w[w])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for it in range(K):
-        run.step_calls(run.layers[it % R])
+        run.step(run.layers[it % R], pos_t[it])
     e1.record()
     torch.cuda.synchronize()
     ms_stream = e0.elapsed_time(e1) / K
@@ -336,7 +422,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": kb / (k_ms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name, name)
     roof["kernel"] = name
     roof["kernel_ms"] = k_ms
     roof["bytes_per_launch"] = kb
@@ -362,10 +448,14 @@ def main():
         "config": {"workload": cfg.name, "sequences": cfg.B, "context": list(cfg.lens) if cfg.B <= 8 else
                    f"{cfg.B} seqs, mean {int(np.mean(cfg.lens))}", "q_heads": cfg.H, "head_dim": cfg.D,
                    "indexer": f"{cfg.HI}x{cfg.dI}", "topk": cfg.k, "m": cfg.m, "m2": cfg.m2, "window": cfg.W,
-                   "layers_rotated": R, "timing": "hip-graph replay" if ms_graph is not None else "stream"},
+                   "layers_rotated": R, "timing": "hip-graph replay" if ms_graph is not None else "stream",
+                   "positions": (f"{K} consecutive decode positions {cfg.lens[0] - K}..{cfg.lens[0] - 1}, each "
+                                 f"appending the entries its token completes") if consecutive else
+                   "last position of every sequence, every append in every step"},
         "hbm_frac_of_peak": sb / (ms / 1e3) / HBM_PEAK,
         "bytes_per_step": sb,
         "ms_per_step_stream": ms_stream,
+        "ms_step_all_appends": ms_last,
         "kernel_ms": {n: float(t) for n, t in zip(run.names, per)},
         "roofline": roof,
         "cpu_baseline": cpu,

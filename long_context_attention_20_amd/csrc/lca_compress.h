@@ -8,6 +8,10 @@
 
 namespace lca {
 
+// The large-window walk partitions a window as a block of this many threads
+// would, whatever the launch's block size.
+constexpr int kLargeLayoutThreads = 512;
+
 
 constexpr int kRunEntries = 16;  // entries per row group in small-window mode
 constexpr int kPrefetchM = 4;    // small-window strides up to this use the prefetching walk
@@ -279,13 +283,20 @@ __device__ void compress_large(const CompressStreamDev& s, const CompressParams&
 #pragma unroll
   for (int v = 0; v < NV; ++v) rc.ch0[v] = (v * G + li) * VE;
 
-  const int chunk = (s.w + RG - 1) / RG;
-  const int tb = rg * chunk;
+  // the window is cut into VG groups of consecutive tokens whatever the
+  // block size (the partition of a 512-thread block), so that every launch
+  // configuration pools and combines in the same order; a row group walks
+  // the groups rg, rg + RG, ...
+  const int VG = kLargeLayoutThreads / G;
+  const int chunk = (s.w + VG - 1) / VG;
+  const int C = s.C;
+  const int64_t base = j * s.m;
+  for (int vg = rg; vg < VG; vg += RG) {
+  const int tb = vg * chunk;
   const int te = min(s.w, tb + chunk);
   PoolState<VE> st[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) st[v].reset();
-  const int64_t base = j * s.m;
   int t = tb;
   // with per-channel logits a full batch of LB tokens keeps all of its raw
   // loads in flight at once (one memory round trip): an HCA window (w = 128
@@ -327,25 +338,25 @@ __device__ void compress_large(const CompressStreamDev& s, const CompressParams&
 #pragma unroll
     for (int v = 0; v < NV; ++v) st[v].add(z[v], x[v]);
   }
-  // partial states -> LDS [RG][3][C]
-  const int C = s.C;
+  // partial states -> LDS [VG][3][C]
 #pragma unroll
   for (int v = 0; v < NV; ++v)
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       const int c = rc.ch0[v] + e;
-      lds[(rg * 3 + 0) * C + c] = st[v].mx[e];
-      lds[(rg * 3 + 1) * C + c] = st[v].se[e];
-      lds[(rg * 3 + 2) * C + c] = st[v].sn[e];
+      lds[(vg * 3 + 0) * C + c] = st[v].mx[e];
+      lds[(vg * 3 + 1) * C + c] = st[v].se[e];
+      lds[(vg * 3 + 2) * C + c] = st[v].sn[e];
     }
+  }
   __syncthreads();
   // combine the row groups' states, one channel per thread; pooled value -> LDS
-  float* pooled = lds + RG * 3 * C;
+  float* pooled = lds + VG * 3 * C;
   for (int c = threadIdx.x; c < C; c += (int)blockDim.x) {
     float M = -INFINITY;
-    for (int r = 0; r < RG; ++r) M = fmaxf(M, lds[(r * 3 + 0) * C + c]);
+    for (int r = 0; r < VG; ++r) M = fmaxf(M, lds[(r * 3 + 0) * C + c]);
     float se = 0.f, sn = 0.f;
-    for (int r = 0; r < RG; ++r) {
+    for (int r = 0; r < VG; ++r) {
       const float m = lds[(r * 3 + 0) * C + c];
       const float f = m == -INFINITY ? 0.f : __expf(m - M);
       se = fmaf(lds[(r * 3 + 1) * C + c], f, se);

@@ -70,7 +70,8 @@ int setup_compress(const lca_compress_stream* streams, int n, const int64_t* tok
     d.block_begin = (int)blocks;
     blocks += (int64_t)d.bps * B;
     if (!d.small) {
-      size_t need = ((size_t)RG * 3 + 1) * in.C * sizeof(float);
+      const int VG = kLargeLayoutThreads / d.G;
+      size_t need = ((size_t)VG * 3 + 1) * in.C * sizeof(float);
       if (need > lds_bytes) lds_bytes = need;
     }
   }

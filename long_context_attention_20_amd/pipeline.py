@@ -78,9 +78,12 @@ class HybridAttention:
             csa_off_h=co, hca_off_h=ho)
 
     # -------------------------------------------------------------- a1
-    def compress_streams(self, caches: Caches, raw: dict, done_h: Sequence[int], which=("csa", "idx", "hca")):
-        """Descriptors of the entries completed after done_h[b] tokens."""
-        lens = caches.lens
+    def compress_streams(self, caches: Caches, raw: dict, done_h: Sequence[int], which=("csa", "idx", "hca"),
+                         lens_h: Optional[Sequence[int]] = None):
+        """Descriptors of the entries completed after done_h[b] tokens (up to
+        lens_h[b] tokens, default the caches' lengths; the sizes only bound
+        the launch, the kernels read the lengths from tok_off)."""
+        lens = caches.lens if lens_h is None else lens_h
         new_csa = max(n_windows(L, self.m, self.w) - n_windows(d, self.m, self.w) for L, d in zip(lens, done_h))
         new_hca = max(n_windows(L, self.m2, self.w2) - n_windows(d, self.m2, self.w2) for L, d in zip(lens, done_h))
         streams = []
@@ -110,10 +113,11 @@ class HybridAttention:
         for g in groups.values():
             ops.kv_compress(g, tok_off, done_len, self.eps)
 
-    def _append(self, caches: Caches, raw: dict, tok_off, done_len, done_h, which=("csa", "idx", "hca")):
+    def _append(self, caches: Caches, raw: dict, tok_off, done_len, done_h, which=("csa", "idx", "hca"),
+                lens_h=None):
         """Launch the compression of the entries completed after done_h tokens
         (one launch when the streams share a vector width)."""
-        streams = self.compress_streams(caches, raw, done_h, which)
+        streams = self.compress_streams(caches, raw, done_h, which, lens_h)
         groups: Dict[int, list] = {}
         for s in streams:
             lanes = s["src"].shape[-1] // (8 if s["src"].dtype == torch.bfloat16 else 4)
@@ -207,14 +211,16 @@ class HybridAttention:
 
     def decode_step(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos,
                     bufs: dict, done_len: Optional[torch.Tensor] = None, done_h: Optional[Sequence[int]] = None,
-                    side: Optional["torch.cuda.Stream"] = None):
+                    side: Optional["torch.cuda.Stream"] = None, lens_h: Optional[Sequence[int]] = None):
         """One decode (or prefill-chunk) step of mode A: append the entries the
         new tokens complete (when done_len is given), score and select the CSA
         entries, attend to the selected CSA entries, the visible HCA entries
         and the window in one launch, and merge the partials with the sink.
         With one query row per sequence the appends ride in the scoring
         launch.  With a side stream the HCA append runs there instead, beside
-        the indexer (the join costs a cross-queue wait in a graph)."""
+        the indexer (the join costs a cross-queue wait in a graph).  lens_h:
+        host copy of the sequence lengths tok_off describes, when they are
+        shorter than the caches'."""
         main = torch.cuda.current_stream()
         join = None
         scored = False
@@ -224,12 +230,12 @@ class HybridAttention:
                 fork.record(main)
                 side.wait_event(fork)
                 with torch.cuda.stream(side):
-                    self._append(caches, raw, tok_off, done_len, done_h, ("hca",))
+                    self._append(caches, raw, tok_off, done_len, done_h, ("hca",), lens_h)
                     join = torch.cuda.Event()
                     join.record(side)
-                self._append(caches, raw, tok_off, done_len, done_h, ("csa", "idx"))
+                self._append(caches, raw, tok_off, done_len, done_h, ("csa", "idx"), lens_h)
             else:
-                streams = self.compress_streams(caches, raw, done_h)
+                streams = self.compress_streams(caches, raw, done_h, lens_h=lens_h)
                 idx_st = [st for st in streams if st["out"] is caches.ikey]
                 kv_st = [st for st in streams if st["out"] is not caches.ikey]
                 if idx_st and q.shape[0] == len(caches.lens):
@@ -238,7 +244,7 @@ class HybridAttention:
                                                self.eps)
                     scored = True
                 else:
-                    self._append(caches, raw, tok_off, done_len, done_h)
+                    self._append(caches, raw, tok_off, done_len, done_h, lens_h=lens_h)
         if not scored:
             ops.csa_index_score(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w,
                                 bufs["max_csa"], bufs["ws_idx"])

@@ -444,3 +444,46 @@ def test_index_score_append_equals_separate(rmsnorm_idx):
             bound = score_bound(f64(d["p"][b]), d["omega"][b].cpu().numpy().astype(np.float64), keys)
             for j in a1 ^ a2:
                 assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + 2 * bound[j], f"row {b}: {j} not a near tie"
+
+
+@pytest.mark.parametrize("p", [4986, 4987, 4991, 4863])
+def test_decode_step_at_earlier_position(p):
+    """A decode step at token position p of a one-sequence cache built for
+    L > p + 1 tokens, reading the sequence as its first p + 1 tokens
+    (tok_off = [0, p + 1]): it appends exactly the entries token p completes
+    and equals the oracle of the (p + 1)-token context.  p spans steps with
+    no append, a CSA/indexer append and an HCA append."""
+    L = 5000
+    cfg = li.small("position", 111, (L,), H=64, D=512, k=256)
+    cfg_p = li.small("position", 111, (p + 1,), H=64, D=512, k=256)
+    raw, raw_p = li.make_raw(cfg), li.make_raw(cfg_p)
+    for name in ("x", "a", "g", "u", "c"):
+        assert np.array_equal(raw[name][:p + 1], raw_p[name]), f"{name}: the generators are not prefix-stable"
+    for name in ("q", "p", "omega", "sigma"):
+        assert np.array_equal(raw[name], raw_p[name])
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    full = (caches.kv_csa.clone(), caches.ikey.clone(), caches.kv_hca.clone())
+    wiped = []
+    for t, m, w in ((caches.kv_csa, cfg.m, cfg.w), (caches.ikey, cfg.m, cfg.w), (caches.kv_hca, cfg.m2, cfg.w2)):
+        n0, n1 = ocmp.n_entries(p, m, w), ocmp.n_entries(p + 1, m, w)
+        t[n0:n1] = 0
+        wiped.append(n1 - n0)
+    tok_off = torch.tensor([0, p + 1], dtype=torch.int64, device="cuda")
+    q_pos = torch.tensor([p], dtype=torch.int32, device="cuda")
+    done = torch.tensor([p], dtype=torch.int64, device="cuda")
+    bufs = layer.decode_buffers(1, ocmp.n_entries(L, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m2, cfg.w2), "cuda",
+                                tdtype(cfg))
+    out = layer.decode_step(caches, d, tok_off, d["q"], d["p"], d["omega"], d["sigma"], q_pos, bufs,
+                            done_len=done, done_h=[p], lens_h=[p + 1])
+    torch.cuda.synchronize()
+    print(f"[position {p}] appended entries csa/idx/hca = {wiped}", flush=True)
+    for got, ref, name in zip((caches.kv_csa, caches.ikey, caches.kv_hca), full, ("kv_csa", "ikey", "kv_hca")):
+        assert torch.equal(got, ref), f"{name}: the step did not restore exactly the entries token {p} completes"
+    _, ores = opipe.run(raw_p, cfg_p)
+    res = ores[(0, 0)]
+    idx_h = bufs["idx"].cpu().numpy()[0]
+    assert set(idx_h[idx_h >= 0].tolist()) == set(res["sel"].tolist())
+    assert_close(f64(out)[0], res["out"], cfg.dtype, f"position {p}")
