@@ -226,6 +226,97 @@ class Runner:
             f()
 
 
+def prefill_flops(cfg):
+    """Algorithmic FLOPs of one prefill chunk step: indexer, sparse, HCA and
+    window attention of every query row (2 FLOP per multiply-add)."""
+    out = dict(indexer=0, sparse=0, hca=0, window=0)
+    for b, L in enumerate(cfg.lens):
+        for i in range(L - cfg.tq, L):
+            nv = n_windows(i + 1, cfg.m, cfg.w)
+            out["indexer"] += 2 * nv * cfg.dI * cfg.HI
+            out["sparse"] += 4 * cfg.H * cfg.D * min(cfg.k, nv)
+            out["hca"] += 4 * cfg.H * cfg.D * n_windows(i + 1, cfg.m2, cfg.w2)
+            out["window"] += 4 * cfg.H * cfg.D * min(cfg.W, i + 1)
+    return out
+
+
+def run_prefill(cfg, args, dev):
+    """One prefill chunk step per iteration: compress the chunk's entries,
+    score and select for every query row, attend (one launch for the three
+    branches), merge.  Reported against the matrix-core peak."""
+    import torch
+    import lca_inputs as li
+    from long_context_attention_20_amd import HybridAttention, ops
+    a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps)
+    raw = li.make_raw_torch(cfg, 0, dev)
+    caches = a.alloc_caches(cfg.lens, dev, raw["x"].dtype)
+    a.compress(caches, raw, raw["tok_off"])
+    done_h = [L - cfg.tq for L in cfg.lens]
+    done = torch.tensor(done_h, dtype=torch.int64, device=dev)
+    q_pos = raw["q_pos"].reshape(-1).contiguous()
+    q_pos_h = raw["q_pos"].reshape(-1).cpu().numpy()
+    rows = q_pos.numel()
+    qmax = int(q_pos_h.max()) + 1
+    max_csa = n_windows(qmax, cfg.m, cfg.w)
+    max_hca = n_windows(qmax, cfg.m2, cfg.w2)
+    ws = a.index_workspace(rows, max_csa, dev)
+    sc, sh, sw = a.fused_splits(rows, min(cfg.k, max_csa), max_hca, cfg.W)
+    bufs = dict(sc=sc, sh=sh, sw=sw, max_hca=max_hca, csa=(None, None), hca=(None, None), swa=(None, None))
+    idx = torch.empty((rows, cfg.k), dtype=torch.int32, device=dev)
+    out = torch.empty_like(raw["q"])
+    streams = a.compress_streams(caches, raw, done_h)
+    names = ["kv_compress", "csa_index_score", "csa_topk_select", "hybrid_attn", "swa_merge"]
+    holder = {}
+    calls = [
+        lambda: ops.kv_compress(streams, raw["tok_off"], done, cfg.eps),
+        lambda: ops.csa_index_score(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
+                                    max_csa, ws),
+        lambda: ops.csa_topk_select(caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws, idx=idx),
+        lambda: holder.__setitem__("parts", ops.hybrid_attn(raw["q"], q_pos,
+                                                            a.attn_sources(caches, raw["x"], raw["tok_off"], idx,
+                                                                           bufs), a.scale, cfg.eps)),
+        lambda: ops.swa_merge(raw["q"], None, None, None, raw["sigma"], holder["parts"], 0, a.scale, cfg.eps, None,
+                              out=out),
+    ]
+    K, W = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
+    for _ in range(W):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    for it in range(K):
+        ev[it][0].record()
+        for j, f in enumerate(calls):
+            f()
+            ev[it][j + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([[ev[it][j].elapsed_time(ev[it][j + 1]) for j in range(len(calls))] for it in range(K)]).mean(0)
+    ms = float(per.sum())
+    fl = prefill_flops(cfg)
+    tot = sum(fl.values())
+    j = names.index("hybrid_attn")
+    attn_fl = fl["sparse"] + fl["hca"] + fl["window"]
+    res = {
+        "metric": "prefill query-tokens/s per layer (Flash shape, 4096-token chunk after 256K); MFMA utilisation",
+        "value": cfg.B * cfg.tq / (ms / 1e3),
+        "unit": "q-tok/s/layer",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1), generated on the GPU)",
+        "config": {"workload": cfg.name, "cached": done_h[0], "chunk": cfg.tq, "q_heads": cfg.H, "head_dim": cfg.D,
+                   "indexer": f"{cfg.HI}x{cfg.dI}", "topk": cfg.k, "splits": [sc, sh, sw],
+                   "timing": "stream, events between the calls"},
+        "flops_per_step": fl,
+        "mfma_frac_of_peak": tot / (ms / 1e3) / MFMA_BF16_PEAK,
+        "kernel_ms": {n: float(t) for n, t in zip(names, per)},
+        "roofline": {"bound": "mfma", "kernel": "hybrid_attn", "achieved": attn_fl / (per[j] / 1e3) / 1e12,
+                     "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": attn_fl / (per[j] / 1e3) / MFMA_BF16_PEAK, "traffic": None,
+                     "kernel_ms": float(per[j]), "flops_per_launch": attn_fl},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res))
+
+
 def cpu_baseline(cfg, state, budget_s):
     """The oracle (float64, numpy) on this host: one decode step per query of
     layer 0 -- append the completed entries, score, select, attend, merge --
@@ -307,10 +398,11 @@ def main():
         return
     import lca_inputs as li
     cfg = li.CONFIGS[args.config]
-    if cfg.tq != 1:
-        raise SystemExit("bench.py measures decode workloads (one query token per sequence)")
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if cfg.tq != 1:
+        run_prefill(cfg, args, dev)
+        return
     sb = step_bytes(cfg)
     R = args.layers or max(1, -(-2 * MALL_BYTES // sb))
     t0 = time.perf_counter()

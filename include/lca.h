@@ -116,8 +116,9 @@ int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int
  * idx[r, 0..k) receives the k candidates of largest score, ties broken toward
  * the smaller j, as local entry indices (0-based within the sequence).  When a
  * query has fewer than k candidates all are selected and the rest of its row is
- * -1.  The order of a row is deterministic (candidates above the k-th score's
- * top bits in index order, then the rest in index order) but is not a ranking.
+ * -1.  A row lists its entries in ascending index order when the query has
+ * at most 262144 candidates (a deterministic order beyond that); it is not a
+ * ranking.
  *
  *   p        [B*Tq, H_I, d_I]  indexer queries (dtype)
  *   omega    [B*Tq, H_I]       fp32 head weights

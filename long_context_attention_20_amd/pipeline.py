@@ -164,15 +164,23 @@ class HybridAttention:
         max_hca = n_windows(qmax, self.m2, self.w2)
         ws = self.index_workspace(rows, max_csa, dev)
         idx = ops.csa_index_topk(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w, max_csa, ws)
-        sc = self.split_csa or self.default_splits(rows, self.k)
-        sh = self.split_hca or self.default_splits(rows, max_hca)
-        csa = ops.csa_sparse_attn(q, caches.kv_csa, caches.csa_off, idx, self.scale, self.eps, sc)
-        hca = ops.hca_attn(q, caches.kv_hca, caches.hca_off, q_pos, self.m2, self.w2, max_hca, self.scale, self.eps,
-                           sh)
         wsm = self._workspace(f"swa{rows}", ops.swa_merge_workspace(rows, self.H, self.D), dev, zero=False)
         if mode == "A":
-            out = ops.swa_merge(q, x, tok_off, q_pos, sigma, [csa, hca], self.W, self.scale, self.eps, wsm)
+            # the three branches in one launch, merged with the sink
+            sc, sh, sw = self.fused_splits(rows, min(self.k, max_csa), max_hca, self.W)
+            sc, sh = self.split_csa or sc, self.split_hca or sh
+            # the dense source is always launched (an empty one writes o = 0,
+            # lse = -inf), so that the partials are there for every row
+            bufs = dict(sc=sc, sh=sh, sw=sw, max_hca=1, csa=(None, None), hca=(None, None), swa=(None, None))
+            parts = ops.hybrid_attn(q, q_pos, self.attn_sources(caches, x, tok_off, idx, bufs), self.scale, self.eps)
+            csa, hca = parts[0], parts[1]
+            out = ops.swa_merge(q, None, None, None, sigma, parts, 0, self.scale, self.eps, None)
         else:
+            sc = self.split_csa or self.default_splits(rows, self.k)
+            sh = self.split_hca or self.default_splits(rows, max_hca)
+            csa = ops.csa_sparse_attn(q, caches.kv_csa, caches.csa_off, idx, self.scale, self.eps, sc)
+            hca = ops.hca_attn(q, caches.kv_hca, caches.hca_off, q_pos, self.m2, self.w2, max_hca, self.scale,
+                               self.eps, sh)
             o1 = ops.swa_merge(q, x, tok_off, q_pos, sigma, [csa], self.W, self.scale, self.eps, wsm)
             o2 = ops.swa_merge(q, x, tok_off, q_pos, sigma, [hca], self.W, self.scale, self.eps, wsm)
             out = (o1, o2)

@@ -119,3 +119,60 @@ def test_pro_varlen_full():
     rows = [int(np.argmin(lens)), int(np.argmax(lens)), 17]
     _check_rows(cfg, raw, caches, bufs, out, rows, np.random.default_rng(3))
     assert torch.isfinite(out.float()).all()
+
+
+def test_flash_prefill_full():
+    """The Flash-shaped chunked prefill (4096 query tokens after 262144 cached
+    ones): the chunk's entries appended by kv_compress, then scores, top-k
+    and the fused attention for every row; rows 0, 1365, 2731 and 4095 are
+    checked against the oracle (selected sets, and outputs stage-wise from
+    the GPU caches and selection, end to end when the sets agree)."""
+    cfg = li.FLASH_PREFILL
+    raw = li.make_raw_torch(cfg, 0, "cuda")
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", raw["x"].dtype)
+    layer.compress(caches, raw, raw["tok_off"])
+    full = (caches.kv_csa.clone(), caches.ikey.clone(), caches.kv_hca.clone())
+    L = cfg.lens[0]
+    cached = L - cfg.tq
+    n0, h0 = ocmp.n_entries(cached, cfg.m, cfg.w), ocmp.n_entries(cached, cfg.m2, cfg.w2)
+    caches.kv_csa[n0:] = 0
+    caches.ikey[n0:] = 0
+    caches.kv_hca[h0:] = 0
+    done = torch.tensor([cached], dtype=torch.int64, device="cuda")
+    layer.compress(caches, raw, raw["tok_off"], done_len=done, done_len_h=[cached])
+    for got, ref, name in zip((caches.kv_csa, caches.ikey, caches.kv_hca), full, ("kv_csa", "ikey", "kv_hca")):
+        assert torch.equal(got, ref), f"{name}: chunk append differs from the full build"
+    q_pos = raw["q_pos"].reshape(-1).contiguous()
+    out, inter = layer.step(caches, raw["x"], raw["tok_off"], raw["q"], raw["p"], raw["omega"], raw["sigma"], q_pos,
+                            raw["q_pos"].reshape(-1).cpu().numpy(), keep=True)
+    torch.cuda.synchronize()
+    idx_h = inter["idx"].cpu().numpy()
+    out_h = f64(out)
+    ikey = f64(caches.ikey)
+    kv_csa = f64(caches.kv_csa)
+    kv_hca = f64(caches.kv_hca)
+    x = _host(raw["x"])
+    sig = raw["sigma"].cpu().numpy().astype(np.float64)
+    for t in (0, 1365, 2731, cfg.tq - 1):
+        i = cached + t
+        print(f"[flash_prefill] row {t} (position {i})", flush=True)
+        nv = ocmp.n_visible(i, cfg.m, cfg.w)
+        nh = ocmp.n_visible(i, cfg.m2, cfg.w2)
+        p = f64(raw["p"][t])
+        om = raw["omega"][t].cpu().numpy().astype(np.float64)
+        s_ref = oidx.scores(p, om, ikey[:nv])
+        bound = score_bound(p, om, ikey[:nv])
+        sel = idx_h[t][idx_h[t] >= 0]
+        assert len(sel) == min(cfg.k, nv) and np.all(sel < nv) and np.all(np.diff(sel) > 0)
+        ref_sel = oidx.topk(s_ref, cfg.k)
+        kth = s_ref[ref_sel[-1]]
+        diff = set(sel.tolist()) ^ set(ref_sel.tolist())
+        for j in diff:
+            assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + bound[j], f"entry {j} is not a near tie"
+        qhat = oatt.normalize_query(f64(raw["q"][t]), cfg.eps, cfg.dtype)
+        win = oatt.normalize_tokens(x[max(0, i - cfg.W + 1):i + 1].astype(np.float64), cfg.eps, cfg.dtype)
+        parts = [oatt.partial(qhat, kv_csa[sel], cfg.scale), oatt.partial(qhat, kv_hca[:nh], cfg.scale),
+                 oatt.partial(qhat, win, cfg.scale)]
+        o_ref, _ = oatt.merge(parts, sig)
+        assert_close(out_h[t], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"prefill row {t}")

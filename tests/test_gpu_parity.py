@@ -487,3 +487,46 @@ def test_decode_step_at_earlier_position(p):
     idx_h = bufs["idx"].cpu().numpy()[0]
     assert set(idx_h[idx_h >= 0].tolist()) == set(res["sel"].tolist())
     assert_close(f64(out)[0], res["out"], cfg.dtype, f"position {p}")
+
+
+def _topk_direct(ikey, p, omega, k, n_entries):
+    """csa_index_topk over one row whose query sees every entry of ikey."""
+    from long_context_attention_20_amd import ops
+    m, w = 4, 8
+    csa_off = torch.tensor([0, n_entries], dtype=torch.int64, device="cuda")
+    q_pos = torch.tensor([(n_entries - 1) * m + w - 1], dtype=torch.int32, device="cuda")
+    ws = torch.zeros(ops.csa_index_topk_workspace(1, n_entries, k), dtype=torch.uint8, device="cuda")
+    scores = torch.empty((1, n_entries), dtype=torch.float32, device="cuda")
+    idx = ops.csa_index_topk(p, omega, ikey, csa_off, q_pos, k, m, w, n_entries, ws, scores=scores)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()[0], scores.cpu().numpy()[0]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_topk_concentrated_in_few_blocks(dtype):
+    """The whole top-k inside two 512-entry score blocks (a clustered score
+    distribution, as when the query matches one stretch of the context): the
+    selected set is the exact top-k (no ties)."""
+    rng = np.random.default_rng(112)
+    N, k, HI, dI = 9000, 256, 4, 64
+    keys = rng.standard_normal((N, dI)).astype(np.float32) * 0.1
+    p = rng.standard_normal((1, HI, dI)).astype(np.float32)
+    om = np.abs(rng.standard_normal((1, HI))).astype(np.float32)
+    hot = np.arange(600, 1500)
+    keys[hot] += 2.0 * p[0, 0] / np.linalg.norm(p[0, 0]) * rng.uniform(1.0, 2.0, (len(hot), 1)).astype(np.float32)
+    kt = torch.from_numpy(keys).to("cuda", dtype)
+    idx, s_gpu = _topk_direct(kt, torch.from_numpy(p).to("cuda", dtype), torch.from_numpy(om).cuda(), k, N)
+    ref = np.sort(oidx.topk(s_gpu.astype(np.float64), k))
+    assert np.array_equal(np.sort(idx), ref)
+    assert np.all((idx >= 600) & (idx < 1500))
+
+
+def test_topk_all_ties():
+    """Every score equal (zero head weights): the k smallest indices."""
+    rng = np.random.default_rng(113)
+    N, k = 20000, 512
+    kt = torch.from_numpy(rng.standard_normal((N, 64)).astype(np.float32)).to("cuda", torch.bfloat16)
+    p = torch.from_numpy(rng.standard_normal((1, 4, 64)).astype(np.float32)).to("cuda", torch.bfloat16)
+    om = torch.zeros((1, 4), dtype=torch.float32, device="cuda")
+    idx, _ = _topk_direct(kt, p, om, k, N)
+    assert np.array_equal(np.sort(idx), np.arange(k))
