@@ -7,18 +7,22 @@ the fraction of peak HBM bandwidth it corresponds to.
 A step is one pass of the whole hot path for one query token per sequence:
   csa_index_score_append (the CSA, indexer-key and HCA entries the new token
     completes, and the index scores, in one launch)
-  -> csa_topk_select -> hybrid_attn (CSA sparse + HCA dense + window
-  partials, one launch) -> swa_merge (sink + merge)
+  -> csa_topk_filter (the entries above the top-k threshold bin, and the
+    candidates inside it)
+  -> hybrid_attn (one launch: each sparse block's share of the exact top-k,
+    CSA sparse + HCA dense + window partials)
+  -> swa_merge (sink + merge)
 on one stream, over caches resident in HBM.  To keep the 256 MB Infinity Cache from serving
 the caches, steps rotate over R layers, each with its own raw streams and
 caches (R * per-step bytes >= 2 x 256 MB).
 
 Timed regions (HIP events on the launch stream, synchronised on both sides):
   1. per kernel: one HIP graph of that kernel's launch for each of the R
-     rotated layers, replayed 8 times (the top-k kernels, which consume the
-     histogram the score kernel builds, are timed with it and the score
-     kernel's time subtracted); the dominant kernel's average launch
-     duration gives the roofline;
+     rotated layers, replayed 8 times (the filter and the attention launch,
+     which consume what the launches before them leave in the index
+     workspace, are timed in a chain after them, whose time is
+     subtracted); the dominant kernel's average launch duration gives the
+     roofline;
   2. the headline: the W warmup steps and then the K timed steps, each set
      captured as one HIP graph of consecutive layer steps and replayed once.
      With one sequence the K steps are K consecutive decode positions, each
@@ -121,9 +125,12 @@ def kernel_cost(cfg, name):
             nwin = min(cfg.W, L)
             by += nwin * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * nwin
-        elif name == "hybrid_attn":
+        elif name == "csa_topk_filter":
+            by += ncsa * 4                                     # every score read once
+        elif name == "hybrid_attn":                      # the selection's end + the three branches
             nwin = min(cfg.W, L)
-            by += (kk + nh + nwin) * cfg.D * e + cfg.H * cfg.D * e + kk * 4
+            by += kk * 4                                       # selection written
+            by += (kk + nh + nwin) * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * (kk + nh + nwin)
         elif name == "swa_merge":
             by += cfg.H * cfg.D * e + cfg.H * 4                # output + sink
@@ -181,12 +188,13 @@ class Runner:
         self.bufs = a.decode_buffers(rows, n_windows(qmax, cfg.m, cfg.w), n_windows(qmax, cfg.m2, cfg.w2), dev,
                                      self.layers[0].q.dtype)
         self.sc, self.sh, self.sw = self.bufs["sc"], self.bufs["sh"], self.bufs["sw"]
-        self.names = ["csa_index_score_append", "csa_topk_select", "hybrid_attn", "swa_merge"]
-        self.launches = {"csa_topk_select": 2}  # kernels per call (default 1)
-        # the top-k kernels consume and clear the histogram the score kernel
-        # builds, so they are timed together with it (score subtracted)
-        self.timed = ["csa_index_score_append", "csa_index_score_append+csa_topk_select", "hybrid_attn",
-                      "swa_merge"]
+        self.names = ["csa_index_score_append", "csa_topk_filter", "hybrid_attn", "swa_merge"]
+        self.launches = {}  # kernels per call (default 1)
+        # the filter consumes the score kernel's histogram and the attention
+        # launch the filter's lists (and clears the histogram): each is timed
+        # at the end of the chain of calls before it (that chain subtracted)
+        self.timed = ["csa_index_score_append", "csa_index_score_append+csa_topk_filter",
+                      "csa_index_score_append+csa_topk_filter+hybrid_attn", "swa_merge"]
 
     def step(self, L, pos=None):
         """The whole decode step (four calls on the current stream), at the
@@ -203,14 +211,13 @@ class Runner:
         st = a.compress_streams(c, L.raw, L.done_h)
         idx_st = [x for x in st if x["out"] is c.ikey][0]
         kv_st = [x for x in st if x["out"] is not c.ikey]
-        srcs = a.attn_sources(c, L.raw["x"], L.tok_off, bf["idx"], bf)
+        srcs = a.attn_sources(c, L.raw["x"], L.tok_off, None, bf)
         parts = [bf["csa"], bf["hca"], bf["swa"]][:len(srcs)]
         return [
             lambda: ops.csa_index_score_append(L.p, L.omega, c.ikey, c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w,
                                                bf["max_csa"], bf["ws_idx"], idx_st, kv_st, L.tok_off, L.done,
                                                cfg.eps),
-            lambda: ops.csa_topk_select(c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, bf["max_csa"], bf["ws_idx"],
-                                        idx=bf["idx"]),
+            lambda: ops.csa_topk_filter(c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, bf["max_csa"], bf["ws_idx"]),
             lambda: ops.hybrid_attn(L.q, L.q_pos, srcs, a.scale, cfg.eps),
             lambda: ops.swa_merge(L.q, None, None, None, L.sigma, parts, 0, a.scale, cfg.eps, None, out=bf["out"]),
         ]
@@ -437,7 +444,14 @@ def main():
         tper[i] = e0.elapsed_time(e1) / (reps * R)
         del g
     tt = dict(zip(run.timed, tper))
-    per = np.array([tt[n] if n in tt else tt[run.names[0] + "+" + n] - tt[run.names[0]] for n in run.names])
+    def own_time(n):
+        for key in run.timed:
+            if key == n:
+                return tt[key]
+            if key.endswith("+" + n):
+                return tt[key] - tt[key[:-len(n) - 1]]
+        raise KeyError(n)
+    per = np.array([own_time(n) for n in run.names])
     # the dominant kernel: the longest single launch
     dom = int(np.argmax([t / run.launches.get(n, 1) for n, t in zip(run.names, per)]))
     print("[bench] per-kernel ms (graph, rotated layers): " +

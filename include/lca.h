@@ -128,9 +128,12 @@ int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int
  *   scores   optional fp32 [B*Tq, max_entries] output of every candidate's
  *            score (entry j at column j); NULL to keep them in the workspace
  *   ws       device workspace of at least lca_csa_index_topk_workspace()
- *            bytes.  It must be ZERO-FILLED before its first use; every call
- *            that returns LCA_OK leaves it zero-filled again.  Calls that
- *            share a workspace must be ordered on one stream.
+ *            bytes.  It must be ZERO-FILLED before its first use; after
+ *            that each score call and the selection that must follow it
+ *            (lca_csa_topk_select, or lca_csa_topk_filter and then a TOPK
+ *            source of lca_hybrid_attn) leave it ready for the next score
+ *            call.  Calls that share a
+ *            workspace must be ordered on one stream.
  * Supported: H_I * d_I <= 1024, d_I multiple of 8, k in [1, 4096],
  * entries per sequence < 2^24. */
 size_t lca_csa_index_topk_workspace(int n_rows, int64_t max_entries, int k);
@@ -139,11 +142,12 @@ int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, cons
                        int64_t max_entries, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
                        int dtype, void* stream);
 
-/* The two halves of lca_csa_index_topk, one kernel each, same arguments and
- * workspace: lca_csa_index_score (a2) writes the scores and the selection
- * histogram into the workspace (and into `scores` when it is not NULL);
- * lca_csa_topk_select (a3) must follow on the same stream with the same
- * arguments and workspace (and the same `scores` pointer). */
+/* The two halves of lca_csa_index_topk, same arguments and workspace:
+ * lca_csa_index_score writes the scores and the selection histogram into the
+ * workspace (and the scores into `scores` when it is not NULL);
+ * lca_csa_topk_select (two launches: filter, then the exact selection) must
+ * follow on the same stream with the same arguments and workspace (and the
+ * same `scores` pointer), or a TOPK source of lca_hybrid_attn in its place. */
 int lca_csa_index_score(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
                         const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
                         int64_t max_entries, float* scores, void* ws, size_t ws_bytes, int dtype,
@@ -165,8 +169,8 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
  *               C == d_I, same m and w
  *   kv_streams  0 to 4 further streams sharing one vector width
  *   tok_off, done_len  as lca_kv_compress (done_len required)
- * Other arguments as lca_csa_index_score with Tq = 1; the workspace must be
- * clean (as left by lca_csa_topk_select). */
+ * Other arguments as lca_csa_index_score with Tq = 1; the workspace as
+ * lca_csa_index_score's. */
 int lca_csa_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
                                const int32_t* q_pos, int B, int H_I, int d_I, int k, int m, int w,
                                int64_t max_entries, const lca_compress_stream* idx_stream,
@@ -177,6 +181,16 @@ int lca_csa_index_score_append(const void* p, const float* omega, const void* ik
 int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                         int64_t max_entries, int32_t* idx, const float* scores, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* The first of lca_csa_topk_select's two launches alone, same arguments but
+ * idx: from the histogram the score call left, every entry above the bin
+ * holding the k-th largest score goes to a list, every entry inside it to a
+ * candidate list (with a histogram of their next key bits), all in the
+ * workspace.  The exact selection from those lists is then made by a TOPK
+ * source of lca_hybrid_attn (same workspace and arguments), which must
+ * follow on the same stream. */
+int lca_csa_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                        int64_t max_entries, const float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Attention partials (a4, a5)
@@ -249,13 +263,27 @@ int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int
  *   LCA_SRC_WINDOW  raw rows max(0, i-W+1) .. i of kv packed by off, each
  *                   RMS-normalised over D on load (as lca_swa_attn, any
  *                   n_split)
+ *   LCA_SRC_TOPK    the end of the top-k selection and the sparse branch in
+ *                   one: after a score call and lca_csa_topk_filter (same
+ *                   stream, workspace ws, scores, k slots, m2 = m, w2 = w
+ *                   (the CSA entries' stride and window), max_entries, kv's
+ *                   offsets as csa_off), it stands for the rest of
+ *                   lca_csa_topk_select into idx_out followed by a GATHER
+ *                   source over idx_out: idx_out receives exactly what
+ *                   lca_csa_topk_select would write (ascending order when a
+ *                   row has at most 262144 candidates).  On the bf16
+ *                   matrix-core path with max_entries <= 262144 every block
+ *                   of the sparse branch runs the exact selection itself
+ *                   from the filtered lists (one launch in all); elsewhere
+ *                   the selection's own launch comes first.  At most one
+ *                   TOPK source per call.
  * The sources share q [B*Tq, H, D], q_pos (device int32 [B*Tq]; read by the
  * DENSE and WINDOW sources), scale and eps.  One launch costs one kernel
  * start and lets the branches' blocks share the machine.  The bf16
  * matrix-core path (H a multiple of 16) stages at most 2048 gathered slots
  * per split: ceil(ceil(k/32) / n_split) * 32 <= 2048, else
  * LCA_ERR_UNSUPPORTED.  1 <= n_src <= 3; 1 <= n_split <= 256 per source. */
-enum { LCA_SRC_DENSE = 0, LCA_SRC_GATHER = 1, LCA_SRC_WINDOW = 2 };
+enum { LCA_SRC_DENSE = 0, LCA_SRC_GATHER = 1, LCA_SRC_WINDOW = 2, LCA_SRC_TOPK = 3 };
 
 typedef struct lca_attn_source {
   int32_t kind;          /* LCA_SRC_* */
@@ -268,6 +296,12 @@ typedef struct lca_attn_source {
   int32_t n_split;       /* key-range parts */
   float* o_part;         /* fp32 [n_split, B*Tq, H, D] */
   float* lse;            /* fp32 [n_split, B*Tq, H] */
+  /* LCA_SRC_TOPK only (zero otherwise): */
+  void* ws;              /* index workspace of the preceding score call */
+  size_t ws_bytes;
+  int64_t max_entries;   /* as passed to the score call */
+  const float* scores;   /* the score call's scores output, or NULL */
+  int32_t* idx_out;      /* device int32 [B*Tq, k]: receives the selection */
 } lca_attn_source;
 
 int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,

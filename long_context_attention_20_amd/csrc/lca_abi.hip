@@ -36,6 +36,8 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
                               int dtype, hipStream_t stream);
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
+int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                       int64_t maxN, const float* scores, void* ws, hipStream_t stream);
 int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
                      int H, int D, float scale, float eps, int dtype, hipStream_t stream);
 
@@ -222,6 +224,16 @@ int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int
                 "csa_topk_select");
 }
 
+int lca_csa_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                        int64_t max_entries, const float* scores, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_index("csa_topk_filter", false, nullptr, nullptr, nullptr, csa_off, q_pos, B, Tq, 1, 8, k, m, w,
+                       max_entries, ws, ws_bytes, LCA_BF16);
+  if (rc != LCA_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_topk_filter(csa_off, q_pos, B, Tq, k, m, w, max_entries, scores, ws, st), st,
+                "csa_topk_filter");
+}
+
 int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
                        const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
                        int64_t max_entries, int32_t* idx, float* scores, void* ws, size_t ws_bytes, int dtype,
@@ -290,12 +302,23 @@ int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const
   LCA_REQUIRE(srcs != nullptr && n_src >= 1 && n_src <= 3, LCA_ERR_INVALID_ARG,
               "hybrid_attn: n_src=%d not in [1,3] (or srcs is NULL)", n_src);
   bool need_pos = false;
+  int n_topk = 0;
   for (int i = 0; i < n_src; ++i) {
     const lca_attn_source& x = srcs[i];
-    LCA_REQUIRE(x.kind == LCA_SRC_DENSE || x.kind == LCA_SRC_GATHER || x.kind == LCA_SRC_WINDOW,
+    LCA_REQUIRE(x.kind == LCA_SRC_DENSE || x.kind == LCA_SRC_GATHER || x.kind == LCA_SRC_WINDOW ||
+                    x.kind == LCA_SRC_TOPK,
                 LCA_ERR_INVALID_ARG, "hybrid_attn: source %d has kind %d", i, x.kind);
-    int rc = check_attn("hybrid_attn", q, x.kv, x.off, x.kind == LCA_SRC_GATHER ? (const void*)x.idx : q, B, Tq, H,
-                        D, scale, eps, x.n_split, x.o_part, x.lse, dtype);
+    if (x.kind == LCA_SRC_TOPK) {
+      LCA_REQUIRE(++n_topk == 1, LCA_ERR_INVALID_ARG, "hybrid_attn: more than one TOPK source");
+      LCA_REQUIRE(x.idx_out != nullptr, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: idx_out is NULL", i);
+      LCA_REQUIRE(q_pos != nullptr, LCA_ERR_INVALID_ARG, "hybrid_attn: q_pos is NULL");
+      int rc = check_index("hybrid_attn", false, nullptr, nullptr, nullptr, x.off, q_pos, B, Tq, 1, 8, x.k, x.m2,
+                           x.w2, x.max_entries, x.ws, x.ws_bytes, LCA_BF16);
+      if (rc != LCA_OK) return rc;
+    }
+    const void* lst = x.kind == LCA_SRC_GATHER ? (const void*)x.idx : x.kind == LCA_SRC_TOPK ? (const void*)x.idx_out : q;
+    int rc = check_attn("hybrid_attn", q, x.kv, x.off, lst, B, Tq, H, D, scale, eps, x.n_split, x.o_part, x.lse,
+                        dtype);
     if (rc != LCA_OK) return rc;
     if (x.kind == LCA_SRC_GATHER)
       LCA_REQUIRE(x.k >= 1 && x.k <= 65536, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: k=%d", i, x.k);

@@ -25,11 +25,11 @@
 // O^T comes from the same rows through ds_read_b64_tr_b16, whose 16-lane
 // transpose hands lane i column i of a 4-row x 16-column block.  The next
 // tile's global loads are in flight while the current tile is computed.
-#include "lca_common.h"
+#include "lca_topk.h"
 
 namespace lca {
 
-enum { SRC_DENSE = 0, SRC_GATHER = 1, SRC_WINDOW = 2 };
+enum { SRC_DENSE = 0, SRC_GATHER = 1, SRC_WINDOW = 2, SRC_TOPK = 3 };
 
 // One key source of a launch; its splits take blockIdx.x in
 // [block_begin, block_begin + n_split).
@@ -37,9 +37,10 @@ struct AttnSrc {
   const void* kv;       // cache rows (DENSE, GATHER) or raw rows (WINDOW)
   const int64_t* off;   // [B+1] row offsets of kv
   const int32_t* idx;   // GATHER: [rows, k]
+  int32_t* idx_out;     // TOPK: [rows, k] receives the selected entries
   int kind;             // SRC_*
-  int k;                // GATHER slots per row
-  int m2, w2;           // DENSE visibility
+  int k;                // GATHER / TOPK slots per row
+  int m2, w2;           // DENSE / TOPK visibility
   int W;                // WINDOW length
   int n_split;
   int block_begin;
@@ -58,6 +59,7 @@ struct AttnParams {
   int n_x;              // splits of all sources (blocks per row and head block)
   int n_hb;             // head blocks per row (matrix-core path)
   AttnSrc s[kMaxSrc];
+  TopkWs tw;            // the index workspace of a TOPK source (filtered)
 };
 
 // Source of split column bx (uniform) and the split inside it.
@@ -78,7 +80,7 @@ __device__ __forceinline__ int64_t attn_keys(const AttnParams& a, const AttnSrc&
   const int64_t nseq = s.off[b + 1] - base;
   *first = base;
   *nseq_out = nseq;
-  if (s.kind == SRC_GATHER) return s.k;
+  if (s.kind == SRC_GATHER || s.kind == SRC_TOPK) return s.k;
   const int64_t i = a.q_pos[r];
   if (s.kind == SRC_DENSE) {
     int64_t n = n_windows(i + 1, s.m2, s.w2);
@@ -135,7 +137,7 @@ constexpr int kAttnThreads = 512;
 constexpr int kTeamThreads = 256;
 constexpr int kAttnHeads = 32;      // query heads per block
 
-template <int D>
+template <int D, bool TOPK>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnParams a) {
   constexpr int DH = D / 2;                 // dims per wave
   constexpr int KS = DH / 32;               // k-steps of the S partial
@@ -147,7 +149,13 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int KB = KS < 2 ? KS : 2;       // k-steps per operand batch
   constexpr int OB = DB < 4 ? DB : 4;       // dim blocks per operand batch
   constexpr int TILE_ELEMS = kTile * PITCH;
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][TILE_ELEMS];  // [team][buffer]
+  // [team][buffer] tiles; with a TOPK source the same memory first holds the
+  // selection's scratch
+  constexpr size_t kTileBytes = 4 * (size_t)TILE_ELEMS * 2;
+  constexpr size_t kLdsBytes = (TOPK && sizeof(SelectLds) > kTileBytes) ? sizeof(SelectLds) : kTileBytes;
+  __shared__ __attribute__((aligned(16))) char lds_raw[kLdsBytes];
+  auto tiles = reinterpret_cast<uint16_t(*)[2][TILE_ELEMS]>(lds_raw);
+  __shared__ SelectShared sel_sh;
   __shared__ int32_t sidx[kIdxLds];
   __shared__ float sx[2][4][8][64];         // S partial exchange, per team
   __shared__ float qss[2][4][16];           // query sum-of-squares exchange, per team
@@ -164,6 +172,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int si = attn_source(a, unit % a.n_x, &split);
   const AttnSrc& S = a.s[si];
   const int kind = S.kind;
+  const bool gather = kind == SRC_GATHER || kind == SRC_TOPK;
+  // a TOPK block's selection loads go out first: they need nothing but the row
+  SelectPrefetch<kAttnThreads> pf;
+  if constexpr (TOPK)
+    if (kind == SRC_TOPK) topk_prefetch(a.tw, r, pf);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int team = wave >> 2, wt = wave & 3;
   const int tt = threadIdx.x & (kTeamThreads - 1);  // thread index inside the team
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const uint16_t* kvp = reinterpret_cast<const uint16_t*>(S.kv);
   auto key_ok = [&](int64_t key) -> bool {
     if (key >= n) return false;
-    return kind != SRC_GATHER || sidx[key - kbase] >= 0;
+    return !gather || sidx[key - kbase] >= 0;
   };
   auto load_tile = [&](int64_t t) {
     okbits = 0;
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       const int64_t key = t * kTile + row;
       bool ok = key < n;
       int64_t off;
-      if (kind == SRC_GATHER) {
+      if (gather) {
         const int32_t j = ok ? sidx[key - kbase] : -1;
         ok = j >= 0;
         off = ok ? j : 0;
@@ -244,7 +257,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   // --- prologue: the query (and, for gathered keys, the block's indices) in
   // one memory round trip; dense and window keys do not depend on staged
   // indices, so their first tile is requested first
-  if (kind != SRC_GATHER && rounds > 0) load_tile(tb + team);
+  if (!gather && rounds > 0) load_tile(tb + team);
   uint4 qraw[KS];
   if (wave_on) {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h) * D + d0;
@@ -256,6 +269,33 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     for (int i = threadIdx.x; i < cnt; i += kAttnThreads) {
       const int32_t j = S.idx[(int64_t)r * S.k + kbase + i];
       sidx[i] = (j < 0 || j >= nseq) ? -1 : j;
+    }
+  }
+  if constexpr (TOPK) {
+    if (kind == SRC_TOPK && te > tb) {  // the block owns slots (even of an empty row)
+      // this block's slots [kbase, kbase + cnt) of the row's top k in
+      // ascending entry order: every block of the row runs the same exact
+      // selection from the filtered lists; the head-block-0 blocks also
+      // write their slots to idx_out
+      const TopkWs& tw = a.tw;
+      const int64_t cnt = min((te - tb) * kTile, n - kbase);
+      if (split == 0 && hb == 0) {
+        // the filter has read the first histogram: clear it for the next call
+        uint32_t* gh = tw.hist + (int64_t)r * tw.nstripe * kHistBins;
+        for (int i = threadIdx.x; i < tw.nstripe * kHistBins; i += kAttnThreads) gh[i] = 0;
+      }
+      const int64_t nv = topk_visible(a.q_pos[r], S.m2, S.w2, nseq, tw.max_entries);
+      const bool all = nv <= S.k;  // every visible entry, in order
+      for (int i = threadIdx.x; i < cnt; i += kAttnThreads) sidx[i] = (all && kbase + i < nv) ? (int32_t)(kbase + i) : -1;
+      if (!all)
+        topk_row_select<kAttnThreads, true>(tw, r, pf, *reinterpret_cast<SelectLds*>(lds_raw), sel_sh,
+                                            [&](uint32_t o, int32_t e) {
+                                              const int64_t j = (int64_t)o - kbase;
+                                              if (j >= 0 && j < cnt) sidx[j] = e;
+                                            });
+      __syncthreads();  // sidx complete; the selection's scratch is free
+      if (hb == 0 && S.idx_out)
+        for (int i = threadIdx.x; i < cnt; i += kAttnThreads) S.idx_out[(int64_t)r * S.k + kbase + i] = sidx[i];
     }
   }
   {
@@ -274,7 +314,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     if (g == 0) qss[team][wt][c16] = ss;
   }
   __syncthreads();  // sidx and qss ready
-  if (kind == SRC_GATHER && rounds > 0) load_tile(tb + team);
+  if (gather && rounds > 0) load_tile(tb + team);
   bf16x8_t qb[KS];
   if (wave_on) {
     const float ss = qss[team][hq][c16] + qss[team][hq + 2][c16];
@@ -667,6 +707,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
 
 // ============================================================ host
 
+void topk_ws_view(int rows, int64_t maxN, int k, const float* scores, void* ws, TopkWs* view);
+int launch_topk_finalize(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                         int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
+
 int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
                      int H, int D, float scale, float eps, int dtype, hipStream_t stream) {
   if (n_src < 1 || n_src > kMaxSrc) {
@@ -678,14 +722,27 @@ int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, cons
   a.scale = scale; a.eps = eps; a.n_src = n_src;
   const bool mfma = dtype == LCA_BF16 && H % 16 == 0;
   int blocks = 0;
+  int topk = -1;          // the TOPK source
+  bool fused_topk = false;  // selected inside the attention blocks
   for (int i = 0; i < n_src; ++i) {
     const lca_attn_source& in = srcs[i];
     AttnSrc& d = a.s[i];
     d.kv = in.kv; d.off = in.off; d.idx = in.idx; d.kind = in.kind; d.k = in.k; d.m2 = in.m2; d.w2 = in.w2;
-    d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse;
+    d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
     d.block_begin = blocks;
     blocks += in.n_split;
-    if (mfma && in.kind == SRC_GATHER &&
+    if (in.kind == SRC_TOPK) {
+      topk = i;
+      fused_topk = mfma && in.max_entries <= kBitmapEntries;
+      if (fused_topk) {
+        d.idx_out = in.idx_out;
+      } else {
+        // the selection's own launches, then the gathered source
+        d.kind = SRC_GATHER;
+        d.idx = in.idx_out;
+      }
+    }
+    if (mfma && (d.kind == SRC_GATHER || d.kind == SRC_TOPK) &&
         (int64_t)((in.k + kTile - 1) / kTile + in.n_split - 1) / in.n_split * kTile > kIdxLds) {
       set_error("attention: n_split=%d leaves more than %d gathered slots per block (k=%d)", in.n_split, kIdxLds,
                 in.k);
@@ -703,14 +760,36 @@ int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, cons
       set_error("attention: %lld blocks exceed the grid limit", (long long)nblk);
       return LCA_ERR_UNSUPPORTED;
     }
-    dim3 grid((unsigned)nblk);
-    switch (D) {
-      case 64: hipLaunchKernelGGL((attn_mfma<64>), grid, dim3(kAttnThreads), 0, stream, a); break;
-      case 128: hipLaunchKernelGGL((attn_mfma<128>), grid, dim3(kAttnThreads), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL((attn_mfma<256>), grid, dim3(kAttnThreads), 0, stream, a); break;
-      case 512: hipLaunchKernelGGL((attn_mfma<512>), grid, dim3(kAttnThreads), 0, stream, a); break;
-      default: set_error("attention: D=%d not supported", D); return LCA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128 && D != 256 && D != 512) {
+      set_error("attention: D=%d not supported", D);
+      return LCA_ERR_UNSUPPORTED;
     }
+  }
+  if (topk >= 0) {
+    // the sparse blocks select from the filtered lists themselves, or the
+    // selection's own launch writes idx_out first
+    const lca_attn_source& in = srcs[topk];
+    if (fused_topk) {
+      topk_ws_view(B * Tq, in.max_entries, in.k, in.scores, in.ws, &a.tw);
+    } else {
+      const int rc = launch_topk_finalize(in.off, q_pos, B, Tq, in.k, in.m2, in.w2, in.max_entries, in.idx_out,
+                                          in.scores, in.ws, stream);
+      if (rc != LCA_OK) return rc;
+    }
+  }
+  if (mfma) {
+    const int64_t units = (int64_t)rows * blocks;
+    dim3 grid((unsigned)((units + 7) / 8 * 8 * a.n_hb));
+#define LCA_MFMA(DD)                                                                                      \
+  if (fused_topk) hipLaunchKernelGGL((attn_mfma<DD, true>), grid, dim3(kAttnThreads), 0, stream, a);       \
+  else hipLaunchKernelGGL((attn_mfma<DD, false>), grid, dim3(kAttnThreads), 0, stream, a);
+    switch (D) {
+      case 64: LCA_MFMA(64) break;
+      case 128: LCA_MFMA(128) break;
+      case 256: LCA_MFMA(256) break;
+      default: LCA_MFMA(512) break;
+    }
+#undef LCA_MFMA
   } else {
     dim3 grid((unsigned)blocks, (unsigned)H, (unsigned)rows);
 #define LCA_VALU(ETy)                                                                      \

@@ -20,19 +20,21 @@
 // histogram (the highest bin whose suffix count reaches k), and appends the
 // entries of its chunk above T to a per-row "selected" list and those inside T
 // (the candidates) to a per-row candidate list, reserving space with one
-// 64-bit atomic per block.  No block waits for another.
+// 64-bit atomic per block, and counts the candidates per next-11-bit bin in a
+// second histogram.  No block waits for another.
 //
-// Kernel 3 (finalize, one block per row): radix-selects the missing
-// candidates exactly on (low 21 key bits, inverted index) -- a total order,
-// so ties go to the smaller index -- marks every chosen entry in an LDS
-// bitmap and writes the row in ascending index order (deterministic whatever
-// order the lists were filled in), then zeroes the histogram and counters.
+// Kernel 3 (finalize, one block per row): the exact selection of lca_topk.h
+// -- the second histogram's threshold bin, radix passes only inside it, a
+// bitmap of the chosen entries written out in ascending index order -- then
+// zeroes the first histogram for the next call.  (The sparse-attention
+// kernel can run the same selection in its own blocks instead.)  The score
+// kernels zero the counters and the second histogram.
 #include "lca_compress.h"
+#include "lca_topk.h"
 
 namespace lca {
 
 constexpr int kIdxThreads = 256;
-constexpr int kHistBins = 2048;
 constexpr int kSelThreads = 256;
 constexpr int kSelChunk = 4096;  // entries per select block
 constexpr int kSelPerThread = kSelChunk / kSelThreads;
@@ -50,6 +52,7 @@ struct IndexParams {
   uint32_t* hist;           // [rows][nstripe][kHistBins]
   int nstripe;              // histogram copies (score blocks spread their atomics)
   unsigned long long* ctr;  // [rows]: selected count | candidate count << 32
+  uint32_t* hist2;          // [rows][kH2Bins]: candidates per second-level bin
   int32_t* sel;             // [rows][k]
   uint64_t* cand;           // [rows][max_entries]
   int32_t* idx;             // [rows][k]
@@ -63,6 +66,13 @@ __device__ __forceinline__ int64_t row_visible(const IndexParams& a, int r, int6
 }
 
 // ------------------------------------------------------------------ scores
+
+// Block 0 of each row's scores zeroes the row's list counters and second
+// histogram, which the filter kernel that follows fills.
+__device__ __forceinline__ void clear_row_state(const IndexParams& a, int r) {
+  for (int i = threadIdx.x; i < kH2Bins; i += blockDim.x) a.hist2[(int64_t)r * kH2Bins + i] = 0;
+  if (threadIdx.x == 0) a.ctr[r] = 0;
+}
 
 __device__ __forceinline__ void hist_add(uint32_t* h, float s) {
   atomicAdd(&h[score_key(s) >> 21], 1u);
@@ -85,6 +95,7 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
   const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - e_base);
   const int64_t c0 = (int64_t)cx * a.chunk;
   const int64_t c1 = min(min(c0 + a.chunk, nv), lim);
+  if (cx == 0) clear_row_state(a, r);
   if (c0 >= c1) return;
   const bool do_hist = nv > a.k;
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0;
@@ -300,6 +311,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
   const int64_t e_base = a.csa_off[b];
   const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - e_base);
   const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+  if (blockIdx.x == 0) clear_row_state(a, r);
   if (c0 >= nv) return;
   const int64_t c1 = min(c0 + a.chunk, nv);
   const bool do_hist = nv > a.k;
@@ -326,151 +338,29 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
 
 // ------------------------------------------------------------------ select
 
-// Exclusive prefix sum over the block; returns the total in *tot.  sm holds
-// one word per wave; the block may reuse it once this returns.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tot, uint32_t* sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane == 63) sm[wave] = inc;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-  const int nw = (int)(blockDim.x >> 6);
-  for (int w = 0; w < nw; ++w) {
-    const uint32_t c = sm[w];
-    before += w < wave ? c : 0u;
-    all += c;
-  }
-  __syncthreads();
-  *tot = all;
-  return before + inc - v;
-}
-
-// Highest bin T whose suffix count reaches need, over a histogram in LDS
-// (nbins a multiple of blockDim.x).  Writes T, the count strictly above T and
-// the count of bin T (0, 0, 0 when the histogram holds fewer than need).
-// The results are visible to the block on return; the histogram is no longer
-// read, so the block may overwrite it.
-__device__ void find_threshold(const uint32_t* h, int nbins, uint32_t need, uint32_t* sm, int* T_out,
-                               uint32_t* above_out, uint32_t* cnt_out) {
-  const int per = nbins / (int)blockDim.x;
-  const int t = threadIdx.x;
-  uint32_t mine = 0;
-  for (int i = 0; i < per; ++i) mine += h[t * per + i];
-  if (t == 0) { *T_out = 0; *above_out = 0; *cnt_out = 0; }
-  uint32_t tot;
-  const uint32_t ex = block_excl_scan(mine, &tot, sm);
-  const uint32_t above_mine = tot - ex - mine;  // bins of the threads after this one
-  if (above_mine < need && above_mine + mine >= need) {
-    uint32_t acc = above_mine;
-    for (int i = per - 1; i >= 0; --i) {
-      const uint32_t c = h[t * per + i];
-      if (acc + c >= need) {
-        *T_out = t * per + i;
-        *above_out = acc;
-        *cnt_out = c;
-        break;
-      }
-      acc += c;
-    }
-  }
-  __syncthreads();
+__device__ __forceinline__ TopkWs topk_view(const IndexParams& a) {
+  TopkWs w;
+  w.scores = a.scores; w.hist = a.hist; w.nstripe = a.nstripe; w.ctr = a.ctr; w.hist2 = a.hist2;
+  w.sel = a.sel; w.cand = a.cand; w.max_entries = a.max_entries; w.k = a.k;
+  return w;
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
-  __shared__ uint32_t sh[kHistBins];
-  __shared__ uint32_t sm[kSelThreads / 64];
-  __shared__ int s_T;
-  __shared__ uint32_t s_above, s_cnt;
-  __shared__ unsigned long long s_base;
+  __shared__ FilterShared F;
   const int r = blockIdx.y;
   const int cb = blockIdx.x;
   const int b = r / a.Tq;
   const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - a.csa_off[b]);
-  if (nv <= a.k) return;  // the finalize kernel takes every visible entry
-  const int64_t c0 = (int64_t)cb * kSelChunk;
-  if (c0 >= nv) return;
-
-  // histogram (summed over its stripes) and this chunk's scores, all loads in
-  // flight together
-  const uint4* gh = reinterpret_cast<const uint4*>(a.hist + (int64_t)r * a.nstripe * kHistBins);
-  const float* S = a.scores + (int64_t)r * a.max_entries;
-  constexpr int HV = kHistBins / 4 / kSelThreads;  // uint4 per thread
-  constexpr int kMaxStripes = 8;
-  uint4 hs[kMaxStripes][HV];
-#pragma unroll
-  for (int st = 0; st < kMaxStripes; ++st)
-#pragma unroll
-    for (int i = 0; i < HV; ++i)
-      hs[st][i] = st < a.nstripe ? gh[st * (kHistBins / 4) + threadIdx.x + i * kSelThreads] : make_uint4(0, 0, 0, 0);
-  uint4 hv[HV];
-#pragma unroll
-  for (int i = 0; i < HV; ++i) {
-    hv[i] = hs[0][i];
-#pragma unroll
-    for (int st = 1; st < kMaxStripes; ++st) {
-      hv[i].x += hs[st][i].x; hv[i].y += hs[st][i].y; hv[i].z += hs[st][i].z; hv[i].w += hs[st][i].w;
-    }
-  }
-  const int64_t e0 = c0 + (int64_t)threadIdx.x * kSelPerThread;
-  float sv[kSelPerThread];
-#pragma unroll
-  for (int i = 0; i < kSelPerThread; ++i) {
-    const int64_t e = e0 + i;
-    sv[i] = S[e < nv ? e : nv - 1];
-  }
-#pragma unroll
-  for (int i = 0; i < HV; ++i) reinterpret_cast<uint4*>(sh)[threadIdx.x + i * kSelThreads] = hv[i];
-  __syncthreads();
-  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, &s_T, &s_above, &s_cnt);
-  const uint32_t T = (uint32_t)s_T;
-
-  uint32_t keys[kSelPerThread];
-  uint32_t ns = 0, nc = 0;
-#pragma unroll
-  for (int i = 0; i < kSelPerThread; ++i) {
-    const bool in = e0 + i < nv;
-    keys[i] = score_key(sv[i]);
-    const uint32_t bin = keys[i] >> 21;
-    ns += (in && bin > T) ? 1u : 0u;
-    nc += (in && bin == T) ? 1u : 0u;
-  }
-  uint32_t tot;
-  const uint32_t pos = block_excl_scan(ns | (nc << 16), &tot, sm);  // both counts < 2^16
-  if (threadIdx.x == 0)
-    s_base = atomicAdd(&a.ctr[r], (unsigned long long)(tot & 0xFFFFu) | ((unsigned long long)(tot >> 16) << 32));
-  __syncthreads();
-  uint32_t ps = (uint32_t)(s_base & 0xFFFFFFFFull) + (pos & 0xFFFFu);
-  uint32_t pc = (uint32_t)(s_base >> 32) + (pos >> 16);
-  int32_t* selr = a.sel + (int64_t)r * a.k;
-  uint64_t* candr = a.cand + (int64_t)r * a.max_entries;
-#pragma unroll
-  for (int i = 0; i < kSelPerThread; ++i) {
-    const int64_t e = e0 + i;
-    if (e >= nv) continue;
-    const uint32_t bin = keys[i] >> 21;
-    if (bin > T) {
-      if (ps < (uint32_t)a.k) selr[ps] = (int32_t)e;
-      ++ps;
-    } else if (bin == T) {
-      if (pc < (uint32_t)a.max_entries)
-        candr[pc] = ((uint64_t)(keys[i] & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
-      ++pc;
-    }
-  }
+  if (nv <= a.k) return;  // the selection takes every visible entry
+  if ((int64_t)cb * kSelChunk >= nv) return;
+  filter_chunk<kSelThreads, kSelPerThread>(topk_view(a), r, nv, cb, F);
 }
 
 constexpr int kFinThreads = 1024;
-constexpr int kCandLds = 8192;                   // candidates kept in LDS
-constexpr int kBitmapWords = 8192;               // 262144 entries
 
 __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
-  __shared__ uint32_t sh[4096];
-  __shared__ uint32_t sm[kFinThreads / 64];
-  __shared__ uint64_t lds_cand[kCandLds];
-  __shared__ uint32_t bitmap[kBitmapWords];
-  __shared__ int s_T;
-  __shared__ uint32_t s_above, s_cnt;
-  __shared__ uint32_t s_fill;
+  __shared__ SelectLds L;
+  __shared__ SelectShared S;
   const int r = blockIdx.x;
   const int b = r / a.Tq;
   const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - a.csa_off[b]);
@@ -479,131 +369,23 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
     for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = t < nv ? t : -1;
     return;
   }
-  const unsigned long long cnt = a.ctr[r];
-  const uint32_t n_sel = (uint32_t)(cnt & 0xFFFFFFFFull);
-  const uint32_t ncands = (uint32_t)(cnt >> 32);
-  // the threshold bin of the filter kernel, recomputed from the same
-  // histogram (every stripe's loads in flight together); the histogram and
-  // the counters are then cleared for the next call right away
+  // the filter kernel has read the histogram: clear it for the next call
   uint32_t* gh = a.hist + (int64_t)r * a.nstripe * kHistBins;
-  {
-    constexpr int kMaxStripes = 8;
-    constexpr int HB = kHistBins / kFinThreads;
-    uint32_t c[HB][kMaxStripes];
-#pragma unroll
-    for (int j = 0; j < HB; ++j)
-#pragma unroll
-      for (int st = 0; st < kMaxStripes; ++st)
-        c[j][st] = st < a.nstripe ? gh[st * kHistBins + threadIdx.x + j * kFinThreads] : 0u;
-#pragma unroll
-    for (int j = 0; j < HB; ++j) {
-      uint32_t sum = 0;
-#pragma unroll
-      for (int st = 0; st < kMaxStripes; ++st) sum += c[j][st];
-      sh[threadIdx.x + j * kFinThreads] = sum;
-    }
-  }
   for (int i = threadIdx.x; i < a.nstripe * kHistBins; i += blockDim.x) gh[i] = 0;
-  if (threadIdx.x == 0) a.ctr[r] = 0;
-  const bool use_bitmap = nv <= (int64_t)kBitmapWords * 32;
-  if (use_bitmap)
-    for (int i = threadIdx.x; i < kBitmapWords; i += blockDim.x) bitmap[i] = 0;
-  __syncthreads();
-  find_threshold(sh, kHistBins, (uint32_t)a.k, sm, &s_T, &s_above, &s_cnt);
-  const uint32_t above = s_above;
-  const bool consistent = n_sel == above && above < (uint32_t)a.k && above + ncands >= (uint32_t)a.k &&
-                          ncands <= (uint32_t)a.max_entries;
-  if (!consistent) {
+  const TopkWs w = topk_view(a);
+  SelectPrefetch<kFinThreads> P;
+  topk_prefetch(w, r, P);
+  auto emit = [&](uint32_t o, int32_t e) { out[o] = e; };
+  const uint32_t got = nv <= kBitmapEntries ? topk_row_select<kFinThreads, true>(w, r, P, L, S, emit)
+                                            : topk_row_select<kFinThreads, false>(w, r, P, L, S, emit);
+  if (got == 0)
     for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = -1;
-  } else {
-    // candidates into LDS when they fit
-    const bool in_lds = ncands <= (uint32_t)kCandLds;
-    const uint64_t* cg = a.cand + (int64_t)r * a.max_entries;
-    if (in_lds)
-      for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) lds_cand[i] = cg[i];
-    const uint64_t* cl = in_lds ? lds_cand : cg;
-    __syncthreads();
-    // radix select of the need-th largest packed value (all distinct)
-    uint32_t need = (uint32_t)a.k - above;
-    uint64_t prefix = 0, mask = 0;
-    const int shifts[4] = {34, 23, 12, 0};
-    const int widths[4] = {11, 11, 11, 12};
-    if (need < ncands) {
-      for (int pass = 0; pass < 4; ++pass) {
-        const int sft = shifts[pass], nb = 1 << widths[pass];
-        for (int i = threadIdx.x; i < nb; i += blockDim.x) sh[i] = 0;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) {
-          const uint64_t v = cl[i];
-          if ((v & mask) == prefix) atomicAdd(&sh[(uint32_t)(v >> sft) & (uint32_t)(nb - 1)], 1u);
-        }
-        __syncthreads();
-        find_threshold(sh, nb, need, sm, &s_T, &s_above, &s_cnt);
-        prefix |= (uint64_t)s_T << sft;
-        mask |= (uint64_t)(nb - 1) << sft;
-        need -= s_above;
-        // every value left in the chosen bucket is needed: its lower bound
-        // (prefix with zero low bits) is the threshold
-        const bool done = s_cnt == need;
-        __syncthreads();  // s_T, s_above and s_cnt are rewritten by the next pass
-        if (done) break;
-      }
-    }
-    const uint64_t vstar = prefix;  // need < ncands: exactly (k - above) values >= vstar; else 0 (all)
-    const int32_t* selr = a.sel + (int64_t)r * a.k;
-    if (use_bitmap) {
-      // ascending index order through a bitmap of the chosen entries
-      for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) {
-        const uint32_t e = (uint32_t)selr[i];
-        atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-      }
-      for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) {
-        const uint64_t v = cl[i];
-        if (v >= vstar) {
-          const uint32_t e = 0xFFFFFFu - (uint32_t)(v & 0xFFFFFFu);
-          atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-        }
-      }
-      __syncthreads();
-      constexpr int WPT = kBitmapWords / kFinThreads;  // words per thread
-      uint32_t wv[WPT], c = 0;
-#pragma unroll
-      for (int i = 0; i < WPT; ++i) {
-        wv[i] = bitmap[threadIdx.x * WPT + i];
-        c += __popc(wv[i]);
-      }
-      uint32_t tot;
-      uint32_t o = block_excl_scan(c, &tot, sm);
-#pragma unroll
-      for (int i = 0; i < WPT; ++i) {
-        uint32_t w = wv[i];
-        while (w) {
-          const int bit = __ffs(w) - 1;
-          w &= w - 1;
-          if (o < (uint32_t)a.k) out[o] = (int32_t)((threadIdx.x * WPT + i) * 32 + bit);
-          ++o;
-        }
-      }
-    } else {
-      // large rows: selected entries in list order, then the chosen candidates
-      if (threadIdx.x == 0) s_fill = 0;
-      __syncthreads();
-      for (uint32_t i = threadIdx.x; i < n_sel; i += blockDim.x) out[i] = selr[i];
-      for (uint32_t i = threadIdx.x; i < ncands; i += blockDim.x) {
-        const uint64_t v = cl[i];
-        if (v >= vstar) {
-          const uint32_t o = above + atomicAdd(&s_fill, 1u);
-          if (o < (uint32_t)a.k) out[o] = (int32_t)(0xFFFFFFu - (uint32_t)(v & 0xFFFFFFu));
-        }
-      }
-    }
-  }
 }
 
 // ------------------------------------------------------------------ host
 
 struct IndexWs {
-  size_t scores, hist, ctr, sel, cand, total;
+  size_t scores, hist, ctr, hist2, sel, cand, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -624,6 +406,7 @@ static IndexWs index_ws_layout(int rows, int64_t maxN, int k) {
   size_t o = 0;
   w.hist = o;     o = align256(o + (size_t)rows * hist_stripes(rows, maxN) * kHistBins * 4);
   w.ctr = o;      o = align256(o + (size_t)rows * 8);
+  w.hist2 = o;    o = align256(o + (size_t)rows * kH2Bins * 4);
   w.scores = o;   o = align256(o + (size_t)rows * maxN * 4);
   w.sel = o;      o = align256(o + (size_t)rows * k * 4);
   w.cand = o;     o = align256(o + (size_t)rows * maxN * 8);
@@ -645,6 +428,7 @@ static IndexParams make_params(const void* p, const float* omega, const void* ik
   a.scores = scores ? const_cast<float*>(scores) : reinterpret_cast<float*>(base + L.scores);
   a.hist = reinterpret_cast<uint32_t*>(base + L.hist);
   a.ctr = reinterpret_cast<unsigned long long*>(base + L.ctr);
+  a.hist2 = reinterpret_cast<uint32_t*>(base + L.hist2);
   a.sel = reinterpret_cast<int32_t*>(base + L.sel);
   a.cand = reinterpret_cast<uint64_t*>(base + L.cand);
   a.idx = idx;
@@ -737,6 +521,32 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
     case 4: hipLaunchKernelGGL((index_score_append<4>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
     default: hipLaunchKernelGGL((index_score_append<8>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
   }
+  return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+}
+
+// The workspace views of the filter's lists, for the sparse-attention launch
+// whose blocks run the exact selection.
+void topk_ws_view(int rows, int64_t maxN, int k, const float* scores, void* ws, TopkWs* view) {
+  IndexParams a = make_params(nullptr, nullptr, nullptr, nullptr, nullptr, rows, 1, 1, 8, k, 1, 1, maxN, nullptr,
+                              scores, ws);
+  view->scores = a.scores; view->hist = a.hist; view->nstripe = a.nstripe; view->ctr = a.ctr;
+  view->hist2 = a.hist2; view->sel = a.sel; view->cand = a.cand; view->max_entries = maxN; view->k = k;
+}
+
+int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                       int64_t maxN, const float* scores, void* ws, hipStream_t stream) {
+  IndexParams a = make_params(nullptr, nullptr, nullptr, csa_off, q_pos, B, Tq, 1, 8, k, m, w, maxN, nullptr, scores,
+                              ws);
+  const int nblk = (int)((maxN + kSelChunk - 1) / kSelChunk);
+  hipLaunchKernelGGL(topk_filter, dim3((unsigned)nblk, (unsigned)(B * Tq)), dim3(kSelThreads), 0, stream, a);
+  return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+}
+
+// The second launch of the selection alone (after the filter).
+int launch_topk_finalize(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                         int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream) {
+  IndexParams a = make_params(nullptr, nullptr, nullptr, csa_off, q_pos, B, Tq, 1, 8, k, m, w, maxN, idx, scores, ws);
+  hipLaunchKernelGGL(topk_finalize, dim3((unsigned)(B * Tq)), dim3(kFinThreads), 0, stream, a);
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 

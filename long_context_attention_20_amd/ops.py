@@ -9,7 +9,7 @@ from typing import Optional, Sequence
 import ctypes
 import torch
 
-from ._lib import (LCA_BF16, LCA_F32, LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_WINDOW, AttnSource, CompressStream,
+from ._lib import (LCA_BF16, LCA_F32, LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_TOPK, LCA_SRC_WINDOW, AttnSource, CompressStream,
                    Partial, check, lib)
 
 
@@ -23,6 +23,10 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _addr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
 
 
 def _dev(*ts):
@@ -160,6 +164,18 @@ def csa_topk_select(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws
     return idx
 
 
+def csa_topk_filter(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws: torch.Tensor,
+                    scores: Optional[torch.Tensor] = None):
+    """First launch of csa_topk_select alone: the filtered lists in the
+    workspace, for a "topk" source of hybrid_attn to select from."""
+    _dev(csa_off, q_pos, ws, scores)
+    B = csa_off.numel() - 1
+    rows = q_pos.numel()
+    check(lib.lca_csa_topk_filter(_ptr(csa_off), _ptr(q_pos), B, rows // B, k, m, w, int(max_entries),
+                                  _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+          "csa_topk_filter")
+
+
 # ---------------------------------------------------------------- a4 / a5
 
 def _parts_out(rows, H, D, n_split, device, o_part, lse):
@@ -217,14 +233,18 @@ def swa_attn(q, x, tok_off, q_pos, W: int, scale: float, eps: float, o_part=None
     return o_part, lse
 
 
-_KINDS = {"dense": LCA_SRC_DENSE, "gather": LCA_SRC_GATHER, "window": LCA_SRC_WINDOW}
+_KINDS = {"dense": LCA_SRC_DENSE, "gather": LCA_SRC_GATHER, "window": LCA_SRC_WINDOW, "topk": LCA_SRC_TOPK}
 
 
 def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
     """The attention branches of a step in one launch.  sources: dicts with
-    kind ("gather", "dense" or "window"), kv, off and n_split, plus idx
-    (gather), m2 and w2 (dense), W (window), and optionally o_part / lse.
-    Returns one (o_part, lse) pair per source, as the single-branch calls."""
+    kind ("gather", "dense", "window" or "topk"), kv, off and n_split, plus
+    idx (gather), m2 and w2 (dense), W (window), and optionally o_part / lse.
+    A "topk" source selects the sparse branch's entries from the lists that
+    csa_index_score(_append) and then csa_topk_filter left in the workspace:
+    it takes k, m2 = m, w2 = w, max_entries, ws, idx_out (int32 [rows, k],
+    written) and optionally scores.  Returns one (o_part, lse) pair per source, as the
+    single-branch calls."""
     if not 1 <= len(sources) <= 3:
         raise ValueError("1..3 sources per call")
     _dev(q, q_pos)
@@ -244,15 +264,24 @@ def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
         elif off.numel() - 1 != B:
             raise ValueError("every source needs the same number of sequences")
         k = 0
+        ws = ws_bytes = max_entries = scores = idx_out = None
         if kind == LCA_SRC_GATHER:
             _i32(idx, "idx")
             k = idx.shape[-1]
+        if kind == LCA_SRC_TOPK:
+            idx_out, ws, scores = s["idx_out"], s["ws"], s.get("scores")
+            _dev(idx_out, ws, scores)
+            _i32(idx_out, "idx_out")
+            k = int(s["k"])
+            if idx_out.shape != (rows, k):
+                raise ValueError(f"idx_out must be [{rows}, {k}]")
+            ws_bytes, max_entries = ws.numel() * ws.element_size(), int(s["max_entries"])
         ns = int(s["n_split"])
         o_part, lse = _parts_out(rows, H, D, ns, q.device, s.get("o_part"), s.get("lse"))
         _dev(o_part, lse)
         arr[i] = AttnSource(kind, kv.data_ptr(), off.data_ptr(), None if idx is None else idx.data_ptr(), k,
                             int(s.get("m2", 1)), int(s.get("w2", 1)), int(s.get("W", 0)), ns, o_part.data_ptr(),
-                            lse.data_ptr())
+                            lse.data_ptr(), _addr(ws), ws_bytes or 0, max_entries or 0, _addr(scores), _addr(idx_out))
         outs.append((o_part, lse))
     check(lib.lca_hybrid_attn(arr, len(sources), _ptr(q), _ptr(q_pos), B, rows // B, H, D, float(scale), float(eps),
                               _dtype_code(q), _stream()), "hybrid_attn")

@@ -5,11 +5,14 @@ strides and windows), the caller's caches as device tensors with their host
 and device offsets, and reusable workspaces.  It only sizes buffers and
 sequences the C entry points; every step runs in the HIP kernels.
 
-Decode step (one query row per sequence), four calls on one stream:
+Decode step (one query row per sequence), four launches on one stream:
     csa_index_score_append  the CSA, indexer-key and HCA entries the new token
-                            completes, and the index scores (one launch)
-    csa_topk_select         exact top-k
-    hybrid_attn             CSA sparse + HCA dense + window partials (one launch)
+                            completes, and the index scores
+    csa_topk_filter         the entries above the top-k threshold bin and the
+                            candidates inside it
+    hybrid_attn             exact top-k (each sparse block selects its share of
+                            the ascending list), then CSA sparse + HCA dense +
+                            window partials
     swa_merge               sink + merge of every partial
 Prefill chunks (several rows per sequence) run kv_compress and
 csa_index_score as separate launches.
@@ -138,17 +141,22 @@ class HybridAttention:
         want = max(1, -(-256 // (rows * hg)))
         return int(max(1, min(want, tiles // 4 if tiles >= 4 else 1, 256)))
 
-    def fused_splits(self, rows: int, n_csa: int, n_hca: int, n_win: int):
+    def fused_splits(self, rows: int, n_csa: int, n_hca: int, n_win: int, select: bool = False):
         """Splits of the three sources of one fused launch: the blocks of all
         sources take about the same number of 32-key tiles (an even number,
-        one per team and round), chosen so that one wave of blocks (one per
-        compute unit) covers the launch when the rows allow it."""
+        one per team and round), the fewest that let one wave of blocks (one
+        per compute unit) cover the launch when the rows allow it.  With
+        select, the sparse blocks also run the top-k selection (about as long
+        as four tiles of attention) and take four tiles fewer."""
         hg = (self.H + 31) // 32
         tiles = [max(1, (n + 31) // 32) for n in (n_csa, n_hca, n_win)]
         budget = max(3, 256 // max(1, rows * hg))
-        per = -(-sum(tiles) // budget)
-        per = min(32, max(2, per + (per & 1)))
-        return tuple(int(min(256, max(1, -(-t // per)))) for t in tiles)
+        for per in range(2, 34, 2):
+            pc = max(2, per - 4) if select else per
+            units = -(-tiles[0] // pc) + -(-tiles[1] // per) + -(-tiles[2] // per)
+            if units <= budget:
+                break
+        return tuple(int(min(256, max(1, -(-t // q)))) for t, q in zip(tiles, (pc, per, per)))
 
     def step(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, q: torch.Tensor, p: torch.Tensor,
              omega: torch.Tensor, sigma: Optional[torch.Tensor], q_pos: torch.Tensor, q_pos_h: np.ndarray,
@@ -193,7 +201,7 @@ class HybridAttention:
         """Preallocated outputs of decode_step (so that the step can be
         captured in a HIP graph and replayed)."""
         f32 = torch.float32
-        sc, sh, sw = self.fused_splits(rows, min(self.k, max(1, max_csa)), max_hca, self.W)
+        sc, sh, sw = self.fused_splits(rows, min(self.k, max(1, max_csa)), max_hca, self.W, select=True)
         sc = self.split_csa or sc
         sh = self.split_hca or sh
         part = lambda n: (torch.empty((n, rows, self.H, self.D), dtype=f32, device=device),
@@ -205,10 +213,18 @@ class HybridAttention:
             csa=part(sc), hca=part(sh), swa=part(sw),
             out=torch.empty((rows, self.H, self.D), dtype=dtype, device=device))
 
-    def attn_sources(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, idx: torch.Tensor, bufs: dict):
-        """The three key sources of the fused attention launch."""
-        src = [dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=bufs["sc"],
-                    o_part=bufs["csa"][0], lse=bufs["csa"][1])]
+    def attn_sources(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, idx: Optional[torch.Tensor],
+                     bufs: dict):
+        """The three key sources of the fused attention launch.  idx None: the
+        sparse source selects its own entries from the index workspace
+        bufs["ws_idx"] (a TOPK source; the selection lands in bufs["idx"])."""
+        if idx is None:
+            src = [dict(kind="topk", kv=caches.kv_csa, off=caches.csa_off, k=self.k, m2=self.m, w2=self.w,
+                        max_entries=bufs["max_csa"], ws=bufs["ws_idx"], idx_out=bufs["idx"], n_split=bufs["sc"],
+                        o_part=bufs["csa"][0], lse=bufs["csa"][1])]
+        else:
+            src = [dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=bufs["sc"],
+                        o_part=bufs["csa"][0], lse=bufs["csa"][1])]
         if bufs["max_hca"] > 0:
             src.append(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2,
                             n_split=bufs["sh"], o_part=bufs["hca"][0], lse=bufs["hca"][1]))
@@ -219,7 +235,8 @@ class HybridAttention:
 
     def decode_step(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos,
                     bufs: dict, done_len: Optional[torch.Tensor] = None, done_h: Optional[Sequence[int]] = None,
-                    side: Optional["torch.cuda.Stream"] = None, lens_h: Optional[Sequence[int]] = None):
+                    side: Optional["torch.cuda.Stream"] = None, lens_h: Optional[Sequence[int]] = None,
+                    fuse_topk: bool = True):
         """One decode (or prefill-chunk) step of mode A: append the entries the
         new tokens complete (when done_len is given), score and select the CSA
         entries, attend to the selected CSA entries, the visible HCA entries
@@ -228,7 +245,9 @@ class HybridAttention:
         launch.  With a side stream the HCA append runs there instead, beside
         the indexer (the join costs a cross-queue wait in a graph).  lens_h:
         host copy of the sequence lengths tok_off describes, when they are
-        shorter than the caches'."""
+        shorter than the caches'.  fuse_topk: after csa_topk_filter, the
+        exact selection runs inside the attention launch (a TOPK source)
+        rather than as csa_topk_select's second launch."""
         main = torch.cuda.current_stream()
         join = None
         scored = False
@@ -256,11 +275,14 @@ class HybridAttention:
         if not scored:
             ops.csa_index_score(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w,
                                 bufs["max_csa"], bufs["ws_idx"])
-        ops.csa_topk_select(caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"], bufs["ws_idx"],
-                            idx=bufs["idx"])
+        if fuse_topk:
+            ops.csa_topk_filter(caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"], bufs["ws_idx"])
+        else:
+            ops.csa_topk_select(caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"], bufs["ws_idx"],
+                                idx=bufs["idx"])
         if join is not None:
             main.wait_event(join)
-        srcs = self.attn_sources(caches, raw["x"], tok_off, bufs["idx"], bufs)
+        srcs = self.attn_sources(caches, raw["x"], tok_off, None if fuse_topk else bufs["idx"], bufs)
         parts = ops.hybrid_attn(q, q_pos, srcs, self.scale, self.eps)
         ops.swa_merge(q, None, None, None, sigma, parts, 0, self.scale, self.eps, None, out=bufs["out"])
         return bufs["out"]

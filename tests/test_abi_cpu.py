@@ -160,6 +160,57 @@ def test_hybrid_attn_rejects(L):
     assert b"gathered slots" in lib.lca_last_error()
 
 
+def test_hybrid_attn_rejects_topk(L):
+    """A TOPK source: the index workspace, its size, k, the CSA stride and
+    window, idx_out and q_pos are checked; at most one TOPK source."""
+    lib = L.lib
+    P = ctypes.c_void_p(256)
+    need = lib.lca_csa_index_topk_workspace(1, 1000, 512)
+    src = (L.AttnSource * 2)()
+
+    def topk(i, k=512, m2=4, w2=8, ws=256, ws_bytes=need, maxN=1000, idx_out=256):
+        src[i] = L.AttnSource(L.LCA_SRC_TOPK, 256, 256, None, k, m2, w2, 0, 4, 256, 256, ws, ws_bytes, maxN, None,
+                              idx_out)
+
+    def call(n=1, qp=P):
+        return lib.lca_hybrid_attn(src, n, P, qp, 1, 1, 64, 512, 0.04, 1e-6, 1, None)
+    topk(0)
+    topk(1)
+    assert call(n=2) == L.LCA_ERR_INVALID_ARG                  # two TOPK sources
+    assert b"more than one TOPK" in lib.lca_last_error()
+    topk(0, idx_out=None)
+    assert call() == L.LCA_ERR_INVALID_ARG
+    topk(0)
+    assert call(qp=None) == L.LCA_ERR_INVALID_ARG
+    topk(0, ws=None)
+    assert call() == L.LCA_ERR_WORKSPACE
+    topk(0, ws_bytes=need - 1)
+    assert call() == L.LCA_ERR_WORKSPACE
+    topk(0, k=0)
+    assert call() == L.LCA_ERR_UNSUPPORTED
+    topk(0, k=5000)
+    assert call() == L.LCA_ERR_UNSUPPORTED
+    topk(0, m2=0)
+    assert call() == L.LCA_ERR_INVALID_ARG
+    topk(0, maxN=0)
+    assert call() == L.LCA_ERR_UNSUPPORTED
+
+
+def test_topk_filter_rejects(L):
+    lib = L.lib
+    P = ctypes.c_void_p(256)
+    need = lib.lca_csa_index_topk_workspace(1, 1000, 512)
+
+    def call(csa_off=P, q_pos=P, k=512, m=4, w=8, maxN=1000, ws=P, ws_bytes=need):
+        return lib.lca_csa_topk_filter(csa_off, q_pos, 1, 1, k, m, w, maxN, None, ws, ws_bytes, None)
+    assert call(csa_off=None) == L.LCA_ERR_INVALID_ARG
+    assert call(q_pos=None) == L.LCA_ERR_INVALID_ARG
+    assert call(k=0) == L.LCA_ERR_UNSUPPORTED
+    assert call(w=0) == L.LCA_ERR_INVALID_ARG
+    assert call(ws=None) == L.LCA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == L.LCA_ERR_WORKSPACE
+
+
 def test_index_score_append_rejects(L):
     lib = L.lib
     P = ctypes.c_void_p(256)
