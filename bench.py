@@ -7,10 +7,9 @@ the fraction of peak HBM bandwidth it corresponds to.
 A step is one pass of the whole hot path for one query token per sequence:
   csa_index_score_append (the CSA, indexer-key and HCA entries the new token
     completes, and the index scores, in one launch)
-  -> csa_topk_filter (the entries above the top-k threshold bin, and the
-    candidates inside it)
-  -> hybrid_attn (one launch: each sparse block's share of the exact top-k,
-    CSA sparse + HCA dense + window partials)
+  -> hybrid_attn (one launch: the sparse blocks filter the scores and each
+    selects its share of the exact top-k; CSA sparse + HCA dense + window
+    partials)
   -> swa_merge (sink + merge)
 on one stream, over caches resident in HBM.  To keep the 256 MB Infinity Cache from serving
 the caches, steps rotate over R layers, each with its own raw streams and
@@ -18,11 +17,10 @@ caches (R * per-step bytes >= 2 x 256 MB).
 
 Timed regions (HIP events on the launch stream, synchronised on both sides):
   1. per kernel: one HIP graph of that kernel's launch for each of the R
-     rotated layers, replayed 8 times (the filter and the attention launch,
-     which consume what the launches before them leave in the index
-     workspace, are timed in a chain after them, whose time is
-     subtracted); the dominant kernel's average launch duration gives the
-     roofline;
+     rotated layers, replayed 8 times (the attention launch, which selects
+     from what the score kernel leaves in the index workspace, is timed
+     after it, the score kernel's time subtracted); the dominant kernel's
+     average launch duration gives the roofline;
   2. the headline: the W warmup steps and then the K timed steps, each set
      captured as one HIP graph of consecutive layer steps and replayed once.
      With one sequence the K steps are K consecutive decode positions, each
@@ -125,11 +123,9 @@ def kernel_cost(cfg, name):
             nwin = min(cfg.W, L)
             by += nwin * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * nwin
-        elif name == "csa_topk_filter":
-            by += ncsa * 4                                     # every score read once
-        elif name == "hybrid_attn":                      # the selection's end + the three branches
+        elif name == "hybrid_attn":                      # the top-k selection + the three branches
             nwin = min(cfg.W, L)
-            by += kk * 4                                       # selection written
+            by += ncsa * 4 + kk * 4                            # every score read, selection written
             by += (kk + nh + nwin) * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * (kk + nh + nwin)
         elif name == "swa_merge":
@@ -188,16 +184,15 @@ class Runner:
         self.bufs = a.decode_buffers(rows, n_windows(qmax, cfg.m, cfg.w), n_windows(qmax, cfg.m2, cfg.w2), dev,
                                      self.layers[0].q.dtype)
         self.sc, self.sh, self.sw = self.bufs["sc"], self.bufs["sh"], self.bufs["sw"]
-        self.names = ["csa_index_score_append", "csa_topk_filter", "hybrid_attn", "swa_merge"]
+        self.names = ["csa_index_score_append", "hybrid_attn", "swa_merge"]
         self.launches = {}  # kernels per call (default 1)
-        # the filter consumes the score kernel's histogram and the attention
-        # launch the filter's lists (and clears the histogram): each is timed
-        # at the end of the chain of calls before it (that chain subtracted)
-        self.timed = ["csa_index_score_append", "csa_index_score_append+csa_topk_filter",
-                      "csa_index_score_append+csa_topk_filter+hybrid_attn", "swa_merge"]
+        # the attention launch selects from what the score kernel leaves in
+        # the index workspace (and clears it): it is timed after the score
+        # kernel, whose time is subtracted
+        self.timed = ["csa_index_score_append", "csa_index_score_append+hybrid_attn", "swa_merge"]
 
     def step(self, L, pos=None):
-        """The whole decode step (four calls on the current stream), at the
+        """The whole decode step (three calls on the current stream), at the
         last position of every sequence or at `pos` (one sequence)."""
         if pos is None:
             return self.attn.decode_step(L.caches, L.raw, L.tok_off, L.q, L.p, L.omega, L.sigma, L.q_pos, self.bufs,
@@ -217,7 +212,6 @@ class Runner:
             lambda: ops.csa_index_score_append(L.p, L.omega, c.ikey, c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w,
                                                bf["max_csa"], bf["ws_idx"], idx_st, kv_st, L.tok_off, L.done,
                                                cfg.eps),
-            lambda: ops.csa_topk_filter(c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w, bf["max_csa"], bf["ws_idx"]),
             lambda: ops.hybrid_attn(L.q, L.q_pos, srcs, a.scale, cfg.eps),
             lambda: ops.swa_merge(L.q, None, None, None, L.sigma, parts, 0, a.scale, cfg.eps, None, out=bf["out"]),
         ]

@@ -130,9 +130,8 @@ int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int
  *   ws       device workspace of at least lca_csa_index_topk_workspace()
  *            bytes.  It must be ZERO-FILLED before its first use; after
  *            that each score call and the selection that must follow it
- *            (lca_csa_topk_select, or lca_csa_topk_filter and then a TOPK
- *            source of lca_hybrid_attn) leave it ready for the next score
- *            call.  Calls that share a
+ *            (lca_csa_topk_select, or a TOPK source of lca_hybrid_attn)
+ *            leave it ready for the next score call.  Calls that share a
  *            workspace must be ordered on one stream.
  * Supported: H_I * d_I <= 1024, d_I multiple of 8, k in [1, 4096],
  * entries per sequence < 2^24. */
@@ -181,16 +180,6 @@ int lca_csa_index_score_append(const void* p, const float* omega, const void* ik
 int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                         int64_t max_entries, int32_t* idx, const float* scores, void* ws, size_t ws_bytes,
                         void* stream);
-
-/* The first of lca_csa_topk_select's two launches alone, same arguments but
- * idx: from the histogram the score call left, every entry above the bin
- * holding the k-th largest score goes to a list, every entry inside it to a
- * candidate list (with a histogram of their next key bits), all in the
- * workspace.  The exact selection from those lists is then made by a TOPK
- * source of lca_hybrid_attn (same workspace and arguments), which must
- * follow on the same stream. */
-int lca_csa_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
-                        int64_t max_entries, const float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Attention partials (a4, a5)
@@ -263,20 +252,21 @@ int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int
  *   LCA_SRC_WINDOW  raw rows max(0, i-W+1) .. i of kv packed by off, each
  *                   RMS-normalised over D on load (as lca_swa_attn, any
  *                   n_split)
- *   LCA_SRC_TOPK    the end of the top-k selection and the sparse branch in
- *                   one: after a score call and lca_csa_topk_filter (same
- *                   stream, workspace ws, scores, k slots, m2 = m, w2 = w
- *                   (the CSA entries' stride and window), max_entries, kv's
- *                   offsets as csa_off), it stands for the rest of
+ *   LCA_SRC_TOPK    the top-k selection and the sparse branch in one: after
+ *                   a score call (same stream, workspace ws, scores, k slots,
+ *                   m2 = m, w2 = w (the CSA entries' stride and window),
+ *                   max_entries, kv's offsets as csa_off), it stands for
  *                   lca_csa_topk_select into idx_out followed by a GATHER
  *                   source over idx_out: idx_out receives exactly what
  *                   lca_csa_topk_select would write (ascending order when a
  *                   row has at most 262144 candidates).  On the bf16
  *                   matrix-core path with max_entries <= 262144 every block
- *                   of the sparse branch runs the exact selection itself
- *                   from the filtered lists (one launch in all); elsewhere
- *                   the selection's own launch comes first.  At most one
- *                   TOPK source per call.
+ *                   of the sparse branch runs the exact selection itself;
+ *                   when the whole launch fits the device at once, those
+ *                   blocks also filter the scores (one launch in all), else
+ *                   a filter launch comes first.  Elsewhere the selection's
+ *                   own launches come first.  At most one TOPK source per
+ *                   call.
  * The sources share q [B*Tq, H, D], q_pos (device int32 [B*Tq]; read by the
  * DENSE and WINDOW sources), scale and eps.  One launch costs one kernel
  * start and lets the branches' blocks share the machine.  The bf16

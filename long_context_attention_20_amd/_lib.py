@@ -24,7 +24,7 @@ LCA_BF16 = 1
 EXPORTS = [
     "lca_strerror", "lca_last_error", "lca_version", "lca_kv_compress",
     "lca_csa_index_topk_workspace", "lca_csa_index_topk", "lca_csa_index_score", "lca_csa_index_score_append",
-    "lca_csa_topk_select", "lca_csa_topk_filter", "lca_csa_sparse_attn", "lca_hca_attn",
+    "lca_csa_topk_select", "lca_csa_sparse_attn", "lca_hca_attn",
     "lca_swa_attn", "lca_hybrid_attn", "lca_swa_merge_workspace", "lca_swa_merge",
 ]
 LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_WINDOW, LCA_SRC_TOPK = 0, 1, 2, 3
@@ -84,8 +84,6 @@ def _load():
                                              vp, vp, f32, vp, vp, sz, i32, vp]
     L.lca_csa_topk_select.restype = i32
     L.lca_csa_topk_select.argtypes = [vp, vp, i32, i32, i32, i32, i32, i64, vp, vp, vp, sz, vp]
-    L.lca_csa_topk_filter.restype = i32
-    L.lca_csa_topk_filter.argtypes = [vp, vp, i32, i32, i32, i32, i32, i64, vp, vp, sz, vp]
     L.lca_csa_sparse_attn.restype = i32
     L.lca_csa_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, i32, vp, vp, i32, vp]
     L.lca_hca_attn.restype = i32

@@ -36,8 +36,6 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
                               int dtype, hipStream_t stream);
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
-int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
-                       int64_t maxN, const float* scores, void* ws, hipStream_t stream);
 int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
                      int H, int D, float scale, float eps, int dtype, hipStream_t stream);
 
@@ -222,16 +220,6 @@ int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return finish(launch_topk_select(csa_off, q_pos, B, Tq, k, m, w, max_entries, idx, scores, ws, st), st,
                 "csa_topk_select");
-}
-
-int lca_csa_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
-                        int64_t max_entries, const float* scores, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_index("csa_topk_filter", false, nullptr, nullptr, nullptr, csa_off, q_pos, B, Tq, 1, 8, k, m, w,
-                       max_entries, ws, ws_bytes, LCA_BF16);
-  if (rc != LCA_OK) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  return finish(launch_topk_filter(csa_off, q_pos, B, Tq, k, m, w, max_entries, scores, ws, st), st,
-                "csa_topk_filter");
 }
 
 int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,

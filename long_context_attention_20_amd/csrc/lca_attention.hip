@@ -59,8 +59,13 @@ struct AttnParams {
   int n_x;              // splits of all sources (blocks per row and head block)
   int n_hb;             // head blocks per row (matrix-core path)
   AttnSrc s[kMaxSrc];
-  TopkWs tw;            // the index workspace of a TOPK source (filtered)
+  TopkWs tw;            // the index workspace of a TOPK source
+  int filter;           // 1: the TOPK blocks filter the scores themselves
+  int tbpr;             // TOPK blocks per row (n_split * n_hb)
 };
+
+constexpr int kFilterPer = 8;  // scores per thread and filter chunk
+constexpr uint32_t kMaxSpins = 1u << 22;
 
 // Source of split column bx (uniform) and the split inside it.
 __device__ __forceinline__ int attn_source(const AttnParams& a, int bx, int* split) {
@@ -174,9 +179,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int kind = S.kind;
   const bool gather = kind == SRC_GATHER || kind == SRC_TOPK;
   // a TOPK block's selection loads go out first: they need nothing but the row
-  SelectPrefetch<kAttnThreads> pf;
-  if constexpr (TOPK)
-    if (kind == SRC_TOPK) topk_prefetch(a.tw, r, pf);
+  __shared__ uint32_t s_timeout;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int team = wave >> 2, wt = wave & 3;
   const int tt = threadIdx.x & (kTeamThreads - 1);  // thread index inside the team
@@ -190,6 +193,20 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 
   int64_t first, nseq;
   const int64_t n = attn_keys(a, S, r, &first, &nseq);
+  // a TOPK block's next loads (its filter chunk, or the filtered lists) need
+  // nothing but the row: they go out right after the row's position, so that
+  // waiting for the position does not wait for them
+  const int32_t qpos_r = kind == SRC_TOPK ? a.q_pos[r] : 0;
+  SelectPrefetch<kAttnThreads> pf;
+  FilterPrefetch<kAttnThreads, kFilterPer> fpf;
+  if constexpr (TOPK) {
+    if (kind == SRC_TOPK) {
+      if (a.filter)
+        filter_prefetch(a.tw, r, split * a.n_hb + hb, fpf);
+      else
+        topk_prefetch(a.tw, r, pf);
+    }
+  }
   const int64_t ntiles = (n + kTile - 1) / kTile;
   const int64_t tps = (ntiles + S.n_split - 1) / S.n_split;
   const int64_t tb = (int64_t)split * tps;
@@ -272,22 +289,50 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     }
   }
   if constexpr (TOPK) {
+    const TopkWs& tw = a.tw;
+    const int64_t nv = kind == SRC_TOPK ? topk_visible(qpos_r, S.m2, S.w2, nseq, tw.max_entries) : 0;
+    const bool all = nv <= S.k;  // every visible entry, in order
+    bool ready = true;
+    if (kind == SRC_TOPK && a.filter && !all) {
+      // every TOPK block of the row (slots or not) filters its share of the
+      // row's scores, then counts itself done and waits for the others.  The
+      // launch fits the machine at once, so they are all resident and the
+      // wait ends (bounded all the same: a count that never completes leaves
+      // the slots empty rather than hanging).
+      const int tbi = split * a.n_hb + hb;
+      constexpr int64_t CH = (int64_t)kAttnThreads * kFilterPer;
+      for (int64_t cb = tbi; cb * CH < nv; cb += a.tbpr) {
+        if (cb != tbi) filter_prefetch(tw, r, (int)cb, fpf);  // the first chunk's loads went out at the start
+        filter_chunk(tw, r, nv, (int)cb, fpf, *reinterpret_cast<FilterShared*>(lds_raw));
+        __syncthreads();
+      }
+      if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(&tw.done[r], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&tw.done[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)a.tbpr &&
+               ++spins < kMaxSpins)
+          __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_timeout = spins >= kMaxSpins;
+      }
+      __syncthreads();
+      ready = !s_timeout;
+      topk_prefetch(tw, r, pf);  // the lists are complete now
+    }
     if (kind == SRC_TOPK && te > tb) {  // the block owns slots (even of an empty row)
       // this block's slots [kbase, kbase + cnt) of the row's top k in
       // ascending entry order: every block of the row runs the same exact
       // selection from the filtered lists; the head-block-0 blocks also
       // write their slots to idx_out
-      const TopkWs& tw = a.tw;
       const int64_t cnt = min((te - tb) * kTile, n - kbase);
       if (split == 0 && hb == 0) {
-        // the filter has read the first histogram: clear it for the next call
+        // every filter of the row has read the first histogram: clear it for
+        // the next call
         uint32_t* gh = tw.hist + (int64_t)r * tw.nstripe * kHistBins;
         for (int i = threadIdx.x; i < tw.nstripe * kHistBins; i += kAttnThreads) gh[i] = 0;
       }
-      const int64_t nv = topk_visible(a.q_pos[r], S.m2, S.w2, nseq, tw.max_entries);
-      const bool all = nv <= S.k;  // every visible entry, in order
       for (int i = threadIdx.x; i < cnt; i += kAttnThreads) sidx[i] = (all && kbase + i < nv) ? (int32_t)(kbase + i) : -1;
-      if (!all)
+      if (!all && ready)
         topk_row_select<kAttnThreads, true>(tw, r, pf, *reinterpret_cast<SelectLds*>(lds_raw), sel_sh,
                                             [&](uint32_t o, int32_t e) {
                                               const int64_t j = (int64_t)o - kbase;
@@ -708,8 +753,30 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
 // ============================================================ host
 
 void topk_ws_view(int rows, int64_t maxN, int k, const float* scores, void* ws, TopkWs* view);
-int launch_topk_finalize(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
-                         int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
+int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                       int64_t maxN, const float* scores, void* ws, hipStream_t stream);
+int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                       int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
+
+// Blocks of attn_mfma<D, true> the current device holds at once (compute
+// units x blocks per unit), queried once per device and D.
+static int64_t resident_blocks(int D) {
+  static int64_t cache[64][4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int di = D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : 3;
+  if (cache[dev][di] == 0) {
+    int cus = 0, per = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const void* fn = D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true>)
+                     : D == 128 ? reinterpret_cast<const void*>(&attn_mfma<128, true>)
+                     : D == 256 ? reinterpret_cast<const void*>(&attn_mfma<256, true>)
+                                : reinterpret_cast<const void*>(&attn_mfma<512, true>);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kAttnThreads, 0);
+    cache[dev][di] = (e == hipSuccess && cus > 0 && per > 0) ? (int64_t)cus * per : -1;
+  }
+  return cache[dev][di];
+}
 
 int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
                      int H, int D, float scale, float eps, int dtype, hipStream_t stream) {
@@ -766,16 +833,25 @@ int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, cons
     }
   }
   if (topk >= 0) {
-    // the sparse blocks select from the filtered lists themselves, or the
-    // selection's own launch writes idx_out first
+    // the sparse blocks select from the filtered lists themselves: they also
+    // filter the scores when the whole launch is resident at once (else the
+    // filter kernel runs first); elsewhere the selection's own launches write
+    // idx_out first
     const lca_attn_source& in = srcs[topk];
+    int rc = LCA_OK;
     if (fused_topk) {
       topk_ws_view(B * Tq, in.max_entries, in.k, in.scores, in.ws, &a.tw);
+      const int64_t units = (int64_t)rows * blocks;
+      const int64_t nblk = (units + 7) / 8 * 8 * a.n_hb;
+      a.tbpr = in.n_split * a.n_hb;
+      a.filter = nblk <= resident_blocks(D) ? 1 : 0;
+      if (!a.filter)
+        rc = launch_topk_filter(in.off, q_pos, B, Tq, in.k, in.m2, in.w2, in.max_entries, in.scores, in.ws, stream);
     } else {
-      const int rc = launch_topk_finalize(in.off, q_pos, B, Tq, in.k, in.m2, in.w2, in.max_entries, in.idx_out,
-                                          in.scores, in.ws, stream);
-      if (rc != LCA_OK) return rc;
+      rc = launch_topk_select(in.off, q_pos, B, Tq, in.k, in.m2, in.w2, in.max_entries, in.idx_out, in.scores,
+                              in.ws, stream);
     }
+    if (rc != LCA_OK) return rc;
   }
   if (mfma) {
     const int64_t units = (int64_t)rows * blocks;

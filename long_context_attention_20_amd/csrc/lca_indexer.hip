@@ -53,6 +53,7 @@ struct IndexParams {
   int nstripe;              // histogram copies (score blocks spread their atomics)
   unsigned long long* ctr;  // [rows]: selected count | candidate count << 32
   uint32_t* hist2;          // [rows][kH2Bins]: candidates per second-level bin
+  uint32_t* done;           // [rows]: blocks that finished filtering (in-launch filtering)
   int32_t* sel;             // [rows][k]
   uint64_t* cand;           // [rows][max_entries]
   int32_t* idx;             // [rows][k]
@@ -71,7 +72,10 @@ __device__ __forceinline__ int64_t row_visible(const IndexParams& a, int r, int6
 // histogram, which the filter kernel that follows fills.
 __device__ __forceinline__ void clear_row_state(const IndexParams& a, int r) {
   for (int i = threadIdx.x; i < kH2Bins; i += blockDim.x) a.hist2[(int64_t)r * kH2Bins + i] = 0;
-  if (threadIdx.x == 0) a.ctr[r] = 0;
+  if (threadIdx.x == 0) {
+    a.ctr[r] = 0;
+    a.done[r] = 0;
+  }
 }
 
 __device__ __forceinline__ void hist_add(uint32_t* h, float s) {
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
 
 __device__ __forceinline__ TopkWs topk_view(const IndexParams& a) {
   TopkWs w;
-  w.scores = a.scores; w.hist = a.hist; w.nstripe = a.nstripe; w.ctr = a.ctr; w.hist2 = a.hist2;
+  w.scores = a.scores; w.hist = a.hist; w.nstripe = a.nstripe; w.ctr = a.ctr; w.hist2 = a.hist2; w.done = a.done;
   w.sel = a.sel; w.cand = a.cand; w.max_entries = a.max_entries; w.k = a.k;
   return w;
 }
@@ -353,7 +357,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
   const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - a.csa_off[b]);
   if (nv <= a.k) return;  // the selection takes every visible entry
   if ((int64_t)cb * kSelChunk >= nv) return;
-  filter_chunk<kSelThreads, kSelPerThread>(topk_view(a), r, nv, cb, F);
+  const TopkWs w = topk_view(a);
+  FilterPrefetch<kSelThreads, kSelPerThread> P;
+  filter_prefetch(w, r, cb, P);
+  filter_chunk(w, r, nv, cb, P, F);
 }
 
 constexpr int kFinThreads = 1024;
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
 // ------------------------------------------------------------------ host
 
 struct IndexWs {
-  size_t scores, hist, ctr, hist2, sel, cand, total;
+  size_t scores, hist, ctr, done, hist2, sel, cand, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -406,6 +413,7 @@ static IndexWs index_ws_layout(int rows, int64_t maxN, int k) {
   size_t o = 0;
   w.hist = o;     o = align256(o + (size_t)rows * hist_stripes(rows, maxN) * kHistBins * 4);
   w.ctr = o;      o = align256(o + (size_t)rows * 8);
+  w.done = o;     o = align256(o + (size_t)rows * 4);
   w.hist2 = o;    o = align256(o + (size_t)rows * kH2Bins * 4);
   w.scores = o;   o = align256(o + (size_t)rows * maxN * 4);
   w.sel = o;      o = align256(o + (size_t)rows * k * 4);
@@ -429,6 +437,7 @@ static IndexParams make_params(const void* p, const float* omega, const void* ik
   a.hist = reinterpret_cast<uint32_t*>(base + L.hist);
   a.ctr = reinterpret_cast<unsigned long long*>(base + L.ctr);
   a.hist2 = reinterpret_cast<uint32_t*>(base + L.hist2);
+  a.done = reinterpret_cast<uint32_t*>(base + L.done);
   a.sel = reinterpret_cast<int32_t*>(base + L.sel);
   a.cand = reinterpret_cast<uint64_t*>(base + L.cand);
   a.idx = idx;
@@ -530,7 +539,7 @@ void topk_ws_view(int rows, int64_t maxN, int k, const float* scores, void* ws, 
   IndexParams a = make_params(nullptr, nullptr, nullptr, nullptr, nullptr, rows, 1, 1, 8, k, 1, 1, maxN, nullptr,
                               scores, ws);
   view->scores = a.scores; view->hist = a.hist; view->nstripe = a.nstripe; view->ctr = a.ctr;
-  view->hist2 = a.hist2; view->sel = a.sel; view->cand = a.cand; view->max_entries = maxN; view->k = k;
+  view->hist2 = a.hist2; view->done = a.done; view->sel = a.sel; view->cand = a.cand; view->max_entries = maxN; view->k = k;
 }
 
 int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,

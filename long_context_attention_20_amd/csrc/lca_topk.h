@@ -25,7 +25,6 @@ namespace lca {
 
 constexpr int kHistBins = 2048;   // first-level bins (top 11 key bits)
 constexpr int kH2Bins = 2048;     // second-level bins (key bits 20..10)
-constexpr int kCandLds = 8192;    // candidates staged in LDS
 constexpr int kBitmapWords = 8192;  // entries covered by the ordering bitmap / 32
 constexpr int64_t kBitmapEntries = (int64_t)kBitmapWords * 32;
 
@@ -86,17 +85,14 @@ struct TopkWs {
   int nstripe;
   unsigned long long* ctr;       // [rows]: sel count | candidate count << 32
   uint32_t* hist2;               // [rows][kH2Bins]
+  uint32_t* done;                // [rows]: blocks that finished filtering the row
   int32_t* sel;                  // [rows][k]
   uint64_t* cand;                // [rows][max_entries]
   int64_t max_entries;
   int k;
 };
 
-// The filter of one chunk of NT * PER scores of row r (k < nv, the chunk
-// starts below nv): the threshold bin T from the row's histogram (summed over
-// its stripes), then every entry of the chunk above T appended to sel, every
-// entry inside T to the candidate list (packed as above) and counted in the
-// second histogram.  The list space comes from one 64-bit atomic on ctr.
+// LDS of filter_chunk.
 struct FilterShared {
   uint32_t h[kHistBins];
   uint32_t sm[16];
@@ -105,34 +101,53 @@ struct FilterShared {
   unsigned long long base;
 };
 
+// The loads of one filter chunk (histogram stripes and the chunk's scores,
+// clamped to the row's columns), issued together; a caller can start them
+// before it knows how many of the scores are visible.
 template <int NT, int PER>
-__device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb, FilterShared& F) {
-  constexpr int kMaxStripes = 8;
-  constexpr int HV = kHistBins / 4 / NT;  // uint4 per thread
-  static_assert(HV * 4 * NT == kHistBins, "the histogram must split evenly over the block");
-  const int64_t c0 = (int64_t)cb * NT * PER;
-  // histogram stripes and this chunk's scores, all loads in flight together
-  const uint4* gh = reinterpret_cast<const uint4*>(w.hist + (int64_t)r * w.nstripe * kHistBins);
-  const float* S = w.scores + (int64_t)r * w.max_entries;
+struct FilterPrefetch {
+  static constexpr int kMaxStripes = 8;
+  static constexpr int HV = kHistBins / 4 / NT;  // uint4 per thread and stripe
   uint4 hs[kMaxStripes][HV];
-#pragma unroll
-  for (int st = 0; st < kMaxStripes; ++st)
-#pragma unroll
-    for (int i = 0; i < HV; ++i)
-      hs[st][i] = st < w.nstripe ? gh[st * (kHistBins / 4) + threadIdx.x + i * NT] : make_uint4(0, 0, 0, 0);
-  const int64_t e0 = c0 + (int64_t)threadIdx.x * PER;
   float sv[PER];
+};
+
+template <int NT, int PER>
+__device__ __forceinline__ void filter_prefetch(const TopkWs& w, int r, int cb, FilterPrefetch<NT, PER>& P) {
+  using FP = FilterPrefetch<NT, PER>;
+  static_assert(FP::HV * 4 * NT == kHistBins, "the histogram must split evenly over the block");
+  const uint4* gh = reinterpret_cast<const uint4*>(w.hist + (int64_t)r * w.nstripe * kHistBins);
+#pragma unroll
+  for (int st = 0; st < FP::kMaxStripes; ++st)
+#pragma unroll
+    for (int i = 0; i < FP::HV; ++i)
+      P.hs[st][i] = st < w.nstripe ? gh[st * (kHistBins / 4) + threadIdx.x + i * NT] : make_uint4(0, 0, 0, 0);
+  const float* S = w.scores + (int64_t)r * w.max_entries;
+  const int64_t e0 = (int64_t)cb * NT * PER + (int64_t)threadIdx.x * PER;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t e = e0 + i;
-    sv[i] = S[e < nv ? e : nv - 1];
+    P.sv[i] = S[e < w.max_entries ? e : w.max_entries - 1];
   }
+}
+
+// The filter of one chunk of NT * PER scores of row r (k < nv, the chunk
+// starts below nv) from its prefetched loads: the threshold bin T from the
+// row's histogram (summed over its stripes), then every entry of the chunk
+// above T appended to sel, every entry inside T to the candidate list (packed
+// as above) and counted in the second histogram.  The list space comes from
+// one 64-bit atomic on ctr.
+template <int NT, int PER>
+__device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb, const FilterPrefetch<NT, PER>& P,
+                             FilterShared& F) {
+  using FP = FilterPrefetch<NT, PER>;
+  const int64_t e0 = (int64_t)cb * NT * PER + (int64_t)threadIdx.x * PER;
 #pragma unroll
-  for (int i = 0; i < HV; ++i) {
-    uint4 v = hs[0][i];
+  for (int i = 0; i < FP::HV; ++i) {
+    uint4 v = P.hs[0][i];
 #pragma unroll
-    for (int st = 1; st < kMaxStripes; ++st) {
-      v.x += hs[st][i].x; v.y += hs[st][i].y; v.z += hs[st][i].z; v.w += hs[st][i].w;
+    for (int st = 1; st < FP::kMaxStripes; ++st) {
+      v.x += P.hs[st][i].x; v.y += P.hs[st][i].y; v.z += P.hs[st][i].z; v.w += P.hs[st][i].w;
     }
     reinterpret_cast<uint4*>(F.h)[threadIdx.x + i * NT] = v;
   }
@@ -145,7 +160,7 @@ __device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb, FilterS
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const bool in = e0 + i < nv;
-    keys[i] = score_key(sv[i]);
+    keys[i] = score_key(P.sv[i]);
     const uint32_t bin = keys[i] >> 21;
     ns += (in && bin > T) ? 1u : 0u;
     nc += (in && bin == T) ? 1u : 0u;

@@ -164,18 +164,6 @@ def csa_topk_select(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws
     return idx
 
 
-def csa_topk_filter(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws: torch.Tensor,
-                    scores: Optional[torch.Tensor] = None):
-    """First launch of csa_topk_select alone: the filtered lists in the
-    workspace, for a "topk" source of hybrid_attn to select from."""
-    _dev(csa_off, q_pos, ws, scores)
-    B = csa_off.numel() - 1
-    rows = q_pos.numel()
-    check(lib.lca_csa_topk_filter(_ptr(csa_off), _ptr(q_pos), B, rows // B, k, m, w, int(max_entries),
-                                  _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(), _stream()),
-          "csa_topk_filter")
-
-
 # ---------------------------------------------------------------- a4 / a5
 
 def _parts_out(rows, H, D, n_split, device, o_part, lse):
@@ -240,10 +228,10 @@ def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
     """The attention branches of a step in one launch.  sources: dicts with
     kind ("gather", "dense", "window" or "topk"), kv, off and n_split, plus
     idx (gather), m2 and w2 (dense), W (window), and optionally o_part / lse.
-    A "topk" source selects the sparse branch's entries from the lists that
-    csa_index_score(_append) and then csa_topk_filter left in the workspace:
-    it takes k, m2 = m, w2 = w, max_entries, ws, idx_out (int32 [rows, k],
-    written) and optionally scores.  Returns one (o_part, lse) pair per source, as the
+    A "topk" source selects the sparse branch's entries from the scores a
+    csa_index_score(_append) call left in its workspace: it takes k, m2 = m,
+    w2 = w, max_entries, ws, idx_out (int32 [rows, k], written) and
+    optionally scores.  Returns one (o_part, lse) pair per source, as the
     single-branch calls."""
     if not 1 <= len(sources) <= 3:
         raise ValueError("1..3 sources per call")

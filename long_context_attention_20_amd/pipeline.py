@@ -5,14 +5,13 @@ strides and windows), the caller's caches as device tensors with their host
 and device offsets, and reusable workspaces.  It only sizes buffers and
 sequences the C entry points; every step runs in the HIP kernels.
 
-Decode step (one query row per sequence), four launches on one stream:
+Decode step (one query row per sequence), three calls on one stream:
     csa_index_score_append  the CSA, indexer-key and HCA entries the new token
-                            completes, and the index scores
-    csa_topk_filter         the entries above the top-k threshold bin and the
-                            candidates inside it
-    hybrid_attn             exact top-k (each sparse block selects its share of
-                            the ascending list), then CSA sparse + HCA dense +
-                            window partials
+                            completes, and the index scores (one launch)
+    hybrid_attn             exact top-k (every sparse block filters a share of
+                            the scores, then selects its share of the ascending
+                            list), CSA sparse + HCA dense + window partials
+                            (one launch when it fits the device at once)
     swa_merge               sink + merge of every partial
 Prefill chunks (several rows per sequence) run kv_compress and
 csa_index_score as separate launches.
@@ -245,9 +244,9 @@ class HybridAttention:
         launch.  With a side stream the HCA append runs there instead, beside
         the indexer (the join costs a cross-queue wait in a graph).  lens_h:
         host copy of the sequence lengths tok_off describes, when they are
-        shorter than the caches'.  fuse_topk: after csa_topk_filter, the
-        exact selection runs inside the attention launch (a TOPK source)
-        rather than as csa_topk_select's second launch."""
+        shorter than the caches'.  fuse_topk: the top-k selection runs
+        inside the attention call (a TOPK source) rather than as
+        csa_topk_select."""
         main = torch.cuda.current_stream()
         join = None
         scored = False
@@ -275,9 +274,7 @@ class HybridAttention:
         if not scored:
             ops.csa_index_score(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w,
                                 bufs["max_csa"], bufs["ws_idx"])
-        if fuse_topk:
-            ops.csa_topk_filter(caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"], bufs["ws_idx"])
-        else:
+        if not fuse_topk:
             ops.csa_topk_select(caches.csa_off, q_pos, self.k, self.m, self.w, bufs["max_csa"], bufs["ws_idx"],
                                 idx=bufs["idx"])
         if join is not None:

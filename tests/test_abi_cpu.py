@@ -196,21 +196,6 @@ def test_hybrid_attn_rejects_topk(L):
     assert call() == L.LCA_ERR_UNSUPPORTED
 
 
-def test_topk_filter_rejects(L):
-    lib = L.lib
-    P = ctypes.c_void_p(256)
-    need = lib.lca_csa_index_topk_workspace(1, 1000, 512)
-
-    def call(csa_off=P, q_pos=P, k=512, m=4, w=8, maxN=1000, ws=P, ws_bytes=need):
-        return lib.lca_csa_topk_filter(csa_off, q_pos, 1, 1, k, m, w, maxN, None, ws, ws_bytes, None)
-    assert call(csa_off=None) == L.LCA_ERR_INVALID_ARG
-    assert call(q_pos=None) == L.LCA_ERR_INVALID_ARG
-    assert call(k=0) == L.LCA_ERR_UNSUPPORTED
-    assert call(w=0) == L.LCA_ERR_INVALID_ARG
-    assert call(ws=None) == L.LCA_ERR_WORKSPACE
-    assert call(ws_bytes=need - 1) == L.LCA_ERR_WORKSPACE
-
-
 def test_index_score_append_rejects(L):
     lib = L.lib
     P = ctypes.c_void_p(256)

@@ -552,7 +552,6 @@ def _topk_source_vs_separate(cfg, d, caches, q_pos, qmax, splits=(3, 5, 2), reps
     for rep in range(reps):
         idx_out = torch.full((rows, cfg.k), -7, dtype=torch.int32, device="cuda")
         ops.csa_index_score(d["p"], d["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws)
-        ops.csa_topk_filter(caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws)
         src = dict(kind="topk", kv=caches.kv_csa, off=caches.csa_off, k=cfg.k, m2=cfg.m, w2=cfg.w,
                    max_entries=max_csa, ws=ws, idx_out=idx_out, n_split=sc)
         got = ops.hybrid_attn(d["q"], q_pos, [src] + others, cfg.scale, cfg.eps)
@@ -578,8 +577,9 @@ def test_topk_source_equals_separate(name):
 
 
 def test_topk_source_many_rows():
-    """129 query rows over 262144 tokens (65535 entries each), every sparse
-    block selecting its row's share from the filtered lists; same results."""
+    """129 query rows over 262144 tokens (65535 entries each): more blocks
+    than the device holds at once, so the filter runs as its own launch and
+    every sparse block selects its row's share; same results."""
     cfg = li.small("topk_ext", 114, (262144,), tq=129, H=16, D=64, HI=4, dI=64, k=512)
     print(f"[topk source many rows] rows={cfg.tq} L={cfg.lens[0]}", flush=True)
     raw = li.make_raw_torch(cfg, 0, "cuda")
