@@ -55,9 +55,10 @@ HBM_PEAK = 8.0e12          # bytes/s, MI355X
 TRAFFIC = {
     ("pro_1m_decode", "hybrid_attn"): {
         "files": ["long_context_attention_20_amd/csrc/lca_attention.hip",
-                  "long_context_attention_20_amd/csrc/lca_common.h"],
-        "sha1": "ea06c7832f3964482b5f65ee0bc1a60a0eac6b37",
-        "fetch_kib": 5305.5, "write_kib": 12825.0, "fetch_scale": 2.0, "write_scale": 1.0,
+                  "long_context_attention_20_amd/csrc/lca_common.h",
+                  "long_context_attention_20_amd/csrc/lca_topk.h"],
+        "sha1": "53461ea90176503a6fd011b1269d79a43f3451b0",
+        "fetch_kib": 6341.0, "write_kib": 15521.6, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
