@@ -384,8 +384,8 @@ def main():
                     help="only run a plain device copy of MIB MiB 10 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1 "
+                                   "(the path has no multi-GPU sharding)"}))
         sys.exit(2)
 
     import torch

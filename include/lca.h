@@ -42,7 +42,7 @@ extern "C" {
 enum lca_status {
   LCA_OK = 0,
   LCA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent sizes */
-  LCA_ERR_UNSUPPORTED = -2, /* a shape or type this build has no kernel for */
+  LCA_ERR_UNSUPPORTED = -2, /* a shape or type the library has no kernel for */
   LCA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   LCA_ERR_HIP = -4          /* the HIP runtime reported an error */
 };
@@ -57,7 +57,7 @@ const char* lca_last_error(void);
 int lca_version(void);
 
 /* ------------------------------------------------------------------------
- * a1. KV compression
+ * KV compression
  *
  * "Why DeepSeek V4 Stands Apart", Core Architectural Innovations (CSA
  * compresses KV entries 4x; HCA compresses 128:1) and "DeepSeek-V4", Design
@@ -96,14 +96,14 @@ typedef struct lca_compress_stream {
  *   streams  host array of n_streams (1..4) descriptors
  *   tok_off  device int64 [B+1]
  *   done_len device int64 [B] or NULL (0 for every sequence)
- *   eps      RMSNorm epsilon (1e-6 in this build's workloads)
+ *   eps      RMSNorm epsilon (1e-6 in the benchmark workloads)
  * Returns LCA_OK or an error; the caller must make ent_off leave room for
  * N(L_b) rows per sequence and max_entries >= N(L_b) - N(done_len[b]). */
 int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int64_t* tok_off,
                     const int64_t* done_len, int B, float eps, int dtype, void* stream);
 
 /* ------------------------------------------------------------------------
- * a2 + a3. Lightning-indexer scores and exact top-k over the CSA entries
+ * Lightning-indexer scores and exact top-k over the CSA entries
  *
  * "DeepSeek-V4", Design overview and Inference efficiency (V3.2's lightning
  * indexer on the compressed entries); "Why DeepSeek V4 Stands Apart", Core
@@ -151,7 +151,7 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
                         const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
                         int64_t max_entries, float* scores, void* ws, size_t ws_bytes, int dtype,
                         void* stream);
-/* a1 + a2 for one decode step: the compression of the entries the newest
+/* Compression + indexer scores for one decode step: the compression of the entries the newest
  * tokens complete and the index scores, in one launch.  Equivalent to
  *     lca_kv_compress({idx_stream} + kv_streams, tok_off, done_len, ...)
  *     lca_csa_index_score(..., Tq = 1, ...)
@@ -182,7 +182,7 @@ int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int
                         void* stream);
 
 /* ------------------------------------------------------------------------
- * Attention partials (a4, a5)
+ * Attention partials (sparse CSA, dense HCA)
  *
  * Shared-KV multi-query attention ("DeepSeek-V4", Inference efficiency): all H
  * query heads attend to the same keys, and a compressed entry is key and value.
@@ -198,7 +198,7 @@ int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int
  * matrix cores for bf16); 1 <= n_split <= 256.
  * ---------------------------------------------------------------------- */
 
-/* a4. Sparse attention over the selected CSA entries ("Why DeepSeek V4
+/* Sparse attention over the selected CSA entries ("Why DeepSeek V4
  * Stands Apart", Core Architectural Innovations: attention over the top-k
  * compressed entries of each query).
  *   q       [B*Tq, H, D] raw queries (dtype)
@@ -208,7 +208,7 @@ int lca_csa_sparse_attn(const void* q, const void* kv_csa, const int64_t* csa_of
                         int B, int Tq, int H, int D, int k, float scale, float eps, int n_split,
                         float* o_part, float* lse, int dtype, void* stream);
 
-/* a5. Dense attention over every visible HCA entry ("Why DeepSeek V4 Stands
+/* Dense attention over every visible HCA entry ("Why DeepSeek V4 Stands
  * Apart", Core Architectural Innovations: dense attention over the 128:1
  * compressed representation).  Entry j of sequence b is visible to the query
  * at position i iff j*m2 + w2 - 1 <= i.
@@ -219,7 +219,7 @@ int lca_hca_attn(const void* q, const void* kv_hca, const int64_t* hca_off, cons
                  int n_split, float* o_part, float* lse, int dtype, void* stream);
 
 /* ------------------------------------------------------------------------
- * a6. Sliding window + sink + merge
+ * Sliding window + sink + merge
  *
  * "Why DeepSeek V4 Stands Apart", Core Architectural Innovations (window of
  * the most recent 128 tokens); "DeepSeek-V4", Core block (attention sinks).

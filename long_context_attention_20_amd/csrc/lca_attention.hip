@@ -1,4 +1,4 @@
-// a4 / a5 / a6. Shared-KV attention partials and the log-sum-exp merge.
+// Shared-KV attention partials and the log-sum-exp merge.
 //
 // Pages: "DeepSeek-V4", Inference efficiency (one KV head shared by all query
 // heads), Core block and Provenance 17-18 (RMSNorm on queries and compressed

@@ -1,4 +1,4 @@
-// a1. KV compression device code: the pooling state, the small-window run
+// KV compression device code: the pooling state, the small-window run
 // walk and the large-window block walk (see lca_compress.hip for the method
 // and its sources).  Shared by the compression kernel and by the index-score
 // launch that appends entries with extra blocks.  The walks take the block

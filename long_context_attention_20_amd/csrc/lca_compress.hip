@@ -1,4 +1,4 @@
-// a1. KV compression: softmax-weighted window pooling (+ RMSNorm) of raw rows.
+// KV compression: softmax-weighted window pooling (+ RMSNorm) of raw rows.
 //
 // Pages: "Why DeepSeek V4 Stands Apart", Core Architectural Innovations (CSA
 // compresses KV entries 4x, HCA 128:1); "DeepSeek-V4", Design overview (every

@@ -1,4 +1,4 @@
-// a2 + a3. Lightning-indexer scores over the visible CSA entries and an exact
+// Lightning-indexer scores over the visible CSA entries and an exact
 // top-k selection.
 //
 // Pages: "DeepSeek-V4", Design overview (CSA applies V3.2's lightning indexer

@@ -53,7 +53,7 @@ def _i32(t: torch.Tensor, what: str):
         raise TypeError(f"{what} must be int32")
 
 
-# ---------------------------------------------------------------- a1
+# ---------------------------------------------------------------- compression
 
 def _stream_array(streams: Sequence[dict]):
     """ctypes array of lca_compress_stream and the common element type."""
@@ -91,7 +91,7 @@ def kv_compress(streams: Sequence[dict], tok_off: torch.Tensor, done_len: Option
           "kv_compress")
 
 
-# ---------------------------------------------------------------- a2 + a3
+# ---------------------------------------------------------------- indexer + top-k
 
 def csa_index_topk_workspace(n_rows: int, max_entries: int, k: int) -> int:
     return int(lib.lca_csa_index_topk_workspace(n_rows, max_entries, k))
@@ -164,7 +164,7 @@ def csa_topk_select(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws
     return idx
 
 
-# ---------------------------------------------------------------- a4 / a5
+# ---------------------------------------------------------------- attention partials
 
 def _parts_out(rows, H, D, n_split, device, o_part, lse):
     if o_part is None:
@@ -206,7 +206,7 @@ def hca_attn(q, kv_hca, hca_off, q_pos, m2: int, w2: int, max_entries: int, scal
     return o_part, lse
 
 
-# ---------------------------------------------------------------- a6
+# ---------------------------------------------------------------- window + sink + merge
 
 def swa_attn(q, x, tok_off, q_pos, W: int, scale: float, eps: float, o_part=None, lse=None):
     """The window branch as a one-split partial (o_part [1, rows, H, D], lse)."""

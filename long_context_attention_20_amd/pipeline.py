@@ -79,7 +79,7 @@ class HybridAttention:
             kv_hca=torch.empty((max(1, int(ho[-1])), self.D), dtype=dtype, device=device),
             csa_off_h=co, hca_off_h=ho)
 
-    # -------------------------------------------------------------- a1
+    # -------------------------------------------------------------- compression
     def compress_streams(self, caches: Caches, raw: dict, done_h: Sequence[int], which=("csa", "idx", "hca"),
                          lens_h: Optional[Sequence[int]] = None):
         """Descriptors of the entries completed after done_h[b] tokens (up to
@@ -127,7 +127,7 @@ class HybridAttention:
         for g in groups.values():
             ops.kv_compress(g, tok_off, done_len, self.eps)
 
-    # -------------------------------------------------------------- a2-a6
+    # -------------------------------------------------------------- indexer, top-k, attention
     def index_workspace(self, rows: int, max_entries: int, device) -> torch.Tensor:
         nbytes = ops.csa_index_topk_workspace(rows, max(1, max_entries), self.k)
         return self._workspace(f"idx{rows}_{max_entries}", nbytes, device, zero=True)

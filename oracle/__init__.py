@@ -17,8 +17,8 @@ the DeepSeek-V4 pages say the attention stack computes:
   compressed KV entries; attention sinks; Inference efficiency: one shared KV
   head (MQA).
 
-Where the pages leave a step open, the oracle takes the reading listed in
-DESIGN.md ("Readings").  Modules:
+Where the pages leave a step open, the oracle takes the plainest reading the
+rest supports and states it in the module that uses it.  Modules:
 
 * ``numerics``  rounding to the storage precisions (bf16 / fp32)
 * ``compress``  softmax-weighted window pooling + RMSNorm      (kv_compress)

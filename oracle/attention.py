@@ -6,7 +6,7 @@ compressed KV entries; attention sinks); "Why DeepSeek V4 Stands Apart", Core
 Architectural Innovations (128-token sliding window; sparse attention over the
 selected CSA entries; dense attention over the HCA entries).
 
-Readings (DESIGN.md): a compressed entry serves as both key and value (K = V);
+Readings: a compressed entry serves as both key and value (K = V);
 logits are scale * qhat_h . key with scale = 1/sqrt(D); the sink of head h is
 one logit sigma_h with a zero value, so it only enlarges the denominator.
 

@@ -5,7 +5,7 @@ compresses KV entries 4x; HCA compresses 128:1); "DeepSeek-V4", Design overview
 (CSA compresses every 4 tokens into two overlapping streams; HCA uses m'=128)
 and Provenance reference 17 (RMSNorm on the compressed KV entries).
 
-Readings (DESIGN.md): entry j of a stream with stride m and window w pools the
+Readings: entry j of a stream with stride m and window w pools the
 tokens t = j*m .. j*m+w-1 with weights softmax_t(z[t, c]) taken separately for
 every channel c; only complete windows exist, so a sequence of L tokens has
 N(L) = 0 if L < w else (L - w) // m + 1 entries.  CSA uses m=4, w=8 (each token

@@ -8,7 +8,7 @@ oracle (its own pooling, norm, scoring, selection and softmax), so the two pin
 each other on tiny inputs.  Too slow for anything but a few hundred tokens and
 a handful of channels.
 
-Same readings as the vectorised oracle ("Readings"); rounding uses
+Same readings as the vectorised oracle (stated in its modules); rounding uses
 oracle.numerics so that both see the same stored values.
 """
 import math

@@ -5,7 +5,7 @@ attention of V3.2 to the compressed entries) and Inference efficiency (the
 indexer QK path); "Why DeepSeek V4 Stands Apart", Core Architectural
 Innovations (top-1024 entries per query for Pro, top-512 for Flash).
 
-Reading (DESIGN.md): the score of compressed entry j for one query is
+Reading: the score of compressed entry j for one query is
     s_j = sum_r omega_r * max(0, p_r . key_j)
 over the H_I indexer heads r, with one shared indexer key per entry, no scale
 and no normalisation.  Only entries whose window ends at or before the query

@@ -18,7 +18,7 @@ token is already part of the context; prefill: every position of the chunk):
 Pages: "Why DeepSeek V4 Stands Apart", Core Architectural Innovations; "DeepSeek-V4",
 Design overview, Core block, Inference efficiency; "DeepSeek V4 Is Not a Better
 Model", 1. CSA + HCA (older tokens compressed, recent tokens kept at full
-resolution).  Readings are listed in the design doc.
+resolution).  The readings taken are stated in the modules this one calls.
 """
 from dataclasses import dataclass
 from typing import List, Optional

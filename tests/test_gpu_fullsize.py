@@ -57,7 +57,7 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
         ikey = f64(caches.ikey[co[b]:co[b + 1]])
         kv_hca = f64(caches.kv_hca[ho[b]:ho[b + 1]])
         ncsa, nhca = ocmp.n_entries(L, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m2, cfg.w2)
-        # ---- a1 on sampled entries (and the appended last ones)
+        # ---- compression on sampled entries (and the appended last ones)
         ent = sorted(set(rng.choice(ncsa, size=min(48, ncsa), replace=False).tolist()) | {ncsa - 1})
         for got, src, lg, norm in ((kv_csa, x, a, True), (ikey, u, c, False)):
             ref = onum.round_to(ocmp.compress(src, lg, cfg.m, cfg.w, norm, cfg.eps, ent), cfg.dtype)
@@ -65,7 +65,7 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
         entj = sorted(set(rng.choice(nhca, size=min(16, nhca), replace=False).tolist()) | {nhca - 1})
         ref = onum.round_to(ocmp.compress(x, g, cfg.m2, cfg.w2, True, cfg.eps, entj), cfg.dtype)
         assert np.max(np.abs(kv_hca[entj] - ref)) <= 2e-2
-        # ---- a2/a3: every visible entry scored in float64 from the GPU-stored keys
+        # ---- scores and top-k: every visible entry scored in float64 from the GPU-stored keys
         i = L - 1
         p = f64(raw["p"][b])
         om = raw["omega"][b].cpu().numpy().astype(np.float64)
@@ -81,7 +81,7 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
         for j in diff:
             assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + bound[j], f"entry {j} is not a near tie"
         print(f"  top-{cfg.k}: {len(diff)} near-tie differences", flush=True)
-        # ---- a4-a6 stage-wise (GPU caches and selection), all heads
+        # ---- attention, window, sink and merge stage-wise (GPU caches and selection), all heads
         qhat = oatt.normalize_query(f64(raw["q"][b]), cfg.eps, cfg.dtype)
         csa = oatt.partial(qhat, kv_csa[chosen], cfg.scale)
         hca = oatt.partial(qhat, kv_hca[:nhca], cfg.scale)
