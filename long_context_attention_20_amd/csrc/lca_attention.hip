@@ -750,6 +750,89 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
   }
 }
 
+// Many rows, few partials (prefill chunks): one wave per (row, head), a lane
+// owning DPL = D/64 consecutive dims; lane s holds slot s's lse, the slot
+// weights come from wave reductions, and every slot's partial is requested
+// before any is used.  At most kRowsSlots slots.
+constexpr int kRowsSlots = 16;
+constexpr int kRowsWaves = 4;  // (row, head) pairs per block
+
+template <typename ET, int DPL>
+__global__ __launch_bounds__(64 * kRowsWaves) void merge_rows_kernel(MergeParams a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t RH = (int64_t)a.rows * a.H;
+  const int64_t rh = (int64_t)blockIdx.x * kRowsWaves + (threadIdx.x >> 6);
+  if (rh >= RH) return;  // uniform per wave
+  const int h = (int)(rh % a.H);
+  // slot -> (part, split): slots list the parts in order
+  auto slot_part = [&](int s, int* t) {
+    int p = 0;
+    while (p + 1 < a.n_parts && s >= a.n_split[p]) { s -= a.n_split[p]; ++p; }
+    *t = s;
+    return p;
+  };
+  float v[kRowsSlots][DPL];
+#pragma unroll
+  for (int s = 0; s < kRowsSlots; ++s) {
+    if (s < a.n_slots) {  // uniform
+      int t;
+      const int p = slot_part(s, &t);
+      const float* op = a.o[p] + ((int64_t)t * RH + rh) * a.D + lane * DPL;
+      if constexpr (DPL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < DPL; i += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(op + i);
+          v[s][i] = x.x; v[s][i + 1] = x.y; v[s][i + 2] = x.z; v[s][i + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) v[s][i] = op[i];
+      }
+    }
+  }
+  float l = -INFINITY;
+  if (lane < a.n_slots) {
+    int t;
+    const int p = slot_part(lane, &t);
+    l = a.lse[p][(int64_t)t * RH + rh];
+  }
+  float mx = wave_max(l, 64);
+  const float sk = a.sink ? a.sink[h] : -INFINITY;
+  mx = fmaxf(mx, sk);
+  float den = (mx != -INFINITY && l != -INFINITY) ? expf(l - mx) : 0.f;
+  den = wave_sum(den, 64);
+  if (a.sink && mx != -INFINITY) den += expf(sk - mx);
+  const float lse_tot = mx != -INFINITY ? mx + logf(den) : -INFINITY;
+  const float w_lane = (l != -INFINITY && lse_tot != -INFINITY) ? expf(l - lse_tot) : 0.f;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kRowsSlots; ++s) {
+    if (s < a.n_slots) {
+      const float w = __shfl(w_lane, s, 64);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, v[s][i], acc[i]);
+    }
+  }
+  const int64_t off = rh * a.D + lane * DPL;
+  if constexpr (ET::kBytes == 2) {
+    uint32_t pk[DPL / 2];
+#pragma unroll
+    for (int i = 0; i < DPL / 2; ++i) pk[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + off;
+    if constexpr (DPL == 8) {
+      *reinterpret_cast<uint4*>(o) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPL / 2; ++i) reinterpret_cast<uint32_t*>(o)[i] = pk[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) reinterpret_cast<float*>(a.out)[off + i] = acc[i];
+  }
+}
+
 // ============================================================ host
 
 void topk_ws_view(int rows, int64_t maxN, int k, const float* scores, void* ws, TopkWs* view);
@@ -897,6 +980,24 @@ int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, cons
   a.n_parts = np;
   a.n_slots = ns;
   a.sink = sink; a.rows = rows; a.H = H; a.D = D; a.out = out;
+  if (ns <= kRowsSlots && (int64_t)rows * H >= 1024 && D >= 128) {
+    // many rows, few partials: one wave per (row, head)
+    const int64_t nblk = ((int64_t)rows * H + kRowsWaves - 1) / kRowsWaves;
+    if (nblk > 0x7FFFFFFF) {
+      set_error("merge: %lld blocks exceed the grid limit", (long long)nblk);
+      return LCA_ERR_UNSUPPORTED;
+    }
+    dim3 grid((unsigned)nblk);
+#define LCA_MERGE_ROWS(ETy)                                                                                  \
+  switch (D) {                                                                                               \
+    case 128: hipLaunchKernelGGL((merge_rows_kernel<ETy, 2>), grid, dim3(64 * kRowsWaves), 0, stream, a); break; \
+    case 256: hipLaunchKernelGGL((merge_rows_kernel<ETy, 4>), grid, dim3(64 * kRowsWaves), 0, stream, a); break; \
+    default: hipLaunchKernelGGL((merge_rows_kernel<ETy, 8>), grid, dim3(64 * kRowsWaves), 0, stream, a); break;  \
+  }
+    if (dtype == LCA_BF16) { LCA_MERGE_ROWS(BF16) } else { LCA_MERGE_ROWS(F32) }
+#undef LCA_MERGE_ROWS
+    return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+  }
   // (row, head) pairs x 256-dim parts
   const int64_t nblk = (int64_t)rows * H * (D > 256 ? D / 256 : 1);
   if (nblk > 0x7FFFFFFF) {
