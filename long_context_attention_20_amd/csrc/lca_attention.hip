@@ -836,6 +836,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void merge_rows_kernel(MergeParams
 // ============================================================ host
 
 void topk_ws_view(int rows, int64_t maxN, int k, const float* scores, void* ws, TopkWs* view);
+bool topk_rows_mode(int Tq, int64_t maxN);
 int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, const float* scores, void* ws, hipStream_t stream);
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
@@ -883,7 +884,8 @@ int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, cons
     blocks += in.n_split;
     if (in.kind == SRC_TOPK) {
       topk = i;
-      fused_topk = mfma && in.max_entries <= kBitmapEntries;
+      // (many rows per sequence are selected one block per row instead)
+      fused_topk = mfma && in.max_entries <= kBitmapEntries && !topk_rows_mode(Tq, in.max_entries);
       if (fused_topk) {
         d.idx_out = in.idx_out;
       } else {

@@ -54,6 +54,7 @@ struct IndexParams {
   unsigned long long* ctr;  // [rows]: selected count | candidate count << 32
   uint32_t* hist2;          // [rows][kH2Bins]: candidates per second-level bin
   uint32_t* done;           // [rows]: blocks that finished filtering (in-launch filtering)
+  int no_hist;              // 1: many rows per sequence, selected one block per row (no histograms)
   int32_t* sel;             // [rows][k]
   uint64_t* cand;           // [rows][max_entries]
   int32_t* idx;             // [rows][k]
@@ -101,7 +102,7 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
   const int64_t c1 = min(min(c0 + a.chunk, nv), lim);
   if (cx == 0) clear_row_state(a, r);
   if (c0 >= c1) return;
-  const bool do_hist = nv > a.k;
+  const bool do_hist = nv > a.k && !a.no_hist;
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -217,7 +218,7 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
   // does); the visible ones are scored
   const int64_t n_hi = n_windows(ap.tok_off[b + 1] - t0, s.m, s.w);
   const int64_t n_lo = n_windows(ap.done_len[b], s.m, s.w);
-  const bool do_hist = nv > a.k;
+  const bool do_hist = nv > a.k && !a.no_hist;
   const int64_t rb = (int64_t)s.C * 2;
   const char* src = reinterpret_cast<const char*>(s.src) + t0 * rb;
   const char* lg = reinterpret_cast<const char*>(s.logits) + (s.per_channel ? t0 * rb : t0 * 2);
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
   if (blockIdx.x == 0) clear_row_state(a, r);
   if (c0 >= nv) return;
   const int64_t c1 = min(c0 + a.chunk, nv);
-  const bool do_hist = nv > a.k;
+  const bool do_hist = nv > a.k && !a.no_hist;
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0;
   const int nq = a.HI * a.dI;
   for (int i = threadIdx.x; i < nq; i += blockDim.x) sp[i] = ET::load1(a.p, (int64_t)r * nq + i);
@@ -338,6 +339,104 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
   }
   __syncthreads();
   if (do_hist) hist_flush(lh, a.hist + ((int64_t)r * a.nstripe + blockIdx.x % a.nstripe) * kHistBins);
+}
+
+// ------------------------------------------------------------------ many rows
+// Prefill chunks and other calls with many query rows per sequence: the
+// scores as a row-tiled matrix product, so that a block reuses every key it
+// loads for 32 query rows.  Block (entry tile, row group): 32 consecutive
+// rows of one sequence x 1024 entries, each wave 256 of them in 16-entry
+// blocks.  The A operand packs (row, head) pairs: with HI heads, an MFMA row
+// block holds 16 / HI query rows, and the accumulator lane (col, grp) holds
+// heads 4*grp .. 4*grp+3 of entry col -- 4 / HI whole query rows, so the
+// weighted ReLU sum over the heads stays inside the lane.  No histogram: the
+// selection of these calls runs one block per row (topk_rows).
+constexpr int kRowsPerBlock = 32;
+constexpr int kRowsEntriesPerWave = 256;
+constexpr int kRowMaxEntries = 98304;  // entries per row the one-block selection takes
+
+static bool rows_mode(int Tq, int64_t maxN) { return Tq >= kRowsPerBlock && maxN <= kRowMaxEntries; }
+
+template <int KS, int HI>
+__global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
+  constexpr int QR = 16 / HI;                // query rows per MFMA row block
+  constexpr int RB = kRowsPerBlock / QR;     // MFMA row blocks per block
+  constexpr int RPL = 4 / HI;                // query rows per accumulator lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int gps = (a.Tq + kRowsPerBlock - 1) / kRowsPerBlock;  // row groups per sequence
+  const int b = blockIdx.y / gps;
+  const int t0 = (blockIdx.y % gps) * kRowsPerBlock;
+  const int nrows = min(kRowsPerBlock, a.Tq - t0);
+  const int r0 = b * a.Tq + t0;
+  const int64_t e_base = a.csa_off[b];
+  const int64_t nseq = a.csa_off[b + 1] - e_base;
+  // the most entries any row of the group sees (lanes 0..31 one row each)
+  int64_t nv_lane = 0;
+  if (lane < nrows) nv_lane = row_visible(a, r0 + lane, nseq);
+  int64_t nv_max = nv_lane;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int64_t x = __shfl_xor(nv_max, o, 64);
+    nv_max = x > nv_max ? x : nv_max;
+  }
+  const int64_t w0 = (int64_t)blockIdx.x * (4 * kRowsEntriesPerWave) + (int64_t)wave * kRowsEntriesPerWave;
+  if (w0 >= nv_max) return;  // uniform per wave
+  // A operands: lane (col, grp) holds (row rb*QR + col/HI, head col%HI), dims 32*ks + 8*grp ..
+  bf16x8_t A[RB][KS];
+  float om[RB][4];
+  const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qr = rb * QR + col / HI;
+    const bool ok = qr < nrows;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ok) v = *reinterpret_cast<const uint4*>(P + ((int64_t)(r0 + qr) * HI + col % HI) * a.dI + ks * 32 + grp * 8);
+      A[rb][ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    // weights of the accumulator rows 4*grp + i: (row rb*QR + (4*grp + i)/HI, head (4*grp + i)%HI)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * grp + i;
+      const int q2 = rb * QR + m / HI;
+      om[rb][i] = q2 < nrows ? a.omega[(int64_t)(r0 + q2) * HI + m % HI] : 0.f;
+    }
+  }
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.ikey) + e_base * a.dI;
+  constexpr int EB = 4;  // 16-entry blocks in flight
+  const int64_t wend = min(w0 + kRowsEntriesPerWave, min(nv_max, a.max_entries));
+  for (int64_t e0 = w0; e0 < wend; e0 += 16 * EB) {
+    uint4 kv[EB][KS];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      int64_t e = e0 + u * 16 + col;
+      if (e >= nseq) e = nseq - 1;  // clamp: stays inside the sequence's keys
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(K + e * a.dI + ks * 32 + grp * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      const int64_t e = e0 + u * 16 + col;
+      const bool e_ok = e < wend;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb][ks], __builtin_bit_cast(bf16x8_t, kv[u][ks]), acc, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) {
+          float sc = 0.f;
+#pragma unroll
+          for (int h = 0; h < HI; ++h) sc = fmaf(om[rb][q * HI + h], fmaxf(acc[q * HI + h], 0.f), sc);
+          const int qr = rb * QR + (4 * grp) / HI + q;
+          if (e_ok && qr < nrows) a.scores[(int64_t)(r0 + qr) * a.max_entries + e] = sc;
+        }
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ select
@@ -387,6 +486,141 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
                                             : topk_row_select<kFinThreads, false>(w, r, P, L, S, emit);
   if (got == 0)
     for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = -1;
+}
+
+// The exact top-k of one row per block, for calls with many rows per
+// sequence (scores from index_score_rows, at most kRowMaxEntries per row):
+// an LDS histogram of the top 11 key bits of every visible score gives the
+// threshold bin T; a second pass over the scores marks every entry above T in
+// an LDS bitmap and lists the candidates inside T (packed as in lca_topk.h)
+// in the row's workspace, counting them per next-11-bit bin; the second
+// histogram's bin T2 and, inside it, a direct ranking (or radix passes when
+// crowded) give the exact cut; the bitmap then yields the row in ascending
+// index order.
+constexpr int kRowThreads = 1024;
+constexpr int kRowBitmapWords = kRowMaxEntries / 32;
+
+__global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
+  __shared__ uint32_t h1[4096];
+  __shared__ uint32_t h2[kH2Bins];
+  __shared__ uint32_t bitmap[kRowBitmapWords];
+  __shared__ uint64_t bl[kBoundaryLds];
+  __shared__ uint32_t sm[kRowThreads / 64];
+  __shared__ int s_T;
+  __shared__ uint32_t s_above, s_cnt, s_nc, s_nbl;
+  __shared__ uint64_t s_vstar;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int b = r / a.Tq;
+  const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - a.csa_off[b]);
+  const uint32_t k = (uint32_t)a.k;
+  int32_t* out = a.idx + (int64_t)r * a.k;
+  if (nv <= a.k) {
+    for (int t = tid; t < a.k; t += kRowThreads) out[t] = t < nv ? t : -1;
+    return;
+  }
+  const float* S = a.scores + (int64_t)r * a.max_entries;
+  uint64_t* cand = a.cand + (int64_t)r * a.max_entries;
+  for (int i = tid; i < kHistBins; i += kRowThreads) h1[i] = 0;
+  for (int i = tid; i < kH2Bins; i += kRowThreads) h2[i] = 0;
+  for (int i = tid; i < kRowBitmapWords; i += kRowThreads) bitmap[i] = 0;
+  if (tid == 0) { s_nc = 0; s_nbl = 0; s_vstar = ~0ull; }
+  __syncthreads();
+  for (int64_t e = tid; e < nv; e += kRowThreads) atomicAdd(&h1[score_key(S[e]) >> 21], 1u);
+  __syncthreads();
+  find_threshold(h1, kHistBins, k, sm, &s_T, &s_above, &s_cnt);
+  const uint32_t T = (uint32_t)s_T;
+  const uint32_t need = k - s_above;
+  for (int64_t e = tid; e < nv; e += kRowThreads) {
+    const uint32_t key = score_key(S[e]);
+    const uint32_t bin = key >> 21;
+    if (bin > T) {
+      atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+    } else if (bin == T) {
+      cand[atomicAdd(&s_nc, 1u)] = ((uint64_t)(key & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
+      atomicAdd(&h2[(key >> 10) & (uint32_t)(kH2Bins - 1)], 1u);
+    }
+  }
+  __syncthreads();  // the candidate list (global, this block's) and h2 are complete
+  const uint32_t nc = s_nc;
+  find_threshold(h2, kH2Bins, need, sm, &s_T, &s_above, &s_cnt);
+  const uint32_t T2 = (uint32_t)s_T;
+  const uint32_t need2 = need - s_above, cnt2 = s_cnt;
+  uint64_t vstar = (uint64_t)T2 << 34;
+  if (cnt2 != need2 && cnt2 <= (uint32_t)kBoundaryLds) {
+    for (uint32_t i = tid; i < nc; i += kRowThreads) {
+      const uint64_t v = cand[i];
+      if ((uint32_t)(v >> 34) == T2) {
+        const uint32_t slot = atomicAdd(&s_nbl, 1u);
+        if (slot < (uint32_t)kBoundaryLds) bl[slot] = v;
+      }
+    }
+    __syncthreads();
+    const uint32_t nb = min(s_nbl, (uint32_t)kBoundaryLds);
+    for (uint32_t i = tid; i < nb; i += kRowThreads) {
+      const uint64_t v = bl[i];
+      uint32_t gt = 0;
+      for (uint32_t j = 0; j < nb; ++j) gt += bl[j] > v ? 1u : 0u;
+      if (gt == need2 - 1) s_vstar = v;
+    }
+    __syncthreads();
+    vstar = s_vstar;
+  } else if (cnt2 != need2) {
+    // a crowded bin (ties): radix passes over the low 34 bits inside it
+    uint64_t prefix = vstar, mask = (uint64_t)(kH2Bins - 1) << 34;
+    uint32_t nd = need2;
+    const int shifts[3] = {23, 12, 0};
+    const int widths[3] = {11, 11, 12};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sft = shifts[pass], nbins = 1 << widths[pass];
+      for (int i = tid; i < nbins; i += kRowThreads) h1[i] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < nc; i += kRowThreads) {
+        const uint64_t v = cand[i];
+        if ((v & mask) == prefix) atomicAdd(&h1[(uint32_t)(v >> sft) & (uint32_t)(nbins - 1)], 1u);
+      }
+      __syncthreads();
+      find_threshold(h1, nbins, nd, sm, &s_T, &s_above, &s_cnt);
+      prefix |= (uint64_t)(uint32_t)s_T << sft;
+      mask |= (uint64_t)(nbins - 1) << sft;
+      nd -= s_above;
+      const bool done = s_cnt == nd;
+      __syncthreads();
+      if (done) break;
+    }
+    vstar = prefix;
+  }
+  for (uint32_t i = tid; i < nc; i += kRowThreads) {
+    const uint64_t v = cand[i];
+    if (v >= vstar) {
+      const uint32_t e = 0xFFFFFFu - (uint32_t)(v & 0xFFFFFFu);
+      atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+  // ascending order: the chosen entries before each thread's words, then its bits
+  constexpr int WPT = kRowBitmapWords / kRowThreads;
+  uint32_t wv[WPT], c = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    wv[i] = bitmap[tid * WPT + i];
+    c += __popc(wv[i]);
+  }
+  uint32_t tot;
+  uint32_t o = block_excl_scan(c, &tot, sm);
+  if (tot != k) {  // inconsistent (cannot happen with a consistent histogram)
+    for (int t = tid; t < a.k; t += kRowThreads) out[t] = -1;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t x = wv[i];
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      x &= x - 1;
+      out[o++] = (int32_t)((tid * WPT + i) * 32 + bit);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ host
@@ -443,6 +677,7 @@ static IndexParams make_params(const void* p, const float* omega, const void* ik
   a.idx = idx;
   a.chunk = (int)score_chunk(rows, maxN);
   a.nstripe = hist_stripes(rows, maxN);
+  a.no_hist = rows_mode(Tq, maxN) ? 1 : 0;
   return a;
 }
 
@@ -453,6 +688,25 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
   const int rows = B * Tq;
   dim3 g1((unsigned)((maxN + a.chunk - 1) / a.chunk), (unsigned)rows);
   const bool mfma = dtype == LCA_BF16 && HI <= 16 && (dI % 32) == 0 && dI <= 256;
+  if (mfma && a.no_hist && (HI == 1 || HI == 2 || HI == 4)) {
+    // many rows per sequence: the row-tiled kernel
+    const int gps = (Tq + kRowsPerBlock - 1) / kRowsPerBlock;
+    dim3 g((unsigned)((maxN + 4 * kRowsEntriesPerWave - 1) / (4 * kRowsEntriesPerWave)), (unsigned)(B * gps));
+#define LCA_ROWS(KSv)                                                                                      \
+  switch (HI) {                                                                                            \
+    case 1: hipLaunchKernelGGL((index_score_rows<KSv, 1>), g, dim3(256), 0, stream, a); break;           \
+    case 2: hipLaunchKernelGGL((index_score_rows<KSv, 2>), g, dim3(256), 0, stream, a); break;           \
+    default: hipLaunchKernelGGL((index_score_rows<KSv, 4>), g, dim3(256), 0, stream, a); break;          \
+  }
+    switch (dI / 32) {
+      case 1: LCA_ROWS(1) break;
+      case 2: LCA_ROWS(2) break;
+      case 4: LCA_ROWS(4) break;
+      default: LCA_ROWS(8) break;
+    }
+#undef LCA_ROWS
+    return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+  }
   if (mfma) {
     switch (dI / 32) {
       case 1: hipLaunchKernelGGL((index_score_mfma<1>), g1, dim3(kIdxThreads), 0, stream, a); break;
@@ -559,9 +813,16 @@ int launch_topk_finalize(const int64_t* csa_off, const int32_t* q_pos, int B, in
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 
+bool topk_rows_mode(int Tq, int64_t maxN) { return rows_mode(Tq, maxN); }
+
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream) {
   IndexParams a = make_params(nullptr, nullptr, nullptr, csa_off, q_pos, B, Tq, 1, 8, k, m, w, maxN, idx, scores, ws);
+  if (a.no_hist) {
+    // many rows per sequence: one block per row
+    hipLaunchKernelGGL(topk_rows, dim3((unsigned)(B * Tq)), dim3(kRowThreads), 0, stream, a);
+    return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+  }
   const int nblk = (int)((maxN + kSelChunk - 1) / kSelChunk);
   hipLaunchKernelGGL(topk_filter, dim3((unsigned)nblk, (unsigned)(B * Tq)), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(topk_finalize, dim3((unsigned)(B * Tq)), dim3(kFinThreads), 0, stream, a);

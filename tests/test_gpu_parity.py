@@ -588,3 +588,37 @@ def test_topk_source_many_rows():
     layer.compress(caches, raw, raw["tok_off"])
     q_pos = raw["q_pos"].reshape(-1).contiguous()
     _topk_source_vs_separate(cfg, raw, caches, q_pos, int(q_pos.max().item()) + 1, splits=(2, 3, 1))
+
+
+def test_many_rows_topk_equals_single_rows():
+    """40 query rows of one sequence (the row-tiled scores and the one-block-
+    per-row selection) against the same rows scored and selected one call per
+    row: identical scores and identical indices, including rows at or below k
+    and rows with planted ties."""
+    from long_context_attention_20_amd import ops
+    cfg = li.small("rows", 115, (30000,), tq=40, H=16, D=64, HI=4, dI=64, k=512, plant=16)
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    q_pos = d["q_pos"].clone()
+    # the first rows see fewer entries than k
+    q_pos[:3] = torch.tensor([40, 2000, 2055], dtype=torch.int32, device="cuda")
+    rows = q_pos.numel()
+    max_csa = ocmp.n_entries(int(q_pos.max().item()) + 1, cfg.m, cfg.w)
+    ws = torch.zeros(ops.csa_index_topk_workspace(rows, max_csa, cfg.k), dtype=torch.uint8, device="cuda")
+    scores = torch.full((rows, max_csa), float("nan"), dtype=torch.float32, device="cuda")
+    idx = ops.csa_index_topk(d["p"], d["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws,
+                             scores=scores)
+    ws1 = torch.zeros(ops.csa_index_topk_workspace(1, max_csa, cfg.k), dtype=torch.uint8, device="cuda")
+    sc1 = torch.full((1, max_csa), float("nan"), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for r in range(rows):
+        nv = ocmp.n_visible(int(q_pos[r].item()), cfg.m, cfg.w)
+        i1 = ops.csa_index_topk(d["p"][r:r + 1].contiguous(), d["omega"][r:r + 1].contiguous(), caches.ikey,
+                                caches.csa_off, q_pos[r:r + 1].contiguous(), cfg.k, cfg.m, cfg.w, max_csa, ws1,
+                                scores=sc1)
+        torch.cuda.synchronize()
+        assert torch.equal(scores[r, :nv], sc1[0, :nv]), f"row {r}: scores differ"
+        assert torch.equal(idx[r], i1[0]), f"row {r}: selection differs"
