@@ -554,6 +554,236 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
+// ============================================================ many query rows
+// Dense attention for calls with many query rows per sequence (prefill
+// chunks): a block holds 128 (query, head) rows -- 8 waves of 16 heads of one
+// query each -- and streams the source's keys through LDS once for all of
+// them, in 32-key tiles (double-buffered, one barrier per tile; the next
+// tile's loads are in flight while the current one is computed).  A wave
+// keeps its 16 normalised query rows over all of D in registers as the B
+// operand of S^T = K . Qhat^T, runs the online softmax on the S^T
+// accumulator, and accumulates O^T = V^T . P^T for all of D (V^T through
+// ds_read_b64_tr_b16, the P^T operand the rounded accumulator itself, as in
+// attn_mfma): no logits are exchanged between waves.  Each wave masks the
+// keys its own query does not see.  Splits cut a row tile's key range into
+// n_split parts, one partial each.
+constexpr int kRowsThreads = 512;
+constexpr int kRowsTile = 32;
+constexpr int kRowsBlockRows = 128;  // (query, head) rows per block
+
+template <int D>
+__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_rows_mfma(AttnParams a) {
+  constexpr int KS = D / 32;      // k-steps of S over D
+  constexpr int DB = D / 16;      // 16-dim blocks of O
+  constexpr int PITCH = D + 8;    // bf16 elements per LDS row
+  constexpr int VPR = D / 8;      // 16-byte vectors per key row
+  constexpr int LOADS = kRowsTile * VPR / kRowsThreads;
+  static_assert(LOADS >= 1 && LOADS * kRowsThreads == kRowsTile * VPR, "a tile must split evenly over the block");
+  constexpr int TILE_ELEMS = kRowsTile * PITCH;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE_ELEMS];
+  __shared__ int64_t s_n[kRowsThreads / 64];
+  const AttnSrc& S = a.s[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  // block -> (sequence b, row tile, split); a sequence's rows are (t, h) -> t*H + h
+  const int64_t rows_seq = (int64_t)a.Tq * a.H;
+  const int64_t tiles_seq = (rows_seq + kRowsBlockRows - 1) / kRowsBlockRows;
+  const int split = (int)(blockIdx.x % S.n_split);
+  const int64_t rest = blockIdx.x / S.n_split;
+  const int b = (int)(rest / tiles_seq);
+  const int64_t rr = (rest % tiles_seq) * kRowsBlockRows + wave * 16;  // this wave's first row
+  const bool wave_on = rr < rows_seq;  // uniform per wave (H is a multiple of 16)
+  const int t = wave_on ? (int)(rr / a.H) : 0;
+  const int h0 = (int)(rr % a.H);
+  const int r = b * a.Tq + t;
+  const int64_t first = S.off[b];
+  const int64_t nseq = S.off[b + 1] - first;
+  int64_t n_w = 0;  // keys this wave's query sees
+  if (wave_on) {
+    const int64_t nh = n_windows((int64_t)a.q_pos[r] + 1, S.m2, S.w2);
+    n_w = nh < nseq ? nh : nseq;
+  }
+  if (lane == 0) s_n[wave] = n_w;
+
+  // the query rows, RMS-normalised over D and rounded to bf16: lane (c16, g)
+  // holds head h0 + c16, dims 32*ks + 8*g .. +7
+  uint4 qraw[KS];
+  if (wave_on) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h0 + c16) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
+  }
+  __syncthreads();  // s_n
+  int64_t nmax = 0;
+#pragma unroll
+  for (int w = 0; w < kRowsThreads / 64; ++w) nmax = s_n[w] > nmax ? s_n[w] : nmax;
+  const int64_t ntiles = (nmax + kRowsTile - 1) / kRowsTile;
+  const int64_t tps = (ntiles + S.n_split - 1) / S.n_split;
+  const int64_t tb = (int64_t)split * tps;
+  const int64_t te = min(ntiles, tb + tps);
+
+  bf16x8_t qb[KS];
+  {
+    float ss = 0.f;
+    if (wave_on) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float f[8];
+        BF16::unpack(qraw[ks], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+      }
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float f[8];
+      BF16::unpack(qraw[ks], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= inv;
+      qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
+    }
+  }
+
+  // tile staging: keys at or beyond the block's visible range load key 0 (its
+  // logits are masked, so it weighs nothing).  D = 512: one wave instruction
+  // moves one 1 KiB key row straight into LDS (wave w loads rows 4w .. 4w+3);
+  // smaller D go through registers.
+  const uint16_t* kvp = reinterpret_cast<const uint16_t*>(S.kv);
+  constexpr bool kDirect = D == 512;
+  static_assert(!kDirect || kRowsTile * VPR == (kRowsThreads / 64) * 4 * 64, "one key row per wave instruction");
+  uint4 stage[kDirect ? 1 : LOADS];
+  auto load_tile = [&](int64_t tt, uint16_t* tile) {
+    if (tt >= te) return;
+    if constexpr (kDirect) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wave * 4 + v;
+        const int64_t key = tt * kRowsTile + row;
+        const uint16_t* src = kvp + (first + (key < nmax ? key : 0)) * D + lane * 8;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + row * PITCH), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < LOADS; ++v) {
+        const int id = threadIdx.x + kRowsThreads * v;
+        const int row = id / VPR, vec = id % VPR;
+        const int64_t key = tt * kRowsTile + row;
+        stage[v] = *reinterpret_cast<const uint4*>(kvp + (first + (key < nmax ? key : 0)) * D + vec * 8);
+      }
+    }
+  };
+  auto store_tile = [&](uint16_t* tile) {
+    if constexpr (!kDirect) {
+#pragma unroll
+      for (int v = 0; v < LOADS; ++v) {
+        const int id = threadIdx.x + kRowsThreads * v;
+        const int row = id / VPR, vec = id % VPR;
+        *reinterpret_cast<uint4*>(&tile[row * PITCH + vec * 8]) = stage[v];
+      }
+    }
+  };
+
+  f32x4 O[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale * kLog2e;
+  load_tile(tb, tiles[0]);
+  for (int64_t tt = tb; tt < te; ++tt) {
+    uint16_t* tile = tiles[(tt - tb) & 1];
+    store_tile(tile);
+    if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the tile have landed
+    // tile in LDS; every wave has left the previous tile, whose buffer the
+    // next loads overwrite
+    __syncthreads();
+    load_tile(tt + 1, tiles[(tt + 1 - tb) & 1]);
+    const int64_t k0 = tt * kRowsTile;
+    if (wave_on && k0 < n_w) {  // uniform per wave
+      // ---- S^T for keys k0 + 0..15 (s0) and k0 + 16..31 (s1)
+      f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+      const uint16_t* krow0 = &tile[c16 * PITCH + g * 8];
+      const uint16_t* krow1 = krow0 + 16 * PITCH;
+#pragma unroll
+      for (int ks = 0; ks < KS; ks += 2) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(krow0 + ks * 32);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(krow1 + ks * 32);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(krow0 + (ks + 1) * 32);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(krow1 + (ks + 1) * 32);
+        s0a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), qb[ks], s0a, 0, 0, 0);
+        s1a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), qb[ks], s1a, 0, 0, 0);
+        s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b0), qb[ks + 1], s0b, 0, 0, 0);
+        s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b1), qb[ks + 1], s1b, 0, 0, 0);
+      }
+      const f32x4 p0 = s0a + s0b, p1 = s1a + s1b;
+      // ---- online softmax: lane (c16 = head, g) holds keys 4g+i and 16+4g+i
+      float lg[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lg[i] = k0 + 4 * g + i < n_w ? p0[i] * sl2 : -INFINITY;
+        lg[4 + i] = k0 + 16 + 4 * g + i < n_w ? p1[i] * sl2 : -INFINITY;
+      }
+      float tmax = lg[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, lg[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // (k0 < n_w: the tile's first key is visible, so tmax is finite)
+      const bool move = tmax > m_run + 8.0f;
+      const float alpha = move ? exp2f(m_run - tmax) : 1.0f;
+      const float m_ref = move ? tmax : m_run;
+      float pr[8], psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pr[i] = exp2f(lg[i] - m_ref);
+        psum += pr[i];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_ref;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) O[db] = O[db] * alpha;
+      }
+      uint4 pb;
+      pb.x = pack_bf16x2(pr[0], pr[1]);
+      pb.y = pack_bf16x2(pr[2], pr[3]);
+      pb.z = pack_bf16x2(pr[4], pr[5]);
+      pb.w = pack_bf16x2(pr[6], pr[7]);
+      const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, pb);
+      // ---- O^T += V^T . P^T: lane c16 of group g reads rows 4g + c16/4 (and
+      // 16 + ...) at columns 16*db + 4*(c16%4); the transpose read returns
+      // dim 16*db + c16 of keys 4g..4g+3 (and 16+4g..)
+      const uint16_t* trow0 = &tile[(4 * g + (c16 >> 2)) * PITCH + 4 * (c16 & 3)];
+      const uint16_t* trow1 = trow0 + 16 * PITCH;
+#pragma unroll
+      for (int db = 0; db < DB; db += 2) {
+        const s4_t v00 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow0 + db * 16));
+        const s4_t v01 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow1 + db * 16));
+        const s4_t v10 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow0 + (db + 1) * 16));
+        const s4_t v11 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow1 + (db + 1) * 16));
+        O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v00, v01)), pt, O[db],
+                                                        0, 0, 0);
+        O[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v10, v11)), pt,
+                                                            O[db + 1], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: lane (c16, g) holds dims 16*db + 4g .. +3 of head h0 + c16
+  if (!wave_on) return;
+  float lsum = l_run + __shfl_xor(l_run, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float w = lsum > 0.f ? 1.0f / lsum : 0.f;
+  const int64_t orow = ((int64_t)split * a.rows + r) * a.H + h0 + c16;
+  float* op = S.o_part + orow * D + 4 * g;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    *reinterpret_cast<float4*>(op + db * 16) = make_float4(O[db][0] * w, O[db][1] * w, O[db][2] * w, O[db][3] * w);
+  if (g == 0) S.lse[orow] = lsum > 0.f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
 // ============================================================ generic path
 // One wavefront per (query row, head, split); a lane owns D/64 dims.  Used for
 // fp32 and for bf16 head counts that are not a multiple of 16.
@@ -862,12 +1092,63 @@ static int64_t resident_blocks(int D) {
   return cache[dev][di];
 }
 
+static int launch_attention_sources(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos,
+                                    int B, int Tq, int H, int D, float scale, float eps, int dtype,
+                                    hipStream_t stream);
+
+// Dense sources over many query rows per sequence take the row-tiled kernel,
+// one launch each; the other sources share one launch as before.
+static bool rows_dense(const lca_attn_source& in, int Tq, int H, int D, int dtype) {
+  return in.kind == SRC_DENSE && dtype == LCA_BF16 && H % 16 == 0 && (D == 128 || D == 256 || D == 512) &&
+         Tq >= 2 && (int64_t)Tq * H >= 2 * kRowsBlockRows;
+}
+
 int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
                      int H, int D, float scale, float eps, int dtype, hipStream_t stream) {
   if (n_src < 1 || n_src > kMaxSrc) {
     set_error("attention: %d key sources, 1 to %d supported", n_src, kMaxSrc);
     return LCA_ERR_UNSUPPORTED;
   }
+  lca_attn_source rest[kMaxSrc];
+  int n_rest = 0, n_rows = 0;
+  const int64_t tiles_seq = ((int64_t)Tq * H + kRowsBlockRows - 1) / kRowsBlockRows;
+  for (int i = 0; i < n_src; ++i) {
+    if (rows_dense(srcs[i], Tq, H, D, dtype)) {
+      ++n_rows;
+      if ((int64_t)B * tiles_seq * srcs[i].n_split > 0x7FFFFFFF) {
+        set_error("attention: %lld blocks exceed the grid limit", (long long)B * tiles_seq * srcs[i].n_split);
+        return LCA_ERR_UNSUPPORTED;
+      }
+    } else {
+      rest[n_rest++] = srcs[i];
+    }
+  }
+  if (n_rest > 0) {
+    const int rc = launch_attention_sources(rest, n_rest, q, q_pos, B, Tq, H, D, scale, eps, dtype, stream);
+    if (rc != LCA_OK || n_rows == 0) return rc;
+  }
+  for (int i = 0; i < n_src; ++i) {
+    if (!rows_dense(srcs[i], Tq, H, D, dtype)) continue;
+    const lca_attn_source& in = srcs[i];
+    AttnParams a{};
+    a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
+    a.scale = scale; a.eps = eps; a.n_src = 1;
+    AttnSrc& d = a.s[0];
+    d.kv = in.kv; d.off = in.off; d.kind = in.kind; d.m2 = in.m2; d.w2 = in.w2; d.n_split = in.n_split;
+    d.o_part = in.o_part; d.lse = in.lse;
+    dim3 grid((unsigned)(B * tiles_seq * in.n_split));
+    switch (D) {
+      case 128: hipLaunchKernelGGL((attn_rows_mfma<128>), grid, dim3(kRowsThreads), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL((attn_rows_mfma<256>), grid, dim3(kRowsThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((attn_rows_mfma<512>), grid, dim3(kRowsThreads), 0, stream, a); break;
+    }
+  }
+  return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+}
+
+static int launch_attention_sources(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos,
+                                    int B, int Tq, int H, int D, float scale, float eps, int dtype,
+                                    hipStream_t stream) {
   AttnParams a{};
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;

@@ -148,6 +148,10 @@ class HybridAttention:
         select, the sparse blocks also run the top-k selection (about as long
         as four tiles of attention) and take four tiles fewer."""
         hg = (self.H + 31) // 32
+        if rows * hg >= 256:
+            # the rows alone give the device a wave of blocks (and the dense
+            # branch then runs row-tiled): one partial per source
+            return (1, 1, 1)
         tiles = [max(1, (n + 31) // 32) for n in (n_csa, n_hca, n_win)]
         budget = max(3, 256 // max(1, rows * hg))
         for per in range(2, 34, 2):

@@ -622,3 +622,38 @@ def test_many_rows_topk_equals_single_rows():
         torch.cuda.synchronize()
         assert torch.equal(scores[r, :nv], sc1[0, :nv]), f"row {r}: scores differ"
         assert torch.equal(idx[r], i1[0]), f"row {r}: selection differs"
+
+
+def test_rows_dense_attention_equals_single_rows():
+    """The dense (HCA) branch over 40 query rows of one sequence (row-tiled,
+    128 (query, head) rows per block) against the same rows one call each
+    (one query row per launch): the same (o, lse) per row and head within
+    rounding, with and without key splits; rows whose query sees no entry
+    give o = 0 and lse = -inf."""
+    from long_context_attention_20_amd import ops
+    cfg = li.small("rows_dense", 116, (9000,), tq=40, H=64, D=512, HI=4, dI=64, k=256)
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    q_pos = d["q_pos"].clone()
+    q_pos[:3] = torch.tensor([5, 127, 300], dtype=torch.int32, device="cuda")  # 0, 1 and 2 visible entries
+    rows = q_pos.numel()
+    max_hca = ocmp.n_entries(int(q_pos.max().item()) + 1, cfg.m2, cfg.w2)
+    for ns in (1, 3):
+        o_all, l_all = ops.hca_attn(d["q"], caches.kv_hca, caches.hca_off, q_pos, cfg.m2, cfg.w2, max_hca, cfg.scale,
+                                    cfg.eps, ns)
+        torch.cuda.synchronize()
+        for r in range(rows):
+            o1, l1 = ops.hca_attn(d["q"][r:r + 1].contiguous(), caches.kv_hca, caches.hca_off, q_pos[r:r + 1].contiguous(),
+                                  cfg.m2, cfg.w2, max_hca, cfg.scale, cfg.eps, 1)
+            torch.cuda.synchronize()
+            a, la = merge_splits(o_all[:, r], l_all[:, r])
+            bb, lb = merge_splits(o1[:, 0], l1[:, 0])
+            nvis = ocmp.n_visible(int(q_pos[r].item()), cfg.m2, cfg.w2)
+            if nvis == 0:
+                assert np.all(np.isneginf(la)) and np.all(a == 0), f"row {r}: no visible entry"
+                continue
+            assert_close(a, bb, cfg.dtype, f"n_split {ns} row {r}")
+            assert np.max(np.abs(la - lb)) <= 1e-3, f"n_split {ns} row {r}: lse"
