@@ -555,56 +555,87 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 }
 
 // ============================================================ many query rows
-// Dense attention for calls with many query rows per sequence (prefill
-// chunks): a block holds 128 (query, head) rows -- 8 waves of 16 heads of one
-// query each -- and streams the source's keys through LDS once for all of
-// them, in 32-key tiles (double-buffered, one barrier per tile; the next
-// tile's loads are in flight while the current one is computed).  A wave
-// keeps its 16 normalised query rows over all of D in registers as the B
-// operand of S^T = K . Qhat^T, runs the online softmax on the S^T
-// accumulator, and accumulates O^T = V^T . P^T for all of D (V^T through
-// ds_read_b64_tr_b16, the P^T operand the rounded accumulator itself, as in
-// attn_mfma): no logits are exchanged between waves.  Each wave masks the
-// keys its own query does not see.  Splits cut a row tile's key range into
-// n_split parts, one partial each.
+// Attention for calls with many query rows per sequence (prefill chunks),
+// D = 512, bf16: a block holds 128 (query, head) rows -- 8 waves of 16 heads
+// of one query each, 128 / H queries -- and streams one source's keys through
+// LDS in 32-key tiles (double-buffered, one barrier per tile, the next tile's
+// key rows moved straight from global memory into LDS while the current one
+// is computed).  A wave keeps its 16 normalised query rows over all of D in
+// registers as the B operand of S^T = K . Qhat^T, runs the online softmax on
+// the S^T accumulator and accumulates O^T = V^T . P^T for all of D (V^T
+// through ds_read_b64_tr_b16, the P^T operand the rounded accumulator itself,
+// as in attn_mfma), so no logits are exchanged between waves.  The block's
+// queries share the tiles of a dense source (the union of what they see) and
+// of a window source (the union of their windows, each row RMS-normalised in
+// LDS by the wave that loaded it); a gathered source gives every query its
+// own stream of tiles (two streams at most: H = 64 or 128).  Each wave masks
+// the keys its own query does not see.  A source's splits cut the block's key
+// range into n_split parts, one partial each.
 constexpr int kRowsThreads = 512;
 constexpr int kRowsTile = 32;
 constexpr int kRowsBlockRows = 128;  // (query, head) rows per block
+constexpr int kRowsStreams = 2;      // gathered streams (queries) per block at most
+constexpr int kRowsIdx = 1024;       // gathered slots per stream and split
 
-template <int D>
 __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_rows_mfma(AttnParams a) {
+  constexpr int D = 512;
   constexpr int KS = D / 32;      // k-steps of S over D
   constexpr int DB = D / 16;      // 16-dim blocks of O
   constexpr int PITCH = D + 8;    // bf16 elements per LDS row
-  constexpr int VPR = D / 8;      // 16-byte vectors per key row
-  constexpr int LOADS = kRowsTile * VPR / kRowsThreads;
-  static_assert(LOADS >= 1 && LOADS * kRowsThreads == kRowsTile * VPR, "a tile must split evenly over the block");
   constexpr int TILE_ELEMS = kRowsTile * PITCH;
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE_ELEMS];
-  __shared__ int64_t s_n[kRowsThreads / 64];
-  const AttnSrc& S = a.s[0];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[kRowsStreams][2][TILE_ELEMS];
+  __shared__ int32_t sidx[kRowsStreams][kRowsIdx];
+  __shared__ int64_t s_lo[kRowsThreads / 64], s_hi[kRowsThreads / 64];
+  const int lane = threadIdx.x & 63;
+  // the wave index in a scalar register: everything derived from it (rows,
+  // key ranges, addresses) stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
-  // block -> (sequence b, row tile, split); a sequence's rows are (t, h) -> t*H + h
+  // block -> (sequence b, row tile, source split); a sequence's rows are (t, h) -> t*H + h
   const int64_t rows_seq = (int64_t)a.Tq * a.H;
   const int64_t tiles_seq = (rows_seq + kRowsBlockRows - 1) / kRowsBlockRows;
-  const int split = (int)(blockIdx.x % S.n_split);
-  const int64_t rest = blockIdx.x / S.n_split;
+  const int bx = (int)(blockIdx.x % a.n_x);
+  const int64_t rest = blockIdx.x / a.n_x;
   const int b = (int)(rest / tiles_seq);
-  const int64_t rr = (rest % tiles_seq) * kRowsBlockRows + wave * 16;  // this wave's first row
-  const bool wave_on = rr < rows_seq;  // uniform per wave (H is a multiple of 16)
+  const int64_t rt = rest % tiles_seq;
+  int split;
+  const int si = attn_source(a, bx, &split);
+  const AttnSrc& S = a.s[si];
+  const int kind = S.kind;
+  const int64_t rr = rt * kRowsBlockRows + wave * 16;  // this wave's first row
+  const bool wave_on = rr < rows_seq;                  // uniform per wave (H divides 128)
   const int t = wave_on ? (int)(rr / a.H) : 0;
   const int h0 = (int)(rr % a.H);
   const int r = b * a.Tq + t;
+  const int nq = kRowsBlockRows / a.H;                 // queries per block
+  const int streams = kind == SRC_GATHER ? nq : 1;
+  const int stream = kind == SRC_GATHER ? (wave * 16) / a.H : 0;
+  const int wps = (kRowsThreads / 64) / streams;       // waves per stream
+  const int wis = wave % wps;                          // this wave's place in its stream
   const int64_t first = S.off[b];
   const int64_t nseq = S.off[b + 1] - first;
-  int64_t n_w = 0;  // keys this wave's query sees
+  // this wave's visible key range [lo, hi) in the source's key coordinates:
+  // entries (dense), token positions (window), slots (gathered)
+  int64_t lo = 0, hi = 0;
   if (wave_on) {
-    const int64_t nh = n_windows((int64_t)a.q_pos[r] + 1, S.m2, S.w2);
-    n_w = nh < nseq ? nh : nseq;
+    if (kind == SRC_DENSE) {
+      const int64_t nh = n_windows((int64_t)a.q_pos[r] + 1, S.m2, S.w2);
+      hi = nh < nseq ? nh : nseq;
+    } else if (kind == SRC_WINDOW) {
+      const int64_t i = a.q_pos[r];
+      lo = i - S.W + 1 > 0 ? i - S.W + 1 : 0;
+      hi = (i < nseq - 1 ? i : nseq - 1) + 1;
+      if (hi < lo) hi = lo;
+    } else {
+      hi = nseq > 0 ? S.k : 0;
+    }
   }
-  if (lane == 0) s_n[wave] = n_w;
-
+  if (lane == 0) {
+    // an empty range adds nothing to the block's union (a window past the
+    // sequence's last token has hi == lo > nseq)
+    s_lo[wave] = wave_on && hi > lo ? lo : INT64_MAX;
+    s_hi[wave] = wave_on && hi > lo ? hi : 0;
+  }
   // the query rows, RMS-normalised over D and rounded to bf16: lane (c16, g)
   // holds head h0 + c16, dims 32*ks + 8*g .. +7
   uint4 qraw[KS];
@@ -613,14 +644,35 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
   }
-  __syncthreads();  // s_n
-  int64_t nmax = 0;
+  __syncthreads();  // s_lo, s_hi
+  // the block's key range (per stream for gathered keys: every stream has k slots)
+  int64_t blo = INT64_MAX, bhi = 0;
 #pragma unroll
-  for (int w = 0; w < kRowsThreads / 64; ++w) nmax = s_n[w] > nmax ? s_n[w] : nmax;
-  const int64_t ntiles = (nmax + kRowsTile - 1) / kRowsTile;
+  for (int w = 0; w < kRowsThreads / 64; ++w) {
+    blo = s_lo[w] < blo ? s_lo[w] : blo;
+    bhi = s_hi[w] > bhi ? s_hi[w] : bhi;
+  }
+  if (blo > bhi) blo = bhi;  // nothing visible
+  const int64_t ntiles = (bhi - blo + kRowsTile - 1) / kRowsTile;
   const int64_t tps = (ntiles + S.n_split - 1) / S.n_split;
   const int64_t tb = (int64_t)split * tps;
   const int64_t te = min(ntiles, tb + tps);
+  const int64_t kbase = blo + tb * kRowsTile;  // key coordinate of the split's first tile row
+  if (kind == SRC_GATHER && te > tb) {
+    // every stream's slots of this split, -1 for unused or out-of-range entries
+    const int64_t cnt = min((te - tb) * kRowsTile, bhi - kbase);
+    const int q0 = (int)((rt * kRowsBlockRows) / a.H);
+    for (int i = threadIdx.x; i < streams * kRowsIdx; i += kRowsThreads) {
+      const int st = i / kRowsIdx, j = i % kRowsIdx;
+      const int tq = q0 + st;
+      int32_t e = -1;
+      if (j < cnt && tq < a.Tq) {
+        e = S.idx[(int64_t)(b * a.Tq + tq) * S.k + kbase + j];
+        if (e < 0 || e >= nseq) e = -1;
+      }
+      sidx[st][j] = e;
+    }
+  }
 
   bf16x8_t qb[KS];
   {
@@ -646,43 +698,48 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
+  __syncthreads();  // sidx
 
-  // tile staging: keys at or beyond the block's visible range load key 0 (its
-  // logits are masked, so it weighs nothing).  D = 512: one wave instruction
-  // moves one 1 KiB key row straight into LDS (wave w loads rows 4w .. 4w+3);
-  // smaller D go through registers.
+  // tile staging: one wave instruction moves one 1 KiB key row straight into
+  // LDS; wave w loads rows wis*rpw .. of its stream's tile.  Rows without a
+  // visible key load a clamped valid row (their logits are masked, so they
+  // weigh nothing).
   const uint16_t* kvp = reinterpret_cast<const uint16_t*>(S.kv);
-  constexpr bool kDirect = D == 512;
-  static_assert(!kDirect || kRowsTile * VPR == (kRowsThreads / 64) * 4 * 64, "one key row per wave instruction");
-  uint4 stage[kDirect ? 1 : LOADS];
-  auto load_tile = [&](int64_t tt, uint16_t* tile) {
+  const int rpw = kRowsTile / wps;  // rows per wave: 4 (one stream) or 8 (two)
+  auto load_tile = [&](int64_t tt) {
     if (tt >= te) return;
-    if constexpr (kDirect) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = wave * 4 + v;
-        const int64_t key = tt * kRowsTile + row;
-        const uint16_t* src = kvp + (first + (key < nmax ? key : 0)) * D + lane * 8;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + row * PITCH), 16, 0, 0);
+    uint16_t* tile = tiles[stream][(tt - tb) & 1];
+    for (int v = 0; v < rpw; ++v) {  // uniform
+      const int row = wis * rpw + v;
+      const int64_t kc = blo + tt * kRowsTile + row;
+      int64_t ent;
+      if (kind == SRC_GATHER) {
+        const int32_t e = sidx[stream][kc - kbase];
+        ent = e >= 0 ? e : 0;
+      } else {
+        ent = kc < bhi ? kc : blo;
       }
-    } else {
-#pragma unroll
-      for (int v = 0; v < LOADS; ++v) {
-        const int id = threadIdx.x + kRowsThreads * v;
-        const int row = id / VPR, vec = id % VPR;
-        const int64_t key = tt * kRowsTile + row;
-        stage[v] = *reinterpret_cast<const uint4*>(kvp + (first + (key < nmax ? key : 0)) * D + vec * 8);
-      }
+      const uint16_t* src = kvp + (first + ent) * D + lane * 8;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + row * PITCH), 16, 0, 0);
     }
   };
-  auto store_tile = [&](uint16_t* tile) {
-    if constexpr (!kDirect) {
+  // window rows: RMS over D of the raw row, rounded to bf16, in place (the
+  // wave that loaded a row normalises it once its loads have landed)
+  auto norm_rows = [&](int64_t tt) {
+    uint16_t* tile = tiles[0][(tt - tb) & 1];
+    for (int v = 0; v < rpw; ++v) {
+      uint16_t* rowp = tile + (wis * rpw + v) * PITCH + lane * 8;
+      uint4 x = *reinterpret_cast<const uint4*>(rowp);
+      float f[8];
+      BF16::unpack(x, f);
+      float ss = 0.f;
 #pragma unroll
-      for (int v = 0; v < LOADS; ++v) {
-        const int id = threadIdx.x + kRowsThreads * v;
-        const int row = id / VPR, vec = id % VPR;
-        *reinterpret_cast<uint4*>(&tile[row * PITCH + vec * 8]) = stage[v];
-      }
+      for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+      ss = lane_group_sum<64>(ss);
+      const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= inv;
+      *reinterpret_cast<uint4*>(rowp) = BF16::pack(f);
     }
   };
 
@@ -691,82 +748,82 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
   for (int d = 0; d < DB; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
-  load_tile(tb, tiles[0]);
+  load_tile(tb);
   for (int64_t tt = tb; tt < te; ++tt) {
-    uint16_t* tile = tiles[(tt - tb) & 1];
-    store_tile(tile);
-    if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the tile have landed
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the tile have landed
+    if (kind == SRC_WINDOW) norm_rows(tt);
     // tile in LDS; every wave has left the previous tile, whose buffer the
     // next loads overwrite
     __syncthreads();
-    load_tile(tt + 1, tiles[(tt + 1 - tb) & 1]);
-    const int64_t k0 = tt * kRowsTile;
-    if (wave_on && k0 < n_w) {  // uniform per wave
-      // ---- S^T for keys k0 + 0..15 (s0) and k0 + 16..31 (s1)
-      f32x4 s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+    load_tile(tt + 1);
+    const uint16_t* tile = tiles[stream][(tt - tb) & 1];
+    const int64_t k0 = blo + tt * kRowsTile;  // key coordinate of the tile's first row
+    // the tile's rows this wave sees, one per lane of the low half-wave
+    const int64_t kl = k0 + lane;
+    const uint64_t vm = __ballot(lane < kRowsTile && kl >= lo && kl < hi &&
+                                 (kind != SRC_GATHER || sidx[stream][kl - kbase] >= 0));
+    if (wave_on && vm != 0) {  // uniform per wave
+      // ---- S^T for tile rows 0..15 (p0) and 16..31 (p1)
+      f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
       const uint16_t* krow0 = &tile[c16 * PITCH + g * 8];
       const uint16_t* krow1 = krow0 + 16 * PITCH;
 #pragma unroll
-      for (int ks = 0; ks < KS; ks += 2) {
+      for (int ks = 0; ks < KS; ++ks) {
         const uint4 a0 = *reinterpret_cast<const uint4*>(krow0 + ks * 32);
         const uint4 a1 = *reinterpret_cast<const uint4*>(krow1 + ks * 32);
-        const uint4 b0 = *reinterpret_cast<const uint4*>(krow0 + (ks + 1) * 32);
-        const uint4 b1 = *reinterpret_cast<const uint4*>(krow1 + (ks + 1) * 32);
-        s0a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), qb[ks], s0a, 0, 0, 0);
-        s1a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), qb[ks], s1a, 0, 0, 0);
-        s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b0), qb[ks + 1], s0b, 0, 0, 0);
-        s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b1), qb[ks + 1], s1b, 0, 0, 0);
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), qb[ks], p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), qb[ks], p1, 0, 0, 0);
       }
-      const f32x4 p0 = s0a + s0b, p1 = s1a + s1b;
-      // ---- online softmax: lane (c16 = head, g) holds keys 4g+i and 16+4g+i
+      // ---- online softmax: lane (c16 = head, g) holds tile rows 4g+i and 16+4g+i
       float lg[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lg[i] = k0 + 4 * g + i < n_w ? p0[i] * sl2 : -INFINITY;
-        lg[4 + i] = k0 + 16 + 4 * g + i < n_w ? p1[i] * sl2 : -INFINITY;
+        lg[i] = ((vm >> (4 * g + i)) & 1u) ? p0[i] * sl2 : -INFINITY;
+        lg[4 + i] = ((vm >> (16 + 4 * g + i)) & 1u) ? p1[i] * sl2 : -INFINITY;
       }
       float tmax = lg[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, lg[i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      // (k0 < n_w: the tile's first key is visible, so tmax is finite)
-      const bool move = tmax > m_run + 8.0f;
-      const float alpha = move ? exp2f(m_run - tmax) : 1.0f;
-      const float m_ref = move ? tmax : m_run;
-      float pr[8], psum = 0.f;
+      if (tmax != -INFINITY) {  // uniform: the masks do not depend on the head
+        const bool move = tmax > m_run + 8.0f;
+        const float alpha = move ? exp2f(m_run - tmax) : 1.0f;
+        const float m_ref = move ? tmax : m_run;
+        float pr[8], psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = exp2f(lg[i] - m_ref);
-        psum += pr[i];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_ref;
-      if (__ballot(alpha != 1.0f)) {
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = exp2f(lg[i] - m_ref);
+          psum += pr[i];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_ref;
+        if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) O[db] = O[db] * alpha;
-      }
-      uint4 pb;
-      pb.x = pack_bf16x2(pr[0], pr[1]);
-      pb.y = pack_bf16x2(pr[2], pr[3]);
-      pb.z = pack_bf16x2(pr[4], pr[5]);
-      pb.w = pack_bf16x2(pr[6], pr[7]);
-      const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, pb);
-      // ---- O^T += V^T . P^T: lane c16 of group g reads rows 4g + c16/4 (and
-      // 16 + ...) at columns 16*db + 4*(c16%4); the transpose read returns
-      // dim 16*db + c16 of keys 4g..4g+3 (and 16+4g..)
-      const uint16_t* trow0 = &tile[(4 * g + (c16 >> 2)) * PITCH + 4 * (c16 & 3)];
-      const uint16_t* trow1 = trow0 + 16 * PITCH;
+          for (int db = 0; db < DB; ++db) O[db] = O[db] * alpha;
+        }
+        uint4 pb;
+        pb.x = pack_bf16x2(pr[0], pr[1]);
+        pb.y = pack_bf16x2(pr[2], pr[3]);
+        pb.z = pack_bf16x2(pr[4], pr[5]);
+        pb.w = pack_bf16x2(pr[6], pr[7]);
+        const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, pb);
+        // ---- O^T += V^T . P^T: lane c16 of group g reads rows 4g + c16/4 (and
+        // 16 + ...) at columns 16*db + 4*(c16%4); the transpose read returns
+        // dim 16*db + c16 of tile rows 4g..4g+3 (and 16+4g..)
+        const uint16_t* trow0 = &tile[(4 * g + (c16 >> 2)) * PITCH + 4 * (c16 & 3)];
+        const uint16_t* trow1 = trow0 + 16 * PITCH;
 #pragma unroll
-      for (int db = 0; db < DB; db += 2) {
-        const s4_t v00 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow0 + db * 16));
-        const s4_t v01 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow1 + db * 16));
-        const s4_t v10 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow0 + (db + 1) * 16));
-        const s4_t v11 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow1 + (db + 1) * 16));
-        O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v00, v01)), pt, O[db],
-                                                        0, 0, 0);
-        O[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v10, v11)), pt,
-                                                            O[db + 1], 0, 0, 0);
+        for (int db = 0; db < DB; db += 2) {
+          const s4_t v00 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow0 + db * 16));
+          const s4_t v01 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow1 + db * 16));
+          const s4_t v10 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow0 + (db + 1) * 16));
+          const s4_t v11 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(trow1 + (db + 1) * 16));
+          O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v00, v01)), pt, O[db],
+                                                          0, 0, 0);
+          O[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v10, v11)), pt,
+                                                              O[db + 1], 0, 0, 0);
+        }
       }
     }
   }
@@ -1095,12 +1152,26 @@ static int64_t resident_blocks(int D) {
 static int launch_attention_sources(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos,
                                     int B, int Tq, int H, int D, float scale, float eps, int dtype,
                                     hipStream_t stream);
+int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
+                       int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
 
-// Dense sources over many query rows per sequence take the row-tiled kernel,
-// one launch each; the other sources share one launch as before.
-static bool rows_dense(const lca_attn_source& in, int Tq, int H, int D, int dtype) {
-  return in.kind == SRC_DENSE && dtype == LCA_BF16 && H % 16 == 0 && (D == 128 || D == 256 || D == 512) &&
-         Tq >= 2 && (int64_t)Tq * H >= 2 * kRowsBlockRows;
+// Many query rows per sequence (D = 512, bf16, 128 divisible by H and at
+// least two blocks of rows): every source takes the row-tiled kernel, in one
+// launch; a gathered source (or a top-k source, selected first) needs at most
+// two queries per block (H >= 64) and at most kRowsIdx slots per split.
+static bool rows_launch(const lca_attn_source* srcs, int n_src, int Tq, int H, int D, int dtype) {
+  if (dtype != LCA_BF16 || D != 512 || H % 16 != 0 || kRowsBlockRows % H != 0 || Tq < 2 ||
+      (int64_t)Tq * H < 2 * kRowsBlockRows)
+    return false;
+  for (int i = 0; i < n_src; ++i) {
+    const lca_attn_source& in = srcs[i];
+    if (in.kind == SRC_GATHER || in.kind == SRC_TOPK) {
+      if (kRowsBlockRows / H > kRowsStreams) return false;
+      if ((int64_t)((in.k + kRowsTile - 1) / kRowsTile + in.n_split - 1) / in.n_split * kRowsTile > kRowsIdx)
+        return false;
+    }
+  }
+  return true;
 }
 
 int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
@@ -1109,40 +1180,40 @@ int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, cons
     set_error("attention: %d key sources, 1 to %d supported", n_src, kMaxSrc);
     return LCA_ERR_UNSUPPORTED;
   }
-  lca_attn_source rest[kMaxSrc];
-  int n_rest = 0, n_rows = 0;
-  const int64_t tiles_seq = ((int64_t)Tq * H + kRowsBlockRows - 1) / kRowsBlockRows;
+  if (!rows_launch(srcs, n_src, Tq, H, D, dtype))
+    return launch_attention_sources(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype, stream);
+  AttnParams a{};
+  a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
+  a.scale = scale; a.eps = eps; a.n_src = n_src;
+  int splits = 0, topk = -1;
   for (int i = 0; i < n_src; ++i) {
-    if (rows_dense(srcs[i], Tq, H, D, dtype)) {
-      ++n_rows;
-      if ((int64_t)B * tiles_seq * srcs[i].n_split > 0x7FFFFFFF) {
-        set_error("attention: %lld blocks exceed the grid limit", (long long)B * tiles_seq * srcs[i].n_split);
-        return LCA_ERR_UNSUPPORTED;
-      }
-    } else {
-      rest[n_rest++] = srcs[i];
-    }
-  }
-  if (n_rest > 0) {
-    const int rc = launch_attention_sources(rest, n_rest, q, q_pos, B, Tq, H, D, scale, eps, dtype, stream);
-    if (rc != LCA_OK || n_rows == 0) return rc;
-  }
-  for (int i = 0; i < n_src; ++i) {
-    if (!rows_dense(srcs[i], Tq, H, D, dtype)) continue;
     const lca_attn_source& in = srcs[i];
-    AttnParams a{};
-    a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
-    a.scale = scale; a.eps = eps; a.n_src = 1;
-    AttnSrc& d = a.s[0];
-    d.kv = in.kv; d.off = in.off; d.kind = in.kind; d.m2 = in.m2; d.w2 = in.w2; d.n_split = in.n_split;
-    d.o_part = in.o_part; d.lse = in.lse;
-    dim3 grid((unsigned)(B * tiles_seq * in.n_split));
-    switch (D) {
-      case 128: hipLaunchKernelGGL((attn_rows_mfma<128>), grid, dim3(kRowsThreads), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL((attn_rows_mfma<256>), grid, dim3(kRowsThreads), 0, stream, a); break;
-      default: hipLaunchKernelGGL((attn_rows_mfma<512>), grid, dim3(kRowsThreads), 0, stream, a); break;
+    AttnSrc& d = a.s[i];
+    d.kv = in.kv; d.off = in.off; d.idx = in.idx; d.kind = in.kind; d.k = in.k; d.m2 = in.m2; d.w2 = in.w2;
+    d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
+    d.block_begin = splits;
+    splits += in.n_split;
+    if (in.kind == SRC_TOPK) {
+      // selected first (its own launches), then gathered
+      topk = i;
+      d.kind = SRC_GATHER;
+      d.idx = in.idx_out;
     }
   }
+  a.n_x = splits;
+  const int64_t tiles_seq = ((int64_t)Tq * H + kRowsBlockRows - 1) / kRowsBlockRows;
+  const int64_t nblk = (int64_t)B * tiles_seq * splits;
+  if (nblk > 0x7FFFFFFF) {
+    set_error("attention: %lld blocks exceed the grid limit", (long long)nblk);
+    return LCA_ERR_UNSUPPORTED;
+  }
+  if (topk >= 0) {
+    const lca_attn_source& in = srcs[topk];
+    const int rc = launch_topk_select(in.off, q_pos, B, Tq, in.k, in.m2, in.w2, in.max_entries, in.idx_out, in.scores,
+                                      in.ws, stream);
+    if (rc != LCA_OK) return rc;
+  }
+  hipLaunchKernelGGL(attn_rows_mfma, dim3((unsigned)nblk), dim3(kRowsThreads), 0, stream, a);
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 

@@ -657,3 +657,61 @@ def test_rows_dense_attention_equals_single_rows():
                 continue
             assert_close(a, bb, cfg.dtype, f"n_split {ns} row {r}")
             assert np.max(np.abs(la - lb)) <= 1e-3, f"n_split {ns} row {r}: lse"
+
+
+@pytest.mark.parametrize("H,k", [(64, 256), (128, 1024)])
+def test_rows_gather_window_against_oracle(H, k):
+    """The gathered and window branches over 41 query rows of each of two
+    sequences (row-tiled kernel: two queries per block at H = 64 with one key
+    stream each, one query per block at H = 128; the last block of a sequence
+    half empty at H = 64) against the oracle row by row: gathered slots
+    include -1 and repeated entries, windows are cut at the sequence start,
+    and the gathered branch runs with and without key splits."""
+    from long_context_attention_20_amd import ops
+    cfg = li.small(f"rows_gw{H}", 117, (9000, 3000), tq=41, H=H, D=512, HI=4, dI=64, k=k)
+    print(f"[rows gather/window H={H} k={k}]", flush=True)
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    qp = raw["q_pos"].reshape(-1).copy()
+    qp[:3] = [5, 127, 300]          # windows cut at the sequence start
+    q_pos = torch.from_numpy(qp).to("cuda")
+    rows = cfg.B * cfg.tq
+    co = caches.csa_off_h
+    rng = np.random.default_rng(np.random.SeedSequence([117, H, 5]))
+    idx = np.empty((rows, k), dtype=np.int32)
+    for r in range(rows):
+        b = r // cfg.tq
+        n = int(co[b + 1] - co[b])
+        idx[r] = rng.integers(0, n, size=k)
+        idx[r][rng.random(k) < 0.1] = -1
+    idx[5, :] = -1                   # a row with no gathered entry
+    idx[6, 1:] = idx[6, 0]           # one entry k times
+    idx_d = torch.from_numpy(idx).to("cuda")
+    seqs = [seq_caches(caches, b) for b in range(cfg.B)]
+    xs = [opipe.seq_slice(raw["x"], raw["tok_off"], b) for b in range(cfg.B)]
+    ow, lw = ops.swa_attn(d["q"], d["x"], d["tok_off"], q_pos, cfg.W, cfg.scale, cfg.eps)
+    gathered = {ns: ops.csa_sparse_attn(d["q"], caches.kv_csa, caches.csa_off, idx_d, cfg.scale, cfg.eps, ns)
+                for ns in (1, 3)}
+    torch.cuda.synchronize()
+    ltol = 1e-2
+    for r in range(rows):
+        b = r // cfg.tq
+        qhat = oatt.normalize_query(raw["q"][r], cfg.eps, cfg.dtype)
+        sel = idx[r][idx[r] >= 0]
+        o_ref, l_ref = oatt.partial(qhat, seqs[b].kv_csa[sel], cfg.scale)
+        for ns, (op_, lp_) in gathered.items():
+            o_g, l_g = merge_splits(op_[:, r], lp_[:, r])
+            if len(sel) == 0:
+                assert np.all(o_g == 0) and np.all(l_g == -np.inf), f"row {r}: empty gather"
+                continue
+            assert_close(o_g, o_ref, cfg.dtype, f"gather n_split {ns} row {r}")
+            assert np.max(np.abs(l_g - l_ref)) <= ltol, f"gather n_split {ns} row {r}: lse"
+        i = int(qp[r])
+        lo, hi = max(i - cfg.W + 1, 0), min(i, cfg.lens[b] - 1)
+        keys = oatt.normalize_tokens(xs[b][lo:hi + 1], cfg.eps, cfg.dtype)
+        o_ref, l_ref = oatt.partial(qhat, keys, cfg.scale)
+        assert_close(f64(ow[0, r]), o_ref, cfg.dtype, f"window row {r}")
+        assert np.max(np.abs(f64(lw[0, r]) - l_ref)) <= ltol, f"window row {r}: lse"
