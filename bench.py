@@ -244,8 +244,9 @@ def prefill_flops(cfg):
 
 def run_prefill(cfg, args, dev):
     """One prefill chunk step per iteration: compress the chunk's entries,
-    score and select for every query row, attend (one launch for the three
-    branches), merge.  Reported against the matrix-core peak."""
+    score and select for every query row, then attend and merge with the sink
+    (one launch: every block takes the three branches for its rows and writes
+    the output).  Reported against the matrix-core peak."""
     import torch
     import lca_inputs as li
     from long_context_attention_20_amd import HybridAttention, ops
@@ -267,18 +268,14 @@ def run_prefill(cfg, args, dev):
     idx = torch.empty((rows, cfg.k), dtype=torch.int32, device=dev)
     out = torch.empty_like(raw["q"])
     streams = a.compress_streams(caches, raw, done_h)
-    names = ["kv_compress", "csa_index_score", "csa_topk_select", "hybrid_attn", "swa_merge"]
-    holder = {}
+    names = ["kv_compress", "csa_index_score", "csa_topk_select", "hybrid_attn_merge"]
+    srcs = a.attn_sources(caches, raw["x"], raw["tok_off"], idx, bufs)
     calls = [
         lambda: ops.kv_compress(streams, raw["tok_off"], done, cfg.eps),
         lambda: ops.csa_index_score(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
                                     max_csa, ws),
         lambda: ops.csa_topk_select(caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws, idx=idx),
-        lambda: holder.__setitem__("parts", ops.hybrid_attn(raw["q"], q_pos,
-                                                            a.attn_sources(caches, raw["x"], raw["tok_off"], idx,
-                                                                           bufs), a.scale, cfg.eps)),
-        lambda: ops.swa_merge(raw["q"], None, None, None, raw["sigma"], holder["parts"], 0, a.scale, cfg.eps, None,
-                              out=out),
+        lambda: ops.hybrid_attn_merge(raw["q"], q_pos, srcs, raw["sigma"], a.scale, cfg.eps, out=out),
     ]
     K, W = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
     for _ in range(W):
@@ -296,7 +293,7 @@ def run_prefill(cfg, args, dev):
     ms = float(per.sum())
     fl = prefill_flops(cfg)
     tot = sum(fl.values())
-    j = names.index("hybrid_attn")
+    j = names.index("hybrid_attn_merge")
     attn_fl = fl["sparse"] + fl["hca"] + fl["window"]
     res = {
         "metric": "prefill query-tokens/s per layer (Flash shape, 4096-token chunk after 256K); MFMA utilisation",
@@ -310,7 +307,7 @@ def run_prefill(cfg, args, dev):
         "flops_per_step": fl,
         "mfma_frac_of_peak": tot / (ms / 1e3) / MFMA_BF16_PEAK,
         "kernel_ms": {n: float(t) for n, t in zip(names, per)},
-        "roofline": {"bound": "mfma", "kernel": "hybrid_attn", "achieved": attn_fl / (per[j] / 1e3) / 1e12,
+        "roofline": {"bound": "mfma", "kernel": "hybrid_attn_merge", "achieved": attn_fl / (per[j] / 1e3) / 1e12,
                      "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
                      "frac": attn_fl / (per[j] / 1e3) / MFMA_BF16_PEAK, "traffic": None,
                      "kernel_ms": float(per[j]), "flops_per_launch": attn_fl},

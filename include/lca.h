@@ -309,6 +309,29 @@ int lca_swa_merge(const void* q, const void* x, const int64_t* tok_off, const in
                   int W, float scale, float eps, void* out, void* ws, size_t ws_bytes, int dtype,
                   void* stream);
 
+/* ------------------------------------------------------------------------
+ * Attention and merge in one call
+ *
+ * The output of lca_hybrid_attn(srcs, ...) followed by lca_swa_merge(q,
+ * NULL, NULL, NULL, sink, the sources' partials in source order, n_src, B,
+ * Tq, H, D, W = 0, ...): one softmax over every key the sources give and the
+ * sink ("Why DeepSeek V4 Stands Apart", Core Architectural Innovations;
+ * "DeepSeek-V4", Core block (attention sinks)), out [B*Tq, H, D] of dtype.
+ * On the row-tiled path (bf16, D = 512, many query rows per sequence) with
+ * one split per source it is one launch: every block attends to all sources
+ * for its rows under one online softmax and writes out, and the sources'
+ * o_part / lse are not written.  Otherwise it is the attention launch(es)
+ * and then the merge launch, the partials written as by lca_hybrid_attn.
+ * The two ways agree within rounding (one softmax over the union against a
+ * log-sum-exp merge of per-source parts).
+ *   sink  device fp32 [H] or NULL (no sink)
+ * Errors as lca_hybrid_attn; LCA_ERR_INVALID_ARG for a NULL out;
+ * LCA_ERR_UNSUPPORTED beyond 512 partial slots in all or B*Tq or H above
+ * 65535. */
+int lca_hybrid_attn_merge(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B,
+                          int Tq, int H, int D, float scale, float eps, const float* sink, void* out, int dtype,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,6 +38,9 @@ int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int 
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
 int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
                      int H, int D, float scale, float eps, int dtype, hipStream_t stream);
+int launch_attention_merge(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B,
+                           int Tq, int H, int D, float scale, float eps, const float* sink, void* out, int dtype,
+                           hipStream_t stream);
 
 static lca_attn_source make_source(int kind, const void* kv, const int64_t* off, const int32_t* idx, int k, int m2,
                                    int w2, int W, int n_split, float* o_part, float* lse) {
@@ -285,8 +288,12 @@ int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int
   return finish(launch_attention(&src, 1, q, q_pos, B, Tq, H, D, scale, eps, dtype, st), st, "swa_attn");
 }
 
-int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
-                    int H, int D, float scale, float eps, int dtype, void* stream) {
+}  // extern "C"
+
+// Argument checks of lca_hybrid_attn (and of the attention part of
+// lca_hybrid_attn_merge).
+static int check_hybrid(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
+                        int H, int D, float scale, float eps, int dtype) {
   LCA_REQUIRE(srcs != nullptr && n_src >= 1 && n_src <= 3, LCA_ERR_INVALID_ARG,
               "hybrid_attn: n_src=%d not in [1,3] (or srcs is NULL)", n_src);
   bool need_pos = false;
@@ -317,8 +324,33 @@ int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const
     need_pos = need_pos || x.kind != LCA_SRC_GATHER;
   }
   LCA_REQUIRE(!need_pos || q_pos != nullptr, LCA_ERR_INVALID_ARG, "hybrid_attn: q_pos is NULL");
+  return LCA_OK;
+}
+
+extern "C" {
+
+int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
+                    int H, int D, float scale, float eps, int dtype, void* stream) {
+  const int rc = check_hybrid(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype);
+  if (rc != LCA_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return finish(launch_attention(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype, st), st, "hybrid_attn");
+}
+
+int lca_hybrid_attn_merge(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B,
+                          int Tq, int H, int D, float scale, float eps, const float* sink, void* out, int dtype,
+                          void* stream) {
+  const int rc = check_hybrid(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype);
+  if (rc != LCA_OK) return rc;
+  LCA_REQUIRE(out != nullptr, LCA_ERR_INVALID_ARG, "hybrid_attn_merge: out is NULL");
+  LCA_REQUIRE((int64_t)B * Tq <= 65535 && H <= 65535, LCA_ERR_UNSUPPORTED,
+              "hybrid_attn_merge: B*Tq and H must be <= 65535");
+  int slots = 0;
+  for (int i = 0; i < n_src; ++i) slots += srcs[i].n_split;
+  LCA_REQUIRE(slots <= 512, LCA_ERR_UNSUPPORTED, "hybrid_attn_merge: %d partial slots, at most 512", slots);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_attention_merge(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, sink, out, dtype, st), st,
+                "hybrid_attn_merge");
 }
 
 size_t lca_swa_merge_workspace(int n_rows, int H, int D) {

@@ -62,6 +62,12 @@ struct AttnParams {
   TopkWs tw;            // the index workspace of a TOPK source
   int filter;           // 1: the TOPK blocks filter the scores themselves
   int tbpr;             // TOPK blocks per row (n_split * n_hb)
+  // row-tiled path: every block takes all sources (one split each) and
+  // writes the merged output with the sink (bf16 [rows, H, D]) instead of
+  // partials
+  int merge;
+  const float* sink;    // [H] or NULL
+  void* out;
 };
 
 constexpr int kFilterPer = 8;  // scores per thread and filter chunk
@@ -601,6 +607,14 @@ __device__ __forceinline__ int rows_swz(int r) {
   return (((r >> 2) & 1) << 3) | ((r & 3) << 1) | (((r >> 2) ^ (r >> 3)) & 1);
 }
 
+// Wave-uniform 64-bit value in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <bool MERGE>
 __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_rows_mfma(AttnParams a) {
   constexpr int D = 512;
   constexpr int KS = D / 32;      // k-steps of S over D
@@ -615,91 +629,32 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
   // key ranges, addresses) stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
-  // block -> (sequence b, row tile, source split); a sequence's rows are (t, h) -> t*H + h
+  // block -> (sequence b, row tile, source split), or (b, row tile) with
+  // every source in turn when the block also merges; a sequence's rows are
+  // (t, h) -> t*H + h
   const int64_t rows_seq = (int64_t)a.Tq * a.H;
   const int64_t tiles_seq = (rows_seq + kRowsBlockRows - 1) / kRowsBlockRows;
-  const int bx = (int)(blockIdx.x % a.n_x);
-  const int64_t rest = blockIdx.x / a.n_x;
+  const int bx = MERGE ? 0 : (int)(blockIdx.x % a.n_x);
+  const int64_t rest = MERGE ? (int64_t)blockIdx.x : (int64_t)(blockIdx.x / a.n_x);
   const int b = (int)(rest / tiles_seq);
   const int64_t rt = rest % tiles_seq;
-  int split;
-  const int si = attn_source(a, bx, &split);
-  const AttnSrc& S = a.s[si];
-  const int kind = S.kind;
   const int64_t rr = rt * kRowsBlockRows + wave * 16;  // this wave's first row
   const bool wave_on = rr < rows_seq;                  // uniform per wave (H divides 128)
   const int t = wave_on ? (int)(rr / a.H) : 0;
   const int h0 = (int)(rr % a.H);
   const int r = b * a.Tq + t;
   const int nq = kRowsBlockRows / a.H;                 // queries per block
-  const int streams = kind == SRC_GATHER ? nq : 1;
-  const int stream = kind == SRC_GATHER ? (wave * 16) / a.H : 0;
-  const int wps = (kRowsThreads / 64) / streams;       // waves per stream
-  const int wis = wave % wps;                          // this wave's place in its stream
-  const int64_t first = S.off[b];
-  const int64_t nseq = S.off[b + 1] - first;
-  // this wave's visible key range [lo, hi) in the source's key coordinates:
-  // entries (dense), token positions (window), slots (gathered)
-  int64_t lo = 0, hi = 0;
-  if (wave_on) {
-    if (kind == SRC_DENSE) {
-      const int64_t nh = n_windows((int64_t)a.q_pos[r] + 1, S.m2, S.w2);
-      hi = nh < nseq ? nh : nseq;
-    } else if (kind == SRC_WINDOW) {
-      const int64_t i = a.q_pos[r];
-      lo = i - S.W + 1 > 0 ? i - S.W + 1 : 0;
-      hi = (i < nseq - 1 ? i : nseq - 1) + 1;
-      if (hi < lo) hi = lo;
-    } else {
-      hi = nseq > 0 ? S.k : 0;
-    }
-  }
-  if (lane == 0) {
-    // an empty range adds nothing to the block's union (a window past the
-    // sequence's last token has hi == lo > nseq)
-    s_lo[wave] = wave_on && hi > lo ? lo : INT64_MAX;
-    s_hi[wave] = wave_on && hi > lo ? hi : 0;
-  }
+
   // the query rows, RMS-normalised over D and rounded to bf16: lane (c16, g)
   // holds head h0 + c16, dims 32*ks + 8*g .. +7
-  uint4 qraw[KS];
-  if (wave_on) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h0 + c16) * D + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
-  }
-  __syncthreads();  // s_lo, s_hi
-  // the block's key range (per stream for gathered keys: every stream has k slots)
-  int64_t blo = INT64_MAX, bhi = 0;
-#pragma unroll
-  for (int w = 0; w < kRowsThreads / 64; ++w) {
-    blo = s_lo[w] < blo ? s_lo[w] : blo;
-    bhi = s_hi[w] > bhi ? s_hi[w] : bhi;
-  }
-  if (blo > bhi) blo = bhi;  // nothing visible
-  const int64_t ntiles = (bhi - blo + kRowsTile - 1) / kRowsTile;
-  const int64_t tps = (ntiles + S.n_split - 1) / S.n_split;
-  const int64_t tb = (int64_t)split * tps;
-  const int64_t te = min(ntiles, tb + tps);
-  const int64_t kbase = blo + tb * kRowsTile;  // key coordinate of the split's first tile row
-  if (kind == SRC_GATHER && te > tb) {
-    // every stream's slots of this split, -1 for unused or out-of-range entries
-    const int64_t cnt = min((te - tb) * kRowsTile, bhi - kbase);
-    const int q0 = (int)((rt * kRowsBlockRows) / a.H);
-    for (int i = threadIdx.x; i < streams * kRowsIdx; i += kRowsThreads) {
-      const int st = i / kRowsIdx, j = i % kRowsIdx;
-      const int tq = q0 + st;
-      int32_t e = -1;
-      if (j < cnt && tq < a.Tq) {
-        e = S.idx[(int64_t)(b * a.Tq + tq) * S.k + kbase + j];
-        if (e < 0 || e >= nseq) e = -1;
-      }
-      sidx[st][j] = e;
-    }
-  }
-
   bf16x8_t qb[KS];
   {
+    uint4 qraw[KS];
+    if (wave_on) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)r * a.H + h0 + c16) * D + g * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
+    }
     float ss = 0.f;
     if (wave_on) {
 #pragma unroll
@@ -722,161 +677,252 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
-  __syncthreads();  // sidx
 
-  // tile staging: one wave instruction moves one 1 KiB key row straight into
-  // LDS; wave w loads rows wis*rpw .. of its stream's tile.  Rows without a
-  // visible key load a clamped valid row (their logits are masked, so they
-  // weigh nothing).
-  const uint16_t* kvp = reinterpret_cast<const uint16_t*>(S.kv);
-  const int rpw = kRowsTile / wps;  // rows per wave: 4 (one stream) or 8 (two)
-  auto load_tile = [&](int64_t tt) {
-    if (tt >= te) return;
-    uint16_t* tile = tiles[stream][(tt - tb) & 1];
-    for (int v = 0; v < rpw; ++v) {  // uniform
-      const int row = wis * rpw + v;
-      const int64_t kc = blo + tt * kRowsTile + row;
-      int64_t ent;
-      if (kind == SRC_GATHER) {
-        const int32_t e = sidx[stream][kc - kbase];
-        ent = e >= 0 ? e : 0;
-      } else {
-        ent = kc < bhi ? kc : blo;
-      }
-      // lane l fills LDS chunk l with the row's chunk l ^ rows_swz(row)
-      const uint16_t* src = kvp + (first + ent) * D + ((lane ^ rows_swz(row)) * 8);
-      lds_dma16(src, tile + row * PITCH);
-    }
-  };
-  // window rows: RMS over D of the raw row, rounded to bf16, in place (the
-  // wave that loaded a row normalises it once its loads have landed; the
-  // chunk order within the row does not matter here)
-  auto norm_rows = [&](int64_t tt) {
-    uint16_t* tile = tiles[0][(tt - tb) & 1];
-    for (int v = 0; v < rpw; ++v) {
-      uint16_t* rowp = tile + (wis * rpw + v) * PITCH + lane * 8;
-      uint4 x = *reinterpret_cast<const uint4*>(rowp);
-      float f[8];
-      BF16::unpack(x, f);
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-      ss = lane_group_sum<64>(ss);
-      const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] *= inv;
-      *reinterpret_cast<uint4*>(rowp) = BF16::pack(f);
-    }
-  };
-
+  // one online softmax over every key the block's sources give (one source,
+  // or all of them in turn when the block merges)
   f32x4 O[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
-  load_tile(tb);
-  for (int64_t tt = tb; tt < te; ++tt) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the tile have landed
-    if (kind == SRC_WINDOW) norm_rows(tt);
-    // tile in LDS; every wave has left the previous tile, whose buffer the
-    // next loads overwrite
+  int split = 0, si = 0;
+  for (int sl = 0; sl < (MERGE ? a.n_src : 1); ++sl) {
+    if (MERGE)
+      si = sl;
+    else
+      si = attn_source(a, bx, &split);
+    const AttnSrc& S = a.s[si];
+    const int kind = S.kind;
+    const int streams = kind == SRC_GATHER ? nq : 1;
+    const int stream = kind == SRC_GATHER ? (wave * 16) / a.H : 0;
+    const int wps = (kRowsThreads / 64) / streams;       // waves per stream
+    const int wis = wave % wps;                          // this wave's place in its stream
+    const int64_t first = S.off[b];
+    const int64_t nseq = S.off[b + 1] - first;
+    // this wave's visible key range [lo, hi) in the source's key coordinates:
+    // entries (dense), token positions (window), slots (gathered)
+    int64_t lo = 0, hi = 0;
+    if (wave_on) {
+      if (kind == SRC_DENSE) {
+        const int64_t nh = n_windows((int64_t)a.q_pos[r] + 1, S.m2, S.w2);
+        hi = nh < nseq ? nh : nseq;
+      } else if (kind == SRC_WINDOW) {
+        const int64_t i = a.q_pos[r];
+        lo = i - S.W + 1 > 0 ? i - S.W + 1 : 0;
+        hi = (i < nseq - 1 ? i : nseq - 1) + 1;
+        if (hi < lo) hi = lo;
+      } else {
+        hi = nseq > 0 ? S.k : 0;
+      }
+    }
+    // the previous source's readers of s_lo / s_hi, sidx and the tiles are done
     __syncthreads();
-    load_tile(tt + 1);
-    const uint16_t* tile = tiles[stream][(tt - tb) & 1];
-    const int64_t k0 = blo + tt * kRowsTile;  // key coordinate of the tile's first row
-    // the tile's rows this wave sees, one per lane of the low half-wave
-    const int64_t kl = k0 + lane;
-    const uint64_t vm = __ballot(lane < kRowsTile && kl >= lo && kl < hi &&
-                                 (kind != SRC_GATHER || sidx[stream][kl - kbase] >= 0));
-    if (wave_on && vm != 0) {  // uniform per wave
-      // ---- S^T for tile rows 0..15 (p0) and 16..31 (p1)
-      f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
-      // rows c16 and 16 + c16 (same swizzle), logical chunk 4 ks + g: with
-      // ks = 4j + i the physical chunk is 16j + ((4i + g) ^ swz), four
-      // per-lane offsets and an immediate.  The swizzle goes through an empty
-      // asm so that the offsets are formed here, not held over the loop.
-      int sk = rows_swz(c16);
-      asm volatile("" : "+v"(sk));
-      int koff[4];
+    lo = uniform64(lo);
+    hi = uniform64(hi);
+    if (lane == 0) {
+      // an empty range adds nothing to the block's union (a window past the
+      // sequence's last token has hi == lo > nseq)
+      s_lo[wave] = wave_on && hi > lo ? lo : INT64_MAX;
+      s_hi[wave] = wave_on && hi > lo ? hi : 0;
+    }
+    __syncthreads();  // s_lo, s_hi
+    // the block's key range (per stream for gathered keys: every stream has k slots)
+    int64_t blo = INT64_MAX, bhi = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) koff[i] = c16 * PITCH + ((4 * i + g) ^ sk) * 8;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint16_t* k0p = tile + koff[ks & 3] + (ks >> 2) * 128;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(k0p);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(k0p + 16 * PITCH);
-        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), qb[ks], p0, 0, 0, 0);
-        p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), qb[ks], p1, 0, 0, 0);
-      }
-      // ---- online softmax: lane (c16 = head, g) holds tile rows 4g+i and 16+4g+i
-      float lg[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lg[i] = ((vm >> (4 * g + i)) & 1u) ? p0[i] * sl2 : -INFINITY;
-        lg[4 + i] = ((vm >> (16 + 4 * g + i)) & 1u) ? p1[i] * sl2 : -INFINITY;
-      }
-      float tmax = lg[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, lg[i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      if (tmax != -INFINITY) {  // uniform: the masks do not depend on the head
-        const bool move = tmax > m_run + 8.0f;
-        const float alpha = move ? exp2f(m_run - tmax) : 1.0f;
-        const float m_ref = move ? tmax : m_run;
-        float pr[8], psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pr[i] = exp2f(lg[i] - m_ref);
-          psum += pr[i];
+    for (int w = 0; w < kRowsThreads / 64; ++w) {
+      blo = s_lo[w] < blo ? s_lo[w] : blo;
+      bhi = s_hi[w] > bhi ? s_hi[w] : bhi;
+    }
+    if (blo > bhi) blo = bhi;  // nothing visible
+    const int64_t ntiles = (bhi - blo + kRowsTile - 1) / kRowsTile;
+    const int64_t tps = (ntiles + S.n_split - 1) / S.n_split;
+    const int64_t tb = (int64_t)split * tps;
+    const int64_t te = min(ntiles, tb + tps);
+    const int64_t kbase = blo + tb * kRowsTile;  // key coordinate of the split's first tile row
+    if (kind == SRC_GATHER && te > tb) {
+      // every stream's slots of this split, -1 for unused or out-of-range entries
+      const int64_t cnt = min((te - tb) * kRowsTile, bhi - kbase);
+      const int q0 = (int)((rt * kRowsBlockRows) / a.H);
+      for (int i = threadIdx.x; i < streams * kRowsIdx; i += kRowsThreads) {
+        const int st = i / kRowsIdx, j = i % kRowsIdx;
+        const int tq = q0 + st;
+        int32_t e = -1;
+        if (j < cnt && tq < a.Tq) {
+          e = S.idx[(int64_t)(b * a.Tq + tq) * S.k + kbase + j];
+          if (e < 0 || e >= nseq) e = -1;
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_ref;
-        if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) O[db] = O[db] * alpha;
+        sidx[st][j] = e;
+      }
+    }
+
+    __syncthreads();  // sidx
+
+    // tile staging: one wave instruction moves one 1 KiB key row straight into
+    // LDS; wave w loads rows wis*rpw .. of its stream's tile.  Rows without a
+    // visible key load a clamped valid row (their logits are masked, so they
+    // weigh nothing).
+    const uint16_t* kvp = reinterpret_cast<const uint16_t*>(S.kv);
+    const int rpw = kRowsTile / wps;  // rows per wave: 4 (one stream) or 8 (two)
+    auto load_tile = [&](int64_t tt) {
+      if (tt >= te) return;
+      uint16_t* tile = tiles[stream][(tt - tb) & 1];
+      for (int v = 0; v < rpw; ++v) {  // uniform
+        const int row = wis * rpw + v;
+        const int64_t kc = blo + tt * kRowsTile + row;
+        int64_t ent;
+        if (kind == SRC_GATHER) {
+          const int32_t e = sidx[stream][kc - kbase];
+          ent = e >= 0 ? e : 0;
+        } else {
+          ent = kc < bhi ? kc : blo;
         }
-        uint4 pb;
-        pb.x = pack_bf16x2(pr[0], pr[1]);
-        pb.y = pack_bf16x2(pr[2], pr[3]);
-        pb.z = pack_bf16x2(pr[4], pr[5]);
-        pb.w = pack_bf16x2(pr[6], pr[7]);
-        const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, pb);
-        // ---- O^T += V^T . P^T: lane c16 of group g reads rows 4g + c16/4 (and
-        // 16 + ...) at columns 16*db + 4*(c16%4); the transpose read returns
-        // dim 16*db + c16 of tile rows 4g..4g+3 (and 16+4g..)
-        // (logical chunk 2 db + bit 1 of c16, half c16 & 1; rows 4g + c16/4
-        // and 16 + 4g + c16/4 share the swizzle)
-        // (with db = 8j + i the physical chunk is 16j + ((2i + hh) ^ swz):
-        // eight per-lane offsets and an immediate)
-        const int tr_r = 4 * g + (c16 >> 2);
-        int st = rows_swz(tr_r);
-        asm volatile("" : "+v"(st));
-        const int hh = (c16 >> 1) & 1;
-        int toff[8];
+        // lane l fills LDS chunk l with the row's chunk l ^ rows_swz(row)
+        const uint16_t* src = kvp + (first + ent) * D + ((lane ^ rows_swz(row)) * 8);
+        lds_dma16(src, tile + row * PITCH);
+      }
+    };
+    // window rows: RMS over D of the raw row, rounded to bf16, in place (the
+    // wave that loaded a row normalises it once its loads have landed; the
+    // chunk order within the row does not matter here)
+    auto norm_rows = [&](int64_t tt) {
+      uint16_t* tile = tiles[0][(tt - tb) & 1];
+      for (int v = 0; v < rpw; ++v) {
+        uint16_t* rowp = tile + (wis * rpw + v) * PITCH + lane * 8;
+        uint4 x = *reinterpret_cast<const uint4*>(rowp);
+        float f[8];
+        BF16::unpack(x, f);
+        float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) toff[i] = tr_r * PITCH + 4 * (c16 & 1) + ((2 * i + hh) ^ st) * 8;
+        for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+        ss = lane_group_sum<64>(ss);
+        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
 #pragma unroll
-        for (int db = 0; db < DB; db += 2) {
-          const uint16_t* t0 = tile + toff[db & 7] + (db >> 3) * 128;
-          const uint16_t* t1 = tile + toff[(db + 1) & 7] + ((db + 1) >> 3) * 128;
-          const s4_t v00 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)t0);
-          const s4_t v01 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(t0 + 16 * PITCH));
-          const s4_t v10 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)t1);
-          const s4_t v11 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(t1 + 16 * PITCH));
-          O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v00, v01)), pt, O[db],
-                                                          0, 0, 0);
-          O[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v10, v11)), pt,
-                                                              O[db + 1], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) f[e] *= inv;
+        *reinterpret_cast<uint4*>(rowp) = BF16::pack(f);
+      }
+    };
+
+    load_tile(tb);
+    for (int64_t tt = tb; tt < te; ++tt) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the tile have landed
+      if (kind == SRC_WINDOW) norm_rows(tt);
+      // tile in LDS; every wave has left the previous tile, whose buffer the
+      // next loads overwrite
+      __syncthreads();
+      load_tile(tt + 1);
+      const uint16_t* tile = tiles[stream][(tt - tb) & 1];
+      const int64_t k0 = blo + tt * kRowsTile;  // key coordinate of the tile's first row
+      // the tile's rows this wave sees, one per lane of the low half-wave
+      const int64_t kl = k0 + lane;
+      const uint64_t vm = __ballot(lane < kRowsTile && kl >= lo && kl < hi &&
+                                   (kind != SRC_GATHER || sidx[stream][kl - kbase] >= 0));
+      if (wave_on && vm != 0) {  // uniform per wave
+        // ---- S^T for tile rows 0..15 (p0) and 16..31 (p1)
+        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
+        // rows c16 and 16 + c16 (same swizzle), logical chunk 4 ks + g: with
+        // ks = 4j + i the physical chunk is 16j + ((4i + g) ^ swz), four
+        // per-lane offsets and an immediate.  The swizzle goes through an empty
+        // asm so that the offsets are formed here, not held over the loop.
+        int sk = rows_swz(c16);
+        asm volatile("" : "+v"(sk));
+        int koff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) koff[i] = c16 * PITCH + ((4 * i + g) ^ sk) * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint16_t* k0p = tile + koff[ks & 3] + (ks >> 2) * 128;
+          const uint4 a0 = *reinterpret_cast<const uint4*>(k0p);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(k0p + 16 * PITCH);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), qb[ks], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), qb[ks], p1, 0, 0, 0);
+        }
+        // ---- online softmax: lane (c16 = head, g) holds tile rows 4g+i and 16+4g+i
+        float lg[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lg[i] = ((vm >> (4 * g + i)) & 1u) ? p0[i] * sl2 : -INFINITY;
+          lg[4 + i] = ((vm >> (16 + 4 * g + i)) & 1u) ? p1[i] * sl2 : -INFINITY;
+        }
+        float tmax = lg[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, lg[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        if (tmax != -INFINITY) {  // uniform: the masks do not depend on the head
+          const bool move = tmax > m_run + 8.0f;
+          const float alpha = move ? exp2f(m_run - tmax) : 1.0f;
+          const float m_ref = move ? tmax : m_run;
+          float pr[8], psum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            pr[i] = exp2f(lg[i] - m_ref);
+            psum += pr[i];
+          }
+          l_run = l_run * alpha + psum;
+          m_run = m_ref;
+          if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) O[db] = O[db] * alpha;
+          }
+          uint4 pb;
+          pb.x = pack_bf16x2(pr[0], pr[1]);
+          pb.y = pack_bf16x2(pr[2], pr[3]);
+          pb.z = pack_bf16x2(pr[4], pr[5]);
+          pb.w = pack_bf16x2(pr[6], pr[7]);
+          const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, pb);
+          // ---- O^T += V^T . P^T: lane c16 of group g reads rows 4g + c16/4 (and
+          // 16 + ...) at columns 16*db + 4*(c16%4); the transpose read returns
+          // dim 16*db + c16 of tile rows 4g..4g+3 (and 16+4g..)
+          // (logical chunk 2 db + bit 1 of c16, half c16 & 1; rows 4g + c16/4
+          // and 16 + 4g + c16/4 share the swizzle)
+          // (with db = 8j + i the physical chunk is 16j + ((2i + hh) ^ swz):
+          // eight per-lane offsets and an immediate)
+          const int tr_r = 4 * g + (c16 >> 2);
+          int st = rows_swz(tr_r);
+          asm volatile("" : "+v"(st));
+          const int hh = (c16 >> 1) & 1;
+          int toff[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) toff[i] = tr_r * PITCH + 4 * (c16 & 1) + ((2 * i + hh) ^ st) * 8;
+#pragma unroll
+          for (int db = 0; db < DB; db += 2) {
+            const uint16_t* t0 = tile + toff[db & 7] + (db >> 3) * 128;
+            const uint16_t* t1 = tile + toff[(db + 1) & 7] + ((db + 1) >> 3) * 128;
+            const s4_t v00 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)t0);
+            const s4_t v01 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(t0 + 16 * PITCH));
+            const s4_t v10 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)t1);
+            const s4_t v11 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(t1 + 16 * PITCH));
+            O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v00, v01)), pt, O[db],
+                                                            0, 0, 0);
+            O[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pack_tr(v10, v11)), pt,
+                                                                O[db + 1], 0, 0, 0);
+          }
         }
       }
     }
-  }
+
+  }  // sources
 
   // ---- epilogue: lane (c16, g) holds dims 16*db + 4g .. +3 of head h0 + c16
   if (!wave_on) return;
   float lsum = l_run + __shfl_xor(l_run, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
+  if (MERGE) {
+    // the sink (zero value) joins the denominator: out = O / (l + e^(sink - m))
+    float den = lsum;
+    if (a.sink && m_run != -INFINITY) den += exp2f(a.sink[h0 + c16] * kLog2e - m_run);
+    const float w = den > 0.f ? 1.0f / den : 0.f;
+    uint16_t* outp = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)r * a.H + h0 + c16) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      uint2 pk;
+      pk.x = pack_bf16x2(O[db][0] * w, O[db][1] * w);
+      pk.y = pack_bf16x2(O[db][2] * w, O[db][3] * w);
+      *reinterpret_cast<uint2*>(outp + db * 16) = pk;
+    }
+    return;
+  }
+  const AttnSrc& S = a.s[si];
   const float w = lsum > 0.f ? 1.0f / lsum : 0.f;
   const int64_t orow = ((int64_t)split * a.rows + r) * a.H + h0 + c16;
   float* op = S.o_part + orow * D + 4 * g;
@@ -1202,9 +1248,28 @@ static int64_t resident_blocks(int D) {
   return cache[dev][di];
 }
 
+// A merge to follow the attention (lca_hybrid_attn_merge): sink and output.
+struct MergeReq {
+  const float* sink;
+  void* out;
+};
 static int launch_attention_sources(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos,
                                     int B, int Tq, int H, int D, float scale, float eps, int dtype,
                                     hipStream_t stream);
+int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, const float* win_lse,
+                 const float* sink, int rows, int H, int D, void* out, int dtype, hipStream_t stream);
+
+// The merge of the sources' partials as its own launch.
+static int merge_sources(const lca_attn_source* srcs, int n_src, int rows, int H, int D, const MergeReq* mr,
+                         int dtype, hipStream_t stream) {
+  lca_partial parts[kMaxSrc];
+  for (int i = 0; i < n_src; ++i) {
+    parts[i].o = srcs[i].o_part;
+    parts[i].lse = srcs[i].lse;
+    parts[i].n_split = srcs[i].n_split;
+  }
+  return launch_merge(parts, n_src, nullptr, nullptr, mr->sink, rows, H, D, mr->out, dtype, stream);
+}
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
 
@@ -1227,14 +1292,18 @@ static bool rows_launch(const lca_attn_source* srcs, int n_src, int Tq, int H, i
   return true;
 }
 
-int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
-                     int H, int D, float scale, float eps, int dtype, hipStream_t stream) {
+static int launch_attention_impl(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B,
+                                 int Tq, int H, int D, float scale, float eps, int dtype, hipStream_t stream,
+                                 const MergeReq* mr) {
   if (n_src < 1 || n_src > kMaxSrc) {
     set_error("attention: %d key sources, 1 to %d supported", n_src, kMaxSrc);
     return LCA_ERR_UNSUPPORTED;
   }
-  if (!rows_launch(srcs, n_src, Tq, H, D, dtype))
-    return launch_attention_sources(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype, stream);
+  if (!rows_launch(srcs, n_src, Tq, H, D, dtype)) {
+    const int rc = launch_attention_sources(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype, stream);
+    if (rc != LCA_OK || !mr) return rc;
+    return merge_sources(srcs, n_src, B * Tq, H, D, mr, dtype, stream);
+  }
   AttnParams a{};
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
@@ -1254,8 +1323,15 @@ int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, cons
     }
   }
   a.n_x = splits;
+  // with one split per source the blocks also merge: each takes every source
+  // for its rows and writes the output
+  if (mr && splits == n_src) {
+    a.merge = 1;
+    a.sink = mr->sink;
+    a.out = mr->out;
+  }
   const int64_t tiles_seq = ((int64_t)Tq * H + kRowsBlockRows - 1) / kRowsBlockRows;
-  const int64_t nblk = (int64_t)B * tiles_seq * splits;
+  const int64_t nblk = (int64_t)B * tiles_seq * (a.merge ? 1 : splits);
   if (nblk > 0x7FFFFFFF) {
     set_error("attention: %lld blocks exceed the grid limit", (long long)nblk);
     return LCA_ERR_UNSUPPORTED;
@@ -1266,8 +1342,27 @@ int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, cons
                                       in.ws, stream);
     if (rc != LCA_OK) return rc;
   }
-  hipLaunchKernelGGL(attn_rows_mfma, dim3((unsigned)nblk), dim3(kRowsThreads), 0, stream, a);
-  return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+  if (a.merge)
+    hipLaunchKernelGGL(attn_rows_mfma<true>, dim3((unsigned)nblk), dim3(kRowsThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_rows_mfma<false>, dim3((unsigned)nblk), dim3(kRowsThreads), 0, stream, a);
+  if (hipPeekAtLastError() != hipSuccess) return LCA_ERR_HIP;
+  return (mr && !a.merge) ? merge_sources(srcs, n_src, B * Tq, H, D, mr, dtype, stream) : LCA_OK;
+}
+
+int launch_attention(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
+                     int H, int D, float scale, float eps, int dtype, hipStream_t stream) {
+  return launch_attention_impl(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype, stream, nullptr);
+}
+
+// The attention of every source and the merge of their partials with the
+// sink into out: one launch on the row-tiled path with one split per source,
+// else the attention and then the merge.
+int launch_attention_merge(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B,
+                           int Tq, int H, int D, float scale, float eps, const float* sink, void* out, int dtype,
+                           hipStream_t stream) {
+  const MergeReq mr{sink, out};
+  return launch_attention_impl(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, dtype, stream, &mr);
 }
 
 static int launch_attention_sources(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos,

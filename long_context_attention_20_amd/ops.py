@@ -224,15 +224,8 @@ def swa_attn(q, x, tok_off, q_pos, W: int, scale: float, eps: float, o_part=None
 _KINDS = {"dense": LCA_SRC_DENSE, "gather": LCA_SRC_GATHER, "window": LCA_SRC_WINDOW, "topk": LCA_SRC_TOPK}
 
 
-def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
-    """The attention branches of a step in one launch.  sources: dicts with
-    kind ("gather", "dense", "window" or "topk"), kv, off and n_split, plus
-    idx (gather), m2 and w2 (dense), W (window), and optionally o_part / lse.
-    A "topk" source selects the sparse branch's entries from the scores a
-    csa_index_score(_append) call left in its workspace: it takes k, m2 = m,
-    w2 = w, max_entries, ws, idx_out (int32 [rows, k], written) and
-    optionally scores.  Returns one (o_part, lse) pair per source, as the
-    single-branch calls."""
+def _attn_sources(q, q_pos, sources: Sequence[dict]):
+    """ctypes array of the sources, their (o_part, lse) outputs and B."""
     if not 1 <= len(sources) <= 3:
         raise ValueError("1..3 sources per call")
     _dev(q, q_pos)
@@ -271,9 +264,39 @@ def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
                             int(s.get("m2", 1)), int(s.get("w2", 1)), int(s.get("W", 0)), ns, o_part.data_ptr(),
                             lse.data_ptr(), _addr(ws), ws_bytes or 0, max_entries or 0, _addr(scores), _addr(idx_out))
         outs.append((o_part, lse))
+    return arr, outs, B
+
+
+def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
+    """The attention branches of a step in one launch.  sources: dicts with
+    kind ("gather", "dense", "window" or "topk"), kv, off and n_split, plus
+    idx (gather), m2 and w2 (dense), W (window), and optionally o_part / lse.
+    A "topk" source selects the sparse branch's entries from the scores a
+    csa_index_score(_append) call left in its workspace: it takes k, m2 = m,
+    w2 = w, max_entries, ws, idx_out (int32 [rows, k], written) and
+    optionally scores.  Returns one (o_part, lse) pair per source, as the
+    single-branch calls."""
+    arr, outs, B = _attn_sources(q, q_pos, sources)
+    rows, H, D = q.shape
     check(lib.lca_hybrid_attn(arr, len(sources), _ptr(q), _ptr(q_pos), B, rows // B, H, D, float(scale), float(eps),
                               _dtype_code(q), _stream()), "hybrid_attn")
     return outs
+
+
+def hybrid_attn_merge(q, q_pos, sources: Sequence[dict], sigma, scale: float, eps: float, out=None):
+    """The sources of hybrid_attn merged with the sink sigma (fp32 [H] or
+    None) into out [rows, H, D] (q's dtype), as hybrid_attn + swa_merge; one
+    launch on the row-tiled path with one split per source (the partial
+    buffers are then not written).  Returns out."""
+    arr, _, B = _attn_sources(q, q_pos, sources)
+    _dev(sigma, out)
+    rows, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    check(lib.lca_hybrid_attn_merge(arr, len(sources), _ptr(q), _ptr(q_pos), B, rows // B, H, D, float(scale),
+                                    float(eps), _ptr(sigma), _ptr(out), _dtype_code(q), _stream()),
+          "hybrid_attn_merge")
+    return out
 
 
 def swa_merge_workspace(n_rows: int, H: int, D: int) -> int:

@@ -183,9 +183,14 @@ class HybridAttention:
             # the dense source is always launched (an empty one writes o = 0,
             # lse = -inf), so that the partials are there for every row
             bufs = dict(sc=sc, sh=sh, sw=sw, max_hca=1, csa=(None, None), hca=(None, None), swa=(None, None))
-            parts = ops.hybrid_attn(q, q_pos, self.attn_sources(caches, x, tok_off, idx, bufs), self.scale, self.eps)
-            csa, hca = parts[0], parts[1]
-            out = ops.swa_merge(q, None, None, None, sigma, parts, 0, self.scale, self.eps, None)
+            srcs = self.attn_sources(caches, x, tok_off, idx, bufs)
+            # attention and merge in one call (one launch when every source
+            # has one split); with keep, the partials are computed as well
+            out = ops.hybrid_attn_merge(q, q_pos, srcs, sigma, self.scale, self.eps)
+            csa = hca = None
+            if keep:
+                parts = ops.hybrid_attn(q, q_pos, srcs, self.scale, self.eps)
+                csa, hca = parts[0], parts[1]
         else:
             sc = self.split_csa or self.default_splits(rows, self.k)
             sh = self.split_hca or self.default_splits(rows, max_hca)

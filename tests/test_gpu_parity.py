@@ -715,3 +715,59 @@ def test_rows_gather_window_against_oracle(H, k):
         o_ref, l_ref = oatt.partial(qhat, keys, cfg.scale)
         assert_close(f64(ow[0, r]), o_ref, cfg.dtype, f"window row {r}")
         assert np.max(np.abs(f64(lw[0, r]) - l_ref)) <= ltol, f"window row {r}: lse"
+
+
+@pytest.mark.parametrize("name", sorted(CASES) + ["rows64", "rows128"])
+def test_hybrid_attn_merge_equals_separate(name):
+    """lca_hybrid_attn_merge against lca_hybrid_attn + lca_swa_merge with the
+    sink: with one query row per sequence (the merge as its own launch) the
+    same output bit for bit; with many rows per sequence (rows64: H = 64, two
+    queries per block; rows128: H = 128) and one split per source, one launch
+    in which every block takes all three sources under one softmax: the same
+    output within rounding, and within the tolerance of the oracle."""
+    from long_context_attention_20_amd import ops
+    if name == "rows64":
+        cfg = li.small("merge_rows64", 118, (9000, 3000), tq=41, H=64, D=512, k=256)
+    elif name == "rows128":
+        cfg = li.small("merge_rows128", 119, (9000,), tq=24, H=128, D=512, k=512)
+    else:
+        cfg = CASES[name]
+    print(f"[attn+merge {name}] lens={cfg.lens} tq={cfg.tq} H={cfg.H} D={cfg.D} k={cfg.k} {cfg.dtype}", flush=True)
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    q_pos = d["q_pos"].clone()
+    if cfg.tq > 3:
+        q_pos[:3] = torch.tensor([5, 127, 300], dtype=torch.int32, device="cuda")  # few or no compressed entries
+    qp = q_pos.cpu().numpy()
+    rows = q_pos.numel()
+    max_csa = max(1, ocmp.n_entries(int(qp.max()) + 1, cfg.m, cfg.w))
+    max_hca = ocmp.n_entries(int(qp.max()) + 1, cfg.m2, cfg.w2)
+    idx = ops.csa_index_topk(d["p"], d["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa,
+                             torch.zeros(ops.csa_index_topk_workspace(rows, max_csa, cfg.k), dtype=torch.uint8,
+                                         device="cuda"))
+    ns = 1 if cfg.tq > 1 else 3
+    srcs = [dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=ns),
+            dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=cfg.m2, w2=cfg.w2, n_split=ns),
+            dict(kind="window", kv=d["x"], off=d["tok_off"], W=cfg.W, n_split=1)]
+    ref = ops.swa_merge(d["q"], None, None, None, d["sigma"], ops.hybrid_attn(d["q"], q_pos, srcs, cfg.scale, cfg.eps),
+                        0, cfg.scale, cfg.eps, None)
+    out = ops.hybrid_attn_merge(d["q"], q_pos, srcs, d["sigma"], cfg.scale, cfg.eps)
+    torch.cuda.synchronize()
+    if cfg.tq == 1:
+        assert torch.equal(out, ref), "merged output differs from hybrid_attn + swa_merge"
+        return
+    assert_close(f64(out), f64(ref), cfg.dtype, "fused against separate")
+    # against the oracle, every row: one softmax over the selected CSA
+    # entries, the visible HCA entries, the window and the sink
+    idx_h = idx.cpu().numpy()
+    out_h = f64(out)
+    for r in range(rows):
+        b = r // cfg.tq
+        g = seq_caches(caches, b)
+        xs = opipe.seq_slice(raw["x"], raw["tok_off"], b)
+        res = opipe.query_step(g, xs, raw["q"][r], raw["p"][r], raw["omega"][r], raw["sigma"], int(qp[r]), cfg,
+                               idx=idx_h[r])
+        assert_close(out_h[r], res["out"], cfg.dtype, f"row {r}")
