@@ -222,3 +222,26 @@ def test_index_score_append_rejects(L):
     idx[0] = L.CompressStream(256, 256, 256, 256, 64, 4, 8, 1, 0, 1)
     kv[1] = L.CompressStream(512, 512, 512, 768, 500, 128, 128, 1, 1, 1)  # C % 8
     assert call() == L.LCA_ERR_INVALID_ARG
+
+
+def test_hybrid_attn_merge_rejects(L):
+    """lca_hybrid_attn_merge checks its sources as lca_hybrid_attn does, then
+    the output pointer and the number of partial slots; nothing is launched
+    on a rejected call."""
+    lib = L.lib
+    P = ctypes.c_void_p(256)
+    src = (L.AttnSource * 1)()
+
+    def gather(n_split=2):
+        src[0] = L.AttnSource(L.LCA_SRC_GATHER, 256, 256, 256, 64, 1, 1, 0, n_split, 256, 256, None, 0, 0, None, None)
+
+    def call(n=1, out=P):
+        return lib.lca_hybrid_attn_merge(src, n, P, P, 1, 1, 64, 512, 0.04, 1e-6, None, out, 1, None)
+    gather()
+    assert call(n=0) == L.LCA_ERR_INVALID_ARG                   # no source
+    assert call(out=None) == L.LCA_ERR_INVALID_ARG              # no output
+    assert b"out is NULL" in lib.lca_last_error()
+    gather(n_split=0)
+    assert call() == L.LCA_ERR_INVALID_ARG                      # a source with no split
+    gather(n_split=300)
+    assert call() == L.LCA_ERR_INVALID_ARG                      # beyond 256 splits per source
