@@ -498,6 +498,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
 // crowded) give the exact cut; the bitmap then yields the row in ascending
 // index order.
 constexpr int kRowThreads = 1024;
+constexpr int kRowLoads = 8;    // score loads in flight per thread and pass
 constexpr int kRowBitmapWords = kRowMaxEntries / 32;
 
 __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
@@ -526,19 +527,43 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
   for (int i = tid; i < kRowBitmapWords; i += kRowThreads) bitmap[i] = 0;
   if (tid == 0) { s_nc = 0; s_nbl = 0; s_vstar = ~0ull; }
   __syncthreads();
-  for (int64_t e = tid; e < nv; e += kRowThreads) atomicAdd(&h1[score_key(S[e]) >> 21], 1u);
+  // both passes over the row's scores keep kRowLoads loads in flight per
+  // thread (one at a time would leave each pass bound by memory latency)
+  constexpr int U = kRowLoads;
+  for (int64_t base = tid; base < nv; base += (int64_t)kRowThreads * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = base + (int64_t)u * kRowThreads;
+      v[u] = e < nv ? S[e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + (int64_t)u * kRowThreads < nv) atomicAdd(&h1[score_key(v[u]) >> 21], 1u);
+  }
   __syncthreads();
   find_threshold(h1, kHistBins, k, sm, &s_T, &s_above, &s_cnt);
   const uint32_t T = (uint32_t)s_T;
   const uint32_t need = k - s_above;
-  for (int64_t e = tid; e < nv; e += kRowThreads) {
-    const uint32_t key = score_key(S[e]);
-    const uint32_t bin = key >> 21;
-    if (bin > T) {
-      atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-    } else if (bin == T) {
-      cand[atomicAdd(&s_nc, 1u)] = ((uint64_t)(key & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
-      atomicAdd(&h2[(key >> 10) & (uint32_t)(kH2Bins - 1)], 1u);
+  for (int64_t base = tid; base < nv; base += (int64_t)kRowThreads * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = base + (int64_t)u * kRowThreads;
+      v[u] = e < nv ? S[e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = base + (int64_t)u * kRowThreads;
+      if (e >= nv) continue;
+      const uint32_t key = score_key(v[u]);
+      const uint32_t bin = key >> 21;
+      if (bin > T) {
+        atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+      } else if (bin == T) {
+        cand[atomicAdd(&s_nc, 1u)] = ((uint64_t)(key & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
+        atomicAdd(&h2[(key >> 10) & (uint32_t)(kH2Bins - 1)], 1u);
+      }
     }
   }
   __syncthreads();  // the candidate list (global, this block's) and h2 are complete
