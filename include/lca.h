@@ -154,24 +154,28 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
 /* Compression + indexer scores for one decode step: the compression of the entries the newest
  * tokens complete and the index scores, in one launch.  Equivalent to
  *     lca_kv_compress({idx_stream} + kv_streams, tok_off, done_len, ...)
- *     lca_csa_index_score(..., Tq = 1, ...)
- * (one query row per sequence): the new indexer keys are pooled, stored and
- * scored by blocks of their own, the entries that existed before by the
- * scoring blocks, and the kv_streams (entries only the attention reads, such
- * as the CSA and HCA KV entries) by further blocks of the same launch; no
- * block reads what another writes.  The caches written are bit-identical to
- * lca_kv_compress's; the new entries' scores agree within rounding order.
- * Falls back to those two calls where the fused launch does not apply: fp32,
- * d_I not in {32, 64, 128, 256}, an indexer window other than w = m or
- * w = 2m <= 16, kv streams wider than 512 bf16 channels.
+ *     lca_csa_index_score(..., Tq, ...)
+ * with Tq query rows per sequence (1, or a few -- such as a step that checks
+ * a drafted token beside the main one, the multi-token prediction of
+ * "DeepSeek-V4", Inference efficiency): the new indexer keys are pooled,
+ * stored and scored (for every row that sees them) by blocks of their own,
+ * the entries that existed before by the scoring blocks, and the kv_streams
+ * (entries only the attention reads, such as the CSA and HCA KV entries) by
+ * further blocks of the same launch; no block reads what another writes.
+ * With 2 <= Tq <= 4 and Tq * H_I <= 16 the rows of a sequence share one read
+ * of the keys (one matrix-core product scores them all).  The caches written
+ * are bit-identical to lca_kv_compress's; the new entries' scores agree
+ * within rounding order.  Falls back to those two calls where the fused
+ * launch does not apply: fp32, d_I not in {32, 64, 128, 256}, an indexer
+ * window other than w = m or w = 2m <= 16, kv streams wider than 512 bf16
+ * channels, Tq > 1 outside the shared-read bounds above.
  *   idx_stream  the indexer-key stream: out == ikey, ent_off == csa_off,
  *               C == d_I, same m and w
  *   kv_streams  0 to 4 further streams sharing one vector width
  *   tok_off, done_len  as lca_kv_compress (done_len required)
- * Other arguments as lca_csa_index_score with Tq = 1; the workspace as
- * lca_csa_index_score's. */
+ * Other arguments, and the workspace, as lca_csa_index_score's. */
 int lca_csa_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
-                               const int32_t* q_pos, int B, int H_I, int d_I, int k, int m, int w,
+                               const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
                                int64_t max_entries, const lca_compress_stream* idx_stream,
                                const lca_compress_stream* kv_streams, int n_kv, const int64_t* tok_off,
                                const int64_t* done_len, float eps, float* scores, void* ws, size_t ws_bytes,

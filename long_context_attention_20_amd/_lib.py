@@ -79,7 +79,7 @@ def _load():
     L.lca_csa_index_score.restype = i32
     L.lca_csa_index_score.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, sz, i32, vp]
     L.lca_csa_index_score_append.restype = i32
-    L.lca_csa_index_score_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+    L.lca_csa_index_score_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64,
                                              ctypes.POINTER(CompressStream), ctypes.POINTER(CompressStream), i32,
                                              vp, vp, f32, vp, vp, sz, i32, vp]
     L.lca_csa_topk_select.restype = i32

@@ -30,7 +30,7 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
                        const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
                        float* scores, void* ws, int dtype, hipStream_t stream);
 int launch_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
-                              const int32_t* q_pos, int B, int HI, int dI, int k, int m, int w, int64_t maxN,
+                              const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
                               const lca_compress_stream* idx_stream, const lca_compress_stream* kv_streams, int n_kv,
                               const int64_t* tok_off, const int64_t* done_len, float eps, float* scores, void* ws,
                               int dtype, hipStream_t stream);
@@ -185,12 +185,12 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
 }
 
 int lca_csa_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
-                               const int32_t* q_pos, int B, int H_I, int d_I, int k, int m, int w,
+                               const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
                                int64_t max_entries, const lca_compress_stream* idx_stream,
                                const lca_compress_stream* kv_streams, int n_kv, const int64_t* tok_off,
                                const int64_t* done_len, float eps, float* scores, void* ws, size_t ws_bytes,
                                int dtype, void* stream) {
-  int rc = check_index("csa_index_score_append", true, p, omega, ikey, csa_off, q_pos, B, 1, H_I, d_I, k, m, w,
+  int rc = check_index("csa_index_score_append", true, p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w,
                        max_entries, ws, ws_bytes, dtype);
   if (rc != LCA_OK) return rc;
   LCA_REQUIRE(idx_stream != nullptr && tok_off != nullptr && done_len != nullptr, LCA_ERR_INVALID_ARG,
@@ -207,7 +207,7 @@ int lca_csa_index_score_append(const void* p, const float* omega, const void* ik
   if (rc == LCA_OK && n_kv > 0) rc = check_streams(kv_streams, n_kv, dtype);
   if (rc != LCA_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  return finish(launch_index_score_append(p, omega, ikey, csa_off, q_pos, B, H_I, d_I, k, m, w, max_entries,
+  return finish(launch_index_score_append(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries,
                                           idx_stream, kv_streams, n_kv, tok_off, done_len, eps, scores, ws, dtype,
                                           st),
                 st, "csa_index_score_append");

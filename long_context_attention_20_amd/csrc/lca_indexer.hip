@@ -171,15 +171,122 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
   score_chunk_mfma<KS>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
 }
 
+// Several query rows of one sequence (a decode step with Tq > 1, as when a
+// draft token is verified beside the main one): block (cx, b) scores entries
+// [cx*chunk, ...) for all Tq rows of sequence b from one read of the keys.
+// The rows share the matrix-core A operand: row q's head h is A row q*HI + h
+// (Tq * HI <= 16, so they fit the 16 rows that one head set pads to).  Each
+// accumulator lane adds the weighted ReLU terms of its four A rows into the
+// partial of the row they belong to; the partials are summed over the four
+// lane groups and lane group q stores row q's score.  lh: TQ * kHistBins
+// words of LDS, one histogram per row.
+template <int KS, int TQ>
+__device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, int cx, int64_t lim, uint32_t* lh) {
+  static_assert(TQ >= 2 && TQ <= 4, "2 to 4 rows per block");
+  const int nq = a.Tq;  // <= TQ, nq * HI <= 16 (checked by the host)
+  const int r0 = b * a.Tq;
+  const int64_t e_base = a.csa_off[b];
+  const int64_t nseq = a.csa_off[b + 1] - e_base;
+  const int64_t c0 = (int64_t)cx * a.chunk;
+  int64_t c1q[TQ];
+  bool hq[TQ];
+  int64_t c1 = c0;
+#pragma unroll
+  for (int q = 0; q < TQ; ++q) {
+    const int64_t nv = q < nq ? row_visible(a, r0 + q, nseq) : 0;
+    c1q[q] = min(min(c0 + a.chunk, nv), lim);
+    hq[q] = q < nq && nv > a.k && !a.no_hist;
+    c1 = max(c1, c1q[q]);
+  }
+  if (cx == 0)
+    for (int q = 0; q < nq; ++q) clear_row_state(a, r0 + q);
+  if (c0 >= c1) return;
+  for (int i = threadIdx.x; i < TQ * kHistBins; i += blockDim.x) lh[i] = 0;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nrow = nq * a.HI;  // A rows in use
+  // A operand: A row `col` = (row col / HI, head col % HI), zero beyond nrow
+  bf16x8_t A[KS];
+  {
+    const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p) + (int64_t)r0 * a.HI * a.dI;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (col < nrow) v = *reinterpret_cast<const uint4*>(P + col * a.dI + ks * 32 + grp * 8);
+      A[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // weights of the accumulator rows this lane holds (A rows 4*grp + i),
+  // sorted by the query row they belong to
+  float om[TQ][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = grp * 4 + i;
+    const float wgt = m < nrow ? a.omega[(int64_t)r0 * a.HI + m] : 0.f;
+    const int qm = m / a.HI;
+#pragma unroll
+    for (int q = 0; q < TQ; ++q) om[q][i] = qm == q ? wgt : 0.f;
+  }
+  __syncthreads();
+
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.ikey) + e_base * a.dI;
+  constexpr int U = 8;  // tiles in flight per wave
+  const int64_t ntile = (c1 - c0 + 15) / 16;
+  const int nw = (int)(blockDim.x >> 6);
+  for (int64_t t0 = wave * U; t0 < ntile; t0 += nw * U) {
+    uint4 kv[U][KS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t e = c0 + (t0 + u) * 16 + col;
+      if (e >= c1) e = c1 - 1;  // clamp: stays inside the visible entries
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(K + e * a.dI + ks * 32 + grp * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], __builtin_bit_cast(bf16x8_t, kv[u][ks]), acc, 0, 0, 0);
+      const int64_t e = c0 + (t0 + u) * 16 + col;
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = fmaf(om[q][i], fmaxf(acc[i], 0.f), part);
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        if (grp == q && t0 + u < ntile && e < c1q[q]) {
+          a.scores[(int64_t)(r0 + q) * a.max_entries + e] = part;
+          if (hq[q]) hist_add(lh + q * kHistBins, part);
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < TQ; ++q)
+    if (hq[q]) hist_flush(lh + q * kHistBins, a.hist + ((int64_t)(r0 + q) * a.nstripe + cx % a.nstripe) * kHistBins);
+}
+
+template <int KS, int TQ>
+__global__ __launch_bounds__(kIdxThreads) void index_score_multi(IndexParams a) {
+  __shared__ uint32_t lh[TQ * kHistBins];
+  score_chunk_multi<KS, TQ>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
+}
+
 // ------------------------------------------------------------------ score + append
-// One decode launch that also appends the entries the new token completes:
+// One decode launch that also appends the entries the new tokens complete:
 //   blocks [0, ncb):             the compression blocks of the other streams
 //                                (KV entries that only the attention reads);
 //   blocks [ncb, ncb + B):       per sequence, pool each new indexer key,
-//                                store it, and score it against the row's
-//                                indexer query (adding it to the histogram);
+//                                store it, and score it against the indexer
+//                                query of each of the sequence's rows that
+//                                sees it (adding it to that row's histogram);
 //   blocks [ncb + B, ... + nsb): scores of the entries that existed before
-//                                the token (as index_score_mfma).
+//                                the tokens (as index_score_mfma, or
+//                                index_score_multi for Tq > 1 rows).
 // Blocks are dispatched in index order, so the few long compression blocks
 // start first and overlap the scoring.  No block reads what another block of
 // the launch writes.
@@ -189,7 +296,7 @@ struct AppendIdx {
   const int64_t* done_len;
   int ncb;                  // compression blocks
   int nsb;                  // score blocks
-  int nsx;                  // score blocks per row
+  int nsx;                  // score blocks per sequence
   int B;
   float eps;
 };
@@ -210,21 +317,17 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
   const int G = s.C / VE;                  // lanes per entry (4 .. 32)
   const int RG = (int)blockDim.x / G;
   const int rg = threadIdx.x / G, li = threadIdx.x % G;
-  const int r = b;                         // one query row per sequence
   const int64_t t0 = ap.tok_off[b];
   const int64_t e_base = a.csa_off[b];
-  const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - e_base);
+  const int64_t nseq = a.csa_off[b + 1] - e_base;
   // every entry the tokens complete is appended (as the compression kernel
-  // does); the visible ones are scored
+  // does); each of the sequence's query rows scores the ones it sees
   const int64_t n_hi = n_windows(ap.tok_off[b + 1] - t0, s.m, s.w);
   const int64_t n_lo = n_windows(ap.done_len[b], s.m, s.w);
-  const bool do_hist = nv > a.k && !a.no_hist;
   const int64_t rb = (int64_t)s.C * 2;
   const char* src = reinterpret_cast<const char*>(s.src) + t0 * rb;
   const char* lg = reinterpret_cast<const char*>(s.logits) + (s.per_channel ? t0 * rb : t0 * 2);
   const int ch0 = li * VE;
-  // indexer query of this row for this lane's channels, all heads
-  const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p) + (int64_t)r * a.HI * a.dI;
   for (int64_t j0 = n_lo; j0 < n_hi; j0 += RG) {
     const int64_t j = j0 + rg;
     const bool on = j < n_hi;              // uniform over a row group
@@ -268,27 +371,37 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
     const uint4 kq = BF16::pack(key);
     if (on) stg16(s.out, (e_base + j) * rb + ch0 * 2, kq);
     BF16::unpack(kq, key);                 // the stored (rounded) key is the one scored
-    float score = 0.f;
-    for (int h = 0; h < a.HI; ++h) {
-      float pv[VE];
-      BF16::unpack(*reinterpret_cast<const uint4*>(P + h * a.dI + ch0), pv);
-      float d = 0.f;
+    for (int q = 0; q < a.Tq; ++q) {
+      const int r = b * a.Tq + q;
+      const int64_t nv = row_visible(a, r, nseq);
+      const bool do_hist = nv > a.k && !a.no_hist;
+      // indexer query of row r for this lane's channels, all heads
+      const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p) + (int64_t)r * a.HI * a.dI;
+      float score = 0.f;
+      for (int h = 0; h < a.HI; ++h) {
+        float pv[VE];
+        BF16::unpack(*reinterpret_cast<const uint4*>(P + h * a.dI + ch0), pv);
+        float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < VE; ++e) d = fmaf(pv[e], key[e], d);
-      d = group_sum_n(d, G);
-      score = fmaf(a.omega[(int64_t)r * a.HI + h], fmaxf(d, 0.f), score);
-    }
-    if (on && j < nv && li == 0) {
-      a.scores[(int64_t)r * a.max_entries + j] = score;
-      if (do_hist)
-        atomicAdd(&a.hist[((int64_t)r * a.nstripe + (int)(j % a.nstripe)) * kHistBins + (score_key(score) >> 21)], 1u);
+        for (int e = 0; e < VE; ++e) d = fmaf(pv[e], key[e], d);
+        d = group_sum_n(d, G);
+        score = fmaf(a.omega[(int64_t)r * a.HI + h], fmaxf(d, 0.f), score);
+      }
+      if (on && j < nv && li == 0) {
+        a.scores[(int64_t)r * a.max_entries + j] = score;
+        if (do_hist)
+          atomicAdd(&a.hist[((int64_t)r * a.nstripe + (int)(j % a.nstripe)) * kHistBins + (score_key(score) >> 21)],
+                    1u);
+      }
     }
   }
 }
 
-template <int KS>
+// TQ: query rows per sequence the score blocks take at once (1: one row;
+// 2 or 4: all Tq <= TQ rows of a sequence, as score_chunk_multi).
+template <int KS, int TQ>
 __global__ __launch_bounds__(kIdxThreads) void index_score_append(IndexParams a, AppendIdx ap, CompressParams cp) {
-  extern __shared__ uint32_t dyn[];  // max(histogram, compression) words
+  extern __shared__ uint32_t dyn[];  // max(histograms, compression) words
   const int blk = blockIdx.x;
   if (blk < ap.ncb) {
     // 8-token batches and no prefetching keep the register budget of the
@@ -298,9 +411,12 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_append(IndexParams a,
     append_and_score(a, ap, blk - ap.ncb);
   } else {
     const int sb = blk - ap.ncb - ap.B;
-    const int r = sb / ap.nsx, cx = sb % ap.nsx;
-    const int b = r / a.Tq;
-    score_chunk_mfma<KS>(a, r, cx, n_windows(ap.done_len[b], a.m, a.w), dyn);
+    const int b = sb / ap.nsx, cx = sb % ap.nsx;
+    const int64_t lim = n_windows(ap.done_len[b], a.m, a.w);
+    if constexpr (TQ == 1)
+      score_chunk_mfma<KS>(a, b, cx, lim, dyn);
+    else
+      score_chunk_multi<KS, TQ>(a, b, cx, lim, dyn);
   }
 }
 
@@ -356,6 +472,8 @@ constexpr int kRowsEntriesPerWave = 256;
 constexpr int kRowMaxEntries = 98304;  // entries per row the one-block selection takes
 
 static bool rows_mode(int Tq, int64_t maxN) { return Tq >= kRowsPerBlock && maxN <= kRowMaxEntries; }
+// the rows of a sequence share one score block (score_chunk_multi)
+static bool multi_rows_ok(int Tq, int HI) { return Tq >= 2 && Tq <= 4 && Tq * HI <= 16; }
 
 template <int KS, int HI>
 __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
@@ -732,6 +850,21 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
 #undef LCA_ROWS
     return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
   }
+  if (mfma && multi_rows_ok(Tq, HI) && !a.no_hist) {
+    // a few rows per sequence: all of them from one read of the keys
+    dim3 g((unsigned)((maxN + a.chunk - 1) / a.chunk), (unsigned)B);
+#define LCA_MULTI(KSv)                                                                                   \
+  if (Tq == 2) hipLaunchKernelGGL((index_score_multi<KSv, 2>), g, dim3(kIdxThreads), 0, stream, a);    \
+  else hipLaunchKernelGGL((index_score_multi<KSv, 4>), g, dim3(kIdxThreads), 0, stream, a);
+    switch (dI / 32) {
+      case 1: LCA_MULTI(1) break;
+      case 2: LCA_MULTI(2) break;
+      case 4: LCA_MULTI(4) break;
+      default: LCA_MULTI(8) break;
+    }
+#undef LCA_MULTI
+    return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+  }
   if (mfma) {
     switch (dI / 32) {
       case 1: hipLaunchKernelGGL((index_score_mfma<1>), g1, dim3(kIdxThreads), 0, stream, a); break;
@@ -752,16 +885,16 @@ int launch_compress(const lca_compress_stream* streams, int n, const int64_t* to
                     int B, float eps, int dtype, hipStream_t stream);
 
 int launch_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
-                              const int32_t* q_pos, int B, int HI, int dI, int k, int m, int w, int64_t maxN,
+                              const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
                               const lca_compress_stream* idx_stream, const lca_compress_stream* kv_streams, int n_kv,
                               const int64_t* tok_off, const int64_t* done_len, float eps, float* scores, void* ws,
                               int dtype, hipStream_t stream) {
-  // the fused launch: bf16 matrix-core scores, one query row per sequence,
-  // KV streams of at most 512 bf16 channels; anything else runs as the two
-  // launches it stands for
+  // the fused launch: bf16 matrix-core scores, one query row per sequence or
+  // a few sharing a score block, KV streams of at most 512 bf16 channels;
+  // anything else runs as the two launches it stands for
   const bool fused = dtype == LCA_BF16 && HI <= 16 && (dI == 32 || dI == 64 || dI == 128 || dI == 256) &&
                      idx_stream->C == dI && idx_stream->m == m && idx_stream->w == w &&
-                     (w == m || w == 2 * m) && w <= 16;
+                     (w == m || w == 2 * m) && w <= 16 && (Tq == 1 || multi_rows_ok(Tq, HI));
   CompressParams cp{};
   int64_t cblocks = 0;
   size_t clds = 0;
@@ -781,9 +914,9 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
     int rc = launch_compress(all, 1, tok_off, done_len, B, eps, dtype, stream);
     if (rc == LCA_OK && n_kv > 0) rc = launch_compress(all + 1, n_kv, tok_off, done_len, B, eps, dtype, stream);
     if (rc != LCA_OK) return rc;
-    return launch_index_score(p, omega, ikey, csa_off, q_pos, B, 1, HI, dI, k, m, w, maxN, scores, ws, dtype, stream);
+    return launch_index_score(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, scores, ws, dtype, stream);
   }
-  IndexParams a = make_params(p, omega, ikey, csa_off, q_pos, B, 1, HI, dI, k, m, w, maxN, nullptr, scores, ws);
+  IndexParams a = make_params(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, nullptr, scores, ws);
   AppendIdx ap{};
   const lca_compress_stream& in = *idx_stream;
   ap.s.src = in.src; ap.s.logits = in.logits; ap.s.out = in.out; ap.s.ent_off = in.ent_off;
@@ -801,14 +934,23 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
     set_error("csa_index_score_append: grid too large (%lld blocks)", (long long)blocks);
     return LCA_ERR_UNSUPPORTED;
   }
-  const size_t lds = clds > kHistBins * 4 ? clds : kHistBins * 4;
+  const int tq = Tq == 1 ? 1 : Tq == 2 ? 2 : 4;  // rows a score block takes
+  const size_t hist_lds = (size_t)tq * kHistBins * 4;
+  const size_t lds = clds > hist_lds ? clds : hist_lds;
   dim3 grid((unsigned)blocks);
-  switch (dI / 32) {
-    case 1: hipLaunchKernelGGL((index_score_append<1>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
-    case 2: hipLaunchKernelGGL((index_score_append<2>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
-    case 4: hipLaunchKernelGGL((index_score_append<4>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
-    default: hipLaunchKernelGGL((index_score_append<8>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break;
+#define LCA_APPEND(KSv)                                                                                          \
+  switch (tq) {                                                                                                  \
+    case 1: hipLaunchKernelGGL((index_score_append<KSv, 1>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
+    case 2: hipLaunchKernelGGL((index_score_append<KSv, 2>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
+    default: hipLaunchKernelGGL((index_score_append<KSv, 4>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
   }
+  switch (dI / 32) {
+    case 1: LCA_APPEND(1) break;
+    case 2: LCA_APPEND(2) break;
+    case 4: LCA_APPEND(4) break;
+    default: LCA_APPEND(8) break;
+  }
+#undef LCA_APPEND
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 

@@ -131,20 +131,21 @@ def csa_index_score_append(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: in
                            ws: torch.Tensor, idx_stream: dict, kv_streams: Sequence[dict], tok_off: torch.Tensor,
                            done_len: torch.Tensor, eps: float = 1e-6, scores: Optional[torch.Tensor] = None):
     """kv_compress of the indexer-key stream and kv_streams (entries completed
-    after done_len tokens) and csa_index_score for one query row per
-    sequence, in one launch."""
+    after done_len tokens) and csa_index_score for the Tq query rows of each
+    sequence (q_pos holds B * Tq positions), in one launch."""
     _dev(p, omega, ikey, csa_off, q_pos, ws, scores, tok_off, done_len)
     _i64(tok_off, "tok_off")
     _i64(done_len, "done_len")
     B = csa_off.numel() - 1
-    if q_pos.numel() != B:
-        raise ValueError("one query row per sequence")
+    rows = q_pos.numel()
+    if rows % B:
+        raise ValueError("q_pos must hold the same number of rows for every sequence")
     if len(kv_streams) > 4:
         raise ValueError("0..4 kv streams per call")
     ia, _ = _stream_array([idx_stream])
     ka, _ = _stream_array(kv_streams)
     check(lib.lca_csa_index_score_append(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B,
-                                         p.shape[-2], p.shape[-1], k, m, w, int(max_entries), ia, ka,
+                                         rows // B, p.shape[-2], p.shape[-1], k, m, w, int(max_entries), ia, ka,
                                          len(kv_streams), _ptr(tok_off), _ptr(done_len), float(eps), _ptr(scores),
                                          _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(p), _stream()),
           "csa_index_score_append")

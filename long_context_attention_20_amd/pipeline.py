@@ -273,7 +273,8 @@ class HybridAttention:
                 streams = self.compress_streams(caches, raw, done_h, lens_h=lens_h)
                 idx_st = [st for st in streams if st["out"] is caches.ikey]
                 kv_st = [st for st in streams if st["out"] is not caches.ikey]
-                if idx_st and q.shape[0] == len(caches.lens):
+                rows_per_seq = q.shape[0] // len(caches.lens)
+                if idx_st and (rows_per_seq == 1 or (rows_per_seq <= 4 and rows_per_seq * self.HI <= 16)):
                     ops.csa_index_score_append(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w,
                                                bufs["max_csa"], bufs["ws_idx"], idx_st[0], kv_st, tok_off, done_len,
                                                self.eps)

@@ -206,15 +206,17 @@ def test_index_score_append_rejects(L):
     kv[0] = L.CompressStream(512, 512, 512, 512, 512, 4, 8, 1, 1, 1)
     kv[1] = L.CompressStream(512, 512, 512, 768, 512, 128, 128, 1, 1, 1)
 
-    def call(idx_s=idx, kv_s=kv, n_kv=2, done=P, dI=64, ws_bytes=need, eps=1e-6):
-        return lib.lca_csa_index_score_append(P, P, P, P, P, 1, 4, dI, 512, 4, 8, 1000, idx_s, kv_s, n_kv, P, done,
-                                              eps, None, P, ws_bytes, 1, None)
+    def call(idx_s=idx, kv_s=kv, n_kv=2, done=P, dI=64, ws_bytes=need, eps=1e-6, tq=1):
+        return lib.lca_csa_index_score_append(P, P, P, P, P, 1, tq, 4, dI, 512, 4, 8, 1000, idx_s, kv_s, n_kv, P,
+                                              done, eps, None, P, ws_bytes, 1, None)
     assert call(idx_s=None) == L.LCA_ERR_INVALID_ARG
     assert call(done=None) == L.LCA_ERR_INVALID_ARG
     assert call(n_kv=5) == L.LCA_ERR_INVALID_ARG
     assert call(kv_s=None) == L.LCA_ERR_INVALID_ARG
     assert call(ws_bytes=need - 1) == L.LCA_ERR_WORKSPACE
     assert call(eps=-1.0) == L.LCA_ERR_INVALID_ARG
+    assert call(tq=0) == L.LCA_ERR_INVALID_ARG
+    assert call(tq=2) == L.LCA_ERR_WORKSPACE          # two rows need a larger workspace
     idx[0] = L.CompressStream(256, 256, 512, 256, 64, 4, 8, 1, 0, 1)    # writes somewhere other than ikey
     assert call() == L.LCA_ERR_INVALID_ARG
     idx[0] = L.CompressStream(256, 256, 256, 256, 32, 4, 8, 1, 0, 1)    # C != d_I

@@ -489,6 +489,104 @@ def test_decode_step_at_earlier_position(p):
     assert_close(f64(out)[0], res["out"], cfg.dtype, f"position {p}")
 
 
+
+@pytest.mark.parametrize("tq,HI,dI", [(2, 4, 64), (3, 4, 64), (4, 4, 64), (4, 2, 32), (2, 1, 128)])
+def test_index_score_multi_rows_match_single_rows(tq, HI, dI):
+    """Tq query rows per sequence scored from one read of the keys (the rows
+    share the matrix-core operand): every row's scores are bit-identical to
+    scoring that row alone, and the selections that read the per-row
+    histograms are the same sets, on sequences spanning several score blocks,
+    a ragged tail and rows that see one entry more than the row before."""
+    from long_context_attention_20_amd import ops
+    cfg = li.small(f"multi{tq}", 120, (9000, 4101, 2052, 13), tq=tq, H=16, D=64, HI=HI, dI=dI, k=256)
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    maxN = ocmp.n_entries(max(cfg.lens), cfg.m, cfg.w)
+    rows = cfg.B * tq
+    print(f"[multi-row scores] tq={tq} HI={HI} dI={dI} lens={cfg.lens}", flush=True)
+    ws = layer.index_workspace(rows, maxN, "cuda")
+    scores = torch.full((rows, maxN), float("nan"), dtype=torch.float32, device="cuda")
+    ops.csa_index_score(d["p"], d["omega"], caches.ikey, caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w, maxN, ws,
+                        scores=scores)
+    idx = ops.csa_topk_select(caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w, maxN, ws, scores=scores)
+    torch.cuda.synchronize()
+    qp = raw["q_pos"]
+    for t in range(tq):
+        sel = torch.arange(cfg.B, device="cuda") * tq + t
+        ws1 = layer.index_workspace(cfg.B, maxN, "cuda")
+        s1 = torch.full((cfg.B, maxN), float("nan"), dtype=torch.float32, device="cuda")
+        q1 = d["q_pos"][sel].contiguous()
+        ops.csa_index_score(d["p"][sel].contiguous(), d["omega"][sel].contiguous(), caches.ikey, caches.csa_off, q1,
+                            cfg.k, cfg.m, cfg.w, maxN, ws1, scores=s1)
+        i1 = ops.csa_topk_select(caches.csa_off, q1, cfg.k, cfg.m, cfg.w, maxN, ws1, scores=s1)
+        torch.cuda.synchronize()
+        for b in range(cfg.B):
+            nv = ocmp.n_entries(int(qp[b, t]) + 1, cfg.m, cfg.w)
+            got = scores[b * tq + t, :nv].cpu().numpy()
+            one = s1[b, :nv].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), one.view(np.uint32)), f"row ({b}, {t}): scores differ"
+            a = idx[b * tq + t].cpu().numpy()
+            a1 = i1[b].cpu().numpy()
+            assert np.array_equal(np.sort(a[a >= 0]), np.sort(a1[a1 >= 0])), f"row ({b}, {t}): selections differ"
+    # and against the oracle's scores
+    co = caches.csa_off_h
+    for b in range(cfg.B):
+        keys = f64(caches.ikey[int(co[b]):int(co[b + 1])])
+        for t in range(tq):
+            r = b * tq + t
+            nv = ocmp.n_entries(int(qp[b, t]) + 1, cfg.m, cfg.w)
+            ref = oidx.scores(f64(d["p"][r]), raw["omega"][r].astype(np.float64), keys[:nv])
+            bound = score_bound(f64(d["p"][r]), raw["omega"][r].astype(np.float64), keys[:nv])
+            err = np.abs(scores[r, :nv].cpu().numpy().astype(np.float64) - ref)
+            assert np.all(err <= 2 * bound + 1e-6), f"row ({b}, {t}): scores off the oracle"
+
+
+@pytest.mark.parametrize("tq", [2, 3])
+def test_decode_step_mtp(tq):
+    """A decode step with tq query rows per sequence (the main token and
+    drafted ones, checked together): the appends of every entry the tq new
+    tokens complete, the multi-row scores, the selection inside the attention
+    launch and the merge, against the oracle row by row.  The sequences'
+    last tokens complete no entry, a CSA/indexer entry, and an HCA entry."""
+    cfg = li.small(f"mtp{tq}", 121, (4001, 2600, 777, 4096), tq=tq, H=64, D=512, k=256)
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    full = (caches.kv_csa.clone(), caches.ikey.clone(), caches.kv_hca.clone())
+    done_h = [L - tq for L in cfg.lens]
+    wiped = []
+    for b, L in enumerate(cfg.lens):
+        for t, off, m, w in ((caches.kv_csa, caches.csa_off_h, cfg.m, cfg.w),
+                             (caches.ikey, caches.csa_off_h, cfg.m, cfg.w),
+                             (caches.kv_hca, caches.hca_off_h, cfg.m2, cfg.w2)):
+            n0, n1 = ocmp.n_entries(L - tq, m, w), ocmp.n_entries(L, m, w)
+            t[int(off[b]) + n0:int(off[b]) + n1] = 0
+            wiped.append(n1 - n0)
+    done = torch.tensor(done_h, dtype=torch.int64, device="cuda")
+    qmax = max(cfg.lens)
+    bufs = layer.decode_buffers(cfg.B * tq, ocmp.n_entries(qmax, cfg.m, cfg.w), ocmp.n_entries(qmax, cfg.m2, cfg.w2),
+                                "cuda", tdtype(cfg))
+    print(f"[mtp decode] tq={tq} lens={cfg.lens} appended={wiped}", flush=True)
+    out = layer.decode_step(caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs,
+                            done_len=done, done_h=done_h)
+    torch.cuda.synchronize()
+    for got, ref, name in zip((caches.kv_csa, caches.ikey, caches.kv_hca), full, ("kv_csa", "ikey", "kv_hca")):
+        assert torch.equal(got, ref), f"{name}: the step did not restore exactly the entries the new tokens complete"
+    _, ores = opipe.run(raw, cfg)
+    idx_h = bufs["idx"].cpu().numpy()
+    out_h = f64(out)
+    for b in range(cfg.B):
+        for t in range(tq):
+            r = b * tq + t
+            res = ores[(b, t)]
+            assert set(idx_h[r][idx_h[r] >= 0].tolist()) == set(res["sel"].tolist()), f"row ({b}, {t}) selection"
+            assert_close(out_h[r], res["out"], cfg.dtype, f"mtp row ({b}, {t})")
+
 def _topk_direct(ikey, p, omega, k, n_entries):
     """csa_index_topk over one row whose query sees every entry of ikey."""
     from long_context_attention_20_amd import ops
