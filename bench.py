@@ -79,6 +79,7 @@ def measured_traffic(workload, kernel):
     return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 FLOP/s, MI355X
 MALL_BYTES = 256 << 20
+MTP_MAX_ROWS = 4           # query rows per sequence timed as a decode step (more: a prefill chunk)
 
 
 def n_windows(L, m, w):
@@ -86,24 +87,30 @@ def n_windows(L, m, w):
 
 
 def step_bytes(cfg):
-    """Algorithmic HBM bytes of one decode step: what the method must move."""
+    """Algorithmic HBM bytes of one decode step: what the method must move.
+    With tq query rows per sequence the indexer keys, the HCA entries and the
+    window rows are read once for all of them; each row has its own
+    selection, query and output."""
     e = 2 if cfg.dtype == "bf16" else 4
+    tq = cfg.tq
     tot = 0
     for L in cfg.lens:
         ncsa = n_windows(L, cfg.m, cfg.w)
         nh = n_windows(L, cfg.m2, cfg.w2)
         kk = min(cfg.k, ncsa)
         tot += ncsa * cfg.dI * e                        # indexer keys
-        tot += kk * (cfg.D * e + 4)                     # selected entries + indices
-        tot += min(cfg.W, L) * cfg.D * e                # window rows
+        tot += tq * kk * (cfg.D * e + 4)                # selected entries + indices, per row
+        tot += min(cfg.W + tq - 1, L) * cfg.D * e       # window rows
         tot += nh * cfg.D * e                           # HCA entries
-        tot += cfg.H * cfg.D * 2 * e + cfg.H * 4        # q, out, sink
+        tot += tq * (cfg.H * cfg.D * 2 * e + cfg.H * 4)  # q, out, sink per row
     return tot
 
 
 def kernel_cost(cfg, name):
-    """(bytes, flops) that one launch of a step's kernel must move / do."""
+    """(bytes, flops) that one launch of a step's kernel must move / do (keys
+    shared by the tq rows of a sequence counted once)."""
     e = 2 if cfg.dtype == "bf16" else 4
+    tq = cfg.tq
     by = fl = 0
     for L in cfg.lens:
         ncsa = n_windows(L, cfg.m, cfg.w)
@@ -126,15 +133,15 @@ def kernel_cost(cfg, name):
             fl += 4 * cfg.H * cfg.D * nwin
         elif name == "hybrid_attn":                      # the top-k selection + the three branches
             nwin = min(cfg.W, L)
-            by += ncsa * 4 + kk * 4                            # every score read, selection written
-            by += (kk + nh + nwin) * cfg.D * e + cfg.H * cfg.D * e
-            fl += 4 * cfg.H * cfg.D * (kk + nh + nwin)
+            by += tq * (ncsa * 4 + kk * 4)                     # every score read, selection written
+            by += (tq * kk + nh + min(cfg.W + tq - 1, L)) * cfg.D * e + tq * cfg.H * cfg.D * e
+            fl += 4 * cfg.H * cfg.D * (kk + nh + nwin) * tq
         elif name == "swa_merge":
-            by += cfg.H * cfg.D * e + cfg.H * 4                # output + sink
-        elif name == "csa_index_score_append":                 # scores + the entries one token completes
+            by += tq * (cfg.H * cfg.D * e + cfg.H * 4)         # output + sink
+        elif name == "csa_index_score_append":                 # scores + the entries the new tokens complete
             by += ncsa * cfg.dI * e
             by += (2 * cfg.w * cfg.D + 2 * cfg.w * cfg.dI + 2 * cfg.w2 * cfg.D) * e + (2 * cfg.D + cfg.dI) * e
-            fl += 2 * ncsa * cfg.dI * cfg.HI
+            fl += 2 * ncsa * cfg.dI * cfg.HI * tq
     return by, fl
 
 
@@ -151,22 +158,23 @@ class LayerState:
         self.q, self.p, self.omega, self.sigma = raw["q"], raw["p"], raw["omega"], raw["sigma"]
         self.q_pos = raw["q_pos"].reshape(-1).contiguous()
         self.tok_off = raw["tok_off"]
-        self.done_h = [L - 1 for L in cfg.lens]
+        self.done_h = [L - cfg.tq for L in cfg.lens]
         self.done = torch.tensor(self.done_h, dtype=torch.int64, device=dev)
 
 
 class Position:
-    """A decode step of a one-sequence workload at token position p: the
-    sequence is read as its first p + 1 tokens, so the step appends exactly
-    the entries token p completes and the query sees positions 0 .. p."""
+    """A decode step of a one-sequence workload ending at token position p:
+    the sequence is read as its first p + 1 tokens and the step's tq query
+    rows sit at positions p - tq + 1 .. p, so the step appends exactly the
+    entries those tokens complete."""
 
-    def __init__(self, p, dev):
+    def __init__(self, p, dev, tq=1):
         import torch
         self.p = p
         self.tok_off = torch.tensor([0, p + 1], dtype=torch.int64, device=dev)
-        self.q_pos = torch.tensor([p], dtype=torch.int32, device=dev)
-        self.done = torch.tensor([p], dtype=torch.int64, device=dev)
-        self.done_h = [p]
+        self.q_pos = torch.arange(p - tq + 1, p + 1, dtype=torch.int32, device=dev)
+        self.done = torch.tensor([p + 1 - tq], dtype=torch.int64, device=dev)
+        self.done_h = [p + 1 - tq]
         self.lens_h = [p + 1]
 
 
@@ -338,29 +346,34 @@ def cpu_baseline(cfg, state, budget_s):
     x, a, g, u, c = host(raw["x"]), host(raw["a"]), host(raw["g"]), host(raw["u"]), host(raw["c"])
     caches = opipe.build_seq_caches(x, a, g, u, c, cfg)
     build_s = time.perf_counter() - t0
-    q = raw["q"][0].float().cpu().numpy().astype(np.float64)
-    p = raw["p"][0].float().cpu().numpy().astype(np.float64)
-    om = raw["omega"][0].cpu().numpy().astype(np.float64)
+    tq = cfg.tq
+    rows = []
+    for t in range(tq):
+        r = b * tq + t
+        rows.append((raw["q"][r].float().cpu().numpy().astype(np.float64),
+                     raw["p"][r].float().cpu().numpy().astype(np.float64),
+                     raw["omega"][r].cpu().numpy().astype(np.float64), L - tq + t))
     sg = raw["sigma"].cpu().numpy().astype(np.float64)
-    i = L - 1
     n = 0
     t0 = time.perf_counter()
     while True:
-        # append: the entries the newest token completes
+        # append: the entries the step's tokens complete
         for m, w, src, lg, norm, name in ((cfg.m, cfg.w, x, a, True, "kv_csa"), (cfg.m, cfg.w, u, c, False, "ikey"),
                                           (cfg.m2, cfg.w2, x, g, True, "kv_hca")):
-            new = range(ocmp.n_entries(L - 1, m, w), ocmp.n_entries(L, m, w))
+            new = range(ocmp.n_entries(L - tq, m, w), ocmp.n_entries(L, m, w))
             if len(new):
                 getattr(caches, name)[list(new)] = onum.round_to(ocmp.compress(src, lg, m, w, norm, cfg.eps, new),
                                                                  cfg.dtype)
-        opipe.query_step(caches, x, q, p, om, sg, i, cfg)
+        for q, p, om, i in rows:
+            opipe.query_step(caches, x, q, p, om, sg, i, cfg)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 1000:
             break
-    return {"value": n / el, "unit": "q-tok/s/layer", "cores": threads,
+    where = f"1 query at position {L - 1}" if tq == 1 else f"{tq} queries at positions {L - tq}..{L - 1}"
+    return {"value": n * tq / el, "unit": "q-tok/s/layer", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n} decode steps of sequence 0 (1 query at position {i}) of layer 0, float64 numpy oracle "
+            "sample": f"{n} decode steps of sequence 0 ({where}) of layer 0, float64 numpy oracle "
                       f"(append + indexer + top-k + sparse + HCA + window + sink + merge) on caches it built "
                       f"itself in {build_s:.1f} s (not timed); {el:.1f} s timed",
             "seconds": round(el, 3)}
@@ -399,7 +412,7 @@ def main():
     cfg = li.CONFIGS[args.config]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    if cfg.tq != 1:
+    if cfg.tq > MTP_MAX_ROWS:
         run_prefill(cfg, args, dev)
         return
     sb = step_bytes(cfg)
@@ -450,13 +463,16 @@ def main():
           ", ".join(f"{n}={t:.4f}" for n, t in zip(run.names, per)), file=sys.stderr, flush=True)
 
     K = args.steps
-    # one sequence: the K timed steps are K consecutive decode positions
-    # L-K .. L-1 (each appends what its token completes: a CSA and an indexer
-    # entry every 4th step, an HCA entry every 128th); several sequences: every
-    # step is the last position (all three appends each step)
-    consecutive = cfg.B == 1 and cfg.lens[0] > K + args.warmup + 2 * cfg.w2
-    pos_t = [Position(cfg.lens[0] - K + it, dev) for it in range(K)] if consecutive else [None] * K
-    pos_w = [Position(cfg.lens[0] - K - args.warmup + w, dev) for w in range(args.warmup)] if consecutive \
+    # one sequence: the K timed steps are K consecutive decode steps ending at
+    # L-1, each taking the next tq tokens (each appends what its tokens
+    # complete: a CSA and an indexer entry every 4th token, an HCA entry every
+    # 128th); several sequences: every step is the last position (all three
+    # appends each step)
+    tq = cfg.tq
+    consecutive = cfg.B == 1 and cfg.lens[0] > tq * (K + args.warmup) + 2 * cfg.w2
+    last = cfg.lens[0] - 1
+    pos_t = [Position(last - tq * (K - 1 - it), dev, tq) for it in range(K)] if consecutive else [None] * K
+    pos_w = [Position(last - tq * (K + args.warmup - 1 - w), dev, tq) for w in range(args.warmup)] if consecutive \
         else [None] * args.warmup
     ms_graph = ms_last = None
     if args.graph:
@@ -511,7 +527,7 @@ def main():
     k_ms = float(per[dom])
 
     ms = ms_graph if ms_graph is not None else ms_stream
-    value = cfg.B / (ms / 1e3)
+    value = cfg.B * cfg.tq / (ms / 1e3)
     name = run.names[dom]
     kb, kf = kernel_cost(cfg, name.split("(")[0])
     if name == "hybrid_attn" and kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
@@ -531,7 +547,9 @@ def main():
         cpu = cpu_baseline(cfg, run.layers[0], args.cpu_seconds)
 
     res = {
-        "metric": "decode query-tokens/s per layer at 1M ctx (Pro shape); % of HBM peak BW",
+        "metric": ("decode query-tokens/s per layer at 1M ctx (Pro shape); % of HBM peak BW" if tq == 1 else
+                   f"decode query-tokens/s per layer at 1M ctx (Pro shape, {tq} query rows per step: the main token "
+                   f"and {tq - 1} drafted); % of HBM peak BW"),
         "value": value,
         "unit": "q-tok/s/layer",
         "n_gpus": 1,
@@ -547,8 +565,9 @@ def main():
                    f"{cfg.B} seqs, mean {int(np.mean(cfg.lens))}", "q_heads": cfg.H, "head_dim": cfg.D,
                    "indexer": f"{cfg.HI}x{cfg.dI}", "topk": cfg.k, "m": cfg.m, "m2": cfg.m2, "window": cfg.W,
                    "layers_rotated": R, "timing": "hip-graph replay" if ms_graph is not None else "stream",
-                   "positions": (f"{K} consecutive decode positions {cfg.lens[0] - K}..{cfg.lens[0] - 1}, each "
-                                 f"appending the entries its token completes") if consecutive else
+                   "query_rows_per_step": tq,
+                   "positions": (f"{K} consecutive decode steps over positions {last - tq * K + 1}..{last}, "
+                                 f"{tq} per step, each appending the entries its tokens complete") if consecutive else
                    "last position of every sequence, every append in every step"},
         "hbm_frac_of_peak": sb / (ms / 1e3) / HBM_PEAK,
         "bytes_per_step": sb,

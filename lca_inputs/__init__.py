@@ -87,7 +87,12 @@ FLASH_PREFILL = Config("flash_prefill", 3, 1, (262144 + 4096,), 4096, 64, 512, 4
 PRO_VARLEN = Config("pro_varlen", 4, 64, _varlen_lengths(4, 64, 16384, 262144), 1, 128, 512, 4, 64,
                     1024, "bf16", plant=32)
 
-CONFIGS: Dict[str, Config] = {c.name: c for c in (TINY, FLASH_DECODE, PRO_1M_DECODE, FLASH_PREFILL, PRO_VARLEN)}
+# The Pro 1M decode with two query rows per step (the main token and one
+# drafted by the multi-token-prediction module, verified together).
+PRO_1M_MTP2 = Config("pro_1m_mtp2", 5, 1, (1048576,), 2, 128, 512, 4, 64, 1024, "bf16")
+
+CONFIGS: Dict[str, Config] = {c.name: c for c in (TINY, FLASH_DECODE, PRO_1M_DECODE, FLASH_PREFILL, PRO_VARLEN,
+                                                  PRO_1M_MTP2)}
 
 
 def small(name: str, cfg_id: int, lens, tq: int = 1, H: int = 64, D: int = 512, HI: int = 4,

@@ -148,7 +148,9 @@ constexpr int kAttnThreads = 512;
 constexpr int kTeamThreads = 256;
 constexpr int kAttnHeads = 32;      // query heads per block
 
-template <int D, bool TOPK>
+// FC: filter chunks a sparse block of a TOPK source loads at its start and
+// filters in one pass (2 when the row's scores give a block more than one).
+template <int D, bool TOPK, int FC = 1>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnParams a) {
   constexpr int DH = D / 2;                 // dims per wave
   constexpr int KS = DH / 32;               // k-steps of the S partial
@@ -165,6 +167,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   constexpr size_t kTileBytes = 4 * (size_t)TILE_ELEMS * 2;
   constexpr size_t kLdsBytes = (TOPK && sizeof(SelectLds) > kTileBytes) ? sizeof(SelectLds) : kTileBytes;
   __shared__ __attribute__((aligned(16))) char lds_raw[kLdsBytes];
+  static_assert(!TOPK || sizeof(FilterShared) <= kLdsBytes, "the filter's LDS lives in the tile memory");
   auto tiles = reinterpret_cast<uint16_t(*)[2][TILE_ELEMS]>(lds_raw);
   __shared__ SelectShared sel_sh;
   __shared__ int32_t sidx[kIdxLds];
@@ -204,11 +207,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   // waiting for the position does not wait for them
   const int32_t qpos_r = kind == SRC_TOPK ? a.q_pos[r] : 0;
   SelectPrefetch<kAttnThreads> pf;
-  FilterPrefetch<kAttnThreads, kFilterPer> fpf;
+  FilterPrefetch<kAttnThreads, kFilterPer, FC> fpf;
   if constexpr (TOPK) {
     if (kind == SRC_TOPK) {
       if (a.filter)
-        filter_prefetch(a.tw, r, split * a.n_hb + hb, fpf);
+        filter_prefetch(a.tw, r, split * a.n_hb + hb, a.tbpr, fpf);
       else
         topk_prefetch(a.tw, r, pf);
     }
@@ -305,11 +308,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       // launch fits the machine at once, so they are all resident and the
       // wait ends (bounded all the same: a count that never completes leaves
       // the slots empty rather than hanging).
+      // the block's chunks are tbi, tbi + tbpr, ...; the first FC of them had
+      // their loads issued at the start and are filtered in one pass (one
+      // threshold, one list reservation)
       const int tbi = split * a.n_hb + hb;
       constexpr int64_t CH = (int64_t)kAttnThreads * kFilterPer;
-      for (int64_t cb = tbi; cb * CH < nv; cb += a.tbpr) {
-        if (cb != tbi) filter_prefetch(tw, r, (int)cb, fpf);  // the first chunk's loads went out at the start
-        filter_chunk(tw, r, nv, (int)cb, fpf, *reinterpret_cast<FilterShared*>(lds_raw));
+      for (int64_t cb = tbi; cb * CH < nv; cb += (int64_t)a.tbpr * FC) {
+        if (cb != tbi) filter_prefetch(tw, r, (int)cb, a.tbpr, fpf);
+        filter_chunk(tw, r, nv, (int)cb, a.tbpr, fpf, *reinterpret_cast<FilterShared*>(lds_raw));
         __syncthreads();
       }
       if (threadIdx.x == 0) {
@@ -1228,24 +1234,27 @@ int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int 
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
 
-// Blocks of attn_mfma<D, true> the current device holds at once (compute
-// units x blocks per unit), queried once per device and D.
-static int64_t resident_blocks(int D) {
-  static int64_t cache[64][4];
+// Blocks of attn_mfma<D, true, fc> the current device holds at once
+// (compute units x blocks per unit), queried once per device, D and fc (2 is
+// built for D = 512 only).
+static int64_t resident_blocks(int D, int fc) {
+  static int64_t cache[64][4][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int di = D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : 3;
-  if (cache[dev][di] == 0) {
+  const int fi = fc == 2 && D == 512 ? 1 : 0;
+  if (cache[dev][di][fi] == 0) {
     int cus = 0, per = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const void* fn = D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true>)
                      : D == 128 ? reinterpret_cast<const void*>(&attn_mfma<128, true>)
                      : D == 256 ? reinterpret_cast<const void*>(&attn_mfma<256, true>)
+                     : fi       ? reinterpret_cast<const void*>(&attn_mfma<512, true, 2>)
                                 : reinterpret_cast<const void*>(&attn_mfma<512, true>);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kAttnThreads, 0);
-    cache[dev][di] = (e == hipSuccess && cus > 0 && per > 0) ? (int64_t)cus * per : -1;
+    cache[dev][di][fi] = (e == hipSuccess && cus > 0 && per > 0) ? (int64_t)cus * per : -1;
   }
-  return cache[dev][di];
+  return cache[dev][di][fi];
 }
 
 // A merge to follow the attention (lca_hybrid_attn_merge): sink and output.
@@ -1273,12 +1282,17 @@ static int merge_sources(const lca_attn_source* srcs, int n_src, int rows, int H
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
 
-// Many query rows per sequence (D = 512, bf16, 128 divisible by H and at
-// least two blocks of rows): every source takes the row-tiled kernel, in one
-// launch; a gathered source (or a top-k source, selected first) needs at most
-// two queries per block (H >= 64) and at most kRowsIdx slots per split.
+// Many query rows per sequence (D = 512, bf16, 128 divisible by H, at least
+// kRowsMinTq queries and two blocks of rows): every source takes the
+// row-tiled kernel, in one launch; a gathered source (or a top-k source,
+// selected first) needs at most two queries per block (H >= 64) and at most
+// kRowsIdx slots per split.  A few rows per sequence (a decode step checking
+// drafted tokens) take the decode kernel: its blocks of 32 heads give the
+// device four times the blocks of a row tile that holds all 128 heads of one
+// query, and such a step's key ranges are too short to fill many row tiles.
+constexpr int kRowsMinTq = 8;
 static bool rows_launch(const lca_attn_source* srcs, int n_src, int Tq, int H, int D, int dtype) {
-  if (dtype != LCA_BF16 || D != 512 || H % 16 != 0 || kRowsBlockRows % H != 0 || Tq < 2 ||
+  if (dtype != LCA_BF16 || D != 512 || H % 16 != 0 || kRowsBlockRows % H != 0 || Tq < kRowsMinTq ||
       (int64_t)Tq * H < 2 * kRowsBlockRows)
     return false;
   for (int i = 0; i < n_src; ++i) {
@@ -1417,6 +1431,7 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
       return LCA_ERR_UNSUPPORTED;
     }
   }
+  int fc = 1;  // filter chunks per sparse block and pass (attn_mfma's FC)
   if (topk >= 0) {
     // the sparse blocks select from the filtered lists themselves: they also
     // filter the scores when the whole launch is resident at once (else the
@@ -1429,7 +1444,10 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
       const int64_t units = (int64_t)rows * blocks;
       const int64_t nblk = (units + 7) / 8 * 8 * a.n_hb;
       a.tbpr = in.n_split * a.n_hb;
-      a.filter = nblk <= resident_blocks(D) ? 1 : 0;
+      // two chunks per sparse block at once when the row's scores give a
+      // block more than one
+      fc = D == 512 && (int64_t)a.tbpr * kAttnThreads * kFilterPer < in.max_entries ? 2 : 1;
+      a.filter = nblk <= resident_blocks(D, fc) ? 1 : 0;
       if (!a.filter)
         rc = launch_topk_filter(in.off, q_pos, B, Tq, in.k, in.m2, in.w2, in.max_entries, in.scores, in.ws, stream);
     } else {
@@ -1448,7 +1466,12 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
       case 64: LCA_MFMA(64) break;
       case 128: LCA_MFMA(128) break;
       case 256: LCA_MFMA(256) break;
-      default: LCA_MFMA(512) break;
+      default:
+        if (fused_topk && fc == 2)
+          hipLaunchKernelGGL((attn_mfma<512, true, 2>), grid, dim3(kAttnThreads), 0, stream, a);
+        else
+          LCA_MFMA(512)
+        break;
     }
 #undef LCA_MFMA
   } else {

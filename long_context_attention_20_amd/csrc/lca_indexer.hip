@@ -20,15 +20,14 @@
 // histogram (the highest bin whose suffix count reaches k), and appends the
 // entries of its chunk above T to a per-row "selected" list and those inside T
 // (the candidates) to a per-row candidate list, reserving space with one
-// 64-bit atomic per block, and counts the candidates per next-11-bit bin in a
-// second histogram.  No block waits for another.
+// 64-bit atomic per block.  No block waits for another.
 //
 // Kernel 3 (finalize, one block per row): the exact selection of lca_topk.h
-// -- the second histogram's threshold bin, radix passes only inside it, a
-// bitmap of the chosen entries written out in ascending index order -- then
-// zeroes the first histogram for the next call.  (The sparse-attention
-// kernel can run the same selection in its own blocks instead.)  The score
-// kernels zero the counters and the second histogram.
+// -- the candidates counted per next-11-bit bin in LDS, radix passes only
+// inside the threshold bin of that count, a bitmap of the chosen entries
+// written out in ascending index order -- then zeroes the first histogram for
+// the next call.  (The sparse-attention kernel can run the same selection in
+// its own blocks instead.)  The score kernels zero the counters.
 #include "lca_compress.h"
 #include "lca_topk.h"
 
@@ -52,7 +51,6 @@ struct IndexParams {
   uint32_t* hist;           // [rows][nstripe][kHistBins]
   int nstripe;              // histogram copies (score blocks spread their atomics)
   unsigned long long* ctr;  // [rows]: selected count | candidate count << 32
-  uint32_t* hist2;          // [rows][kH2Bins]: candidates per second-level bin
   uint32_t* done;           // [rows]: blocks that finished filtering (in-launch filtering)
   int no_hist;              // 1: many rows per sequence, selected one block per row (no histograms)
   int32_t* sel;             // [rows][k]
@@ -69,10 +67,9 @@ __device__ __forceinline__ int64_t row_visible(const IndexParams& a, int r, int6
 
 // ------------------------------------------------------------------ scores
 
-// Block 0 of each row's scores zeroes the row's list counters and second
-// histogram, which the filter kernel that follows fills.
+// Block 0 of each row's scores zeroes the row's list counters, which the
+// filter that follows fills.
 __device__ __forceinline__ void clear_row_state(const IndexParams& a, int r) {
-  for (int i = threadIdx.x; i < kH2Bins; i += blockDim.x) a.hist2[(int64_t)r * kH2Bins + i] = 0;
   if (threadIdx.x == 0) {
     a.ctr[r] = 0;
     a.done[r] = 0;
@@ -561,7 +558,7 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
 
 __device__ __forceinline__ TopkWs topk_view(const IndexParams& a) {
   TopkWs w;
-  w.scores = a.scores; w.hist = a.hist; w.nstripe = a.nstripe; w.ctr = a.ctr; w.hist2 = a.hist2; w.done = a.done;
+  w.scores = a.scores; w.hist = a.hist; w.nstripe = a.nstripe; w.ctr = a.ctr; w.done = a.done;
   w.sel = a.sel; w.cand = a.cand; w.max_entries = a.max_entries; w.k = a.k;
   return w;
 }
@@ -576,8 +573,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
   if ((int64_t)cb * kSelChunk >= nv) return;
   const TopkWs w = topk_view(a);
   FilterPrefetch<kSelThreads, kSelPerThread> P;
-  filter_prefetch(w, r, cb, P);
-  filter_chunk(w, r, nv, cb, P, F);
+  filter_prefetch(w, r, cb, 1, P);
+  filter_chunk(w, r, nv, cb, 1, P, F);
 }
 
 constexpr int kFinThreads = 1024;
@@ -680,7 +677,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
         atomicOr(&bitmap[e >> 5], 1u << (e & 31));
       } else if (bin == T) {
         cand[atomicAdd(&s_nc, 1u)] = ((uint64_t)(key & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
-        atomicAdd(&h2[(key >> 10) & (uint32_t)(kH2Bins - 1)], 1u);
+        lds_count(h2, (key >> 10) & (uint32_t)(kH2Bins - 1));
       }
     }
   }
@@ -691,13 +688,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
   const uint32_t need2 = need - s_above, cnt2 = s_cnt;
   uint64_t vstar = (uint64_t)T2 << 34;
   if (cnt2 != need2 && cnt2 <= (uint32_t)kBoundaryLds) {
-    for (uint32_t i = tid; i < nc; i += kRowThreads) {
-      const uint64_t v = cand[i];
+    walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint64_t v) {
       if ((uint32_t)(v >> 34) == T2) {
         const uint32_t slot = atomicAdd(&s_nbl, 1u);
         if (slot < (uint32_t)kBoundaryLds) bl[slot] = v;
       }
-    }
+    });
     __syncthreads();
     const uint32_t nb = min(s_nbl, (uint32_t)kBoundaryLds);
     for (uint32_t i = tid; i < nb; i += kRowThreads) {
@@ -718,10 +714,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
       const int sft = shifts[pass], nbins = 1 << widths[pass];
       for (int i = tid; i < nbins; i += kRowThreads) h1[i] = 0;
       __syncthreads();
-      for (uint32_t i = tid; i < nc; i += kRowThreads) {
-        const uint64_t v = cand[i];
-        if ((v & mask) == prefix) atomicAdd(&h1[(uint32_t)(v >> sft) & (uint32_t)(nbins - 1)], 1u);
-      }
+      walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint64_t v) {
+        if ((v & mask) == prefix) lds_count(h1, (uint32_t)(v >> sft) & (uint32_t)(nbins - 1));
+      });
       __syncthreads();
       find_threshold(h1, nbins, nd, sm, &s_T, &s_above, &s_cnt);
       prefix |= (uint64_t)(uint32_t)s_T << sft;
@@ -733,13 +728,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
     }
     vstar = prefix;
   }
-  for (uint32_t i = tid; i < nc; i += kRowThreads) {
-    const uint64_t v = cand[i];
+  walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint64_t v) {
     if (v >= vstar) {
       const uint32_t e = 0xFFFFFFu - (uint32_t)(v & 0xFFFFFFu);
       atomicOr(&bitmap[e >> 5], 1u << (e & 31));
     }
-  }
+  });
   __syncthreads();
   // ascending order: the chosen entries before each thread's words, then its bits
   constexpr int WPT = kRowBitmapWords / kRowThreads;
@@ -769,7 +763,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
 // ------------------------------------------------------------------ host
 
 struct IndexWs {
-  size_t scores, hist, ctr, done, hist2, sel, cand, total;
+  size_t scores, hist, ctr, done, sel, cand, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -791,7 +785,6 @@ static IndexWs index_ws_layout(int rows, int64_t maxN, int k) {
   w.hist = o;     o = align256(o + (size_t)rows * hist_stripes(rows, maxN) * kHistBins * 4);
   w.ctr = o;      o = align256(o + (size_t)rows * 8);
   w.done = o;     o = align256(o + (size_t)rows * 4);
-  w.hist2 = o;    o = align256(o + (size_t)rows * kH2Bins * 4);
   w.scores = o;   o = align256(o + (size_t)rows * maxN * 4);
   w.sel = o;      o = align256(o + (size_t)rows * k * 4);
   w.cand = o;     o = align256(o + (size_t)rows * maxN * 8);
@@ -813,7 +806,6 @@ static IndexParams make_params(const void* p, const float* omega, const void* ik
   a.scores = scores ? const_cast<float*>(scores) : reinterpret_cast<float*>(base + L.scores);
   a.hist = reinterpret_cast<uint32_t*>(base + L.hist);
   a.ctr = reinterpret_cast<unsigned long long*>(base + L.ctr);
-  a.hist2 = reinterpret_cast<uint32_t*>(base + L.hist2);
   a.done = reinterpret_cast<uint32_t*>(base + L.done);
   a.sel = reinterpret_cast<int32_t*>(base + L.sel);
   a.cand = reinterpret_cast<uint64_t*>(base + L.cand);
@@ -960,7 +952,7 @@ void topk_ws_view(int rows, int64_t maxN, int k, const float* scores, void* ws, 
   IndexParams a = make_params(nullptr, nullptr, nullptr, nullptr, nullptr, rows, 1, 1, 8, k, 1, 1, maxN, nullptr,
                               scores, ws);
   view->scores = a.scores; view->hist = a.hist; view->nstripe = a.nstripe; view->ctr = a.ctr;
-  view->hist2 = a.hist2; view->done = a.done; view->sel = a.sel; view->cand = a.cand; view->max_entries = maxN; view->k = k;
+  view->done = a.done; view->sel = a.sel; view->cand = a.cand; view->max_entries = maxN; view->k = k;
 }
 
 int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,

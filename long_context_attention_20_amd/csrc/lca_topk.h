@@ -8,16 +8,15 @@
 //
 // Keys: score_key maps a float score to a 32-bit integer of the same order.
 // The score kernels build a histogram of the top 11 key bits; the filter
-// kernel finds the bin T holding the k-th largest, appends every entry above
-// T to a per-row list `sel` (exactly `above` entries), every entry inside T to
-// a candidate list as the packed value
+// finds the bin T holding the k-th largest, appends every entry above T to a
+// per-row list `sel` (exactly `above` entries) and every entry inside T to a
+// candidate list as the packed value
 //     (key & 0x1FFFFF) << 24 | (0xFFFFFF - entry)
-// (a total order: larger key first, then smaller entry), and counts the
-// candidates per next-11-bit bin (bits 20..10 of the key) in a second
-// histogram.  Selecting then needs the k - above largest packed candidates:
-// the second histogram gives their bin T2 without a pass over the
-// candidates, and only the candidates inside T2 (usually very few) need the
-// exact radix passes over their low 34 bits.
+// (a total order: larger key first, then smaller entry).  Selecting then
+// needs the k - above largest packed candidates: the selection counts the
+// candidates per next-11-bit bin (bits 20..10 of the key) in LDS, which gives
+// their bin T2, and only the candidates inside T2 (usually very few) need
+// the exact radix passes over their low 34 bits.
 #pragma once
 #include "lca_common.h"
 
@@ -84,7 +83,6 @@ struct TopkWs {
   uint32_t* hist;                // [rows][nstripe][kHistBins]
   int nstripe;
   unsigned long long* ctr;       // [rows]: sel count | candidate count << 32
-  uint32_t* hist2;               // [rows][kH2Bins]
   uint32_t* done;                // [rows]: blocks that finished filtering the row
   int32_t* sel;                  // [rows][k]
   uint64_t* cand;                // [rows][max_entries]
@@ -101,20 +99,22 @@ struct FilterShared {
   unsigned long long base;
 };
 
-// The loads of one filter chunk (histogram stripes and the chunk's scores,
-// clamped to the row's columns), issued together; a caller can start them
-// before it knows how many of the scores are visible.
-template <int NT, int PER>
+// The loads of NC filter chunks of a row (histogram stripes and the chunks'
+// scores, clamped to the row's columns), issued together; a caller can start
+// them before it knows how many of the scores are visible.  Chunk c is chunk
+// number cb0 + c * stride of the row (NT * PER scores each).
+template <int NT, int PER, int NC = 1>
 struct FilterPrefetch {
   static constexpr int kMaxStripes = 8;
   static constexpr int HV = kHistBins / 4 / NT;  // uint4 per thread and stripe
   uint4 hs[kMaxStripes][HV];
-  float sv[PER];
+  float sv[NC][PER];
 };
 
-template <int NT, int PER>
-__device__ __forceinline__ void filter_prefetch(const TopkWs& w, int r, int cb, FilterPrefetch<NT, PER>& P) {
-  using FP = FilterPrefetch<NT, PER>;
+template <int NT, int PER, int NC>
+__device__ __forceinline__ void filter_prefetch(const TopkWs& w, int r, int cb0, int stride,
+                                                FilterPrefetch<NT, PER, NC>& P) {
+  using FP = FilterPrefetch<NT, PER, NC>;
   static_assert(FP::HV * 4 * NT == kHistBins, "the histogram must split evenly over the block");
   const uint4* gh = reinterpret_cast<const uint4*>(w.hist + (int64_t)r * w.nstripe * kHistBins);
 #pragma unroll
@@ -123,25 +123,31 @@ __device__ __forceinline__ void filter_prefetch(const TopkWs& w, int r, int cb, 
     for (int i = 0; i < FP::HV; ++i)
       P.hs[st][i] = st < w.nstripe ? gh[st * (kHistBins / 4) + threadIdx.x + i * NT] : make_uint4(0, 0, 0, 0);
   const float* S = w.scores + (int64_t)r * w.max_entries;
-  const int64_t e0 = (int64_t)cb * NT * PER + (int64_t)threadIdx.x * PER;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t e = e0 + i;
-    P.sv[i] = S[e < w.max_entries ? e : w.max_entries - 1];
+  for (int c = 0; c < NC; ++c) {
+    const int64_t base = (int64_t)(cb0 + c * stride) * NT * PER;
+    if (c > 0 && base >= w.max_entries) continue;  // past every row's columns: never visible (uniform)
+    const int64_t e0 = base + (int64_t)threadIdx.x * PER;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int64_t e = e0 + i;
+      P.sv[c][i] = S[e < w.max_entries ? e : w.max_entries - 1];
+    }
   }
 }
 
-// The filter of one chunk of NT * PER scores of row r (k < nv, the chunk
-// starts below nv) from its prefetched loads: the threshold bin T from the
-// row's histogram (summed over its stripes), then every entry of the chunk
-// above T appended to sel, every entry inside T to the candidate list (packed
-// as above) and counted in the second histogram.  The list space comes from
-// one 64-bit atomic on ctr.
-template <int NT, int PER>
-__device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb, const FilterPrefetch<NT, PER>& P,
-                             FilterShared& F) {
-  using FP = FilterPrefetch<NT, PER>;
-  const int64_t e0 = (int64_t)cb * NT * PER + (int64_t)threadIdx.x * PER;
+// The filter of NC chunks of row r (k < nv; the first chunk starts below
+// nv) from their prefetched loads: the threshold bin T from the row's
+// histogram (summed over its stripes), then every entry of the chunks above T
+// appended to sel and every entry inside T to the candidate list (packed as
+// above).  The list space comes from one 64-bit atomic on ctr for all the
+// chunks.  No per-candidate counting here: with many equal scores (a row
+// whose head weights are all negative scores thousands of entries exactly 0)
+// per-candidate atomics would all hit one word.
+template <int NT, int PER, int NC>
+__device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb0, int stride,
+                             const FilterPrefetch<NT, PER, NC>& P, FilterShared& F) {
+  using FP = FilterPrefetch<NT, PER, NC>;
 #pragma unroll
   for (int i = 0; i < FP::HV; ++i) {
     uint4 v = P.hs[0][i];
@@ -155,15 +161,19 @@ __device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb, const F
   find_threshold(F.h, kHistBins, (uint32_t)w.k, F.sm, &F.T, &F.above, &F.cnt);
   const uint32_t T = (uint32_t)F.T;
 
-  uint32_t keys[PER];
+  uint32_t keys[NC][PER];
   uint32_t ns = 0, nc = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const bool in = e0 + i < nv;
-    keys[i] = score_key(P.sv[i]);
-    const uint32_t bin = keys[i] >> 21;
-    ns += (in && bin > T) ? 1u : 0u;
-    nc += (in && bin == T) ? 1u : 0u;
+  for (int c = 0; c < NC; ++c) {
+    const int64_t e0 = (int64_t)(cb0 + c * stride) * NT * PER + (int64_t)threadIdx.x * PER;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool in = e0 + i < nv;
+      keys[c][i] = score_key(P.sv[c][i]);
+      const uint32_t bin = keys[c][i] >> 21;
+      ns += (in && bin > T) ? 1u : 0u;
+      nc += (in && bin == T) ? 1u : 0u;
+    }
   }
   uint32_t tot;
   const uint32_t pos = block_excl_scan(ns | (nc << 16), &tot, F.sm);  // both counts < 2^16
@@ -175,18 +185,21 @@ __device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb, const F
   int32_t* selr = w.sel + (int64_t)r * w.k;
   uint64_t* candr = w.cand + (int64_t)r * w.max_entries;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t e = e0 + i;
-    if (e >= nv) continue;
-    const uint32_t bin = keys[i] >> 21;
-    if (bin > T) {
-      if (ps < (uint32_t)w.k) selr[ps] = (int32_t)e;
-      ++ps;
-    } else if (bin == T) {
-      if (pc < (uint32_t)w.max_entries)
-        candr[pc] = ((uint64_t)(keys[i] & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
-      ++pc;
-      atomicAdd(&w.hist2[(int64_t)r * kH2Bins + ((keys[i] >> 10) & (uint32_t)(kH2Bins - 1))], 1u);
+  for (int c = 0; c < NC; ++c) {
+    const int64_t e0 = (int64_t)(cb0 + c * stride) * NT * PER + (int64_t)threadIdx.x * PER;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int64_t e = e0 + i;
+      if (e >= nv) continue;
+      const uint32_t bin = keys[c][i] >> 21;
+      if (bin > T) {
+        if (ps < (uint32_t)w.k) selr[ps] = (int32_t)e;
+        ++ps;
+      } else if (bin == T) {
+        if (pc < (uint32_t)w.max_entries)
+          candr[pc] = ((uint64_t)(keys[c][i] & 0x1FFFFFu) << 24) | (uint64_t)(0xFFFFFFu - (uint32_t)e);
+        ++pc;
+      }
     }
   }
 }
@@ -200,6 +213,37 @@ __device__ __forceinline__ int64_t topk_visible(int64_t i, int m, int w, int64_t
 }
 
 constexpr int kBoundaryLds = 256;  // threshold-bin candidates ranked directly
+
+// h[bin] += 1 for every active lane: when all active lanes of the wave count
+// the same bin (equal scores, the crowded case) one lane adds their number,
+// else each lane adds its own (LDS atomics on one word serialize).
+__device__ __forceinline__ void lds_count(uint32_t* h, uint32_t bin) {
+  const uint32_t first = __builtin_amdgcn_readfirstlane(bin);
+  const uint64_t act = __ballot(1);
+  if (__ballot(bin == first) == act) {
+    if ((int)(threadIdx.x & 63) == __ffsll((long long)act) - 1) atomicAdd(&h[first], (uint32_t)__popcll(act));
+  } else {
+    atomicAdd(&h[bin], 1u);
+  }
+}
+
+// f(ptr[j]) for j = j0, j0 + stride, ... below n, with U loads in flight per
+// thread: a walk over a list in global memory is bound by load latency, and
+// a crowded threshold bin (many equal scores) makes the candidate list long.
+template <int U, typename T, typename F>
+__device__ __forceinline__ void walk_loads(const T* ptr, uint32_t j0, uint32_t n, uint32_t stride, F f) {
+  for (uint32_t j = j0; j < n; j += stride * U) {
+    T v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t jj = j + u * stride;
+      v[u] = jj < n ? ptr[jj] : T{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j + u * stride < n) f(v[u]);
+  }
+}
 
 // LDS of topk_row_select (66 KB): radix histogram (for a crowded threshold
 // bin), chosen-entry bitmap, chosen entries before each bitmap word, and the
@@ -218,16 +262,13 @@ struct SelectShared {
 };
 
 // The loads of topk_row_select whose addresses do not depend on the list
-// counts (the counts, the second histogram, the selected list and the first
-// candidates), issued together: a caller can start them before anything
+// counts (the counts, the selected list and the first candidates), issued together: a caller can start them before anything
 // else it needs, and pass them in.
 template <int NT>
 struct SelectPrefetch {
-  static constexpr int HPT = kH2Bins / NT;  // second-level bins per thread
   static constexpr int SPT = 4096 / NT;     // selected-list slots per thread (k <= 4096)
   static constexpr int CPT = 2048 / NT;     // candidates per thread before the count is known
   unsigned long long cnt;
-  uint32_t hv[HPT];
   int32_t sv[SPT];
   uint64_t cv[CPT];
 };
@@ -236,9 +277,6 @@ template <int NT>
 __device__ __forceinline__ void topk_prefetch(const TopkWs& w, int r, SelectPrefetch<NT>& P) {
   const int tid = threadIdx.x;
   P.cnt = w.ctr[r];
-  const uint32_t* h2 = w.hist2 + (int64_t)r * kH2Bins;
-#pragma unroll
-  for (int i = 0; i < SelectPrefetch<NT>::HPT; ++i) P.hv[i] = h2[tid * SelectPrefetch<NT>::HPT + i];
   const int32_t* selr = w.sel + (int64_t)r * w.k;
 #pragma unroll
   for (int i = 0; i < SelectPrefetch<NT>::SPT; ++i) {
@@ -257,7 +295,9 @@ template <int NT, bool ORDERED, class Emit>
 __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch<NT>& P, SelectLds& L,
                                     SelectShared& S, Emit emit) {
   constexpr int NW = NT / 64;
-  constexpr int HPT = SelectPrefetch<NT>::HPT, SPT = SelectPrefetch<NT>::SPT, CPT = SelectPrefetch<NT>::CPT;
+  constexpr int SPT = SelectPrefetch<NT>::SPT, CPT = SelectPrefetch<NT>::CPT;
+  constexpr int HPT = kH2Bins / NT;  // second-level bins per thread
+  static_assert(HPT * NT == kH2Bins, "the second-level bins must split evenly over the block");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t k = (uint32_t)w.k;
   const uint64_t* cg = w.cand + (int64_t)r * w.max_entries;
@@ -268,26 +308,24 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
   const bool consistent = n_sel < k && (uint64_t)n_sel + ncands >= k && ncands <= (uint64_t)w.max_entries;
   if (!consistent) return 0;
   const uint32_t need = k - n_sel;
-  // this thread's candidates: the prefetched ones, then (rarely) the rest
-  // straight from global memory
+  // this thread's candidates: the prefetched ones, then (a crowded
+  // threshold bin) the rest straight from global memory
   auto for_cands = [&](auto f) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
       if ((uint32_t)(tid + i * NT) < ncands) f(P.cv[i]);
-    for (uint32_t j = tid + CPT * NT; j < ncands; j += NT) f(cg[j]);
+    walk_loads<8>(cg, (uint32_t)(tid + CPT * NT), ncands, (uint32_t)NT, f);
   };
 
-  // 1. bin T2 of the second histogram (held in registers: thread t has bins
-  // t*HPT ..) whose suffix count reaches need: one block scan
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < HPT; ++i) mine += P.hv[i];
-  const uint32_t inc = wave_incl_scan(mine);
-  if (lane == 63) S.sm[wave] = inc;
+  // 1. the candidates per second-level bin (key bits 20..10, the top bits
+  // of the packed value's low 34), counted in LDS; then the bin T2 whose
+  // suffix count reaches need: one block scan (thread t holds bins t*HPT ..)
+  for (int i = tid; i < kH2Bins; i += NT) L.h[i] = 0;
   if (tid == 0) { S.T = 0; S.above = 0; S.cnt = 0; S.fill = 0; S.nbl = 0; S.vstar = ~0ull; }
   if (ORDERED)
     for (int i = tid; i < kBitmapWords; i += NT) L.bitmap[i] = 0;
   __syncthreads();
+  for_cands([&](uint64_t v) { lds_count(L.h, (uint32_t)(v >> 34) & (uint32_t)(kH2Bins - 1)); });
   if (ORDERED) {
     // the selected list is chosen whole
 #pragma unroll
@@ -296,6 +334,17 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
       if ((uint32_t)(tid + i * NT) < n_sel && e < (uint32_t)kBitmapEntries) atomicOr(&L.bitmap[e >> 5], 1u << (e & 31));
     }
   }
+  __syncthreads();
+  uint32_t hv[HPT];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
+    hv[i] = L.h[tid * HPT + i];
+    mine += hv[i];
+  }
+  const uint32_t inc = wave_incl_scan(mine);
+  if (lane == 63) S.sm[wave] = inc;
+  __syncthreads();
   {
     uint32_t later = 0;  // bins of the waves after this one
 #pragma unroll
@@ -305,7 +354,7 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
       uint32_t acc = above_mine;
 #pragma unroll
       for (int i = HPT - 1; i >= 0; --i) {
-        const uint32_t c = P.hv[i];
+        const uint32_t c = hv[i];
         if (acc < need && acc + c >= need) {
           S.T = tid * HPT + i;
           S.above = acc;
@@ -330,7 +379,7 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
       }
     });
     __syncthreads();
-    // (a count other than cnt2 means an inconsistent second histogram: the
+    // (a count other than cnt2 means an inconsistent candidate list: the
     // chosen total then differs from k and the row is rejected below)
     const uint32_t nb = min(S.nbl, (uint32_t)kBoundaryLds);
     for (uint32_t i = tid; i < nb; i += NT) {
@@ -352,7 +401,7 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
       for (int i = tid; i < nb; i += NT) L.h[i] = 0;
       __syncthreads();
       for_cands([&](uint64_t v) {
-        if ((v & mask) == prefix) atomicAdd(&L.h[(uint32_t)(v >> sft) & (uint32_t)(nb - 1)], 1u);
+        if ((v & mask) == prefix) lds_count(L.h, (uint32_t)(v >> sft) & (uint32_t)(nb - 1));
       });
       __syncthreads();
       find_threshold(L.h, nb, nd, S.sm, &S.T, &S.above, &S.cnt);

@@ -140,13 +140,20 @@ class HybridAttention:
         want = max(1, -(-256 // (rows * hg)))
         return int(max(1, min(want, tiles // 4 if tiles >= 4 else 1, 256)))
 
-    def fused_splits(self, rows: int, n_csa: int, n_hca: int, n_win: int, select: bool = False):
+    # the row's scores a sparse block filters in one pass when it selects:
+    # chunks of 512 threads x 8 scores, two chunks loaded at the block's start
+    FILTER_PASS_SCORES = 2 * 512 * 8
+
+    def fused_splits(self, rows: int, n_csa: int, n_hca: int, n_win: int, select: bool = False,
+                     n_scores: int = 0):
         """Splits of the three sources of one fused launch: the blocks of all
         sources take about the same number of 32-key tiles (an even number,
         one per team and round), the fewest that let one wave of blocks (one
         per compute unit) cover the launch when the rows allow it.  With
         select, the sparse blocks also run the top-k selection (about as long
-        as four tiles of attention) and take four tiles fewer."""
+        as four tiles of attention) and take four tiles fewer, and there are
+        enough of them that each filters its share of the row's n_scores
+        scores in one pass."""
         hg = (self.H + 31) // 32
         if rows * hg >= 256:
             # the rows alone give the device a wave of blocks (and the dense
@@ -154,12 +161,18 @@ class HybridAttention:
             return (1, 1, 1)
         tiles = [max(1, (n + 31) // 32) for n in (n_csa, n_hca, n_win)]
         budget = max(3, 256 // max(1, rows * hg))
-        for per in range(2, 34, 2):
-            pc = max(2, per - 4) if select else per
-            units = -(-tiles[0] // pc) + -(-tiles[1] // per) + -(-tiles[2] // per)
+        sc_min = -(-n_scores // (self.FILTER_PASS_SCORES * hg)) if select else 1
+        for floor in (sc_min, 1):  # a floor that does not fit the budget is dropped
+            for per in range(2, 34, 2):
+                pc = max(2, per - 4) if select else per
+                sc = max(-(-tiles[0] // pc), floor)
+                units = sc + -(-tiles[1] // per) + -(-tiles[2] // per)
+                if units <= budget:
+                    break
             if units <= budget:
                 break
-        return tuple(int(min(256, max(1, -(-t // q)))) for t, q in zip(tiles, (pc, per, per)))
+        return (int(min(256, max(1, sc))), int(min(256, max(1, -(-tiles[1] // per)))),
+                int(min(256, max(1, -(-tiles[2] // per)))))
 
     def step(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, q: torch.Tensor, p: torch.Tensor,
              omega: torch.Tensor, sigma: Optional[torch.Tensor], q_pos: torch.Tensor, q_pos_h: np.ndarray,
@@ -209,7 +222,8 @@ class HybridAttention:
         """Preallocated outputs of decode_step (so that the step can be
         captured in a HIP graph and replayed)."""
         f32 = torch.float32
-        sc, sh, sw = self.fused_splits(rows, min(self.k, max(1, max_csa)), max_hca, self.W, select=True)
+        sc, sh, sw = self.fused_splits(rows, min(self.k, max(1, max_csa)), max_hca, self.W, select=True,
+                                       n_scores=max_csa)
         sc = self.split_csa or sc
         sh = self.split_hca or sh
         part = lambda n: (torch.empty((n, rows, self.H, self.D), dtype=f32, device=device),

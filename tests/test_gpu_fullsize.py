@@ -25,19 +25,21 @@ def _host(t):
     return t.float().cpu().numpy()
 
 
-def _run(cfg):
+def _run(cfg, side=True):
+    """One decode step of every sequence over its last cfg.tq tokens (the
+    entries they complete appended by the step, the rest built first)."""
     raw = li.make_raw_torch(cfg, 0, "cuda")
     layer = layer_for(cfg)
     caches = layer.alloc_caches(cfg.lens, "cuda", raw["x"].dtype)
     layer.compress(caches, raw, raw["tok_off"])
     q_pos = raw["q_pos"].reshape(-1).contiguous()
-    done_h = [L - 1 for L in cfg.lens]
+    done_h = [L - cfg.tq for L in cfg.lens]
     done = torch.tensor(done_h, dtype=torch.int64, device="cuda")
     qmax = max(cfg.lens)
-    bufs = layer.decode_buffers(cfg.B, ocmp.n_entries(qmax, cfg.m, cfg.w), ocmp.n_entries(qmax, cfg.m2, cfg.w2),
-                                "cuda", raw["x"].dtype)
+    bufs = layer.decode_buffers(cfg.B * cfg.tq, ocmp.n_entries(qmax, cfg.m, cfg.w),
+                                ocmp.n_entries(qmax, cfg.m2, cfg.w2), "cuda", raw["x"].dtype)
     out = layer.decode_step(caches, raw, raw["tok_off"], raw["q"], raw["p"], raw["omega"], raw["sigma"], q_pos, bufs,
-                            done_len=done, done_h=done_h, side=torch.cuda.Stream())
+                            done_len=done, done_h=done_h, side=torch.cuda.Stream() if side else None)
     torch.cuda.synchronize()
     return raw, layer, caches, bufs, out
 
@@ -65,39 +67,47 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
         entj = sorted(set(rng.choice(nhca, size=min(16, nhca), replace=False).tolist()) | {nhca - 1})
         ref = onum.round_to(ocmp.compress(x, g, cfg.m2, cfg.w2, True, cfg.eps, entj), cfg.dtype)
         assert np.max(np.abs(kv_hca[entj] - ref)) <= 2e-2
-        # ---- scores and top-k: every visible entry scored in float64 from the GPU-stored keys
-        i = L - 1
-        p = f64(raw["p"][b])
-        om = raw["omega"][b].cpu().numpy().astype(np.float64)
-        s_ref = oidx.scores(p, om, ikey)
-        bound = score_bound(p, om, ikey)
-        sel = idx_h[b]
-        chosen = sel[sel >= 0]
-        assert len(chosen) == min(cfg.k, ncsa)
-        assert np.all(np.diff(chosen) > 0)
-        ref_sel = oidx.topk(s_ref, cfg.k)
-        kth = s_ref[ref_sel[-1]]
-        diff = set(chosen.tolist()) ^ set(ref_sel.tolist())
-        for j in diff:
-            assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + bound[j], f"entry {j} is not a near tie"
-        print(f"  top-{cfg.k}: {len(diff)} near-tie differences", flush=True)
-        # ---- attention, window, sink and merge stage-wise (GPU caches and selection), all heads
-        qhat = oatt.normalize_query(f64(raw["q"][b]), cfg.eps, cfg.dtype)
-        csa = oatt.partial(qhat, kv_csa[chosen], cfg.scale)
-        hca = oatt.partial(qhat, kv_hca[:nhca], cfg.scale)
-        win = oatt.normalize_tokens(x[max(0, i - cfg.W + 1):i + 1].astype(np.float64), cfg.eps, cfg.dtype)
-        swa = oatt.partial(qhat, win, cfg.scale)
-        sig = raw["sigma"].cpu().numpy().astype(np.float64)
-        o_ref, _ = oatt.merge([csa, hca, swa], sig)
-        assert_close(out_h[b], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"{cfg.name} row {b}")
-        # ---- end to end: oracle keys from raw inputs, if the selected sets agree
-        if not diff:
-            ikey_o = onum.round_to(ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps), cfg.dtype)
-            sel_o = oidx.topk(oidx.scores(p, om, ikey_o), cfg.k)
-            kv_sel = onum.round_to(ocmp.compress(x, a, cfg.m, cfg.w, True, cfg.eps, sorted(sel_o)), cfg.dtype)
-            kv_h = onum.round_to(ocmp.compress(x, g, cfg.m2, cfg.w2, True, cfg.eps), cfg.dtype)
-            o_e2e, _ = oatt.merge([oatt.partial(qhat, kv_sel, cfg.scale), oatt.partial(qhat, kv_h, cfg.scale), swa], sig)
-            assert_close(out_h[b], onum.round_to(o_e2e, cfg.dtype), cfg.dtype, f"{cfg.name} row {b} e2e")
+        ikey_o = None
+        for t in range(cfg.tq):
+            # ---- scores and top-k of row (b, t): every visible entry scored in
+            # float64 from the GPU-stored keys
+            r = b * cfg.tq + t
+            i = L - cfg.tq + t
+            nv, nh = ocmp.n_visible(i, cfg.m, cfg.w), ocmp.n_visible(i, cfg.m2, cfg.w2)
+            p = f64(raw["p"][r])
+            om = raw["omega"][r].cpu().numpy().astype(np.float64)
+            s_ref = oidx.scores(p, om, ikey[:nv])
+            bound = score_bound(p, om, ikey[:nv])
+            sel = idx_h[r]
+            chosen = sel[sel >= 0]
+            assert len(chosen) == min(cfg.k, nv)
+            assert np.all(np.diff(chosen) > 0)
+            ref_sel = oidx.topk(s_ref, cfg.k)
+            kth = s_ref[ref_sel[-1]]
+            diff = set(chosen.tolist()) ^ set(ref_sel.tolist())
+            for j in diff:
+                assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + bound[j], f"entry {j} is not a near tie"
+            print(f"  row {t} (position {i}): top-{cfg.k}, {len(diff)} near-tie differences", flush=True)
+            # ---- attention, window, sink and merge stage-wise (GPU caches and
+            # selection), all heads
+            qhat = oatt.normalize_query(f64(raw["q"][r]), cfg.eps, cfg.dtype)
+            csa = oatt.partial(qhat, kv_csa[chosen], cfg.scale)
+            hca = oatt.partial(qhat, kv_hca[:nh], cfg.scale)
+            win = oatt.normalize_tokens(x[max(0, i - cfg.W + 1):i + 1].astype(np.float64), cfg.eps, cfg.dtype)
+            swa = oatt.partial(qhat, win, cfg.scale)
+            sig = raw["sigma"].cpu().numpy().astype(np.float64)
+            o_ref, _ = oatt.merge([csa, hca, swa], sig)
+            assert_close(out_h[r], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"{cfg.name} row ({b}, {t})")
+            # ---- end to end: oracle keys from raw inputs, if the selected sets agree
+            if not diff:
+                if ikey_o is None:
+                    ikey_o = onum.round_to(ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps), cfg.dtype)
+                sel_o = oidx.topk(oidx.scores(p, om, ikey_o[:nv]), cfg.k)
+                kv_sel = onum.round_to(ocmp.compress(x, a, cfg.m, cfg.w, True, cfg.eps, sorted(sel_o)), cfg.dtype)
+                kv_h = onum.round_to(ocmp.compress(x, g, cfg.m2, cfg.w2, True, cfg.eps, list(range(nh))), cfg.dtype)
+                o_e2e, _ = oatt.merge([oatt.partial(qhat, kv_sel, cfg.scale), oatt.partial(qhat, kv_h, cfg.scale),
+                                       swa], sig)
+                assert_close(out_h[r], onum.round_to(o_e2e, cfg.dtype), cfg.dtype, f"{cfg.name} row ({b}, {t}) e2e")
 
 
 def test_flash_decode_full():
@@ -110,6 +120,15 @@ def test_pro_1m_decode_full():
     cfg = li.PRO_1M_DECODE
     raw, layer, caches, bufs, out = _run(cfg)
     _check_rows(cfg, raw, caches, bufs, out, [0], np.random.default_rng(2))
+
+
+def test_pro_1m_mtp2_full():
+    """The Pro 1M decode with two query rows per step (positions L-2 and
+    L-1), in the configuration the benchmark times for it: the appends inside
+    the multi-row scoring launch, the selection inside the attention launch."""
+    cfg = li.PRO_1M_MTP2
+    raw, layer, caches, bufs, out = _run(cfg, side=False)
+    _check_rows(cfg, raw, caches, bufs, out, [0], np.random.default_rng(4))
 
 
 def test_pro_varlen_full():

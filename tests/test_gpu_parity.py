@@ -587,6 +587,82 @@ def test_decode_step_mtp(tq):
             assert set(idx_h[r][idx_h[r] >= 0].tolist()) == set(res["sel"].tolist()), f"row ({b}, {t}) selection"
             assert_close(out_h[r], res["out"], cfg.dtype, f"mtp row ({b}, {t})")
 
+
+@pytest.mark.parametrize("path", ["decode_two_rows", "many_rows"])
+def test_topk_crowded_zero_ties(path):
+    """Rows whose indexer head weights are all negative: every score is <= 0,
+    and the entries whose four head products are all <= 0 score exactly 0 --
+    thousands of exact ties at the k-th score, more candidates than the
+    selection holds in registers, so its passes walk the candidate list in
+    memory.  The k chosen are the smallest indices among the ties (the exact
+    top-k of the GPU scores; against the oracle, differences only at near
+    ties), in the decode path (two rows per step, the selection inside the
+    attention launch; outputs checked stage-wise) and the many-row path."""
+    from long_context_attention_20_amd import ops
+    tq, H = (2, 64) if path == "decode_two_rows" else (40, 16)
+    cfg = li.small(f"ties_{path}", 122, (200000,), tq=tq, H=H, D=512, k=512)
+    raw = li.make_raw_torch(cfg, 0, "cuda")
+    neg = [0] if tq == 2 else list(range(0, tq, 4))
+    for r in neg:
+        raw["omega"][r] = -raw["omega"][r].abs()
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", raw["x"].dtype)
+    layer.compress(caches, raw, raw["tok_off"])
+    q_pos = raw["q_pos"].reshape(-1).contiguous()
+    L = cfg.lens[0]
+    maxN = ocmp.n_entries(L, cfg.m, cfg.w)
+    print(f"[crowded ties {path}] L={L} entries={maxN} rows={tq} all-negative rows={neg}", flush=True)
+    s_gpu = torch.empty((tq, maxN), dtype=torch.float32, device="cuda")
+    if path == "decode_two_rows":
+        bufs = layer.decode_buffers(tq, maxN, ocmp.n_entries(L, cfg.m2, cfg.w2), "cuda", raw["x"].dtype)
+        out = layer.decode_step(caches, raw, raw["tok_off"], raw["q"], raw["p"], raw["omega"], raw["sigma"], q_pos,
+                                bufs)
+        # the same scores again, kept (the kernel is deterministic)
+        ws2 = layer.index_workspace(tq, maxN, "cuda")
+        ops.csa_index_score(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, maxN,
+                            ws2, scores=s_gpu)
+        idx = bufs["idx"]
+    else:
+        ws = layer.index_workspace(tq, maxN, "cuda")
+        idx = ops.csa_index_topk(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
+                                 maxN, ws, scores=s_gpu)
+        out = None
+    torch.cuda.synchronize()
+    ikey = f64(caches.ikey)
+    idx_h = idx.cpu().numpy()
+    sg = s_gpu.cpu().numpy()
+    for t in range(tq):
+        i = L - tq + t
+        nv = ocmp.n_visible(i, cfg.m, cfg.w)
+        p = f64(raw["p"][t])
+        om = raw["omega"][t].cpu().numpy().astype(np.float64)
+        s_ref = oidx.scores(p, om, ikey[:nv])
+        if t in neg:
+            # the premise: ties beyond the candidates the decode selection holds
+            # in registers (512 threads x 4), or, for the many-row selection
+            # (1024 threads, every candidate from memory), beyond one pass
+            zeros = int(np.sum(sg[t, :nv] == 0.0))
+            need = 2048 + cfg.k if tq == 2 else 1024 + cfg.k
+            assert zeros > need, f"row {t}: only {zeros} exact ties"
+            assert np.all(sg[t, :nv] <= 0.0)
+        check_topk(idx_h[t], sg[t], s_ref, score_bound(p, om, ikey[:nv]), cfg.k)
+        if t in neg:
+            chosen = np.sort(idx_h[t][idx_h[t] >= 0])
+            assert np.array_equal(chosen, np.nonzero(sg[t, :nv] == 0.0)[0][:cfg.k]), f"row {t}: not the smallest tied"
+    if out is not None:
+        kv_csa, kv_hca = f64(caches.kv_csa), f64(caches.kv_hca)
+        x = raw["x"].float().cpu().numpy()
+        sig = raw["sigma"].cpu().numpy().astype(np.float64)
+        for t in range(tq):
+            i = L - tq + t
+            chosen = idx_h[t][idx_h[t] >= 0]
+            qhat = oatt.normalize_query(f64(raw["q"][t]), cfg.eps, cfg.dtype)
+            win = oatt.normalize_tokens(x[max(0, i - cfg.W + 1):i + 1].astype(np.float64), cfg.eps, cfg.dtype)
+            nh = ocmp.n_visible(i, cfg.m2, cfg.w2)
+            o_ref, _ = oatt.merge([oatt.partial(qhat, kv_csa[chosen], cfg.scale),
+                                   oatt.partial(qhat, kv_hca[:nh], cfg.scale), oatt.partial(qhat, win, cfg.scale)], sig)
+            assert_close(f64(out)[t], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"ties row {t}")
+
 def _topk_direct(ikey, p, omega, k, n_entries):
     """csa_index_topk over one row whose query sees every entry of ikey."""
     from long_context_attention_20_amd import ops
