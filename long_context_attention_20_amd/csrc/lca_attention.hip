@@ -344,12 +344,17 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
         for (int i = threadIdx.x; i < tw.nstripe * kHistBins; i += kAttnThreads) gh[i] = 0;
       }
       for (int i = threadIdx.x; i < cnt; i += kAttnThreads) sidx[i] = (all && kbase + i < nv) ? (int32_t)(kbase + i) : -1;
+      // the tile memory beyond the selection's scratch keeps candidates the
+      // selection reads more than once (8192 of them at D = 512)
+      constexpr uint32_t kCandLds = (uint32_t)((kLdsBytes - sizeof(SelectLds)) / sizeof(uint64_t));
+      static_assert(sizeof(SelectLds) % sizeof(uint64_t) == 0, "the candidate area must be 8-byte aligned");
       if (!all && ready)
         topk_row_select<kAttnThreads, true>(tw, r, pf, *reinterpret_cast<SelectLds*>(lds_raw), sel_sh,
                                             [&](uint32_t o, int32_t e) {
                                               const int64_t j = (int64_t)o - kbase;
                                               if (j >= 0 && j < cnt) sidx[j] = e;
-                                            });
+                                            },
+                                            reinterpret_cast<uint64_t*>(lds_raw + sizeof(SelectLds)), kCandLds);
       __syncthreads();  // sidx complete; the selection's scratch is free
       if (hb == 0 && S.idx_out)
         for (int i = threadIdx.x; i < cnt; i += kAttnThreads) S.idx_out[(int64_t)r * S.k + kbase + i] = sidx[i];

@@ -579,9 +579,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
 
 constexpr int kFinThreads = 1024;
 
+constexpr uint32_t kFinCandLds = 8192;  // candidates beyond the prefetched ones kept in LDS
 __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
   __shared__ SelectLds L;
   __shared__ SelectShared S;
+  __shared__ uint64_t cl[kFinCandLds];
   const int r = blockIdx.x;
   const int b = r / a.Tq;
   const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - a.csa_off[b]);
@@ -597,8 +599,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
   SelectPrefetch<kFinThreads> P;
   topk_prefetch(w, r, P);
   auto emit = [&](uint32_t o, int32_t e) { out[o] = e; };
-  const uint32_t got = nv <= kBitmapEntries ? topk_row_select<kFinThreads, true>(w, r, P, L, S, emit)
-                                            : topk_row_select<kFinThreads, false>(w, r, P, L, S, emit);
+  const uint32_t got = nv <= kBitmapEntries ? topk_row_select<kFinThreads, true>(w, r, P, L, S, emit, cl, kFinCandLds)
+                                            : topk_row_select<kFinThreads, false>(w, r, P, L, S, emit, cl, kFinCandLds);
   if (got == 0)
     for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = -1;
 }
@@ -688,7 +690,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
   const uint32_t need2 = need - s_above, cnt2 = s_cnt;
   uint64_t vstar = (uint64_t)T2 << 34;
   if (cnt2 != need2 && cnt2 <= (uint32_t)kBoundaryLds) {
-    walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint64_t v) {
+    walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint32_t, uint64_t v) {
       if ((uint32_t)(v >> 34) == T2) {
         const uint32_t slot = atomicAdd(&s_nbl, 1u);
         if (slot < (uint32_t)kBoundaryLds) bl[slot] = v;
@@ -714,7 +716,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
       const int sft = shifts[pass], nbins = 1 << widths[pass];
       for (int i = tid; i < nbins; i += kRowThreads) h1[i] = 0;
       __syncthreads();
-      walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint64_t v) {
+      walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint32_t, uint64_t v) {
         if ((v & mask) == prefix) lds_count(h1, (uint32_t)(v >> sft) & (uint32_t)(nbins - 1));
       });
       __syncthreads();
@@ -728,7 +730,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
     }
     vstar = prefix;
   }
-  walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint64_t v) {
+  walk_loads<8>(cand, (uint32_t)tid, nc, (uint32_t)kRowThreads, [&](uint32_t, uint64_t v) {
     if (v >= vstar) {
       const uint32_t e = 0xFFFFFFu - (uint32_t)(v & 0xFFFFFFu);
       atomicOr(&bitmap[e >> 5], 1u << (e & 31));

@@ -213,6 +213,7 @@ __device__ __forceinline__ int64_t topk_visible(int64_t i, int m, int w, int64_t
 }
 
 constexpr int kBoundaryLds = 256;  // threshold-bin candidates ranked directly
+constexpr int kSelLoads = 4;       // candidate loads in flight per thread in the selection's walks
 
 // h[bin] += 1 for every active lane: when all active lanes of the wave count
 // the same bin (equal scores, the crowded case) one lane adds their number,
@@ -241,7 +242,7 @@ __device__ __forceinline__ void walk_loads(const T* ptr, uint32_t j0, uint32_t n
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (j + u * stride < n) f(v[u]);
+      if (j + u * stride < n) f(j + u * stride, v[u]);
   }
 }
 
@@ -293,7 +294,7 @@ __device__ __forceinline__ void topk_prefetch(const TopkWs& w, int r, SelectPref
 
 template <int NT, bool ORDERED, class Emit>
 __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch<NT>& P, SelectLds& L,
-                                    SelectShared& S, Emit emit) {
+                                    SelectShared& S, Emit emit, uint64_t* cl, uint32_t ncl) {
   constexpr int NW = NT / 64;
   constexpr int SPT = SelectPrefetch<NT>::SPT, CPT = SelectPrefetch<NT>::CPT;
   constexpr int HPT = kH2Bins / NT;  // second-level bins per thread
@@ -308,13 +309,26 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
   const bool consistent = n_sel < k && (uint64_t)n_sel + ncands >= k && ncands <= (uint64_t)w.max_entries;
   if (!consistent) return 0;
   const uint32_t need = k - n_sel;
-  // this thread's candidates: the prefetched ones, then (a crowded
-  // threshold bin) the rest straight from global memory
+  // this thread's candidates: the prefetched ones, then the rest from
+  // global memory, which the first pass copies into cl (ncl of them fit, in
+  // LDS) and later passes read from there
+  const uint32_t nreg = (uint32_t)(CPT * NT);
+  const uint32_t nlds = ncands > nreg ? min(ncands - nreg, ncl) : 0u;
+  auto for_cands_staging = [&](auto f) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if ((uint32_t)(tid + i * NT) < ncands) f(P.cv[i]);
+    walk_loads<kSelLoads>(cg, (uint32_t)tid + nreg, ncands, (uint32_t)NT, [&](uint32_t j, uint64_t v) {
+      if (j - nreg < nlds) cl[j - nreg] = v;
+      f(v);
+    });
+  };
   auto for_cands = [&](auto f) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
       if ((uint32_t)(tid + i * NT) < ncands) f(P.cv[i]);
-    walk_loads<8>(cg, (uint32_t)(tid + CPT * NT), ncands, (uint32_t)NT, f);
+    for (uint32_t j = tid; j < nlds; j += NT) f(cl[j]);
+    walk_loads<kSelLoads>(cg, (uint32_t)tid + nreg + nlds, ncands, (uint32_t)NT, [&](uint32_t, uint64_t v) { f(v); });
   };
 
   // 1. the candidates per second-level bin (key bits 20..10, the top bits
@@ -325,7 +339,7 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
   if (ORDERED)
     for (int i = tid; i < kBitmapWords; i += NT) L.bitmap[i] = 0;
   __syncthreads();
-  for_cands([&](uint64_t v) { lds_count(L.h, (uint32_t)(v >> 34) & (uint32_t)(kH2Bins - 1)); });
+  for_cands_staging([&](uint64_t v) { lds_count(L.h, (uint32_t)(v >> 34) & (uint32_t)(kH2Bins - 1)); });
   if (ORDERED) {
     // the selected list is chosen whole
 #pragma unroll
