@@ -57,8 +57,8 @@ TRAFFIC = {
         "files": ["long_context_attention_20_amd/csrc/lca_attention.hip",
                   "long_context_attention_20_amd/csrc/lca_common.h",
                   "long_context_attention_20_amd/csrc/lca_topk.h"],
-        "sha1": "a1108e6f005161ac6721657c0eef46bf60f8829e",
-        "fetch_kib": 6334.1, "write_kib": 15521.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha1": "349a35f21acbded9566d0baee2b2aed6f84e167d",
+        "fetch_kib": 6319.6, "write_kib": 15476.9, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
