@@ -27,6 +27,7 @@ import numpy as np
 
 from . import attention as att
 from .compress import compress, n_entries, n_visible
+from . import quant
 from .indexer import scores, topk
 from .numerics import round_to
 
@@ -42,10 +43,17 @@ def seq_slice(arr, tok_off, b):
     return np.asarray(arr[int(tok_off[b]):int(tok_off[b + 1])], dtype=np.float64)
 
 
+def fp8_keys(cfg) -> bool:
+    """Indexer keys stored as E4M3 rows with a scale (oracle.quant)."""
+    return getattr(cfg, "ikey", "bf16") == "fp8"
+
+
 def build_seq_caches(x, a, g, u, c, cfg) -> SeqCaches:
-    """Caches of one sequence from its raw streams (all float64 views)."""
+    """Caches of one sequence from its raw streams (all float64 views).  With
+    fp8 indexer keys the key cache holds the rows they stand for (s * q)."""
     kv_csa = round_to(compress(x, a, cfg.m, cfg.w, True, cfg.eps), cfg.dtype)
-    ikey = round_to(compress(u, c, cfg.m, cfg.w, False, cfg.eps), cfg.dtype)
+    pooled = compress(u, c, cfg.m, cfg.w, False, cfg.eps)
+    ikey = quant.dequantize_rows(*quant.quantize_rows(pooled)) if fp8_keys(cfg) else round_to(pooled, cfg.dtype)
     kv_hca = round_to(compress(x, g, cfg.m2, cfg.w2, True, cfg.eps), cfg.dtype)
     return SeqCaches(kv_csa, ikey, kv_hca)
 
@@ -60,7 +68,8 @@ def build_caches(raw, cfg) -> List[SeqCaches]:
 
 
 def select(ikey, p, omega, i, cfg):
-    """Visible CSA entries, their scores and the selected indices for query i."""
+    """Visible CSA entries, their scores and the selected indices for query i
+    (with fp8 indexer keys, ikey holds the rows they stand for)."""
     nv = n_visible(i, cfg.m, cfg.w)
     s = scores(p, omega, ikey[:nv])
     return s, topk(s, cfg.k)

@@ -14,7 +14,8 @@ import torch
 import lca_inputs as li
 from oracle import attention as att
 from oracle import compress as cmp
-from oracle import dense, indexer, numerics, pipeline
+from oracle import dense, indexer, numerics, pipeline, quant
+from oracle import indexer as idx
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -396,3 +397,75 @@ def test_generator_is_seeded_and_rounded():
         assert np.array_equal(a[k], b[k])
     assert np.array_equal(numerics.round_bf16(a["x"].astype(np.float64)), a["x"].astype(np.float64))
     assert abs(float(np.mean(a["x"]))) < 0.05 and abs(float(np.std(a["x"])) - 1) < 0.05
+
+
+# --------------------------------------------------------------------------
+# fp8 (E4M3) indexer rows
+# --------------------------------------------------------------------------
+
+def _e4m3_grid():
+    """Every finite E4M3 value, decoded by torch from its bit pattern."""
+    import torch
+    v = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    return np.unique(v[np.isfinite(v)].astype(np.float64))
+
+
+def test_e4m3_grid_is_fixed_and_midpoints_go_to_even():
+    g = _e4m3_grid()
+    assert g.max() == 448.0 and g.min() == -448.0 and len(g) == 253   # +-0 merge
+    assert np.array_equal(quant.round_e4m3(g), g)
+    pos = g[g >= 0]
+    mid = (pos[:-1] + pos[1:]) / 2
+    r = quant.round_e4m3(mid)
+    # ties to the neighbour with an even mantissa (the even multiple of the spacing)
+    import torch
+    even = torch.tensor(pos).to(torch.float8_e4m3fn).view(torch.uint8).numpy() % 2 == 0
+    want = np.where(even[:-1], pos[:-1], pos[1:])
+    assert np.array_equal(r, want)
+    assert np.array_equal(quant.round_e4m3(-mid), -want)
+
+
+def test_e4m3_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 8, 20000),
+                        [0.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -6, 447.9, 448.0, -448.0]])
+    x = np.clip(x, -448, 448)
+    ref = torch.tensor(x, dtype=torch.float64).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(quant.round_e4m3(x), ref)
+
+
+def test_quantize_rows_invariants():
+    rng = np.random.default_rng(8)
+    v = rng.standard_normal((500, 64)) * np.exp(rng.uniform(-6, 6, (500, 1)))
+    v[3] = 0.0
+    q, s = quant.quantize_rows(v)
+    assert np.all(q[3] == 0) and s[3] == 0
+    live = s > 0
+    assert np.all(np.max(np.abs(q[live]), axis=1) == 448.0)          # the largest channel hits the top value
+    assert np.array_equal(s, s.astype(np.float32).astype(np.float64))  # fp32 scales
+    err = np.abs(quant.dequantize_rows(q, s) - v)
+    # half a spacing of the E4M3 value (relative 2**-4), or half the subnormal spacing
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** -10 * s[:, None]) * (1 + 2.0 ** -20)
+    assert np.all(err <= bound)
+
+
+def test_fp8_scores_reduce_to_plain_scores_on_the_grid():
+    """Rows already on the E4M3 grid with a power-of-two scale (and the
+    largest at 448 times it) quantize exactly: the fp8 score equals the plain
+    one, negative head weights included; rows off the grid score as the rows
+    they stand for."""
+    rng = np.random.default_rng(9)
+    g = _e4m3_grid()
+    keys = rng.choice(g, (300, 64)) * 2.0 ** -5
+    keys[:, 0] = 448.0 * 2.0 ** -5
+    p = rng.choice(g, (4, 64)) * 2.0 ** -3
+    p[:, 5] = -448.0 * 2.0 ** -3
+    om = np.array([1.5, -0.7, 0.25, 2.0])
+    q, s = quant.quantize_rows(keys)
+    assert np.all(s == 2.0 ** -5) and np.array_equal(q * s[:, None], keys)
+    assert np.array_equal(quant.scores_fp8(p, om, q, s), idx.scores(p, om, keys))
+    off = keys + rng.standard_normal(keys.shape) * 0.01
+    q2, s2 = quant.quantize_rows(off)
+    assert not np.array_equal(quant.scores_fp8(p, om, q2, s2), idx.scores(p, om, off))
+    assert np.allclose(quant.scores_fp8(p, om, q2, s2), idx.scores(p, om, q2 * s2[:, None]), rtol=0, atol=0)
