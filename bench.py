@@ -86,6 +86,12 @@ def n_windows(L, m, w):
     return 0 if L < w else (L - w) // m + 1
 
 
+def key_bytes(cfg):
+    """Bytes of one indexer key in the cache: d_I elements, or for fp8 rows
+    d_I E4M3 bytes + the fp32 scale + 4 pad bytes."""
+    return cfg.dI + 8 if cfg.ikey == "fp8" else cfg.dI * (2 if cfg.dtype == "bf16" else 4)
+
+
 def step_bytes(cfg):
     """Algorithmic HBM bytes of one decode step: what the method must move.
     With tq query rows per sequence the indexer keys, the HCA entries and the
@@ -98,7 +104,7 @@ def step_bytes(cfg):
         ncsa = n_windows(L, cfg.m, cfg.w)
         nh = n_windows(L, cfg.m2, cfg.w2)
         kk = min(cfg.k, ncsa)
-        tot += ncsa * cfg.dI * e                        # indexer keys
+        tot += ncsa * key_bytes(cfg)                    # indexer keys
         tot += tq * kk * (cfg.D * e + 4)                # selected entries + indices, per row
         tot += min(cfg.W + tq - 1, L) * cfg.D * e       # window rows
         tot += nh * cfg.D * e                           # HCA entries
@@ -117,7 +123,7 @@ def kernel_cost(cfg, name):
         nh = n_windows(L, cfg.m2, cfg.w2)
         kk = min(cfg.k, ncsa)
         if name == "csa_index_score":
-            by += ncsa * cfg.dI * e
+            by += ncsa * key_bytes(cfg)
             fl += 2 * ncsa * cfg.dI * cfg.HI
         elif name == "csa_topk_select":
             by += ncsa * 4 + kk * 4
@@ -139,7 +145,7 @@ def kernel_cost(cfg, name):
         elif name == "swa_merge":
             by += tq * (cfg.H * cfg.D * e + cfg.H * 4)         # output + sink
         elif name == "csa_index_score_append":                 # scores + the entries the new tokens complete
-            by += ncsa * cfg.dI * e
+            by += ncsa * key_bytes(cfg)
             by += (2 * cfg.w * cfg.D + 2 * cfg.w * cfg.dI + 2 * cfg.w2 * cfg.D) * e + (2 * cfg.D + cfg.dI) * e
             fl += 2 * ncsa * cfg.dI * cfg.HI * tq
     return by, fl
@@ -185,7 +191,7 @@ class Runner:
         self.torch, self.ops = torch, ops
         self.cfg = cfg
         a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
-                            split_csa=split_csa or None, split_hca=split_hca or None)
+                            split_csa=split_csa or None, split_hca=split_hca or None, ikey_fp8=cfg.ikey == "fp8")
         self.attn = a
         self.layers = [LayerState(cfg, r, a, dev) for r in range(R)]
         rows = cfg.B * cfg.tq
@@ -331,6 +337,7 @@ def cpu_baseline(cfg, state, budget_s):
     from oracle import compress as ocmp
     from oracle import numerics as onum
     from oracle import pipeline as opipe
+    from oracle import quant as oquant
     try:
         from threadpoolctl import threadpool_info
         threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
@@ -362,8 +369,10 @@ def cpu_baseline(cfg, state, budget_s):
                                           (cfg.m2, cfg.w2, x, g, True, "kv_hca")):
             new = range(ocmp.n_entries(L - tq, m, w), ocmp.n_entries(L, m, w))
             if len(new):
-                getattr(caches, name)[list(new)] = onum.round_to(ocmp.compress(src, lg, m, w, norm, cfg.eps, new),
-                                                                 cfg.dtype)
+                pooled = ocmp.compress(src, lg, m, w, norm, cfg.eps, new)
+                getattr(caches, name)[list(new)] = (oquant.dequantize_rows(*oquant.quantize_rows(pooled))
+                                                    if name == "ikey" and cfg.ikey == "fp8"
+                                                    else onum.round_to(pooled, cfg.dtype))
         for q, p, om, i in rows:
             opipe.query_step(caches, x, q, p, om, sg, i, cfg)
         n += 1
@@ -547,7 +556,10 @@ def main():
         cpu = cpu_baseline(cfg, run.layers[0], args.cpu_seconds)
 
     res = {
-        "metric": ("decode query-tokens/s per layer at 1M ctx (Pro shape); % of HBM peak BW" if tq == 1 else
+        "metric": ("decode query-tokens/s per layer at 1M ctx (Pro shape); % of HBM peak BW" if tq == 1 and
+                   cfg.ikey != "fp8" else
+                   "decode query-tokens/s per layer at 1M ctx (Pro shape, fp8 indexer keys); % of HBM peak BW"
+                   if tq == 1 else
                    f"decode query-tokens/s per layer at 1M ctx (Pro shape, {tq} query rows per step: the main token "
                    f"and {tq - 1} drafted); % of HBM peak BW"),
         "value": value,
@@ -565,7 +577,7 @@ def main():
                    f"{cfg.B} seqs, mean {int(np.mean(cfg.lens))}", "q_heads": cfg.H, "head_dim": cfg.D,
                    "indexer": f"{cfg.HI}x{cfg.dI}", "topk": cfg.k, "m": cfg.m, "m2": cfg.m2, "window": cfg.W,
                    "layers_rotated": R, "timing": "hip-graph replay" if ms_graph is not None else "stream",
-                   "query_rows_per_step": tq,
+                   "query_rows_per_step": tq, "indexer_keys": cfg.ikey,
                    "positions": (f"{K} consecutive decode steps over positions {last - tq * K + 1}..{last}, "
                                  f"{tq} per step, each appending the entries its tokens complete") if consecutive else
                    "last position of every sequence, every append in every step"},

@@ -47,7 +47,15 @@ enum lca_status {
   LCA_ERR_HIP = -4          /* the HIP runtime reported an error */
 };
 
-enum lca_dtype { LCA_F32 = 0, LCA_BF16 = 1 };
+enum lca_dtype { LCA_F32 = 0, LCA_BF16 = 1, LCA_BF16_FP8KEY = 2 };
+/* LCA_BF16_FP8KEY (index-score calls only): indexer queries p bf16, weights
+ * fp32, and the indexer-key cache in fp8 rows: d_I OCP E4M3 bytes (1 sign, 4
+ * exponent bits of bias 7, 3 mantissa bits; largest finite 448), then the
+ * row's fp32 scale s, then 4 zero bytes -- d_I + 8 bytes per entry.  The row
+ * stands for s * q (s = max|key| / 448, q rounded to nearest even); its score
+ * is the bf16 formula on that row ("DeepSeek-V4", Inference efficiency: the
+ * indexer's query-key path in low precision).  Written by lca_kv_compress
+ * with out_fp8 = 1. */
 
 /* Static text for a status code. */
 const char* lca_strerror(int status);
@@ -90,6 +98,8 @@ typedef struct lca_compress_stream {
   int32_t per_channel;    /* 1: logits [T, C]; 0: logits [T]                          */
   int32_t rmsnorm;        /* 1: RMS-normalise each entry over its C channels          */
   int32_t max_entries;    /* host bound on entries written per sequence (>= 0)        */
+  int32_t out_fp8;        /* 1: write fp8 key rows (see LCA_BF16_FP8KEY): bf16 input,  */
+                          /* C <= 512, w = m or w = 2m <= 16; 0: rows of the input type */
 } lca_compress_stream;
 
 /* Compress up to 4 streams in one launch.

@@ -22,6 +22,7 @@ struct CompressStreamDev {
   void* out;
   const int64_t* ent_off;
   int C, m, w, per_channel, rmsnorm, max_entries;
+  int fp8;      // 1: E4M3 rows of C bytes + fp32 scale + 4 zero bytes (one lane group per row, NV = 1)
   int G;        // lanes per row
   int NV;       // 16-byte vectors per lane per row
   int small;    // 1: small-window run mode
@@ -97,6 +98,26 @@ struct RowCtx {
   }
 };
 
+// Eight values as OCP E4M3 bytes of value / scale (round to nearest even,
+// kept inside +-448); scale > 0.  Byte c of the result is value c.
+__device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], float scale) {
+  float y[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) y[c] = fminf(fmaxf(x[c] / scale, -448.f), 448.f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+// The values of eight E4M3 bytes (exact in fp32).
+__device__ __forceinline__ void unpack_fp8x8(uint2 v, float (&x)[8]) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+  x[0] = a.x; x[1] = a.y; x[2] = b.x; x[3] = b.y; x[4] = c.x; x[5] = c.y; x[6] = d.x; x[7] = d.y;
+}
+
 template <typename ET, int NV>
 __device__ __forceinline__ void finish_entry(const CompressStreamDev& s, float eps, int G,
                                              PoolState<ET::kVec> (&st)[NV], const int (&ch0)[NV],
@@ -118,6 +139,26 @@ __device__ __forceinline__ void finish_entry(const CompressStreamDev& s, float e
     for (int v = 0; v < NV; ++v)
 #pragma unroll
       for (int k = 0; k < VE; ++k) e[v][k] *= inv;
+  }
+  if (s.fp8) {
+    // one E4M3 byte per channel and the row's fp32 scale amax / 448 (the
+    // row stands for scale * q; q = round-to-nearest-even of value / scale,
+    // kept inside +-448).  bf16 input, C <= 512: one 8-channel vector per
+    // lane (NV = 1)
+    if constexpr (VE == 8) {
+      float am = 0.f;
+#pragma unroll
+      for (int k = 0; k < VE; ++k) am = fmaxf(am, fabsf(e[0][k]));
+      am = wave_max(am, G);  // all lanes of the row group take part
+      const float sc = am / 448.0f;
+      const uint2 q = sc > 0.f ? pack_fp8x8(e[0], sc) : make_uint2(0u, 0u);
+      if (active) {
+        char* row = reinterpret_cast<char*>(s.out) + out_row * (int64_t)(s.C + 8);
+        *reinterpret_cast<uint2*>(row + ch0[0]) = q;
+        if (ch0[0] == 0) *reinterpret_cast<uint2*>(row + s.C) = make_uint2(__float_as_uint(sc), 0u);
+      }
+    }
+    return;
   }
   if (active) {
     const int64_t rb = (int64_t)s.C * ET::kBytes;

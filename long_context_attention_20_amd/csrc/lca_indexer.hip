@@ -65,6 +65,50 @@ __device__ __forceinline__ int64_t row_visible(const IndexParams& a, int r, int6
   return nv < a.max_entries ? nv : a.max_entries;
 }
 
+// ------------------------------------------------------------------ fp8 key rows
+// A key row of the fp8 cache: d_I OCP E4M3 bytes, the row's fp32 scale, 4 zero
+// bytes.  The bytes are widened to bf16 (every E4M3 value is exact in bf16:
+// the upper half of its fp32 form) and fed to the bf16 matrix cores, so the
+// products are exact; the scale multiplies the row's score (s >= 0).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(f32x2_t f) {
+  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
+}
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
+  return make_uint4(bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false)),
+                    bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true)),
+                    bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false)),
+                    bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true)));
+}
+__device__ __forceinline__ int64_t key_row_bytes(const IndexParams& a, bool fp8) {
+  return fp8 ? (int64_t)a.dI + 8 : (int64_t)a.dI * 2;
+}
+// The 8 dims lane group grp feeds k-step ks of a 16x16x32 product.  bf16
+// rows: dims 32*ks + 8*grp ..; fp8 rows: lane group grp takes the KS*8
+// consecutive dims from KS*8*grp (one 16-byte load per two k-steps) -- the
+// contraction runs over every dim once either way, and the query operand
+// uses the same order.
+template <int KS>
+__device__ __forceinline__ int key_dim(int ks, int grp, bool fp8) {
+  return fp8 ? (KS * grp + ks) * 8 : ks * 32 + grp * 8;
+}
+// Lane group grp's KS slices of 8 E4M3 bytes of one fp8 row, in 16-byte loads
+// (rows are d_I + 8 bytes: 8-byte aligned, which the dword loads accept).
+template <int KS>
+__device__ __forceinline__ void load_fp8_slices(const char* row, int grp, uint2 (&out)[KS]) {
+  const char* base = row + grp * KS * 8;
+  if constexpr (KS == 1) {
+    out[0] = *reinterpret_cast<const uint2*>(base);
+  } else {
+#pragma unroll
+    for (int i = 0; i < KS / 2; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + 16 * i);
+      out[2 * i] = make_uint2(v.x, v.y);
+      out[2 * i + 1] = make_uint2(v.z, v.w);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ scores
 
 // Block 0 of each row's scores zeroes the row's list counters, which the
@@ -89,8 +133,9 @@ __device__ __forceinline__ void hist_flush(const uint32_t* lh, uint32_t* gh) {
 
 // bf16, matrix cores.  KS = dI / 32 k-steps.  Block (cx, r) scores the
 // entries [cx*chunk, min((cx+1)*chunk, lim)) of row r; lh: kHistBins words
-// of LDS.
-template <int KS>
+// of LDS.  FP8K: fp8 key rows (widened to bf16 in registers, score times the
+// row's scale).
+template <int KS, bool FP8K = false>
 __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, int cx, int64_t lim, uint32_t* lh) {
   const int b = r / a.Tq;
   const int64_t e_base = a.csa_off[b];
@@ -111,7 +156,7 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < a.HI) v = *reinterpret_cast<const uint4*>(P + col * a.dI + ks * 32 + grp * 8);
+      if (col < a.HI) v = *reinterpret_cast<const uint4*>(P + col * a.dI + key_dim<KS>(ks, grp, FP8K));
       A[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -124,19 +169,28 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
   }
   __syncthreads();
 
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.ikey) + e_base * a.dI;
+  const char* K = reinterpret_cast<const char*>(a.ikey);
+  const int64_t rowb = key_row_bytes(a, FP8K);
   float* S = a.scores + (int64_t)r * a.max_entries;
   constexpr int U = 8;  // tiles in flight per wave
   const int64_t ntile = (c1 - c0 + 15) / 16;
   const int nw = (int)(blockDim.x >> 6);
   for (int64_t t0 = wave * U; t0 < ntile; t0 += nw * U) {
     uint4 kv[U][KS];
+    uint2 k8[U][KS];
+    float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int64_t e = c0 + (t0 + u) * 16 + col;
       if (e >= c1) e = c1 - 1;  // clamp: stays inside the visible entries
+      const char* row = K + (e_base + e) * rowb;
+      if constexpr (FP8K) {
+        load_fp8_slices<KS>(row, grp, k8[u]);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(K + e * a.dI + ks * 32 + grp * 8);
+        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
+      }
+      if constexpr (FP8K) sc[u] = *reinterpret_cast<const float*>(row + a.dI);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -144,13 +198,16 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
       // entry `col` against heads 4*grp .. 4*grp+3
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (FP8K) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], __builtin_bit_cast(bf16x8_t, kv[u][ks]), acc, 0, 0, 0);
+      }
       float part = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) part = fmaf(om[i], fmaxf(acc[i], 0.f), part);
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
+      if constexpr (FP8K) part *= sc[u];
       const int64_t e = c0 + (t0 + u) * 16 + col;
       if (grp == 0 && t0 + u < ntile && e < c1) {
         S[e] = part;
@@ -162,10 +219,10 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
   if (do_hist) hist_flush(lh, a.hist + ((int64_t)r * a.nstripe + cx % a.nstripe) * kHistBins);
 }
 
-template <int KS>
+template <int KS, bool FP8K = false>
 __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
   __shared__ uint32_t lh[kHistBins];
-  score_chunk_mfma<KS>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
+  score_chunk_mfma<KS, FP8K>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
 }
 
 // Several query rows of one sequence (a decode step with Tq > 1, as when a
@@ -176,8 +233,8 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
 // accumulator lane adds the weighted ReLU terms of its four A rows into the
 // partial of the row they belong to; the partials are summed over the four
 // lane groups and lane group q stores row q's score.  lh: TQ * kHistBins
-// words of LDS, one histogram per row.
-template <int KS, int TQ>
+// words of LDS, one histogram per row.  FP8K as score_chunk_mfma.
+template <int KS, int TQ, bool FP8K = false>
 __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, int cx, int64_t lim, uint32_t* lh) {
   static_assert(TQ >= 2 && TQ <= 4, "2 to 4 rows per block");
   const int nq = a.Tq;  // <= TQ, nq * HI <= 16 (checked by the host)
@@ -210,7 +267,7 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < nrow) v = *reinterpret_cast<const uint4*>(P + col * a.dI + ks * 32 + grp * 8);
+      if (col < nrow) v = *reinterpret_cast<const uint4*>(P + col * a.dI + key_dim<KS>(ks, grp, FP8K));
       A[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -227,25 +284,36 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
   }
   __syncthreads();
 
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.ikey) + e_base * a.dI;
+  const char* K = reinterpret_cast<const char*>(a.ikey);
+  const int64_t rowb = key_row_bytes(a, FP8K);
   constexpr int U = 8;  // tiles in flight per wave
   const int64_t ntile = (c1 - c0 + 15) / 16;
   const int nw = (int)(blockDim.x >> 6);
   for (int64_t t0 = wave * U; t0 < ntile; t0 += nw * U) {
     uint4 kv[U][KS];
+    uint2 k8[U][KS];
+    float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int64_t e = c0 + (t0 + u) * 16 + col;
       if (e >= c1) e = c1 - 1;  // clamp: stays inside the visible entries
+      const char* row = K + (e_base + e) * rowb;
+      if constexpr (FP8K) {
+        load_fp8_slices<KS>(row, grp, k8[u]);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(K + e * a.dI + ks * 32 + grp * 8);
+        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
+      }
+      if constexpr (FP8K) sc[u] = *reinterpret_cast<const float*>(row + a.dI);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (FP8K) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], __builtin_bit_cast(bf16x8_t, kv[u][ks]), acc, 0, 0, 0);
+      }
       const int64_t e = c0 + (t0 + u) * 16 + col;
 #pragma unroll
       for (int q = 0; q < TQ; ++q) {
@@ -254,6 +322,7 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
         for (int i = 0; i < 4; ++i) part = fmaf(om[q][i], fmaxf(acc[i], 0.f), part);
         part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
+        if constexpr (FP8K) part *= sc[u];
         if (grp == q && t0 + u < ntile && e < c1q[q]) {
           a.scores[(int64_t)(r0 + q) * a.max_entries + e] = part;
           if (hq[q]) hist_add(lh + q * kHistBins, part);
@@ -267,10 +336,10 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
     if (hq[q]) hist_flush(lh + q * kHistBins, a.hist + ((int64_t)(r0 + q) * a.nstripe + cx % a.nstripe) * kHistBins);
 }
 
-template <int KS, int TQ>
+template <int KS, int TQ, bool FP8K = false>
 __global__ __launch_bounds__(kIdxThreads) void index_score_multi(IndexParams a) {
   __shared__ uint32_t lh[TQ * kHistBins];
-  score_chunk_multi<KS, TQ>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
+  score_chunk_multi<KS, TQ, FP8K>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
 }
 
 // ------------------------------------------------------------------ score + append
@@ -308,6 +377,7 @@ __device__ __forceinline__ float group_sum_n(float v, int n) {
   }
 }
 
+template <bool FP8K>
 __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int b) {
   constexpr int VE = 8;                    // bf16 channels per 16-byte vector
   const CompressStreamDev& s = ap.s;
@@ -365,9 +435,30 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
 #pragma unroll
       for (int e = 0; e < VE; ++e) key[e] *= inv;
     }
-    const uint4 kq = BF16::pack(key);
-    if (on) stg16(s.out, (e_base + j) * rb + ch0 * 2, kq);
-    BF16::unpack(kq, key);                 // the stored (rounded) key is the one scored
+    // the stored (rounded) key is the one scored
+    float row_scale = 1.f;
+    if constexpr (FP8K) {
+      // an fp8 key row (as the compression kernel writes it): E4M3 bytes of
+      // value / scale, scale = amax / 448 over the row's lanes; scored as the
+      // bytes' values, times the scale
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) am = fmaxf(am, fabsf(key[e]));
+      am = wave_max(am, G);
+      const float sc = am / 448.0f;
+      const uint2 q = sc > 0.f ? pack_fp8x8(key, sc) : make_uint2(0u, 0u);
+      if (on) {
+        char* row = reinterpret_cast<char*>(s.out) + (e_base + j) * (int64_t)(s.C + 8);
+        *reinterpret_cast<uint2*>(row + ch0) = q;
+        if (li == 0) *reinterpret_cast<uint2*>(row + s.C) = make_uint2(__float_as_uint(sc), 0u);
+      }
+      unpack_fp8x8(q, key);
+      row_scale = sc;
+    } else {
+      const uint4 kq = BF16::pack(key);
+      if (on) stg16(s.out, (e_base + j) * rb + ch0 * 2, kq);
+      BF16::unpack(kq, key);
+    }
     for (int q = 0; q < a.Tq; ++q) {
       const int r = b * a.Tq + q;
       const int64_t nv = row_visible(a, r, nseq);
@@ -384,6 +475,7 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
         d = group_sum_n(d, G);
         score = fmaf(a.omega[(int64_t)r * a.HI + h], fmaxf(d, 0.f), score);
       }
+      if constexpr (FP8K) score *= row_scale;
       if (on && j < nv && li == 0) {
         a.scores[(int64_t)r * a.max_entries + j] = score;
         if (do_hist)
@@ -395,8 +487,9 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
 }
 
 // TQ: query rows per sequence the score blocks take at once (1: one row;
-// 2 or 4: all Tq <= TQ rows of a sequence, as score_chunk_multi).
-template <int KS, int TQ>
+// 2 or 4: all Tq <= TQ rows of a sequence, as score_chunk_multi).  FP8K: the
+// indexer-key stream writes fp8 rows, which the score blocks read.
+template <int KS, int TQ, bool FP8K>
 __global__ __launch_bounds__(kIdxThreads) void index_score_append(IndexParams a, AppendIdx ap, CompressParams cp) {
   extern __shared__ uint32_t dyn[];  // max(histograms, compression) words
   const int blk = blockIdx.x;
@@ -405,15 +498,15 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_append(IndexParams a,
     // scoring blocks
     compress_block<BF16, 1, 8, false>(cp, blk, reinterpret_cast<float*>(dyn));
   } else if (blk < ap.ncb + ap.B) {
-    append_and_score(a, ap, blk - ap.ncb);
+    append_and_score<FP8K>(a, ap, blk - ap.ncb);
   } else {
     const int sb = blk - ap.ncb - ap.B;
     const int b = sb / ap.nsx, cx = sb % ap.nsx;
     const int64_t lim = n_windows(ap.done_len[b], a.m, a.w);
     if constexpr (TQ == 1)
-      score_chunk_mfma<KS>(a, b, cx, lim, dyn);
+      score_chunk_mfma<KS, FP8K>(a, b, cx, lim, dyn);
     else
-      score_chunk_multi<KS, TQ>(a, b, cx, lim, dyn);
+      score_chunk_multi<KS, TQ, FP8K>(a, b, cx, lim, dyn);
   }
 }
 
@@ -824,7 +917,13 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
   IndexParams a = make_params(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, nullptr, scores, ws);
   const int rows = B * Tq;
   dim3 g1((unsigned)((maxN + a.chunk - 1) / a.chunk), (unsigned)rows);
-  const bool mfma = dtype == LCA_BF16 && HI <= 16 && (dI % 32) == 0 && dI <= 256;
+  const bool fp8k = dtype == LCA_BF16_FP8KEY;
+  const bool mfma = (dtype == LCA_BF16 || fp8k) && HI <= 16 && (dI % 32) == 0 && dI <= 256;
+  if (fp8k && (!mfma || a.no_hist)) {
+    set_error("csa_index_score: fp8 key rows are scored for H_I <= 16 and fewer than %d rows per sequence",
+              kRowsPerBlock);
+    return LCA_ERR_UNSUPPORTED;
+  }
   if (mfma && a.no_hist && (HI == 1 || HI == 2 || HI == 4)) {
     // many rows per sequence: the row-tiled kernel
     const int gps = (Tq + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -847,9 +946,14 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
   if (mfma && multi_rows_ok(Tq, HI) && !a.no_hist) {
     // a few rows per sequence: all of them from one read of the keys
     dim3 g((unsigned)((maxN + a.chunk - 1) / a.chunk), (unsigned)B);
-#define LCA_MULTI(KSv)                                                                                   \
-  if (Tq == 2) hipLaunchKernelGGL((index_score_multi<KSv, 2>), g, dim3(kIdxThreads), 0, stream, a);    \
-  else hipLaunchKernelGGL((index_score_multi<KSv, 4>), g, dim3(kIdxThreads), 0, stream, a);
+#define LCA_MULTI(KSv)                                                                                         \
+  if (fp8k) {                                                                                                  \
+    if (Tq == 2) hipLaunchKernelGGL((index_score_multi<KSv, 2, true>), g, dim3(kIdxThreads), 0, stream, a);    \
+    else hipLaunchKernelGGL((index_score_multi<KSv, 4, true>), g, dim3(kIdxThreads), 0, stream, a);            \
+  } else {                                                                                                     \
+    if (Tq == 2) hipLaunchKernelGGL((index_score_multi<KSv, 2>), g, dim3(kIdxThreads), 0, stream, a);          \
+    else hipLaunchKernelGGL((index_score_multi<KSv, 4>), g, dim3(kIdxThreads), 0, stream, a);                  \
+  }
     switch (dI / 32) {
       case 1: LCA_MULTI(1) break;
       case 2: LCA_MULTI(2) break;
@@ -859,7 +963,14 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
 #undef LCA_MULTI
     return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
   }
-  if (mfma) {
+  if (mfma && fp8k) {
+    switch (dI / 32) {
+      case 1: hipLaunchKernelGGL((index_score_mfma<1, true>), g1, dim3(kIdxThreads), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((index_score_mfma<2, true>), g1, dim3(kIdxThreads), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((index_score_mfma<4, true>), g1, dim3(kIdxThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((index_score_mfma<8, true>), g1, dim3(kIdxThreads), 0, stream, a); break;
+    }
+  } else if (mfma) {
     switch (dI / 32) {
       case 1: hipLaunchKernelGGL((index_score_mfma<1>), g1, dim3(kIdxThreads), 0, stream, a); break;
       case 2: hipLaunchKernelGGL((index_score_mfma<2>), g1, dim3(kIdxThreads), 0, stream, a); break;
@@ -886,7 +997,11 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
   // the fused launch: bf16 matrix-core scores, one query row per sequence or
   // a few sharing a score block, KV streams of at most 512 bf16 channels;
   // anything else runs as the two launches it stands for
-  const bool fused = dtype == LCA_BF16 && HI <= 16 && (dI == 32 || dI == 64 || dI == 128 || dI == 256) &&
+  // dtype LCA_BF16_FP8KEY: bf16 inputs, the indexer-key stream writes (and
+  // the scores read) fp8 key rows
+  const bool fp8k = dtype == LCA_BF16_FP8KEY;
+  const int in_dtype = fp8k ? LCA_BF16 : dtype;
+  const bool fused = in_dtype == LCA_BF16 && HI <= 16 && (dI == 32 || dI == 64 || dI == 128 || dI == 256) &&
                      idx_stream->C == dI && idx_stream->m == m && idx_stream->w == w &&
                      (w == m || w == 2 * m) && w <= 16 && (Tq == 1 || multi_rows_ok(Tq, HI));
   CompressParams cp{};
@@ -894,7 +1009,7 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
   size_t clds = 0;
   int nv = 1;
   if (fused && n_kv > 0) {
-    const int rc = setup_compress(kv_streams, n_kv, tok_off, done_len, B, eps, dtype, kIdxThreads, &cp, &cblocks,
+    const int rc = setup_compress(kv_streams, n_kv, tok_off, done_len, B, eps, in_dtype, kIdxThreads, &cp, &cblocks,
                                   &clds, &nv);
     if (rc != LCA_OK) return rc;
   }
@@ -905,8 +1020,8 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
     for (int i = 0; i < n_kv; ++i) all[n++] = kv_streams[i];
     // streams of one compression launch share the vector width: the indexer
     // keys go first, alone when they differ
-    int rc = launch_compress(all, 1, tok_off, done_len, B, eps, dtype, stream);
-    if (rc == LCA_OK && n_kv > 0) rc = launch_compress(all + 1, n_kv, tok_off, done_len, B, eps, dtype, stream);
+    int rc = launch_compress(all, 1, tok_off, done_len, B, eps, in_dtype, stream);
+    if (rc == LCA_OK && n_kv > 0) rc = launch_compress(all + 1, n_kv, tok_off, done_len, B, eps, in_dtype, stream);
     if (rc != LCA_OK) return rc;
     return launch_index_score(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, scores, ws, dtype, stream);
   }
@@ -915,6 +1030,7 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
   const lca_compress_stream& in = *idx_stream;
   ap.s.src = in.src; ap.s.logits = in.logits; ap.s.out = in.out; ap.s.ent_off = in.ent_off;
   ap.s.C = in.C; ap.s.m = in.m; ap.s.w = in.w; ap.s.per_channel = in.per_channel; ap.s.rmsnorm = in.rmsnorm;
+  ap.s.fp8 = in.out_fp8;
   ap.s.max_entries = in.max_entries;
   ap.tok_off = tok_off;
   ap.done_len = done_len;
@@ -932,11 +1048,17 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
   const size_t hist_lds = (size_t)tq * kHistBins * 4;
   const size_t lds = clds > hist_lds ? clds : hist_lds;
   dim3 grid((unsigned)blocks);
-#define LCA_APPEND(KSv)                                                                                          \
+#define LCA_APPEND2(KSv, F8)                                                                                     \
   switch (tq) {                                                                                                  \
-    case 1: hipLaunchKernelGGL((index_score_append<KSv, 1>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
-    case 2: hipLaunchKernelGGL((index_score_append<KSv, 2>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
-    default: hipLaunchKernelGGL((index_score_append<KSv, 4>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
+    case 1: hipLaunchKernelGGL((index_score_append<KSv, 1, F8>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
+    case 2: hipLaunchKernelGGL((index_score_append<KSv, 2, F8>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
+    default: hipLaunchKernelGGL((index_score_append<KSv, 4, F8>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
+  }
+#define LCA_APPEND(KSv)        \
+  if (fp8k) {                  \
+    LCA_APPEND2(KSv, true)     \
+  } else {                     \
+    LCA_APPEND2(KSv, false)    \
   }
   switch (dI / 32) {
     case 1: LCA_APPEND(1) break;
@@ -945,6 +1067,7 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
     default: LCA_APPEND(8) break;
   }
 #undef LCA_APPEND
+#undef LCA_APPEND2
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 

@@ -9,7 +9,7 @@ from typing import Optional, Sequence
 import ctypes
 import torch
 
-from ._lib import (LCA_BF16, LCA_F32, LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_TOPK, LCA_SRC_WINDOW, AttnSource, CompressStream,
+from ._lib import (LCA_BF16, LCA_BF16_FP8KEY, LCA_F32, LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_TOPK, LCA_SRC_WINDOW, AttnSource, CompressStream,
                    Partial, check, lib)
 
 
@@ -19,6 +19,16 @@ def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return LCA_F32
     raise TypeError(f"unsupported element type {t.dtype} (bfloat16 or float32)")
+
+
+def _index_dtype(p: torch.Tensor, ikey: torch.Tensor) -> int:
+    """Element type code of an index-score call: the query's type, or
+    LCA_BF16_FP8KEY for a uint8 key cache of fp8 rows (d_I + 8 bytes each)."""
+    if ikey.dtype == torch.uint8:
+        if p.dtype != torch.bfloat16 or ikey.dim() != 2 or ikey.shape[1] != p.shape[-1] + 8:
+            raise TypeError("fp8 key rows: bf16 queries and a uint8 cache of d_I + 8 bytes per row")
+        return LCA_BF16_FP8KEY
+    return _dtype_code(p)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -66,12 +76,19 @@ def _stream_array(streams: Sequence[dict]):
         d = _dtype_code(src)
         if dt is None:
             dt = d
-        if d != dt or _dtype_code(lg) != d or _dtype_code(out) != d:
-            raise TypeError("one element type per call")
+        fp8 = int(s.get("fp8", 0))
         C = src.shape[-1]
+        if fp8:
+            # fp8 key rows: C E4M3 bytes, the fp32 scale, 4 zero bytes
+            if out.dtype != torch.uint8 or out.dim() != 2 or out.shape[1] != C + 8:
+                raise TypeError("fp8 rows: a uint8 output of C + 8 bytes per row")
+        elif _dtype_code(out) != d:
+            raise TypeError("one element type per call")
+        if d != dt or _dtype_code(lg) != d:
+            raise TypeError("one element type per call")
         pc = 1 if lg.dim() == 2 else 0
         arr[i] = CompressStream(src.data_ptr(), lg.data_ptr(), out.data_ptr(), eo.data_ptr(), C, int(s["m"]),
-                                int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]))
+                                int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]), fp8)
     return arr, dt
 
 
@@ -112,7 +129,7 @@ def csa_index_topk(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: int, max_e
         idx = torch.empty((rows, k), dtype=torch.int32, device=p.device)
     check(lib.lca_csa_index_topk(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B, Tq, HI, dI, k, m,
                                  w, int(max_entries), _ptr(idx), _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
-                                 _dtype_code(p), _stream()), "csa_index_topk")
+                                 _index_dtype(p, ikey), _stream()), "csa_index_topk")
     return idx
 
 
@@ -124,7 +141,7 @@ def csa_index_score(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: int, max_
     rows = q_pos.numel()
     check(lib.lca_csa_index_score(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B, rows // B,
                                   p.shape[-2], p.shape[-1], k, m, w, int(max_entries), _ptr(scores), _ptr(ws),
-                                  ws.numel() * ws.element_size(), _dtype_code(p), _stream()), "csa_index_score")
+                                  ws.numel() * ws.element_size(), _index_dtype(p, ikey), _stream()), "csa_index_score")
 
 
 def csa_index_score_append(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: int, max_entries: int,
@@ -147,7 +164,7 @@ def csa_index_score_append(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: in
     check(lib.lca_csa_index_score_append(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B,
                                          rows // B, p.shape[-2], p.shape[-1], k, m, w, int(max_entries), ia, ka,
                                          len(kv_streams), _ptr(tok_off), _ptr(done_len), float(eps), _ptr(scores),
-                                         _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(p), _stream()),
+                                         _ptr(ws), ws.numel() * ws.element_size(), _index_dtype(p, ikey), _stream()),
           "csa_index_score_append")
 
 

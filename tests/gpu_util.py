@@ -31,7 +31,27 @@ def to_device(raw, cfg, dev="cuda"):
 
 def layer_for(cfg, **kw):
     from long_context_attention_20_amd import HybridAttention
+    kw.setdefault("ikey_fp8", getattr(cfg, "ikey", "bf16") == "fp8")
     return HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps, **kw)
+
+
+def fp8_rows(t):
+    """An fp8 key cache (uint8 rows: d_I E4M3 bytes, fp32 scale, 4 zero bytes)
+    -> (q [N, d_I] float64 E4M3 values, s [N] float64 scales, pad [N, 4])."""
+    t = t.contiguous().cpu()
+    dI = t.shape[1] - 8
+    q = t[:, :dI].contiguous().view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    s = t[:, dI:dI + 4].contiguous().view(torch.float32).to(torch.float64).numpy()[:, 0]
+    return q, s, t[:, dI + 4:].numpy()
+
+
+def key_rows(ikey):
+    """The indexer-key rows a cache stands for (float64): bf16/fp32 rows as
+    they are, fp8 rows as scale * value."""
+    if ikey.dtype == torch.uint8:
+        q, s, _ = fp8_rows(ikey)
+        return q * s[:, None]
+    return f64(ikey)
 
 
 def f64(t):

@@ -247,3 +247,31 @@ def test_hybrid_attn_merge_rejects(L):
     assert call() == L.LCA_ERR_INVALID_ARG                      # a source with no split
     gather(n_split=300)
     assert call() == L.LCA_ERR_INVALID_ARG                      # beyond 256 splits per source
+
+
+
+def test_fp8_key_rows_rejects(L):
+    """fp8 key rows: the compression takes them only from bf16 input streams
+    of at most 512 channels with small windows; the index calls only with
+    d_I in {32, 64, 128, 256}; the fused append only with an indexer stream
+    that writes them; nothing is launched on a rejected call."""
+    lib = L.lib
+    P = ctypes.c_void_p(256)
+    tok = ctypes.c_void_p(512)
+
+    def compress(C=64, m=4, w=8, dtype=1, fp8=1):
+        st = (L.CompressStream * 1)()
+        st[0] = L.CompressStream(256, 256, 256, 256, C, m, w, 1, 0, 10, fp8)
+        return lib.lca_kv_compress(st, 1, tok, None, 1, 1e-6, dtype, None)
+    assert compress(dtype=0) == L.LCA_ERR_UNSUPPORTED                 # fp32 input
+    assert compress(C=1024) == L.LCA_ERR_UNSUPPORTED                  # wider than 512
+    assert compress(m=128, w=128) == L.LCA_ERR_UNSUPPORTED            # a large window
+    assert compress(fp8=2) == L.LCA_ERR_INVALID_ARG
+    need = lib.lca_csa_index_topk_workspace(1, 1000, 64)
+    rc = lib.lca_csa_index_score(P, P, P, P, P, 1, 1, 4, 40, 64, 4, 8, 1000, None, P, need, 2, None)
+    assert rc == L.LCA_ERR_UNSUPPORTED                                  # d_I = 40
+    idx = (L.CompressStream * 1)()
+    idx[0] = L.CompressStream(256, 256, 256, 256, 64, 4, 8, 1, 0, 1, 0)   # writes bf16 rows
+    rc = lib.lca_csa_index_score_append(P, P, P, P, P, 1, 1, 4, 64, 512, 4, 8, 1000, idx, None, 0, P, P,
+                                        1e-6, None, P, lib.lca_csa_index_topk_workspace(1, 1000, 512), 2, None)
+    assert rc == L.LCA_ERR_INVALID_ARG

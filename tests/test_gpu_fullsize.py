@@ -16,7 +16,9 @@ from oracle import compress as ocmp
 from oracle import indexer as oidx
 from oracle import numerics as onum
 
-from gpu_util import assert_close, check_topk, f64, layer_for, score_bound
+from oracle import quant as oquant
+
+from gpu_util import assert_close, check_topk, f64, key_rows, layer_for, score_bound
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -56,13 +58,21 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
         u, c = _host(raw["u"][s0:s1]), _host(raw["c"][s0:s1])
         co, ho = caches.csa_off_h, caches.hca_off_h
         kv_csa = f64(caches.kv_csa[co[b]:co[b + 1]])
-        ikey = f64(caches.ikey[co[b]:co[b + 1]])
+        ikey = key_rows(caches.ikey[co[b]:co[b + 1]])
+        fp8 = caches.ikey.dtype == torch.uint8
         kv_hca = f64(caches.kv_hca[ho[b]:ho[b + 1]])
         ncsa, nhca = ocmp.n_entries(L, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m2, cfg.w2)
         # ---- compression on sampled entries (and the appended last ones)
         ent = sorted(set(rng.choice(ncsa, size=min(48, ncsa), replace=False).tolist()) | {ncsa - 1})
         for got, src, lg, norm in ((kv_csa, x, a, True), (ikey, u, c, False)):
-            ref = onum.round_to(ocmp.compress(src, lg, cfg.m, cfg.w, norm, cfg.eps, ent), cfg.dtype)
+            pooled = ocmp.compress(src, lg, cfg.m, cfg.w, norm, cfg.eps, ent)
+            if fp8 and got is ikey:
+                # fp8 rows: the oracle's quantization, or one E4M3 step from it
+                ref = oquant.dequantize_rows(*oquant.quantize_rows(pooled))
+                sc = np.max(np.abs(ref), axis=1, keepdims=True) / 448.0
+                assert np.all(np.abs(got[ent] - ref) <= 2.0 ** -3 * np.abs(ref) + 2.0 ** -9 * sc + 1e-30)
+                continue
+            ref = onum.round_to(pooled, cfg.dtype)
             assert np.max(np.abs(got[ent] - ref)) <= 2e-2
         entj = sorted(set(rng.choice(nhca, size=min(16, nhca), replace=False).tolist()) | {nhca - 1})
         ref = onum.round_to(ocmp.compress(x, g, cfg.m2, cfg.w2, True, cfg.eps, entj), cfg.dtype)
@@ -101,7 +111,9 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
             # ---- end to end: oracle keys from raw inputs, if the selected sets agree
             if not diff:
                 if ikey_o is None:
-                    ikey_o = onum.round_to(ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps), cfg.dtype)
+                    pooled_k = ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps)
+                    ikey_o = (oquant.dequantize_rows(*oquant.quantize_rows(pooled_k)) if fp8
+                              else onum.round_to(pooled_k, cfg.dtype))
                 sel_o = oidx.topk(oidx.scores(p, om, ikey_o[:nv]), cfg.k)
                 kv_sel = onum.round_to(ocmp.compress(x, a, cfg.m, cfg.w, True, cfg.eps, sorted(sel_o)), cfg.dtype)
                 kv_h = onum.round_to(ocmp.compress(x, g, cfg.m2, cfg.w2, True, cfg.eps, list(range(nh))), cfg.dtype)
@@ -129,6 +141,14 @@ def test_pro_1m_mtp2_full():
     cfg = li.PRO_1M_MTP2
     raw, layer, caches, bufs, out = _run(cfg, side=False)
     _check_rows(cfg, raw, caches, bufs, out, [0], np.random.default_rng(4))
+
+
+def test_pro_1m_decode_fp8_full():
+    """The Pro 1M decode with the indexer-key cache as fp8 rows (E4M3 bytes and
+    a scale per entry), in the configuration the benchmark times for it."""
+    cfg = li.PRO_1M_DECODE_FP8
+    raw, layer, caches, bufs, out = _run(cfg, side=False)
+    _check_rows(cfg, raw, caches, bufs, out, [0], np.random.default_rng(5))
 
 
 def test_pro_varlen_full():

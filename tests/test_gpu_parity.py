@@ -15,9 +15,10 @@ from oracle import compress as ocmp
 from oracle import indexer as oidx
 from oracle import numerics as onum
 from oracle import pipeline as opipe
+from oracle import quant as oquant
 
-from gpu_util import (TOL, assert_close, check_topk, f64, layer_for, merge_splits, run_gpu, score_bound,
-                      seq_caches, tdtype, to_device)
+from gpu_util import (TOL, assert_close, check_topk, f64, fp8_rows, key_rows, layer_for, merge_splits, run_gpu,
+                      score_bound, seq_caches, tdtype, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -662,6 +663,127 @@ def test_topk_crowded_zero_ties(path):
             o_ref, _ = oatt.merge([oatt.partial(qhat, kv_csa[chosen], cfg.scale),
                                    oatt.partial(qhat, kv_hca[:nh], cfg.scale), oatt.partial(qhat, win, cfg.scale)], sig)
             assert_close(f64(out)[t], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"ties row {t}")
+
+
+def _check_fp8_cache(cfg, raw, ikey, csa_off_h):
+    """The fp8 key rows against the oracle's quantization of its own pooled keys:
+    scales within fp32 rounding, every byte the oracle's value or (where the
+    fp32 pooling sits on a rounding boundary) its grid neighbour, pad zero."""
+    q, s, pad = fp8_rows(ikey)
+    assert np.all(pad == 0)
+    off = raw["tok_off"]
+    flips = total = 0
+    for b in range(cfg.B):
+        u = raw["u"][off[b]:off[b + 1]].astype(np.float64)
+        c = raw["c"][off[b]:off[b + 1]].astype(np.float64)
+        qr, sr = oquant.quantize_rows(ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps))
+        qg, sg = q[csa_off_h[b]:csa_off_h[b + 1]], s[csa_off_h[b]:csa_off_h[b + 1]]
+        assert np.all(np.abs(sg - sr) <= 2.0 ** -20 * sr), f"sequence {b}: scales"
+        d = np.abs(qg - qr)
+        assert np.all(d <= 2.0 ** -3 * np.maximum(np.abs(qg), np.abs(qr)) + 2.0 ** -9), f"sequence {b}: more than one step"
+        flips += int(np.sum(d > 0))
+        total += qr.size
+    assert flips <= max(2, total // 1000), f"{flips} of {total} bytes off the oracle"
+    return q, s
+
+
+@pytest.mark.parametrize("tq", [1, 2])
+def test_fp8_key_cache_and_scores(tq):
+    """Indexer keys kept as fp8 rows (E4M3 bytes and an fp32 scale per entry):
+    the compression writes the oracle's quantization, and the scores read from
+    the rows (bytes widened to bf16 on the matrix cores, times the scale) are
+    the oracle's scores of the rows they stand for within fp32 rounding; the
+    selections are the exact top-k of the GPU scores and the oracle's except
+    at near ties.  One and two query rows per sequence."""
+    from long_context_attention_20_amd import ops
+    cfg = li.small(f"fp8k{tq}", 123, (9000, 4101, 777), tq=tq, H=64, D=512, k=256, ikey="fp8")
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    torch.cuda.synchronize()
+    print(f"[fp8 keys] tq={tq} lens={cfg.lens} rows {caches.ikey.shape}", flush=True)
+    q, s = _check_fp8_cache(cfg, raw, caches.ikey, caches.csa_off_h)
+    maxN = ocmp.n_entries(max(cfg.lens), cfg.m, cfg.w)
+    rows = cfg.B * tq
+    ws = layer.index_workspace(rows, maxN, "cuda")
+    sc = torch.full((rows, maxN), float("nan"), dtype=torch.float32, device="cuda")
+    idx = ops.csa_index_topk(d["p"], d["omega"], caches.ikey, caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w, maxN,
+                             ws, scores=sc)
+    torch.cuda.synchronize()
+    idx_h, sc_h = idx.cpu().numpy(), sc.cpu().numpy()
+    co = caches.csa_off_h
+    for b in range(cfg.B):
+        for t in range(tq):
+            r = b * tq + t
+            nv = ocmp.n_visible(int(raw["q_pos"][b, t]), cfg.m, cfg.w)
+            qb, sb = q[co[b]:co[b] + nv], s[co[b]:co[b] + nv]
+            p64 = raw["p"][r].astype(np.float64)
+            om = raw["omega"][r].astype(np.float64)
+            s_ref = oquant.scores_fp8(p64, om, qb, sb)
+            check_topk(idx_h[r], sc_h[r], s_ref, score_bound(p64, om, qb * sb[:, None]), cfg.k)
+
+
+def test_decode_step_fp8_keys():
+    """A decode step over fp8 key rows: the fused append writes exactly the
+    bytes the cache build wrote, the selection inside the attention launch is
+    the exact top-k of the row's scores (oracle scores of the GPU rows, near
+    ties aside), and the output equals the oracle's attention over that
+    selection, end to end from raw inputs where the selected sets agree."""
+    cfg = li.small("fp8_decode", 124, (4001, 2600, 777, 4096), H=64, D=512, k=256, ikey="fp8")
+    raw = li.make_raw(cfg)
+    d, layer, caches, full, done, done_h, bufs = _decode_setup(cfg, raw)
+    out = layer.decode_step(caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs,
+                            done_len=done, done_h=done_h)
+    torch.cuda.synchronize()
+    assert torch.equal(caches.kv_csa, full[0]) and torch.equal(caches.kv_hca, full[2])
+    # the appended fp8 rows are the build's up to the fp32 rounding of the
+    # pooling (the stored scale shows every bit of it): other rows untouched,
+    # scales within fp32 rounding, bytes within one E4M3 step
+    qa, sa, pa = fp8_rows(caches.ikey)
+    qb, sb, _ = fp8_rows(full[1])
+    appended = set()
+    for b, L in enumerate(cfg.lens):
+        n0, n1 = ocmp.n_entries(L - 1, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m, cfg.w)
+        appended |= set(range(int(caches.csa_off_h[b]) + n0, int(caches.csa_off_h[b]) + n1))
+    differ = set(np.nonzero(np.any(qa != qb, axis=1) | (sa != sb))[0].tolist())
+    print(f"[fp8 decode] appended rows {sorted(appended)}, differing from the build {sorted(differ)}", flush=True)
+    assert differ <= appended
+    assert np.all(pa == 0) and np.all(np.abs(sa - sb) <= 2.0 ** -20 * sb)
+    assert np.all(np.abs(qa - qb) <= 2.0 ** -3 * np.maximum(np.abs(qa), np.abs(qb)) + 2.0 ** -9)
+    _check_fp8_cache(cfg, raw, caches.ikey, caches.csa_off_h)
+    keys = key_rows(caches.ikey)
+    _, ores = opipe.run(raw, cfg)
+    idx_h = bufs["idx"].cpu().numpy()
+    out_h = f64(out)
+    co, ho = caches.csa_off_h, caches.hca_off_h
+    kv_csa, kv_hca = f64(caches.kv_csa), f64(caches.kv_hca)
+    off = raw["tok_off"]
+    for b in range(cfg.B):
+        i = cfg.lens[b] - 1
+        nv = ocmp.n_visible(i, cfg.m, cfg.w)
+        kb = keys[co[b]:co[b] + nv]
+        p64 = raw["p"][b].astype(np.float64)
+        om = raw["omega"][b].astype(np.float64)
+        s_ref = oidx.scores(p64, om, kb)
+        sel = idx_h[b]
+        chosen = sel[sel >= 0]
+        ref = oidx.topk(s_ref, cfg.k)
+        kth = s_ref[ref[-1]] if len(ref) else 0.0
+        bound = score_bound(p64, om, kb)
+        for j in set(chosen.tolist()) ^ set(ref.tolist()):
+            assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + 2 * bound[j], f"row {b}: {j} not a near tie"
+        qhat = oatt.normalize_query(raw["q"][b].astype(np.float64), cfg.eps, cfg.dtype)
+        x = raw["x"][off[b]:off[b + 1]].astype(np.float64)
+        win = oatt.normalize_tokens(x[max(0, i - cfg.W + 1):i + 1], cfg.eps, cfg.dtype)
+        nh = ocmp.n_visible(i, cfg.m2, cfg.w2)
+        o_ref, _ = oatt.merge([oatt.partial(qhat, kv_csa[co[b] + chosen], cfg.scale),
+                               oatt.partial(qhat, kv_hca[ho[b]:ho[b] + nh], cfg.scale),
+                               oatt.partial(qhat, win, cfg.scale)], raw["sigma"].astype(np.float64))
+        assert_close(out_h[b], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"fp8 decode row {b}")
+        if set(chosen.tolist()) == set(ores[(b, 0)]["sel"].tolist()):
+            assert_close(out_h[b], ores[(b, 0)]["out"], cfg.dtype, f"fp8 decode row {b} e2e")
 
 def _topk_direct(ikey, p, omega, k, n_entries):
     """csa_index_topk over one row whose query sees every entry of ikey."""

@@ -44,6 +44,8 @@ def test_presets_match_page_constants():
     assert li.PRO_1M_DECODE.lens[0] == g["context"]["value"]
     # the two-row decode is the Pro 1M decode with one drafted token beside the main one
     assert li.PRO_1M_MTP2 == li.PRO_1M_DECODE.with_(name="pro_1m_mtp2", cfg_id=li.PRO_1M_MTP2.cfg_id, tq=2)
+    # the fp8-key decode draws the same inputs as the Pro 1M decode
+    assert li.PRO_1M_DECODE_FP8 == li.PRO_1M_DECODE.with_(name="pro_1m_decode_fp8", ikey="fp8")
 
 
 def test_entry_counts_match_workloads():
