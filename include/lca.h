@@ -174,8 +174,10 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
  * further blocks of the same launch; no block reads what another writes.
  * With 2 <= Tq <= 4 and Tq * H_I <= 16 the rows of a sequence share one read
  * of the keys (one matrix-core product scores them all).  The caches written
- * are bit-identical to lca_kv_compress's; the new entries' scores agree
- * within rounding order.  Falls back to those two calls where the fused
+ * are bit-identical to lca_kv_compress's for bf16 rows; fp8 key rows
+ * (dtype LCA_BF16_FP8KEY, idx_stream->out_fp8 = 1) agree up to the fp32
+ * rounding of the pooling (the stored scale shows it); the new entries'
+ * scores agree within rounding order.  Falls back to those two calls where the fused
  * launch does not apply: fp32, d_I not in {32, 64, 128, 256}, an indexer
  * window other than w = m or w = 2m <= 16, kv streams wider than 512 bf16
  * channels, Tq > 1 outside the shared-read bounds above.
