@@ -57,8 +57,8 @@ TRAFFIC = {
         "files": ["long_context_attention_20_amd/csrc/lca_attention.hip",
                   "long_context_attention_20_amd/csrc/lca_common.h",
                   "long_context_attention_20_amd/csrc/lca_topk.h"],
-        "sha1": "349a35f21acbded9566d0baee2b2aed6f84e167d",
-        "fetch_kib": 6319.6, "write_kib": 15476.9, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha1": "487e30f3cc2f5e0f92d3d48f38cc476e22fc3f22",
+        "fetch_kib": 6320.4, "write_kib": 15477.5, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 

@@ -126,7 +126,11 @@ __device__ __forceinline__ void filter_prefetch(const TopkWs& w, int r, int cb0,
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int64_t base = (int64_t)(cb0 + c * stride) * NT * PER;
-    if (c > 0 && base >= w.max_entries) continue;  // past every row's columns: never visible (uniform)
+    if (c > 0 && base >= w.max_entries) {  // past every row's columns: never visible (uniform)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) P.sv[c][i] = 0.f;
+      continue;
+    }
     const int64_t e0 = base + (int64_t)threadIdx.x * PER;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {

@@ -545,14 +545,16 @@ def test_index_score_multi_rows_match_single_rows(tq, HI, dI):
             assert np.all(err <= 2 * bound + 1e-6), f"row ({b}, {t}): scores off the oracle"
 
 
-@pytest.mark.parametrize("tq", [2, 3])
-def test_decode_step_mtp(tq):
+@pytest.mark.parametrize("tq,ikey", [(2, "bf16"), (3, "bf16"), (2, "fp8")])
+def test_decode_step_mtp(tq, ikey):
     """A decode step with tq query rows per sequence (the main token and
     drafted ones, checked together): the appends of every entry the tq new
     tokens complete, the multi-row scores, the selection inside the attention
     launch and the merge, against the oracle row by row.  The sequences'
-    last tokens complete no entry, a CSA/indexer entry, and an HCA entry."""
-    cfg = li.small(f"mtp{tq}", 121, (4001, 2600, 777, 4096), tq=tq, H=64, D=512, k=256)
+    last tokens complete no entry, a CSA/indexer entry, and an HCA entry.
+    With fp8 key rows the appended rows match the build up to the fp32
+    rounding of the pooling, and the selections the oracle's up to near ties."""
+    cfg = li.small(f"mtp{tq}", 121, (4001, 2600, 777, 4096), tq=tq, H=64, D=512, k=256, ikey=ikey)
     raw = li.make_raw(cfg)
     d = to_device(raw, cfg)
     layer = layer_for(cfg)
@@ -576,17 +578,42 @@ def test_decode_step_mtp(tq):
     out = layer.decode_step(caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs,
                             done_len=done, done_h=done_h)
     torch.cuda.synchronize()
+    fp8 = ikey == "fp8"
     for got, ref, name in zip((caches.kv_csa, caches.ikey, caches.kv_hca), full, ("kv_csa", "ikey", "kv_hca")):
+        if fp8 and name == "ikey":
+            qa, sa, _ = fp8_rows(got)
+            qb, sb, _ = fp8_rows(ref)
+            assert np.all(np.abs(sa - sb) <= 2.0 ** -20 * sb)
+            assert np.all(np.abs(qa - qb) <= 2.0 ** -3 * np.maximum(np.abs(qa), np.abs(qb)) + 2.0 ** -9)
+            continue
         assert torch.equal(got, ref), f"{name}: the step did not restore exactly the entries the new tokens complete"
     _, ores = opipe.run(raw, cfg)
     idx_h = bufs["idx"].cpu().numpy()
     out_h = f64(out)
+    keys = key_rows(caches.ikey)
+    co = caches.csa_off_h
     for b in range(cfg.B):
         for t in range(tq):
             r = b * tq + t
             res = ores[(b, t)]
-            assert set(idx_h[r][idx_h[r] >= 0].tolist()) == set(res["sel"].tolist()), f"row ({b}, {t}) selection"
-            assert_close(out_h[r], res["out"], cfg.dtype, f"mtp row ({b}, {t})")
+            chosen = set(idx_h[r][idx_h[r] >= 0].tolist())
+            if not fp8:
+                assert chosen == set(res["sel"].tolist()), f"row ({b}, {t}) selection"
+                assert_close(out_h[r], res["out"], cfg.dtype, f"mtp row ({b}, {t})")
+                continue
+            # fp8 keys: the exact top-k of the oracle scores of the GPU rows, near ties aside
+            i = int(raw["q_pos"][b, t])
+            nv = ocmp.n_visible(i, cfg.m, cfg.w)
+            kb = keys[co[b]:co[b] + nv]
+            p64, om = raw["p"][r].astype(np.float64), raw["omega"][r].astype(np.float64)
+            s_ref = oidx.scores(p64, om, kb)
+            ref = oidx.topk(s_ref, cfg.k)
+            kth = s_ref[ref[-1]]
+            bound = score_bound(p64, om, kb)
+            for j in chosen ^ set(ref.tolist()):
+                assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + 2 * bound[j], f"row ({b}, {t}): {j}"
+            if chosen == set(res["sel"].tolist()):
+                assert_close(out_h[r], res["out"], cfg.dtype, f"mtp fp8 row ({b}, {t})")
 
 
 @pytest.mark.parametrize("path", ["decode_two_rows", "many_rows"])
