@@ -264,7 +264,8 @@ def run_prefill(cfg, args, dev):
     import torch
     import lca_inputs as li
     from long_context_attention_20_amd import HybridAttention, ops
-    a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps)
+    a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
+                        ikey_fp8=cfg.ikey == "fp8")
     raw = li.make_raw_torch(cfg, 0, dev)
     caches = a.alloc_caches(cfg.lens, dev, raw["x"].dtype)
     a.compress(caches, raw, raw["tok_off"])

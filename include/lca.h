@@ -135,8 +135,8 @@ int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int
  *   ikey     [sum_b N, d_I]    indexer keys (dtype), packed by csa_off; with
  *            dtype LCA_BF16_FP8KEY: [sum_b N] fp8 rows of d_I + 8 bytes (see
  *            LCA_BF16_FP8KEY; p bf16), scored as the rows they stand for, for
- *            d_I in {32, 64, 128, 256} and fewer than 32 query rows per
- *            sequence (LCA_ERR_UNSUPPORTED otherwise)
+ *            d_I in {32, 64, 128, 256} and H_I <= 16 (LCA_ERR_UNSUPPORTED
+ *            otherwise)
  *   q_pos    device int32 [B*Tq]
  *   max_entries  host bound on the candidates of any query (>= 1)
  *   scores   optional fp32 [B*Tq, max_entries] output of every candidate's

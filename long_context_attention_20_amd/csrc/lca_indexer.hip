@@ -565,7 +565,7 @@ static bool rows_mode(int Tq, int64_t maxN) { return Tq >= kRowsPerBlock && maxN
 // the rows of a sequence share one score block (score_chunk_multi)
 static bool multi_rows_ok(int Tq, int HI) { return Tq >= 2 && Tq <= 4 && Tq * HI <= 16; }
 
-template <int KS, int HI>
+template <int KS, int HI, bool FP8K = false>
 __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
   constexpr int QR = 16 / HI;                // query rows per MFMA row block
   constexpr int RB = kRowsPerBlock / QR;     // MFMA row blocks per block
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (ok) v = *reinterpret_cast<const uint4*>(P + ((int64_t)(r0 + qr) * HI + col % HI) * a.dI + ks * 32 + grp * 8);
+      if (ok) v = *reinterpret_cast<const uint4*>(P + ((int64_t)(r0 + qr) * HI + col % HI) * a.dI + key_dim<KS>(ks, grp, FP8K));
       A[rb][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
     // weights of the accumulator rows 4*grp + i: (row rb*QR + (4*grp + i)/HI, head (4*grp + i)%HI)
@@ -612,22 +612,35 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
       om[rb][i] = q2 < nrows ? a.omega[(int64_t)(r0 + q2) * HI + m % HI] : 0.f;
     }
   }
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.ikey) + e_base * a.dI;
+  const char* K = reinterpret_cast<const char*>(a.ikey);
+  const int64_t rowb = key_row_bytes(a, FP8K);
   constexpr int EB = 4;  // 16-entry blocks in flight
   const int64_t wend = min(w0 + kRowsEntriesPerWave, min(nv_max, a.max_entries));
   for (int64_t e0 = w0; e0 < wend; e0 += 16 * EB) {
     uint4 kv[EB][KS];
+    uint2 k8[EB][KS];
+    float rscale[EB];
 #pragma unroll
     for (int u = 0; u < EB; ++u) {
       int64_t e = e0 + u * 16 + col;
       if (e >= nseq) e = nseq - 1;  // clamp: stays inside the sequence's keys
+      const char* row = K + (e_base + e) * rowb;
+      if constexpr (FP8K) {
+        load_fp8_slices<KS>(row, grp, k8[u]);
+        rscale[u] = *reinterpret_cast<const float*>(row + a.dI);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(K + e * a.dI + ks * 32 + grp * 8);
+        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
+      }
     }
 #pragma unroll
     for (int u = 0; u < EB; ++u) {
       const int64_t e = e0 + u * 16 + col;
       const bool e_ok = e < wend;
+      if constexpr (FP8K) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -640,6 +653,7 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
 #pragma unroll
           for (int h = 0; h < HI; ++h) sc = fmaf(om[rb][q * HI + h], fmaxf(acc[q * HI + h], 0.f), sc);
           const int qr = rb * QR + (4 * grp) / HI + q;
+          if constexpr (FP8K) sc *= rscale[u];
           if (e_ok && qr < nrows) a.scores[(int64_t)(r0 + qr) * a.max_entries + e] = sc;
         }
       }
@@ -919,20 +933,25 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
   dim3 g1((unsigned)((maxN + a.chunk - 1) / a.chunk), (unsigned)rows);
   const bool fp8k = dtype == LCA_BF16_FP8KEY;
   const bool mfma = (dtype == LCA_BF16 || fp8k) && HI <= 16 && (dI % 32) == 0 && dI <= 256;
-  if (fp8k && (!mfma || a.no_hist)) {
-    set_error("csa_index_score: fp8 key rows are scored for H_I <= 16 and fewer than %d rows per sequence",
-              kRowsPerBlock);
+  if (fp8k && !mfma) {
+    set_error("csa_index_score: fp8 key rows are scored for H_I <= 16 and d_I in {32, 64, 128, 256}");
     return LCA_ERR_UNSUPPORTED;
   }
   if (mfma && a.no_hist && (HI == 1 || HI == 2 || HI == 4)) {
     // many rows per sequence: the row-tiled kernel
     const int gps = (Tq + kRowsPerBlock - 1) / kRowsPerBlock;
     dim3 g((unsigned)((maxN + 4 * kRowsEntriesPerWave - 1) / (4 * kRowsEntriesPerWave)), (unsigned)(B * gps));
-#define LCA_ROWS(KSv)                                                                                      \
+#define LCA_ROWS2(KSv, F8)                                                                                 \
   switch (HI) {                                                                                            \
-    case 1: hipLaunchKernelGGL((index_score_rows<KSv, 1>), g, dim3(256), 0, stream, a); break;           \
-    case 2: hipLaunchKernelGGL((index_score_rows<KSv, 2>), g, dim3(256), 0, stream, a); break;           \
-    default: hipLaunchKernelGGL((index_score_rows<KSv, 4>), g, dim3(256), 0, stream, a); break;          \
+    case 1: hipLaunchKernelGGL((index_score_rows<KSv, 1, F8>), g, dim3(256), 0, stream, a); break;       \
+    case 2: hipLaunchKernelGGL((index_score_rows<KSv, 2, F8>), g, dim3(256), 0, stream, a); break;       \
+    default: hipLaunchKernelGGL((index_score_rows<KSv, 4, F8>), g, dim3(256), 0, stream, a); break;      \
+  }
+#define LCA_ROWS(KSv)      \
+  if (fp8k) {              \
+    LCA_ROWS2(KSv, true)   \
+  } else {                 \
+    LCA_ROWS2(KSv, false)  \
   }
     switch (dI / 32) {
       case 1: LCA_ROWS(1) break;
@@ -941,6 +960,7 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
       default: LCA_ROWS(8) break;
     }
 #undef LCA_ROWS
+#undef LCA_ROWS2
     return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
   }
   if (mfma && multi_rows_ok(Tq, HI) && !a.no_hist) {

@@ -714,14 +714,15 @@ def _check_fp8_cache(cfg, raw, ikey, csa_off_h):
     return q, s
 
 
-@pytest.mark.parametrize("tq", [1, 2])
+@pytest.mark.parametrize("tq", [1, 2, 40])
 def test_fp8_key_cache_and_scores(tq):
     """Indexer keys kept as fp8 rows (E4M3 bytes and an fp32 scale per entry):
     the compression writes the oracle's quantization, and the scores read from
     the rows (bytes widened to bf16 on the matrix cores, times the scale) are
     the oracle's scores of the rows they stand for within fp32 rounding; the
     selections are the exact top-k of the GPU scores and the oracle's except
-    at near ties.  One and two query rows per sequence."""
+    at near ties.  One, two and 40 query rows per sequence (the row-tiled
+    scoring and the one-block-per-row selection)."""
     from long_context_attention_20_amd import ops
     cfg = li.small(f"fp8k{tq}", 123, (9000, 4101, 777), tq=tq, H=64, D=512, k=256, ikey="fp8")
     raw = li.make_raw(cfg)
