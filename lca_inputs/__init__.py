@@ -62,7 +62,7 @@ class Config:
     plant: int = 0
     eps: float = 1e-6
     logit_per_channel: bool = True
-    ikey: str = "bf16"  # indexer-key cache: "bf16" (the workload dtype) or "fp8" (E4M3 rows with a scale)
+    ikey: str = "bf16"  # indexer-key cache: "bf16" (the workload dtype), "fp8" (E4M3 rows with a scale) or "mxfp4"
 
     @property
     def scale(self) -> float:

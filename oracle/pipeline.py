@@ -50,10 +50,16 @@ def fp8_keys(cfg) -> bool:
 
 def build_seq_caches(x, a, g, u, c, cfg) -> SeqCaches:
     """Caches of one sequence from its raw streams (all float64 views).  With
-    fp8 indexer keys the key cache holds the rows they stand for (s * q)."""
+    fp8 or MXFP4 indexer keys the key cache holds the rows they stand for."""
     kv_csa = round_to(compress(x, a, cfg.m, cfg.w, True, cfg.eps), cfg.dtype)
     pooled = compress(u, c, cfg.m, cfg.w, False, cfg.eps)
-    ikey = quant.dequantize_rows(*quant.quantize_rows(pooled)) if fp8_keys(cfg) else round_to(pooled, cfg.dtype)
+    kind = getattr(cfg, "ikey", "bf16")
+    if kind == "fp8":
+        ikey = quant.dequantize_rows(*quant.quantize_rows(pooled))
+    elif kind == "mxfp4":
+        ikey = quant.dequantize_mx_rows(*quant.quantize_mx_rows(pooled))
+    else:
+        ikey = round_to(pooled, cfg.dtype)
     kv_hca = round_to(compress(x, g, cfg.m2, cfg.w2, True, cfg.eps), cfg.dtype)
     return SeqCaches(kv_csa, ikey, kv_hca)
 

@@ -471,3 +471,63 @@ def test_fp8_scores_reduce_to_plain_scores_on_the_grid():
     q2, s2 = quant.quantize_rows(off)
     assert not np.array_equal(quant.scores_fp8(p, om, q2, s2), idx.scores(p, om, off))
     assert np.allclose(quant.scores_fp8(p, om, q2, s2), idx.scores(p, om, q2 * s2[:, None]), rtol=0, atol=0)
+
+
+# --------------------------------------------------------------------------
+# MXFP4 (E2M1 elements, E8M0 block scales) indexer rows
+# --------------------------------------------------------------------------
+
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _e2m1_brute(x):
+    """Nearest grid value by enumeration; a tie goes to the value whose
+    mantissa bit is 0 (0, 1, 2, 4)."""
+    out = np.empty_like(x)
+    even = {0.0: True, 0.5: False, 1.0: True, 1.5: False, 2.0: True, 3.0: False, 4.0: True, 6.0: False}
+    for i, v in enumerate(np.abs(x)):
+        d = np.abs(E2M1_GRID - v)
+        best = np.nonzero(d == d.min())[0]
+        pick = [g for g in E2M1_GRID[best] if even[g]] if len(best) > 1 else list(E2M1_GRID[best])
+        out[i] = np.copysign(pick[0], x[i])
+    return out
+
+
+def test_e2m1_rounding_matches_brute_force():
+    rng = np.random.default_rng(10)
+    mids = (E2M1_GRID[:-1] + E2M1_GRID[1:]) / 2
+    x = np.concatenate([rng.uniform(-6, 6, 5000), E2M1_GRID, -E2M1_GRID, mids, -mids])
+    assert np.array_equal(quant.round_e2m1(x), _e2m1_brute(x))
+    assert np.array_equal(quant.round_e2m1(E2M1_GRID), E2M1_GRID)
+
+
+def test_mx_quantize_invariants():
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((300, 64)) * np.exp(rng.uniform(-5, 5, (300, 1)))
+    v[5, :32] = 0.0
+    q, s = quant.quantize_mx_rows(v)
+    assert s.shape == (300, 2) and s[5, 0] == 2.0 ** -127 and np.all(q[5, :32] == 0)
+    # power-of-two scales; the block maximum sits in [4, 8) before the clamp at 6
+    live = np.ones_like(s, dtype=bool)
+    live[5, 0] = False
+    assert np.all(np.log2(s) == np.round(np.log2(s)))
+    amax = np.max(np.abs(v.reshape(300, 2, 32)), axis=-1)
+    r = amax[live] / s[live]
+    assert np.all((r >= 4) & (r < 8))
+    assert set(np.unique(np.abs(q))).issubset(set(E2M1_GRID.tolist()))
+    # error: half a spacing of the element (at most 1 at the top binade), or the clamp from [6, 8)
+    err = np.abs(quant.dequantize_mx_rows(q, s) - v).reshape(300, 2, 32) / s[..., None]
+    a = np.abs(v.reshape(300, 2, 32)) / s[..., None]
+    assert np.all(err <= np.where(a >= 6, a - 6, np.maximum(0.25, np.where(a >= 4, 1.0, np.where(a >= 2, 0.5, 0.25)))) + 1e-12)
+
+
+def test_mx_scores_reduce_to_plain_scores_on_the_grid():
+    rng = np.random.default_rng(12)
+    keys = rng.choice(E2M1_GRID, (200, 64)) * rng.choice([-1, 1], (200, 64)) * 2.0 ** -3
+    keys[:, 0] = 4.0 * 2.0 ** -3
+    keys[:, 32] = -6.0 * 2.0 ** -3          # block maxima 4 and 6 times 2**-3: scale 2**-3
+    q, s = quant.quantize_mx_rows(keys)
+    assert np.all(s == 2.0 ** -3) and np.array_equal(quant.dequantize_mx_rows(q, s), keys)
+    p = rng.standard_normal((4, 64))
+    om = np.array([0.5, -1.0, 2.0, 0.25])
+    assert np.array_equal(idx.scores(p, om, quant.dequantize_mx_rows(q, s)), idx.scores(p, om, keys))
