@@ -89,7 +89,11 @@ def n_windows(L, m, w):
 def key_bytes(cfg):
     """Bytes of one indexer key in the cache: d_I elements, or for fp8 rows
     d_I E4M3 bytes + the fp32 scale + 4 pad bytes."""
-    return cfg.dI + 8 if cfg.ikey == "fp8" else cfg.dI * (2 if cfg.dtype == "bf16" else 4)
+    if cfg.ikey == "fp8":
+        return cfg.dI + 8
+    if cfg.ikey == "mxfp4":
+        return cfg.dI // 2 + 8
+    return cfg.dI * (2 if cfg.dtype == "bf16" else 4)
 
 
 def step_bytes(cfg):
@@ -191,7 +195,7 @@ class Runner:
         self.torch, self.ops = torch, ops
         self.cfg = cfg
         a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
-                            split_csa=split_csa or None, split_hca=split_hca or None, ikey_fp8=cfg.ikey == "fp8")
+                            split_csa=split_csa or None, split_hca=split_hca or None, ikey=cfg.ikey)
         self.attn = a
         self.layers = [LayerState(cfg, r, a, dev) for r in range(R)]
         rows = cfg.B * cfg.tq
@@ -265,7 +269,7 @@ def run_prefill(cfg, args, dev):
     import lca_inputs as li
     from long_context_attention_20_amd import HybridAttention, ops
     a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
-                        ikey_fp8=cfg.ikey == "fp8")
+                        ikey=cfg.ikey)
     raw = li.make_raw_torch(cfg, 0, dev)
     caches = a.alloc_caches(cfg.lens, dev, raw["x"].dtype)
     a.compress(caches, raw, raw["tok_off"])
@@ -373,6 +377,8 @@ def cpu_baseline(cfg, state, budget_s):
                 pooled = ocmp.compress(src, lg, m, w, norm, cfg.eps, new)
                 getattr(caches, name)[list(new)] = (oquant.dequantize_rows(*oquant.quantize_rows(pooled))
                                                     if name == "ikey" and cfg.ikey == "fp8"
+                                                    else oquant.dequantize_mx_rows(*oquant.quantize_mx_rows(pooled))
+                                                    if name == "ikey" and cfg.ikey == "mxfp4"
                                                     else onum.round_to(pooled, cfg.dtype))
         for q, p, om, i in rows:
             opipe.query_step(caches, x, q, p, om, sg, i, cfg)
@@ -558,8 +564,8 @@ def main():
 
     res = {
         "metric": ("decode query-tokens/s per layer at 1M ctx (Pro shape); % of HBM peak BW" if tq == 1 and
-                   cfg.ikey != "fp8" else
-                   "decode query-tokens/s per layer at 1M ctx (Pro shape, fp8 indexer keys); % of HBM peak BW"
+                   cfg.ikey == "bf16" else
+                   f"decode query-tokens/s per layer at 1M ctx (Pro shape, {cfg.ikey} indexer keys); % of HBM peak BW"
                    if tq == 1 else
                    f"decode query-tokens/s per layer at 1M ctx (Pro shape, {tq} query rows per step: the main token "
                    f"and {tq - 1} drafted); % of HBM peak BW"),

@@ -47,7 +47,7 @@ enum lca_status {
   LCA_ERR_HIP = -4          /* the HIP runtime reported an error */
 };
 
-enum lca_dtype { LCA_F32 = 0, LCA_BF16 = 1, LCA_BF16_FP8KEY = 2 };
+enum lca_dtype { LCA_F32 = 0, LCA_BF16 = 1, LCA_BF16_FP8KEY = 2, LCA_BF16_MXFP4KEY = 3 };
 /* LCA_BF16_FP8KEY (index-score calls only): indexer queries p bf16, weights
  * fp32, and the indexer-key cache in fp8 rows: d_I OCP E4M3 bytes (1 sign, 4
  * exponent bits of bias 7, 3 mantissa bits; largest finite 448), then the
@@ -55,7 +55,15 @@ enum lca_dtype { LCA_F32 = 0, LCA_BF16 = 1, LCA_BF16_FP8KEY = 2 };
  * stands for s * q (s = max|key| / 448, q rounded to nearest even); its score
  * is the bf16 formula on that row ("DeepSeek-V4", Inference efficiency: the
  * indexer's query-key path in low precision).  Written by lca_kv_compress
- * with out_fp8 = 1. */
+ * with out_key = 1.
+ * LCA_BF16_MXFP4KEY (index-score calls only): as LCA_BF16_FP8KEY with MXFP4
+ * key rows (OCP microscaling FP4): d_I/2 bytes of E2M1 elements (1 sign, 2
+ * exponent bits of bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6; two per
+ * byte, the even channel in the low nibble), then one E8M0 scale byte per 32
+ * channels (2**(byte - 127)), zero-padded -- d_I/2 + 8 bytes per entry.  A
+ * block's scale is 2**(floor(log2 amax) - 2), its elements value / scale
+ * rounded to nearest even and clamped to +-6 (scale 2**-127 and zero elements
+ * for an all-zero block).  Written by lca_kv_compress with out_key = 2. */
 
 /* Static text for a status code. */
 const char* lca_strerror(int status);
@@ -98,8 +106,10 @@ typedef struct lca_compress_stream {
   int32_t per_channel;    /* 1: logits [T, C]; 0: logits [T]                          */
   int32_t rmsnorm;        /* 1: RMS-normalise each entry over its C channels          */
   int32_t max_entries;    /* host bound on entries written per sequence (>= 0)        */
-  int32_t out_fp8;        /* 1: write fp8 key rows (see LCA_BF16_FP8KEY): bf16 input,  */
-                          /* C <= 512, w = m or w = 2m <= 16; 0: rows of the input type */
+  int32_t out_key;        /* 0: rows of the input type; 1: fp8 key rows (see          */
+                          /* LCA_BF16_FP8KEY), 2: MXFP4 key rows (LCA_BF16_MXFP4KEY):  */
+                          /* bf16 input, C <= 512 (MXFP4: C in {32,64,128,256}),       */
+                          /* w = m or w = 2m <= 16                                      */
 } lca_compress_stream;
 
 /* Compress up to 4 streams in one launch.
@@ -133,8 +143,8 @@ int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int
  *   p        [B*Tq, H_I, d_I]  indexer queries (dtype)
  *   omega    [B*Tq, H_I]       fp32 head weights
  *   ikey     [sum_b N, d_I]    indexer keys (dtype), packed by csa_off; with
- *            dtype LCA_BF16_FP8KEY: [sum_b N] fp8 rows of d_I + 8 bytes (see
- *            LCA_BF16_FP8KEY; p bf16), scored as the rows they stand for, for
+ *            dtype LCA_BF16_FP8KEY / LCA_BF16_MXFP4KEY: [sum_b N] key rows of
+ *            d_I + 8 / d_I/2 + 8 bytes (p bf16), scored as the rows they stand for, for
  *            d_I in {32, 64, 128, 256} and H_I <= 16 (LCA_ERR_UNSUPPORTED
  *            otherwise)
  *   q_pos    device int32 [B*Tq]
@@ -179,7 +189,8 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
  * With 2 <= Tq <= 4 and Tq * H_I <= 16 the rows of a sequence share one read
  * of the keys (one matrix-core product scores them all).  The caches written
  * are bit-identical to lca_kv_compress's for bf16 rows; fp8 key rows
- * (dtype LCA_BF16_FP8KEY, idx_stream->out_fp8 = 1) agree up to the fp32
+ * (dtype LCA_BF16_FP8KEY / LCA_BF16_MXFP4KEY, idx_stream->out_key = 1 / 2)
+ * agree up to the fp32
  * rounding of the pooling (the stored scale shows it); the new entries'
  * scores agree within rounding order.  Falls back to those two calls where the fused
  * launch does not apply: fp32, d_I not in {32, 64, 128, 256}, an indexer

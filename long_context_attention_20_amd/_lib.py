@@ -21,6 +21,7 @@ LCA_ERR_HIP = -4
 LCA_F32 = 0
 LCA_BF16 = 1
 LCA_BF16_FP8KEY = 2  # index calls: bf16 queries, fp8 key rows (d_I E4M3 bytes, fp32 scale, 4 zero bytes)
+LCA_BF16_MXFP4KEY = 3  # index calls: bf16 queries, MXFP4 key rows (d_I/2 bytes of E2M1 pairs, E8M0 scales, pad)
 
 EXPORTS = [
     "lca_strerror", "lca_last_error", "lca_version", "lca_kv_compress",
@@ -36,7 +37,7 @@ class CompressStream(ctypes.Structure):
         ("src", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("out", ctypes.c_void_p),
         ("ent_off", ctypes.c_void_p), ("C", ctypes.c_int32), ("m", ctypes.c_int32), ("w", ctypes.c_int32),
         ("per_channel", ctypes.c_int32), ("rmsnorm", ctypes.c_int32), ("max_entries", ctypes.c_int32),
-        ("out_fp8", ctypes.c_int32),
+        ("out_key", ctypes.c_int32),
     ]
 
 

@@ -126,10 +126,12 @@ static int check_streams(const lca_compress_stream* streams, int n_streams, int 
     LCA_REQUIRE(s.per_channel == 0 || s.per_channel == 1, LCA_ERR_INVALID_ARG, "kv_compress: per_channel");
     LCA_REQUIRE(s.rmsnorm == 0 || s.rmsnorm == 1, LCA_ERR_INVALID_ARG, "kv_compress: rmsnorm");
     LCA_REQUIRE(s.max_entries >= 0, LCA_ERR_INVALID_ARG, "kv_compress: max_entries < 0");
-    LCA_REQUIRE(s.out_fp8 == 0 || s.out_fp8 == 1, LCA_ERR_INVALID_ARG, "kv_compress: out_fp8");
-    LCA_REQUIRE(!s.out_fp8 || (dtype == LCA_BF16 && s.C <= 512 && s.w <= 16 && (s.w == s.m || s.w == 2 * s.m)),
-                LCA_ERR_UNSUPPORTED, "kv_compress: stream %d: fp8 rows need bf16 input, C <= 512 and w = m or 2m <= 16",
+    LCA_REQUIRE(s.out_key >= 0 && s.out_key <= 2, LCA_ERR_INVALID_ARG, "kv_compress: out_key");
+    LCA_REQUIRE(!s.out_key || (dtype == LCA_BF16 && s.C <= 512 && s.w <= 16 && (s.w == s.m || s.w == 2 * s.m)),
+                LCA_ERR_UNSUPPORTED, "kv_compress: stream %d: key rows need bf16 input, C <= 512 and w = m or 2m <= 16",
                 k);
+    LCA_REQUIRE(s.out_key != 2 || (s.C == 32 || s.C == 64 || s.C == 128 || s.C == 256), LCA_ERR_UNSUPPORTED,
+                "kv_compress: stream %d: MXFP4 rows need C in {32, 64, 128, 256}", k);
   }
   return LCA_OK;
 }
@@ -161,9 +163,10 @@ static int check_index(const char* what, bool need_inputs, const void* p, const 
     LCA_REQUIRE(p && omega && ikey, LCA_ERR_INVALID_ARG, "%s: a required pointer is NULL", what);
     LCA_REQUIRE(H_I >= 1 && H_I <= 16 && d_I >= 8 && d_I % 8 == 0 && H_I * d_I <= 1024, LCA_ERR_UNSUPPORTED,
                 "%s: H_I=%d d_I=%d unsupported", what, H_I, d_I);
-    LCA_REQUIRE(valid_dtype(dtype) || dtype == LCA_BF16_FP8KEY, LCA_ERR_INVALID_ARG, "%s: dtype=%d", what, dtype);
-    LCA_REQUIRE(dtype != LCA_BF16_FP8KEY || (d_I == 32 || d_I == 64 || d_I == 128 || d_I == 256),
-                LCA_ERR_UNSUPPORTED, "%s: fp8 key rows need d_I in {32, 64, 128, 256} (d_I=%d)", what, d_I);
+    const bool keyrows = dtype == LCA_BF16_FP8KEY || dtype == LCA_BF16_MXFP4KEY;
+    LCA_REQUIRE(valid_dtype(dtype) || keyrows, LCA_ERR_INVALID_ARG, "%s: dtype=%d", what, dtype);
+    LCA_REQUIRE(!keyrows || (d_I == 32 || d_I == 64 || d_I == 128 || d_I == 256), LCA_ERR_UNSUPPORTED,
+                "%s: fp8 / MXFP4 key rows need d_I in {32, 64, 128, 256} (d_I=%d)", what, d_I);
   }
   LCA_REQUIRE(csa_off && q_pos, LCA_ERR_INVALID_ARG, "%s: a required pointer is NULL", what);
   LCA_REQUIRE(B >= 1 && Tq >= 1, LCA_ERR_INVALID_ARG, "%s: B=%d Tq=%d", what, B, Tq);
@@ -210,11 +213,12 @@ int lca_csa_index_score_append(const void* p, const float* omega, const void* ik
   LCA_REQUIRE(std::isfinite(eps) && eps >= 0.f, LCA_ERR_INVALID_ARG,
               "csa_index_score_append: eps must be finite and >= 0");
   // the streams' inputs are bf16 when the keys are written as fp8 rows
-  const int in_dtype = dtype == LCA_BF16_FP8KEY ? LCA_BF16 : dtype;
-  LCA_REQUIRE(idx_stream->out_fp8 == (dtype == LCA_BF16_FP8KEY ? 1 : 0), LCA_ERR_INVALID_ARG,
-              "csa_index_score_append: the indexer-key stream writes fp8 rows exactly when dtype is LCA_BF16_FP8KEY");
+  const int want_key = dtype == LCA_BF16_FP8KEY ? 1 : dtype == LCA_BF16_MXFP4KEY ? 2 : 0;
+  const int in_dtype = want_key ? LCA_BF16 : dtype;
+  LCA_REQUIRE(idx_stream->out_key == want_key, LCA_ERR_INVALID_ARG,
+              "csa_index_score_append: the indexer-key stream's rows (out_key) must match dtype");
   for (int i = 0; i < n_kv; ++i)
-    LCA_REQUIRE(kv_streams[i].out_fp8 == 0, LCA_ERR_INVALID_ARG, "csa_index_score_append: kv stream %d writes fp8", i);
+    LCA_REQUIRE(kv_streams[i].out_key == 0, LCA_ERR_INVALID_ARG, "csa_index_score_append: kv stream %d writes key rows", i);
   rc = check_streams(idx_stream, 1, in_dtype);
   if (rc == LCA_OK && n_kv > 0) rc = check_streams(kv_streams, n_kv, in_dtype);
   if (rc != LCA_OK) return rc;

@@ -22,7 +22,8 @@ struct CompressStreamDev {
   void* out;
   const int64_t* ent_off;
   int C, m, w, per_channel, rmsnorm, max_entries;
-  int fp8;      // 1: E4M3 rows of C bytes + fp32 scale + 4 zero bytes (one lane group per row, NV = 1)
+  int key;      // key rows: 1 fp8 (C E4M3 bytes, fp32 scale, 4 zero bytes), 2 MXFP4 (C/2 bytes of E2M1
+                // pairs, one E8M0 scale per 32 channels, zero pad to C/2 + 8); one lane group per row, NV = 1
   int G;        // lanes per row
   int NV;       // 16-byte vectors per lane per row
   int small;    // 1: small-window run mode
@@ -110,6 +111,72 @@ __device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], float scale) {
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
+// MXFP4: fp32 bits of the E2M1 value of nibble n (bit 3 the sign).
+__device__ __forceinline__ uint32_t e2m1_bits(uint32_t n) {
+  const uint32_t e = (n >> 1) & 3u, m = n & 1u;
+  const uint32_t mag = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
+  return mag | ((n & 8u) << 28);
+}
+// The E8M0 scale byte b as a float: 2**(b - 127).
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return __uint_as_float(b ? (b << 23) : 0x00400000u);
+}
+// Eight values of one 32-channel block as E2M1 nibbles (channel c at bits
+// 4c): value * 2**-k rounded to nearest even on 0, .5, 1, 1.5, 2, 3, 4, 6
+// (ties to the even mantissa) and clamped to 6; k = floor(log2 amax) - 2 of
+// the block (its E8M0 byte k + 127 in *code), amax = 0: all zero, code 0.
+__device__ __forceinline__ uint32_t pack_e2m1x8(const float (&x)[8], float amax, uint32_t* code) {
+  if (!(amax > 0.f)) {
+    *code = 0u;
+    return 0u;
+  }
+  int ex;
+  frexpf(amax, &ex);                       // amax = f * 2**ex, 0.5 <= f < 1
+  const int k = max(-127, min(127, ex - 3));
+  *code = (uint32_t)(k + 127);
+  const float inv = ldexpf(1.0f, -k);      // exact
+  uint32_t w = 0u;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float a = fminf(fabsf(x[c]) * inv, 6.0f);
+    const uint32_t q = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                     : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+    w |= (q | (signbit(x[c]) ? 8u : 0u)) << (4 * c);
+  }
+  return w;
+}
+// The values of eight E2M1 nibbles of a block with scale s (exact in fp32).
+__device__ __forceinline__ void unpack_e2m1x8(uint32_t w, float s, float (&x)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) x[c] = __uint_as_float(e2m1_bits((w >> (4 * c)) & 15u)) * s;
+}
+// One MXFP4 key row from its row group (G lanes x 8 channels, G >= 4): every
+// lane packs its 8 channels against its block's amax (the 4 lanes of a
+// 32-channel block), lane 0 writes the block scale bytes and the zero pad.
+// Returns this lane's nibbles and block scale (for scoring the stored row).
+__device__ __forceinline__ uint32_t store_mx_row(const float (&x)[8], int G, int li, char* row, int C, bool active,
+                                                 float* scale) {
+  float am = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(x[c]));
+  am = wave_max(am, 4);
+  uint32_t code;
+  const uint32_t w = pack_e2m1x8(x, am, &code);
+  *scale = e8m0_value(code);
+  // lane 0 of the row group gathers the block codes of lanes 0, 4, 8, ...
+  const int base = ((int)threadIdx.x & 63) - li;
+  uint32_t lo = 0u, hi = 0u;
+  for (int b = 0; b < G / 4; ++b) {
+    const uint32_t cb = (uint32_t)__shfl((int)code, base + 4 * b, 64);
+    if (b < 4) lo |= cb << (8 * b); else hi |= cb << (8 * (b - 4));
+  }
+  if (active) {
+    *reinterpret_cast<uint32_t*>(row + li * 4) = w;
+    if (li == 0) *reinterpret_cast<uint2*>(row + C / 2) = make_uint2(lo, hi);
+  }
+  return w;
+}
+
 // The values of eight E4M3 bytes (exact in fp32).
 __device__ __forceinline__ void unpack_fp8x8(uint2 v, float (&x)[8]) {
   typedef float f2 __attribute__((ext_vector_type(2)));
@@ -140,7 +207,15 @@ __device__ __forceinline__ void finish_entry(const CompressStreamDev& s, float e
 #pragma unroll
       for (int k = 0; k < VE; ++k) e[v][k] *= inv;
   }
-  if (s.fp8) {
+  if (s.key == 2) {
+    if constexpr (VE == 8) {
+      char* row = reinterpret_cast<char*>(s.out) + out_row * (int64_t)(s.C / 2 + 8);
+      float sc;
+      store_mx_row(e[0], G, ch0[0] / 8, row, s.C, active, &sc);
+    }
+    return;
+  }
+  if (s.key == 1) {
     // one E4M3 byte per channel and the row's fp32 scale amax / 448 (the
     // row stands for scale * q; q = round-to-nearest-even of value / scale,
     // kept inside +-448).  bf16 input, C <= 512: one 8-channel vector per

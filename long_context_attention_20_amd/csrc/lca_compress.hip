@@ -55,7 +55,7 @@ int setup_compress(const lca_compress_stream* streams, int n, const int64_t* tok
     d.src = in.src; d.logits = in.logits; d.out = in.out; d.ent_off = in.ent_off;
     d.C = in.C; d.m = in.m; d.w = in.w; d.per_channel = in.per_channel; d.rmsnorm = in.rmsnorm;
     d.max_entries = in.max_entries;
-    d.fp8 = in.out_fp8;
+    d.key = in.out_key;
     const int lanes = in.C / VE;
     d.G = lanes < 64 ? lanes : 64;
     d.NV = lanes < 64 ? 1 : lanes / 64;

@@ -80,8 +80,9 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
                     bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false)),
                     bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true)));
 }
-__device__ __forceinline__ int64_t key_row_bytes(const IndexParams& a, bool fp8) {
-  return fp8 ? (int64_t)a.dI + 8 : (int64_t)a.dI * 2;
+// Bytes per key row: bf16 (KF 0), fp8 rows (1), MXFP4 rows (2).
+__device__ __forceinline__ int64_t key_row_bytes(const IndexParams& a, int kf) {
+  return kf == 1 ? (int64_t)a.dI + 8 : kf == 2 ? (int64_t)a.dI / 2 + 8 : (int64_t)a.dI * 2;
 }
 // The 8 dims lane group grp feeds k-step ks of a 16x16x32 product.  bf16
 // rows: dims 32*ks + 8*grp ..; fp8 rows: lane group grp takes the KS*8
@@ -92,6 +93,27 @@ template <int KS>
 __device__ __forceinline__ int key_dim(int ks, int grp, bool fp8) {
   return fp8 ? (KS * grp + ks) * 8 : ks * 32 + grp * 8;
 }
+// MXFP4 rows: lane group grp's KS words of 8 E2M1 nibbles (its KS*8
+// consecutive channels) and the E8M0 scale of each word's 32-channel block.
+template <int KS>
+__device__ __forceinline__ void load_mx_slices(const char* row, int grp, int dI, uint32_t (&w)[KS], float (&sc)[KS]) {
+  const uint32_t* nib = reinterpret_cast<const uint32_t*>(row + grp * KS * 4);
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(row + dI / 2);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    w[ks] = nib[ks];
+    sc[ks] = e8m0_value(scales[(grp * KS * 8 + ks * 8) >> 5]);
+  }
+}
+__device__ __forceinline__ uint4 e2m1x8_to_bf16x8(uint32_t w, float s) {
+  float x[8];
+  unpack_e2m1x8(w, s, x);  // E2M1 value times a power of two: exact in bf16
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xFFFF0000u);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Lane group grp's KS slices of 8 E4M3 bytes of one fp8 row, in 16-byte loads
 // (rows are d_I + 8 bytes: 8-byte aligned, which the dword loads accept).
 template <int KS>
@@ -133,9 +155,9 @@ __device__ __forceinline__ void hist_flush(const uint32_t* lh, uint32_t* gh) {
 
 // bf16, matrix cores.  KS = dI / 32 k-steps.  Block (cx, r) scores the
 // entries [cx*chunk, min((cx+1)*chunk, lim)) of row r; lh: kHistBins words
-// of LDS.  FP8K: fp8 key rows (widened to bf16 in registers, score times the
-// row's scale).
-template <int KS, bool FP8K = false>
+// of LDS.  KF: key rows 0 bf16, 1 fp8 (widened to bf16 in registers, score
+// times the row's scale), 2 MXFP4 (widened with their block scales).
+template <int KS, int KF = 0>
 __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, int cx, int64_t lim, uint32_t* lh) {
   const int b = r / a.Tq;
   const int64_t e_base = a.csa_off[b];
@@ -156,7 +178,7 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < a.HI) v = *reinterpret_cast<const uint4*>(P + col * a.dI + key_dim<KS>(ks, grp, FP8K));
+      if (col < a.HI) v = *reinterpret_cast<const uint4*>(P + col * a.dI + key_dim<KS>(ks, grp, KF != 0));
       A[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -170,7 +192,7 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
   __syncthreads();
 
   const char* K = reinterpret_cast<const char*>(a.ikey);
-  const int64_t rowb = key_row_bytes(a, FP8K);
+  const int64_t rowb = key_row_bytes(a, KF);
   float* S = a.scores + (int64_t)r * a.max_entries;
   constexpr int U = 8;  // tiles in flight per wave
   const int64_t ntile = (c1 - c0 + 15) / 16;
@@ -179,18 +201,22 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
     uint4 kv[U][KS];
     uint2 k8[U][KS];
     float sc[U];
+    uint32_t k4[U][KS];
+    float ms[U][KS];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int64_t e = c0 + (t0 + u) * 16 + col;
       if (e >= c1) e = c1 - 1;  // clamp: stays inside the visible entries
       const char* row = K + (e_base + e) * rowb;
-      if constexpr (FP8K) {
+      if constexpr (KF == 1) {
         load_fp8_slices<KS>(row, grp, k8[u]);
+        sc[u] = *reinterpret_cast<const float*>(row + a.dI);
+      } else if constexpr (KF == 2) {
+        load_mx_slices<KS>(row, grp, a.dI, k4[u], ms[u]);
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
       }
-      if constexpr (FP8K) sc[u] = *reinterpret_cast<const float*>(row + a.dI);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -199,7 +225,8 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (FP8K) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
+        if constexpr (KF == 1) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
+        if constexpr (KF == 2) kv[u][ks] = e2m1x8_to_bf16x8(k4[u][ks], ms[u][ks]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], __builtin_bit_cast(bf16x8_t, kv[u][ks]), acc, 0, 0, 0);
       }
       float part = 0.f;
@@ -207,7 +234,7 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
       for (int i = 0; i < 4; ++i) part = fmaf(om[i], fmaxf(acc[i], 0.f), part);
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
-      if constexpr (FP8K) part *= sc[u];
+      if constexpr (KF == 1) part *= sc[u];
       const int64_t e = c0 + (t0 + u) * 16 + col;
       if (grp == 0 && t0 + u < ntile && e < c1) {
         S[e] = part;
@@ -219,10 +246,10 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
   if (do_hist) hist_flush(lh, a.hist + ((int64_t)r * a.nstripe + cx % a.nstripe) * kHistBins);
 }
 
-template <int KS, bool FP8K = false>
+template <int KS, int KF = 0>
 __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
   __shared__ uint32_t lh[kHistBins];
-  score_chunk_mfma<KS, FP8K>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
+  score_chunk_mfma<KS, KF>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
 }
 
 // Several query rows of one sequence (a decode step with Tq > 1, as when a
@@ -233,8 +260,8 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
 // accumulator lane adds the weighted ReLU terms of its four A rows into the
 // partial of the row they belong to; the partials are summed over the four
 // lane groups and lane group q stores row q's score.  lh: TQ * kHistBins
-// words of LDS, one histogram per row.  FP8K as score_chunk_mfma.
-template <int KS, int TQ, bool FP8K = false>
+// words of LDS, one histogram per row.  KF as score_chunk_mfma.
+template <int KS, int TQ, int KF = 0>
 __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, int cx, int64_t lim, uint32_t* lh) {
   static_assert(TQ >= 2 && TQ <= 4, "2 to 4 rows per block");
   const int nq = a.Tq;  // <= TQ, nq * HI <= 16 (checked by the host)
@@ -267,7 +294,7 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < nrow) v = *reinterpret_cast<const uint4*>(P + col * a.dI + key_dim<KS>(ks, grp, FP8K));
+      if (col < nrow) v = *reinterpret_cast<const uint4*>(P + col * a.dI + key_dim<KS>(ks, grp, KF != 0));
       A[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -285,7 +312,7 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
   __syncthreads();
 
   const char* K = reinterpret_cast<const char*>(a.ikey);
-  const int64_t rowb = key_row_bytes(a, FP8K);
+  const int64_t rowb = key_row_bytes(a, KF);
   constexpr int U = 8;  // tiles in flight per wave
   const int64_t ntile = (c1 - c0 + 15) / 16;
   const int nw = (int)(blockDim.x >> 6);
@@ -293,25 +320,30 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
     uint4 kv[U][KS];
     uint2 k8[U][KS];
     float sc[U];
+    uint32_t k4[U][KS];
+    float ms[U][KS];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int64_t e = c0 + (t0 + u) * 16 + col;
       if (e >= c1) e = c1 - 1;  // clamp: stays inside the visible entries
       const char* row = K + (e_base + e) * rowb;
-      if constexpr (FP8K) {
+      if constexpr (KF == 1) {
         load_fp8_slices<KS>(row, grp, k8[u]);
+        sc[u] = *reinterpret_cast<const float*>(row + a.dI);
+      } else if constexpr (KF == 2) {
+        load_mx_slices<KS>(row, grp, a.dI, k4[u], ms[u]);
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
       }
-      if constexpr (FP8K) sc[u] = *reinterpret_cast<const float*>(row + a.dI);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (FP8K) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
+        if constexpr (KF == 1) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
+        if constexpr (KF == 2) kv[u][ks] = e2m1x8_to_bf16x8(k4[u][ks], ms[u][ks]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], __builtin_bit_cast(bf16x8_t, kv[u][ks]), acc, 0, 0, 0);
       }
       const int64_t e = c0 + (t0 + u) * 16 + col;
@@ -322,7 +354,7 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
         for (int i = 0; i < 4; ++i) part = fmaf(om[q][i], fmaxf(acc[i], 0.f), part);
         part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
-        if constexpr (FP8K) part *= sc[u];
+        if constexpr (KF == 1) part *= sc[u];
         if (grp == q && t0 + u < ntile && e < c1q[q]) {
           a.scores[(int64_t)(r0 + q) * a.max_entries + e] = part;
           if (hq[q]) hist_add(lh + q * kHistBins, part);
@@ -336,10 +368,10 @@ __device__ __forceinline__ void score_chunk_multi(const IndexParams& a, int b, i
     if (hq[q]) hist_flush(lh + q * kHistBins, a.hist + ((int64_t)(r0 + q) * a.nstripe + cx % a.nstripe) * kHistBins);
 }
 
-template <int KS, int TQ, bool FP8K = false>
+template <int KS, int TQ, int KF = 0>
 __global__ __launch_bounds__(kIdxThreads) void index_score_multi(IndexParams a) {
   __shared__ uint32_t lh[TQ * kHistBins];
-  score_chunk_multi<KS, TQ, FP8K>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
+  score_chunk_multi<KS, TQ, KF>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
 }
 
 // ------------------------------------------------------------------ score + append
@@ -377,7 +409,7 @@ __device__ __forceinline__ float group_sum_n(float v, int n) {
   }
 }
 
-template <bool FP8K>
+template <int KF>
 __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int b) {
   constexpr int VE = 8;                    // bf16 channels per 16-byte vector
   const CompressStreamDev& s = ap.s;
@@ -437,7 +469,14 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
     }
     // the stored (rounded) key is the one scored
     float row_scale = 1.f;
-    if constexpr (FP8K) {
+    if constexpr (KF == 2) {
+      // an MXFP4 key row (as the compression kernel writes it), scored as
+      // its elements' values times their block scales
+      char* row = reinterpret_cast<char*>(s.out) + (e_base + j) * (int64_t)(s.C / 2 + 8);
+      float bs;
+      const uint32_t w = store_mx_row(key, G, li, row, s.C, on, &bs);
+      unpack_e2m1x8(w, bs, key);
+    } else if constexpr (KF == 1) {
       // an fp8 key row (as the compression kernel writes it): E4M3 bytes of
       // value / scale, scale = amax / 448 over the row's lanes; scored as the
       // bytes' values, times the scale
@@ -475,7 +514,7 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
         d = group_sum_n(d, G);
         score = fmaf(a.omega[(int64_t)r * a.HI + h], fmaxf(d, 0.f), score);
       }
-      if constexpr (FP8K) score *= row_scale;
+      if constexpr (KF == 1) score *= row_scale;
       if (on && j < nv && li == 0) {
         a.scores[(int64_t)r * a.max_entries + j] = score;
         if (do_hist)
@@ -487,9 +526,9 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
 }
 
 // TQ: query rows per sequence the score blocks take at once (1: one row;
-// 2 or 4: all Tq <= TQ rows of a sequence, as score_chunk_multi).  FP8K: the
+// 2 or 4: all Tq <= TQ rows of a sequence, as score_chunk_multi).  KF (0, 1 fp8, 2 MXFP4): the
 // indexer-key stream writes fp8 rows, which the score blocks read.
-template <int KS, int TQ, bool FP8K>
+template <int KS, int TQ, int KF>
 __global__ __launch_bounds__(kIdxThreads) void index_score_append(IndexParams a, AppendIdx ap, CompressParams cp) {
   extern __shared__ uint32_t dyn[];  // max(histograms, compression) words
   const int blk = blockIdx.x;
@@ -498,15 +537,15 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_append(IndexParams a,
     // scoring blocks
     compress_block<BF16, 1, 8, false>(cp, blk, reinterpret_cast<float*>(dyn));
   } else if (blk < ap.ncb + ap.B) {
-    append_and_score<FP8K>(a, ap, blk - ap.ncb);
+    append_and_score<KF>(a, ap, blk - ap.ncb);
   } else {
     const int sb = blk - ap.ncb - ap.B;
     const int b = sb / ap.nsx, cx = sb % ap.nsx;
     const int64_t lim = n_windows(ap.done_len[b], a.m, a.w);
     if constexpr (TQ == 1)
-      score_chunk_mfma<KS, FP8K>(a, b, cx, lim, dyn);
+      score_chunk_mfma<KS, KF>(a, b, cx, lim, dyn);
     else
-      score_chunk_multi<KS, TQ, FP8K>(a, b, cx, lim, dyn);
+      score_chunk_multi<KS, TQ, KF>(a, b, cx, lim, dyn);
   }
 }
 
@@ -565,7 +604,7 @@ static bool rows_mode(int Tq, int64_t maxN) { return Tq >= kRowsPerBlock && maxN
 // the rows of a sequence share one score block (score_chunk_multi)
 static bool multi_rows_ok(int Tq, int HI) { return Tq >= 2 && Tq <= 4 && Tq * HI <= 16; }
 
-template <int KS, int HI, bool FP8K = false>
+template <int KS, int HI, int KF = 0>
 __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
   constexpr int QR = 16 / HI;                // query rows per MFMA row block
   constexpr int RB = kRowsPerBlock / QR;     // MFMA row blocks per block
@@ -601,7 +640,7 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (ok) v = *reinterpret_cast<const uint4*>(P + ((int64_t)(r0 + qr) * HI + col % HI) * a.dI + key_dim<KS>(ks, grp, FP8K));
+      if (ok) v = *reinterpret_cast<const uint4*>(P + ((int64_t)(r0 + qr) * HI + col % HI) * a.dI + key_dim<KS>(ks, grp, KF != 0));
       A[rb][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
     // weights of the accumulator rows 4*grp + i: (row rb*QR + (4*grp + i)/HI, head (4*grp + i)%HI)
@@ -613,21 +652,25 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
     }
   }
   const char* K = reinterpret_cast<const char*>(a.ikey);
-  const int64_t rowb = key_row_bytes(a, FP8K);
+  const int64_t rowb = key_row_bytes(a, KF);
   constexpr int EB = 4;  // 16-entry blocks in flight
   const int64_t wend = min(w0 + kRowsEntriesPerWave, min(nv_max, a.max_entries));
   for (int64_t e0 = w0; e0 < wend; e0 += 16 * EB) {
     uint4 kv[EB][KS];
     uint2 k8[EB][KS];
     float rscale[EB];
+    uint32_t k4[EB][KS];
+    float ms[EB][KS];
 #pragma unroll
     for (int u = 0; u < EB; ++u) {
       int64_t e = e0 + u * 16 + col;
       if (e >= nseq) e = nseq - 1;  // clamp: stays inside the sequence's keys
       const char* row = K + (e_base + e) * rowb;
-      if constexpr (FP8K) {
+      if constexpr (KF == 1) {
         load_fp8_slices<KS>(row, grp, k8[u]);
         rscale[u] = *reinterpret_cast<const float*>(row + a.dI);
+      } else if constexpr (KF == 2) {
+        load_mx_slices<KS>(row, grp, a.dI, k4[u], ms[u]);
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
@@ -637,9 +680,12 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
     for (int u = 0; u < EB; ++u) {
       const int64_t e = e0 + u * 16 + col;
       const bool e_ok = e < wend;
-      if constexpr (FP8K) {
+      if constexpr (KF == 1) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
+      } else if constexpr (KF == 2) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = e2m1x8_to_bf16x8(k4[u][ks], ms[u][ks]);
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -653,7 +699,7 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
 #pragma unroll
           for (int h = 0; h < HI; ++h) sc = fmaf(om[rb][q * HI + h], fmaxf(acc[q * HI + h], 0.f), sc);
           const int qr = rb * QR + (4 * grp) / HI + q;
-          if constexpr (FP8K) sc *= rscale[u];
+          if constexpr (KF == 1) sc *= rscale[u];
           if (e_ok && qr < nrows) a.scores[(int64_t)(r0 + qr) * a.max_entries + e] = sc;
         }
       }
@@ -931,10 +977,11 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
   IndexParams a = make_params(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, nullptr, scores, ws);
   const int rows = B * Tq;
   dim3 g1((unsigned)((maxN + a.chunk - 1) / a.chunk), (unsigned)rows);
-  const bool fp8k = dtype == LCA_BF16_FP8KEY;
-  const bool mfma = (dtype == LCA_BF16 || fp8k) && HI <= 16 && (dI % 32) == 0 && dI <= 256;
-  if (fp8k && !mfma) {
-    set_error("csa_index_score: fp8 key rows are scored for H_I <= 16 and d_I in {32, 64, 128, 256}");
+  // key rows: 0 bf16/fp32, 1 fp8, 2 MXFP4
+  const int kf = dtype == LCA_BF16_FP8KEY ? 1 : dtype == LCA_BF16_MXFP4KEY ? 2 : 0;
+  const bool mfma = (dtype == LCA_BF16 || kf) && HI <= 16 && (dI % 32) == 0 && dI <= 256;
+  if (kf && !mfma) {
+    set_error("csa_index_score: fp8 / MXFP4 key rows are scored for H_I <= 16 and d_I in {32, 64, 128, 256}");
     return LCA_ERR_UNSUPPORTED;
   }
   if (mfma && a.no_hist && (HI == 1 || HI == 2 || HI == 4)) {
@@ -948,10 +995,12 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
     default: hipLaunchKernelGGL((index_score_rows<KSv, 4, F8>), g, dim3(256), 0, stream, a); break;      \
   }
 #define LCA_ROWS(KSv)      \
-  if (fp8k) {              \
-    LCA_ROWS2(KSv, true)   \
+  if (kf == 1) {           \
+    LCA_ROWS2(KSv, 1)      \
+  } else if (kf == 2) {    \
+    LCA_ROWS2(KSv, 2)      \
   } else {                 \
-    LCA_ROWS2(KSv, false)  \
+    LCA_ROWS2(KSv, 0)      \
   }
     switch (dI / 32) {
       case 1: LCA_ROWS(1) break;
@@ -966,13 +1015,16 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
   if (mfma && multi_rows_ok(Tq, HI) && !a.no_hist) {
     // a few rows per sequence: all of them from one read of the keys
     dim3 g((unsigned)((maxN + a.chunk - 1) / a.chunk), (unsigned)B);
+#define LCA_MULTI2(KSv, KFv)                                                                                   \
+  if (Tq == 2) hipLaunchKernelGGL((index_score_multi<KSv, 2, KFv>), g, dim3(kIdxThreads), 0, stream, a);       \
+  else hipLaunchKernelGGL((index_score_multi<KSv, 4, KFv>), g, dim3(kIdxThreads), 0, stream, a);
 #define LCA_MULTI(KSv)                                                                                         \
-  if (fp8k) {                                                                                                  \
-    if (Tq == 2) hipLaunchKernelGGL((index_score_multi<KSv, 2, true>), g, dim3(kIdxThreads), 0, stream, a);    \
-    else hipLaunchKernelGGL((index_score_multi<KSv, 4, true>), g, dim3(kIdxThreads), 0, stream, a);            \
+  if (kf == 1) {                                                                                               \
+    LCA_MULTI2(KSv, 1)                                                                                         \
+  } else if (kf == 2) {                                                                                        \
+    LCA_MULTI2(KSv, 2)                                                                                         \
   } else {                                                                                                     \
-    if (Tq == 2) hipLaunchKernelGGL((index_score_multi<KSv, 2>), g, dim3(kIdxThreads), 0, stream, a);          \
-    else hipLaunchKernelGGL((index_score_multi<KSv, 4>), g, dim3(kIdxThreads), 0, stream, a);                  \
+    LCA_MULTI2(KSv, 0)                                                                                         \
   }
     switch (dI / 32) {
       case 1: LCA_MULTI(1) break;
@@ -981,15 +1033,23 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
       default: LCA_MULTI(8) break;
     }
 #undef LCA_MULTI
+#undef LCA_MULTI2
     return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
   }
-  if (mfma && fp8k) {
-    switch (dI / 32) {
-      case 1: hipLaunchKernelGGL((index_score_mfma<1, true>), g1, dim3(kIdxThreads), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((index_score_mfma<2, true>), g1, dim3(kIdxThreads), 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((index_score_mfma<4, true>), g1, dim3(kIdxThreads), 0, stream, a); break;
-      default: hipLaunchKernelGGL((index_score_mfma<8, true>), g1, dim3(kIdxThreads), 0, stream, a); break;
+  if (mfma && kf) {
+#define LCA_KEYROWS(KFv)                                                                                  \
+  switch (dI / 32) {                                                                                      \
+    case 1: hipLaunchKernelGGL((index_score_mfma<1, KFv>), g1, dim3(kIdxThreads), 0, stream, a); break;   \
+    case 2: hipLaunchKernelGGL((index_score_mfma<2, KFv>), g1, dim3(kIdxThreads), 0, stream, a); break;   \
+    case 4: hipLaunchKernelGGL((index_score_mfma<4, KFv>), g1, dim3(kIdxThreads), 0, stream, a); break;   \
+    default: hipLaunchKernelGGL((index_score_mfma<8, KFv>), g1, dim3(kIdxThreads), 0, stream, a); break;  \
+  }
+    if (kf == 1) {
+      LCA_KEYROWS(1)
+    } else {
+      LCA_KEYROWS(2)
     }
+#undef LCA_KEYROWS
   } else if (mfma) {
     switch (dI / 32) {
       case 1: hipLaunchKernelGGL((index_score_mfma<1>), g1, dim3(kIdxThreads), 0, stream, a); break;
@@ -1017,10 +1077,10 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
   // the fused launch: bf16 matrix-core scores, one query row per sequence or
   // a few sharing a score block, KV streams of at most 512 bf16 channels;
   // anything else runs as the two launches it stands for
-  // dtype LCA_BF16_FP8KEY: bf16 inputs, the indexer-key stream writes (and
-  // the scores read) fp8 key rows
-  const bool fp8k = dtype == LCA_BF16_FP8KEY;
-  const int in_dtype = fp8k ? LCA_BF16 : dtype;
+  // dtype LCA_BF16_FP8KEY / LCA_BF16_MXFP4KEY: bf16 inputs, the indexer-key
+  // stream writes (and the scores read) fp8 / MXFP4 key rows
+  const int kf = dtype == LCA_BF16_FP8KEY ? 1 : dtype == LCA_BF16_MXFP4KEY ? 2 : 0;
+  const int in_dtype = kf ? LCA_BF16 : dtype;
   const bool fused = in_dtype == LCA_BF16 && HI <= 16 && (dI == 32 || dI == 64 || dI == 128 || dI == 256) &&
                      idx_stream->C == dI && idx_stream->m == m && idx_stream->w == w &&
                      (w == m || w == 2 * m) && w <= 16 && (Tq == 1 || multi_rows_ok(Tq, HI));
@@ -1050,7 +1110,7 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
   const lca_compress_stream& in = *idx_stream;
   ap.s.src = in.src; ap.s.logits = in.logits; ap.s.out = in.out; ap.s.ent_off = in.ent_off;
   ap.s.C = in.C; ap.s.m = in.m; ap.s.w = in.w; ap.s.per_channel = in.per_channel; ap.s.rmsnorm = in.rmsnorm;
-  ap.s.fp8 = in.out_fp8;
+  ap.s.key = in.out_key;
   ap.s.max_entries = in.max_entries;
   ap.tok_off = tok_off;
   ap.done_len = done_len;
@@ -1075,10 +1135,12 @@ int launch_index_score_append(const void* p, const float* omega, const void* ike
     default: hipLaunchKernelGGL((index_score_append<KSv, 4, F8>), grid, dim3(kIdxThreads), lds, stream, a, ap, cp); break; \
   }
 #define LCA_APPEND(KSv)        \
-  if (fp8k) {                  \
-    LCA_APPEND2(KSv, true)     \
+  if (kf == 1) {               \
+    LCA_APPEND2(KSv, 1)        \
+  } else if (kf == 2) {        \
+    LCA_APPEND2(KSv, 2)        \
   } else {                     \
-    LCA_APPEND2(KSv, false)    \
+    LCA_APPEND2(KSv, 0)        \
   }
   switch (dI / 32) {
     case 1: LCA_APPEND(1) break;

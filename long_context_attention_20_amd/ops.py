@@ -9,7 +9,7 @@ from typing import Optional, Sequence
 import ctypes
 import torch
 
-from ._lib import (LCA_BF16, LCA_BF16_FP8KEY, LCA_F32, LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_TOPK, LCA_SRC_WINDOW, AttnSource, CompressStream,
+from ._lib import (LCA_BF16, LCA_BF16_FP8KEY, LCA_BF16_MXFP4KEY, LCA_F32, LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_TOPK, LCA_SRC_WINDOW, AttnSource, CompressStream,
                    Partial, check, lib)
 
 
@@ -22,12 +22,14 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _index_dtype(p: torch.Tensor, ikey: torch.Tensor) -> int:
-    """Element type code of an index-score call: the query's type, or
-    LCA_BF16_FP8KEY for a uint8 key cache of fp8 rows (d_I + 8 bytes each)."""
+    """Element type code of an index-score call: the query's type, or for a
+    uint8 key cache LCA_BF16_FP8KEY (rows of d_I + 8 bytes) or
+    LCA_BF16_MXFP4KEY (rows of d_I/2 + 8 bytes)."""
     if ikey.dtype == torch.uint8:
-        if p.dtype != torch.bfloat16 or ikey.dim() != 2 or ikey.shape[1] != p.shape[-1] + 8:
-            raise TypeError("fp8 key rows: bf16 queries and a uint8 cache of d_I + 8 bytes per row")
-        return LCA_BF16_FP8KEY
+        dI = p.shape[-1]
+        if p.dtype != torch.bfloat16 or ikey.dim() != 2 or ikey.shape[1] not in (dI + 8, dI // 2 + 8):
+            raise TypeError("key rows: bf16 queries and a uint8 cache of d_I + 8 (fp8) or d_I/2 + 8 (MXFP4) bytes per row")
+        return LCA_BF16_FP8KEY if ikey.shape[1] == dI + 8 else LCA_BF16_MXFP4KEY
     return _dtype_code(p)
 
 
@@ -76,19 +78,21 @@ def _stream_array(streams: Sequence[dict]):
         d = _dtype_code(src)
         if dt is None:
             dt = d
-        fp8 = int(s.get("fp8", 0))
+        key = int(s.get("key", 0))
         C = src.shape[-1]
-        if fp8:
-            # fp8 key rows: C E4M3 bytes, the fp32 scale, 4 zero bytes
-            if out.dtype != torch.uint8 or out.dim() != 2 or out.shape[1] != C + 8:
-                raise TypeError("fp8 rows: a uint8 output of C + 8 bytes per row")
+        if key:
+            # key rows: fp8 (C E4M3 bytes, fp32 scale, 4 zero bytes) or MXFP4
+            # (C/2 bytes of E2M1 pairs, one E8M0 scale per 32 channels, pad)
+            rb = C + 8 if key == 1 else C // 2 + 8
+            if out.dtype != torch.uint8 or out.dim() != 2 or out.shape[1] != rb:
+                raise TypeError(f"key rows: a uint8 output of {rb} bytes per row")
         elif _dtype_code(out) != d:
             raise TypeError("one element type per call")
         if d != dt or _dtype_code(lg) != d:
             raise TypeError("one element type per call")
         pc = 1 if lg.dim() == 2 else 0
         arr[i] = CompressStream(src.data_ptr(), lg.data_ptr(), out.data_ptr(), eo.data_ptr(), C, int(s["m"]),
-                                int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]), fp8)
+                                int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]), key)
     return arr, dt
 
 

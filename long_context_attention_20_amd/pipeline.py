@@ -51,10 +51,15 @@ def _offsets(counts) -> np.ndarray:
 class HybridAttention:
     def __init__(self, H: int, D: int, HI: int, dI: int, k: int, m: int = 4, w: int = 8, m2: int = 128,
                  w2: int = 128, W: int = 128, eps: float = 1e-6, scale: Optional[float] = None,
-                 split_csa: Optional[int] = None, split_hca: Optional[int] = None, ikey_fp8: bool = False):
+                 split_csa: Optional[int] = None, split_hca: Optional[int] = None, ikey: str = "bf16"):
         self.H, self.D, self.HI, self.dI, self.k = H, D, HI, dI, k
-        # indexer-key cache as fp8 rows (d_I E4M3 bytes, fp32 scale, 4 zero bytes)
-        self.ikey_fp8 = bool(ikey_fp8)
+        # indexer-key cache: rows of the inputs' type ("bf16"), fp8 rows (d_I
+        # E4M3 bytes, fp32 scale, 4 zero bytes) or MXFP4 rows (d_I/2 bytes of
+        # E2M1 pairs, one E8M0 scale per 32 channels, zero pad to d_I/2 + 8)
+        if ikey not in ("bf16", "fp8", "mxfp4"):
+            raise ValueError(f"ikey: bf16, fp8 or mxfp4, not {ikey}")
+        self.ikey = ikey
+        self.ikey_code = {"bf16": 0, "fp8": 1, "mxfp4": 2}[ikey]
         self.m, self.w, self.m2, self.w2, self.W, self.eps = m, w, m2, w2, W, eps
         self.scale = float(scale) if scale is not None else 1.0 / float(np.sqrt(D))
         self.split_csa, self.split_hca = split_csa, split_hca
@@ -77,7 +82,8 @@ class HybridAttention:
             csa_off=torch.from_numpy(co).to(device), hca_off=torch.from_numpy(ho).to(device),
             # at least one row each, so that empty caches still have an address
             kv_csa=torch.empty((max(1, int(co[-1])), self.D), dtype=dtype, device=device),
-            ikey=(torch.empty((max(1, int(co[-1])), self.dI + 8), dtype=torch.uint8, device=device) if self.ikey_fp8
+            ikey=(torch.empty((max(1, int(co[-1])), self.dI + 8 if self.ikey == "fp8" else self.dI // 2 + 8),
+                              dtype=torch.uint8, device=device) if self.ikey_code
                   else torch.empty((max(1, int(co[-1])), self.dI), dtype=dtype, device=device)),
             kv_hca=torch.empty((max(1, int(ho[-1])), self.D), dtype=dtype, device=device),
             csa_off_h=co, hca_off_h=ho)
@@ -97,7 +103,7 @@ class HybridAttention:
                                 m=self.m, w=self.w, rmsnorm=1, max_entries=new_csa))
         if new_csa > 0 and "idx" in which:
             streams.append(dict(src=raw["u"], logits=raw["c"], out=caches.ikey, ent_off=caches.csa_off,
-                                m=self.m, w=self.w, rmsnorm=0, max_entries=new_csa, fp8=int(self.ikey_fp8)))
+                                m=self.m, w=self.w, rmsnorm=0, max_entries=new_csa, key=self.ikey_code))
         if new_hca > 0 and "hca" in which:
             streams.append(dict(src=raw["x"], logits=raw["g"], out=caches.kv_hca, ent_off=caches.hca_off,
                                 m=self.m2, w=self.w2, rmsnorm=1, max_entries=new_hca))

@@ -31,7 +31,7 @@ def to_device(raw, cfg, dev="cuda"):
 
 def layer_for(cfg, **kw):
     from long_context_attention_20_amd import HybridAttention
-    kw.setdefault("ikey_fp8", getattr(cfg, "ikey", "bf16") == "fp8")
+    kw.setdefault("ikey", getattr(cfg, "ikey", "bf16"))
     return HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps, **kw)
 
 
@@ -45,10 +45,30 @@ def fp8_rows(t):
     return q, s, t[:, dI + 4:].numpy()
 
 
-def key_rows(ikey):
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mx_rows(t, dI):
+    """An MXFP4 key cache (uint8 rows: d_I/2 bytes of E2M1 pairs, the even
+    channel in the low nibble, then d_I/32 E8M0 scale bytes, zero pad) ->
+    (q [N, d_I] E2M1 values, s [N, d_I/32] scales, pad bytes)."""
+    t = t.contiguous().cpu().numpy()
+    b = t[:, :dI // 2]
+    nib = np.stack([b & 15, b >> 4], axis=-1).reshape(t.shape[0], dI)
+    q = E2M1_VALUES[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    codes = t[:, dI // 2:dI // 2 + dI // 32].astype(np.int64)
+    s = np.where(codes > 0, np.ldexp(1.0, codes - 127), 2.0 ** -127)
+    return q, s, t[:, dI // 2 + dI // 32:]
+
+
+def key_rows(ikey, dI=None):
     """The indexer-key rows a cache stands for (float64): bf16/fp32 rows as
-    they are, fp8 rows as scale * value."""
+    they are, fp8 rows as scale * value, MXFP4 rows as block scale * value
+    (dI tells the two byte layouts apart)."""
     if ikey.dtype == torch.uint8:
+        if dI is not None and ikey.shape[1] == dI // 2 + 8:
+            q, s, _ = mx_rows(ikey, dI)
+            return (q.reshape(q.shape[0], -1, 32) * s[..., None]).reshape(q.shape)
         q, s, _ = fp8_rows(ikey)
         return q * s[:, None]
     return f64(ikey)

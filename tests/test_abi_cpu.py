@@ -251,10 +251,11 @@ def test_hybrid_attn_merge_rejects(L):
 
 
 def test_fp8_key_rows_rejects(L):
-    """fp8 key rows: the compression takes them only from bf16 input streams
-    of at most 512 channels with small windows; the index calls only with
-    d_I in {32, 64, 128, 256}; the fused append only with an indexer stream
-    that writes them; nothing is launched on a rejected call."""
+    """fp8 and MXFP4 key rows: the compression takes them only from bf16
+    input streams of at most 512 channels with small windows (MXFP4: C in
+    {32, 64, 128, 256}); the index calls only with d_I in {32, 64, 128, 256};
+    the fused append only with an indexer stream that writes them; every call
+    here is rejected before anything is launched."""
     lib = L.lib
     P = ctypes.c_void_p(256)
     tok = ctypes.c_void_p(512)
@@ -266,7 +267,9 @@ def test_fp8_key_rows_rejects(L):
     assert compress(dtype=0) == L.LCA_ERR_UNSUPPORTED                 # fp32 input
     assert compress(C=1024) == L.LCA_ERR_UNSUPPORTED                  # wider than 512
     assert compress(m=128, w=128) == L.LCA_ERR_UNSUPPORTED            # a large window
-    assert compress(fp8=2) == L.LCA_ERR_INVALID_ARG
+    assert compress(fp8=3) == L.LCA_ERR_INVALID_ARG                   # no such key-row format
+    assert compress(C=48, fp8=2) == L.LCA_ERR_UNSUPPORTED             # MXFP4 needs C in {32, 64, 128, 256}
+    assert compress(dtype=0, fp8=2) == L.LCA_ERR_UNSUPPORTED          # MXFP4 from fp32 input
     need = lib.lca_csa_index_topk_workspace(1, 1000, 64)
     rc = lib.lca_csa_index_score(P, P, P, P, P, 1, 1, 4, 40, 64, 4, 8, 1000, None, P, need, 2, None)
     assert rc == L.LCA_ERR_UNSUPPORTED                                  # d_I = 40

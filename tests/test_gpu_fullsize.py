@@ -58,14 +58,21 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
         u, c = _host(raw["u"][s0:s1]), _host(raw["c"][s0:s1])
         co, ho = caches.csa_off_h, caches.hca_off_h
         kv_csa = f64(caches.kv_csa[co[b]:co[b + 1]])
-        ikey = key_rows(caches.ikey[co[b]:co[b + 1]])
-        fp8 = caches.ikey.dtype == torch.uint8
+        ikey = key_rows(caches.ikey[co[b]:co[b + 1]], cfg.dI)
+        fp8 = caches.ikey.dtype == torch.uint8   # fp8 or MXFP4 key rows
         kv_hca = f64(caches.kv_hca[ho[b]:ho[b + 1]])
         ncsa, nhca = ocmp.n_entries(L, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m2, cfg.w2)
         # ---- compression on sampled entries (and the appended last ones)
         ent = sorted(set(rng.choice(ncsa, size=min(48, ncsa), replace=False).tolist()) | {ncsa - 1})
         for got, src, lg, norm in ((kv_csa, x, a, True), (ikey, u, c, False)):
             pooled = ocmp.compress(src, lg, cfg.m, cfg.w, norm, cfg.eps, ent)
+            if fp8 and got is ikey and cfg.ikey == "mxfp4":
+                # MXFP4 rows: the oracle's quantization, or one element step
+                # (at most a quarter of the block's amax) from it
+                ref = oquant.dequantize_mx_rows(*oquant.quantize_mx_rows(pooled))
+                am = np.repeat(np.max(np.abs(ref.reshape(len(ent), -1, 32)), axis=2), 32, axis=1)
+                assert np.all(np.abs(got[ent] - ref) <= 0.5 * am + 1e-30)
+                continue
             if fp8 and got is ikey:
                 # fp8 rows: the oracle's quantization, or one E4M3 step from it
                 ref = oquant.dequantize_rows(*oquant.quantize_rows(pooled))
@@ -112,7 +119,8 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
             if not diff:
                 if ikey_o is None:
                     pooled_k = ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps)
-                    ikey_o = (oquant.dequantize_rows(*oquant.quantize_rows(pooled_k)) if fp8
+                    ikey_o = (oquant.dequantize_mx_rows(*oquant.quantize_mx_rows(pooled_k)) if cfg.ikey == "mxfp4"
+                              else oquant.dequantize_rows(*oquant.quantize_rows(pooled_k)) if fp8
                               else onum.round_to(pooled_k, cfg.dtype))
                 sel_o = oidx.topk(oidx.scores(p, om, ikey_o[:nv]), cfg.k)
                 kv_sel = onum.round_to(ocmp.compress(x, a, cfg.m, cfg.w, True, cfg.eps, sorted(sel_o)), cfg.dtype)
@@ -149,6 +157,13 @@ def test_pro_1m_decode_fp8_full():
     cfg = li.PRO_1M_DECODE_FP8
     raw, layer, caches, bufs, out = _run(cfg, side=False)
     _check_rows(cfg, raw, caches, bufs, out, [0], np.random.default_rng(5))
+
+
+def test_pro_1m_decode_mxfp4_full():
+    """The Pro 1M decode with MXFP4 indexer-key rows."""
+    cfg = li.PRO_1M_DECODE_MXFP4
+    raw, layer, caches, bufs, out = _run(cfg, side=False)
+    _check_rows(cfg, raw, caches, bufs, out, [0], np.random.default_rng(6))
 
 
 def test_pro_varlen_full():

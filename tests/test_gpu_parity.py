@@ -17,8 +17,8 @@ from oracle import numerics as onum
 from oracle import pipeline as opipe
 from oracle import quant as oquant
 
-from gpu_util import (TOL, assert_close, check_topk, f64, fp8_rows, key_rows, layer_for, merge_splits, run_gpu,
-                      score_bound, seq_caches, tdtype, to_device)
+from gpu_util import (TOL, assert_close, check_topk, f64, fp8_rows, key_rows, layer_for, merge_splits, mx_rows,
+                      run_gpu, score_bound, seq_caches, tdtype, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -692,6 +692,34 @@ def test_topk_crowded_zero_ties(path):
             assert_close(f64(out)[t], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"ties row {t}")
 
 
+def _check_key_cache(cfg, raw, ikey, csa_off_h):
+    """The key rows (fp8 or MXFP4) against the oracle's quantization; returns
+    the rows they stand for (float64 [N, d_I])."""
+    if cfg.ikey == "fp8":
+        q, s = _check_fp8_cache(cfg, raw, ikey, csa_off_h)
+        return q * s[:, None]
+    q, s, pad = mx_rows(ikey, cfg.dI)
+    assert np.all(pad == 0)
+    off = raw["tok_off"]
+    flips = total = 0
+    for b in range(cfg.B):
+        u = raw["u"][off[b]:off[b + 1]].astype(np.float64)
+        c = raw["c"][off[b]:off[b + 1]].astype(np.float64)
+        qr, sr = oquant.quantize_mx_rows(ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps))
+        qg, sg = q[csa_off_h[b]:csa_off_h[b + 1]], s[csa_off_h[b]:csa_off_h[b + 1]]
+        vg = oquant.dequantize_mx_rows(qg, sg)
+        vr = oquant.dequantize_mx_rows(qr, sr)
+        # a block's scale moves only when its amax sits on a power of two;
+        # an element moves at most one step (2 x the scale at the top)
+        assert np.mean(sg != sr) <= 1e-3, f"sequence {b}: block scales"
+        step = 2.0 * np.repeat(np.maximum(sg, sr), 32, axis=1)
+        assert np.all(np.abs(vg - vr) <= step), f"sequence {b}: more than one step"
+        flips += int(np.sum(vg != vr))
+        total += vr.size
+    assert flips <= max(2, total // 1000), f"{flips} of {total} values off the oracle"
+    return oquant.dequantize_mx_rows(q, s)
+
+
 def _check_fp8_cache(cfg, raw, ikey, csa_off_h):
     """The fp8 key rows against the oracle's quantization of its own pooled keys:
     scales within fp32 rounding, every byte the oracle's value or (where the
@@ -714,8 +742,8 @@ def _check_fp8_cache(cfg, raw, ikey, csa_off_h):
     return q, s
 
 
-@pytest.mark.parametrize("tq", [1, 2, 40])
-def test_fp8_key_cache_and_scores(tq):
+@pytest.mark.parametrize("fmt,tq", [("fp8", 1), ("fp8", 2), ("fp8", 40), ("mxfp4", 1), ("mxfp4", 2), ("mxfp4", 40)])
+def test_fp8_key_cache_and_scores(fmt, tq):
     """Indexer keys kept as fp8 rows (E4M3 bytes and an fp32 scale per entry):
     the compression writes the oracle's quantization, and the scores read from
     the rows (bytes widened to bf16 on the matrix cores, times the scale) are
@@ -724,15 +752,15 @@ def test_fp8_key_cache_and_scores(tq):
     at near ties.  One, two and 40 query rows per sequence (the row-tiled
     scoring and the one-block-per-row selection)."""
     from long_context_attention_20_amd import ops
-    cfg = li.small(f"fp8k{tq}", 123, (9000, 4101, 777), tq=tq, H=64, D=512, k=256, ikey="fp8")
+    cfg = li.small(f"fp8k{tq}", 123, (9000, 4101, 777), tq=tq, H=64, D=512, k=256, ikey=fmt)
     raw = li.make_raw(cfg)
     d = to_device(raw, cfg)
     layer = layer_for(cfg)
     caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
     layer.compress(caches, d, d["tok_off"])
     torch.cuda.synchronize()
-    print(f"[fp8 keys] tq={tq} lens={cfg.lens} rows {caches.ikey.shape}", flush=True)
-    q, s = _check_fp8_cache(cfg, raw, caches.ikey, caches.csa_off_h)
+    print(f"[{fmt} keys] tq={tq} lens={cfg.lens} rows {caches.ikey.shape}", flush=True)
+    keys = _check_key_cache(cfg, raw, caches.ikey, caches.csa_off_h)
     maxN = ocmp.n_entries(max(cfg.lens), cfg.m, cfg.w)
     rows = cfg.B * tq
     ws = layer.index_workspace(rows, maxN, "cuda")
@@ -746,20 +774,21 @@ def test_fp8_key_cache_and_scores(tq):
         for t in range(tq):
             r = b * tq + t
             nv = ocmp.n_visible(int(raw["q_pos"][b, t]), cfg.m, cfg.w)
-            qb, sb = q[co[b]:co[b] + nv], s[co[b]:co[b] + nv]
+            kb = keys[co[b]:co[b] + nv]
             p64 = raw["p"][r].astype(np.float64)
             om = raw["omega"][r].astype(np.float64)
-            s_ref = oquant.scores_fp8(p64, om, qb, sb)
-            check_topk(idx_h[r], sc_h[r], s_ref, score_bound(p64, om, qb * sb[:, None]), cfg.k)
+            s_ref = oidx.scores(p64, om, kb)   # the plain score of the rows the keys stand for
+            check_topk(idx_h[r], sc_h[r], s_ref, score_bound(p64, om, kb), cfg.k)
 
 
-def test_decode_step_fp8_keys():
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_decode_step_fp8_keys(fmt):
     """A decode step over fp8 key rows: the fused append writes exactly the
     bytes the cache build wrote, the selection inside the attention launch is
     the exact top-k of the row's scores (oracle scores of the GPU rows, near
     ties aside), and the output equals the oracle's attention over that
     selection, end to end from raw inputs where the selected sets agree."""
-    cfg = li.small("fp8_decode", 124, (4001, 2600, 777, 4096), H=64, D=512, k=256, ikey="fp8")
+    cfg = li.small("fp8_decode", 124, (4001, 2600, 777, 4096), H=64, D=512, k=256, ikey=fmt)
     raw = li.make_raw(cfg)
     d, layer, caches, full, done, done_h, bufs = _decode_setup(cfg, raw)
     out = layer.decode_step(caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs,
@@ -769,19 +798,17 @@ def test_decode_step_fp8_keys():
     # the appended fp8 rows are the build's up to the fp32 rounding of the
     # pooling (the stored scale shows every bit of it): other rows untouched,
     # scales within fp32 rounding, bytes within one E4M3 step
-    qa, sa, pa = fp8_rows(caches.ikey)
-    qb, sb, _ = fp8_rows(full[1])
     appended = set()
     for b, L in enumerate(cfg.lens):
         n0, n1 = ocmp.n_entries(L - 1, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m, cfg.w)
         appended |= set(range(int(caches.csa_off_h[b]) + n0, int(caches.csa_off_h[b]) + n1))
-    differ = set(np.nonzero(np.any(qa != qb, axis=1) | (sa != sb))[0].tolist())
-    print(f"[fp8 decode] appended rows {sorted(appended)}, differing from the build {sorted(differ)}", flush=True)
+    ga, gb = caches.ikey.cpu().numpy(), full[1].cpu().numpy()
+    differ = set(np.nonzero(np.any(ga != gb, axis=1))[0].tolist())
+    print(f"[{fmt} decode] appended rows {sorted(appended)}, differing from the build {sorted(differ)}", flush=True)
     assert differ <= appended
-    assert np.all(pa == 0) and np.all(np.abs(sa - sb) <= 2.0 ** -20 * sb)
-    assert np.all(np.abs(qa - qb) <= 2.0 ** -3 * np.maximum(np.abs(qa), np.abs(qb)) + 2.0 ** -9)
-    _check_fp8_cache(cfg, raw, caches.ikey, caches.csa_off_h)
-    keys = key_rows(caches.ikey)
+    va, vb = key_rows(caches.ikey, cfg.dI), key_rows(full[1], cfg.dI)
+    assert np.all(np.abs(va - vb) <= 2.0 ** -2 * np.max(np.abs(vb), axis=1, keepdims=True) + 1e-30)
+    keys = _check_key_cache(cfg, raw, caches.ikey, caches.csa_off_h)
     _, ores = opipe.run(raw, cfg)
     idx_h = bufs["idx"].cpu().numpy()
     out_h = f64(out)

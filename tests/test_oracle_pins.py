@@ -46,6 +46,7 @@ def test_presets_match_page_constants():
     assert li.PRO_1M_MTP2 == li.PRO_1M_DECODE.with_(name="pro_1m_mtp2", cfg_id=li.PRO_1M_MTP2.cfg_id, tq=2)
     # the fp8-key decode draws the same inputs as the Pro 1M decode
     assert li.PRO_1M_DECODE_FP8 == li.PRO_1M_DECODE.with_(name="pro_1m_decode_fp8", ikey="fp8")
+    assert li.PRO_1M_DECODE_MXFP4 == li.PRO_1M_DECODE.with_(name="pro_1m_decode_mxfp4", ikey="mxfp4")
 
 
 def test_entry_counts_match_workloads():
