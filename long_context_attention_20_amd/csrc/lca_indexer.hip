@@ -105,13 +105,20 @@ __device__ __forceinline__ void load_mx_slices(const char* row, int grp, int dI,
     sc[ks] = e8m0_value(scales[(grp * KS * 8 + ks * 8) >> 5]);
   }
 }
+// Eight E2M1 nibbles (channel c at bits 4c) times the block scale s as bf16:
+// gfx950's scaled FP4 conversion takes the two nibbles of one byte (low
+// nibble first) per call; an E2M1 value times a power of two is exact in bf16.
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w, float s, int byte) {
+  switch (byte) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  }
+}
 __device__ __forceinline__ uint4 e2m1x8_to_bf16x8(uint32_t w, float s) {
-  float x[8];
-  unpack_e2m1x8(w, s, x);  // E2M1 value times a power of two: exact in bf16
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xFFFF0000u);
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  return make_uint4(e2m1x2_to_bf16x2(w, s, 0), e2m1x2_to_bf16x2(w, s, 1), e2m1x2_to_bf16x2(w, s, 2),
+                    e2m1x2_to_bf16x2(w, s, 3));
 }
 
 // Lane group grp's KS slices of 8 E4M3 bytes of one fp8 row, in 16-byte loads
