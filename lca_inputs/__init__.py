@@ -100,10 +100,14 @@ PRO_VARLEN_FP8 = dataclasses.replace(PRO_VARLEN, name="pro_varlen_fp8", ikey="fp
 PRO_1M_DECODE_MXFP4 = dataclasses.replace(PRO_1M_DECODE, name="pro_1m_decode_mxfp4", ikey="mxfp4")
 # The Flash prefill chunk (same seeds) with fp8 indexer keys.
 FLASH_PREFILL_FP8 = dataclasses.replace(FLASH_PREFILL, name="flash_prefill_fp8", ikey="fp8")
+# The Pro variable-length batch and the Flash prefill chunk (same seeds) with
+# MXFP4 indexer keys.
+PRO_VARLEN_MXFP4 = dataclasses.replace(PRO_VARLEN, name="pro_varlen_mxfp4", ikey="mxfp4")
+FLASH_PREFILL_MXFP4 = dataclasses.replace(FLASH_PREFILL, name="flash_prefill_mxfp4", ikey="mxfp4")
 
 CONFIGS: Dict[str, Config] = {c.name: c for c in (TINY, FLASH_DECODE, PRO_1M_DECODE, FLASH_PREFILL, PRO_VARLEN,
                                                   PRO_1M_MTP2, PRO_1M_DECODE_FP8, PRO_VARLEN_FP8, FLASH_PREFILL_FP8,
-                                                  PRO_1M_DECODE_MXFP4)}
+                                                  PRO_1M_DECODE_MXFP4, PRO_VARLEN_MXFP4, FLASH_PREFILL_MXFP4)}
 
 
 def small(name: str, cfg_id: int, lens, tq: int = 1, H: int = 64, D: int = 512, HI: int = 4,
