@@ -545,7 +545,7 @@ def test_index_score_multi_rows_match_single_rows(tq, HI, dI):
             assert np.all(err <= 2 * bound + 1e-6), f"row ({b}, {t}): scores off the oracle"
 
 
-@pytest.mark.parametrize("tq,ikey", [(2, "bf16"), (3, "bf16"), (2, "fp8")])
+@pytest.mark.parametrize("tq,ikey", [(2, "bf16"), (3, "bf16"), (2, "fp8"), (2, "mxfp4")])
 def test_decode_step_mtp(tq, ikey):
     """A decode step with tq query rows per sequence (the main token and
     drafted ones, checked together): the appends of every entry the tq new
@@ -578,8 +578,18 @@ def test_decode_step_mtp(tq, ikey):
     out = layer.decode_step(caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs,
                             done_len=done, done_h=done_h)
     torch.cuda.synchronize()
-    fp8 = ikey == "fp8"
+    fp8 = ikey in ("fp8", "mxfp4")
     for got, ref, name in zip((caches.kv_csa, caches.ikey, caches.kv_hca), full, ("kv_csa", "ikey", "kv_hca")):
+        if ikey == "mxfp4" and name == "ikey":
+            # both rows round the same key (pooled in another fp32 order) to
+            # within half an E2M1 spacing, at most one block scale each
+            qa, sa, pa = mx_rows(got, cfg.dI)
+            qb, sb, pb = mx_rows(ref, cfg.dI)
+            da = (qa.reshape(qa.shape[0], -1, 32) * sa[..., None])
+            db = (qb.reshape(qb.shape[0], -1, 32) * sb[..., None])
+            assert np.all(np.abs(da - db) <= (sa + sb)[..., None])
+            assert np.array_equal(pa, pb)
+            continue
         if fp8 and name == "ikey":
             qa, sa, _ = fp8_rows(got)
             qb, sb, _ = fp8_rows(ref)
@@ -590,7 +600,7 @@ def test_decode_step_mtp(tq, ikey):
     _, ores = opipe.run(raw, cfg)
     idx_h = bufs["idx"].cpu().numpy()
     out_h = f64(out)
-    keys = key_rows(caches.ikey)
+    keys = key_rows(caches.ikey, cfg.dI)
     co = caches.csa_off_h
     for b in range(cfg.B):
         for t in range(tq):
