@@ -335,6 +335,67 @@ def run_prefill(cfg, args, dev):
     print(json.dumps(res))
 
 
+TRACE_PHASES = ["start", "filter done", "wait done", "selection done", "prologue done", "key loop done", "stored"]
+KIND_NAMES = {0: "HCA (dense)", 1: "sparse (gather)", 2: "window", 3: "sparse (top-k inside)"}
+
+
+def trace_attention(run, path, reps=6):
+    """Per-block phase stamps of the attention launch of a decode step (the
+    library's diagnostic trace, 100 MHz clock): for each source kind, the
+    median over blocks and the maximum of every phase, in microseconds after
+    the first block of the launch started; medians over `reps` steps on the
+    rotated layers.  Written as a markdown table to `path`."""
+    import ctypes
+    import torch
+    from long_context_attention_20_amd import _lib
+    words = 8 * 65536
+    buf = torch.zeros(words, dtype=torch.int64, device="cuda:0")
+    _lib.check(_lib.lib.lca_diag_trace(ctypes.c_void_p(buf.data_ptr()), words), "diag_trace")
+    per_rep = []
+    try:
+        for rep in range(reps):
+            L = run.layers[rep % len(run.layers)]
+            buf.zero_()
+            torch.cuda.synchronize()
+            run.step(L)
+            torch.cuda.synchronize()
+            rec = buf.view(-1, 8).cpu().numpy().view(np.uint64).astype(np.int64)
+            per_rep.append(rec[rec[:, 0] != 0])
+    finally:
+        _lib.lib.lca_diag_trace(None, 0)
+    tick_us = 0.01
+    kinds = sorted(set(int(k) for r in per_rep for k in (r[:, 7] & 3)))
+    lines = ["| source | blocks | " + " | ".join(f"{p} (median / max)" for p in TRACE_PHASES) + " |",
+             "|---|---|" + "---|" * len(TRACE_PHASES)]
+    spans, gave_up = [], 0
+    for kd in kinds:
+        cells = []
+        for ph in range(7):
+            med, mx = [], []
+            for r in per_rep:
+                t0 = r[:, 0].min()
+                sel = r[(r[:, 7] & 3) == kd]
+                v = sel[:, ph]
+                v = v[v != 0]
+                if len(v):
+                    med.append(np.median(v - t0) * tick_us)
+                    mx.append(np.max(v - t0) * tick_us)
+            cells.append(f"{np.median(med):.2f} / {np.median(mx):.2f}" if med else "-")
+        nb = int(np.median([np.sum((r[:, 7] & 3) == kd) for r in per_rep]))
+        lines.append(f"| {KIND_NAMES.get(kd, kd)} | {nb} | " + " | ".join(cells) + " |")
+    for r in per_rep:
+        spans.append((r[:, 6].max() - r[:, 0].min()) * tick_us)
+        gave_up += int(np.sum((r[:, 7] >> 2) & 1))
+    xcc = [np.median([np.median(r[((r[:, 7] >> 8) & 15) == x][:, 0] - r[:, 0].min()) * tick_us
+                      for r in per_rep if np.any(((r[:, 7] >> 8) & 15) == x)]) for x in range(8)]
+    text = "\n".join(lines) + (f"\n\nfirst block start to last partial stored: median {np.median(spans):.2f} us "
+                                f"over {reps} steps; waits that gave up: {gave_up}\n"
+                                f"median block start per XCC (us): " + ", ".join(f"{v:.2f}" for v in xcc) + "\n")
+    with open(path, "w") as f:
+        f.write(text)
+    print(text, file=sys.stderr, flush=True)
+
+
 def cpu_baseline(cfg, state, budget_s):
     """The oracle (float64, numpy) on this host: one decode step per query of
     layer 0 -- append the completed entries, score, select, attend, merge --
@@ -406,6 +467,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
     ap.add_argument("--split-csa", type=int, default=0, help="entry splits of the sparse attention (0: default)")
     ap.add_argument("--split-hca", type=int, default=0, help="entry splits of the HCA attention (0: default)")
+    ap.add_argument("--trace-attn", default="", metavar="PATH",
+                    help="also write the attention launch's per-block phase timeline to PATH")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB 10 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -465,6 +528,8 @@ def main():
         tper[i] = e0.elapsed_time(e1) / (reps * R)
         del g
     tt = dict(zip(run.timed, tper))
+    if args.trace_attn:
+        trace_attention(run, args.trace_attn)
     def own_time(n):
         for key in run.timed:
             if key == n:

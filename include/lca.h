@@ -27,7 +27,14 @@
  *   tensor; offsets are device int64 arrays of length B+1.
  * - Row-major layouts; "[a, b, c]" lists dimensions from slowest to fastest.
  * - Thread safety: concurrent calls are safe when they use different
- *   workspaces and outputs.
+ *   workspaces and outputs.  One case is slower, not wrong, under concurrent
+ *   work: the sparse blocks of a TOPK source (lca_hybrid_attn) that filter
+ *   the scores themselves wait for each other, which assumes that the whole
+ *   launch is resident at once (the library checks this against the
+ *   device's occupancy when nothing else runs).  Work on other streams or in
+ *   other processes can keep some of those blocks from starting; a waiting
+ *   block gives up after 100 us and selects the exact top-k from the row's
+ *   scores alone, so the output is the same.
  */
 #ifndef LCA_H_
 #define LCA_H_
@@ -294,8 +301,10 @@ int lca_swa_attn(const void* q, const void* x, const int64_t* tok_off, const int
  *                   matrix-core path with max_entries <= 262144 every block
  *                   of the sparse branch runs the exact selection itself;
  *                   when the whole launch fits the device at once, those
- *                   blocks also filter the scores (one launch in all), else
- *                   a filter launch comes first.  Elsewhere the selection's
+ *                   blocks also filter the scores (one launch in all; a
+ *                   block whose wait for the others gives up, see the
+ *                   thread-safety note above, selects from the scores
+ *                   alone), else a filter launch comes first.  Elsewhere the selection's
  *                   own launches come first.  At most one TOPK source per
  *                   call.
  * The sources share q [B*Tq, H, D], q_pos (device int32 [B*Tq]; read by the
@@ -362,6 +371,33 @@ int lca_swa_merge(const void* q, const void* x, const int64_t* tok_off, const in
 int lca_hybrid_attn_merge(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B,
                           int Tq, int H, int D, float scale, float eps, const float* sink, void* out, int dtype,
                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics (process-wide settings read by every later launch; not meant
+ * for production use, and not synchronised with launches in flight)
+ *
+ * lca_diag_trace: when buf is not NULL, every later launch of the few-row
+ * attention kernel (lca_hybrid_attn / lca_csa_sparse_attn / lca_hca_attn /
+ * lca_swa_attn with few query rows per sequence) writes, for each block b
+ * with 8*(b+1) <= n_words, 8 uint64 words at buf[8*b]: the 100 MHz constant
+ * clock (s_memrealtime) at 0 block start, 1 top-k filter done, 2 wait done,
+ * 3 selection done, 4 prologue done, 5 key loop done, 6 partial stored (0 for
+ * phases the block does not have), and word 7 = source kind (LCA_SRC_*) |
+ * wait gave up << 2 | fallback selection << 3 | owns top-k slots << 4 | XCC
+ * id << 8 | query row << 12 (20 bits) | the wave's HW_ID register << 32.  buf is a device pointer the caller keeps alive while
+ * tracing; NULL turns tracing off.
+ *
+ * lca_diag_topk_wait: the top-k wait inside the attention launch (a TOPK
+ * source whose sparse blocks filter the scores themselves) waits until the
+ * row's sparse blocks have all filtered their shares, for at most max_ticks
+ * of the 100 MHz clock (0: the default, 10000 = 100 us).  A block whose wait
+ * gives up selects the exact top-k from the row's scores alone, so the
+ * result does not change, only the time.  extra_shares > 0 makes every wait
+ * expect that many shares more than exist, so that every wait gives up (for
+ * testing that path); 0 restores normal operation.
+ * ---------------------------------------------------------------------- */
+int lca_diag_trace(uint64_t* buf, int64_t n_words);
+int lca_diag_topk_wait(int extra_shares, int64_t max_ticks);
 
 #ifdef __cplusplus
 }

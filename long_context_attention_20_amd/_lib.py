@@ -28,6 +28,7 @@ EXPORTS = [
     "lca_csa_index_topk_workspace", "lca_csa_index_topk", "lca_csa_index_score", "lca_csa_index_score_append",
     "lca_csa_topk_select", "lca_csa_sparse_attn", "lca_hca_attn",
     "lca_swa_attn", "lca_hybrid_attn", "lca_swa_merge_workspace", "lca_swa_merge", "lca_hybrid_attn_merge",
+    "lca_diag_trace", "lca_diag_topk_wait",
 ]
 LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_WINDOW, LCA_SRC_TOPK = 0, 1, 2, 3
 
@@ -103,6 +104,10 @@ def _load():
     L.lca_hybrid_attn_merge.restype = i32
     L.lca_hybrid_attn_merge.argtypes = [ctypes.POINTER(AttnSource), i32, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp,
                                         i32, vp]
+    L.lca_diag_trace.restype = i32
+    L.lca_diag_trace.argtypes = [vp, i64]
+    L.lca_diag_topk_wait.restype = i32
+    L.lca_diag_topk_wait.argtypes = [i32, i64]
     return L
 
 

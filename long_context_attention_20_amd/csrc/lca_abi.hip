@@ -51,6 +51,8 @@ static lca_attn_source make_source(int kind, const void* kv, const int64_t* off,
 }
 int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, const float* win_lse,
                  const float* sink, int rows, int H, int D, void* out, int dtype, hipStream_t stream);
+void diag_set_trace(uint64_t* buf, int64_t words);
+void diag_set_topk_wait(uint32_t extra, uint32_t ticks);
 
 static bool sync_mode() {
   static int v = -1;
@@ -108,7 +110,25 @@ const char* lca_strerror(int status) {
 
 const char* lca_last_error(void) { return g_last_error.c_str(); }
 
-int lca_version(void) { return 100; }
+int lca_version(void) { return 200; }
+
+int lca_diag_trace(uint64_t* buf, int64_t n_words) {
+  LCA_REQUIRE(buf == nullptr || n_words >= 0, LCA_ERR_INVALID_ARG, "diag_trace: n_words=%lld < 0",
+              (long long)n_words);
+  diag_set_trace(buf, n_words);
+  g_last_error.clear();
+  return LCA_OK;
+}
+
+int lca_diag_topk_wait(int extra_shares, int64_t max_ticks) {
+  LCA_REQUIRE(extra_shares >= 0 && extra_shares <= 1024, LCA_ERR_INVALID_ARG,
+              "diag_topk_wait: extra_shares=%d outside [0, 1024]", extra_shares);
+  LCA_REQUIRE(max_ticks >= 0 && max_ticks <= 100000000, LCA_ERR_INVALID_ARG,
+              "diag_topk_wait: max_ticks=%lld outside [0, 1e8]", (long long)max_ticks);
+  diag_set_topk_wait((uint32_t)extra_shares, (uint32_t)max_ticks);
+  g_last_error.clear();
+  return LCA_OK;
+}
 
 static int check_streams(const lca_compress_stream* streams, int n_streams, int dtype) {
   const int VE = dtype == LCA_BF16 ? 8 : 4;

@@ -25,6 +25,8 @@
 // O^T comes from the same rows through ds_read_b64_tr_b16, whose 16-lane
 // transpose hands lane i column i of a 4-row x 16-column block.  The next
 // tile's global loads are in flight while the current tile is computed.
+#include <atomic>
+
 #include "lca_topk.h"
 
 namespace lca {
@@ -68,10 +70,40 @@ struct AttnParams {
   int merge;
   const float* sink;    // [H] or NULL
   void* out;
+  // the in-launch top-k wait: it waits for tbpr + wait_extra filter shares
+  // (wait_extra > 0 only as a diagnostic: the wait then always gives up) for
+  // at most wait_ticks of the 100 MHz constant clock
+  uint32_t wait_extra;
+  uint32_t wait_ticks;
+  // diagnostics: per-block phase stamps (kTraceWords per block), or NULL
+  uint64_t* trace;
+  int64_t trace_words;
 };
 
 constexpr int kFilterPer = 8;  // scores per thread and filter chunk
-constexpr uint32_t kMaxSpins = 1u << 22;
+constexpr uint32_t kDefaultWaitTicks = 10000;  // 100 us of the 100 MHz clock
+
+// Phase stamps of a block (diagnostics): s_memrealtime (100 MHz) at
+//   0 block start, 1 filter done, 2 wait done, 3 selection done,
+//   4 prologue done (query normalised, first tile requested), 5 key loop
+//   done, 6 partial stored;
+// word 7: source kind | wait gave up << 2 | fallback selection << 3 |
+//   owns top-k slots << 4 | XCC id << 8 | query row << 12 (20 bits) |
+//   HW_ID register << 32.
+constexpr int kTraceWords = 8;
+__device__ __forceinline__ void trace_stamp(const AttnParams& a, int phase) {
+  if (a.trace && threadIdx.x == 0 && (int64_t)(blockIdx.x + 1) * kTraceWords <= a.trace_words)
+    a.trace[(int64_t)blockIdx.x * kTraceWords + phase] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void trace_flags(const AttnParams& a, uint32_t flags) {
+  if (a.trace && threadIdx.x == 0 && (int64_t)(blockIdx.x + 1) * kTraceWords <= a.trace_words) {
+    uint32_t hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    a.trace[(int64_t)blockIdx.x * kTraceWords + 7] = ((uint64_t)hw << 32) | ((xcc & 0xFu) << 8) | flags;
+    // (flags carries the row in bits 12..31)
+  }
+}
 
 // Source of split column bx (uniform) and the split inside it.
 __device__ __forceinline__ int attn_source(const AttnParams& a, int bx, int* split) {
@@ -181,13 +213,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int hb = jj % a.n_hb;
   const int unit = (jj / a.n_hb) * 8 + xcd;
   if (unit >= a.rows * a.n_x) return;  // padding of the last group (uniform)
+  trace_stamp(a, 0);
   const int r = unit / a.n_x;
   int split;
   const int si = attn_source(a, unit % a.n_x, &split);
   const AttnSrc& S = a.s[si];
   const int kind = S.kind;
   const bool gather = kind == SRC_GATHER || kind == SRC_TOPK;
-  // a TOPK block's selection loads go out first: they need nothing but the row
+  uint32_t tflags = (uint32_t)kind | ((uint32_t)(r & 0xFFFFF) << 12);
   __shared__ uint32_t s_timeout;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int team = wave >> 2, wt = wave & 3;
@@ -305,9 +338,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     if (kind == SRC_TOPK && a.filter && !all) {
       // every TOPK block of the row (slots or not) filters its share of the
       // row's scores, then counts itself done and waits for the others.  The
-      // launch fits the machine at once, so they are all resident and the
-      // wait ends (bounded all the same: a count that never completes leaves
-      // the slots empty rather than hanging).
+      // launch is sized to fit the machine at once, so normally they are all
+      // resident and the wait ends; the wait is bounded all the same (other
+      // work on the device can keep blocks of this launch from starting), and
+      // a block that gives up selects from the scores alone (below), so the
+      // result is the same either way.
       // the block's chunks are tbi, tbi + tbpr, ...; the first FC of them had
       // their loads issued at the start and are filtered in one pass (one
       // threshold, one list reservation)
@@ -318,28 +353,45 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
         filter_chunk(tw, r, nv, (int)cb, a.tbpr, fpf, *reinterpret_cast<FilterShared*>(lds_raw));
         __syncthreads();
       }
+      trace_stamp(a, 1);
       if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(&tw.done[r], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t spins = 0;
-        while (__hip_atomic_load(&tw.done[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)a.tbpr &&
-               ++spins < kMaxSpins)
+        // the block that completes the count knows that every filter of the
+        // row has read the first histogram (each reads it before it counts
+        // itself): it clears the histogram for the next score call
+        const uint32_t before = __hip_atomic_fetch_add(&tw.done[r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_timeout = before + 1 == (uint32_t)a.tbpr ? 2u : 0u;
+        const uint32_t target = (uint32_t)a.tbpr + a.wait_extra;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(&tw.done[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+          if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)a.wait_ticks) {
+            s_timeout |= 1u;
+            break;
+          }
           __builtin_amdgcn_s_sleep(1);
+        }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        s_timeout = spins >= kMaxSpins;
       }
       __syncthreads();
-      ready = !s_timeout;
-      topk_prefetch(tw, r, pf);  // the lists are complete now
+      const uint32_t wst = s_timeout;
+      ready = !(wst & 1u);
+      tflags |= (wst & 1u) << 2;
+      if (wst & 2u) {
+        uint32_t* gh = tw.hist + (int64_t)r * tw.nstripe * kHistBins;
+        for (int i = threadIdx.x; i < tw.nstripe * kHistBins; i += kAttnThreads) gh[i] = 0;
+      }
+      if (ready) topk_prefetch(tw, r, pf);  // the lists are complete now
     }
+    trace_stamp(a, 2);
     if (kind == SRC_TOPK && te > tb) {  // the block owns slots (even of an empty row)
+      tflags |= 1u << 4;
       // this block's slots [kbase, kbase + cnt) of the row's top k in
       // ascending entry order: every block of the row runs the same exact
       // selection from the filtered lists; the head-block-0 blocks also
       // write their slots to idx_out
       const int64_t cnt = min((te - tb) * kTile, n - kbase);
-      if (split == 0 && hb == 0) {
-        // every filter of the row has read the first histogram: clear it for
-        // the next call
+      if (!a.filter && split == 0 && hb == 0 && !all) {
+        // the filter launch before this one has read the first histogram:
+        // clear it for the next call
         uint32_t* gh = tw.hist + (int64_t)r * tw.nstripe * kHistBins;
         for (int i = threadIdx.x; i < tw.nstripe * kHistBins; i += kAttnThreads) gh[i] = 0;
       }
@@ -348,18 +400,31 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       // selection reads more than once (8192 of them at D = 512)
       constexpr uint32_t kCandLds = (uint32_t)((kLdsBytes - sizeof(SelectLds)) / sizeof(uint64_t));
       static_assert(sizeof(SelectLds) % sizeof(uint64_t) == 0, "the candidate area must be 8-byte aligned");
+      static_assert(kHistBins * sizeof(uint32_t) <= kLdsBytes, "the fallback's histogram lives in the tile memory");
+      auto emit = [&](uint32_t o, int32_t e) {
+        const int64_t j = (int64_t)o - kbase;
+        if (j >= 0 && j < cnt) sidx[j] = e;
+      };
+      bool got = false;
       if (!all && ready)
-        topk_row_select<kAttnThreads, true>(tw, r, pf, *reinterpret_cast<SelectLds*>(lds_raw), sel_sh,
-                                            [&](uint32_t o, int32_t e) {
-                                              const int64_t j = (int64_t)o - kbase;
-                                              if (j >= 0 && j < cnt) sidx[j] = e;
-                                            },
-                                            reinterpret_cast<uint64_t*>(lds_raw + sizeof(SelectLds)), kCandLds);
+        got = topk_row_select<kAttnThreads, true>(tw, r, pf, *reinterpret_cast<SelectLds*>(lds_raw), sel_sh, emit,
+                                                  reinterpret_cast<uint64_t*>(lds_raw + sizeof(SelectLds)),
+                                                  kCandLds) != 0;
+      if (!all && !got) {
+        // the wait gave up or the lists are not consistent: the exact
+        // selection from the row's scores alone (the score launch before
+        // this one wrote every score); nothing was emitted above
+        __syncthreads();
+        topk_row_scan_select<kAttnThreads>(tw.scores + (int64_t)r * tw.max_entries, nv, (uint32_t)S.k,
+                                           reinterpret_cast<uint32_t*>(lds_raw), sel_sh, emit);
+        tflags |= 1u << 3;
+      }
       __syncthreads();  // sidx complete; the selection's scratch is free
       if (hb == 0 && S.idx_out)
         for (int i = threadIdx.x; i < cnt; i += kAttnThreads) S.idx_out[(int64_t)r * S.k + kbase + i] = sidx[i];
     }
   }
+  trace_stamp(a, 3);
   {
     float ss = 0.f;
     if (wave_on) {
@@ -396,6 +461,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   for (int d = 0; d < DB; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
+  trace_stamp(a, 4);
 
   for (int64_t rd = 0; rd < rounds; ++rd) {
     const int64_t t = tb + 2 * rd + team;   // this team's tile (may be past te)
@@ -524,6 +590,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   // contiguous run of 32 heads x D floats
   __shared__ float st_m[2][2][16], st_l[2][2][16];
   __syncthreads();  // every wave has left the last round: tiles and sx are free
+  trace_stamp(a, 5);
   {
     float lg = l_run + __shfl_xor(l_run, 16, 64);
     lg += __shfl_xor(lg, 32, 64);
@@ -569,6 +636,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     S.lse[((int64_t)split * a.rows + r) * a.H + hbase + threadIdx.x] =
         lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
+  trace_stamp(a, 6);
+  trace_flags(a, tflags);
 }
 
 // ============================================================ many query rows
@@ -1240,15 +1309,21 @@ int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int 
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
 
 // Blocks of attn_mfma<D, true, fc> the current device holds at once
-// (compute units x blocks per unit), queried once per device, D and fc (2 is
-// built for D = 512 only).
+// (compute units x blocks per unit, from the occupancy query on the idle
+// device), queried once per device, D and fc (2 is built for D = 512 only).
+// The cache is read and written atomically: concurrent first calls may both
+// query, and both store the same value.  Residency is what lets the sparse
+// blocks wait for each other; it is not guaranteed while other work holds
+// compute units, which is why their wait is bounded (and falls back to an
+// exact selection of its own).
 static int64_t resident_blocks(int D, int fc) {
-  static int64_t cache[64][4][2];
+  static std::atomic<int64_t> cache[64][4][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int di = D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : 3;
   const int fi = fc == 2 && D == 512 ? 1 : 0;
-  if (cache[dev][di][fi] == 0) {
+  int64_t v = cache[dev][di][fi].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0, per = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const void* fn = D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true>)
@@ -1257,9 +1332,32 @@ static int64_t resident_blocks(int D, int fc) {
                      : fi       ? reinterpret_cast<const void*>(&attn_mfma<512, true, 2>)
                                 : reinterpret_cast<const void*>(&attn_mfma<512, true>);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kAttnThreads, 0);
-    cache[dev][di][fi] = (e == hipSuccess && cus > 0 && per > 0) ? (int64_t)cus * per : -1;
+    v = (e == hipSuccess && cus > 0 && per > 0) ? (int64_t)cus * per : -1;
+    cache[dev][di][fi].store(v, std::memory_order_relaxed);
   }
-  return cache[dev][di][fi];
+  return v;
+}
+
+// Diagnostics set through lca_diag_*: a per-block phase trace of the
+// attention launches, and a top-k wait that is made to give up.
+static std::atomic<uint64_t*> g_trace{nullptr};
+static std::atomic<int64_t> g_trace_words{0};
+static std::atomic<uint32_t> g_wait_extra{0};
+static std::atomic<uint32_t> g_wait_ticks{kDefaultWaitTicks};
+
+void diag_set_trace(uint64_t* buf, int64_t words) {
+  g_trace_words.store(buf ? words : 0);
+  g_trace.store(buf);
+}
+void diag_set_topk_wait(uint32_t extra, uint32_t ticks) {
+  g_wait_extra.store(extra);
+  g_wait_ticks.store(ticks ? ticks : kDefaultWaitTicks);
+}
+static void apply_diag(AttnParams* a) {
+  a->wait_extra = g_wait_extra.load();
+  a->wait_ticks = g_wait_ticks.load();
+  a->trace = g_trace.load();
+  a->trace_words = g_trace_words.load();
 }
 
 // A merge to follow the attention (lca_hybrid_attn_merge): sink and output.
@@ -1326,6 +1424,7 @@ static int launch_attention_impl(const lca_attn_source* srcs, int n_src, const v
   AttnParams a{};
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
+  apply_diag(&a);
   int splits = 0, topk = -1;
   for (int i = 0; i < n_src; ++i) {
     const lca_attn_source& in = srcs[i];
@@ -1390,6 +1489,7 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
   AttnParams a{};
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
+  apply_diag(&a);
   const bool mfma = dtype == LCA_BF16 && H % 16 == 0;
   int blocks = 0;
   int topk = -1;          // the TOPK source

@@ -761,8 +761,12 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
   auto emit = [&](uint32_t o, int32_t e) { out[o] = e; };
   const uint32_t got = nv <= kBitmapEntries ? topk_row_select<kFinThreads, true>(w, r, P, L, S, emit, cl, kFinCandLds)
                                             : topk_row_select<kFinThreads, false>(w, r, P, L, S, emit, cl, kFinCandLds);
-  if (got == 0)
-    for (int t = threadIdx.x; t < a.k; t += blockDim.x) out[t] = -1;
+  if (got == 0) {
+    // inconsistent lists (nothing was emitted): the exact selection from the
+    // row's scores alone
+    __syncthreads();
+    topk_row_scan_select<kFinThreads>(a.scores + (int64_t)r * a.max_entries, nv, (uint32_t)a.k, L.h, S, emit);
+  }
 }
 
 // The exact top-k of one row per block, for calls with many rows per

@@ -296,6 +296,97 @@ __device__ __forceinline__ void topk_prefetch(const TopkWs& w, int r, SelectPref
   }
 }
 
+// Exact top-k of one row straight from its scores, with nothing but a 2048-word
+// LDS histogram h and the block scan's scratch: three radix passes over the
+// score keys (bits 31..21, 20..10, 9..0) find the k-th largest key v and how
+// many entries of key v are taken (the smallest indices among them); a fourth
+// pass emits every chosen entry with its rank in ascending index order.  Used
+// when the filtered lists cannot be trusted (a bounded wait gave up, or the
+// lists are inconsistent); slower than the list selection (four reads of the
+// row's scores) but it depends on no other block.  k < nv.
+template <int NT, int U, class F>
+__device__ __forceinline__ void for_row_keys(const float* S, int64_t nv, F f) {
+  for (int64_t base = threadIdx.x; base < nv; base += (int64_t)NT * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = base + (int64_t)u * NT;
+      v[u] = e < nv ? S[e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + (int64_t)u * NT < nv) f(score_key(v[u]));
+  }
+}
+
+template <int NT, class Emit>
+__device__ void topk_row_scan_select(const float* S, int64_t nv, uint32_t k, uint32_t* h, SelectShared& sh,
+                                     Emit emit) {
+  static_assert(kHistBins % NT == 0 && 1024 % NT == 0, "the bins must split evenly over the block");
+  constexpr int U = 8;
+  // level 1: the top 11 key bits
+  for (int i = threadIdx.x; i < kHistBins; i += NT) h[i] = 0;
+  __syncthreads();
+  for_row_keys<NT, U>(S, nv, [&](uint32_t key) { lds_count(h, key >> 21); });
+  __syncthreads();
+  find_threshold(h, kHistBins, k, sh.sm, &sh.T, &sh.above, &sh.cnt);
+  const uint32_t T1 = (uint32_t)sh.T;
+  uint32_t need = k - sh.above;
+  // level 2: bits 20..10 inside bin T1
+  for (int i = threadIdx.x; i < kHistBins; i += NT) h[i] = 0;
+  __syncthreads();
+  for_row_keys<NT, U>(S, nv, [&](uint32_t key) {
+    if ((key >> 21) == T1) lds_count(h, (key >> 10) & 0x7FFu);
+  });
+  __syncthreads();
+  find_threshold(h, kHistBins, need, sh.sm, &sh.T, &sh.above, &sh.cnt);
+  const uint32_t p2 = (T1 << 11) | (uint32_t)sh.T;
+  need -= sh.above;
+  // level 3: bits 9..0 inside that bin
+  for (int i = threadIdx.x; i < 1024; i += NT) h[i] = 0;
+  __syncthreads();
+  for_row_keys<NT, U>(S, nv, [&](uint32_t key) {
+    if ((key >> 10) == p2) lds_count(h, key & 0x3FFu);
+  });
+  __syncthreads();
+  find_threshold(h, 1024, need, sh.sm, &sh.T, &sh.above, &sh.cnt);
+  const uint32_t vkey = (p2 << 10) | (uint32_t)sh.T;
+  const uint32_t neq = need - sh.above;  // entries of key vkey taken: the first neq in index order
+  // emission: thread t takes P consecutive entries of each NT*P chunk; one
+  // block scan of (entries above vkey, entries equal to vkey) per chunk
+  constexpr int P = 8;
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int64_t base = 0; base < nv; base += (int64_t)NT * P) {
+    const int64_t e0 = base + (int64_t)threadIdx.x * P;
+    uint32_t keys[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) keys[i] = e0 + i < nv ? score_key(S[e0 + i]) : 0u;
+    uint32_t ngt = 0, nq = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const bool in = e0 + i < nv;
+      ngt += (in && keys[i] > vkey) ? 1u : 0u;
+      nq += (in && keys[i] == vkey) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan(ngt | (nq << 16), &tot, sh.sm);  // both < 2^16
+    uint32_t eq = run_eq + (pre >> 16);
+    uint32_t o = run_gt + (pre & 0xFFFFu) + min(eq, neq);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (e0 + i >= nv) continue;
+      if (keys[i] > vkey) {
+        emit(o++, (int32_t)(e0 + i));
+      } else if (keys[i] == vkey) {
+        if (eq < neq) emit(o++, (int32_t)(e0 + i));
+        ++eq;
+      }
+    }
+    run_gt += tot & 0xFFFFu;
+    run_eq += tot >> 16;
+  }
+}
+
 template <int NT, bool ORDERED, class Emit>
 __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch<NT>& P, SelectLds& L,
                                     SelectShared& S, Emit emit, uint64_t* cl, uint32_t ncl) {

@@ -39,6 +39,16 @@ def test_strerror_and_version(L):
     assert lib.lca_strerror(-99) == b"unknown status"
 
 
+def test_diag_settings(L):
+    lib = L.lib
+    assert lib.lca_diag_topk_wait(-1, 0) == L.LCA_ERR_INVALID_ARG
+    assert lib.lca_diag_topk_wait(0, -5) == L.LCA_ERR_INVALID_ARG
+    assert lib.lca_diag_topk_wait(2000, 0) == L.LCA_ERR_INVALID_ARG
+    assert lib.lca_diag_topk_wait(0, 0) == L.LCA_OK          # the defaults
+    assert lib.lca_diag_trace(ctypes.c_void_p(256), -1) == L.LCA_ERR_INVALID_ARG
+    assert lib.lca_diag_trace(None, 0) == L.LCA_OK            # tracing off
+
+
 def test_kv_compress_rejects(L):
     lib = L.lib
     assert lib.lca_kv_compress(None, 1, None, None, 1, 1e-6, 1, None) == L.LCA_ERR_INVALID_ARG

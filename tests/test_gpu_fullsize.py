@@ -18,7 +18,7 @@ from oracle import numerics as onum
 
 from oracle import quant as oquant
 
-from gpu_util import assert_close, check_topk, f64, key_rows, layer_for, score_bound
+from gpu_util import assert_close, check_topk, f64, key_rows, layer_for, mx_rows, score_bound
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -67,11 +67,18 @@ def _check_rows(cfg, raw, caches, bufs, out, rows, rng):
         for got, src, lg, norm in ((kv_csa, x, a, True), (ikey, u, c, False)):
             pooled = ocmp.compress(src, lg, cfg.m, cfg.w, norm, cfg.eps, ent)
             if fp8 and got is ikey and cfg.ikey == "mxfp4":
-                # MXFP4 rows: the oracle's quantization, or one element step
-                # (at most a quarter of the block's amax) from it
-                ref = oquant.dequantize_mx_rows(*oquant.quantize_mx_rows(pooled))
-                am = np.repeat(np.max(np.abs(ref.reshape(len(ent), -1, 32)), axis=2), 32, axis=1)
-                assert np.all(np.abs(got[ent] - ref) <= 0.5 * am + 1e-30)
+                # MXFP4 rows: the oracle's quantization, or (where the fp32
+                # pooling sits on a rounding boundary) one element step from
+                # it; block scales move only when a block's amax sits on a
+                # power of two; at most 0.1% of the values differ
+                qr, sr = oquant.quantize_mx_rows(pooled)
+                _, sg, _ = mx_rows(caches.ikey[co[b]:co[b + 1]][ent], cfg.dI)
+                vr = oquant.dequantize_mx_rows(qr, sr)
+                assert np.mean(sg != sr) <= 1e-3, "block scales"
+                step = 2.0 * np.repeat(np.maximum(sg, sr), 32, axis=1)
+                assert np.all(np.abs(got[ent] - vr) <= step), "an element more than one step off"
+                flips = int(np.sum(got[ent] != vr))
+                assert flips <= max(2, vr.size // 1000), f"{flips} of {vr.size} values off the oracle"
                 continue
             if fp8 and got is ikey:
                 # fp8 rows: the oracle's quantization, or one E4M3 step from it
@@ -175,12 +182,28 @@ def test_pro_varlen_full():
     assert torch.isfinite(out.float()).all()
 
 
+def prefill_rows(cached, chunk, n=256, seed=7):
+    """256 seeded rows of a prefill chunk: the first, second and last rows,
+    every row at a position where an HCA entry completes (i = 127 mod 128),
+    rows where a CSA entry completes (i = 3 mod 4), and random others."""
+    rng = np.random.default_rng(seed)
+    pos = cached + np.arange(chunk)
+    rows = {0, 1, chunk - 1} | set(np.nonzero(pos % 128 == 127)[0].tolist())
+    c4 = np.nonzero(pos % 4 == 3)[0]
+    rows |= set(rng.choice(c4, size=min(len(c4), 96), replace=False).tolist())
+    rest = np.setdiff1d(np.arange(chunk), np.fromiter(rows, dtype=np.int64))
+    rows |= set(rng.choice(rest, size=max(0, min(len(rest), n - len(rows))), replace=False).tolist())
+    return sorted(rows)
+
+
 def test_flash_prefill_full():
     """The Flash-shaped chunked prefill (4096 query tokens after 262144 cached
     ones): the chunk's entries appended by kv_compress, then scores, top-k
-    and the fused attention for every row; rows 0, 1365, 2731 and 4095 are
-    checked against the oracle (selected sets, and outputs stage-wise from
-    the GPU caches and selection, end to end when the sets agree)."""
+    and the fused attention for every row; 256 seeded rows (first, last, the
+    positions where CSA and HCA entries complete, random others) are checked
+    against the oracle: each selection is the exact top-k of the GPU's own
+    scores and the oracle's up to near ties, and each output equals the
+    oracle's attention over the GPU caches and selection."""
     cfg = li.FLASH_PREFILL
     raw = li.make_raw_torch(cfg, 0, "cuda")
     layer = layer_for(cfg)
@@ -200,7 +223,17 @@ def test_flash_prefill_full():
     q_pos = raw["q_pos"].reshape(-1).contiguous()
     out, inter = layer.step(caches, raw["x"], raw["tok_off"], raw["q"], raw["p"], raw["omega"], raw["sigma"], q_pos,
                             raw["q_pos"].reshape(-1).cpu().numpy(), keep=True)
+    # the scores again, kept (the score kernel is deterministic), for the
+    # exact self-consistency check of each selection
+    from long_context_attention_20_amd import ops
+    max_csa = ocmp.n_entries(L, cfg.m, cfg.w)
+    rows = prefill_rows(cached, cfg.tq)
+    s_gpu = torch.empty((cfg.tq, max_csa), dtype=torch.float32, device="cuda")
+    ops.csa_index_score(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa,
+                        layer.index_workspace(cfg.tq, max_csa, "cuda"), scores=s_gpu)
     torch.cuda.synchronize()
+    sg = s_gpu[rows].cpu().numpy()
+    del s_gpu
     idx_h = inter["idx"].cpu().numpy()
     out_h = f64(out)
     ikey = f64(caches.ikey)
@@ -208,9 +241,12 @@ def test_flash_prefill_full():
     kv_hca = f64(caches.kv_hca)
     x = _host(raw["x"])
     sig = raw["sigma"].cpu().numpy().astype(np.float64)
-    for t in (0, 1365, 2731, cfg.tq - 1):
+    near = 0
+    print(f"[flash_prefill] checking {len(rows)} rows", flush=True)
+    for n_done, t in enumerate(rows):
         i = cached + t
-        print(f"[flash_prefill] row {t} (position {i})", flush=True)
+        if n_done % 32 == 0:
+            print(f"[flash_prefill] row {t} (position {i}), {n_done} of {len(rows)} done", flush=True)
         nv = ocmp.n_visible(i, cfg.m, cfg.w)
         nh = ocmp.n_visible(i, cfg.m2, cfg.w2)
         p = f64(raw["p"][t])
@@ -219,14 +255,12 @@ def test_flash_prefill_full():
         bound = score_bound(p, om, ikey[:nv])
         sel = idx_h[t][idx_h[t] >= 0]
         assert len(sel) == min(cfg.k, nv) and np.all(sel < nv) and np.all(np.diff(sel) > 0)
-        ref_sel = oidx.topk(s_ref, cfg.k)
-        kth = s_ref[ref_sel[-1]]
-        diff = set(sel.tolist()) ^ set(ref_sel.tolist())
-        for j in diff:
-            assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + bound[j], f"entry {j} is not a near tie"
+        near += check_topk(idx_h[t], sg[n_done], s_ref, bound, cfg.k)
         qhat = oatt.normalize_query(f64(raw["q"][t]), cfg.eps, cfg.dtype)
         win = oatt.normalize_tokens(x[max(0, i - cfg.W + 1):i + 1].astype(np.float64), cfg.eps, cfg.dtype)
         parts = [oatt.partial(qhat, kv_csa[sel], cfg.scale), oatt.partial(qhat, kv_hca[:nh], cfg.scale),
                  oatt.partial(qhat, win, cfg.scale)]
         o_ref, _ = oatt.merge(parts, sig)
         assert_close(out_h[t], onum.round_to(o_ref, cfg.dtype), cfg.dtype, f"prefill row {t}")
+    print(f"[flash_prefill] {len(rows)} rows checked, {near} near-tie differences from the oracle's selections",
+          flush=True)

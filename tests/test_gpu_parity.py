@@ -241,21 +241,30 @@ def test_prefill_chunk_causal():
     assert torch.equal(caches.kv_csa, full[0]) and torch.equal(caches.ikey, full[1]) and torch.equal(caches.kv_hca, full[2])
     out, inter = layer.step(caches, d["x"], d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"],
                             raw["q_pos"].reshape(-1), keep=True)
+    # the same scores again, kept (the score kernel is deterministic)
+    from long_context_attention_20_amd import ops
+    qmax = cached + chunk
+    max_csa = ocmp.n_entries(qmax, cfg.m, cfg.w)
+    s_gpu = torch.empty((chunk, max_csa), dtype=torch.float32, device="cuda")
+    ops.csa_index_score(d["p"], d["omega"], caches.ikey, caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w, max_csa,
+                        layer.index_workspace(chunk, max_csa, "cuda"), scores=s_gpu)
     torch.cuda.synchronize()
+    sg = s_gpu.cpu().numpy()
     idx_h = inter["idx"].cpu().numpy()
     g = seq_caches(caches, 0)
     xs = opipe.seq_slice(raw["x"], raw["tok_off"], 0)
     out_h = f64(out)
-    for t in list(range(0, chunk, 7)) + [chunk - 1]:
+    near = 0
+    for t in range(chunk):  # every row of the chunk
         i = int(raw["q_pos"][0, t])
         nv = ocmp.n_visible(i, cfg.m, cfg.w)
-        s_ref = oidx.scores(raw["p"][t], raw["omega"][t], g.ikey[:nv])
-        sel = idx_h[t][idx_h[t] >= 0]
-        assert np.all(sel < nv)
+        p64, om = raw["p"][t].astype(np.float64), raw["omega"][t].astype(np.float64)
+        s_ref = oidx.scores(p64, om, g.ikey[:nv])
+        # exact top-k of the GPU's own scores; against the oracle, near ties only
+        near += check_topk(idx_h[t], sg[t], s_ref, score_bound(p64, om, g.ikey[:nv]), cfg.k)
         res = opipe.query_step(g, xs, raw["q"][t], raw["p"][t], raw["omega"][t], raw["sigma"], i, cfg, idx=idx_h[t])
         assert_close(out_h[t], res["out"], cfg.dtype, f"prefill row {t}")
-        ref_sel = set(oidx.topk(s_ref, cfg.k).tolist())
-        assert len(set(sel.tolist()) ^ ref_sel) <= 2
+    print(f"  prefill chunk: {chunk} rows, {near} near-tie differences from the oracle's selection", flush=True)
 
 
 def test_index_permutation_invariance():
@@ -601,19 +610,25 @@ def test_decode_step_mtp(tq, ikey):
     idx_h = bufs["idx"].cpu().numpy()
     out_h = f64(out)
     keys = key_rows(caches.ikey, cfg.dI)
-    co = caches.csa_off_h
+    co, ho = caches.csa_off_h, caches.hca_off_h
+    end_to_end = 0
     for b in range(cfg.B):
+        # the GPU's caches as the oracle sees them (key rows as the values they stand for)
+        g = opipe.SeqCaches(f64(caches.kv_csa[co[b]:co[b + 1]]), keys[co[b]:co[b + 1]],
+                            f64(caches.kv_hca[ho[b]:ho[b + 1]]))
+        xs = opipe.seq_slice(raw["x"], raw["tok_off"], b)
         for t in range(tq):
             r = b * tq + t
             res = ores[(b, t)]
             chosen = set(idx_h[r][idx_h[r] >= 0].tolist())
+            i = int(raw["q_pos"][b, t])
+            nv = ocmp.n_visible(i, cfg.m, cfg.w)
             if not fp8:
                 assert chosen == set(res["sel"].tolist()), f"row ({b}, {t}) selection"
                 assert_close(out_h[r], res["out"], cfg.dtype, f"mtp row ({b}, {t})")
+                end_to_end += nv > cfg.k
                 continue
             # fp8 keys: the exact top-k of the oracle scores of the GPU rows, near ties aside
-            i = int(raw["q_pos"][b, t])
-            nv = ocmp.n_visible(i, cfg.m, cfg.w)
             kb = keys[co[b]:co[b] + nv]
             p64, om = raw["p"][r].astype(np.float64), raw["omega"][r].astype(np.float64)
             s_ref = oidx.scores(p64, om, kb)
@@ -622,8 +637,16 @@ def test_decode_step_mtp(tq, ikey):
             bound = score_bound(p64, om, kb)
             for j in chosen ^ set(ref.tolist()):
                 assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + 2 * bound[j], f"row ({b}, {t}): {j}"
+            # stage-wise: the oracle's attention over the GPU-chosen set and the GPU caches (always)
+            staged = opipe.query_step(g, xs, raw["q"][r], raw["p"][r], raw["omega"][r], raw["sigma"], i, cfg,
+                                      idx=idx_h[r])
+            assert_close(out_h[r], staged["out"], cfg.dtype, f"mtp {ikey} row ({b}, {t}) over the GPU selection")
+            # end to end (oracle from raw inputs) where the selections agree
             if chosen == set(res["sel"].tolist()):
-                assert_close(out_h[r], res["out"], cfg.dtype, f"mtp fp8 row ({b}, {t})")
+                assert_close(out_h[r], res["out"], cfg.dtype, f"mtp {ikey} row ({b}, {t})")
+                end_to_end += nv > cfg.k
+    assert end_to_end >= 1, "no row with more than k visible entries was checked end to end"
+    print(f"  rows checked end to end with more than k candidates: {end_to_end}", flush=True)
 
 
 @pytest.mark.parametrize("path", ["decode_two_rows", "many_rows"])
@@ -805,9 +828,11 @@ def test_decode_step_fp8_keys(fmt):
                             done_len=done, done_h=done_h)
     torch.cuda.synchronize()
     assert torch.equal(caches.kv_csa, full[0]) and torch.equal(caches.kv_hca, full[2])
-    # the appended fp8 rows are the build's up to the fp32 rounding of the
-    # pooling (the stored scale shows every bit of it): other rows untouched,
-    # scales within fp32 rounding, bytes within one E4M3 step
+    # the appended key rows are the build's up to the fp32 rounding of the
+    # pooling (the same key pooled in another fp32 order): other rows
+    # untouched; fp8 rows: scales within fp32 rounding, each byte's value
+    # within one E4M3 step; MXFP4 rows: each element within one block scale
+    # of either row's (at most half an E2M1 spacing each), pad bytes equal
     appended = set()
     for b, L in enumerate(cfg.lens):
         n0, n1 = ocmp.n_entries(L - 1, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m, cfg.w)
@@ -816,8 +841,18 @@ def test_decode_step_fp8_keys(fmt):
     differ = set(np.nonzero(np.any(ga != gb, axis=1))[0].tolist())
     print(f"[{fmt} decode] appended rows {sorted(appended)}, differing from the build {sorted(differ)}", flush=True)
     assert differ <= appended
-    va, vb = key_rows(caches.ikey, cfg.dI), key_rows(full[1], cfg.dI)
-    assert np.all(np.abs(va - vb) <= 2.0 ** -2 * np.max(np.abs(vb), axis=1, keepdims=True) + 1e-30)
+    if fmt == "fp8":
+        qa, sa, _ = fp8_rows(caches.ikey)
+        qb, sb, _ = fp8_rows(full[1])
+        assert np.all(np.abs(sa - sb) <= 2.0 ** -20 * sb)
+        assert np.all(np.abs(qa - qb) <= 2.0 ** -3 * np.maximum(np.abs(qa), np.abs(qb)) + 2.0 ** -9)
+    else:
+        qa, sa, pa = mx_rows(caches.ikey, cfg.dI)
+        qb, sb, pb = mx_rows(full[1], cfg.dI)
+        da = qa.reshape(qa.shape[0], -1, 32) * sa[..., None]
+        db = qb.reshape(qb.shape[0], -1, 32) * sb[..., None]
+        assert np.all(np.abs(da - db) <= (sa + sb)[..., None])
+        assert np.array_equal(pa, pb)
     keys = _check_key_cache(cfg, raw, caches.ikey, caches.csa_off_h)
     _, ores = opipe.run(raw, cfg)
     idx_h = bufs["idx"].cpu().numpy()

@@ -1,0 +1,174 @@
+"""GPU: the top-k selection inside the attention launch when the sparse
+blocks' wait for each other gives up.
+
+The sparse blocks of a TOPK source filter their shares of a row's scores and
+wait for the row's other blocks; the wait is bounded.  A block whose wait
+gives up selects the exact top-k from the row's scores alone.  The tests
+force that path from the host (lca_diag_topk_wait: every wait expects one
+share more than exists and gives up after 1 us; every kernel still exits
+normally) and require the same indices and bit-identical partials as the
+separate selection, on consecutive calls sharing one workspace (so the
+workspace is also left ready for the next call).  The per-block trace shows
+that the path was taken.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import lca_inputs as li
+from oracle import compress as ocmp
+
+from gpu_util import layer_for, tdtype, to_device
+
+pytestmark = pytest.mark.gpu
+
+TRACE_WORDS = 8
+GAVE_UP, FALLBACK, OWNS = 1 << 2, 1 << 3, 1 << 4
+
+
+def _lib():
+    from long_context_attention_20_amd import _lib
+    return _lib
+
+
+class Diag:
+    """Forced give-up of the top-k wait and the per-block trace, restored on exit."""
+
+    def __init__(self, extra, ticks, trace_blocks=4096):
+        self.extra, self.ticks = extra, ticks
+        self.trace = torch.zeros(trace_blocks * TRACE_WORDS, dtype=torch.int64, device="cuda")
+
+    def __enter__(self):
+        L = _lib()
+        L.check(L.lib.lca_diag_topk_wait(self.extra, self.ticks), "diag_topk_wait")
+        L.check(L.lib.lca_diag_trace(ctypes.c_void_p(self.trace.data_ptr()), self.trace.numel()), "diag_trace")
+        return self
+
+    def __exit__(self, *exc):
+        torch.cuda.synchronize()
+        L = _lib()
+        L.check(L.lib.lca_diag_trace(None, 0), "diag_trace")
+        L.check(L.lib.lca_diag_topk_wait(0, 0), "diag_topk_wait")
+        return False
+
+    def records(self):
+        t = self.trace.view(-1, TRACE_WORDS).cpu().numpy().view(np.uint64)
+        return t[t[:, 0] != 0]
+
+
+def _setup(cfg, torch_inputs=False):
+    if torch_inputs:
+        d = li.make_raw_torch(cfg, 0, "cuda")
+        raw = None
+    else:
+        raw = li.make_raw(cfg)
+        d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", d["x"].dtype)
+    layer.compress(caches, d, d["tok_off"])
+    q_pos = d["q_pos"].reshape(-1).contiguous()
+    return d, caches, q_pos, int(q_pos.max().item()) + 1
+
+
+def _reference(cfg, d, caches, q_pos, max_csa, splits):
+    from long_context_attention_20_amd import ops
+    rows = q_pos.numel()
+    sc, sh, sw = splits
+    ws_ref = torch.zeros(ops.csa_index_topk_workspace(rows, max_csa, cfg.k), dtype=torch.uint8, device="cuda")
+    idx_ref = ops.csa_index_topk(d["p"], d["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
+                                 max_csa, ws_ref)
+    others = [dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=cfg.m2, w2=cfg.w2, n_split=sh),
+              dict(kind="window", kv=d["x"], off=d["tok_off"], W=cfg.W, n_split=sw)]
+    ref = ops.hybrid_attn(d["q"], q_pos, [dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx_ref,
+                                               n_split=sc)] + others, cfg.scale, cfg.eps)
+    return idx_ref, ref, others
+
+
+def _topk_calls(cfg, d, caches, q_pos, max_csa, splits, others, ws, reps):
+    from long_context_attention_20_amd import ops
+    rows = q_pos.numel()
+    outs = []
+    for _ in range(reps):
+        idx_out = torch.full((rows, cfg.k), -7, dtype=torch.int32, device="cuda")
+        ops.csa_index_score(d["p"], d["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws)
+        src = dict(kind="topk", kv=caches.kv_csa, off=caches.csa_off, k=cfg.k, m2=cfg.m, w2=cfg.w,
+                   max_entries=max_csa, ws=ws, idx_out=idx_out, n_split=splits[0])
+        got = ops.hybrid_attn(d["q"], q_pos, [src] + others, cfg.scale, cfg.eps)
+        torch.cuda.synchronize()
+        outs.append((idx_out, got))
+    return outs
+
+
+CASES = {
+    # two sequences with planted duplicate high-norm keys (exact ties at the cut)
+    "pro_planted": (li.small("wait_planted", 102, (9000, 5003), H=128, D=512, k=1024, plant=32), (3, 5, 2), False),
+    # rows above and below k; one sequence shorter than the window
+    "flash_ragged": (li.small("wait_ragged", 101, (3000, 1029, 517, 7), H=64, D=512, k=512), (3, 5, 2), False),
+    # two rows, one with all head weights negative: thousands of exact zero ties
+    "zero_ties": (li.small("wait_ties", 122, (200000,), tq=2, H=64, D=512, k=512), (8, 6, 1), True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_topk_wait_gives_up_same_result(name):
+    from long_context_attention_20_amd import ops
+    cfg, splits, torch_inputs = CASES[name]
+    print(f"[topk wait {name}] lens={cfg.lens} tq={cfg.tq} H={cfg.H} k={cfg.k} splits={splits}", flush=True)
+    d, caches, q_pos, qmax = _setup(cfg, torch_inputs)
+    if name == "zero_ties":
+        d["omega"][0] = -d["omega"][0].abs()
+    max_csa = max(1, ocmp.n_entries(qmax, cfg.m, cfg.w))
+    idx_ref, ref, others = _reference(cfg, d, caches, q_pos, max_csa, splits)
+    rows = q_pos.numel()
+    ws = torch.zeros(ops.csa_index_topk_workspace(rows, max_csa, cfg.k), dtype=torch.uint8, device="cuda")
+    # normal operation first (the waits end), then every wait forced to give up
+    # after 1 us, then normal operation again on the same workspace
+    for extra, ticks, want_fallback in ((0, 0, False), (1, 100, True), (0, 0, False)):
+        with Diag(extra, ticks) as dg:
+            outs = _topk_calls(cfg, d, caches, q_pos, max_csa, splits, others, ws, reps=2)
+            recs = dg.records()
+        for rep, (idx_out, got) in enumerate(outs):
+            assert torch.equal(idx_out, idx_ref), f"extra={extra} call {rep}: indices differ from csa_index_topk"
+            for (go, gl), (ro, rl), what in zip(got, ref, ("csa", "hca", "window")):
+                assert torch.equal(go, ro) and torch.equal(gl, rl), f"extra={extra} call {rep}: {what} partials differ"
+        # the trace holds the last call's blocks
+        flags = (recs[:, 7] & np.uint64(0xFFFFFFFF)).astype(np.int64)
+        kind = flags & 3
+        row = flags >> 12
+        assert np.any(kind == 3), "no top-k block traced"
+        q_pos_h = q_pos.cpu().numpy()
+        lens = cfg.lens
+        for i in np.nonzero(kind == 3)[0]:
+            r = int(row[i])
+            L = lens[r // cfg.tq]
+            nv = min(ocmp.n_entries(int(q_pos_h[r]) + 1, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m, cfg.w))
+            selects = nv > cfg.k and (flags[i] & OWNS)
+            if want_fallback and selects:
+                assert flags[i] & GAVE_UP and flags[i] & FALLBACK, f"block {i} (row {r}) did not fall back"
+            if not want_fallback:
+                assert not (flags[i] & FALLBACK) or (flags[i] & GAVE_UP), "fallback without a reason"
+        gave_up = int(np.sum((kind == 3) & ((flags & GAVE_UP) != 0)))
+        print(f"  extra={extra}: {int(np.sum(kind == 3))} top-k blocks traced, {gave_up} gave up", flush=True)
+
+
+def test_trace_phases_ordered():
+    """The per-block trace of a decode step's attention launch: every block's
+    stamps are in phase order, and every source kind of the launch appears."""
+    cfg = li.small("trace", 109, (3000, 1500), H=64, D=512, k=256)
+    d, caches, q_pos, qmax = _setup(cfg)
+    max_csa = max(1, ocmp.n_entries(qmax, cfg.m, cfg.w))
+    from long_context_attention_20_amd import ops
+    splits = (3, 5, 2)
+    _, _, others = _reference(cfg, d, caches, q_pos, max_csa, splits)
+    ws = torch.zeros(ops.csa_index_topk_workspace(q_pos.numel(), max_csa, cfg.k), dtype=torch.uint8, device="cuda")
+    with Diag(0, 0) as dg:
+        _topk_calls(cfg, d, caches, q_pos, max_csa, splits, others, ws, reps=1)
+        recs = dg.records()
+    kinds = set(int(v) & 3 for v in recs[:, 7])
+    assert kinds == {0, 2, 3}, kinds
+    for rec in recs:
+        st = [int(v) for v in rec[:7]]
+        seq = [st[0]] + [v for v in st[1:4] if v] + st[4:7]
+        assert all(b >= a for a, b in zip(seq, seq[1:])), f"phases out of order: {st}"
