@@ -117,42 +117,48 @@ def step_bytes(cfg):
 
 
 def kernel_cost(cfg, name):
-    """(bytes, flops) that one launch of a step's kernel must move / do (keys
-    shared by the tq rows of a sequence counted once)."""
+    """(bytes, flops, overhead bytes) of one launch of a step's kernel: the
+    bytes are its share of the step's algorithmic bytes (the byte model of
+    step_bytes: keys shared by the tq rows of a sequence counted once); the
+    overhead is traffic the design adds that the method does not need (the
+    row's scores written by the front launch and read back by the sparse
+    launch, the fp32 split partials)."""
     e = 2 if cfg.dtype == "bf16" else 4
     tq = cfg.tq
-    by = fl = 0
+    by = fl = ov = 0
     for L in cfg.lens:
         ncsa = n_windows(L, cfg.m, cfg.w)
         nh = n_windows(L, cfg.m2, cfg.w2)
         kk = min(cfg.k, ncsa)
-        if name == "csa_index_score":
+        nwin = min(cfg.W + tq - 1, L)
+        if name in ("csa_index_score", "csa_index_score_append", "decode_front"):
             by += ncsa * key_bytes(cfg)
-            fl += 2 * ncsa * cfg.dI * cfg.HI
-        elif name == "csa_topk_select":
-            by += ncsa * 4 + kk * 4
-        elif name == "csa_sparse_attn":
+            fl += 2 * ncsa * cfg.dI * cfg.HI * tq
+            ov += tq * ncsa * 4                                  # scores written
+        if name in ("csa_index_score_append", "decode_front"):  # the entries the new tokens complete
+            by += (2 * cfg.w * cfg.D + 2 * cfg.w * cfg.dI + 2 * cfg.w2 * cfg.D) * e + (2 * cfg.D + cfg.dI) * e
+        if name == "decode_front":                               # HCA entries, window rows, the queries
+            by += (nh + nwin) * cfg.D * e + tq * cfg.H * cfg.D * e
+            fl += 4 * cfg.H * cfg.D * (nh + min(cfg.W, L)) * tq
+        if name == "csa_topk_select":
+            by += kk * 4
+            ov += tq * ncsa * 4
+        if name == "csa_sparse_attn":
             by += kk * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * kk
-        elif name == "hca_attn":
+        if name == "hca_attn":
             by += nh * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * nh
-        elif name == "swa_attn":
-            nwin = min(cfg.W, L)
-            by += nwin * cfg.D * e + cfg.H * cfg.D * e
-            fl += 4 * cfg.H * cfg.D * nwin
-        elif name == "hybrid_attn":                      # the top-k selection + the three branches
-            nwin = min(cfg.W, L)
-            by += tq * (ncsa * 4 + kk * 4)                     # every score read, selection written
-            by += (tq * kk + nh + min(cfg.W + tq - 1, L)) * cfg.D * e + tq * cfg.H * cfg.D * e
-            fl += 4 * cfg.H * cfg.D * (kk + nh + nwin) * tq
-        elif name == "swa_merge":
-            by += tq * (cfg.H * cfg.D * e + cfg.H * 4)         # output + sink
-        elif name == "csa_index_score_append":                 # scores + the entries the new tokens complete
-            by += ncsa * key_bytes(cfg)
-            by += (2 * cfg.w * cfg.D + 2 * cfg.w * cfg.dI + 2 * cfg.w2 * cfg.D) * e + (2 * cfg.D + cfg.dI) * e
-            fl += 2 * ncsa * cfg.dI * cfg.HI * tq
-    return by, fl
+        if name == "swa_attn":
+            by += min(cfg.W, L) * cfg.D * e + cfg.H * cfg.D * e
+            fl += 4 * cfg.H * cfg.D * min(cfg.W, L)
+        if name == "hybrid_attn":                                # the selection + the sparse branch
+            by += tq * kk * (cfg.D * e + 4) + tq * cfg.H * cfg.D * e
+            fl += 4 * cfg.H * cfg.D * kk * tq
+            ov += tq * ncsa * 4                                  # the row's scores read back
+        if name == "swa_merge":
+            by += tq * (cfg.H * cfg.D * e + cfg.H * 4)           # output + sink
+    return by, fl, ov
 
 
 class LayerState:
@@ -189,7 +195,7 @@ class Position:
 
 
 class Runner:
-    def __init__(self, cfg, R, dev, split_csa=0, split_hca=0):
+    def __init__(self, cfg, R, dev, split_csa=0, split_hca=0, front=None):
         import torch
         from long_context_attention_20_amd import HybridAttention, ops
         self.torch, self.ops = torch, ops
@@ -201,14 +207,16 @@ class Runner:
         rows = cfg.B * cfg.tq
         qmax = max(cfg.lens)
         self.bufs = a.decode_buffers(rows, n_windows(qmax, cfg.m, cfg.w), n_windows(qmax, cfg.m2, cfg.w2), dev,
-                                     self.layers[0].q.dtype)
+                                     self.layers[0].q.dtype, front=front)
+        self.front = self.bufs["front"]
         self.sc, self.sh, self.sw = self.bufs["sc"], self.bufs["sh"], self.bufs["sw"]
-        self.names = ["csa_index_score_append", "hybrid_attn", "swa_merge"]
+        first = "decode_front" if self.front else "csa_index_score_append"
+        self.names = [first, "hybrid_attn", "swa_merge"]
         self.launches = {}  # kernels per call (default 1)
-        # the attention launch selects from what the score kernel leaves in
+        # the attention launch selects from what the score launch leaves in
         # the index workspace (and clears it): it is timed after the score
-        # kernel, whose time is subtracted
-        self.timed = ["csa_index_score_append", "csa_index_score_append+hybrid_attn", "swa_merge"]
+        # launch, whose time is subtracted
+        self.timed = [first, first + "+hybrid_attn", "swa_merge"]
 
     def step(self, L, pos=None):
         """The whole decode step (three calls on the current stream), at the
@@ -220,7 +228,11 @@ class Runner:
                                      done_len=pos.done, done_h=pos.done_h, lens_h=pos.lens_h)
 
     def calls(self, L):
-        """The same step as a sequence of single-kernel calls."""
+        """The same step (at the last position: every append) as its three
+        single-kernel calls."""
+        if self.front:
+            return self.attn.front_calls(L.caches, L.raw, L.tok_off, L.q, L.p, L.omega, L.sigma, L.q_pos, self.bufs,
+                                         L.done, L.done_h)
         cfg, ops, a, c, bf = self.cfg, self.ops, self.attn, L.caches, self.bufs
         st = a.compress_streams(c, L.raw, L.done_h)
         idx_st = [x for x in st if x["out"] is c.ikey][0]
@@ -337,60 +349,89 @@ def run_prefill(cfg, args, dev):
 
 TRACE_PHASES = ["start", "filter done", "wait done", "selection done", "prologue done", "key loop done", "stored"]
 KIND_NAMES = {0: "HCA (dense)", 1: "sparse (gather)", 2: "window", 3: "sparse (top-k inside)"}
+SUB_PHASES = [(15, "filter loads issued"), (8, "histogram summed"), (9, "threshold found"), (10, "list space reserved"),
+              (11, "own share counted"), (12, "lists loaded"), (13, "second threshold"), (14, "cut found")]
 
 
 def trace_attention(run, path, reps=6):
-    """Per-block phase stamps of the attention launch of a decode step (the
-    library's diagnostic trace, 100 MHz clock): for each source kind, the
-    median over blocks and the maximum of every phase, in microseconds after
-    the first block of the launch started; medians over `reps` steps on the
-    rotated layers.  Written as a markdown table to `path`."""
+    """Per-block phase stamps of the attention blocks of the decode step's
+    launches (the library's diagnostic trace, 100 MHz clock), one launch at a
+    time: the front launch's attention blocks and the sparse launch.  For
+    each source kind, the median over blocks and the maximum of every phase,
+    in microseconds after the first traced block of the launch started;
+    medians over `reps` steps on the rotated layers.  Written as markdown to
+    `path`."""
     import ctypes
     import torch
     from long_context_attention_20_amd import _lib
-    words = 8 * 65536
+    words = 16 * 65536
     buf = torch.zeros(words, dtype=torch.int64, device="cuda:0")
-    _lib.check(_lib.lib.lca_diag_trace(ctypes.c_void_p(buf.data_ptr()), words), "diag_trace")
-    per_rep = []
+    recs = {0: [], 1: []}
     try:
         for rep in range(reps):
-            L = run.layers[rep % len(run.layers)]
-            buf.zero_()
+            calls = run.calls(run.layers[rep % len(run.layers)])
+            for j, f in enumerate(calls):
+                traced = j in recs
+                if traced:
+                    buf.zero_()
+                    torch.cuda.synchronize()
+                    _lib.check(_lib.lib.lca_diag_trace(ctypes.c_void_p(buf.data_ptr()), words), "diag_trace")
+                f()
+                if traced:
+                    torch.cuda.synchronize()
+                    _lib.check(_lib.lib.lca_diag_trace(None, 0), "diag_trace")
+                    rec = buf.view(-1, 16).cpu().numpy().view(np.uint64).astype(np.int64)
+                    recs[j].append(rec[rec[:, 0] != 0])
             torch.cuda.synchronize()
-            run.step(L)
-            torch.cuda.synchronize()
-            rec = buf.view(-1, 8).cpu().numpy().view(np.uint64).astype(np.int64)
-            per_rep.append(rec[rec[:, 0] != 0])
     finally:
         _lib.lib.lca_diag_trace(None, 0)
     tick_us = 0.01
-    kinds = sorted(set(int(k) for r in per_rep for k in (r[:, 7] & 3)))
-    lines = ["| source | blocks | " + " | ".join(f"{p} (median / max)" for p in TRACE_PHASES) + " |",
-             "|---|---|" + "---|" * len(TRACE_PHASES)]
-    spans, gave_up = [], 0
-    for kd in kinds:
-        cells = []
-        for ph in range(7):
-            med, mx = [], []
-            for r in per_rep:
-                t0 = r[:, 0].min()
-                sel = r[(r[:, 7] & 3) == kd]
-                v = sel[:, ph]
-                v = v[v != 0]
-                if len(v):
-                    med.append(np.median(v - t0) * tick_us)
-                    mx.append(np.max(v - t0) * tick_us)
-            cells.append(f"{np.median(med):.2f} / {np.median(mx):.2f}" if med else "-")
-        nb = int(np.median([np.sum((r[:, 7] & 3) == kd) for r in per_rep]))
-        lines.append(f"| {KIND_NAMES.get(kd, kd)} | {nb} | " + " | ".join(cells) + " |")
-    for r in per_rep:
-        spans.append((r[:, 6].max() - r[:, 0].min()) * tick_us)
-        gave_up += int(np.sum((r[:, 7] >> 2) & 1))
-    xcc = [np.median([np.median(r[((r[:, 7] >> 8) & 15) == x][:, 0] - r[:, 0].min()) * tick_us
-                      for r in per_rep if np.any(((r[:, 7] >> 8) & 15) == x)]) for x in range(8)]
-    text = "\n".join(lines) + (f"\n\nfirst block start to last partial stored: median {np.median(spans):.2f} us "
-                                f"over {reps} steps; waits that gave up: {gave_up}\n"
-                                f"median block start per XCC (us): " + ", ".join(f"{v:.2f}" for v in xcc) + "\n")
+    out = []
+    for j, title in ((0, run.names[0]), (1, run.names[1])):
+        per_rep = [r for r in recs[j] if len(r)]
+        if not per_rep:
+            continue
+        kinds = sorted(set(int(k) for r in per_rep for k in (r[:, 7] & 3)))
+        lines = [f"### {title}", "",
+                 "| source | blocks | " + " | ".join(f"{p} (median / max)" for p in TRACE_PHASES) + " |",
+                 "|---|---|" + "---|" * len(TRACE_PHASES)]
+        for kd in kinds:
+            cells = []
+            for ph in range(7):
+                med, mx = [], []
+                for r in per_rep:
+                    t0 = r[:, 0].min()
+                    v = r[(r[:, 7] & 3) == kd][:, ph]
+                    v = v[v != 0]
+                    if len(v):
+                        med.append(np.median(v - t0) * tick_us)
+                        mx.append(np.max(v - t0) * tick_us)
+                cells.append(f"{np.median(med):.2f} / {np.median(mx):.2f}" if med else "-")
+            nb = int(np.median([np.sum((r[:, 7] & 3) == kd) for r in per_rep]))
+            lines.append(f"| {KIND_NAMES.get(kd, kd)} | {nb} | " + " | ".join(cells) + " |")
+        sub = [(ph, nm) for ph, nm in SUB_PHASES]
+        topk = [r[(r[:, 7] & 3) == 3] for r in per_rep]
+        if any(len(t) for t in topk):
+            cells = []
+            for ph, nm in sub:
+                med, mx = [], []
+                for r, t in zip(per_rep, topk):
+                    v = t[:, ph]
+                    v = v[v != 0]
+                    if len(v):
+                        med.append(np.median(v - r[:, 0].min()) * tick_us)
+                        mx.append(np.max(v - r[:, 0].min()) * tick_us)
+                cells.append(f"{np.median(med):.2f} / {np.median(mx):.2f}" if med else "-")
+            lines += ["", "top-k steps of the sparse blocks (median / max, us after the first block start):", "",
+                      "| " + " | ".join(nm for _, nm in sub) + " |", "|" + "---|" * len(sub),
+                      "| " + " | ".join(cells) + " |"]
+        spans = [(r[:, 6].max() - r[:, 0].min()) * tick_us for r in per_rep]
+        gave_up = sum(int(np.sum((r[:, 7] >> 2) & 1)) for r in per_rep)
+        lines.append("")
+        lines.append(f"first traced block start to last partial stored: median {np.median(spans):.2f} us over "
+                     f"{len(per_rep)} steps; waits that gave up: {gave_up}")
+        out.append("\n".join(lines))
+    text = "\n\n".join(out) + "\n"
     with open(path, "w") as f:
         f.write(text)
     print(text, file=sys.stderr, flush=True)
@@ -467,6 +508,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
     ap.add_argument("--split-csa", type=int, default=0, help="entry splits of the sparse attention (0: default)")
     ap.add_argument("--split-hca", type=int, default=0, help="entry splits of the HCA attention (0: default)")
+    ap.add_argument("--front", type=int, default=-1,
+                    help="1: decode step in front form (HCA and window beside the scores), 0: HCA and window "
+                         "beside the sparse blocks; -1: the layer's default for the workload")
     ap.add_argument("--trace-attn", default="", metavar="PATH",
                     help="also write the attention launch's per-block phase timeline to PATH")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -497,7 +541,7 @@ def main():
     sb = step_bytes(cfg)
     R = args.layers or max(1, -(-2 * MALL_BYTES // sb))
     t0 = time.perf_counter()
-    run = Runner(cfg, R, dev, args.split_csa, args.split_hca)
+    run = Runner(cfg, R, dev, args.split_csa, args.split_hca, front=None if args.front < 0 else bool(args.front))
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     print(f"[bench] {cfg.name}: {R} layers built in {setup_s:.1f} s; {sb / 1e6:.2f} MB/step; "
@@ -610,8 +654,8 @@ def main():
     ms = ms_graph if ms_graph is not None else ms_stream
     value = cfg.B * cfg.tq / (ms / 1e3)
     name = run.names[dom]
-    kb, kf = kernel_cost(cfg, name.split("(")[0])
-    if name == "hybrid_attn" and kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
+    kb, kf, kov = kernel_cost(cfg, name.split("(")[0])
+    if kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
         roof = {"bound": "mfma", "achieved": kf / (k_ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
                 "unit": "TFLOP/s"}
     else:
@@ -622,6 +666,13 @@ def main():
     roof["kernel_ms"] = k_ms
     roof["bytes_per_launch"] = kb
     roof["flops_per_launch"] = kf
+    roof["overhead_bytes_per_launch"] = kov
+    # every launch of the step against its share of the algorithmic bytes
+    per_kernel = {}
+    for n, t in zip(run.names, per):
+        b_, f_, o_ = kernel_cost(cfg, n)
+        per_kernel[n] = {"ms": float(t), "bytes": b_, "overhead_bytes": o_, "flops": f_,
+                         "hbm_frac": b_ / (t / 1e3) / HBM_PEAK if t > 0 else None}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -658,6 +709,7 @@ def main():
         "ms_per_step_stream": ms_stream,
         "ms_step_all_appends": ms_last,
         "kernel_ms": {n: float(t) for n, t in zip(run.names, per)},
+        "kernels": per_kernel,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

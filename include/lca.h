@@ -332,6 +332,22 @@ typedef struct lca_attn_source {
   int64_t max_entries;   /* as passed to the score call */
   const float* scores;   /* the score call's scores output, or NULL */
   int32_t* idx_out;      /* device int32 [B*Tq, k]: receives the selection */
+  /* optional (zero: off) */
+  const int64_t* done_len;  /* DENSE with part != 0: device int64 [B] */
+  int32_t part;             /* DENSE: 0 every visible entry; 1 only the visible entries
+                               complete within the first done_len[b] tokens of sequence b;
+                               2 only the visible entries completed after them.  Parts
+                               1 and 2 together give exactly the entries of part 0 (a
+                               decode step can attend to the entries that existed before
+                               it while it appends the new ones, and to those after) */
+  int32_t tiles_per_split;  /* > 0: split s takes the row's keys [32 t s, 32 t (s + 1)),
+                               t = tiles_per_split, whatever the other rows of the call
+                               (the last split also takes any keys beyond; for GATHER and
+                               TOPK n_split * 32 t >= k is required); 0: each row's keys
+                               are cut into n_split equal parts.  Applies to calls with
+                               few query rows per sequence; the row-tiled path (many
+                               rows per sequence) always cuts a block's key range into
+                               n_split parts */
 } lca_attn_source;
 
 int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
@@ -373,18 +389,55 @@ int lca_hybrid_attn_merge(const lca_attn_source* srcs, int n_src, const void* q,
                           void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode front: the work of a decode step that does not depend on the top-k
+ * selection, in one launch
+ *
+ * The same as
+ *     lca_csa_index_score_append(p, ..., dtype, stream)
+ *     lca_hybrid_attn(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps,
+ *                     dtype == LCA_F32 ? LCA_F32 : LCA_BF16, stream)
+ * with every argument as in those calls: the appends of the entries the
+ * newest tokens complete, the lightning-indexer scores (a TOPK source of
+ * lca_hybrid_attn or lca_csa_topk_select follows), and the attention over
+ * DENSE and WINDOW sources ("DeepSeek-V4", Design overview and Inference
+ * efficiency; "Why DeepSeek V4 Stands Apart", Core Architectural
+ * Innovations: the dense attention over the 128:1 entries and the window do
+ * not depend on the indexer).  On the bf16 matrix-core path (D = 512, H a
+ * multiple of 16, d_I = 64, one query row per sequence or a few sharing a
+ * score block) it is one launch whose attention blocks run beside the score
+ * blocks; elsewhere the two launches above.
+ *   srcs  DENSE or WINDOW sources only (LCA_ERR_INVALID_ARG otherwise); a
+ *         source over a cache that the appends write must be DENSE with
+ *         part = 1 and this call's done_len (the entries that existed
+ *         before the step), so that no block reads what another writes.
+ *         The entries the step completes are attended by a later call (a
+ *         DENSE source with part = 2).
+ * Errors as the two calls. */
+int lca_decode_front(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                     const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w, int64_t max_entries,
+                     const lca_compress_stream* idx_stream, const lca_compress_stream* kv_streams, int n_kv,
+                     const int64_t* tok_off, const int64_t* done_len, float eps, float* scores, void* ws,
+                     size_t ws_bytes, const lca_attn_source* srcs, int n_src, const void* q, int H, int D,
+                     float scale, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics (process-wide settings read by every later launch; not meant
  * for production use, and not synchronised with launches in flight)
  *
  * lca_diag_trace: when buf is not NULL, every later launch of the few-row
  * attention kernel (lca_hybrid_attn / lca_csa_sparse_attn / lca_hca_attn /
- * lca_swa_attn with few query rows per sequence) writes, for each block b
- * with 8*(b+1) <= n_words, 8 uint64 words at buf[8*b]: the 100 MHz constant
+ * lca_swa_attn with few query rows per sequence, and the attention blocks of
+ * lca_decode_front) writes, for each block b with 16*(b+1) <= n_words, 16
+ * uint64 words at buf[16*b]: the 100 MHz constant
  * clock (s_memrealtime) at 0 block start, 1 top-k filter done, 2 wait done,
  * 3 selection done, 4 prologue done, 5 key loop done, 6 partial stored (0 for
  * phases the block does not have), and word 7 = source kind (LCA_SRC_*) |
  * wait gave up << 2 | fallback selection << 3 | owns top-k slots << 4 | XCC
- * id << 8 | query row << 12 (20 bits) | the wave's HW_ID register << 32.  buf is a device pointer the caller keeps alive while
+ * id << 8 | query row << 12 (20 bits) | the wave's HW_ID register << 32;
+ * words 8-15 stamp the top-k steps of a TOPK block (8 histogram summed,
+ * 9 threshold found, 10 list space reserved, 11 own share counted, 12 lists
+ * loaded, 13 second-level threshold found, 14 cut found, 15 filter loads
+ * issued; 0 if not reached).  buf is a device pointer the caller keeps alive while
  * tracing; NULL turns tracing off.
  *
  * lca_diag_topk_wait: the top-k wait inside the attention launch (a TOPK

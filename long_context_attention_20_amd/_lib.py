@@ -28,7 +28,7 @@ EXPORTS = [
     "lca_csa_index_topk_workspace", "lca_csa_index_topk", "lca_csa_index_score", "lca_csa_index_score_append",
     "lca_csa_topk_select", "lca_csa_sparse_attn", "lca_hca_attn",
     "lca_swa_attn", "lca_hybrid_attn", "lca_swa_merge_workspace", "lca_swa_merge", "lca_hybrid_attn_merge",
-    "lca_diag_trace", "lca_diag_topk_wait",
+    "lca_diag_trace", "lca_diag_topk_wait", "lca_decode_front",
 ]
 LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_WINDOW, LCA_SRC_TOPK = 0, 1, 2, 3
 
@@ -53,6 +53,7 @@ class AttnSource(ctypes.Structure):
         ("n_split", ctypes.c_int32), ("o_part", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("max_entries", ctypes.c_int64),
         ("scores", ctypes.c_void_p), ("idx_out", ctypes.c_void_p),
+        ("done_len", ctypes.c_void_p), ("part", ctypes.c_int32), ("tiles_per_split", ctypes.c_int32),
     ]
 
 
@@ -104,6 +105,10 @@ def _load():
     L.lca_hybrid_attn_merge.restype = i32
     L.lca_hybrid_attn_merge.argtypes = [ctypes.POINTER(AttnSource), i32, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp,
                                         i32, vp]
+    L.lca_decode_front.restype = i32
+    L.lca_decode_front.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64,
+                                   ctypes.POINTER(CompressStream), ctypes.POINTER(CompressStream), i32, vp, vp, f32,
+                                   vp, vp, sz, ctypes.POINTER(AttnSource), i32, vp, i32, i32, f32, i32, vp]
     L.lca_diag_trace.restype = i32
     L.lca_diag_trace.argtypes = [vp, i64]
     L.lca_diag_topk_wait.restype = i32

@@ -52,6 +52,12 @@ static lca_attn_source make_source(int kind, const void* kv, const int64_t* off,
 int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, const float* win_lse,
                  const float* sink, int rows, int H, int D, void* out, int dtype, hipStream_t stream);
 void diag_set_trace(uint64_t* buf, int64_t words);
+int launch_decode_front(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                        const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
+                        const lca_compress_stream* idx_stream, const lca_compress_stream* kv_streams, int n_kv,
+                        const int64_t* tok_off, const int64_t* done_len, float eps, float* scores, void* ws,
+                        const lca_attn_source* srcs, int n_src, const void* q, int H, int D, float scale, int dtype,
+                        hipStream_t stream);
 void diag_set_topk_wait(uint32_t extra, uint32_t ticks);
 
 static bool sync_mode() {
@@ -213,12 +219,13 @@ int lca_csa_index_score(const void* p, const float* omega, const void* ikey, con
                 st, "csa_index_score");
 }
 
-int lca_csa_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
-                               const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
-                               int64_t max_entries, const lca_compress_stream* idx_stream,
-                               const lca_compress_stream* kv_streams, int n_kv, const int64_t* tok_off,
-                               const int64_t* done_len, float eps, float* scores, void* ws, size_t ws_bytes,
-                               int dtype, void* stream) {
+}  // extern "C"
+
+static int check_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                              const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
+                              int64_t max_entries, const lca_compress_stream* idx_stream,
+                              const lca_compress_stream* kv_streams, int n_kv, const int64_t* tok_off,
+                              const int64_t* done_len, float eps, void* ws, size_t ws_bytes, int dtype) {
   int rc = check_index("csa_index_score_append", true, p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w,
                        max_entries, ws, ws_bytes, dtype);
   if (rc != LCA_OK) return rc;
@@ -241,6 +248,19 @@ int lca_csa_index_score_append(const void* p, const float* omega, const void* ik
     LCA_REQUIRE(kv_streams[i].out_key == 0, LCA_ERR_INVALID_ARG, "csa_index_score_append: kv stream %d writes key rows", i);
   rc = check_streams(idx_stream, 1, in_dtype);
   if (rc == LCA_OK && n_kv > 0) rc = check_streams(kv_streams, n_kv, in_dtype);
+  return rc;
+}
+
+extern "C" {
+
+int lca_csa_index_score_append(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                               const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
+                               int64_t max_entries, const lca_compress_stream* idx_stream,
+                               const lca_compress_stream* kv_streams, int n_kv, const int64_t* tok_off,
+                               const int64_t* done_len, float eps, float* scores, void* ws, size_t ws_bytes,
+                               int dtype, void* stream) {
+  const int rc = check_score_append(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries,
+                                    idx_stream, kv_streams, n_kv, tok_off, done_len, eps, ws, ws_bytes, dtype);
   if (rc != LCA_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return finish(launch_index_score_append(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries,
@@ -357,6 +377,15 @@ static int check_hybrid(const lca_attn_source* srcs, int n_src, const void* q, c
       LCA_REQUIRE(x.m2 >= 1 && x.w2 >= 1, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: m2=%d w2=%d", i, x.m2, x.w2);
     if (x.kind == LCA_SRC_WINDOW)
       LCA_REQUIRE(x.W >= 1, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: W=%d must be >= 1", i, x.W);
+    LCA_REQUIRE(x.part >= 0 && x.part <= 2 && (x.part == 0 || (x.kind == LCA_SRC_DENSE && x.done_len != nullptr)),
+                LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: part=%d (dense sources only, with done_len)", i,
+                x.part);
+    LCA_REQUIRE(x.tiles_per_split >= 0, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: tiles_per_split=%d < 0", i,
+                x.tiles_per_split);
+    if (x.tiles_per_split > 0 && (x.kind == LCA_SRC_GATHER || x.kind == LCA_SRC_TOPK))
+      LCA_REQUIRE((int64_t)x.n_split * x.tiles_per_split * 32 >= x.k, LCA_ERR_INVALID_ARG,
+                  "hybrid_attn: source %d: n_split=%d x tiles_per_split=%d x 32 < k=%d", i, x.n_split,
+                  x.tiles_per_split, x.k);
     need_pos = need_pos || x.kind != LCA_SRC_GATHER;
   }
   LCA_REQUIRE(!need_pos || q_pos != nullptr, LCA_ERR_INVALID_ARG, "hybrid_attn: q_pos is NULL");
@@ -387,6 +416,36 @@ int lca_hybrid_attn_merge(const lca_attn_source* srcs, int n_src, const void* q,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return finish(launch_attention_merge(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, sink, out, dtype, st), st,
                 "hybrid_attn_merge");
+}
+
+int lca_decode_front(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                     const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w, int64_t max_entries,
+                     const lca_compress_stream* idx_stream, const lca_compress_stream* kv_streams, int n_kv,
+                     const int64_t* tok_off, const int64_t* done_len, float eps, float* scores, void* ws,
+                     size_t ws_bytes, const lca_attn_source* srcs, int n_src, const void* q, int H, int D,
+                     float scale, int dtype, void* stream) {
+  int rc = check_score_append(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries, idx_stream,
+                              kv_streams, n_kv, tok_off, done_len, eps, ws, ws_bytes, dtype);
+  if (rc != LCA_OK) return rc;
+  const int adt = dtype == LCA_F32 ? LCA_F32 : LCA_BF16;
+  rc = check_hybrid(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, adt);
+  if (rc != LCA_OK) return rc;
+  for (int i = 0; i < n_src; ++i) {
+    const lca_attn_source& x = srcs[i];
+    LCA_REQUIRE(x.kind == LCA_SRC_DENSE || x.kind == LCA_SRC_WINDOW, LCA_ERR_INVALID_ARG,
+                "decode_front: source %d: only DENSE and WINDOW sources run beside the scores", i);
+    // a source must not read entries the appends of the same launch write
+    bool written = x.kv == idx_stream->out;
+    for (int j = 0; j < n_kv; ++j) written = written || x.kv == kv_streams[j].out;
+    LCA_REQUIRE(!written || (x.kind == LCA_SRC_DENSE && x.part == 1 && x.done_len == done_len), LCA_ERR_INVALID_ARG,
+                "decode_front: source %d reads a cache the appends write: it must be DENSE with part = 1 and the "
+                "call's done_len", i);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_decode_front(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries,
+                                    idx_stream, kv_streams, n_kv, tok_off, done_len, eps, scores, ws, srcs, n_src, q,
+                                    H, D, scale, dtype, st),
+                st, "decode_front");
 }
 
 size_t lca_swa_merge_workspace(int n_rows, int H, int D) {

@@ -140,6 +140,11 @@ __device__ __forceinline__ void filter_prefetch(const TopkWs& w, int r, int cb0,
   }
 }
 
+// A diagnostic hook (sub-phase stamps) that does nothing.
+struct NoStamp {
+  __device__ void operator()(int) const {}
+};
+
 // The filter of NC chunks of row r (k < nv; the first chunk starts below
 // nv) from their prefetched loads: the threshold bin T from the row's
 // histogram (summed over its stripes), then every entry of the chunks above T
@@ -147,10 +152,12 @@ __device__ __forceinline__ void filter_prefetch(const TopkWs& w, int r, int cb0,
 // above).  The list space comes from one 64-bit atomic on ctr for all the
 // chunks.  No per-candidate counting here: with many equal scores (a row
 // whose head weights are all negative scores thousands of entries exactly 0)
-// per-candidate atomics would all hit one word.
-template <int NT, int PER, int NC>
+// per-candidate atomics would all hit one word.  (stamp: a diagnostic hook
+// called with sub-phase numbers.)
+
+template <int NT, int PER, int NC, class Stamp = NoStamp>
 __device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb0, int stride,
-                             const FilterPrefetch<NT, PER, NC>& P, FilterShared& F) {
+                             const FilterPrefetch<NT, PER, NC>& P, FilterShared& F, Stamp stamp = Stamp()) {
   using FP = FilterPrefetch<NT, PER, NC>;
 #pragma unroll
   for (int i = 0; i < FP::HV; ++i) {
@@ -162,8 +169,10 @@ __device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb0, int st
     reinterpret_cast<uint4*>(F.h)[threadIdx.x + i * NT] = v;
   }
   __syncthreads();
+  stamp(8);
   find_threshold(F.h, kHistBins, (uint32_t)w.k, F.sm, &F.T, &F.above, &F.cnt);
   const uint32_t T = (uint32_t)F.T;
+  stamp(9);
 
   uint32_t keys[NC][PER];
   uint32_t ns = 0, nc = 0;
@@ -184,6 +193,7 @@ __device__ void filter_chunk(const TopkWs& w, int r, int64_t nv, int cb0, int st
   if (threadIdx.x == 0)
     F.base = atomicAdd(&w.ctr[r], (unsigned long long)(tot & 0xFFFFu) | ((unsigned long long)(tot >> 16) << 32));
   __syncthreads();
+  stamp(10);
   uint32_t ps = (uint32_t)(F.base & 0xFFFFFFFFull) + (pos & 0xFFFFu);
   uint32_t pc = (uint32_t)(F.base >> 32) + (pos >> 16);
   int32_t* selr = w.sel + (int64_t)r * w.k;
@@ -387,9 +397,9 @@ __device__ void topk_row_scan_select(const float* S, int64_t nv, uint32_t k, uin
   }
 }
 
-template <int NT, bool ORDERED, class Emit>
+template <int NT, bool ORDERED, class Emit, class Stamp = NoStamp>
 __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch<NT>& P, SelectLds& L,
-                                    SelectShared& S, Emit emit, uint64_t* cl, uint32_t ncl) {
+                                    SelectShared& S, Emit emit, uint64_t* cl, uint32_t ncl, Stamp stamp = Stamp()) {
   constexpr int NW = NT / 64;
   constexpr int SPT = SelectPrefetch<NT>::SPT, CPT = SelectPrefetch<NT>::CPT;
   constexpr int HPT = kH2Bins / NT;  // second-level bins per thread
@@ -434,6 +444,7 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
   if (ORDERED)
     for (int i = tid; i < kBitmapWords; i += NT) L.bitmap[i] = 0;
   __syncthreads();
+  stamp(12);
   for_cands_staging([&](uint64_t v) { lds_count(L.h, (uint32_t)(v >> 34) & (uint32_t)(kH2Bins - 1)); });
   if (ORDERED) {
     // the selected list is chosen whole
@@ -474,6 +485,7 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
     }
   }
   __syncthreads();
+  stamp(13);
   const uint32_t T2 = (uint32_t)S.T;
   const uint32_t need2 = need - S.above, cnt2 = S.cnt;
 
@@ -542,6 +554,7 @@ __device__ uint32_t topk_row_select(const TopkWs& w, int r, const SelectPrefetch
 
   // 3. the chosen candidates into the bitmap, the chosen entries before
   // each bitmap word, then every chosen entry's rank in ascending order
+  stamp(14);
   for_cands([&](uint64_t v) {
     if (v >= vstar) {
       const uint32_t e = 0xFFFFFFu - (uint32_t)(v & 0xFFFFFFu);

@@ -172,6 +172,38 @@ def csa_index_score_append(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: in
           "csa_index_score_append")
 
 
+def decode_front(p, omega, ikey, csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws: torch.Tensor,
+                 idx_stream: dict, kv_streams: Sequence[dict], tok_off: torch.Tensor, done_len: torch.Tensor,
+                 q, sources: Sequence[dict], scale: float, eps: float = 1e-6,
+                 scores: Optional[torch.Tensor] = None):
+    """csa_index_score_append followed by hybrid_attn(q, q_pos, sources), in
+    one launch where it applies: the appends, the index scores and the
+    attention over dense / window sources (a dense source over a cache the
+    appends write takes part 1 with this done_len).  Returns the sources'
+    (o_part, lse) pairs."""
+    _dev(p, omega, ikey, csa_off, q_pos, ws, scores, tok_off, done_len, q)
+    _i64(tok_off, "tok_off")
+    _i64(done_len, "done_len")
+    B = csa_off.numel() - 1
+    rows = q_pos.numel()
+    if rows % B:
+        raise ValueError("q_pos must hold the same number of rows for every sequence")
+    if len(kv_streams) > 4:
+        raise ValueError("0..4 kv streams per call")
+    ia, _ = _stream_array([idx_stream])
+    ka, _ = _stream_array(kv_streams)
+    arr, outs, Bs = _attn_sources(q, q_pos, sources)
+    if Bs != B:
+        raise ValueError("the sources and the caches must hold the same sequences")
+    _, H, D = q.shape
+    check(lib.lca_decode_front(_ptr(p), _ptr(omega), _ptr(ikey), _ptr(csa_off), _ptr(q_pos), B, rows // B,
+                               p.shape[-2], p.shape[-1], k, m, w, int(max_entries), ia, ka, len(kv_streams),
+                               _ptr(tok_off), _ptr(done_len), float(eps), _ptr(scores), _ptr(ws),
+                               ws.numel() * ws.element_size(), arr, len(sources), _ptr(q), H, D, float(scale),
+                               _index_dtype(p, ikey), _stream()), "decode_front")
+    return outs
+
+
 def csa_topk_select(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws: torch.Tensor,
                     idx: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None):
     """Second half of csa_index_topk: exact top-k from the scored workspace."""
@@ -282,9 +314,14 @@ def _attn_sources(q, q_pos, sources: Sequence[dict]):
         ns = int(s["n_split"])
         o_part, lse = _parts_out(rows, H, D, ns, q.device, s.get("o_part"), s.get("lse"))
         _dev(o_part, lse)
+        done_len, part = s.get("done_len"), int(s.get("part", 0))
+        if part:
+            _dev(done_len)
+            _i64(done_len, "done_len")
         arr[i] = AttnSource(kind, kv.data_ptr(), off.data_ptr(), None if idx is None else idx.data_ptr(), k,
                             int(s.get("m2", 1)), int(s.get("w2", 1)), int(s.get("W", 0)), ns, o_part.data_ptr(),
-                            lse.data_ptr(), _addr(ws), ws_bytes or 0, max_entries or 0, _addr(scores), _addr(idx_out))
+                            lse.data_ptr(), _addr(ws), ws_bytes or 0, max_entries or 0, _addr(scores), _addr(idx_out),
+                            _addr(done_len) if part else None, part, int(s.get("tiles_per_split", 0)))
         outs.append((o_part, lse))
     return arr, outs, B
 
@@ -292,7 +329,10 @@ def _attn_sources(q, q_pos, sources: Sequence[dict]):
 def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
     """The attention branches of a step in one launch.  sources: dicts with
     kind ("gather", "dense", "window" or "topk"), kv, off and n_split, plus
-    idx (gather), m2 and w2 (dense), W (window), and optionally o_part / lse.
+    idx (gather), m2 and w2 (dense), W (window), and optionally o_part / lse,
+    tiles_per_split (a fixed partition of each row's keys) and, for a dense
+    source, part (1: the entries complete within the first done_len[b]
+    tokens; 2: those completed after them) with done_len (int64 [B]).
     A "topk" source selects the sparse branch's entries from the scores a
     csa_index_score(_append) call left in its workspace: it takes k, m2 = m,
     w2 = w, max_entries, ws, idx_out (int32 [rows, k], written) and

@@ -5,16 +5,18 @@ strides and windows), the caller's caches as device tensors with their host
 and device offsets, and reusable workspaces.  It only sizes buffers and
 sequences the C entry points; every step runs in the HIP kernels.
 
-Decode step (one query row per sequence), three calls on one stream:
-    csa_index_score_append  the CSA, indexer-key and HCA entries the new token
-                            completes, and the index scores (one launch)
-    hybrid_attn             exact top-k (every sparse block filters a share of
-                            the scores, then selects its share of the ascending
-                            list), CSA sparse + HCA dense + window partials
-                            (one launch when it fits the device at once)
-    swa_merge               sink + merge of every partial
-Prefill chunks (several rows per sequence) run kv_compress and
-csa_index_score as separate launches.
+Decode step (one query row per sequence, or a few), three calls on one stream:
+    decode_front  the CSA, indexer-key and HCA entries the new token
+                  completes, the index scores, and the attention over the HCA
+                  entries that existed before the step and over the window
+                  (one launch: the attention blocks run beside the score blocks)
+    hybrid_attn   exact top-k (every sparse block filters a share of the
+                  scores, then selects its share of the ascending list) and
+                  the sparse attention over it; the HCA entry the step
+                  completes, when it completes one
+    swa_merge     sink + merge of every partial
+Prefill chunks (many rows per sequence) run kv_compress, csa_index_score,
+csa_topk_select and hybrid_attn_merge.
 """
 from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
@@ -226,22 +228,54 @@ class HybridAttention:
             return out, dict(idx=idx, csa=csa, hca=hca)
         return out
 
+    def front_splits(self, rows: int, n_csa: int, n_hca: int, n_scores: int):
+        """Splits of the decode step in front / sparse form: the HCA source
+        runs beside the index scores (its blocks hold about half of the
+        compute units there, the score blocks the rest); the sparse launch
+        holds the sparse source alone, two 32-key tiles per block and enough
+        blocks that each filters its share of the row's n_scores scores in
+        one pass."""
+        hg = (self.H + 31) // 32
+        per_row = max(1, rows * hg)
+        t_hca = max(1, (n_hca + 31) // 32)
+        sh = max(1, min(t_hca // 4 if t_hca >= 4 else 1, 128 // per_row if per_row < 128 else 1, 256))
+        t_csa = max(1, (n_csa + 31) // 32)
+        sc = max(1, -(-t_csa // 2))
+        sc = max(sc, -(-n_scores // (self.FILTER_PASS_SCORES * hg)))
+        sc = max(1, min(sc, t_csa, 256 // per_row if per_row < 256 else 1))
+        return int(sc), int(sh), 1
+
     # -------------------------------------------------------------- whole step
-    def decode_buffers(self, rows: int, max_csa: int, max_hca: int, device, dtype):
+    def front_default(self, rows: int) -> bool:
+        """Whether a decode step takes the front form by default: never on
+        the measured workloads (Pro 1M, Pro varlen, Flash decode), where the
+        HCA blocks beside the sparse blocks hide under the selection chain,
+        while beside the score blocks they queue behind the key stream and
+        lengthen the score launch by more than they take off the other."""
+        return False
+
+    def decode_buffers(self, rows: int, max_csa: int, max_hca: int, device, dtype, front: Optional[bool] = None):
         """Preallocated outputs of decode_step (so that the step can be
-        captured in a HIP graph and replayed)."""
+        captured in a HIP graph and replayed).  front: the front / sparse
+        form of the step (decode_step then runs front_calls); None: the
+        default for `rows` (front_default)."""
+        if front is None:
+            front = self.front_default(rows)
         f32 = torch.float32
-        sc, sh, sw = self.fused_splits(rows, min(self.k, max(1, max_csa)), max_hca, self.W, select=True,
-                                       n_scores=max_csa)
+        if front:
+            sc, sh, sw = self.front_splits(rows, min(self.k, max(1, max_csa)), max_hca, max_csa)
+        else:
+            sc, sh, sw = self.fused_splits(rows, min(self.k, max(1, max_csa)), max_hca, self.W, select=True,
+                                           n_scores=max_csa)
         sc = self.split_csa or sc
         sh = self.split_hca or sh
         part = lambda n: (torch.empty((n, rows, self.H, self.D), dtype=f32, device=device),
                           torch.empty((n, rows, self.H), dtype=f32, device=device))
         return dict(
-            sc=sc, sh=sh, sw=sw, max_csa=max(1, max_csa), max_hca=max_hca,
+            sc=sc, sh=sh, sw=sw, max_csa=max(1, max_csa), max_hca=max_hca, front=front,
             ws_idx=self.index_workspace(rows, max(1, max_csa), device),
             idx=torch.empty((rows, self.k), dtype=torch.int32, device=device),
-            csa=part(sc), hca=part(sh), swa=part(sw),
+            csa=part(sc), hca=part(sh), swa=part(sw), hca_new=part(1),
             out=torch.empty((rows, self.H, self.D), dtype=dtype, device=device))
 
     def attn_sources(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, idx: Optional[torch.Tensor],
@@ -264,6 +298,53 @@ class HybridAttention:
                             lse=bufs["swa"][1]))
         return src
 
+    def front_calls(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos, bufs: dict,
+                    done_len: torch.Tensor, done_h: Sequence[int], lens_h: Optional[Sequence[int]] = None):
+        """The decode step as three launches, returned as three callables (so
+        that each can be timed on its own): decode_front (the appends of the
+        entries the new tokens complete, the index scores, and the attention
+        over the HCA entries that existed before the step and over the
+        window), hybrid_attn (the exact top-k inside the sparse blocks, and
+        the HCA entries the step completes, if any), swa_merge (every partial
+        and the sink into bufs["out"])."""
+        lens = caches.lens if lens_h is None else lens_h
+        streams = self.compress_streams(caches, raw, done_h, lens_h=lens_h)
+        idx_st = [st for st in streams if st["out"] is caches.ikey]
+        kv_st = [st for st in streams if st["out"] is not caches.ikey]
+        if not idx_st:  # no new indexer key: the stream appends nothing
+            idx_st = [dict(src=raw["u"], logits=raw["c"], out=caches.ikey, ent_off=caches.csa_off, m=self.m,
+                           w=self.w, rmsnorm=0, max_entries=0, key=self.ikey_code)]
+        front, parts = [], [bufs["csa"]]
+        if bufs["max_hca"] > 0:
+            front.append(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2,
+                              part=1, done_len=done_len, n_split=bufs["sh"], o_part=bufs["hca"][0],
+                              lse=bufs["hca"][1]))
+            parts.append(bufs["hca"])
+        if self.W > 0:
+            front.append(dict(kind="window", kv=raw["x"], off=tok_off, W=self.W, n_split=bufs["sw"],
+                              o_part=bufs["swa"][0], lse=bufs["swa"][1]))
+            parts.append(bufs["swa"])
+        back = [dict(kind="topk", kv=caches.kv_csa, off=caches.csa_off, k=self.k, m2=self.m, w2=self.w,
+                     max_entries=bufs["max_csa"], ws=bufs["ws_idx"], idx_out=bufs["idx"], n_split=bufs["sc"],
+                     o_part=bufs["csa"][0], lse=bufs["csa"][1])]
+        if bufs["max_hca"] > 0 and any(n_windows(L, self.m2, self.w2) > n_windows(d, self.m2, self.w2)
+                                       for L, d in zip(lens, done_h)):
+            back.append(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2, part=2,
+                             done_len=done_len, n_split=1, o_part=bufs["hca_new"][0], lse=bufs["hca_new"][1]))
+            parts.append(bufs["hca_new"])
+        if not front:  # nothing to attend beside the scores
+            f0 = lambda: ops.csa_index_score_append(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m,  # noqa: E731
+                                                    self.w, bufs["max_csa"], bufs["ws_idx"], idx_st[0], kv_st,
+                                                    tok_off, done_len, self.eps)
+        else:
+            f0 = lambda: ops.decode_front(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m, self.w,  # noqa: E731
+                                          bufs["max_csa"], bufs["ws_idx"], idx_st[0], kv_st, tok_off, done_len, q,
+                                          front, self.scale, self.eps)
+        return [f0,
+                lambda: ops.hybrid_attn(q, q_pos, back, self.scale, self.eps),
+                lambda: ops.swa_merge(q, None, None, None, sigma, parts, 0, self.scale, self.eps, None,
+                                      out=bufs["out"])]
+
     def decode_step(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos,
                     bufs: dict, done_len: Optional[torch.Tensor] = None, done_h: Optional[Sequence[int]] = None,
                     side: Optional["torch.cuda.Stream"] = None, lens_h: Optional[Sequence[int]] = None,
@@ -278,7 +359,16 @@ class HybridAttention:
         host copy of the sequence lengths tok_off describes, when they are
         shorter than the caches'.  fuse_topk: the top-k selection runs
         inside the attention call (a TOPK source) rather than as
-        csa_topk_select."""
+        csa_topk_select.  Buffers from decode_buffers(front=True) with
+        done_len, one query row or a few per sequence, no side stream and
+        the fused top-k: the three-launch front form (front_calls)."""
+        rows_per_seq = q.shape[0] // len(caches.lens)
+        if (bufs.get("front") and done_len is not None and side is None and fuse_topk and
+                (rows_per_seq == 1 or (rows_per_seq <= 4 and rows_per_seq * self.HI <= 16))):
+            for f in self.front_calls(caches, raw, tok_off, q, p, omega, sigma, q_pos, bufs, done_len, done_h,
+                                      lens_h):
+                f()
+            return bufs["out"]
         main = torch.cuda.current_stream()
         join = None
         scored = False

@@ -24,7 +24,7 @@ from gpu_util import layer_for, tdtype, to_device
 
 pytestmark = pytest.mark.gpu
 
-TRACE_WORDS = 8
+TRACE_WORDS = 16
 GAVE_UP, FALLBACK, OWNS = 1 << 2, 1 << 3, 1 << 4
 
 
