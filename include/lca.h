@@ -172,6 +172,24 @@ int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, cons
                        int64_t max_entries, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
                        int dtype, void* stream);
 
+/* lca_csa_index_topk for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without the workspace, which is a static device array of the
+ * library (lca_csa_index_topk_noalloc_max_bytes() bytes, 8 MiB; each GPU the
+ * library runs on holds its own copy until the process ends).  The call
+ * allocates nothing.  A call whose workspace (lca_csa_index_topk_workspace of
+ * the same arguments) exceeds that size returns LCA_ERR_WORKSPACE and
+ * launches nothing.  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from different threads) race
+ * and must not be issued.  The array keeps the last call's contents; the
+ * first call on a device, and every call whose (B*Tq, max_entries, k)
+ * differs from the previous call's on that device, first clears it with a
+ * fill kernel on `stream`.  Results are those of lca_csa_index_topk. */
+size_t lca_csa_index_topk_noalloc_max_bytes(void);
+int lca_csa_index_topk_noalloc(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                               const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
+                               int64_t max_entries, int32_t* idx, float* scores, int dtype, void* stream);
+
 /* The two halves of lca_csa_index_topk, same arguments and workspace:
  * lca_csa_index_score writes the scores and the selection histogram into the
  * workspace (and the scores into `scores` when it is not NULL);

@@ -29,6 +29,7 @@ EXPORTS = [
     "lca_csa_topk_select", "lca_csa_sparse_attn", "lca_hca_attn",
     "lca_swa_attn", "lca_hybrid_attn", "lca_swa_merge_workspace", "lca_swa_merge", "lca_hybrid_attn_merge",
     "lca_diag_trace", "lca_diag_topk_wait", "lca_decode_front",
+    "lca_csa_index_topk_noalloc_max_bytes", "lca_csa_index_topk_noalloc",
 ]
 LCA_SRC_DENSE, LCA_SRC_GATHER, LCA_SRC_WINDOW, LCA_SRC_TOPK = 0, 1, 2, 3
 
@@ -109,6 +110,11 @@ def _load():
     L.lca_decode_front.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64,
                                    ctypes.POINTER(CompressStream), ctypes.POINTER(CompressStream), i32, vp, vp, f32,
                                    vp, vp, sz, ctypes.POINTER(AttnSource), i32, vp, i32, i32, f32, i32, vp]
+    L.lca_csa_index_topk_noalloc_max_bytes.restype = sz
+    L.lca_csa_index_topk_noalloc_max_bytes.argtypes = []
+    L.lca_csa_index_topk_noalloc.restype = i32
+    L.lca_csa_index_topk_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, vp, vp,
+                                             i32, vp]
     L.lca_diag_trace.restype = i32
     L.lca_diag_trace.argtypes = [vp, i64]
     L.lca_diag_topk_wait.restype = i32

@@ -52,6 +52,10 @@ static lca_attn_source make_source(int kind, const void* kv, const int64_t* off,
 int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, const float* win_lse,
                  const float* sink, int rows, int H, int D, void* out, int dtype, hipStream_t stream);
 void diag_set_trace(uint64_t* buf, int64_t words);
+size_t index_noalloc_max_bytes();
+int launch_index_topk_noalloc(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                              const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w,
+                              int64_t maxN, int32_t* idx, float* scores, int dtype, hipStream_t stream);
 int launch_decode_front(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
                         const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
                         const lca_compress_stream* idx_stream, const lca_compress_stream* kv_streams, int n_kv,
@@ -290,6 +294,23 @@ int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, cons
                                ws_bytes, dtype, stream);
   if (rc != LCA_OK) return rc;
   return lca_csa_topk_select(csa_off, q_pos, B, Tq, k, m, w, max_entries, idx, scores, ws, ws_bytes, stream);
+}
+
+size_t lca_csa_index_topk_noalloc_max_bytes(void) { return index_noalloc_max_bytes(); }
+
+int lca_csa_index_topk_noalloc(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                               const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int k, int m, int w,
+                               int64_t max_entries, int32_t* idx, float* scores, int dtype, void* stream) {
+  LCA_REQUIRE(idx != nullptr, LCA_ERR_INVALID_ARG, "csa_index_topk_noalloc: idx is NULL");
+  // the argument checks of lca_csa_index_topk, with a workspace that always fits them
+  static char ws_standin;
+  int rc = check_index("csa_index_topk_noalloc", true, p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w,
+                       max_entries, &ws_standin, (size_t)-1, dtype);
+  if (rc != LCA_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return finish(launch_index_topk_noalloc(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries, idx,
+                                          scores, dtype, st),
+                st, "csa_index_topk_noalloc");
 }
 
 static int check_attn(const char* what, const void* q, const void* kv, const void* off, const void* lst,

@@ -29,6 +29,9 @@
 // the next call.  (The sparse-attention kernel can run the same selection in
 // its own blocks instead.)  The score kernels zero the counters.
 
+#include <algorithm>
+#include <mutex>
+
 #include "lca_score.h"
 
 namespace lca {
@@ -771,6 +774,76 @@ int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int 
   hipLaunchKernelGGL(topk_filter, dim3((unsigned)nblk, (unsigned)(B * Tq)), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(topk_finalize, dim3((unsigned)(B * Tq)), dim3(kFinThreads), 0, stream, a);
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ no allocation
+// The index workspace of lca_csa_index_topk_noalloc: a file-scope device
+// array (each GPU the library runs on holds its own copy until the process
+// ends).  Host code never passes the array's name to a kernel: its device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+size_t index_noalloc_max_bytes() { return kScratchBytes; }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];          // device address of scratch, per device
+uint64_t g_scratch_layout[kMaxDevices];    // layout of the last call on the device (0: none)
+}  // namespace
+
+__global__ __launch_bounds__(256) void zero_words(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// lca_csa_index_topk with the workspace in `scratch`: the device's address of
+// the array is looked up at the first call on a device (with that device
+// current); the workspace is cleared by a fill kernel at the first call and
+// whenever the layout (rows, max_entries, k) differs from the last call's on
+// the device, since a call leaves zero only what its own layout needs.
+int launch_index_topk_noalloc(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                              const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w,
+                              int64_t maxN, int32_t* idx, float* scores, int dtype, hipStream_t stream) {
+  const int rows = B * Tq;
+  const size_t need = index_topk_workspace(rows, maxN, k);
+  if (need > kScratchBytes) {
+    set_error("csa_index_topk_noalloc: %zu workspace bytes needed, the static workspace holds %zu", need,
+              kScratchBytes);
+    return LCA_ERR_WORKSPACE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("csa_index_topk_noalloc: no current device (or more than %d devices)", kMaxDevices);
+    return LCA_ERR_HIP;
+  }
+  void* ws = nullptr;
+  bool clear = false;
+  const uint64_t layout = ((uint64_t)(uint32_t)rows << 40) ^ ((uint64_t)maxN << 13) ^ (uint64_t)(uint32_t)k ^ 1ull;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr) {
+        set_error("csa_index_topk_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        return LCA_ERR_HIP;
+      }
+      g_scratch_ptr[dev] = ptr;
+    }
+    ws = g_scratch_ptr[dev];
+    clear = g_scratch_layout[dev] != layout;
+    g_scratch_layout[dev] = layout;
+  }
+  if (clear) {
+    const int64_t words = (int64_t)((need + 3) / 4);
+    hipLaunchKernelGGL(zero_words, dim3((unsigned)std::min<int64_t>(1024, (words + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(ws), words);
+    if (hipPeekAtLastError() != hipSuccess) return LCA_ERR_HIP;
+  }
+  int rc = launch_index_score(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, scores, ws, dtype, stream);
+  if (rc != LCA_OK) return rc;
+  return launch_topk_select(csa_off, q_pos, B, Tq, k, m, w, maxN, idx, scores, ws, stream);
 }
 
 }  // namespace lca

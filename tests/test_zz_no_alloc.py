@@ -1,0 +1,97 @@
+"""GPU: lca_csa_index_topk_noalloc, the index-score + top-k call whose
+workspace is a static device array of the library (for callers that cannot
+allocate), against lca_csa_index_topk with a caller workspace, through the
+C-ABI: identical indices and scores on calls in a row (the second with a
+smaller input, the third back at the first's size), and the size limit."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import lca_inputs as li
+from oracle import compress as ocmp
+
+from gpu_util import layer_for, tdtype, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    from long_context_attention_20_amd import _lib
+    return _lib
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _setup(cfg):
+    raw = li.make_raw(cfg)
+    d = to_device(raw, cfg)
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", tdtype(cfg))
+    layer.compress(caches, d, d["tok_off"])
+    q_pos = d["q_pos"].reshape(-1).contiguous()
+    max_csa = max(1, ocmp.n_entries(int(q_pos.max().item()) + 1, cfg.m, cfg.w))
+    return d, caches, q_pos, max_csa
+
+
+def _run(cfg, d, caches, q_pos, max_csa, noalloc):
+    L = _lib()
+    rows = q_pos.numel()
+    B = caches.csa_off.numel() - 1
+    idx = torch.full((rows, cfg.k), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((rows, max_csa), float("nan"), dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = (_p(d["p"]), _p(d["omega"]), _p(caches.ikey), _p(caches.csa_off), _p(q_pos), B, rows // B, cfg.HI, cfg.dI,
+            cfg.k, cfg.m, cfg.w, max_csa)
+    if noalloc:
+        rc = L.lib.lca_csa_index_topk_noalloc(*args, _p(idx), _p(sc), L.LCA_BF16, stream)
+    else:
+        ws = torch.zeros(L.lib.lca_csa_index_topk_workspace(rows, max_csa, cfg.k), dtype=torch.uint8, device="cuda")
+        rc = L.lib.lca_csa_index_topk(*args, _p(idx), _p(sc), _p(ws), ws.numel(), L.LCA_BF16, stream)
+    L.check(rc, "csa_index_topk" + ("_noalloc" if noalloc else ""))
+    torch.cuda.synchronize()
+    return idx, sc
+
+
+def test_noalloc_equals_workspace_call():
+    big = li.small("noalloc_big", 141, (9000, 5003), H=16, D=64, k=1024, plant=32)
+    small = li.small("noalloc_small", 142, (3000, 1029, 517, 7), H=16, D=64, k=512)
+    L = _lib()
+    print(f"[noalloc] static workspace {L.lib.lca_csa_index_topk_noalloc_max_bytes()} bytes", flush=True)
+    for n, cfg in enumerate((big, small, big)):
+        d, caches, q_pos, max_csa = _setup(cfg)
+        need = L.lib.lca_csa_index_topk_workspace(q_pos.numel(), max_csa, cfg.k)
+        print(f"[noalloc] call {n}: {cfg.name} rows={q_pos.numel()} max_entries={max_csa} k={cfg.k} "
+              f"workspace={need} bytes", flush=True)
+        got_idx, got_sc = _run(cfg, d, caches, q_pos, max_csa, noalloc=True)
+        ref_idx, ref_sc = _run(cfg, d, caches, q_pos, max_csa, noalloc=False)
+        assert torch.equal(got_idx, ref_idx), f"call {n}: indices differ"
+        qp = q_pos.cpu().numpy()
+        gs, rs = got_sc.cpu().numpy(), ref_sc.cpu().numpy()
+        for r in range(q_pos.numel()):
+            b = r // cfg.tq
+            nv = min(ocmp.n_entries(int(qp[r]) + 1, cfg.m, cfg.w), ocmp.n_entries(cfg.lens[b], cfg.m, cfg.w))
+            assert np.array_equal(gs[r, :nv], rs[r, :nv]), f"call {n}: row {r} scores differ"
+        # a second call with the same layout (no clear in between) as well
+        again, _ = _run(cfg, d, caches, q_pos, max_csa, noalloc=True)
+        assert torch.equal(again, ref_idx), f"call {n}: repeated call differs"
+
+
+def test_noalloc_rejects_oversized():
+    L = _lib()
+    cap = L.lib.lca_csa_index_topk_noalloc_max_bytes()
+    big_n = 1 << 20
+    assert L.lib.lca_csa_index_topk_workspace(1, big_n, 512) > cap
+    cfg = li.small("noalloc_rej", 143, (3000,), H=16, D=64, k=512)
+    d, caches, q_pos, _ = _setup(cfg)
+    idx = torch.full((1, cfg.k), -7, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = L.lib.lca_csa_index_topk_noalloc(_p(d["p"]), _p(d["omega"]), _p(caches.ikey), _p(caches.csa_off), _p(q_pos),
+                                          1, 1, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, big_n, _p(idx), None,
+                                          L.LCA_BF16, stream)
+    assert rc == L.LCA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(idx == -7), "a rejected call launched work"
