@@ -63,6 +63,8 @@ class Config:
     eps: float = 1e-6
     logit_per_channel: bool = True
     ikey: str = "bf16"  # indexer-key cache: "bf16" (the workload dtype), "fp8" (E4M3 rows with a scale) or "mxfp4"
+    rope: int = 0       # rotated dims at the end of each head (0: no rotary embedding)
+    rope_base: float = 10000.0
 
     @property
     def scale(self) -> float:

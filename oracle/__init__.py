@@ -25,8 +25,9 @@ rest supports and states it in the module that uses it.  Modules:
 * ``indexer``   lightning-indexer scores + exact top-k         (csa_index_topk)
 * ``attention`` partial softmax attention, sink, LSE merge     (csa_sparse_attn,
                 hca_attn, swa_merge)
+* ``rope``      partial rotary position embedding (last 64 dims; -i on outputs)
 * ``pipeline``  the decode / prefill step composed from the above
 * ``dense``     a second, independent formulation (one masked softmax over every
                 candidate key) used to pin the first one on tiny inputs
 """
-from . import numerics, compress, indexer, attention, pipeline, dense  # noqa: F401
+from . import numerics, compress, indexer, rope, attention, pipeline, dense  # noqa: F401

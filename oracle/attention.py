@@ -19,16 +19,25 @@ import numpy as np
 
 from .compress import rmsnorm
 from .numerics import round_to
+from .rope import BASE, rotate
 
 
-def normalize_query(q, eps: float, dtype: str):
-    """q: [H, D] raw -> RMS-normalised per head, rounded to the KV type."""
-    return round_to(rmsnorm(q, eps), dtype)
+def normalize_query(q, eps: float, dtype: str, pos=None, rope: int = 0, base: float = BASE):
+    """q: [H, D] raw -> RMS-normalised per head (then, with rope > 0, turned
+    by the query position pos on its last rope dims), rounded to the KV type."""
+    qn = rmsnorm(q, eps)
+    if rope:
+        qn = rotate(qn, pos, rope, base)
+    return round_to(qn, dtype)
 
 
-def normalize_tokens(x, eps: float, dtype: str):
-    """Raw window tokens [n, D] -> RMS-normalised keys rounded to the KV type."""
-    return round_to(rmsnorm(x, eps), dtype)
+def normalize_tokens(x, eps: float, dtype: str, pos=None, rope: int = 0, base: float = BASE):
+    """Raw window tokens [n, D] -> RMS-normalised keys (with rope > 0, token
+    r turned by its position pos[r]), rounded to the KV type."""
+    xn = rmsnorm(x, eps)
+    if rope:
+        xn = rotate(xn, pos, rope, base)
+    return round_to(xn, dtype)
 
 
 def logits(qhat, keys, scale: float):

@@ -33,14 +33,33 @@ def _rms(v, eps):
     return [e * r for e in v]
 
 
-def _entries(src, z, m, w, norm, eps, per_channel):
+def _turn(v, pos, d_rope, base):
+    """Rotary embedding of one vector, pair by pair on its last d_rope dims:
+    (v[a], v[a+1]) -> (v[a] cos t - v[a+1] sin t, v[a] sin t + v[a+1] cos t)
+    with t = pos * base ** (-(a - lo) / d_rope), lo = len(v) - d_rope."""
+    if not d_rope:
+        return list(v)
+    n = len(v)
+    d = min(d_rope, n)
+    lo = n - d
+    out = list(v)
+    for a in range(lo, n, 2):
+        t = pos * base ** (-(a - lo) / d)
+        c, s = math.cos(t), math.sin(t)
+        out[a] = v[a] * c - v[a + 1] * s
+        out[a + 1] = v[a] * s + v[a + 1] * c
+    return out
+
+
+def _entries(src, z, m, w, norm, eps, per_channel, turn=None):
     L = len(src)
     C = len(src[0])
     out = []
     j = 0
     while j * m + w <= L:
         e = _pool(src[j * m:j * m + w], z[j * m:j * m + w], C, per_channel)
-        out.append(_rms(e, eps) if norm else e)
+        e = _rms(e, eps) if norm else e
+        out.append(turn(e, j * m + w - 1) if turn else e)
         j += 1
     return out
 
@@ -54,9 +73,11 @@ def query(x, a, g, u, c, q, p, omega, sigma, i, cfg):
     x = [list(map(float, r)) for r in x]
     pc = cfg.logit_per_channel
     rnd = lambda v: [float(t) for t in round_to(v, dt)]  # noqa: E731
-    kv_csa = [rnd(e) for e in _entries(x, a, cfg.m, cfg.w, True, eps, pc)]
+    dr, base = getattr(cfg, "rope", 0), getattr(cfg, "rope_base", 10000.0)
+    turn = (lambda v, pos: _turn(v, pos, dr, base)) if dr else None  # noqa: E731
+    kv_csa = [rnd(e) for e in _entries(x, a, cfg.m, cfg.w, True, eps, pc, turn)]
     ikey = [rnd(e) for e in _entries(u, c, cfg.m, cfg.w, False, eps, pc)]
-    kv_hca = [rnd(e) for e in _entries(x, g, cfg.m2, cfg.w2, True, eps, pc)]
+    kv_hca = [rnd(e) for e in _entries(x, g, cfg.m2, cfg.w2, True, eps, pc, turn)]
 
     # indexer over visible entries: window end j*m + w - 1 <= i
     cand = []
@@ -78,12 +99,14 @@ def query(x, a, g, u, c, q, p, omega, sigma, i, cfg):
         keys.append(e)
         mask.append(j * cfg.m2 + cfg.w2 - 1 <= i)
     for t in range(len(x)):
-        keys.append(rnd(_rms(x[t], eps)))
+        xn = _rms(x[t], eps)
+        keys.append(rnd(turn(xn, t) if turn else xn))
         mask.append(i - cfg.W + 1 <= t <= i)
 
     out = []
     for h in range(len(q)):
-        qh = rnd(_rms([float(v) for v in q[h]], eps))
+        qn = _rms([float(v) for v in q[h]], eps)
+        qh = rnd(turn(qn, i) if turn else qn)
         lg = []
         for key, on in zip(keys, mask):
             lg.append(cfg.scale * sum(qa * kb for qa, kb in zip(qh, key)) if on else -math.inf)
@@ -96,5 +119,6 @@ def query(x, a, g, u, c, q, p, omega, sigma, i, cfg):
             if e_w:
                 for d in range(len(row)):
                     row[d] += e_w * key[d]
-        out.append([v / den for v in row])
+        row = [v / den for v in row]
+        out.append(turn(row, -i) if turn else row)
     return out, chosen

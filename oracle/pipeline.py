@@ -30,6 +30,7 @@ from .compress import compress, n_entries, n_visible
 from . import quant
 from .indexer import scores, topk
 from .numerics import round_to
+from .rope import entry_positions, rotate
 
 
 @dataclass
@@ -48,10 +49,21 @@ def fp8_keys(cfg) -> bool:
     return getattr(cfg, "ikey", "bf16") == "fp8"
 
 
+def kv_entries(src, z, m, w, cfg, entries=None):
+    """RMS-normalised KV entries of one stream (with cfg.rope, entry j turned
+    by the position of its window's last token), rounded to the storage type."""
+    e = compress(src, z, m, w, True, cfg.eps, entries)
+    rope = getattr(cfg, "rope", 0)
+    if rope and len(e):
+        js = range(n_entries(src.shape[0], m, w)) if entries is None else entries
+        e = rotate(e, entry_positions(js, m, w), rope, cfg.rope_base)
+    return round_to(e, cfg.dtype)
+
+
 def build_seq_caches(x, a, g, u, c, cfg) -> SeqCaches:
     """Caches of one sequence from its raw streams (all float64 views).  With
     fp8 or MXFP4 indexer keys the key cache holds the rows they stand for."""
-    kv_csa = round_to(compress(x, a, cfg.m, cfg.w, True, cfg.eps), cfg.dtype)
+    kv_csa = kv_entries(x, a, cfg.m, cfg.w, cfg)
     pooled = compress(u, c, cfg.m, cfg.w, False, cfg.eps)
     kind = getattr(cfg, "ikey", "bf16")
     if kind == "fp8":
@@ -60,7 +72,7 @@ def build_seq_caches(x, a, g, u, c, cfg) -> SeqCaches:
         ikey = quant.dequantize_mx_rows(*quant.quantize_mx_rows(pooled))
     else:
         ikey = round_to(pooled, cfg.dtype)
-    kv_hca = round_to(compress(x, g, cfg.m2, cfg.w2, True, cfg.eps), cfg.dtype)
+    kv_hca = kv_entries(x, g, cfg.m2, cfg.w2, cfg)
     return SeqCaches(kv_csa, ikey, kv_hca)
 
 
@@ -83,7 +95,17 @@ def select(ikey, p, omega, i, cfg):
 
 def window_keys(x_seq, i, cfg):
     lo = max(0, i - cfg.W + 1)
-    return att.normalize_tokens(x_seq[lo:i + 1], cfg.eps, cfg.dtype)
+    return att.normalize_tokens(x_seq[lo:i + 1], cfg.eps, cfg.dtype, pos=np.arange(lo, i + 1),
+                                rope=getattr(cfg, "rope", 0), base=getattr(cfg, "rope_base", 10000.0))
+
+
+def finish(o, i, cfg):
+    """The attention output of the query at position i: with cfg.rope turned
+    by -i (the values carry their own positions' rotation), then rounded."""
+    rope = getattr(cfg, "rope", 0)
+    if rope:
+        o = rotate(o, -i, rope, cfg.rope_base)
+    return round_to(o, cfg.dtype)
 
 
 def query_step(caches: SeqCaches, x_seq, q, p, omega, sigma, i, cfg, idx=None):
@@ -93,7 +115,8 @@ def query_step(caches: SeqCaches, x_seq, q, p, omega, sigma, i, cfg, idx=None):
     s, sel = select(caches.ikey, p, omega, i, cfg)
     if idx is None:
         idx = sel
-    qhat = att.normalize_query(q, cfg.eps, cfg.dtype)
+    qhat = att.normalize_query(q, cfg.eps, cfg.dtype, pos=i, rope=getattr(cfg, "rope", 0),
+                               base=getattr(cfg, "rope_base", 10000.0))
     idx = np.asarray(idx, dtype=np.int64)
     idx = idx[idx >= 0]
     csa = att.partial(qhat, caches.kv_csa[idx], cfg.scale)
@@ -104,8 +127,8 @@ def query_step(caches: SeqCaches, x_seq, q, p, omega, sigma, i, cfg, idx=None):
     o_csa, _ = att.merge([csa, swa], sigma)
     o_hca, _ = att.merge([hca, swa], sigma)
     return dict(scores=s, sel=sel, idx=idx, qhat=qhat, csa=csa, hca=hca, swa=swa,
-                out=round_to(o_a, cfg.dtype), out_raw=o_a, lse=lse_a,
-                out_csa=round_to(o_csa, cfg.dtype), out_hca=round_to(o_hca, cfg.dtype))
+                out=finish(o_a, i, cfg), out_raw=o_a, lse=lse_a,
+                out_csa=finish(o_csa, i, cfg), out_hca=finish(o_hca, i, cfg))
 
 
 def run(raw, cfg, caches: Optional[List[SeqCaches]] = None, queries=None):
@@ -127,5 +150,5 @@ def run(raw, cfg, caches: Optional[List[SeqCaches]] = None, queries=None):
     return caches, res
 
 
-__all__ = ["SeqCaches", "build_seq_caches", "build_caches", "select", "window_keys",
+__all__ = ["SeqCaches", "kv_entries", "build_seq_caches", "build_caches", "select", "window_keys", "finish",
            "query_step", "run", "n_entries", "n_visible"]

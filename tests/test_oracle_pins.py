@@ -532,3 +532,123 @@ def test_mx_scores_reduce_to_plain_scores_on_the_grid():
     p = rng.standard_normal((4, 64))
     om = np.array([0.5, -1.0, 2.0, 0.25])
     assert np.array_equal(idx.scores(p, om, quant.dequantize_mx_rows(q, s)), idx.scores(p, om, keys))
+
+
+# --------------------------------------------------------------------------
+# partial rotary embedding ("DeepSeek-V4", Core block and Provenance 16)
+# --------------------------------------------------------------------------
+
+from oracle import rope  # noqa: E402
+
+
+def test_rope_identity_lengths_and_untouched_dims():
+    rng = np.random.default_rng(30)
+    x = rng.standard_normal((5, 128))
+    assert np.array_equal(rope.rotate(x, 0, 64), x)          # position 0 turns by exp(0) = 1
+    y = rope.rotate(x, 12345, 64)
+    assert np.array_equal(y[:, :64], x[:, :64])                # the first D - 64 dims stay
+    pair = lambda v: v[:, 64::2] ** 2 + v[:, 65::2] ** 2     # noqa: E731
+    assert np.allclose(pair(y), pair(x), rtol=1e-13, atol=0)  # every pair keeps its length
+    # D <= 64: every dim rotates
+    z = rope.rotate(x[:, :64], 9, 64)
+    assert not np.allclose(z[:, :2], x[:, :2])
+
+
+def test_rope_closed_form_on_basis_vectors():
+    # the first rotated pair turns by pos radians (theta_0 = base**0 = 1), the
+    # last by pos * base**(-62/64); (1, 0) -> (cos t, sin t), (0, 1) -> (-sin t, cos t)
+    for pos in (1, 7, 1048575):
+        for a, t in ((64, float(pos)), (126, pos * 10000.0 ** (-62.0 / 64.0))):
+            e = np.zeros(128)
+            e[a] = 1.0
+            y = rope.rotate(e, pos, 64)
+            assert abs(y[a] - math.cos(t)) < 1e-9 and abs(y[a + 1] - math.sin(t)) < 1e-9
+            e = np.zeros(128)
+            e[a + 1] = 1.0
+            y = rope.rotate(e, pos, 64)
+            assert abs(y[a] + math.sin(t)) < 1e-9 and abs(y[a + 1] - math.cos(t)) < 1e-9
+            assert np.count_nonzero(y) == 2
+
+
+def test_rope_composes_and_inverts():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((4, 96))
+    for a, b in ((3, 5), (1000, -1000), (262143, 786432)):
+        assert np.allclose(rope.rotate(rope.rotate(x, a, 64), b, 64), rope.rotate(x, a + b, 64), atol=1e-9)
+    assert np.allclose(rope.rotate(rope.rotate(x, 777, 64), -777, 64), x, atol=1e-12)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(32)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    for d in (0, 3, 127, 5000):
+        vals = [rope.rotate(q, i, 64) @ rope.rotate(k, i - d, 64) for i in (d, d + 1, d + 977, 1048575)]
+        assert np.allclose(vals, vals[0], rtol=0, atol=1e-9)
+    assert abs(rope.rotate(q, 10, 64) @ rope.rotate(k, 0, 64) - rope.rotate(q, 11, 64) @ rope.rotate(k, 0, 64)) > 1e-6
+
+
+def test_rope_single_key_output_turns_back_to_the_key():
+    # one attended entry, no sink: the output is the stored (rotated) entry, and
+    # the -i turn of the output gives back the unrotated key when the entry
+    # sits at the query's position, or the key turned by their distance
+    rng = np.random.default_rng(33)
+    D, H = 64, 3
+    key = cmp.rmsnorm(rng.standard_normal(D), 1e-6)
+    cfg = li.TINY.with_(D=D, H=H, rope=64)
+    qhat = rng.standard_normal((H, D))
+    for i, j in ((500, 500), (500, 380)):
+        stored = rope.rotate(key, j, 64)
+        o, _, _ = att.attend(qhat, stored[None], cfg.scale, sigma=np.full(H, -np.inf))
+        got = pipeline.finish(o, i, cfg)
+        want = rope.rotate(key, j - i, 64)
+        assert np.allclose(got, np.repeat(want[None], H, axis=0), atol=1e-6)
+    assert np.allclose(pipeline.finish(np.repeat(rope.rotate(key, 500, 64)[None], H, 0), 500, cfg), key, atol=1e-6)
+
+
+def test_rope_window_one_reduces_to_rotary_causal_attention():
+    """m = w = 1 (one token per entry), k >= N, no sink, the CSA branch alone
+    with rope: textbook rotary causal attention, the query turned by i, token j
+    (key and value) by j, the output turned back by -i (torch SDPA)."""
+    rng = np.random.default_rng(34)
+    L, H, D = 29, 3, 16
+    x = numerics.round_bf16(rng.standard_normal((L, D)))
+    z = rng.standard_normal((L, D))
+    q = rng.standard_normal((H, D))
+    eps = 1e-6
+    cfg = li.TINY.with_(D=D, H=H, dtype="f32", rope=8, m=1, w=1)
+    ent = pipeline.kv_entries(x, z, 1, 1, cfg)                  # rotated by their positions j
+    for i in (0, 6, L - 1):
+        qhat = att.normalize_query(q, eps, "f32", pos=i, rope=8)
+        o, _ = att.partial(qhat, ent[:i + 1], cfg.scale)
+        got = pipeline.finish(o, i, cfg)
+        # textbook: pooling with w = 1 is the token itself
+        kr = np.stack([rope.rotate(cmp.rmsnorm(x[j], eps), j, 8) for j in range(i + 1)])
+        qr = rope.rotate(cmp.rmsnorm(q, eps), i, 8)
+        o_ref = rope.rotate(_sdpa(qr, kr, cfg.scale), -i, 8)
+        assert np.allclose(got, numerics.round_f32(o_ref), rtol=0, atol=2e-6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gather_oracle_equals_dense_bruteforce_with_rope(dtype):
+    cfg = _tiny_cfg(dtype, rope=4)
+    raw = li.make_raw(cfg)
+    caches, _ = pipeline.run(raw, cfg)
+    off = raw["tok_off"]
+    for b in range(cfg.B):
+        L = cfg.lens[b]
+        sl = lambda k: pipeline.seq_slice(raw[k], off, b)  # noqa: E731
+        for i in (L - 1, L - 9, 20, 7, 0):
+            r = pipeline.query_step(caches[b], sl("x"), raw["q"][b], raw["p"][b], raw["omega"][b],
+                                    raw["sigma"], i, cfg)
+            od, chosen = dense.query(sl("x"), sl("a"), sl("g"), sl("u"), sl("c"), raw["q"][b],
+                                     raw["p"][b], raw["omega"][b], raw["sigma"], i, cfg)
+            assert set(int(j) for j in r["sel"]) == chosen
+            turned = rope.rotate(r["out_raw"], -i, cfg.rope)
+            assert np.allclose(turned, np.array(od), rtol=0, atol=1e-12 if dtype == "f32" else 1e-2)
+            # rotation changes the output (the pins can see a missing turn)
+            plain = pipeline.query_step(pipeline.build_seq_caches(sl("x"), sl("a"), sl("g"), sl("u"), sl("c"),
+                                                                  cfg.with_(rope=0)),
+                                        sl("x"), raw["q"][b], raw["p"][b], raw["omega"][b], raw["sigma"], i,
+                                        cfg.with_(rope=0))
+            if i > 0:
+                assert np.max(np.abs(plain["out"] - r["out"])) > 1e-3
