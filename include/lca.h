@@ -117,6 +117,15 @@ typedef struct lca_compress_stream {
                           /* LCA_BF16_FP8KEY), 2: MXFP4 key rows (LCA_BF16_MXFP4KEY):  */
                           /* bf16 input, C <= 512 (MXFP4: C in {32,64,128,256}),       */
                           /* w = m or w = 2m <= 16                                      */
+  int32_t rope_dims;      /* 0, or the rotary embedding of each entry ("DeepSeek-V4",  */
+                          /* Core block and Provenance 16: partial RoPE on the last   */
+                          /* 64 dims): after the norm, the last rope_dims channels    */
+                          /* (even, <= C) turn pair by pair, pair p (channels         */
+                          /* C - rope_dims + 2p, +1) as a complex number times        */
+                          /* exp(i pos theta_p), theta_p = rope_base^(-2p/rope_dims), */
+                          /* pos = j*m + w - 1 (the last token of entry j's window);  */
+                          /* rows of the input type only (out_key = 0)                 */
+  float rope_base;        /* > 0 when rope_dims > 0 (10000 in the benchmark layers)    */
 } lca_compress_stream;
 
 /* Compress up to 4 streams in one launch.
@@ -358,6 +367,16 @@ typedef struct lca_attn_source {
                                1 and 2 together give exactly the entries of part 0 (a
                                decode step can attend to the entries that existed before
                                it while it appends the new ones, and to those after) */
+  int32_t rope_dims;        /* 0, or the rotary embedding of the call (every source of
+                               a call gives the same rope_dims and rope_base): the
+                               normalised query of row r turns by q_pos[r] (q_pos
+                               required), a WINDOW source's raw row at token t by t
+                               (DENSE and GATHER entries are stored turned, see
+                               lca_compress_stream), and each partial o_part turns by
+                               -q_pos[r] ("DeepSeek-V4", Provenance 16: -i RoPE on
+                               the outputs; the merge of turned partials is the turned
+                               merge).  Last rope_dims dims of each head, even, <= D */
+  float rope_base;
   int32_t tiles_per_split;  /* > 0: split s takes the row's keys [32 t s, 32 t (s + 1)),
                                t = tiles_per_split, whatever the other rows of the call
                                (the last split also takes any keys beyond; for GATHER and

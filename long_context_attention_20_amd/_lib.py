@@ -39,7 +39,7 @@ class CompressStream(ctypes.Structure):
         ("src", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("out", ctypes.c_void_p),
         ("ent_off", ctypes.c_void_p), ("C", ctypes.c_int32), ("m", ctypes.c_int32), ("w", ctypes.c_int32),
         ("per_channel", ctypes.c_int32), ("rmsnorm", ctypes.c_int32), ("max_entries", ctypes.c_int32),
-        ("out_key", ctypes.c_int32),
+        ("out_key", ctypes.c_int32), ("rope_dims", ctypes.c_int32), ("rope_base", ctypes.c_float),
     ]
 
 
@@ -54,7 +54,8 @@ class AttnSource(ctypes.Structure):
         ("n_split", ctypes.c_int32), ("o_part", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("max_entries", ctypes.c_int64),
         ("scores", ctypes.c_void_p), ("idx_out", ctypes.c_void_p),
-        ("done_len", ctypes.c_void_p), ("part", ctypes.c_int32), ("tiles_per_split", ctypes.c_int32),
+        ("done_len", ctypes.c_void_p), ("part", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
+        ("rope_base", ctypes.c_float), ("tiles_per_split", ctypes.c_int32),
     ]
 
 

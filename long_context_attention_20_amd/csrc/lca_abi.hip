@@ -162,6 +162,11 @@ static int check_streams(const lca_compress_stream* streams, int n_streams, int 
                 k);
     LCA_REQUIRE(s.out_key != 2 || (s.C == 32 || s.C == 64 || s.C == 128 || s.C == 256), LCA_ERR_UNSUPPORTED,
                 "kv_compress: stream %d: MXFP4 rows need C in {32, 64, 128, 256}", k);
+    LCA_REQUIRE(s.rope_dims >= 0 && s.rope_dims <= s.C && s.rope_dims % 2 == 0 &&
+                    (s.rope_dims == 0 || (s.out_key == 0 && std::isfinite(s.rope_base) && s.rope_base > 0.f)),
+                LCA_ERR_INVALID_ARG,
+                "kv_compress: stream %d: rope_dims=%d must be even, <= C, on rows of the input type, with a "
+                "positive rope_base", k, s.rope_dims);
   }
   return LCA_OK;
 }
@@ -248,6 +253,8 @@ static int check_score_append(const void* p, const float* omega, const void* ike
   const int in_dtype = want_key ? LCA_BF16 : dtype;
   LCA_REQUIRE(idx_stream->out_key == want_key, LCA_ERR_INVALID_ARG,
               "csa_index_score_append: the indexer-key stream's rows (out_key) must match dtype");
+  LCA_REQUIRE(idx_stream->rope_dims == 0, LCA_ERR_INVALID_ARG,
+              "csa_index_score_append: indexer keys are not rotated (rope_dims must be 0)");
   for (int i = 0; i < n_kv; ++i)
     LCA_REQUIRE(kv_streams[i].out_key == 0, LCA_ERR_INVALID_ARG, "csa_index_score_append: kv stream %d writes key rows", i);
   rc = check_streams(idx_stream, 1, in_dtype);
@@ -403,6 +410,8 @@ static int check_hybrid(const lca_attn_source* srcs, int n_src, const void* q, c
                 x.part);
     LCA_REQUIRE(x.tiles_per_split >= 0, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: tiles_per_split=%d < 0", i,
                 x.tiles_per_split);
+    LCA_REQUIRE(x.rope_dims == srcs[0].rope_dims && x.rope_base == srcs[0].rope_base, LCA_ERR_INVALID_ARG,
+                "hybrid_attn: source %d: every source of a call gives the same rope_dims and rope_base", i);
     if (x.tiles_per_split > 0 && (x.kind == LCA_SRC_GATHER || x.kind == LCA_SRC_TOPK))
       LCA_REQUIRE((int64_t)x.n_split * x.tiles_per_split * 32 >= x.k, LCA_ERR_INVALID_ARG,
                   "hybrid_attn: source %d: n_split=%d x tiles_per_split=%d x 32 < k=%d", i, x.n_split,
@@ -410,6 +419,11 @@ static int check_hybrid(const lca_attn_source* srcs, int n_src, const void* q, c
     need_pos = need_pos || x.kind != LCA_SRC_GATHER;
   }
   LCA_REQUIRE(!need_pos || q_pos != nullptr, LCA_ERR_INVALID_ARG, "hybrid_attn: q_pos is NULL");
+  const int rope = srcs[0].rope_dims;
+  LCA_REQUIRE(rope >= 0 && rope <= D && rope % 2 == 0 &&
+                  (rope == 0 || (q_pos != nullptr && std::isfinite(srcs[0].rope_base) && srcs[0].rope_base > 0.f)),
+              LCA_ERR_INVALID_ARG,
+              "hybrid_attn: rope_dims=%d must be even and <= D, with q_pos and a positive rope_base", rope);
   return LCA_OK;
 }
 

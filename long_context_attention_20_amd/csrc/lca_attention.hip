@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
       BF16::unpack(qraw[ks], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= inv;
+      if (a.rope) rope_turn<8>(f, 32 * ks + 8 * g, D, a.rope, a.rope_base, (double)a.q_pos[r]);
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
@@ -243,13 +244,15 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
         lds_dma16(src, tile + row * PITCH);
       }
     };
-    // window rows: RMS over D of the raw row, rounded to bf16, in place (the
-    // wave that loaded a row normalises it once its loads have landed; the
-    // chunk order within the row does not matter here)
+    // window rows: RMS over D of the raw row, then the rotary turn by the
+    // token's position, rounded to bf16, in place (the wave that loaded a row
+    // normalises it once its loads have landed; LDS chunk l of the row holds
+    // its channels 8 (l ^ rows_swz(row)) ..)
     auto norm_rows = [&](int64_t tt) {
       uint16_t* tile = tiles[0][(tt - tb) & 1];
       for (int v = 0; v < rpw; ++v) {
-        uint16_t* rowp = tile + (wis * rpw + v) * PITCH + lane * 8;
+        const int row = wis * rpw + v;
+        uint16_t* rowp = tile + row * PITCH + lane * 8;
         uint4 x = *reinterpret_cast<const uint4*>(rowp);
         float f[8];
         BF16::unpack(x, f);
@@ -260,6 +263,10 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
         const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] *= inv;
+        if (a.rope) {
+          const int64_t kc = blo + tt * kRowsTile + row;  // the token position load_tile read
+          rope_turn<8>(f, (lane ^ rows_swz(row)) * 8, D, a.rope, a.rope_base, (double)(kc < bhi ? kc : blo));
+        }
         *reinterpret_cast<uint4*>(rowp) = BF16::pack(f);
       }
     };
@@ -377,9 +384,11 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
     uint16_t* outp = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)r * a.H + h0 + c16) * D + 4 * g;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
+      float o4[4] = {O[db][0] * w, O[db][1] * w, O[db][2] * w, O[db][3] * w};
+      if (a.rope) rope_turn<4>(o4, 16 * db + 4 * g, D, a.rope, a.rope_base, -(double)a.q_pos[r]);
       uint2 pk;
-      pk.x = pack_bf16x2(O[db][0] * w, O[db][1] * w);
-      pk.y = pack_bf16x2(O[db][2] * w, O[db][3] * w);
+      pk.x = pack_bf16x2(o4[0], o4[1]);
+      pk.y = pack_bf16x2(o4[2], o4[3]);
       *reinterpret_cast<uint2*>(outp + db * 16) = pk;
     }
     return;
@@ -389,22 +398,33 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int64_t orow = ((int64_t)split * a.rows + r) * a.H + h0 + c16;
   float* op = S.o_part + orow * D + 4 * g;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    *reinterpret_cast<float4*>(op + db * 16) = make_float4(O[db][0] * w, O[db][1] * w, O[db][2] * w, O[db][3] * w);
+  for (int db = 0; db < DB; ++db) {
+    float o4[4] = {O[db][0] * w, O[db][1] * w, O[db][2] * w, O[db][3] * w};
+    // the turn back by the query position (it commutes with the merge, a sum
+    // of partials scaled by the same query's weights)
+    if (a.rope) rope_turn<4>(o4, 16 * db + 4 * g, D, a.rope, a.rope_base, -(double)a.q_pos[r]);
+    *reinterpret_cast<float4*>(op + db * 16) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+  }
   if (g == 0) S.lse[orow] = lsum > 0.f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-// Row-tiled attention, two head groups per wave.  The same block shape and
-// key staging as attn_rows_mfma (128 rows, 32-key tiles through swizzled LDS
-// rows), but four waves of 32 rows each, one wave per SIMD with the whole
-// register file: every K fragment read from LDS feeds the S^T products of both
-// 16-head groups and every V^T fragment both O^T products, so a wave does
-// twice the matrix work per LDS byte, and the accumulators of O^T (2 x 16 x D
-// floats) live in the accumulation registers while the architectural ones
-// hold the queries and the fragments in flight.
 // ============================================================ generic path
 // One wavefront per (query row, head, split); a lane owns D/64 dims.  Used for
 // fp32 and for bf16 head counts that are not a multiple of 16.
+// The rotary turn of the lane's DPL dims (dims lane*DPL ..); with one dim per
+// lane the pair (2i, 2i+1) spans lanes 2i and 2i+1 (every lane active).
+template <int DPL>
+__device__ __forceinline__ void valu_turn(float (&v)[DPL], int lane, int D, int rope, float base, double pos) {
+  if constexpr (DPL >= 2) {
+    rope_turn<DPL>(v, lane * DPL, D, rope, base, pos);
+  } else {
+    const float other = __shfl_xor(v[0], 1, 64);
+    float pr[2] = {(lane & 1) ? other : v[0], (lane & 1) ? v[0] : other};
+    rope_turn<2>(pr, lane & ~1, D, rope, base, pos);
+    v[0] = (lane & 1) ? pr[1] : pr[0];
+  }
+}
+
 template <typename ET, int DPL>
 __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
   const int r = blockIdx.z;
@@ -415,6 +435,9 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
   const int D = a.D;
   int64_t first, nseq;
   const int64_t n = attn_keys(a, S, r, &first, &nseq);
+  // positions for the rotary embedding: the query's, and the window's first token
+  const double qpos = a.rope ? (double)a.q_pos[r] : 0.0;
+  const int64_t kpos0 = (a.rope && S.kind == SRC_WINDOW) ? first - S.off[r / a.Tq] : 0;
   const int64_t per = S.tps > 0 ? (int64_t)S.tps * 32 : (n + S.n_split - 1) / S.n_split;
   const int64_t kb = (int64_t)split * per;
   const int64_t ke = (S.tps > 0 && split == S.n_split - 1) ? n : min(n, kb + per);
@@ -430,7 +453,10 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
     ss = wave_sum(ss, 64);
     const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) qh[i] = ET::round(qh[i] * inv);
+    for (int i = 0; i < DPL; ++i) qh[i] *= inv;
+    if (a.rope) valu_turn<DPL>(qh, lane, D, a.rope, a.rope_base, qpos);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) qh[i] = ET::round(qh[i]);
   }
   float o[DPL];
 #pragma unroll
@@ -450,7 +476,10 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
       ss = wave_sum(ss, 64);
       const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) kv[i] = ET::round(kv[i] * inv);
+      for (int i = 0; i < DPL; ++i) kv[i] *= inv;
+      if (a.rope) valu_turn<DPL>(kv, lane, D, a.rope, a.rope_base, (double)(kpos0 + t));
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) kv[i] = ET::round(kv[i]);
     }
 #pragma unroll
     for (int i = 0; i < DPL; ++i) dot = fmaf(qh[i], kv[i], dot);
@@ -466,7 +495,10 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
   float* op = S.o_part + (((int64_t)split * a.rows + r) * a.H + h) * D;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) op[lane * DPL + i] = o[i] * inv;
+  for (int i = 0; i < DPL; ++i) o[i] *= inv;
+  if (a.rope) valu_turn<DPL>(o, lane, D, a.rope, a.rope_base, -qpos);  // -i on the output
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) op[lane * DPL + i] = o[i];
   if (lane == 0) S.lse[((int64_t)split * a.rows + r) * a.H + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
 }
 
@@ -806,6 +838,7 @@ static int launch_attention_impl(const lca_attn_source* srcs, int n_src, const v
   AttnParams a{};
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
+  a.rope = srcs[0].rope_dims; a.rope_base = srcs[0].rope_base;
   apply_diag(&a);
   int splits = 0, topk = -1;
   for (int i = 0; i < n_src; ++i) {
@@ -872,6 +905,7 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
   AttnParams a{};
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
+  a.rope = srcs[0].rope_dims; a.rope_base = srcs[0].rope_base;
   apply_diag(&a);
   const bool mfma = dtype == LCA_BF16 && H % 16 == 0;
   int blocks = 0;
@@ -991,6 +1025,7 @@ int setup_attention_front(const lca_attn_source* srcs, int n_src, const void* q,
   *a = AttnParams{};
   a->q = q; a->q_pos = q_pos; a->Tq = Tq; a->H = H; a->D = D; a->rows = B * Tq;
   a->scale = scale; a->eps = eps; a->n_src = n_src;
+  a->rope = srcs[0].rope_dims; a->rope_base = srcs[0].rope_base;
   apply_diag(a);
   int blocks = 0;
   for (int i = 0; i < n_src; ++i) {

@@ -85,6 +85,11 @@ struct AttnParams {
   int merge;
   const float* sink;    // [H] or NULL
   void* out;
+  // the rotary embedding of the call: the last `rope` dims of each head (0:
+  // none); queries turn by their position, window rows by theirs, partials
+  // and outputs by minus the query's
+  int rope;
+  float rope_base;
   // the in-launch top-k wait: it waits for tbpr + wait_extra filter shares
   // (wait_extra > 0 only as a diagnostic: the wait then always gives up) for
   // at most wait_ticks of the 100 MHz constant clock
@@ -341,7 +346,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     }
   }
   // --- the key count and the block's key range
-  const int32_t qpos_r = (kind != SRC_GATHER && a.q_pos) ? qpos_ld : 0;
+  const int32_t qpos_r = ((kind != SRC_GATHER || a.rope) && a.q_pos) ? qpos_ld : 0;
   const int64_t dlen = (kind == SRC_DENSE && S.part != 0) ? dlen_ld : 0;
   const int64_t nseq = off1 - off0;
   int64_t first = off0;
@@ -379,6 +384,8 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   // clamped valid row) and zeroed when stored
   uint4 stage[LOADS];
   uint32_t okbits = 0;
+  int64_t stage_t = 0;               // tile index of the staged loads (window rows' positions)
+  const int64_t kpos0 = first - off0;  // window: position of key 0 (the window's first token)
   const uint16_t* kvp = reinterpret_cast<const uint16_t*>(S.kv);
   auto key_ok = [&](int64_t key) -> bool {
     if (key >= n) return false;
@@ -386,6 +393,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   };
   auto load_tile = [&](int64_t t) {
     okbits = 0;
+    stage_t = t;
     if (t >= te) return;
 #pragma unroll
     for (int v = 0; v < LOADS; ++v) {
@@ -420,6 +428,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
         const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] *= inv;
+        if (a.rope) {
+          const int id = tt + kTeamThreads * v;
+          rope_turn<8>(f, (id % VPR) * 8, D, a.rope, a.rope_base, (double)(kpos0 + stage_t * kTile + id / VPR));
+        }
         stage[v] = BF16::pack(f);
       }
     }
@@ -567,6 +579,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       BF16::unpack(qraw[ks], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= inv;
+      if (a.rope) rope_turn<8>(f, d0 + ks * 32 + g * 8, D, a.rope, a.rope_base, (double)qpos_r);
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
@@ -743,7 +756,9 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     const int hh = i / (D / 4), d = (i % (D / 4)) * 4;
     const float4 u = *reinterpret_cast<const float4*>(ox + hh * XP + d);
     const float4 v = *reinterpret_cast<const float4*>(ox + (kAttnHeads + hh) * XP + d);
-    *reinterpret_cast<float4*>(op + (int64_t)i * 4) = make_float4(u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w);
+    float o4[4] = {u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w};
+    if (a.rope) rope_turn<4>(o4, d, D, a.rope, a.rope_base, -(double)qpos_r);  // -i on the output
+    *reinterpret_cast<float4*>(op + (int64_t)i * 4) = make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   if (threadIdx.x < nh) {
     float M, f0, f1, lsum;

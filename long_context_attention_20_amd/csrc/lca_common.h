@@ -141,6 +141,37 @@ __device__ __host__ __forceinline__ int64_t n_windows(int64_t L, int m, int w) {
   return L < w ? 0 : (L - w) / m + 1;
 }
 
+// ---------------------------------------------------------------- rotary embedding
+// "DeepSeek-V4" spec sheet, Core block and Provenance 16: partial RoPE on the
+// last dims of a head.  Channels [ch0, ch0 + N) of a C-channel vector (ch0
+// and N even): the last `rope` channels turn pair by pair, pair p (channels
+// C - rope + 2p and the next) as a complex number times exp(i pos theta_p),
+// theta_p = base^(-2p / rope).  The angle is formed and reduced modulo 2 pi
+// in double precision (positions reach 2^20, where a float product would
+// lose most of the angle); its sine and cosine are taken in float.
+template <int N>
+__device__ __forceinline__ void rope_turn(float (&v)[N], int ch0, int C, int rope, float base, double pos) {
+  static_assert(N % 2 == 0, "pairs");
+  const int lo = C - rope;
+  const double l2b = log2((double)base);
+#pragma unroll
+  for (int k = 0; k < N; k += 2) {
+    const int c = ch0 + k;
+    if (rope > 0 && c >= lo) {
+      const int p = (c - lo) >> 1;
+      const double theta = exp2(-(double)(2 * p) / (double)rope * l2b);
+      double a = pos * theta;
+      constexpr double kTwoPi = 6.283185307179586476925286766559;
+      a -= kTwoPi * floor(a / kTwoPi);
+      float sn, cs;
+      sincosf((float)a, &sn, &cs);
+      const float x0 = v[k], x1 = v[k + 1];
+      v[k] = x0 * cs - x1 * sn;
+      v[k + 1] = x0 * sn + x1 * cs;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- ordering
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
 // -0 is folded into +0 so that the two zeros tie, as they compare equal.
@@ -150,7 +181,7 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 }
 
 // ---------------------------------------------------------------- launch status
-// Implemented in lca_abi.cpp: records a message for lca_last_error().
+// Implemented in lca_abi.hip: records a message for lca_last_error().
 void set_error(const char* fmt, ...);
 
 }  // namespace lca

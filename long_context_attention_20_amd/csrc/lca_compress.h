@@ -22,6 +22,8 @@ struct CompressStreamDev {
   void* out;
   const int64_t* ent_off;
   int C, m, w, per_channel, rmsnorm, max_entries;
+  int rope;     // rotated channels at the end of an entry (0: none); entry j turns by j*m + w - 1
+  float rope_base;
   int key;      // key rows: 1 fp8 (C E4M3 bytes, fp32 scale, 4 zero bytes), 2 MXFP4 (C/2 bytes of E2M1
                 // pairs, one E8M0 scale per 32 channels, zero pad to C/2 + 8); one lane group per row, NV = 1
   int G;        // lanes per row
@@ -188,7 +190,7 @@ __device__ __forceinline__ void unpack_fp8x8(uint2 v, float (&x)[8]) {
 template <typename ET, int NV>
 __device__ __forceinline__ void finish_entry(const CompressStreamDev& s, float eps, int G,
                                              PoolState<ET::kVec> (&st)[NV], const int (&ch0)[NV],
-                                             int64_t out_row, bool active) {
+                                             int64_t out_row, bool active, int64_t j) {
   constexpr int VE = ET::kVec;
   float e[NV][VE];
   float ss = 0.f;
@@ -207,6 +209,9 @@ __device__ __forceinline__ void finish_entry(const CompressStreamDev& s, float e
 #pragma unroll
       for (int k = 0; k < VE; ++k) e[v][k] *= inv;
   }
+  if (s.rope)  // after the norm, before the rounding; entry j sits at the last token of its window
+#pragma unroll
+    for (int v = 0; v < NV; ++v) rope_turn<VE>(e[v], ch0[v], s.C, s.rope, s.rope_base, (double)(j * s.m + s.w - 1));
   if (s.key == 2) {
     if constexpr (VE == 8) {
       char* row = reinterpret_cast<char*>(s.out) + out_row * (int64_t)(s.C / 2 + 8);
@@ -333,9 +338,9 @@ __device__ void compress_small(const CompressStreamDev& s, const CompressParams&
         PoolState<VE> e[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) { e[v] = prev[v]; e[v].merge(cur[v]); prev[v] = cur[v]; }
-        finish_entry<ET, NV>(s, P.eps, G, e, rc.ch0, ent_base + j, true);
+        finish_entry<ET, NV>(s, P.eps, G, e, rc.ch0, ent_base + j, true, j);
       } else {
-        finish_entry<ET, NV>(s, P.eps, G, cur, rc.ch0, ent_base + j, true);
+        finish_entry<ET, NV>(s, P.eps, G, cur, rc.ch0, ent_base + j, true, j);
       }
     }
     return;
@@ -369,10 +374,10 @@ __device__ void compress_small(const CompressStreamDev& s, const CompressParams&
       PoolState<VE> e[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) { e[v] = prev[v]; e[v].merge(cur[v]); prev[v] = cur[v]; }
-      finish_entry<ET, NV>(s, P.eps, G, e, rc.ch0, ent_base + j, true);
+      finish_entry<ET, NV>(s, P.eps, G, e, rc.ch0, ent_base + j, true, j);
     } else {
       segment(j, cur);
-      finish_entry<ET, NV>(s, P.eps, G, cur, rc.ch0, ent_base + j, true);
+      finish_entry<ET, NV>(s, P.eps, G, cur, rc.ch0, ent_base + j, true, j);
     }
   }
 }
@@ -499,6 +504,9 @@ __device__ void compress_large(const CompressStreamDev& s, const CompressParams&
 #pragma unroll
       for (int k = 0; k < VE; ++k) e[v][k] *= inv;
   }
+  if (s.rope)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) rope_turn<VE>(e[v], rc.ch0[v], C, s.rope, s.rope_base, (double)(j * s.m + s.w - 1));
   const int64_t rb = (int64_t)C * ET::kBytes;
   const int64_t out_row = s.ent_off[b] + j;
 #pragma unroll

@@ -92,7 +92,8 @@ def _stream_array(streams: Sequence[dict]):
             raise TypeError("one element type per call")
         pc = 1 if lg.dim() == 2 else 0
         arr[i] = CompressStream(src.data_ptr(), lg.data_ptr(), out.data_ptr(), eo.data_ptr(), C, int(s["m"]),
-                                int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]), key)
+                                int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]), key,
+                                int(s.get("rope", 0)), float(s.get("rope_base", 10000.0)))
     return arr, dt
 
 
@@ -321,7 +322,8 @@ def _attn_sources(q, q_pos, sources: Sequence[dict]):
         arr[i] = AttnSource(kind, kv.data_ptr(), off.data_ptr(), None if idx is None else idx.data_ptr(), k,
                             int(s.get("m2", 1)), int(s.get("w2", 1)), int(s.get("W", 0)), ns, o_part.data_ptr(),
                             lse.data_ptr(), _addr(ws), ws_bytes or 0, max_entries or 0, _addr(scores), _addr(idx_out),
-                            _addr(done_len) if part else None, part, int(s.get("tiles_per_split", 0)))
+                            _addr(done_len) if part else None, part, int(s.get("rope", 0)),
+                            float(s.get("rope_base", 10000.0)), int(s.get("tiles_per_split", 0)))
         outs.append((o_part, lse))
     return arr, outs, B
 
@@ -330,7 +332,8 @@ def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
     """The attention branches of a step in one launch.  sources: dicts with
     kind ("gather", "dense", "window" or "topk"), kv, off and n_split, plus
     idx (gather), m2 and w2 (dense), W (window), and optionally o_part / lse,
-    tiles_per_split (a fixed partition of each row's keys) and, for a dense
+    tiles_per_split (a fixed partition of each row's keys), rope / rope_base
+    (the rotary embedding of the call: the same in every source) and, for a dense
     source, part (1: the entries complete within the first done_len[b]
     tokens; 2: those completed after them) with done_len (int64 [B]).
     A "topk" source selects the sparse branch's entries from the scores a

@@ -53,8 +53,17 @@ def _offsets(counts) -> np.ndarray:
 class HybridAttention:
     def __init__(self, H: int, D: int, HI: int, dI: int, k: int, m: int = 4, w: int = 8, m2: int = 128,
                  w2: int = 128, W: int = 128, eps: float = 1e-6, scale: Optional[float] = None,
-                 split_csa: Optional[int] = None, split_hca: Optional[int] = None, ikey: str = "bf16"):
+                 split_csa: Optional[int] = None, split_hca: Optional[int] = None, ikey: str = "bf16",
+                 rope: int = 0, rope_base: float = 10000.0):
         self.H, self.D, self.HI, self.dI, self.k = H, D, HI, dI, k
+        # partial rotary embedding on the last `rope` dims of each head (0:
+        # none): compressed entries are stored turned by the position of
+        # their window's last token, queries and window tokens turn by their
+        # own positions, and every attention output is turned back by the
+        # query position; indexer keys and queries are not turned
+        if rope < 0 or rope % 2 or rope > D:
+            raise ValueError(f"rope: an even number of dims <= D, not {rope}")
+        self.rope, self.rope_base = int(rope), float(rope_base)
         # indexer-key cache: rows of the inputs' type ("bf16"), fp8 rows (d_I
         # E4M3 bytes, fp32 scale, 4 zero bytes) or MXFP4 rows (d_I/2 bytes of
         # E2M1 pairs, one E8M0 scale per 32 channels, zero pad to d_I/2 + 8)
@@ -90,6 +99,13 @@ class HybridAttention:
             kv_hca=torch.empty((max(1, int(ho[-1])), self.D), dtype=dtype, device=device),
             csa_off_h=co, hca_off_h=ho)
 
+    def _turn(self, d: dict) -> dict:
+        """A compression stream or attention source with the layer's rotary
+        embedding."""
+        if self.rope:
+            d.update(rope=self.rope, rope_base=self.rope_base)
+        return d
+
     # -------------------------------------------------------------- compression
     def compress_streams(self, caches: Caches, raw: dict, done_h: Sequence[int], which=("csa", "idx", "hca"),
                          lens_h: Optional[Sequence[int]] = None):
@@ -101,14 +117,14 @@ class HybridAttention:
         new_hca = max(n_windows(L, self.m2, self.w2) - n_windows(d, self.m2, self.w2) for L, d in zip(lens, done_h))
         streams = []
         if new_csa > 0 and "csa" in which:
-            streams.append(dict(src=raw["x"], logits=raw["a"], out=caches.kv_csa, ent_off=caches.csa_off,
-                                m=self.m, w=self.w, rmsnorm=1, max_entries=new_csa))
+            streams.append(self._turn(dict(src=raw["x"], logits=raw["a"], out=caches.kv_csa, ent_off=caches.csa_off,
+                                           m=self.m, w=self.w, rmsnorm=1, max_entries=new_csa)))
         if new_csa > 0 and "idx" in which:
             streams.append(dict(src=raw["u"], logits=raw["c"], out=caches.ikey, ent_off=caches.csa_off,
                                 m=self.m, w=self.w, rmsnorm=0, max_entries=new_csa, key=self.ikey_code))
         if new_hca > 0 and "hca" in which:
-            streams.append(dict(src=raw["x"], logits=raw["g"], out=caches.kv_hca, ent_off=caches.hca_off,
-                                m=self.m2, w=self.w2, rmsnorm=1, max_entries=new_hca))
+            streams.append(self._turn(dict(src=raw["x"], logits=raw["g"], out=caches.kv_hca, ent_off=caches.hca_off,
+                                           m=self.m2, w=self.w2, rmsnorm=1, max_entries=new_hca)))
         return streams
 
     def compress(self, caches: Caches, raw: dict, tok_off: torch.Tensor,
@@ -215,6 +231,22 @@ class HybridAttention:
             if keep:
                 parts = ops.hybrid_attn(q, q_pos, srcs, self.scale, self.eps)
                 csa, hca = parts[0], parts[1]
+        elif self.rope:
+            # the per-branch calls take no rotary embedding: each layer is
+            # one merged call over its compressed entries and the window
+            sc = self.split_csa or self.default_splits(rows, self.k)
+            sh = self.split_hca or self.default_splits(rows, max_hca)
+            win = [self._turn(dict(kind="window", kv=x, off=tok_off, W=self.W, n_split=1))] if self.W > 0 else []
+            csa_src = self._turn(dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=sc))
+            hca_src = self._turn(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2,
+                                      n_split=sh))
+            o1 = ops.hybrid_attn_merge(q, q_pos, [csa_src] + win, sigma, self.scale, self.eps)
+            o2 = ops.hybrid_attn_merge(q, q_pos, [hca_src] + win, sigma, self.scale, self.eps)
+            out = (o1, o2)
+            csa = hca = None
+            if keep:
+                csa = ops.hybrid_attn(q, q_pos, [csa_src], self.scale, self.eps)[0]
+                hca = ops.hybrid_attn(q, q_pos, [hca_src], self.scale, self.eps)[0]
         else:
             sc = self.split_csa or self.default_splits(rows, self.k)
             sh = self.split_hca or self.default_splits(rows, max_hca)
@@ -296,7 +328,7 @@ class HybridAttention:
         if self.W > 0:
             src.append(dict(kind="window", kv=x, off=tok_off, W=self.W, n_split=bufs["sw"], o_part=bufs["swa"][0],
                             lse=bufs["swa"][1]))
-        return src
+        return [self._turn(d) for d in src]
 
     def front_calls(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos, bufs: dict,
                     done_len: torch.Tensor, done_h: Sequence[int], lens_h: Optional[Sequence[int]] = None):
@@ -332,6 +364,8 @@ class HybridAttention:
             back.append(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2, part=2,
                              done_len=done_len, n_split=1, o_part=bufs["hca_new"][0], lse=bufs["hca_new"][1]))
             parts.append(bufs["hca_new"])
+        front = [self._turn(d) for d in front]
+        back = [self._turn(d) for d in back]
         if not front:  # nothing to attend beside the scores
             f0 = lambda: ops.csa_index_score_append(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m,  # noqa: E731
                                                     self.w, bufs["max_csa"], bufs["ws_idx"], idx_st[0], kv_st,

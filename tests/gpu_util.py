@@ -32,6 +32,8 @@ def to_device(raw, cfg, dev="cuda"):
 def layer_for(cfg, **kw):
     from long_context_attention_20_amd import HybridAttention
     kw.setdefault("ikey", getattr(cfg, "ikey", "bf16"))
+    kw.setdefault("rope", getattr(cfg, "rope", 0))
+    kw.setdefault("rope_base", getattr(cfg, "rope_base", 10000.0))
     return HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps, **kw)
 
 
