@@ -24,7 +24,9 @@ is much faster; the oracle then reads those values back from the device.
 Tensor ids: x=0 (raw KV), a=1 (CSA pooling logits), g=2 (HCA pooling logits),
 u=3 (raw indexer keys), c=4 (indexer pooling logits), q=5, p=6 (indexer
 queries), omega=7 (indexer head weights), sigma=8 (sink logits), lens=9,
-plant=10.
+plant=10; with the dual-stream compressor the second-half streams x_b=11,
+a_b=12, u_b=13, c_b=14; with separate values the raw value tokens v=15 (and
+v_b=16 with both options).
 """
 from __future__ import annotations
 
@@ -34,7 +36,8 @@ from typing import Dict, Optional, Tuple
 
 import numpy as np
 
-TID = dict(x=0, a=1, g=2, u=3, c=4, q=5, p=6, omega=7, sigma=8, lens=9, plant=10)
+TID = dict(x=0, a=1, g=2, u=3, c=4, q=5, p=6, omega=7, sigma=8, lens=9, plant=10, x_b=11, a_b=12, u_b=13, c_b=14,
+           v=15, v_b=16)
 
 
 @dataclass(frozen=True)
@@ -65,6 +68,8 @@ class Config:
     ikey: str = "bf16"  # indexer-key cache: "bf16" (the workload dtype), "fp8" (E4M3 rows with a scale) or "mxfp4"
     rope: int = 0       # rotated dims at the end of each head (0: no rotary embedding)
     rope_base: float = 10000.0
+    dual: bool = False  # CSA windows: first half from (x, a) / (u, c), second half from (x_b, a_b) / (u_b, c_b)
+    sepv: bool = False  # values from their own raw stream v (keys from x)
 
     @property
     def scale(self) -> float:
@@ -193,6 +198,8 @@ def make_raw(cfg: Config, layer: int = 0) -> Dict[str, np.ndarray]:
     out["p"] = _normal(cfg, layer, TID["p"], (Q, cfg.HI, cfg.dI), dt)
     out["omega"] = _normal(cfg, layer, TID["omega"], (Q, cfg.HI), "f32")
     out["sigma"] = _normal(cfg, layer, TID["sigma"], (cfg.H,), "f32")
+    for name, shape in _option_streams(cfg, T):
+        out[name] = _normal(cfg, layer, TID[name], shape, dt)
     q_pos = np.zeros((cfg.B, cfg.tq), dtype=np.int32)
     for b, L in enumerate(cfg.lens):
         q_pos[b] = np.arange(L - cfg.tq, L, dtype=np.int32)
@@ -203,6 +210,23 @@ def make_raw(cfg: Config, layer: int = 0) -> Dict[str, np.ndarray]:
             base = int(out["tok_off"][b])
             for t0 in plant_positions(cfg, layer, b, _n_full_windows(L, cfg.m, cfg.w)):
                 out["u"][base + t0: base + t0 + cfg.w] = v[None, :]
+                if cfg.dual:
+                    out["u_b"][base + t0: base + t0 + cfg.w] = v[None, :]
+    return out
+
+
+def _option_streams(cfg: Config, T: int):
+    """(name, shape) of the raw streams the dual-stream compressor and the
+    separate values add."""
+    lshape_kv = (T, cfg.D) if cfg.logit_per_channel else (T,)
+    lshape_i = (T, cfg.dI) if cfg.logit_per_channel else (T,)
+    out = []
+    if cfg.dual:
+        out += [("x_b", (T, cfg.D)), ("a_b", lshape_kv), ("u_b", (T, cfg.dI)), ("c_b", lshape_i)]
+    if cfg.sepv:
+        out.append(("v", (T, cfg.D)))
+        if cfg.dual:
+            out.append(("v_b", (T, cfg.D)))
     return out
 
 
@@ -235,6 +259,8 @@ def make_raw_torch(cfg: Config, layer: int = 0, device: str = "cuda"):
     out["p"] = normal(TID["p"], (Q, cfg.HI, cfg.dI))
     out["omega"] = normal(TID["omega"], (Q, cfg.HI), torch.float32)
     out["sigma"] = normal(TID["sigma"], (cfg.H,), torch.float32)
+    for name, shape in _option_streams(cfg, T):
+        out[name] = normal(TID[name], shape)
     q_pos = np.zeros((cfg.B, cfg.tq), dtype=np.int32)
     for b, L in enumerate(cfg.lens):
         q_pos[b] = np.arange(L - cfg.tq, L, dtype=np.int32)
@@ -248,4 +274,6 @@ def make_raw_torch(cfg: Config, layer: int = 0, device: str = "cuda"):
                 continue
             rows = (torch.from_numpy(pos)[:, None] + torch.arange(cfg.w)[None, :]).reshape(-1) + int(offs[b])
             out["u"][rows.to(device)] = v
+            if cfg.dual:
+                out["u_b"][rows.to(device)] = v
     return out

@@ -6,7 +6,9 @@ compressed KV entries; attention sinks); "Why DeepSeek V4 Stands Apart", Core
 Architectural Innovations (128-token sliding window; sparse attention over the
 selected CSA entries; dense attention over the HCA entries).
 
-Readings: a compressed entry serves as both key and value (K = V);
+Readings: a compressed entry serves as both key and value (K = V), unless
+the layer takes its values from a separate raw stream (then every key row has
+a value row beside it, built by the same steps);
 logits are scale * qhat_h . key with scale = 1/sqrt(D); the sink of head h is
 one logit sigma_h with a zero value, so it only enlarges the denominator.
 
@@ -45,12 +47,16 @@ def logits(qhat, keys, scale: float):
     return scale * (np.asarray(qhat, np.float64) @ np.asarray(keys, np.float64).T)
 
 
-def partial(qhat, keys, scale: float):
-    """Normalised partial attention of every head over ``keys`` (K = V).
+def partial(qhat, keys, scale: float, values=None):
+    """Normalised partial attention of every head over ``keys``, averaging
+    ``values`` (row n the value of key n; None: the keys themselves).
 
     Returns o [H, D] and lse [H]; an empty key set gives o = 0, lse = -inf."""
     qhat = np.asarray(qhat, np.float64)
     keys = np.asarray(keys, np.float64)
+    vals = keys if values is None else np.asarray(values, np.float64)
+    if vals.shape != keys.shape:
+        raise ValueError("one value row per key row")
     H, D = qhat.shape
     if keys.shape[0] == 0:
         return np.zeros((H, D)), np.full(H, -np.inf)
@@ -58,7 +64,7 @@ def partial(qhat, keys, scale: float):
     mx = np.max(lg, axis=1, keepdims=True)
     e = np.exp(lg - mx)
     se = np.sum(e, axis=1, keepdims=True)
-    o = (e / se) @ keys
+    o = (e / se) @ vals
     lse = (mx + np.log(se))[:, 0]
     return o, lse
 
@@ -85,13 +91,14 @@ def merge(parts, sigma=None):
     return o, tot
 
 
-def attend(qhat, keys, scale: float, sigma=None):
+def attend(qhat, keys, scale: float, sigma=None, values=None):
     """One softmax over ``keys`` plus the sink, written directly (no partials).
 
     Returns o [H, D] and the per-head probabilities [H, n] and sink
     probability [H] (so callers can check that they sum to one)."""
     qhat = np.asarray(qhat, np.float64)
     keys = np.asarray(keys, np.float64)
+    vals = keys if values is None else np.asarray(values, np.float64)
     lg = logits(qhat, keys, scale)
     cols = [lg]
     if sigma is not None:
@@ -101,6 +108,6 @@ def attend(qhat, keys, scale: float, sigma=None):
     e = np.exp(allg - mx)
     prob = e / np.sum(e, axis=1, keepdims=True)
     n = keys.shape[0]
-    o = prob[:, :n] @ keys
+    o = prob[:, :n] @ vals
     psink = prob[:, n] if sigma is not None else np.zeros(qhat.shape[0])
     return o, prob[:, :n], psink

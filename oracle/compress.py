@@ -13,6 +13,13 @@ feeds two consecutive windows: the "two overlapping streams"), HCA uses
 m = w = 128.  KV entries are then RMS-normalised over channels with unit gain:
 e / sqrt(mean(e**2) + eps).  Indexer keys are pooled the same way (CSA windows)
 but not normalised.
+
+Dual-stream form (the other reading of "two overlapping streams"; CSA only,
+w = 2m): every token t carries two (value, logit) pairs, one for the window
+in whose first half it lies (window t // m: src, z) and one for the window in
+whose second half it lies (window t // m - 1: src2, z2).  An entry pools its
+first m tokens from the first pair and its last m tokens from the second,
+under one softmax over all w logits of a channel.
 """
 import numpy as np
 
@@ -51,14 +58,18 @@ def pool_window(src_win, z_win):
     return np.sum(alpha * src_win, axis=0), alpha
 
 
-def compress(src, z, m: int, w: int, norm: bool, eps: float = 1e-6, entries=None):
+def compress(src, z, m: int, w: int, norm: bool, eps: float = 1e-6, entries=None, src2=None, z2=None):
     """Compressed entries of one sequence (float64, not yet rounded).
 
     src: [L, C] raw stream of the sequence; z: [L, C] or [L] pooling logits.
     entries: optional iterable of entry indices to compute (default: all).
-    Returns [len(entries), C]."""
+    src2, z2: the second-half stream of the dual-stream form (w = 2m), or
+    None.  Returns [len(entries), C]."""
     L = src.shape[0]
     N = n_entries(L, m, w)
+    dual = src2 is not None
+    if dual and (w != 2 * m or z2 is None or np.shape(src2) != np.shape(src) or np.shape(z2) != np.shape(z)):
+        raise ValueError("the dual-stream form needs w = 2m and second-half streams shaped as the first")
     if entries is None:
         entries = range(N)
     entries = list(entries)
@@ -68,7 +79,14 @@ def compress(src, z, m: int, w: int, norm: bool, eps: float = 1e-6, entries=None
         if not (0 <= j < N):
             raise IndexError(f"entry {j} outside [0, {N})")
         t0 = j * m
-        e, _ = pool_window(src[t0:t0 + w], z[t0:t0 + w])
+        if dual:
+            # the window's rows: its first half from the first stream, its
+            # second half from the second
+            xs = np.concatenate([np.asarray(src[t0:t0 + m]), np.asarray(src2[t0 + m:t0 + w])])
+            zs = np.concatenate([np.asarray(z[t0:t0 + m]), np.asarray(z2[t0 + m:t0 + w])])
+            e, _ = pool_window(xs, zs)
+        else:
+            e, _ = pool_window(src[t0:t0 + w], z[t0:t0 + w])
         out[r] = e
     if norm and len(entries):
         out = rmsnorm(out, eps)

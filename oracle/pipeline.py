@@ -15,6 +15,13 @@ token is already part of the context; prefill: every position of the chunk):
    three branches), or as two layer outputs ("mode B": CSA + window + sink and
    HCA + window + sink).
 
+Options: the dual-stream compressor (cfg.dual: the CSA windows' second halves
+from the streams x_b, a_b, u_b, c_b; see oracle.compress) and separate values
+(cfg.sepv: a raw value stream v, pooled with the key entries' logits over the
+same windows -- in the dual form its second halves from v_b -- and normalised
+and turned as the keys; the window's values are the raw v tokens, normalised
+and turned as the window keys).
+
 Pages: "Why DeepSeek V4 Stands Apart", Core Architectural Innovations; "DeepSeek-V4",
 Design overview, Core block, Inference efficiency; "DeepSeek V4 Is Not a Better
 Model", 1. CSA + HCA (older tokens compressed, recent tokens kept at full
@@ -38,6 +45,8 @@ class SeqCaches:
     kv_csa: np.ndarray   # [N_csa, D]
     ikey: np.ndarray     # [N_csa, dI]
     kv_hca: np.ndarray   # [N_hca, D]
+    v_csa: Optional[np.ndarray] = None   # value rows of the CSA entries (separate values), else None
+    v_hca: Optional[np.ndarray] = None
 
 
 def seq_slice(arr, tok_off, b):
@@ -49,10 +58,11 @@ def fp8_keys(cfg) -> bool:
     return getattr(cfg, "ikey", "bf16") == "fp8"
 
 
-def kv_entries(src, z, m, w, cfg, entries=None):
+def kv_entries(src, z, m, w, cfg, entries=None, src2=None, z2=None):
     """RMS-normalised KV entries of one stream (with cfg.rope, entry j turned
-    by the position of its window's last token), rounded to the storage type."""
-    e = compress(src, z, m, w, True, cfg.eps, entries)
+    by the position of its window's last token), rounded to the storage type;
+    src2, z2: the second-half stream of the dual-stream form."""
+    e = compress(src, z, m, w, True, cfg.eps, entries, src2=src2, z2=z2)
     rope = getattr(cfg, "rope", 0)
     if rope and len(e):
         js = range(n_entries(src.shape[0], m, w)) if entries is None else entries
@@ -60,11 +70,17 @@ def kv_entries(src, z, m, w, cfg, entries=None):
     return round_to(e, cfg.dtype)
 
 
-def build_seq_caches(x, a, g, u, c, cfg) -> SeqCaches:
+def build_seq_caches(x, a, g, u, c, cfg, opt=None) -> SeqCaches:
     """Caches of one sequence from its raw streams (all float64 views).  With
-    fp8 or MXFP4 indexer keys the key cache holds the rows they stand for."""
-    kv_csa = kv_entries(x, a, cfg.m, cfg.w, cfg)
-    pooled = compress(u, c, cfg.m, cfg.w, False, cfg.eps)
+    fp8 or MXFP4 indexer keys the key cache holds the rows they stand for.
+    opt: the option streams of the sequence (x_b, a_b, u_b, c_b with
+    cfg.dual; v, and v_b with both options, with cfg.sepv)."""
+    opt = opt or {}
+    dual = getattr(cfg, "dual", False)
+    sepv = getattr(cfg, "sepv", False)
+    second = (lambda k: opt[k]) if dual else (lambda k: None)  # noqa: E731
+    kv_csa = kv_entries(x, a, cfg.m, cfg.w, cfg, src2=second("x_b"), z2=second("a_b"))
+    pooled = compress(u, c, cfg.m, cfg.w, False, cfg.eps, src2=second("u_b"), z2=second("c_b"))
     kind = getattr(cfg, "ikey", "bf16")
     if kind == "fp8":
         ikey = quant.dequantize_rows(*quant.quantize_rows(pooled))
@@ -73,7 +89,14 @@ def build_seq_caches(x, a, g, u, c, cfg) -> SeqCaches:
     else:
         ikey = round_to(pooled, cfg.dtype)
     kv_hca = kv_entries(x, g, cfg.m2, cfg.w2, cfg)
-    return SeqCaches(kv_csa, ikey, kv_hca)
+    v_csa = v_hca = None
+    if sepv:
+        v_csa = kv_entries(opt["v"], a, cfg.m, cfg.w, cfg, src2=second("v_b"), z2=second("a_b"))
+        v_hca = kv_entries(opt["v"], g, cfg.m2, cfg.w2, cfg)
+    return SeqCaches(kv_csa, ikey, kv_hca, v_csa, v_hca)
+
+
+OPTION_STREAMS = ("x_b", "a_b", "u_b", "c_b", "v", "v_b")
 
 
 def build_caches(raw, cfg) -> List[SeqCaches]:
@@ -81,7 +104,8 @@ def build_caches(raw, cfg) -> List[SeqCaches]:
     out = []
     for b in range(cfg.B):
         s = lambda k: seq_slice(raw[k], off, b)  # noqa: E731
-        out.append(build_seq_caches(s("x"), s("a"), s("g"), s("u"), s("c"), cfg))
+        opt = {k: s(k) for k in OPTION_STREAMS if k in raw}
+        out.append(build_seq_caches(s("x"), s("a"), s("g"), s("u"), s("c"), cfg, opt))
     return out
 
 
@@ -108,10 +132,11 @@ def finish(o, i, cfg):
     return round_to(o, cfg.dtype)
 
 
-def query_step(caches: SeqCaches, x_seq, q, p, omega, sigma, i, cfg, idx=None):
+def query_step(caches: SeqCaches, x_seq, q, p, omega, sigma, i, cfg, idx=None, v_seq=None):
     """Every intermediate of one query (float64; outputs rounded at the end).
 
-    ``idx`` overrides the selection (to attend over another selected set)."""
+    ``idx`` overrides the selection (to attend over another selected set);
+    ``v_seq``: the sequence's raw value tokens (separate values)."""
     s, sel = select(caches.ikey, p, omega, i, cfg)
     if idx is None:
         idx = sel
@@ -119,10 +144,13 @@ def query_step(caches: SeqCaches, x_seq, q, p, omega, sigma, i, cfg, idx=None):
                                base=getattr(cfg, "rope_base", 10000.0))
     idx = np.asarray(idx, dtype=np.int64)
     idx = idx[idx >= 0]
-    csa = att.partial(qhat, caches.kv_csa[idx], cfg.scale)
+    sepv = getattr(cfg, "sepv", False)
+    if sepv and (caches.v_csa is None or v_seq is None):
+        raise ValueError("separate values need the value caches and the raw value tokens")
+    csa = att.partial(qhat, caches.kv_csa[idx], cfg.scale, caches.v_csa[idx] if sepv else None)
     nh = n_visible(i, cfg.m2, cfg.w2)
-    hca = att.partial(qhat, caches.kv_hca[:nh], cfg.scale)
-    swa = att.partial(qhat, window_keys(x_seq, i, cfg), cfg.scale)
+    hca = att.partial(qhat, caches.kv_hca[:nh], cfg.scale, caches.v_hca[:nh] if sepv else None)
+    swa = att.partial(qhat, window_keys(x_seq, i, cfg), cfg.scale, window_keys(v_seq, i, cfg) if sepv else None)
     o_a, lse_a = att.merge([csa, hca, swa], sigma)
     o_csa, _ = att.merge([csa, swa], sigma)
     o_hca, _ = att.merge([hca, swa], sigma)
@@ -146,7 +174,8 @@ def run(raw, cfg, caches: Optional[List[SeqCaches]] = None, queries=None):
         r = b * cfg.tq + t
         i = int(raw["q_pos"][b, t])
         res[(b, t)] = query_step(caches[b], seq_slice(raw["x"], off, b), raw["q"][r], raw["p"][r],
-                                 raw["omega"][r], raw["sigma"], i, cfg)
+                                 raw["omega"][r], raw["sigma"], i, cfg,
+                                 v_seq=seq_slice(raw["v"], off, b) if getattr(cfg, "sepv", False) else None)
     return caches, res
 
 

@@ -652,3 +652,129 @@ def test_gather_oracle_equals_dense_bruteforce_with_rope(dtype):
                                         cfg.with_(rope=0))
             if i > 0:
                 assert np.max(np.abs(plain["out"] - r["out"])) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# dual-stream compressor and separate values
+# --------------------------------------------------------------------------
+
+def _streams(seed, L=41, C=6, per_channel=True):
+    rng = np.random.default_rng(seed)
+    zs = (L, C) if per_channel else (L,)
+    return (rng.standard_normal((L, C)), rng.standard_normal(zs), rng.standard_normal((L, C)),
+            rng.standard_normal(zs))
+
+
+@pytest.mark.parametrize("per_channel", [True, False])
+@pytest.mark.parametrize("norm", [False, True])
+def test_dual_with_equal_streams_is_the_single_stream(per_channel, norm):
+    x, z, _, _ = _streams(40, per_channel=per_channel)
+    single = cmp.compress(x, z, 4, 8, norm)
+    dual = cmp.compress(x, z, 4, 8, norm, src2=x.copy(), z2=z.copy())
+    assert dual.shape == single.shape == (cmp.n_entries(41, 4, 8), 6)
+    assert np.array_equal(dual, single)
+
+
+@pytest.mark.parametrize("per_channel", [True, False])
+def test_dual_halves_come_from_their_streams(per_channel):
+    """With one half's logits pushed to -1e4 (weights underflow to zero) an
+    entry is the pool of the other half alone: entry j of the non-overlapping
+    pool (w = m) of the first stream, or entry j + 1 of that of the second."""
+    x, z, x2, z2 = _streams(41, per_channel=per_channel)
+    n = cmp.n_entries(41, 4, 8)
+    first_only = cmp.compress(x, z, 4, 8, False, src2=x2, z2=z2 - 1e4)
+    assert np.allclose(first_only, cmp.compress(x, z, 4, 4, False)[:n], rtol=0, atol=1e-15)
+    second_only = cmp.compress(x, z - 1e4, 4, 8, False, src2=x2, z2=z2)
+    assert np.allclose(second_only, cmp.compress(x2, z2, 4, 4, False)[1:n + 1], rtol=0, atol=1e-15)
+    # the two halves really differ (a swapped half fails one of the above)
+    assert np.max(np.abs(first_only - second_only)) > 0.1
+
+
+def test_dual_closed_form_on_constant_streams():
+    """Constant first-half rows c1 with logit 0 and second-half rows c2 with
+    logit log 3: every entry is (c1 + 3 c2) / 4 per channel."""
+    L, C = 30, 5
+    c1, c2 = np.arange(1.0, C + 1), -2.0 * np.arange(1.0, C + 1)
+    x, x2 = np.tile(c1, (L, 1)), np.tile(c2, (L, 1))
+    z, z2 = np.zeros((L, C)), np.full((L, C), math.log(3.0))
+    e = cmp.compress(x, z, 4, 8, False, src2=x2, z2=z2)
+    assert np.allclose(e, np.tile((c1 + 3 * c2) / 4, (cmp.n_entries(L, 4, 8), 1)), rtol=0, atol=1e-14)
+    with pytest.raises(ValueError):
+        cmp.compress(x, z, 4, 4, False, src2=x2, z2=z2)   # no overlap: no second half
+
+
+def _sdpa_v(qhat, keys, vals, scale):
+    q = torch.from_numpy(np.ascontiguousarray(qhat))[None]
+    k = torch.from_numpy(np.ascontiguousarray(keys))[None]
+    v = torch.from_numpy(np.ascontiguousarray(vals))[None]
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)[0].numpy()
+
+
+def test_separate_values_partial_is_textbook_attention():
+    rng = np.random.default_rng(42)
+    H, D, n = 5, 12, 23
+    qhat, keys, vals = rng.standard_normal((H, D)), rng.standard_normal((n, D)), rng.standard_normal((n, D))
+    o, lse = att.partial(qhat, keys, 0.4, vals)
+    assert np.allclose(o, _sdpa_v(qhat, keys, vals, 0.4), rtol=0, atol=1e-12)
+    # the weights are the keys' (lse does not depend on the values)
+    assert np.array_equal(lse, att.partial(qhat, keys, 0.4)[1])
+    # constant values come out unchanged; with a sink they are scaled by the
+    # probability mass of the keys
+    c = rng.standard_normal(D)
+    oc, _ = att.partial(qhat, keys, 0.4, np.tile(c, (n, 1)))
+    assert np.allclose(oc, np.tile(c, (H, 1)), rtol=0, atol=1e-13)
+    sig = rng.standard_normal(H)
+    o_s, prob, ps = att.attend(qhat, keys, 0.4, sig, values=np.tile(c, (n, 1)))
+    assert np.allclose(o_s, (1.0 - ps)[:, None] * c[None], rtol=0, atol=1e-13)
+    with pytest.raises(ValueError):
+        att.partial(qhat, keys, 0.4, vals[:-1])
+
+
+def test_separate_values_window_one_reduces_to_causal_attention():
+    """m = w = 1, k >= N, one branch: textbook causal attention with keys the
+    normalised x tokens and values the normalised v tokens (torch SDPA)."""
+    rng = np.random.default_rng(43)
+    L, H, D = 31, 3, 16
+    x = numerics.round_bf16(rng.standard_normal((L, D)))
+    v = numerics.round_bf16(rng.standard_normal((L, D)))
+    z, g = rng.standard_normal((L, D)), rng.standard_normal((L, D))
+    u, c = rng.standard_normal((L, 4)), rng.standard_normal((L, 4))
+    q = rng.standard_normal((H, D))
+    cfg = li.TINY.with_(D=D, H=H, dI=4, dtype="f32", m=1, w=1, m2=1, w2=1, k=4 * L, W=L + 3, sepv=True)
+    caches = pipeline.build_seq_caches(x, z, g, u, c, cfg, {"v": v})
+    for i in (0, 7, L - 1):
+        r = pipeline.query_step(caches, x, q, rng.standard_normal((2, 4)), np.ones(2), np.full(H, -np.inf), i, cfg,
+                                v_seq=v)
+        qhat = att.normalize_query(q, cfg.eps, "f32")
+        kref = np.stack([cmp.rmsnorm(x[j], cfg.eps) for j in range(i + 1)])
+        vref = np.stack([cmp.rmsnorm(v[j], cfg.eps) for j in range(i + 1)])
+        o_ref = _sdpa_v(qhat, kref, vref, cfg.scale)
+        for branch in ("csa", "hca", "swa"):
+            assert np.allclose(r[branch][0], o_ref, rtol=0, atol=1e-6), branch
+        # the keys' own average differs (the values are really used)
+        assert i == 0 or np.max(np.abs(_sdpa_v(qhat, kref, kref, cfg.scale) - o_ref)) > 1e-2
+
+
+@pytest.mark.parametrize("dtype,d_rope", [("bf16", 0), ("f32", 0), ("f32", 4)])
+@pytest.mark.parametrize("dual,sepv", [(True, False), (False, True), (True, True)])
+def test_options_oracle_equals_dense_bruteforce(dtype, d_rope, dual, sepv):
+    cfg = _tiny_cfg(dtype, rope=d_rope, dual=dual, sepv=sepv)
+    raw = li.make_raw(cfg)
+    caches, _ = pipeline.run(raw, cfg)
+    off = raw["tok_off"]
+    for b in range(cfg.B):
+        L = cfg.lens[b]
+        sl = lambda k: pipeline.seq_slice(raw[k], off, b)  # noqa: E731
+        opt = {k: sl(k) for k in pipeline.OPTION_STREAMS if k in raw}
+        for i in (L - 1, L - 9, 20, 7, 0):
+            r = pipeline.query_step(caches[b], sl("x"), raw["q"][b], raw["p"][b], raw["omega"][b],
+                                    raw["sigma"], i, cfg, v_seq=opt.get("v"))
+            od, chosen = dense.query(sl("x"), sl("a"), sl("g"), sl("u"), sl("c"), raw["q"][b],
+                                     raw["p"][b], raw["omega"][b], raw["sigma"], i, cfg, opt)
+            assert set(int(j) for j in r["sel"]) == chosen
+            got = rope.rotate(r["out_raw"], -i, cfg.rope) if cfg.rope else r["out_raw"]
+            assert np.allclose(got, np.array(od), rtol=0, atol=1e-12 if dtype == "f32" else 1e-2)
+    # the option changes the result (the pins can see it ignored)
+    plain, _ = pipeline.run(raw, cfg.with_(dual=False, sepv=False))
+    assert any(np.max(np.abs(plain[b].kv_csa - caches[b].kv_csa)) > 1e-3 for b in range(cfg.B)) or not dual
+    assert all(caches[b].v_csa is not None for b in range(cfg.B)) or not sepv
