@@ -116,13 +116,14 @@ def step_bytes(cfg):
     return tot
 
 
-def kernel_cost(cfg, name):
+def kernel_cost(cfg, name, front=False):
     """(bytes, flops, overhead bytes) of one launch of a step's kernel: the
     bytes are its share of the step's algorithmic bytes (the byte model of
     step_bytes: keys shared by the tq rows of a sequence counted once); the
     overhead is traffic the design adds that the method does not need (the
-    row's scores written by the front launch and read back by the sparse
-    launch, the fp32 split partials)."""
+    row's scores written by the scoring launch and read back by the sparse
+    blocks).  front: the step in front form, where the HCA entries and the
+    window are attended beside the scores rather than in hybrid_attn."""
     e = 2 if cfg.dtype == "bf16" else 4
     tq = cfg.tq
     by = fl = ov = 0
@@ -156,6 +157,9 @@ def kernel_cost(cfg, name):
             by += tq * kk * (cfg.D * e + 4) + tq * cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * kk * tq
             ov += tq * ncsa * 4                                  # the row's scores read back
+            if not front:                                        # the HCA entries and the window
+                by += (nh + nwin) * cfg.D * e
+                fl += 4 * cfg.H * cfg.D * (nh + min(cfg.W, L)) * tq
         if name == "swa_merge":
             by += tq * (cfg.H * cfg.D * e + cfg.H * 4)           # output + sink
     return by, fl, ov
@@ -654,7 +658,7 @@ def main():
     ms = ms_graph if ms_graph is not None else ms_stream
     value = cfg.B * cfg.tq / (ms / 1e3)
     name = run.names[dom]
-    kb, kf, kov = kernel_cost(cfg, name.split("(")[0])
+    kb, kf, kov = kernel_cost(cfg, name.split("(")[0], run.front)
     if kf / max(kb, 1) >= MFMA_BF16_PEAK / HBM_PEAK:
         roof = {"bound": "mfma", "achieved": kf / (k_ms / 1e3) / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
                 "unit": "TFLOP/s"}
@@ -670,7 +674,7 @@ def main():
     # every launch of the step against its share of the algorithmic bytes
     per_kernel = {}
     for n, t in zip(run.names, per):
-        b_, f_, o_ = kernel_cost(cfg, n)
+        b_, f_, o_ = kernel_cost(cfg, n, run.front)
         per_kernel[n] = {"ms": float(t), "bytes": b_, "overhead_bytes": o_, "flops": f_,
                          "hbm_frac": b_ / (t / 1e3) / HBM_PEAK if t > 0 else None}
 

@@ -126,6 +126,14 @@ typedef struct lca_compress_stream {
                           /* pos = j*m + w - 1 (the last token of entry j's window);  */
                           /* rows of the input type only (out_key = 0)                 */
   float rope_base;        /* > 0 when rope_dims > 0 (10000 in the benchmark layers)    */
+  const void* src2;       /* NULL, or the dual-stream form ("DeepSeek-V4", Design      */
+                          /* overview: every 4 tokens into two overlapping streams;  */
+                          /* Core block: overlapping dual compressed streams): the   */
+                          /* last m tokens of each window are read from src2 and     */
+                          /* logits2 (same shapes and type as src and logits), the   */
+                          /* first m from src and logits, one softmax over all w     */
+                          /* logits of a channel.  Needs w = 2m <= 16                */
+  const void* logits2;    /* with src2: the second-half logits; else NULL            */
 } lca_compress_stream;
 
 /* Compress up to 4 streams in one launch.
@@ -385,6 +393,14 @@ typedef struct lca_attn_source {
                                few query rows per sequence; the row-tiled path (many
                                rows per sequence) always cuts a block's key range into
                                n_split parts */
+  const void* v;            /* NULL: the keys are the values (one shared KV vector per
+                               entry, "DeepSeek-V4", Inference efficiency: shared-KV
+                               MQA).  Else the values, rows laid out as kv (same dtype,
+                               D wide, same row for the same key): a DENSE / GATHER /
+                               TOPK source's value entries, a WINDOW source's raw value
+                               tokens (RMS-normalised and turned on load as the window
+                               keys).  Such calls take the per-row kernel, also with
+                               many query rows per sequence */
 } lca_attn_source;
 
 int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
@@ -441,8 +457,9 @@ int lca_hybrid_attn_merge(const lca_attn_source* srcs, int n_src, const void* q,
  * Innovations: the dense attention over the 128:1 entries and the window do
  * not depend on the indexer).  On the bf16 matrix-core path (D = 512, H a
  * multiple of 16, d_I = 64, one query row per sequence or a few sharing a
- * score block) it is one launch whose attention blocks run beside the score
- * blocks; elsewhere the two launches above.
+ * score block, no rotary embedding, no separate values) it is one launch
+ * whose attention blocks run beside the score blocks; elsewhere the two
+ * launches above.
  *   srcs  DENSE or WINDOW sources only (LCA_ERR_INVALID_ARG otherwise); a
  *         source over a cache that the appends write must be DENSE with
  *         part = 1 and this call's done_len (the entries that existed

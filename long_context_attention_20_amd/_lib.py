@@ -40,6 +40,7 @@ class CompressStream(ctypes.Structure):
         ("ent_off", ctypes.c_void_p), ("C", ctypes.c_int32), ("m", ctypes.c_int32), ("w", ctypes.c_int32),
         ("per_channel", ctypes.c_int32), ("rmsnorm", ctypes.c_int32), ("max_entries", ctypes.c_int32),
         ("out_key", ctypes.c_int32), ("rope_dims", ctypes.c_int32), ("rope_base", ctypes.c_float),
+        ("src2", ctypes.c_void_p), ("logits2", ctypes.c_void_p),
     ]
 
 
@@ -55,7 +56,7 @@ class AttnSource(ctypes.Structure):
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("max_entries", ctypes.c_int64),
         ("scores", ctypes.c_void_p), ("idx_out", ctypes.c_void_p),
         ("done_len", ctypes.c_void_p), ("part", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
-        ("rope_base", ctypes.c_float), ("tiles_per_split", ctypes.c_int32),
+        ("rope_base", ctypes.c_float), ("tiles_per_split", ctypes.c_int32), ("v", ctypes.c_void_p),
     ]
 
 

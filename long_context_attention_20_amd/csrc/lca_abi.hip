@@ -167,6 +167,10 @@ static int check_streams(const lca_compress_stream* streams, int n_streams, int 
                 LCA_ERR_INVALID_ARG,
                 "kv_compress: stream %d: rope_dims=%d must be even, <= C, on rows of the input type, with a "
                 "positive rope_base", k, s.rope_dims);
+    LCA_REQUIRE((s.src2 == nullptr) == (s.logits2 == nullptr), LCA_ERR_INVALID_ARG,
+                "kv_compress: stream %d: src2 and logits2 are given together or not at all", k);
+    LCA_REQUIRE(!s.src2 || (s.w == 2 * s.m && s.w <= 16), LCA_ERR_UNSUPPORTED,
+                "kv_compress: stream %d: the dual-stream form needs w = 2m <= 16 (m=%d, w=%d)", k, s.m, s.w);
   }
   return LCA_OK;
 }
@@ -470,8 +474,8 @@ int lca_decode_front(const void* p, const float* omega, const void* ikey, const 
     LCA_REQUIRE(x.kind == LCA_SRC_DENSE || x.kind == LCA_SRC_WINDOW, LCA_ERR_INVALID_ARG,
                 "decode_front: source %d: only DENSE and WINDOW sources run beside the scores", i);
     // a source must not read entries the appends of the same launch write
-    bool written = x.kv == idx_stream->out;
-    for (int j = 0; j < n_kv; ++j) written = written || x.kv == kv_streams[j].out;
+    bool written = x.kv == idx_stream->out || (x.v && x.v == idx_stream->out);
+    for (int j = 0; j < n_kv; ++j) written = written || x.kv == kv_streams[j].out || (x.v && x.v == kv_streams[j].out);
     LCA_REQUIRE(!written || (x.kind == LCA_SRC_DENSE && x.part == 1 && x.done_len == done_len), LCA_ERR_INVALID_ARG,
                 "decode_front: source %d reads a cache the appends write: it must be DENSE with part = 1 and the "
                 "call's done_len", i);

@@ -15,11 +15,14 @@
 
 namespace lca {
 
-// The attention kernel of few query rows per sequence (see attn_block).
-template <int D, bool TOPK, int FC = 1>
+// The attention kernel of few query rows per sequence (see attn_block);
+// OPT: the call may turn by a rotary embedding and its sources may give
+// values apart from their keys (kept out of the plain kernel, whose register
+// budget it would strain).
+template <int D, bool TOPK, int FC = 1, bool OPT = false>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnParams a) {
   __shared__ __attribute__((aligned(16))) char lds_raw[AttnLds<D, TOPK>::kBytes];
-  attn_block<D, TOPK, FC>(a, blockIdx.x, lds_raw);
+  attn_block<D, TOPK, FC, OPT>(a, blockIdx.x, lds_raw);
 }
 
 // ============================================================ many query rows
@@ -76,7 +79,9 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <bool MERGE>
+// ROPE: the call turns by a rotary embedding (a kernel of its own, to keep
+// the plain one within its register budget).
+template <bool MERGE, bool ROPE>
 __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_rows_mfma(AttnParams a) {
   constexpr int D = 512;
   constexpr int KS = D / 32;      // k-steps of S over D
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
       BF16::unpack(qraw[ks], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= inv;
-      if (a.rope) rope_turn<8>(f, 32 * ks + 8 * g, D, a.rope, a.rope_base, (double)a.q_pos[r]);
+      if (ROPE) rope_turn<8>(f, 32 * ks + 8 * g, D, a.rope, (double)a.q_pos[r]);
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
@@ -263,9 +268,9 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
         const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] *= inv;
-        if (a.rope) {
+        if (ROPE) {
           const int64_t kc = blo + tt * kRowsTile + row;  // the token position load_tile read
-          rope_turn<8>(f, (lane ^ rows_swz(row)) * 8, D, a.rope, a.rope_base, (double)(kc < bhi ? kc : blo));
+          rope_turn<8>(f, (lane ^ rows_swz(row)) * 8, D, a.rope, (double)(kc < bhi ? kc : blo));
         }
         *reinterpret_cast<uint4*>(rowp) = BF16::pack(f);
       }
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       float o4[4] = {O[db][0] * w, O[db][1] * w, O[db][2] * w, O[db][3] * w};
-      if (a.rope) rope_turn<4>(o4, 16 * db + 4 * g, D, a.rope, a.rope_base, -(double)a.q_pos[r]);
+      if (ROPE) rope_turn<4>(o4, 16 * db + 4 * g, D, a.rope, -(double)a.q_pos[r]);
       uint2 pk;
       pk.x = pack_bf16x2(o4[0], o4[1]);
       pk.y = pack_bf16x2(o4[2], o4[3]);
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
     float o4[4] = {O[db][0] * w, O[db][1] * w, O[db][2] * w, O[db][3] * w};
     // the turn back by the query position (it commutes with the merge, a sum
     // of partials scaled by the same query's weights)
-    if (a.rope) rope_turn<4>(o4, 16 * db + 4 * g, D, a.rope, a.rope_base, -(double)a.q_pos[r]);
+    if (ROPE) rope_turn<4>(o4, 16 * db + 4 * g, D, a.rope, -(double)a.q_pos[r]);
     *reinterpret_cast<float4*>(op + db * 16) = make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   if (g == 0) S.lse[orow] = lsum > 0.f ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
@@ -414,13 +419,13 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
 // The rotary turn of the lane's DPL dims (dims lane*DPL ..); with one dim per
 // lane the pair (2i, 2i+1) spans lanes 2i and 2i+1 (every lane active).
 template <int DPL>
-__device__ __forceinline__ void valu_turn(float (&v)[DPL], int lane, int D, int rope, float base, double pos) {
+__device__ __forceinline__ void valu_turn(float (&v)[DPL], int lane, int D, const RopeTab& rope, double pos) {
   if constexpr (DPL >= 2) {
-    rope_turn<DPL>(v, lane * DPL, D, rope, base, pos);
+    rope_turn<DPL>(v, lane * DPL, D, rope, pos);
   } else {
     const float other = __shfl_xor(v[0], 1, 64);
     float pr[2] = {(lane & 1) ? other : v[0], (lane & 1) ? v[0] : other};
-    rope_turn<2>(pr, lane & ~1, D, rope, base, pos);
+    rope_turn<2>(pr, lane & ~1, D, rope, pos);
     v[0] = (lane & 1) ? pr[1] : pr[0];
   }
 }
@@ -436,8 +441,8 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
   int64_t first, nseq;
   const int64_t n = attn_keys(a, S, r, &first, &nseq);
   // positions for the rotary embedding: the query's, and the window's first token
-  const double qpos = a.rope ? (double)a.q_pos[r] : 0.0;
-  const int64_t kpos0 = (a.rope && S.kind == SRC_WINDOW) ? first - S.off[r / a.Tq] : 0;
+  const double qpos = a.rope.dims ? (double)a.q_pos[r] : 0.0;
+  const int64_t kpos0 = (a.rope.dims && S.kind == SRC_WINDOW) ? first - S.off[r / a.Tq] : 0;
   const int64_t per = S.tps > 0 ? (int64_t)S.tps * 32 : (n + S.n_split - 1) / S.n_split;
   const int64_t kb = (int64_t)split * per;
   const int64_t ke = (S.tps > 0 && split == S.n_split - 1) ? n : min(n, kb + per);
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
     const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
     for (int i = 0; i < DPL; ++i) qh[i] *= inv;
-    if (a.rope) valu_turn<DPL>(qh, lane, D, a.rope, a.rope_base, qpos);
+    if (a.rope.dims) valu_turn<DPL>(qh, lane, D, a.rope, qpos);
 #pragma unroll
     for (int i = 0; i < DPL; ++i) qh[i] = ET::round(qh[i]);
   }
@@ -465,22 +470,34 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
   for (int64_t t = kb; t < ke; ++t) {
     const int64_t row = attn_row(S, r, first, nseq, t);
     if (row < 0) continue;
-    float kv[DPL];
-    float dot = 0.f, ss = 0.f;
+    // a key row (and the value row beside it, with separate values); raw
+    // window rows are normalised, turned and rounded on load
+    auto fetch = [&](const void* base, float (&x)[DPL]) {
+      float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      kv[i] = ET::load1(S.kv, row * D + lane * DPL + i);
-      ss = fmaf(kv[i], kv[i], ss);
+      for (int i = 0; i < DPL; ++i) {
+        x[i] = ET::load1(base, row * D + lane * DPL + i);
+        ss = fmaf(x[i], x[i], ss);
+      }
+      if (S.kind == SRC_WINDOW) {
+        ss = wave_sum(ss, 64);
+        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) x[i] *= inv;
+        if (a.rope.dims) valu_turn<DPL>(x, lane, D, a.rope, (double)(kpos0 + t));
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) x[i] = ET::round(x[i]);
+      }
+    };
+    float kv[DPL], vv[DPL];
+    fetch(S.kv, kv);
+    if (S.v) {
+      fetch(S.v, vv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) vv[i] = kv[i];
     }
-    if (S.kind == SRC_WINDOW) {
-      ss = wave_sum(ss, 64);
-      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) kv[i] *= inv;
-      if (a.rope) valu_turn<DPL>(kv, lane, D, a.rope, a.rope_base, (double)(kpos0 + t));
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) kv[i] = ET::round(kv[i]);
-    }
+    float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) dot = fmaf(qh[i], kv[i], dot);
     dot = wave_sum(dot, 64) * a.scale;
@@ -490,13 +507,13 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
     l_run = l_run * alpha + p;
     m_run = m_new;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) o[i] = fmaf(o[i], alpha, p * kv[i]);
+    for (int i = 0; i < DPL; ++i) o[i] = fmaf(o[i], alpha, p * vv[i]);
   }
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
   float* op = S.o_part + (((int64_t)split * a.rows + r) * a.H + h) * D;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[i] *= inv;
-  if (a.rope) valu_turn<DPL>(o, lane, D, a.rope, a.rope_base, -qpos);  // -i on the output
+  if (a.rope.dims) valu_turn<DPL>(o, lane, D, a.rope, -qpos);  // -i on the output
 #pragma unroll
   for (int i = 0; i < DPL; ++i) op[lane * DPL + i] = o[i];
   if (lane == 0) S.lse[((int64_t)split * a.rows + r) * a.H + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
@@ -722,29 +739,37 @@ int launch_topk_filter(const int64_t* csa_off, const int32_t* q_pos, int B, int 
 int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int Tq, int k, int m, int w,
                        int64_t maxN, int32_t* idx, const float* scores, void* ws, hipStream_t stream);
 
-// Blocks of attn_mfma<D, true, fc> the current device holds at once
+// Blocks of attn_mfma<D, true, fc, opt> the current device holds at once
 // (compute units x blocks per unit, from the occupancy query on the idle
-// device), queried once per device, D and fc (2 is built for D = 512 only).
+// device), queried once per device, D, fc (2 is built for D = 512 without
+// the options only) and opt.
 // The cache is read and written atomically: concurrent first calls may both
 // query, and both store the same value.  Residency is what lets the sparse
 // blocks wait for each other; it is not guaranteed while other work holds
 // compute units, which is why their wait is bounded (and falls back to an
 // exact selection of its own).
-static int64_t resident_blocks(int D, int fc) {
-  static std::atomic<int64_t> cache[64][4][2];
+static int64_t resident_blocks(int D, int fc, bool opt) {
+  static std::atomic<int64_t> cache[64][4][3];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int di = D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : 3;
-  const int fi = fc == 2 && D == 512 ? 1 : 0;
+  const int fi = opt ? 2 : (fc == 2 && D == 512 ? 1 : 0);
   int64_t v = cache[dev][di][fi].load(std::memory_order_relaxed);
   if (v == 0) {
     int cus = 0, per = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const void* fn = D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true>)
-                     : D == 128 ? reinterpret_cast<const void*>(&attn_mfma<128, true>)
-                     : D == 256 ? reinterpret_cast<const void*>(&attn_mfma<256, true>)
-                     : fi       ? reinterpret_cast<const void*>(&attn_mfma<512, true, 2>)
-                                : reinterpret_cast<const void*>(&attn_mfma<512, true>);
+    const void* fn;
+    if (opt)
+      fn = D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true, 1, true>)
+           : D == 128 ? reinterpret_cast<const void*>(&attn_mfma<128, true, 1, true>)
+           : D == 256 ? reinterpret_cast<const void*>(&attn_mfma<256, true, 1, true>)
+                      : reinterpret_cast<const void*>(&attn_mfma<512, true, 1, true>);
+    else
+      fn = D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true>)
+           : D == 128 ? reinterpret_cast<const void*>(&attn_mfma<128, true>)
+           : D == 256 ? reinterpret_cast<const void*>(&attn_mfma<256, true>)
+           : fi       ? reinterpret_cast<const void*>(&attn_mfma<512, true, 2>)
+                      : reinterpret_cast<const void*>(&attn_mfma<512, true>);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kAttnThreads, 0);
     v = (e == hipSuccess && cus > 0 && per > 0) ? (int64_t)cus * per : -1;
     cache[dev][di][fi].store(v, std::memory_order_relaxed);
@@ -814,6 +839,7 @@ static bool rows_launch(const lca_attn_source* srcs, int n_src, int Tq, int H, i
     return false;
   for (int i = 0; i < n_src; ++i) {
     const lca_attn_source& in = srcs[i];
+    if (in.v) return false;  // separate values: the per-row kernel
     if (in.kind == SRC_GATHER || in.kind == SRC_TOPK) {
       if (kRowsBlockRows / H > kRowsStreams) return false;
       if ((int64_t)((in.k + kRowsTile - 1) / kRowsTile + in.n_split - 1) / in.n_split * kRowsTile > kRowsIdx)
@@ -838,7 +864,7 @@ static int launch_attention_impl(const lca_attn_source* srcs, int n_src, const v
   AttnParams a{};
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
-  a.rope = srcs[0].rope_dims; a.rope_base = srcs[0].rope_base;
+  a.rope = make_rope_tab(srcs[0].rope_dims, srcs[0].rope_base);
   apply_diag(&a);
   int splits = 0, topk = -1;
   for (int i = 0; i < n_src; ++i) {
@@ -846,7 +872,7 @@ static int launch_attention_impl(const lca_attn_source* srcs, int n_src, const v
     AttnSrc& d = a.s[i];
     d.kv = in.kv; d.off = in.off; d.idx = in.idx; d.kind = in.kind; d.k = in.k; d.m2 = in.m2; d.w2 = in.w2;
     d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
-    d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split;
+    d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split; d.v = in.v;
     d.block_begin = splits;
     splits += in.n_split;
     if (in.kind == SRC_TOPK) {
@@ -876,10 +902,14 @@ static int launch_attention_impl(const lca_attn_source* srcs, int n_src, const v
                                       in.ws, stream);
     if (rc != LCA_OK) return rc;
   }
-  if (a.merge)
-    hipLaunchKernelGGL(attn_rows_mfma<true>, dim3((unsigned)nblk), dim3(kRowsThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_rows_mfma<false>, dim3((unsigned)nblk), dim3(kRowsThreads), 0, stream, a);
+  const dim3 grid((unsigned)nblk), block(kRowsThreads);
+  if (a.rope.dims) {
+    if (a.merge) hipLaunchKernelGGL((attn_rows_mfma<true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_rows_mfma<false, true>), grid, block, 0, stream, a);
+  } else {
+    if (a.merge) hipLaunchKernelGGL((attn_rows_mfma<true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_rows_mfma<false, false>), grid, block, 0, stream, a);
+  }
   if (hipPeekAtLastError() != hipSuccess) return LCA_ERR_HIP;
   return (mr && !a.merge) ? merge_sources(srcs, n_src, B * Tq, H, D, mr, dtype, stream) : LCA_OK;
 }
@@ -905,18 +935,20 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
   AttnParams a{};
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
-  a.rope = srcs[0].rope_dims; a.rope_base = srcs[0].rope_base;
+  a.rope = make_rope_tab(srcs[0].rope_dims, srcs[0].rope_base);
   apply_diag(&a);
   const bool mfma = dtype == LCA_BF16 && H % 16 == 0;
   int blocks = 0;
   int topk = -1;          // the TOPK source
   bool fused_topk = false;  // selected inside the attention blocks
+  bool opt = a.rope.dims > 0;  // a rotary embedding, or a source with separate values
   for (int i = 0; i < n_src; ++i) {
     const lca_attn_source& in = srcs[i];
     AttnSrc& d = a.s[i];
     d.kv = in.kv; d.off = in.off; d.idx = in.idx; d.kind = in.kind; d.k = in.k; d.m2 = in.m2; d.w2 = in.w2;
     d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
-    d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split;
+    d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split; d.v = in.v;
+    opt = opt || in.v != nullptr;
     d.block_begin = blocks;
     blocks += in.n_split;
     if (in.kind == SRC_TOPK) {
@@ -970,8 +1002,8 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
       a.tbpr = in.n_split * a.n_hb;
       // two chunks per sparse block at once when the row's scores give a
       // block more than one
-      fc = D == 512 && (int64_t)a.tbpr * kAttnThreads * kFilterPer < in.max_entries ? 2 : 1;
-      a.filter = nblk <= resident_blocks(D, fc) ? 1 : 0;
+      fc = !opt && D == 512 && (int64_t)a.tbpr * kAttnThreads * kFilterPer < in.max_entries ? 2 : 1;
+      a.filter = nblk <= resident_blocks(D, fc, opt) ? 1 : 0;
       if (!a.filter)
         rc = launch_topk_filter(in.off, q_pos, B, Tq, in.k, in.m2, in.w2, in.max_entries, in.scores, in.ws, stream);
     } else {
@@ -983,9 +1015,17 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
   if (mfma) {
     const int64_t units = (int64_t)rows * blocks;
     dim3 grid((unsigned)((units + 7) / 8 * 8 * a.n_hb));
-#define LCA_MFMA(DD)                                                                                      \
-  if (fused_topk) hipLaunchKernelGGL((attn_mfma<DD, true>), grid, dim3(kAttnThreads), 0, stream, a);       \
-  else hipLaunchKernelGGL((attn_mfma<DD, false>), grid, dim3(kAttnThreads), 0, stream, a);
+#define LCA_MFMA(DD)                                                                                       \
+  if (opt) {                                                                                               \
+    if (fused_topk)                                                                                        \
+      hipLaunchKernelGGL((attn_mfma<DD, true, 1, true>), grid, dim3(kAttnThreads), 0, stream, a);          \
+    else                                                                                                   \
+      hipLaunchKernelGGL((attn_mfma<DD, false, 1, true>), grid, dim3(kAttnThreads), 0, stream, a);         \
+  } else if (fused_topk) {                                                                                 \
+    hipLaunchKernelGGL((attn_mfma<DD, true>), grid, dim3(kAttnThreads), 0, stream, a);                     \
+  } else {                                                                                                 \
+    hipLaunchKernelGGL((attn_mfma<DD, false>), grid, dim3(kAttnThreads), 0, stream, a);                    \
+  }
     switch (D) {
       case 64: LCA_MFMA(64) break;
       case 128: LCA_MFMA(128) break;
@@ -1025,7 +1065,7 @@ int setup_attention_front(const lca_attn_source* srcs, int n_src, const void* q,
   *a = AttnParams{};
   a->q = q; a->q_pos = q_pos; a->Tq = Tq; a->H = H; a->D = D; a->rows = B * Tq;
   a->scale = scale; a->eps = eps; a->n_src = n_src;
-  a->rope = srcs[0].rope_dims; a->rope_base = srcs[0].rope_base;
+  a->rope = make_rope_tab(srcs[0].rope_dims, srcs[0].rope_base);
   apply_diag(a);
   int blocks = 0;
   for (int i = 0; i < n_src; ++i) {
@@ -1034,7 +1074,7 @@ int setup_attention_front(const lca_attn_source* srcs, int n_src, const void* q,
     AttnSrc& d = a->s[i];
     d.kv = in.kv; d.off = in.off; d.idx = nullptr; d.kind = in.kind; d.k = 0; d.m2 = in.m2; d.w2 = in.w2;
     d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
-    d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split;
+    d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split; d.v = nullptr;
     d.block_begin = blocks;
     blocks += in.n_split;
   }

@@ -63,6 +63,7 @@ struct AttnSrc {
   const int64_t* done_len;
   int part;
   int tps;              // > 0: 32-key tiles per split (a fixed partition); 0: from n_split
+  const void* v;        // values, rows laid out as kv; null: the keys are the values
 };
 
 constexpr int kMaxSrc = 3;
@@ -85,11 +86,10 @@ struct AttnParams {
   int merge;
   const float* sink;    // [H] or NULL
   void* out;
-  // the rotary embedding of the call: the last `rope` dims of each head (0:
-  // none); queries turn by their position, window rows by theirs, partials
-  // and outputs by minus the query's
-  int rope;
-  float rope_base;
+  // the rotary embedding of the call: the last rope.dims dims of each head
+  // (0: none); queries turn by their position, window rows by theirs,
+  // partials and outputs by minus the query's
+  RopeTab rope;
   // the in-launch top-k wait: it waits for tbpr + wait_extra filter shares
   // (wait_extra > 0 only as a diagnostic: the wait then always gives up) for
   // at most wait_ticks of the 100 MHz constant clock
@@ -232,7 +232,7 @@ struct AttnLds {
 // grid (1-D, XCD-aware numbering below), lds_raw AttnLds<D, TOPK>::kBytes of
 // LDS.  Called by the attention kernel, and by the decode front launch for
 // its attention blocks.
-template <int D, bool TOPK, int FC = 1>
+template <int D, bool TOPK, int FC = 1, bool OPT = false>
 __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, char* lds_raw) {
   constexpr int DH = D / 2;                 // dims per wave
   constexpr int KS = DH / 32;               // k-steps of the S partial
@@ -346,7 +346,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     }
   }
   // --- the key count and the block's key range
-  const int32_t qpos_r = ((kind != SRC_GATHER || a.rope) && a.q_pos) ? qpos_ld : 0;
+  const int32_t qpos_r = ((kind != SRC_GATHER || (OPT && a.rope.dims)) && a.q_pos) ? qpos_ld : 0;
   const int64_t dlen = (kind == SRC_DENSE && S.part != 0) ? dlen_ld : 0;
   const int64_t nseq = off1 - off0;
   int64_t first = off0;
@@ -383,10 +383,13 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   // --- tile staging (per team): loads are unconditional (invalid keys read a
   // clamped valid row) and zeroed when stored
   uint4 stage[LOADS];
+  uint4 vstage[OPT ? LOADS : 1];    // the value rows beside the keys (separate values)
+  const bool sv = OPT && S.v != nullptr;  // uniform over the block
   uint32_t okbits = 0;
   int64_t stage_t = 0;               // tile index of the staged loads (window rows' positions)
   const int64_t kpos0 = first - off0;  // window: position of key 0 (the window's first token)
   const uint16_t* kvp = reinterpret_cast<const uint16_t*>(S.kv);
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(sv ? S.v : S.kv);
   auto key_ok = [&](int64_t key) -> bool {
     if (key >= n) return false;
     return !gather || sidx[key - kbase] >= 0;
@@ -411,29 +414,36 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       }
       okbits |= (ok ? 1u : 0u) << v;
       stage[v] = *reinterpret_cast<const uint4*>(kvp + (first + off) * D + vec * 8);
+      if constexpr (OPT)
+        if (sv) vstage[v] = *reinterpret_cast<const uint4*>(vp + (first + off) * D + vec * 8);
     }
   };
-  auto store_tile = [&](uint16_t* tile) {
-    if (kind == SRC_WINDOW) {
-      // RMS-normalise each row over D: the VPR lanes holding a row are
-      // consecutive lanes of one wave
+  // raw window rows: RMS-normalised over D (the VPR lanes holding a row are
+  // consecutive lanes of one wave), turned by the token's position, rounded
+  auto norm_rows = [&](uint4 (&rows)[LOADS]) {
 #pragma unroll
-      for (int v = 0; v < LOADS; ++v) {
-        float f[8];
-        BF16::unpack(stage[v], f);
-        float ss = 0.f;
+    for (int v = 0; v < LOADS; ++v) {
+      float f[8];
+      BF16::unpack(rows[v], f);
+      float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-        ss = lane_group_sum<VPR>(ss);
-        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
+      for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+      ss = lane_group_sum<VPR>(ss);
+      const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] *= inv;
-        if (a.rope) {
-          const int id = tt + kTeamThreads * v;
-          rope_turn<8>(f, (id % VPR) * 8, D, a.rope, a.rope_base, (double)(kpos0 + stage_t * kTile + id / VPR));
-        }
-        stage[v] = BF16::pack(f);
+      for (int e = 0; e < 8; ++e) f[e] *= inv;
+      if (OPT && a.rope.dims) {
+        const int id = tt + kTeamThreads * v;
+        rope_turn<8>(f, (id % VPR) * 8, D, a.rope, (double)(kpos0 + stage_t * kTile + id / VPR));
       }
+      rows[v] = BF16::pack(f);
+    }
+  };
+  auto store_tile = [&](uint16_t* tile, uint16_t* vtile) {
+    if (kind == SRC_WINDOW) {
+      norm_rows(stage);
+      if constexpr (OPT)
+        if (sv) norm_rows(vstage);
     }
 #pragma unroll
     for (int v = 0; v < LOADS; ++v) {
@@ -441,6 +451,8 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       const int row = id / VPR, vec = id % VPR;
       const bool ok = (okbits >> v) & 1u;
       *reinterpret_cast<uint4*>(&tile[row * PITCH + vec * 8]) = ok ? stage[v] : make_uint4(0, 0, 0, 0);
+      if constexpr (OPT)
+        if (sv) *reinterpret_cast<uint4*>(&vtile[row * PITCH + vec * 8]) = ok ? vstage[v] : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -579,7 +591,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       BF16::unpack(qraw[ks], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= inv;
-      if (a.rope) rope_turn<8>(f, d0 + ks * 32 + g * 8, D, a.rope, a.rope_base, (double)qpos_r);
+      if (OPT && a.rope.dims) rope_turn<8>(f, d0 + ks * 32 + g * 8, D, a.rope, (double)qpos_r);
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
@@ -594,8 +606,14 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   for (int64_t rd = 0; rd < rounds; ++rd) {
     const int64_t t = tb + 2 * rd + team;   // this team's tile (may be past te)
     const bool active = t < te;
-    uint16_t* tile = tiles[team][rd & 1];
-    store_tile(tile);
+    // keys and values share one tile with one vector per key; separate
+    // values take the team's second buffer, so the tiles are single-buffered
+    // (the register staging still prefetches the next tile) and every wave
+    // leaves the previous round before they are overwritten
+    uint16_t* tile = tiles[team][sv ? 0 : (rd & 1)];
+    uint16_t* vtile = sv ? tiles[team][1] : tile;
+    if (sv && rd > 0) __syncthreads();
+    store_tile(tile, vtile);
     // validity of the tile's 32 keys, one per lane of the low half-wave
     const uint64_t vm = __ballot(lane < kTile && active && key_ok(t * kTile + lane));
     __syncthreads();  // A: tile in LDS
@@ -683,7 +701,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
         // c16 in group g holds entries 4g..4g+3 and 16+4g..16+4g+3 at dim
         // d0 + 16*db + c16: it addresses row 4g + c16/4 (and 16 + ...) at
         // columns d0 + 16*db + 4*(c16%4); the transpose read returns its column.
-        const uint16_t* trow0 = &tile[(4 * g + (c16 >> 2)) * PITCH + d0 + 4 * (c16 & 3)];
+        const uint16_t* trow0 = &vtile[(4 * g + (c16 >> 2)) * PITCH + d0 + 4 * (c16 & 3)];
         const uint16_t* trow1 = trow0 + 16 * PITCH;
         s4_t vbuf[2][OB][2];
 #pragma unroll
@@ -757,7 +775,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     const float4 u = *reinterpret_cast<const float4*>(ox + hh * XP + d);
     const float4 v = *reinterpret_cast<const float4*>(ox + (kAttnHeads + hh) * XP + d);
     float o4[4] = {u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w};
-    if (a.rope) rope_turn<4>(o4, d, D, a.rope, a.rope_base, -(double)qpos_r);  // -i on the output
+    if (OPT && a.rope.dims) rope_turn<4>(o4, d, D, a.rope, -(double)qpos_r);  // -i on the output
     *reinterpret_cast<float4*>(op + (int64_t)i * 4) = make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   if (threadIdx.x < nh) {

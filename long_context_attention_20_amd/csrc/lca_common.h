@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "lca.h"
 
 namespace lca {
@@ -143,28 +145,60 @@ __device__ __host__ __forceinline__ int64_t n_windows(int64_t L, int m, int w) {
 
 // ---------------------------------------------------------------- rotary embedding
 // "DeepSeek-V4" spec sheet, Core block and Provenance 16: partial RoPE on the
-// last dims of a head.  Channels [ch0, ch0 + N) of a C-channel vector (ch0
-// and N even): the last `rope` channels turn pair by pair, pair p (channels
-// C - rope + 2p and the next) as a complex number times exp(i pos theta_p),
-// theta_p = base^(-2p / rope).  The angle is formed and reduced modulo 2 pi
-// in double precision (positions reach 2^20, where a float product would
-// lose most of the angle); its sine and cosine are taken in float.
+// last dims of a head.  The last `dims` channels of a C-channel vector turn
+// pair by pair, pair p (channels C - dims + 2p and the next) as a complex
+// number times exp(i pos theta_p), theta_p = base^(-2p / dims).
+//
+// theta_p is the product of t2k[k] = base^(-2 * 2^k / dims) over the set bits
+// k of p (at most 8 double products, so a few ulp of a double), the angle
+// pos * theta_p is formed and reduced to revolutions in double (positions
+// reach 2^20, where a float product would lose most of the angle), and the
+// sine and cosine of the reduced angle come from Taylor polynomials on a
+// quarter turn (degree 9 and 8: truncation below 3e-8 on |r| <= pi/4), moved
+// to the right quadrant by the usual identities.
+struct RopeTab {
+  int dims;        // rotated channels (0: none)
+  double t2k[8];   // base^(-2 * 2^k / dims)
+};
+
+inline RopeTab make_rope_tab(int dims, float base) {
+  RopeTab t{};
+  t.dims = dims;
+  for (int k = 0; k < 8; ++k) t.t2k[k] = dims > 0 ? std::pow((double)base, -2.0 * (double)(1 << k) / dims) : 0.0;
+  return t;
+}
+
+__device__ __forceinline__ void rope_sincos(double pos, int p, const RopeTab& t, float* sn, float* cs) {
+  double theta = 1.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if ((p >> k) & 1) theta *= t.t2k[k];
+  constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+  double rev = pos * theta * kInvTwoPi;
+  rev -= rint(rev);                                   // [-1/2, 1/2] of a turn
+  const float f = (float)(rev * 4.0);                 // quarter turns, [-2, 2]
+  const float q = rintf(f);
+  const float r = (f - q) * 1.57079632679489661923f;  // [-pi/4, pi/4]
+  const float r2 = r * r;
+  const float s = r * (1.f + r2 * (-1.f / 6 + r2 * (1.f / 120 + r2 * (-1.f / 5040 + r2 * (1.f / 362880)))));
+  const float c = 1.f + r2 * (-0.5f + r2 * (1.f / 24 + r2 * (-1.f / 720 + r2 * (1.f / 40320))));
+  const int qi = (int)q & 3;                          // angle = qi quarter turns + r
+  *sn = qi == 0 ? s : qi == 1 ? c : qi == 2 ? -s : -c;
+  *cs = qi == 0 ? c : qi == 1 ? -s : qi == 2 ? -c : s;
+}
+
+// Channels [ch0, ch0 + N) of a C-channel vector (ch0 and N even), turned by
+// the angles of position pos.
 template <int N>
-__device__ __forceinline__ void rope_turn(float (&v)[N], int ch0, int C, int rope, float base, double pos) {
+__device__ __forceinline__ void rope_turn(float (&v)[N], int ch0, int C, const RopeTab& t, double pos) {
   static_assert(N % 2 == 0, "pairs");
-  const int lo = C - rope;
-  const double l2b = log2((double)base);
+  const int lo = C - t.dims;
 #pragma unroll
   for (int k = 0; k < N; k += 2) {
     const int c = ch0 + k;
-    if (rope > 0 && c >= lo) {
-      const int p = (c - lo) >> 1;
-      const double theta = exp2(-(double)(2 * p) / (double)rope * l2b);
-      double a = pos * theta;
-      constexpr double kTwoPi = 6.283185307179586476925286766559;
-      a -= kTwoPi * floor(a / kTwoPi);
+    if (t.dims > 0 && c >= lo) {
       float sn, cs;
-      sincosf((float)a, &sn, &cs);
+      rope_sincos(pos, (c - lo) >> 1, t, &sn, &cs);
       const float x0 = v[k], x1 = v[k + 1];
       v[k] = x0 * cs - x1 * sn;
       v[k + 1] = x0 * sn + x1 * cs;

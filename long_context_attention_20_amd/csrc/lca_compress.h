@@ -22,8 +22,9 @@ struct CompressStreamDev {
   void* out;
   const int64_t* ent_off;
   int C, m, w, per_channel, rmsnorm, max_entries;
-  int rope;     // rotated channels at the end of an entry (0: none); entry j turns by j*m + w - 1
-  float rope_base;
+  RopeTab rope;  // rotated channels at the end of an entry (rope.dims, 0: none); entry j turns by j*m + w - 1
+  const void* src2;     // dual-stream form (w = 2m): a window's last m tokens from src2 / logits2, or null
+  const void* logits2;
   int key;      // key rows: 1 fp8 (C E4M3 bytes, fp32 scale, 4 zero bytes), 2 MXFP4 (C/2 bytes of E2M1
                 // pairs, one E8M0 scale per 32 channels, zero pad to C/2 + 8); one lane group per row, NV = 1
   int G;        // lanes per row
@@ -209,9 +210,9 @@ __device__ __forceinline__ void finish_entry(const CompressStreamDev& s, float e
 #pragma unroll
       for (int k = 0; k < VE; ++k) e[v][k] *= inv;
   }
-  if (s.rope)  // after the norm, before the rounding; entry j sits at the last token of its window
+  if (s.rope.dims)  // after the norm, before the rounding; entry j sits at the last token of its window
 #pragma unroll
-    for (int v = 0; v < NV; ++v) rope_turn<VE>(e[v], ch0[v], s.C, s.rope, s.rope_base, (double)(j * s.m + s.w - 1));
+    for (int v = 0; v < NV; ++v) rope_turn<VE>(e[v], ch0[v], s.C, s.rope, (double)(j * s.m + s.w - 1));
   if (s.key == 2) {
     if constexpr (VE == 8) {
       char* row = reinterpret_cast<char*>(s.out) + out_row * (int64_t)(s.C / 2 + 8);
@@ -276,7 +277,7 @@ __device__ void compress_small(const CompressStreamDev& s, const CompressParams&
   const bool two = (s.w == 2 * s.m);
 
   PoolState<VE> prev[NV], cur[NV];
-  if constexpr (NV == 1 && PF) if (m <= kPrefetchM) {
+  if constexpr (NV == 1 && PF) if (m <= kPrefetchM && !s.src2) {
     // raw rows of the next segment are requested before the current one is
     // pooled, so a run costs one memory round trip per segment at most and a
     // single entry (decode append) costs one in all
@@ -345,7 +346,7 @@ __device__ void compress_small(const CompressStreamDev& s, const CompressParams&
     }
     return;
   }
-  auto segment = [&](int64_t q, PoolState<VE>(&st)[NV]) {
+  auto segment = [&](int64_t q, PoolState<VE>(&st)[NV], const RowCtx<ET, NV>& r) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) st[v].reset();
     const int64_t tb = q * m;
@@ -353,7 +354,7 @@ __device__ void compress_small(const CompressStreamDev& s, const CompressParams&
     for (; t + 4 <= m; t += 4) {
       float x[4][NV][VE], z[4][NV][VE];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) rc.load(tb + t + u, x[u], z[u]);
+      for (int u = 0; u < 4; ++u) r.load(tb + t + u, x[u], z[u]);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -361,22 +362,38 @@ __device__ void compress_small(const CompressStreamDev& s, const CompressParams&
     }
     for (; t < m; ++t) {
       float x[NV][VE], z[NV][VE];
-      rc.load(tb + t, x, z);
+      r.load(tb + t, x, z);
 #pragma unroll
       for (int v = 0; v < NV; ++v) st[v].add(z[v], x[v]);
     }
   };
 
-  if (two) segment(j0, prev);
+  if (s.src2) {
+    // dual-stream form (w = 2m): entry j merges segment j of the first
+    // stream with segment j + 1 of the second, so each segment is pooled
+    // once per stream
+    RowCtx<ET, NV> rc2 = rc;
+    rc2.src = reinterpret_cast<const char*>(s.src2) + t0 * rc.row_bytes;
+    rc2.lg = reinterpret_cast<const char*>(s.logits2) + (s.per_channel ? t0 * rc.row_bytes : t0 * ET::kBytes);
+    for (int64_t j = j0; j < j1; ++j) {
+      segment(j, prev, rc);
+      segment(j + 1, cur, rc2);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) prev[v].merge(cur[v]);
+      finish_entry<ET, NV>(s, P.eps, G, prev, rc.ch0, ent_base + j, true, j);
+    }
+    return;
+  }
+  if (two) segment(j0, prev, rc);
   for (int64_t j = j0; j < j1; ++j) {
     if (two) {
-      segment(j + 1, cur);
+      segment(j + 1, cur, rc);
       PoolState<VE> e[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) { e[v] = prev[v]; e[v].merge(cur[v]); prev[v] = cur[v]; }
       finish_entry<ET, NV>(s, P.eps, G, e, rc.ch0, ent_base + j, true, j);
     } else {
-      segment(j, cur);
+      segment(j, cur, rc);
       finish_entry<ET, NV>(s, P.eps, G, cur, rc.ch0, ent_base + j, true, j);
     }
   }
@@ -504,9 +521,9 @@ __device__ void compress_large(const CompressStreamDev& s, const CompressParams&
 #pragma unroll
       for (int k = 0; k < VE; ++k) e[v][k] *= inv;
   }
-  if (s.rope)
+  if (s.rope.dims)
 #pragma unroll
-    for (int v = 0; v < NV; ++v) rope_turn<VE>(e[v], rc.ch0[v], C, s.rope, s.rope_base, (double)(j * s.m + s.w - 1));
+    for (int v = 0; v < NV; ++v) rope_turn<VE>(e[v], rc.ch0[v], C, s.rope, (double)(j * s.m + s.w - 1));
   const int64_t rb = (int64_t)C * ET::kBytes;
   const int64_t out_row = s.ent_off[b] + j;
 #pragma unroll

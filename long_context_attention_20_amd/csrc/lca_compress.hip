@@ -56,8 +56,9 @@ int setup_compress(const lca_compress_stream* streams, int n, const int64_t* tok
     d.C = in.C; d.m = in.m; d.w = in.w; d.per_channel = in.per_channel; d.rmsnorm = in.rmsnorm;
     d.max_entries = in.max_entries;
     d.key = in.out_key;
-    d.rope = in.rope_dims;
-    d.rope_base = in.rope_base;
+    d.rope = make_rope_tab(in.rope_dims, in.rope_base);
+    d.src2 = in.src2;
+    d.logits2 = in.logits2;
     const int lanes = in.C / VE;
     d.G = lanes < 64 ? lanes : 64;
     d.NV = lanes < 64 ? 1 : lanes / 64;

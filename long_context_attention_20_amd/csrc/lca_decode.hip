@@ -98,7 +98,11 @@ int launch_decode_front(const void* p, const float* omega, const void* ikey, con
   AttnParams a;
   int64_t n_attn = 0;
   int rc = LCA_ERR_UNSUPPORTED;
-  if (dI == 64 && index_append_fusable(dtype, Tq, HI, dI, m, w, idx_stream) && (dtype != LCA_F32))
+  // (the front's attention blocks are the plain ones: a rotary embedding or
+  // separate values take the two launches)
+  bool plain = true;
+  for (int i = 0; i < n_src; ++i) plain = plain && srcs[i].rope_dims == 0 && srcs[i].v == nullptr;
+  if (plain && dI == 64 && index_append_fusable(dtype, Tq, HI, dI, m, w, idx_stream) && (dtype != LCA_F32))
     rc = setup_attention_front(srcs, n_src, q, q_pos, B, Tq, H, D, scale, eps, &a, &n_attn);
   FrontParams f{};
   size_t lds = 0;

@@ -611,7 +611,9 @@ static void fill_append_params(const void* p, const float* omega, const void* ik
   ap->s.src = in.src; ap->s.logits = in.logits; ap->s.out = in.out; ap->s.ent_off = in.ent_off;
   ap->s.C = in.C; ap->s.m = in.m; ap->s.w = in.w; ap->s.per_channel = in.per_channel; ap->s.rmsnorm = in.rmsnorm;
   ap->s.key = in.out_key;
-  ap->s.rope = 0;  // indexer keys are not rotated (the call rejects a rotated indexer stream)
+  ap->s.rope = RopeTab{};  // indexer keys are not rotated (the call rejects a rotated indexer stream)
+  ap->s.src2 = in.src2;
+  ap->s.logits2 = in.logits2;
   ap->s.max_entries = in.max_entries;
   ap->tok_off = tok_off;
   ap->done_len = done_len;

@@ -401,6 +401,9 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
   const int64_t rb = (int64_t)s.C * 2;
   const char* src = reinterpret_cast<const char*>(s.src) + t0 * rb;
   const char* lg = reinterpret_cast<const char*>(s.logits) + (s.per_channel ? t0 * rb : t0 * 2);
+  // the dual-stream form reads a window's second half from the second stream
+  const char* src2 = s.src2 ? reinterpret_cast<const char*>(s.src2) + t0 * rb : src;
+  const char* lg2 = s.src2 ? reinterpret_cast<const char*>(s.logits2) + (s.per_channel ? t0 * rb : t0 * 2) : lg;
   const int ch0 = li * VE;
   for (int64_t j0 = n_lo; j0 < n_hi; j0 += RG) {
     const int64_t j = j0 + rg;
@@ -415,13 +418,15 @@ __device__ void append_and_score(const IndexParams& a, const AppendIdx& ap, int 
     for (int q = 0; q < 2; ++q) {
       st[q].reset();
       if (q >= nseg) continue;
+      const char* sq = q ? src2 : src;
+      const char* lq = q ? lg2 : lg;
       for (int t = q * s.m; t < (q + 1) * s.m; ++t) {
         float x[VE], z[VE];
-        BF16::unpack(ldg16(src, (tb + t) * rb + ch0 * 2), x);
+        BF16::unpack(ldg16(sq, (tb + t) * rb + ch0 * 2), x);
         if (s.per_channel) {
-          BF16::unpack(ldg16(lg, (tb + t) * rb + ch0 * 2), z);
+          BF16::unpack(ldg16(lq, (tb + t) * rb + ch0 * 2), z);
         } else {
-          const float zs = BF16::load1(lg, tb + t);
+          const float zs = BF16::load1(lq, tb + t);
 #pragma unroll
           for (int e = 0; e < VE; ++e) z[e] = zs;
         }

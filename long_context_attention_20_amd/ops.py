@@ -91,9 +91,16 @@ def _stream_array(streams: Sequence[dict]):
         if d != dt or _dtype_code(lg) != d:
             raise TypeError("one element type per call")
         pc = 1 if lg.dim() == 2 else 0
+        src2, lg2 = s.get("src2"), s.get("logits2")
+        if (src2 is None) != (lg2 is None):
+            raise ValueError("src2 and logits2 come together")
+        if src2 is not None:
+            _dev(src2, lg2)
+            if src2.shape != src.shape or lg2.shape != lg.shape or _dtype_code(src2) != d or _dtype_code(lg2) != d:
+                raise TypeError("second-half streams shaped and typed as the first")
         arr[i] = CompressStream(src.data_ptr(), lg.data_ptr(), out.data_ptr(), eo.data_ptr(), C, int(s["m"]),
                                 int(s["w"]), pc, int(s["rmsnorm"]), int(s["max_entries"]), key,
-                                int(s.get("rope", 0)), float(s.get("rope_base", 10000.0)))
+                                int(s.get("rope", 0)), float(s.get("rope_base", 10000.0)), _addr(src2), _addr(lg2))
     return arr, dt
 
 
@@ -319,11 +326,16 @@ def _attn_sources(q, q_pos, sources: Sequence[dict]):
         if part:
             _dev(done_len)
             _i64(done_len, "done_len")
+        v = s.get("v")
+        if v is not None:
+            _dev(v)
+            if v.shape != kv.shape or v.dtype != kv.dtype:
+                raise TypeError("values shaped and typed as the keys")
         arr[i] = AttnSource(kind, kv.data_ptr(), off.data_ptr(), None if idx is None else idx.data_ptr(), k,
                             int(s.get("m2", 1)), int(s.get("w2", 1)), int(s.get("W", 0)), ns, o_part.data_ptr(),
                             lse.data_ptr(), _addr(ws), ws_bytes or 0, max_entries or 0, _addr(scores), _addr(idx_out),
                             _addr(done_len) if part else None, part, int(s.get("rope", 0)),
-                            float(s.get("rope_base", 10000.0)), int(s.get("tiles_per_split", 0)))
+                            float(s.get("rope_base", 10000.0)), int(s.get("tiles_per_split", 0)), _addr(v))
         outs.append((o_part, lse))
     return arr, outs, B
 

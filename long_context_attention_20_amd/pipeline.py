@@ -42,6 +42,8 @@ class Caches:
     kv_hca: torch.Tensor     # [sum N_hca, D]
     csa_off_h: np.ndarray
     hca_off_h: np.ndarray
+    v_csa: Optional[torch.Tensor] = None   # value entries (separate values), rows as kv_csa
+    v_hca: Optional[torch.Tensor] = None
 
 
 def _offsets(counts) -> np.ndarray:
@@ -54,7 +56,7 @@ class HybridAttention:
     def __init__(self, H: int, D: int, HI: int, dI: int, k: int, m: int = 4, w: int = 8, m2: int = 128,
                  w2: int = 128, W: int = 128, eps: float = 1e-6, scale: Optional[float] = None,
                  split_csa: Optional[int] = None, split_hca: Optional[int] = None, ikey: str = "bf16",
-                 rope: int = 0, rope_base: float = 10000.0):
+                 rope: int = 0, rope_base: float = 10000.0, dual: bool = False, sepv: bool = False):
         self.H, self.D, self.HI, self.dI, self.k = H, D, HI, dI, k
         # partial rotary embedding on the last `rope` dims of each head (0:
         # none): compressed entries are stored turned by the position of
@@ -64,6 +66,14 @@ class HybridAttention:
         if rope < 0 or rope % 2 or rope > D:
             raise ValueError(f"rope: an even number of dims <= D, not {rope}")
         self.rope, self.rope_base = int(rope), float(rope_base)
+        # dual: the CSA windows (KV, values and indexer keys) pool their last
+        # m tokens from second-half streams (raw inputs x_b, a_b, u_b, c_b,
+        # and v_b with separate values); needs w = 2m.  sepv: values from
+        # the raw stream v, pooled with the keys' logits (value caches
+        # v_csa, v_hca), the window's values the raw v tokens
+        if dual and w != 2 * m:
+            raise ValueError("the dual-stream compressor needs w = 2m")
+        self.dual, self.sepv = bool(dual), bool(sepv)
         # indexer-key cache: rows of the inputs' type ("bf16"), fp8 rows (d_I
         # E4M3 bytes, fp32 scale, 4 zero bytes) or MXFP4 rows (d_I/2 bytes of
         # E2M1 pairs, one E8M0 scale per 32 channels, zero pad to d_I/2 + 8)
@@ -97,7 +107,20 @@ class HybridAttention:
                               dtype=torch.uint8, device=device) if self.ikey_code
                   else torch.empty((max(1, int(co[-1])), self.dI), dtype=dtype, device=device)),
             kv_hca=torch.empty((max(1, int(ho[-1])), self.D), dtype=dtype, device=device),
-            csa_off_h=co, hca_off_h=ho)
+            csa_off_h=co, hca_off_h=ho,
+            v_csa=torch.empty((max(1, int(co[-1])), self.D), dtype=dtype, device=device) if self.sepv else None,
+            v_hca=torch.empty((max(1, int(ho[-1])), self.D), dtype=dtype, device=device) if self.sepv else None)
+
+    def _values(self, srcs, caches: Caches, v: Optional[torch.Tensor]):
+        """Attention sources with their value rows (separate values): the
+        value caches beside the CSA and HCA entries, the raw value tokens
+        beside the window's."""
+        if self.sepv:
+            if v is None:
+                raise ValueError("separate values: the raw value tokens v are required")
+            for d in srcs:
+                d["v"] = {"topk": caches.v_csa, "gather": caches.v_csa, "dense": caches.v_hca, "window": v}[d["kind"]]
+        return srcs
 
     def _turn(self, d: dict) -> dict:
         """A compression stream or attention source with the layer's rotary
@@ -115,17 +138,37 @@ class HybridAttention:
         lens = caches.lens if lens_h is None else lens_h
         new_csa = max(n_windows(L, self.m, self.w) - n_windows(d, self.m, self.w) for L, d in zip(lens, done_h))
         new_hca = max(n_windows(L, self.m2, self.w2) - n_windows(d, self.m2, self.w2) for L, d in zip(lens, done_h))
+        sec = (lambda s, z: dict(src2=raw[s], logits2=raw[z])) if self.dual else (lambda s, z: {})  # noqa: E731
         streams = []
         if new_csa > 0 and "csa" in which:
             streams.append(self._turn(dict(src=raw["x"], logits=raw["a"], out=caches.kv_csa, ent_off=caches.csa_off,
-                                           m=self.m, w=self.w, rmsnorm=1, max_entries=new_csa)))
+                                           m=self.m, w=self.w, rmsnorm=1, max_entries=new_csa, **sec("x_b", "a_b"))))
+            if self.sepv:
+                streams.append(self._turn(dict(src=raw["v"], logits=raw["a"], out=caches.v_csa,
+                                               ent_off=caches.csa_off, m=self.m, w=self.w, rmsnorm=1,
+                                               max_entries=new_csa, **sec("v_b", "a_b"))))
         if new_csa > 0 and "idx" in which:
             streams.append(dict(src=raw["u"], logits=raw["c"], out=caches.ikey, ent_off=caches.csa_off,
-                                m=self.m, w=self.w, rmsnorm=0, max_entries=new_csa, key=self.ikey_code))
+                                m=self.m, w=self.w, rmsnorm=0, max_entries=new_csa, key=self.ikey_code,
+                                **sec("u_b", "c_b")))
         if new_hca > 0 and "hca" in which:
             streams.append(self._turn(dict(src=raw["x"], logits=raw["g"], out=caches.kv_hca, ent_off=caches.hca_off,
                                            m=self.m2, w=self.w2, rmsnorm=1, max_entries=new_hca)))
+            if self.sepv:
+                streams.append(self._turn(dict(src=raw["v"], logits=raw["g"], out=caches.v_hca,
+                                               ent_off=caches.hca_off, m=self.m2, w=self.w2, rmsnorm=1,
+                                               max_entries=new_hca)))
         return streams
+
+    @staticmethod
+    def _launch_groups(streams):
+        """The streams as kv_compress calls: one vector width and at most four
+        streams per call."""
+        groups: Dict[int, list] = {}
+        for s in streams:
+            lanes = s["src"].shape[-1] // (8 if s["src"].dtype == torch.bfloat16 else 4)
+            groups.setdefault(1 if lanes <= 64 else lanes // 64, []).append(s)
+        return [g[i:i + 4] for g in groups.values() for i in range(0, len(g), 4)]
 
     def compress(self, caches: Caches, raw: dict, tok_off: torch.Tensor,
                  done_len: Optional[torch.Tensor] = None, done_len_h: Optional[Sequence[int]] = None,
@@ -134,12 +177,7 @@ class HybridAttention:
         (all of them when done_len is None)."""
         done = [0] * len(caches.lens) if done_len_h is None else [int(v) for v in done_len_h]
         streams = self.compress_streams(caches, raw, done, which)
-        # streams of one launch share the number of 16-byte vectors per lane
-        groups: Dict[int, list] = {}
-        for s in streams:
-            lanes = s["src"].shape[-1] // (8 if s["src"].dtype == torch.bfloat16 else 4)
-            groups.setdefault(1 if lanes <= 64 else lanes // 64, []).append(s)
-        for g in groups.values():
+        for g in self._launch_groups(streams):
             ops.kv_compress(g, tok_off, done_len, self.eps)
 
     def _append(self, caches: Caches, raw: dict, tok_off, done_len, done_h, which=("csa", "idx", "hca"),
@@ -147,11 +185,7 @@ class HybridAttention:
         """Launch the compression of the entries completed after done_h tokens
         (one launch when the streams share a vector width)."""
         streams = self.compress_streams(caches, raw, done_h, which, lens_h)
-        groups: Dict[int, list] = {}
-        for s in streams:
-            lanes = s["src"].shape[-1] // (8 if s["src"].dtype == torch.bfloat16 else 4)
-            groups.setdefault(1 if lanes <= 64 else lanes // 64, []).append(s)
-        for g in groups.values():
+        for g in self._launch_groups(streams):
             ops.kv_compress(g, tok_off, done_len, self.eps)
 
     # -------------------------------------------------------------- indexer, top-k, attention
@@ -203,11 +237,14 @@ class HybridAttention:
 
     def step(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, q: torch.Tensor, p: torch.Tensor,
              omega: torch.Tensor, sigma: Optional[torch.Tensor], q_pos: torch.Tensor, q_pos_h: np.ndarray,
-             mode: str = "A", keep: bool = False):
+             mode: str = "A", keep: bool = False, v: Optional[torch.Tensor] = None):
         """Attention output for every query row (after the caches hold every
         entry the query positions can see).  mode "A": one softmax over the
         selected CSA entries, the visible HCA entries, the window and the sink;
-        "B": returns (csa-layer output, hca-layer output)."""
+        "B": returns (csa-layer output, hca-layer output).  v: the raw value
+        tokens (separate values)."""
+        if self.sepv and v is None:
+            raise ValueError("separate values: pass the raw value tokens v")
         rows = q.shape[0]
         dev = q.device
         qmax = int(np.max(q_pos_h)) + 1
@@ -223,7 +260,7 @@ class HybridAttention:
             # the dense source is always launched (an empty one writes o = 0,
             # lse = -inf), so that the partials are there for every row
             bufs = dict(sc=sc, sh=sh, sw=sw, max_hca=1, csa=(None, None), hca=(None, None), swa=(None, None))
-            srcs = self.attn_sources(caches, x, tok_off, idx, bufs)
+            srcs = self.attn_sources(caches, x, tok_off, idx, bufs, v)
             # attention and merge in one call (one launch when every source
             # has one split); with keep, the partials are computed as well
             out = ops.hybrid_attn_merge(q, q_pos, srcs, sigma, self.scale, self.eps)
@@ -231,15 +268,19 @@ class HybridAttention:
             if keep:
                 parts = ops.hybrid_attn(q, q_pos, srcs, self.scale, self.eps)
                 csa, hca = parts[0], parts[1]
-        elif self.rope:
-            # the per-branch calls take no rotary embedding: each layer is
-            # one merged call over its compressed entries and the window
+        elif self.rope or self.sepv:
+            # the per-branch calls take no rotary embedding and no separate
+            # values: each layer is one merged call over its compressed
+            # entries and the window
             sc = self.split_csa or self.default_splits(rows, self.k)
             sh = self.split_hca or self.default_splits(rows, max_hca)
-            win = [self._turn(dict(kind="window", kv=x, off=tok_off, W=self.W, n_split=1))] if self.W > 0 else []
-            csa_src = self._turn(dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=sc))
+            vals = lambda t: dict(v=t) if self.sepv else {}  # noqa: E731
+            win = ([self._turn(dict(kind="window", kv=x, off=tok_off, W=self.W, n_split=1, **vals(v)))]
+                   if self.W > 0 else [])
+            csa_src = self._turn(dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=sc,
+                                      **vals(caches.v_csa)))
             hca_src = self._turn(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2,
-                                      n_split=sh))
+                                      n_split=sh, **vals(caches.v_hca)))
             o1 = ops.hybrid_attn_merge(q, q_pos, [csa_src] + win, sigma, self.scale, self.eps)
             o2 = ops.hybrid_attn_merge(q, q_pos, [hca_src] + win, sigma, self.scale, self.eps)
             out = (o1, o2)
@@ -311,10 +352,11 @@ class HybridAttention:
             out=torch.empty((rows, self.H, self.D), dtype=dtype, device=device))
 
     def attn_sources(self, caches: Caches, x: torch.Tensor, tok_off: torch.Tensor, idx: Optional[torch.Tensor],
-                     bufs: dict):
+                     bufs: dict, v: Optional[torch.Tensor] = None):
         """The three key sources of the fused attention launch.  idx None: the
         sparse source selects its own entries from the index workspace
-        bufs["ws_idx"] (a TOPK source; the selection lands in bufs["idx"])."""
+        bufs["ws_idx"] (a TOPK source; the selection lands in bufs["idx"]).
+        v: the raw value tokens (separate values)."""
         if idx is None:
             src = [dict(kind="topk", kv=caches.kv_csa, off=caches.csa_off, k=self.k, m2=self.m, w2=self.w,
                         max_entries=bufs["max_csa"], ws=bufs["ws_idx"], idx_out=bufs["idx"], n_split=bufs["sc"],
@@ -328,7 +370,7 @@ class HybridAttention:
         if self.W > 0:
             src.append(dict(kind="window", kv=x, off=tok_off, W=self.W, n_split=bufs["sw"], o_part=bufs["swa"][0],
                             lse=bufs["swa"][1]))
-        return [self._turn(d) for d in src]
+        return [self._turn(d) for d in self._values(src, caches, v)]
 
     def front_calls(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos, bufs: dict,
                     done_len: torch.Tensor, done_h: Sequence[int], lens_h: Optional[Sequence[int]] = None):
@@ -364,8 +406,8 @@ class HybridAttention:
             back.append(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2, part=2,
                              done_len=done_len, n_split=1, o_part=bufs["hca_new"][0], lse=bufs["hca_new"][1]))
             parts.append(bufs["hca_new"])
-        front = [self._turn(d) for d in front]
-        back = [self._turn(d) for d in back]
+        front = [self._turn(d) for d in self._values(front, caches, raw.get("v"))]
+        back = [self._turn(d) for d in self._values(back, caches, raw.get("v"))]
         if not front:  # nothing to attend beside the scores
             f0 = lambda: ops.csa_index_score_append(p, omega, caches.ikey, caches.csa_off, q_pos, self.k, self.m,  # noqa: E731
                                                     self.w, bufs["max_csa"], bufs["ws_idx"], idx_st[0], kv_st,
@@ -436,7 +478,7 @@ class HybridAttention:
                                 idx=bufs["idx"])
         if join is not None:
             main.wait_event(join)
-        srcs = self.attn_sources(caches, raw["x"], tok_off, None if fuse_topk else bufs["idx"], bufs)
+        srcs = self.attn_sources(caches, raw["x"], tok_off, None if fuse_topk else bufs["idx"], bufs, raw.get("v"))
         parts = ops.hybrid_attn(q, q_pos, srcs, self.scale, self.eps)
         ops.swa_merge(q, None, None, None, sigma, parts, 0, self.scale, self.eps, None, out=bufs["out"])
         return bufs["out"]

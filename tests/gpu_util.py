@@ -20,8 +20,9 @@ def tdtype(cfg):
 def to_device(raw, cfg, dev="cuda"):
     dt = tdtype(cfg)
     d = {}
-    for k in ("x", "a", "g", "u", "c", "q", "p"):
-        d[k] = torch.from_numpy(np.ascontiguousarray(raw[k])).to(dev).to(dt)
+    for k in ("x", "a", "g", "u", "c", "q", "p") + opipe.OPTION_STREAMS:
+        if k in raw:
+            d[k] = torch.from_numpy(np.ascontiguousarray(raw[k])).to(dev).to(dt)
     d["omega"] = torch.from_numpy(raw["omega"]).to(dev).contiguous()
     d["sigma"] = torch.from_numpy(raw["sigma"]).to(dev).contiguous()
     d["tok_off"] = torch.from_numpy(raw["tok_off"]).to(dev)
@@ -34,6 +35,8 @@ def layer_for(cfg, **kw):
     kw.setdefault("ikey", getattr(cfg, "ikey", "bf16"))
     kw.setdefault("rope", getattr(cfg, "rope", 0))
     kw.setdefault("rope_base", getattr(cfg, "rope_base", 10000.0))
+    kw.setdefault("dual", getattr(cfg, "dual", False))
+    kw.setdefault("sepv", getattr(cfg, "sepv", False))
     return HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps, **kw)
 
 
@@ -82,8 +85,11 @@ def f64(t):
 
 def seq_caches(caches, b):
     co, ho = caches.csa_off_h, caches.hca_off_h
+    vals = getattr(caches, "v_csa", None) is not None
     return opipe.SeqCaches(f64(caches.kv_csa[co[b]:co[b + 1]]), f64(caches.ikey[co[b]:co[b + 1]]),
-                           f64(caches.kv_hca[ho[b]:ho[b + 1]]))
+                           f64(caches.kv_hca[ho[b]:ho[b + 1]]),
+                           f64(caches.v_csa[co[b]:co[b + 1]]) if vals else None,
+                           f64(caches.v_hca[ho[b]:ho[b + 1]]) if vals else None)
 
 
 def run_gpu(cfg, raw, dev="cuda", mode="A", **kw):
@@ -92,7 +98,7 @@ def run_gpu(cfg, raw, dev="cuda", mode="A", **kw):
     caches = layer.alloc_caches(cfg.lens, dev, tdtype(cfg))
     layer.compress(caches, d, d["tok_off"])
     out, inter = layer.step(caches, d["x"], d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"],
-                            raw["q_pos"].reshape(-1), mode=mode, keep=True)
+                            raw["q_pos"].reshape(-1), mode=mode, keep=True, v=d.get("v"))
     torch.cuda.synchronize()
     return d, layer, caches, out, inter
 
