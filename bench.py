@@ -108,12 +108,39 @@ def step_bytes(cfg):
         ncsa = n_windows(L, cfg.m, cfg.w)
         nh = n_windows(L, cfg.m2, cfg.w2)
         kk = min(cfg.k, ncsa)
+        kv = 2 if cfg.sepv else 1                       # key rows, and value rows beside them
         tot += ncsa * key_bytes(cfg)                    # indexer keys
-        tot += tq * kk * (cfg.D * e + 4)                # selected entries + indices, per row
-        tot += min(cfg.W + tq - 1, L) * cfg.D * e       # window rows
-        tot += nh * cfg.D * e                           # HCA entries
+        tot += tq * kk * (kv * cfg.D * e + 4)           # selected entries + indices, per row
+        tot += kv * min(cfg.W + tq - 1, L) * cfg.D * e  # window rows
+        tot += kv * nh * cfg.D * e                      # HCA entries
         tot += tq * (cfg.H * cfg.D * 2 * e + cfg.H * 4)  # q, out, sink per row
     return tot
+
+
+METRIC = "decode query-tokens/s per layer at 1M ctx (Pro shape); % of HBM peak BW"
+
+
+def metric_name(cfg):
+    """The headline metric for the Pro 1M decode; for other workloads the
+    same measure, named with what differs."""
+    if cfg.name == "pro_1m_decode":
+        return METRIC
+    what = []
+    if cfg.ikey != "bf16":
+        what.append(f"{cfg.ikey} indexer keys")
+    if cfg.tq > 1:
+        what.append(f"{cfg.tq} query rows per step: the main token and {cfg.tq - 1} drafted")
+    if cfg.rope:
+        what.append(f"rotary embedding on {cfg.rope} dims")
+    if cfg.dual:
+        what.append("dual-stream compressor")
+    if cfg.sepv:
+        what.append("separate values")
+    if cfg.name.startswith("pro_1m"):
+        where = "1M ctx (Pro shape" + "".join(", " + w for w in what) + ")"
+    else:
+        where = f"the {cfg.name} workload" + (" (" + ", ".join(what) + ")" if what else "")
+    return f"decode query-tokens/s per layer at {where}; % of HBM peak BW"
 
 
 def kernel_cost(cfg, name, front=False):
@@ -126,6 +153,7 @@ def kernel_cost(cfg, name, front=False):
     window are attended beside the scores rather than in hybrid_attn."""
     e = 2 if cfg.dtype == "bf16" else 4
     tq = cfg.tq
+    kv = 2 if cfg.sepv else 1                                    # key rows, and value rows beside them
     by = fl = ov = 0
     for L in cfg.lens:
         ncsa = n_windows(L, cfg.m, cfg.w)
@@ -137,9 +165,9 @@ def kernel_cost(cfg, name, front=False):
             fl += 2 * ncsa * cfg.dI * cfg.HI * tq
             ov += tq * ncsa * 4                                  # scores written
         if name in ("csa_index_score_append", "decode_front"):  # the entries the new tokens complete
-            by += (2 * cfg.w * cfg.D + 2 * cfg.w * cfg.dI + 2 * cfg.w2 * cfg.D) * e + (2 * cfg.D + cfg.dI) * e
+            by += (kv * (2 * cfg.w * cfg.D + 2 * cfg.w2 * cfg.D) + 2 * cfg.w * cfg.dI) * e + (kv * 2 * cfg.D + cfg.dI) * e
         if name == "decode_front":                               # HCA entries, window rows, the queries
-            by += (nh + nwin) * cfg.D * e + tq * cfg.H * cfg.D * e
+            by += kv * (nh + nwin) * cfg.D * e + tq * cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * (nh + min(cfg.W, L)) * tq
         if name == "csa_topk_select":
             by += kk * 4
@@ -154,11 +182,11 @@ def kernel_cost(cfg, name, front=False):
             by += min(cfg.W, L) * cfg.D * e + cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * min(cfg.W, L)
         if name == "hybrid_attn":                                # the selection + the sparse branch
-            by += tq * kk * (cfg.D * e + 4) + tq * cfg.H * cfg.D * e
+            by += tq * kk * (kv * cfg.D * e + 4) + tq * cfg.H * cfg.D * e
             fl += 4 * cfg.H * cfg.D * kk * tq
             ov += tq * ncsa * 4                                  # the row's scores read back
             if not front:                                        # the HCA entries and the window
-                by += (nh + nwin) * cfg.D * e
+                by += kv * (nh + nwin) * cfg.D * e
                 fl += 4 * cfg.H * cfg.D * (nh + min(cfg.W, L)) * tq
         if name == "swa_merge":
             by += tq * (cfg.H * cfg.D * e + cfg.H * 4)           # output + sink
@@ -205,7 +233,8 @@ class Runner:
         self.torch, self.ops = torch, ops
         self.cfg = cfg
         a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
-                            split_csa=split_csa or None, split_hca=split_hca or None, ikey=cfg.ikey)
+                            split_csa=split_csa or None, split_hca=split_hca or None, ikey=cfg.ikey,
+                            rope=cfg.rope, rope_base=cfg.rope_base, dual=cfg.dual, sepv=cfg.sepv)
         self.attn = a
         self.layers = [LayerState(cfg, r, a, dev) for r in range(R)]
         rows = cfg.B * cfg.tq
@@ -241,7 +270,7 @@ class Runner:
         st = a.compress_streams(c, L.raw, L.done_h)
         idx_st = [x for x in st if x["out"] is c.ikey][0]
         kv_st = [x for x in st if x["out"] is not c.ikey]
-        srcs = a.attn_sources(c, L.raw["x"], L.tok_off, None, bf)
+        srcs = a.attn_sources(c, L.raw["x"], L.tok_off, None, bf, L.raw.get("v"))
         parts = [bf["csa"], bf["hca"], bf["swa"]][:len(srcs)]
         return [
             lambda: ops.csa_index_score_append(L.p, L.omega, c.ikey, c.csa_off, L.q_pos, cfg.k, cfg.m, cfg.w,
@@ -285,7 +314,7 @@ def run_prefill(cfg, args, dev):
     import lca_inputs as li
     from long_context_attention_20_amd import HybridAttention, ops
     a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
-                        ikey=cfg.ikey)
+                        ikey=cfg.ikey, rope=cfg.rope, rope_base=cfg.rope_base, dual=cfg.dual, sepv=cfg.sepv)
     raw = li.make_raw_torch(cfg, 0, dev)
     caches = a.alloc_caches(cfg.lens, dev, raw["x"].dtype)
     a.compress(caches, raw, raw["tok_off"])
@@ -304,7 +333,7 @@ def run_prefill(cfg, args, dev):
     out = torch.empty_like(raw["q"])
     streams = a.compress_streams(caches, raw, done_h)
     names = ["kv_compress", "csa_index_score", "csa_topk_select", "hybrid_attn_merge"]
-    srcs = a.attn_sources(caches, raw["x"], raw["tok_off"], idx, bufs)
+    srcs = a.attn_sources(caches, raw["x"], raw["tok_off"], idx, bufs, raw.get("v"))
     calls = [
         lambda: ops.kv_compress(streams, raw["tok_off"], done, cfg.eps),
         lambda: ops.csa_index_score(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
@@ -346,7 +375,7 @@ def run_prefill(cfg, args, dev):
                      "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
                      "frac": attn_fl / (per[j] / 1e3) / MFMA_BF16_PEAK, "traffic": None,
                      "kernel_ms": float(per[j]), "flops_per_launch": attn_fl},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu_baseline_prefill(cfg, raw, args.cpu_seconds) if args.cpu_seconds > 0 else None,
     }
     print(json.dumps(res))
 
@@ -441,28 +470,77 @@ def trace_attention(run, path, reps=6):
     print(text, file=sys.stderr, flush=True)
 
 
+def _host_info():
+    """The host's CPU model and hardware thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
+def _host_seq(raw, b, cfg):
+    """Sequence b's raw streams on the host (float64): x, a, g, u, c and the
+    option streams the workload has."""
+    from oracle import pipeline as opipe
+    off = raw["tok_off"].cpu().numpy()
+    host = lambda t: t[int(off[b]):int(off[b + 1])].float().cpu().numpy().astype(np.float64)  # noqa: E731
+    seq = {k: host(raw[k]) for k in ("x", "a", "g", "u", "c")}
+    opt = {k: host(raw[k]) for k in opipe.OPTION_STREAMS if k in raw}
+    return seq, opt
+
+
+def _timed(fn, budget_s, cap):
+    """Calls fn() until budget_s seconds or cap calls; (calls, seconds)."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= cap:
+            return n, el
+
+
+def _with_one_thread(fn):
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return None
+    with threadpool_limits(limits=1):
+        return fn()
+
+
 def cpu_baseline(cfg, state, budget_s):
     """The oracle (float64, numpy) on this host: one decode step per query of
     layer 0 -- append the completed entries, score, select, attend, merge --
-    on caches it builds itself from the same raw inputs (build not timed)."""
+    on caches it builds itself from the same raw inputs (build not timed);
+    timed with the BLAS threads numpy starts with, then with one thread."""
     from oracle import compress as ocmp
     from oracle import numerics as onum
     from oracle import pipeline as opipe
     from oracle import quant as oquant
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    threads = _blas_threads()
     raw = state.raw
     b = 0
     L = cfg.lens[b]
-    off = raw["tok_off"].cpu().numpy()
-    def host(t):
-        return t[int(off[b]):int(off[b + 1])].float().cpu().numpy().astype(np.float64)
     t0 = time.perf_counter()
-    x, a, g, u, c = host(raw["x"]), host(raw["a"]), host(raw["g"]), host(raw["u"]), host(raw["c"])
-    caches = opipe.build_seq_caches(x, a, g, u, c, cfg)
+    seq, opt = _host_seq(raw, b, cfg)
+    x, a, g, u, c = (seq[k] for k in ("x", "a", "g", "u", "c"))
+    caches = opipe.build_seq_caches(x, a, g, u, c, cfg, opt)
     build_s = time.perf_counter() - t0
     tq = cfg.tq
     rows = []
@@ -472,33 +550,83 @@ def cpu_baseline(cfg, state, budget_s):
                      raw["p"][r].float().cpu().numpy().astype(np.float64),
                      raw["omega"][r].cpu().numpy().astype(np.float64), L - tq + t))
     sg = raw["sigma"].cpu().numpy().astype(np.float64)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+    dual = (lambda k: opt[k]) if cfg.dual else (lambda k: None)  # noqa: E731
+
+    def step():
         # append: the entries the step's tokens complete
-        for m, w, src, lg, norm, name in ((cfg.m, cfg.w, x, a, True, "kv_csa"), (cfg.m, cfg.w, u, c, False, "ikey"),
-                                          (cfg.m2, cfg.w2, x, g, True, "kv_hca")):
-            new = range(ocmp.n_entries(L - tq, m, w), ocmp.n_entries(L, m, w))
-            if len(new):
-                pooled = ocmp.compress(src, lg, m, w, norm, cfg.eps, new)
-                getattr(caches, name)[list(new)] = (oquant.dequantize_rows(*oquant.quantize_rows(pooled))
-                                                    if name == "ikey" and cfg.ikey == "fp8"
-                                                    else oquant.dequantize_mx_rows(*oquant.quantize_mx_rows(pooled))
-                                                    if name == "ikey" and cfg.ikey == "mxfp4"
-                                                    else onum.round_to(pooled, cfg.dtype))
+        def new(m, w):
+            return list(range(ocmp.n_entries(L - tq, m, w), ocmp.n_entries(L, m, w)))
+        j = new(cfg.m, cfg.w)
+        if j:
+            caches.kv_csa[j] = opipe.kv_entries(x, a, cfg.m, cfg.w, cfg, j, dual("x_b"), dual("a_b"))
+            pooled = ocmp.compress(u, c, cfg.m, cfg.w, False, cfg.eps, j, src2=dual("u_b"), z2=dual("c_b"))
+            caches.ikey[j] = (oquant.dequantize_rows(*oquant.quantize_rows(pooled)) if cfg.ikey == "fp8" else
+                              oquant.dequantize_mx_rows(*oquant.quantize_mx_rows(pooled)) if cfg.ikey == "mxfp4"
+                              else onum.round_to(pooled, cfg.dtype))
+            if cfg.sepv:
+                caches.v_csa[j] = opipe.kv_entries(opt["v"], a, cfg.m, cfg.w, cfg, j, dual("v_b"), dual("a_b"))
+        j = new(cfg.m2, cfg.w2)
+        if j:
+            caches.kv_hca[j] = opipe.kv_entries(x, g, cfg.m2, cfg.w2, cfg, j)
+            if cfg.sepv:
+                caches.v_hca[j] = opipe.kv_entries(opt["v"], g, cfg.m2, cfg.w2, cfg, j)
         for q, p, om, i in rows:
-            opipe.query_step(caches, x, q, p, om, sg, i, cfg)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 1000:
-            break
+            opipe.query_step(caches, x, q, p, om, sg, i, cfg, v_seq=opt.get("v"))
+
+    n, el = _timed(step, budget_s, 1000)
+    one = _with_one_thread(lambda: _timed(step, budget_s / 3, 1000))
+    model, hw = _host_info()
     where = f"1 query at position {L - 1}" if tq == 1 else f"{tq} queries at positions {L - tq}..{L - 1}"
     return {"value": n * tq / el, "unit": "q-tok/s/layer", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} decode steps of sequence 0 ({where}) of layer 0, float64 numpy oracle "
                       f"(append + indexer + top-k + sparse + HCA + window + sink + merge) on caches it built "
-                      f"itself in {build_s:.1f} s (not timed); {el:.1f} s timed",
-            "seconds": round(el, 3)}
+                      f"itself in {build_s:.1f} s (not timed); {el:.1f} s timed with {threads} BLAS threads",
+            "seconds": round(el, 3),
+            "value_1_thread": (one[0] * tq / one[1]) if one else None,
+            "seconds_1_thread": round(one[1], 3) if one else None,
+            "host_cpu": model, "host_threads": hw}
+
+
+def cpu_baseline_prefill(cfg, raw, budget_s):
+    """The oracle on this host for the prefill chunk: query rows of the chunk
+    spread evenly over it (first and last included), each scored, selected
+    and attended on caches the oracle builds from the whole context (build
+    not timed)."""
+    from oracle import pipeline as opipe
+    threads = _blas_threads()
+    b = 0
+    L = cfg.lens[b]
+    t0 = time.perf_counter()
+    seq, opt = _host_seq(raw, b, cfg)
+    caches = opipe.build_seq_caches(seq["x"], seq["a"], seq["g"], seq["u"], seq["c"], cfg, opt)
+    build_s = time.perf_counter() - t0
+    sg = raw["sigma"].cpu().numpy().astype(np.float64)
+    order = np.unique(np.linspace(0, cfg.tq - 1, 257).astype(int))
+    q = raw["q"].float().cpu().numpy()
+    p = raw["p"].float().cpu().numpy()
+    om = raw["omega"].cpu().numpy()
+    state = {"k": 0}
+
+    def row():
+        t = int(order[state["k"] % len(order)])
+        state["k"] += 1
+        opipe.query_step(caches, seq["x"], q[t].astype(np.float64), p[t].astype(np.float64),
+                         om[t].astype(np.float64), sg, L - cfg.tq + t, cfg, v_seq=opt.get("v"))
+
+    n, el = _timed(row, budget_s, len(order))
+    state["k"] = 0
+    one = _with_one_thread(lambda: _timed(row, budget_s / 3, len(order)))
+    model, hw = _host_info()
+    return {"value": n / el, "unit": "q-tok/s/layer", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows of the {cfg.tq}-row chunk (evenly spaced, from the first), float64 numpy "
+                      f"oracle (indexer + top-k + sparse + HCA + window + sink + merge) on caches of the whole "
+                      f"{L}-token context it built itself in {build_s:.1f} s (not timed); {el:.1f} s timed with "
+                      f"{threads} BLAS threads",
+            "seconds": round(el, 3),
+            "value_1_thread": (one[0] / one[1]) if one else None,
+            "seconds_1_thread": round(one[1], 3) if one else None,
+            "host_cpu": model, "host_threads": hw}
 
 
 def main():
@@ -683,12 +811,7 @@ def main():
         cpu = cpu_baseline(cfg, run.layers[0], args.cpu_seconds)
 
     res = {
-        "metric": ("decode query-tokens/s per layer at 1M ctx (Pro shape); % of HBM peak BW" if tq == 1 and
-                   cfg.ikey == "bf16" else
-                   f"decode query-tokens/s per layer at 1M ctx (Pro shape, {cfg.ikey} indexer keys); % of HBM peak BW"
-                   if tq == 1 else
-                   f"decode query-tokens/s per layer at 1M ctx (Pro shape, {tq} query rows per step: the main token "
-                   f"and {tq - 1} drafted); % of HBM peak BW"),
+        "metric": metric_name(cfg),
         "value": value,
         "unit": "q-tok/s/layer",
         "n_gpus": 1,

@@ -112,9 +112,17 @@ FLASH_PREFILL_FP8 = dataclasses.replace(FLASH_PREFILL, name="flash_prefill_fp8",
 PRO_VARLEN_MXFP4 = dataclasses.replace(PRO_VARLEN, name="pro_varlen_mxfp4", ikey="mxfp4")
 FLASH_PREFILL_MXFP4 = dataclasses.replace(FLASH_PREFILL, name="flash_prefill_mxfp4", ikey="mxfp4")
 
+# The Pro 1M decode (same seeds) with the partial rotary embedding on the
+# last 64 dims of each head; and with every model option at once: the rotary
+# embedding, the dual-stream compressor and separate values.
+PRO_1M_DECODE_ROPE = dataclasses.replace(PRO_1M_DECODE, name="pro_1m_decode_rope", rope=64)
+PRO_1M_DECODE_ALL = dataclasses.replace(PRO_1M_DECODE, name="pro_1m_decode_all_options", rope=64, dual=True,
+                                        sepv=True)
+
 CONFIGS: Dict[str, Config] = {c.name: c for c in (TINY, FLASH_DECODE, PRO_1M_DECODE, FLASH_PREFILL, PRO_VARLEN,
                                                   PRO_1M_MTP2, PRO_1M_DECODE_FP8, PRO_VARLEN_FP8, FLASH_PREFILL_FP8,
-                                                  PRO_1M_DECODE_MXFP4, PRO_VARLEN_MXFP4, FLASH_PREFILL_MXFP4)}
+                                                  PRO_1M_DECODE_MXFP4, PRO_VARLEN_MXFP4, FLASH_PREFILL_MXFP4,
+                                                  PRO_1M_DECODE_ROPE, PRO_1M_DECODE_ALL)}
 
 
 def small(name: str, cfg_id: int, lens, tq: int = 1, H: int = 64, D: int = 512, HI: int = 4,
