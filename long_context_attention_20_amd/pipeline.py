@@ -56,7 +56,8 @@ class HybridAttention:
     def __init__(self, H: int, D: int, HI: int, dI: int, k: int, m: int = 4, w: int = 8, m2: int = 128,
                  w2: int = 128, W: int = 128, eps: float = 1e-6, scale: Optional[float] = None,
                  split_csa: Optional[int] = None, split_hca: Optional[int] = None, ikey: str = "bf16",
-                 rope: int = 0, rope_base: float = 10000.0, dual: bool = False, sepv: bool = False):
+                 rope: int = 0, rope_base: float = 10000.0, dual: bool = False, sepv: bool = False,
+                 batch_invariant: bool = False, max_context: int = 1 << 20):
         self.H, self.D, self.HI, self.dI, self.k = H, D, HI, dI, k
         # partial rotary embedding on the last `rope` dims of each head (0:
         # none): compressed entries are stored turned by the position of
@@ -74,6 +75,10 @@ class HybridAttention:
         if dual and w != 2 * m:
             raise ValueError("the dual-stream compressor needs w = 2m")
         self.dual, self.sepv = bool(dual), bool(sepv)
+        # batch_invariant: a decode step gives every sequence the same output
+        # bits alone and inside any batch (invariant_splits); max_context
+        # bounds the contexts the layer serves (it fixes the split counts)
+        self.batch_invariant, self.max_context = bool(batch_invariant), int(max_context)
         # indexer-key cache: rows of the inputs' type ("bf16"), fp8 rows (d_I
         # E4M3 bytes, fp32 scale, 4 zero bytes) or MXFP4 rows (d_I/2 bytes of
         # E2M1 pairs, one E8M0 scale per 32 channels, zero pad to d_I/2 + 8)
@@ -200,6 +205,24 @@ class HybridAttention:
         tiles = max(1, (n_keys + 31) // 32)
         want = max(1, -(-256 // (rows * hg)))
         return int(max(1, min(want, tiles // 4 if tiles >= 4 else 1, 256)))
+
+    # batch-invariant decode: 32-key tiles per split of the sparse and the
+    # HCA source
+    INV_TILES = (2, 4)
+
+    def invariant_splits(self):
+        """Splits of a batch-invariant decode step: every split of a source
+        takes a fixed range of a row's keys (tiles_per_split: 64 selected
+        entries, 128 HCA entries; the window whole) and the split counts
+        follow from k and max_context alone, so a row's partials, the merge's
+        slot layout and its summation order do not depend on the other rows
+        of the call; more than 16 slots in all, so that the merge is the same
+        kernel for any number of rows."""
+        sc = -(-self.k // (32 * self.INV_TILES[0]))
+        sh = max(1, -(-n_windows(self.max_context, self.m2, self.w2) // (32 * self.INV_TILES[1])))
+        sw = 1
+        sh = max(sh, 17 - sc - sw)
+        return sc, sh, sw
 
     # the row's scores a sparse block filters in one pass when it selects:
     # chunks of 512 threads x 8 scores, two chunks loaded at the block's start
@@ -335,13 +358,17 @@ class HybridAttention:
         if front is None:
             front = self.front_default(rows)
         f32 = torch.float32
-        if front:
+        if self.batch_invariant:
+            front = False
+            sc, sh, sw = self.invariant_splits()
+        elif front:
             sc, sh, sw = self.front_splits(rows, min(self.k, max(1, max_csa)), max_hca, max_csa)
         else:
             sc, sh, sw = self.fused_splits(rows, min(self.k, max(1, max_csa)), max_hca, self.W, select=True,
                                            n_scores=max_csa)
-        sc = self.split_csa or sc
-        sh = self.split_hca or sh
+        if not self.batch_invariant:
+            sc = self.split_csa or sc
+            sh = self.split_hca or sh
         part = lambda n: (torch.empty((n, rows, self.H, self.D), dtype=f32, device=device),
                           torch.empty((n, rows, self.H), dtype=f32, device=device))
         return dict(
@@ -364,12 +391,17 @@ class HybridAttention:
         else:
             src = [dict(kind="gather", kv=caches.kv_csa, off=caches.csa_off, idx=idx, n_split=bufs["sc"],
                         o_part=bufs["csa"][0], lse=bufs["csa"][1])]
-        if bufs["max_hca"] > 0:
+        if bufs["max_hca"] > 0 or self.batch_invariant:  # (a fixed slot layout: always present)
             src.append(dict(kind="dense", kv=caches.kv_hca, off=caches.hca_off, m2=self.m2, w2=self.w2,
                             n_split=bufs["sh"], o_part=bufs["hca"][0], lse=bufs["hca"][1]))
         if self.W > 0:
             src.append(dict(kind="window", kv=x, off=tok_off, W=self.W, n_split=bufs["sw"], o_part=bufs["swa"][0],
                             lse=bufs["swa"][1]))
+        if self.batch_invariant:
+            tps = {"topk": self.INV_TILES[0], "gather": self.INV_TILES[0], "dense": self.INV_TILES[1],
+                   "window": -(-self.W // 32)}
+            for d in src:
+                d["tiles_per_split"] = tps[d["kind"]]
         return [self._turn(d) for d in self._values(src, caches, v)]
 
     def front_calls(self, caches: Caches, raw: dict, tok_off: torch.Tensor, q, p, omega, sigma, q_pos, bufs: dict,
