@@ -776,13 +776,13 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     const float4 v = *reinterpret_cast<const float4*>(ox + (kAttnHeads + hh) * XP + d);
     float o4[4] = {u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w};
     if (OPT && a.rope.dims) rope_turn<4>(o4, d, D, a.rope, -(double)qpos_r);  // -i on the output
-    *reinterpret_cast<float4*>(op + (int64_t)i * 4) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    __builtin_nontemporal_store(f32x4{o4[0], o4[1], o4[2], o4[3]}, reinterpret_cast<f32x4*>(op + (int64_t)i * 4));
   }
   if (threadIdx.x < nh) {
     float M, f0, f1, lsum;
     head_state(threadIdx.x, &M, &f0, &f1, &lsum);
-    S.lse[((int64_t)split * a.rows + r) * a.H + hbase + threadIdx.x] =
-        lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+    __builtin_nontemporal_store(lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY,
+                                &S.lse[((int64_t)split * a.rows + r) * a.H + hbase + threadIdx.x]);
   }
   trace_stamp(a, 6);
   trace_flags(a, tflags);
