@@ -55,10 +55,11 @@ HBM_PEAK = 8.0e12          # bytes/s, MI355X
 TRAFFIC = {
     ("pro_1m_decode", "hybrid_attn"): {
         "files": ["long_context_attention_20_amd/csrc/lca_attention.hip",
+                  "long_context_attention_20_amd/csrc/lca_attn_block.h",
                   "long_context_attention_20_amd/csrc/lca_common.h",
                   "long_context_attention_20_amd/csrc/lca_topk.h"],
-        "sha1": "487e30f3cc2f5e0f92d3d48f38cc476e22fc3f22",
-        "fetch_kib": 6320.4, "write_kib": 15477.5, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha1": "891598b042815fbab2b8b438d1ffe49bf70bc4db",
+        "fetch_kib": 6388.5, "write_kib": 16694.6, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
