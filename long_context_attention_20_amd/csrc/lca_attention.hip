@@ -16,10 +16,9 @@
 namespace lca {
 
 // The attention kernel of few query rows per sequence (see attn_block);
-// OPT: the call may turn by a rotary embedding and its sources may give
-// values apart from their keys (kept out of the plain kernel, whose register
-// budget it would strain).
-template <int D, bool TOPK, int FC = 1, bool OPT = false>
+// OPT: kOptRope (the call turns by a rotary embedding) and / or kOptValues
+// (its sources may give values apart from their keys).
+template <int D, bool TOPK, int FC = 1, int OPT = 0>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnParams a) {
   __shared__ __attribute__((aligned(16))) char lds_raw[AttnLds<D, TOPK>::kBytes];
   attn_block<D, TOPK, FC, OPT>(a, blockIdx.x, lds_raw);
@@ -742,34 +741,41 @@ int launch_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int 
 // Blocks of attn_mfma<D, true, fc, opt> the current device holds at once
 // (compute units x blocks per unit, from the occupancy query on the idle
 // device), queried once per device, D, fc (2 is built for D = 512 without
-// the options only) and opt.
+// options only) and opt (0..3).
 // The cache is read and written atomically: concurrent first calls may both
 // query, and both store the same value.  Residency is what lets the sparse
 // blocks wait for each other; it is not guaranteed while other work holds
 // compute units, which is why their wait is bounded (and falls back to an
 // exact selection of its own).
-static int64_t resident_blocks(int D, int fc, bool opt) {
-  static std::atomic<int64_t> cache[64][4][3];
+static int64_t resident_blocks(int D, int fc, int opt) {
+  static std::atomic<int64_t> cache[64][4][5];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int di = D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : 3;
-  const int fi = opt ? 2 : (fc == 2 && D == 512 ? 1 : 0);
+  const int fi = opt ? 1 + opt : (fc == 2 && D == 512 ? 1 : 0);
   int64_t v = cache[dev][di][fi].load(std::memory_order_relaxed);
   if (v == 0) {
     int cus = 0, per = 0;
     hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const void* fn;
-    if (opt)
-      fn = D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true, 1, true>)
-           : D == 128 ? reinterpret_cast<const void*>(&attn_mfma<128, true, 1, true>)
-           : D == 256 ? reinterpret_cast<const void*>(&attn_mfma<256, true, 1, true>)
-                      : reinterpret_cast<const void*>(&attn_mfma<512, true, 1, true>);
+#define LCA_OPT_FN(O)                                                                \
+  (D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true, 1, O>)                \
+   : D == 128 ? reinterpret_cast<const void*>(&attn_mfma<128, true, 1, O>)               \
+   : D == 256 ? reinterpret_cast<const void*>(&attn_mfma<256, true, 1, O>)               \
+              : reinterpret_cast<const void*>(&attn_mfma<512, true, 1, O>))
+    if (opt == 1)
+      fn = LCA_OPT_FN(1);
+    else if (opt == 2)
+      fn = LCA_OPT_FN(2);
+    else if (opt == 3)
+      fn = LCA_OPT_FN(3);
     else
       fn = D == 64    ? reinterpret_cast<const void*>(&attn_mfma<64, true>)
            : D == 128 ? reinterpret_cast<const void*>(&attn_mfma<128, true>)
            : D == 256 ? reinterpret_cast<const void*>(&attn_mfma<256, true>)
            : fi       ? reinterpret_cast<const void*>(&attn_mfma<512, true, 2>)
                       : reinterpret_cast<const void*>(&attn_mfma<512, true>);
+#undef LCA_OPT_FN
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kAttnThreads, 0);
     v = (e == hipSuccess && cus > 0 && per > 0) ? (int64_t)cus * per : -1;
     cache[dev][di][fi].store(v, std::memory_order_relaxed);
@@ -941,14 +947,14 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
   int blocks = 0;
   int topk = -1;          // the TOPK source
   bool fused_topk = false;  // selected inside the attention blocks
-  bool opt = a.rope.dims > 0;  // a rotary embedding, or a source with separate values
+  int opt = a.rope.dims > 0 ? kOptRope : 0;  // | kOptValues: a source with separate values
   for (int i = 0; i < n_src; ++i) {
     const lca_attn_source& in = srcs[i];
     AttnSrc& d = a.s[i];
     d.kv = in.kv; d.off = in.off; d.idx = in.idx; d.kind = in.kind; d.k = in.k; d.m2 = in.m2; d.w2 = in.w2;
     d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
     d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split; d.v = in.v;
-    opt = opt || in.v != nullptr;
+    if (in.v) opt |= kOptValues;
     d.block_begin = blocks;
     blocks += in.n_split;
     if (in.kind == SRC_TOPK) {
@@ -1015,16 +1021,15 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
   if (mfma) {
     const int64_t units = (int64_t)rows * blocks;
     dim3 grid((unsigned)((units + 7) / 8 * 8 * a.n_hb));
-#define LCA_MFMA(DD)                                                                                       \
-  if (opt) {                                                                                               \
-    if (fused_topk)                                                                                        \
-      hipLaunchKernelGGL((attn_mfma<DD, true, 1, true>), grid, dim3(kAttnThreads), 0, stream, a);          \
-    else                                                                                                   \
-      hipLaunchKernelGGL((attn_mfma<DD, false, 1, true>), grid, dim3(kAttnThreads), 0, stream, a);         \
-  } else if (fused_topk) {                                                                                 \
-    hipLaunchKernelGGL((attn_mfma<DD, true>), grid, dim3(kAttnThreads), 0, stream, a);                     \
-  } else {                                                                                                 \
-    hipLaunchKernelGGL((attn_mfma<DD, false>), grid, dim3(kAttnThreads), 0, stream, a);                    \
+#define LCA_MFMA_T(DD, O)                                                                         \
+  if (fused_topk) hipLaunchKernelGGL((attn_mfma<DD, true, 1, O>), grid, dim3(kAttnThreads), 0, stream, a); \
+  else hipLaunchKernelGGL((attn_mfma<DD, false, 1, O>), grid, dim3(kAttnThreads), 0, stream, a);
+#define LCA_MFMA(DD)                                \
+  switch (opt) {                                    \
+    case 1: LCA_MFMA_T(DD, 1) break;                \
+    case 2: LCA_MFMA_T(DD, 2) break;                \
+    case 3: LCA_MFMA_T(DD, 3) break;                \
+    default: LCA_MFMA_T(DD, 0) break;               \
   }
     switch (D) {
       case 64: LCA_MFMA(64) break;
@@ -1038,6 +1043,7 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
         break;
     }
 #undef LCA_MFMA
+#undef LCA_MFMA_T
   } else {
     dim3 grid((unsigned)blocks, (unsigned)H, (unsigned)rows);
 #define LCA_VALU(ETy)                                                                      \

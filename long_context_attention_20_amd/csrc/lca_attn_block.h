@@ -220,6 +220,12 @@ constexpr int kAttnHeads = 32;      // query heads per block
 
 // FC: filter chunks a sparse block of a TOPK source loads at its start and
 // filters in one pass (2 when the row's scores give a block more than one).
+// Options of a kernel variant (the OPT template argument): the rotary
+// embedding, separate values.  Their code stays out of the plain kernel,
+// whose register budget it would strain.
+constexpr int kOptRope = 1;
+constexpr int kOptValues = 2;
+
 // LDS of the block (besides a few small arrays it declares itself): the
 // tiles, or with a TOPK source the selection's scratch when that is larger.
 template <int D, bool TOPK>
@@ -232,7 +238,7 @@ struct AttnLds {
 // grid (1-D, XCD-aware numbering below), lds_raw AttnLds<D, TOPK>::kBytes of
 // LDS.  Called by the attention kernel, and by the decode front launch for
 // its attention blocks.
-template <int D, bool TOPK, int FC = 1, bool OPT = false>
+template <int D, bool TOPK, int FC = 1, int OPT = 0>
 __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, char* lds_raw) {
   constexpr int DH = D / 2;                 // dims per wave
   constexpr int KS = DH / 32;               // k-steps of the S partial
@@ -254,6 +260,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   __shared__ int32_t sidx[kIdxLds];
   __shared__ float sx[2][4][8][64];         // S partial exchange, per team
   __shared__ float qss[2][4][16];           // query sum-of-squares exchange, per team
+  // rotary embedding of a window block's rows: the angles of its first
+  // token's position and the turns per position, per pair (rope_turn_near)
+  __shared__ float2 s_rot[(OPT & kOptRope) ? D / 2 : 1];
+  __shared__ float s_turns[(OPT & kOptRope) ? D / 2 : 1];
   // 1-D grid, XCD-aware: workgroups go to the 8 XCDs round-robin by linear
   // id, so the n_hb head blocks of one (row, split) unit take ids 8 apart and
   // share an XCD's L2 for the keys they all read
@@ -346,7 +356,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     }
   }
   // --- the key count and the block's key range
-  const int32_t qpos_r = ((kind != SRC_GATHER || (OPT && a.rope.dims)) && a.q_pos) ? qpos_ld : 0;
+  const int32_t qpos_r = ((kind != SRC_GATHER || ((OPT & kOptRope) && a.rope.dims)) && a.q_pos) ? qpos_ld : 0;
   const int64_t dlen = (kind == SRC_DENSE && S.part != 0) ? dlen_ld : 0;
   const int64_t nseq = off1 - off0;
   int64_t first = off0;
@@ -383,8 +393,8 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   // --- tile staging (per team): loads are unconditional (invalid keys read a
   // clamped valid row) and zeroed when stored
   uint4 stage[LOADS];
-  uint4 vstage[OPT ? LOADS : 1];    // the value rows beside the keys (separate values)
-  const bool sv = OPT && S.v != nullptr;  // uniform over the block
+  uint4 vstage[(OPT & kOptValues) ? LOADS : 1];  // the value rows beside the keys (separate values)
+  const bool sv = (OPT & kOptValues) && S.v != nullptr;  // uniform over the block
   uint32_t okbits = 0;
   int64_t stage_t = 0;               // tile index of the staged loads (window rows' positions)
   const int64_t kpos0 = first - off0;  // window: position of key 0 (the window's first token)
@@ -414,7 +424,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       }
       okbits |= (ok ? 1u : 0u) << v;
       stage[v] = *reinterpret_cast<const uint4*>(kvp + (first + off) * D + vec * 8);
-      if constexpr (OPT)
+      if constexpr ((OPT & kOptValues) != 0)
         if (sv) vstage[v] = *reinterpret_cast<const uint4*>(vp + (first + off) * D + vec * 8);
     }
   };
@@ -432,9 +442,11 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= inv;
-      if (OPT && a.rope.dims) {
+      if ((OPT & kOptRope) && a.rope.dims) {
+        // (the block's first token at kpos0; its rows are a few thousand
+        // positions from it at most)
         const int id = tt + kTeamThreads * v;
-        rope_turn<8>(f, (id % VPR) * 8, D, a.rope, (double)(kpos0 + stage_t * kTile + id / VPR));
+        rope_turn_near<8>(f, (id % VPR) * 8, D, a.rope.dims, s_rot, s_turns, (float)(stage_t * kTile + id / VPR));
       }
       rows[v] = BF16::pack(f);
     }
@@ -442,7 +454,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   auto store_tile = [&](uint16_t* tile, uint16_t* vtile) {
     if (kind == SRC_WINDOW) {
       norm_rows(stage);
-      if constexpr (OPT)
+      if constexpr ((OPT & kOptValues) != 0)
         if (sv) norm_rows(vstage);
     }
 #pragma unroll
@@ -451,11 +463,25 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       const int row = id / VPR, vec = id % VPR;
       const bool ok = (okbits >> v) & 1u;
       *reinterpret_cast<uint4*>(&tile[row * PITCH + vec * 8]) = ok ? stage[v] : make_uint4(0, 0, 0, 0);
-      if constexpr (OPT)
+      if constexpr ((OPT & kOptValues) != 0)
         if (sv) *reinterpret_cast<uint4*>(&vtile[row * PITCH + vec * 8]) = ok ? vstage[v] : make_uint4(0, 0, 0, 0);
     }
   };
 
+  if constexpr ((OPT & kOptRope) != 0) {
+    if (kind == SRC_WINDOW && a.rope.dims) {  // (block-uniform)
+      for (int p = threadIdx.x; p < a.rope.dims / 2; p += kAttnThreads) {
+        const double th = rope_theta(p, a.rope);
+        double rev = (double)kpos0 * th * kInvTwoPi;
+        rev -= rint(rev);
+        float sn, cs;
+        sincos_quarters((float)(rev * 4.0), &sn, &cs);
+        s_rot[p] = make_float2(cs, sn);
+        s_turns[p] = (float)(th * kInvTwoPi);
+      }
+      __syncthreads();
+    }
+  }
   // --- prologue: dense and window keys do not depend on staged indices, so
   // their first tile is requested first
   if (!gather && rounds > 0) load_tile(tb + team);
@@ -591,7 +617,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       BF16::unpack(qraw[ks], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= inv;
-      if (OPT && a.rope.dims) rope_turn<8>(f, d0 + ks * 32 + g * 8, D, a.rope, (double)qpos_r);
+      if ((OPT & kOptRope) && a.rope.dims) rope_turn<8>(f, d0 + ks * 32 + g * 8, D, a.rope, (double)qpos_r);
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
@@ -775,7 +801,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     const float4 u = *reinterpret_cast<const float4*>(ox + hh * XP + d);
     const float4 v = *reinterpret_cast<const float4*>(ox + (kAttnHeads + hh) * XP + d);
     float o4[4] = {u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w};
-    if (OPT && a.rope.dims) rope_turn<4>(o4, d, D, a.rope, -(double)qpos_r);  // -i on the output
+    if ((OPT & kOptRope) && a.rope.dims) rope_turn<4>(o4, d, D, a.rope, -(double)qpos_r);  // -i on the output
     __builtin_nontemporal_store(f32x4{o4[0], o4[1], o4[2], o4[3]}, reinterpret_cast<f32x4*>(op + (int64_t)i * 4));
   }
   if (threadIdx.x < nh) {

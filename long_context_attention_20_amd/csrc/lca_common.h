@@ -168,15 +168,17 @@ inline RopeTab make_rope_tab(int dims, float base) {
   return t;
 }
 
-__device__ __forceinline__ void rope_sincos(double pos, int p, const RopeTab& t, float* sn, float* cs) {
+// theta_p of a table (a product of its powers, double precision).
+__device__ __forceinline__ double rope_theta(int p, const RopeTab& t) {
   double theta = 1.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     if ((p >> k) & 1) theta *= t.t2k[k];
-  constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
-  double rev = pos * theta * kInvTwoPi;
-  rev -= rint(rev);                                   // [-1/2, 1/2] of a turn
-  const float f = (float)(rev * 4.0);                 // quarter turns, [-2, 2]
+  return theta;
+}
+
+// Sine and cosine of an angle given in quarter turns f, |f| <= 2.
+__device__ __forceinline__ void sincos_quarters(float f, float* sn, float* cs) {
   const float q = rintf(f);
   const float r = (f - q) * 1.57079632679489661923f;  // [-pi/4, pi/4]
   const float r2 = r * r;
@@ -185,6 +187,42 @@ __device__ __forceinline__ void rope_sincos(double pos, int p, const RopeTab& t,
   const int qi = (int)q & 3;                          // angle = qi quarter turns + r
   *sn = qi == 0 ? s : qi == 1 ? c : qi == 2 ? -s : -c;
   *cs = qi == 0 ? c : qi == 1 ? -s : qi == 2 ? -c : s;
+}
+
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+
+__device__ __forceinline__ void rope_sincos(double pos, int p, const RopeTab& t, float* sn, float* cs) {
+  double rev = pos * rope_theta(p, t) * kInvTwoPi;
+  rev -= rint(rev);                                   // [-1/2, 1/2] of a turn
+  sincos_quarters((float)(rev * 4.0), sn, cs);        // quarter turns, [-2, 2]
+}
+
+// Channels [ch0, ch0 + N) of a C-channel vector turned by the angles of
+// position base + off, where base's angles are given (rot[p]: cosine and
+// sine of base * theta_p) and off is small (a few thousand at most): the
+// offset's angle off * theta_p is formed in float (turns[p] = theta_p / 2 pi)
+// and the two rotations are composed.
+template <int N>
+__device__ __forceinline__ void rope_turn_near(float (&v)[N], int ch0, int C, int dims, const float2* rot,
+                                               const float* turns, float off) {
+  static_assert(N % 2 == 0, "pairs");
+  const int lo = C - dims;
+#pragma unroll
+  for (int k = 0; k < N; k += 2) {
+    const int c = ch0 + k;
+    if (dims > 0 && c >= lo) {
+      const int p = (c - lo) >> 1;
+      float rev = off * turns[p];
+      rev -= rintf(rev);
+      float s1, c1;
+      sincos_quarters(rev * 4.f, &s1, &c1);
+      const float2 b = rot[p];
+      const float cs = b.x * c1 - b.y * s1, sn = b.y * c1 + b.x * s1;
+      const float x0 = v[k], x1 = v[k + 1];
+      v[k] = x0 * cs - x1 * sn;
+      v[k + 1] = x0 * sn + x1 * cs;
+    }
+  }
 }
 
 // Channels [ch0, ch0 + N) of a C-channel vector (ch0 and N even), turned by
