@@ -251,3 +251,65 @@ def test_options_many_rows(H):
         res = opipe.query_step(g, xs, raw["q"][r], raw["p"][r], raw["omega"][r], raw["sigma"], int(qp[r]), cfg,
                                idx=idx_h[r], v_seq=vs)
         assert_close(out_h[r], res["out"], cfg.dtype, f"row {r}")
+
+
+def test_all_options_pro_1m_full():
+    """The Pro 1M decode with every option (rotary embedding, dual-stream
+    compressor, separate values), generated on the GPU: sampled entries of
+    every cache against the oracle's pooling (+ norm + turn) of their windows,
+    and the decode step's output (appends of the newest token included)
+    against the oracle from the GPU's caches and selection."""
+    from oracle import attention as oatt
+    from oracle import rope as orope
+    cfg = li.PRO_1M_DECODE_ALL
+    L = cfg.lens[0]
+    print(f"[all options 1M] L={L} H={cfg.H} k={cfg.k} rope={cfg.rope} dual sepv", flush=True)
+    d = li.make_raw_torch(cfg, 0, "cuda")
+    layer = layer_for(cfg)
+    caches = layer.alloc_caches(cfg.lens, "cuda", d["x"].dtype)
+    layer.compress(caches, d, d["tok_off"])
+    done = torch.tensor([L - 1], dtype=torch.int64, device="cuda")
+    bufs = layer.decode_buffers(1, ocmp.n_entries(L, cfg.m, cfg.w), ocmp.n_entries(L, cfg.m2, cfg.w2), "cuda",
+                                d["x"].dtype)
+    out = layer.decode_step(caches, d, d["tok_off"], d["q"], d["p"], d["omega"], d["sigma"], d["q_pos"], bufs,
+                            done_len=done, done_h=[L - 1])
+    torch.cuda.synchronize()
+    host = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    rng = np.random.default_rng(11)
+    for name, src, z, src2, z2, m, w, norm, turn in (
+            ("kv_csa", "x", "a", "x_b", "a_b", cfg.m, cfg.w, True, True),
+            ("v_csa", "v", "a", "v_b", "a_b", cfg.m, cfg.w, True, True),
+            ("ikey", "u", "c", "u_b", "c_b", cfg.m, cfg.w, False, False),
+            ("kv_hca", "x", "g", None, None, cfg.m2, cfg.w2, True, True),
+            ("v_hca", "v", "g", None, None, cfg.m2, cfg.w2, True, True)):
+        n = ocmp.n_entries(L, m, w)
+        js = sorted(set(rng.integers(0, n, 12).tolist()) | {0, n - 1})
+        cache = getattr(caches, name)
+        for j in js:
+            sl = slice(j * m, j * m + w)
+            e = ocmp.compress(host(d[src][sl]), host(d[z][sl]), m, w, norm, cfg.eps,
+                              src2=host(d[src2][sl]) if src2 else None, z2=host(d[z2][sl]) if z2 else None)
+            if turn:
+                e = orope.rotate(e, j * m + w - 1, cfg.rope, cfg.rope_base)
+            ref = opipe.round_to(e, cfg.dtype)[0]
+            got = host(cache[j])
+            lim = np.abs(ref) * 2.0 ** -7 + 1e-5
+            assert np.all(np.abs(got - ref) <= lim), f"{name}[{j}]: beyond one bf16 step"
+    i = L - 1
+    sel = bufs["idx"][0].cpu().numpy()
+    sel = sel[sel >= 0]
+    assert len(sel) == cfg.k
+    sel_t = torch.from_numpy(sel).long().cuda()
+    qhat = oatt.normalize_query(host(d["q"][0]), cfg.eps, cfg.dtype, pos=i, rope=cfg.rope, base=cfg.rope_base)
+    nh = ocmp.n_visible(i, cfg.m2, cfg.w2)
+    csa = oatt.partial(qhat, host(caches.kv_csa[sel_t]), cfg.scale, host(caches.v_csa[sel_t]))
+    hca = oatt.partial(qhat, host(caches.kv_hca[:nh]), cfg.scale, host(caches.v_hca[:nh]))
+    lo = i - cfg.W + 1
+    pos = np.arange(lo, i + 1)
+    keys = oatt.normalize_tokens(host(d["x"][lo:i + 1]), cfg.eps, cfg.dtype, pos=pos, rope=cfg.rope,
+                                 base=cfg.rope_base)
+    vals = oatt.normalize_tokens(host(d["v"][lo:i + 1]), cfg.eps, cfg.dtype, pos=pos, rope=cfg.rope,
+                                 base=cfg.rope_base)
+    swa = oatt.partial(qhat, keys, cfg.scale, vals)
+    o, _ = oatt.merge([csa, hca, swa], host(d["sigma"]))
+    assert_close(f64(out[0]), opipe.finish(o, i, cfg), cfg.dtype, "1M decode output, every option")
