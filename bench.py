@@ -333,13 +333,14 @@ def run_prefill(cfg, args, dev):
     idx = torch.empty((rows, cfg.k), dtype=torch.int32, device=dev)
     out = torch.empty_like(raw["q"])
     streams = a.compress_streams(caches, raw, done_h)
-    names = ["kv_compress", "csa_index_score", "csa_topk_select", "hybrid_attn_merge"]
+    # csa_index_topk with no scores requested: scores and selection in one
+    # launch, no score stored
+    names = ["kv_compress", "csa_index_topk", "hybrid_attn_merge"]
     srcs = a.attn_sources(caches, raw["x"], raw["tok_off"], idx, bufs, raw.get("v"))
     calls = [
         lambda: ops.kv_compress(streams, raw["tok_off"], done, cfg.eps),
-        lambda: ops.csa_index_score(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
-                                    max_csa, ws),
-        lambda: ops.csa_topk_select(caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws, idx=idx),
+        lambda: ops.csa_index_topk(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
+                                   max_csa, ws, idx=idx),
         lambda: ops.hybrid_attn_merge(raw["q"], q_pos, srcs, raw["sigma"], a.scale, cfg.eps, out=out),
     ]
     K, W = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))

@@ -174,7 +174,14 @@ int lca_kv_compress(const lca_compress_stream* streams, int n_streams, const int
  *   q_pos    device int32 [B*Tq]
  *   max_entries  host bound on the candidates of any query (>= 1)
  *   scores   optional fp32 [B*Tq, max_entries] output of every candidate's
- *            score (entry j at column j); NULL to keep them in the workspace
+ *            score (entry j at column j); NULL to keep them in the workspace.
+ *            With NULL, many rows per sequence (Tq >= 32, max_entries <=
+ *            98304), k <= 512, H_I in {1, 2, 4} and d_I a multiple of 32
+ *            up to 256 (a prefill chunk), the scores and the selection run
+ *            in one launch that stores no score: each block streams the
+ *            keys for 16 query rows and keeps per row, in LDS, a bounded
+ *            list of the entries at or above a running threshold (a key
+ *            with at least k listed keys at or above it)
  *   ws       device workspace of at least lca_csa_index_topk_workspace()
  *            bytes.  It must be ZERO-FILLED before its first use; after
  *            that each score call and the selection that must follow it

@@ -53,6 +53,10 @@ int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, cons
                  const float* sink, int rows, int H, int D, void* out, int dtype, hipStream_t stream);
 void diag_set_trace(uint64_t* buf, int64_t words);
 size_t index_noalloc_max_bytes();
+bool index_topk_stream_applies(int B, int Tq, int HI, int dI, int k, int64_t maxN, int dtype);
+int launch_index_topk_stream(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                             const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
+                             int32_t* idx, void* ws, int dtype, hipStream_t stream);
 int launch_index_topk_noalloc(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
                               const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w,
                               int64_t maxN, int32_t* idx, float* scores, int dtype, hipStream_t stream);
@@ -301,6 +305,16 @@ int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, cons
                        int64_t max_entries, int32_t* idx, float* scores, void* ws, size_t ws_bytes, int dtype,
                        void* stream) {
   LCA_REQUIRE(idx != nullptr, LCA_ERR_INVALID_ARG, "csa_index_topk: idx is NULL");
+  if (!scores && index_topk_stream_applies(B, Tq, H_I, d_I, k, max_entries, dtype)) {
+    // many rows per sequence: scores and selection in one launch, no score stored
+    int rc = check_index("csa_index_topk", true, p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w,
+                         max_entries, ws, ws_bytes, dtype);
+    if (rc != LCA_OK) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    return finish(launch_index_topk_stream(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries,
+                                           idx, ws, dtype, st),
+                  st, "csa_index_topk");
+  }
   int rc = lca_csa_index_score(p, omega, ikey, csa_off, q_pos, B, Tq, H_I, d_I, k, m, w, max_entries, scores, ws,
                                ws_bytes, dtype, stream);
   if (rc != LCA_OK) return rc;

@@ -122,16 +122,150 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_valu(IndexParams a) {
 constexpr int kRowsPerBlock = 32;
 constexpr int kRowsEntriesPerWave = 256;
 constexpr int kRowMaxEntries = 98304;  // entries per row the one-block selection takes
+constexpr int kRowBitmapWords = kRowMaxEntries / 32;
 
 static bool rows_mode(int Tq, int64_t maxN) { return Tq >= kRowsPerBlock && maxN <= kRowMaxEntries; }
 // the rows of a sequence share one score block (score_chunk_multi)
 static bool multi_rows_ok(int Tq, int HI) { return Tq >= 2 && Tq <= 4 && Tq * HI <= 16; }
 
+// The raw key-row data of EB blocks of 16 entries from e0 in one lane: lane
+// (col, grp) holds entry e0 + 16u + col, the 8 dims (bf16 rows) or bytes
+// (fp8 / MXFP4 rows) lane group grp feeds each k-step.  Entries at or past
+// nseq read the sequence's last key (their scores are not used).
+template <int KS, int KF, int EB>
+struct KeyRegs {
+  uint4 kv[EB][KS];
+  uint2 k8[EB][KS];
+  float rscale[EB];
+  uint32_t k4[EB][KS];
+  float ms[EB][KS];
+
+  __device__ __forceinline__ void load(const IndexParams& a, int64_t e_base, int64_t nseq, int64_t e0, int col,
+                                       int grp) {
+    const char* K = reinterpret_cast<const char*>(a.ikey);
+    const int64_t rowb = key_row_bytes(a, KF);
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      int64_t e = e0 + u * 16 + col;
+      if (e >= nseq) e = nseq - 1;  // clamp: stays inside the sequence's keys
+      const char* row = K + (e_base + e) * rowb;
+      if constexpr (KF == 1) {
+        load_fp8_slices<KS>(row, grp, k8[u]);
+        rscale[u] = *reinterpret_cast<const float*>(row + a.dI);
+      } else if constexpr (KF == 2) {
+        load_mx_slices<KS>(row, grp, a.dI, k4[u], ms[u]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
+      }
+    }
+  }
+
+  // The same, with the row stride known at compile time (d_I = 32 KS) and
+  // the addresses taken from the sequence's first row: entries from e0
+  // (lane col: e0 + 16u + col), clamped below nseq only in a round that
+  // reaches it.
+  static constexpr int kRowBytes = KF == 1 ? KS * 32 + 8 : KF == 2 ? KS * 16 + 8 : KS * 64;
+  __device__ __forceinline__ void load_rows(const char* seq, uint32_t e0, uint32_t nseq, int col, int grp) {
+    const bool tail = e0 + EB * 16 > nseq;  // uniform
+    const char* base = seq + (size_t)(e0 + (uint32_t)col) * kRowBytes;
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      const char* row = base + u * 16 * kRowBytes;
+      if (tail) {
+        uint32_t e = e0 + (uint32_t)(u * 16 + col);
+        e = e < nseq ? e : nseq - 1;
+        row = seq + (size_t)e * kRowBytes;
+      }
+      if constexpr (KF == 1) {
+        load_fp8_slices<KS>(row, grp, k8[u]);
+        rscale[u] = *reinterpret_cast<const float*>(row + KS * 32);
+      } else if constexpr (KF == 2) {
+        load_mx_slices<KS>(row, grp, KS * 32, k4[u], ms[u]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
+      }
+    }
+  }
+};
+
+// max(x, 0) as one integer max: a negative float's bit pattern is a negative
+// integer (and -0 becomes +0); the same value as fmaxf(x, 0) for every
+// non-NaN x, without the canonicalizing instruction fmaxf costs here
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// The row-tiled product's operands for NR consecutive query rows r0 ..
+// r0 + nrows - 1 of one sequence: lane (col, grp) holds, for MFMA row block
+// rb, the query dims of (row rb*QR + col/HI, head col%HI) and the weights of
+// its accumulator rows 4*grp + i (rows past nrows weigh 0).
+template <int KS, int HI, int KF, int NR>
+struct RowTile {
+  static constexpr int QR = 16 / HI;   // query rows per MFMA row block
+  static constexpr int RB = NR / QR;   // MFMA row blocks
+  static constexpr int RPL = 4 / HI;   // query rows per accumulator lane
+  bf16x8_t A[RB][KS];
+  float om[RB][4];
+
+  // the query row (0 .. NR-1) of accumulator (rb, q) in lane group grp
+  static __device__ __forceinline__ int row(int rb, int q, int grp) { return rb * QR + (4 * grp) / HI + q; }
+
+  __device__ __forceinline__ void load(const IndexParams& a, int r0, int nrows, int col, int grp) {
+    const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qr = rb * QR + col / HI;
+      const bool ok = qr < nrows;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ok) v = *reinterpret_cast<const uint4*>(P + ((int64_t)(r0 + qr) * HI + col % HI) * a.dI + key_dim<KS>(ks, grp, KF != 0));
+        A[rb][ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * grp + i;
+        const int q2 = rb * QR + m / HI;
+        om[rb][i] = q2 < nrows ? a.omega[(int64_t)(r0 + q2) * HI + m % HI] : 0.f;
+      }
+    }
+  }
+
+  // Scores of the loaded keys: sc[u][rb][q] is the score of entry
+  // e0 + 16u + col for row(rb, q, grp).
+  template <int EB>
+  __device__ __forceinline__ void scores(KeyRegs<KS, KF, EB>& K, float (&sc)[EB][RB][RPL]) const {
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      uint4 kv[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (KF == 1) kv[ks] = fp8x8_to_bf16x8(K.k8[u][ks]);
+        else if constexpr (KF == 2) kv[ks] = e2m1x8_to_bf16x8(K.k4[u][ks], K.ms[u][ks]);
+        else kv[ks] = K.kv[u][ks];
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb][ks], __builtin_bit_cast(bf16x8_t, kv[ks]), acc, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) {
+          float s = 0.f;
+#pragma unroll
+          for (int h = 0; h < HI; ++h) s = fmaf(om[rb][q * HI + h], relu_bits(acc[q * HI + h]), s);
+          if constexpr (KF == 1) s *= K.rscale[u];
+          sc[u][rb][q] = s;
+        }
+      }
+    }
+  }
+};
+
 template <int KS, int HI, int KF = 0>
 __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
-  constexpr int QR = 16 / HI;                // query rows per MFMA row block
-  constexpr int RB = kRowsPerBlock / QR;     // MFMA row blocks per block
-  constexpr int RPL = 4 / HI;                // query rows per accumulator lane
+  using Tile = RowTile<KS, HI, KF, kRowsPerBlock>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int gps = (a.Tq + kRowsPerBlock - 1) / kRowsPerBlock;  // row groups per sequence
@@ -152,81 +286,398 @@ __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
   }
   const int64_t w0 = (int64_t)blockIdx.x * (4 * kRowsEntriesPerWave) + (int64_t)wave * kRowsEntriesPerWave;
   if (w0 >= nv_max) return;  // uniform per wave
-  // A operands: lane (col, grp) holds (row rb*QR + col/HI, head col%HI), dims 32*ks + 8*grp ..
-  bf16x8_t A[RB][KS];
-  float om[RB][4];
-  const uint16_t* P = reinterpret_cast<const uint16_t*>(a.p);
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int qr = rb * QR + col / HI;
-    const bool ok = qr < nrows;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (ok) v = *reinterpret_cast<const uint4*>(P + ((int64_t)(r0 + qr) * HI + col % HI) * a.dI + key_dim<KS>(ks, grp, KF != 0));
-      A[rb][ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
-    // weights of the accumulator rows 4*grp + i: (row rb*QR + (4*grp + i)/HI, head (4*grp + i)%HI)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * grp + i;
-      const int q2 = rb * QR + m / HI;
-      om[rb][i] = q2 < nrows ? a.omega[(int64_t)(r0 + q2) * HI + m % HI] : 0.f;
-    }
-  }
-  const char* K = reinterpret_cast<const char*>(a.ikey);
-  const int64_t rowb = key_row_bytes(a, KF);
+  Tile T;
+  T.load(a, r0, nrows, col, grp);
   constexpr int EB = 4;  // 16-entry blocks in flight
   const int64_t wend = min(w0 + kRowsEntriesPerWave, min(nv_max, a.max_entries));
   for (int64_t e0 = w0; e0 < wend; e0 += 16 * EB) {
-    uint4 kv[EB][KS];
-    uint2 k8[EB][KS];
-    float rscale[EB];
-    uint32_t k4[EB][KS];
-    float ms[EB][KS];
-#pragma unroll
-    for (int u = 0; u < EB; ++u) {
-      int64_t e = e0 + u * 16 + col;
-      if (e >= nseq) e = nseq - 1;  // clamp: stays inside the sequence's keys
-      const char* row = K + (e_base + e) * rowb;
-      if constexpr (KF == 1) {
-        load_fp8_slices<KS>(row, grp, k8[u]);
-        rscale[u] = *reinterpret_cast<const float*>(row + a.dI);
-      } else if constexpr (KF == 2) {
-        load_mx_slices<KS>(row, grp, a.dI, k4[u], ms[u]);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
-      }
-    }
+    KeyRegs<KS, KF, EB> K;
+    K.load(a, e_base, nseq, e0, col, grp);
+    float sc[EB][Tile::RB][Tile::RPL];
+    T.template scores<EB>(K, sc);
 #pragma unroll
     for (int u = 0; u < EB; ++u) {
       const int64_t e = e0 + u * 16 + col;
       const bool e_ok = e < wend;
-      if constexpr (KF == 1) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = fp8x8_to_bf16x8(k8[u][ks]);
-      } else if constexpr (KF == 2) {
+      for (int rb = 0; rb < Tile::RB; ++rb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = e2m1x8_to_bf16x8(k4[u][ks], ms[u][ks]);
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb][ks], __builtin_bit_cast(bf16x8_t, kv[u][ks]), acc, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < RPL; ++q) {
-          float sc = 0.f;
-#pragma unroll
-          for (int h = 0; h < HI; ++h) sc = fmaf(om[rb][q * HI + h], fmaxf(acc[q * HI + h], 0.f), sc);
-          const int qr = rb * QR + (4 * grp) / HI + q;
-          if constexpr (KF == 1) sc *= rscale[u];
-          if (e_ok && qr < nrows) a.scores[(int64_t)(r0 + qr) * a.max_entries + e] = sc;
+        for (int q = 0; q < Tile::RPL; ++q) {
+          const int qr = Tile::row(rb, q, grp);
+          if (e_ok && qr < nrows) a.scores[(int64_t)(r0 + qr) * a.max_entries + e] = sc[u][rb][q];
         }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ many rows, streaming selection
+// Scores and the exact top-k of many rows per sequence in one launch, with
+// no score stored: block = 16 consecutive query rows of one sequence x every
+// entry they see, 8 waves.  The entries go by in rounds of 512 (each wave 64;
+// 256 and 128 for d_I = 128 and 256), in the row-tiled product above (so the
+// scores are bit-identical to index_score_rows'); each wave loads the keys of its next round before it
+// scores the current one.  Each row keeps, in LDS, a list of candidates as
+// 64-bit keys
+//     score_key(s) << 32 | ~j
+// (a total order: larger score first, then smaller entry), and a threshold
+// tau: a key with at least k listed keys at or above it, so that an entry
+// whose key is below tau cannot be among the row's k largest.  Every entry
+// at or above tau is listed.  When a round's keys would overflow a list, a
+// wave shrinks it first: histogram passes over the listed keys (256 equal bins of
+// the current key range per pass) narrow down a bin edge T with at least k
+// keys at or above it and at most k + k/4, the keys below T are dropped and T
+// becomes tau.  At the end the same passes find the exact k-th key, and the
+// chosen entries are sorted (bitonic, in LDS) and written in ascending
+// order.  For k up to kStreamMaxK (the lists of 16 rows fill the LDS).
+constexpr int kStreamRows = 16;
+constexpr int kStreamWaves = 8;
+// 16-entry blocks per wave and round (fewer for wide keys: the next round's
+// keys are held in registers beside the current one's)
+template <int KS>
+constexpr int stream_eb() { return KS >= 8 ? 1 : KS >= 4 ? 2 : 4; }
+constexpr int kStreamRound = kStreamWaves * 16 * 4;  // the largest round
+constexpr int kStreamMaxK = 512;
+constexpr int kStreamCap = kStreamMaxK + kStreamMaxK / 4 + kStreamRound;  // keys per row list
+
+// The lanes of one wave exchange data through LDS (each lane clears or
+// writes words that other lanes then update or read): the hardware keeps a
+// wave's LDS operations in order, and the fence keeps the compiler from
+// moving a lane's LDS access across this point or forwarding its own earlier
+// store to a later load (which would miss the other lanes' writes).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// A block barrier that orders LDS only: the waves of the streaming selection
+// share nothing else, and a full barrier would also wait for every global
+// load in flight (the next round's keys).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// f(L[j]) for this lane's j < n (j = lane, lane + 64, ...), four LDS reads in
+// flight at a time.
+template <class F>
+__device__ __forceinline__ void lds_walk(const uint64_t* L, uint32_t n, F f) {
+  const uint32_t lane = threadIdx.x & 63;
+  for (uint32_t j = lane; j < n; j += 256) {
+    uint64_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = j + 64 * i < n ? L[j + 64 * i] : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (j + 64 * i < n) f(v[i]);
+  }
+}
+
+// One wave: a key T such that at least `need` of the n listed keys L[0..n)
+// are >= T, and exactly `need` (exact) or at most need + slack.  Requires
+// n >= need >= 1, distinct keys and lo <= every key <= hi.  h: the wave's
+// 256 LDS bins.
+__device__ __forceinline__ uint64_t wave_threshold(const uint64_t* L, uint32_t n, uint32_t need, uint32_t slack,
+                                                   bool exact, uint32_t* h, uint64_t lo, uint64_t hi) {
+  const int lane = threadIdx.x & 63;
+  uint32_t rem = need;  // keys still needed from [lo, hi]
+  for (int pass = 0; pass < 9; ++pass) {
+    const uint64_t span = hi - lo;
+    const int sft = span < 256 ? 0 : 56 - __builtin_clzll(span);  // (span >> sft) < 256
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[lane * 4 + i] = 0;
+    wave_lds_sync();
+    lds_walk(L, n, [&](uint64_t v) {
+      if (v >= lo && v <= hi) atomicAdd(&h[(uint32_t)((v - lo) >> sft)], 1u);
+    });
+    wave_lds_sync();
+    uint32_t c[4], mine = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = h[lane * 4 + i];
+      mine += c[i];
+    }
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t tot = __shfl(incl, 63, 64);
+    const uint32_t above_mine = tot - incl;  // keys in the bins of the lanes after this one
+    // the bin holding the rem-th largest key: its index, the keys above it, its count
+    uint32_t pick = 0, above_b = 0, cnt_b = 0;
+    if (above_mine < rem && above_mine + mine >= rem) {
+      uint32_t acc = above_mine;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (acc < rem && acc + c[i] >= rem) {
+          pick = (uint32_t)(lane * 4 + i);
+          above_b = acc;
+          cnt_b = c[i];
+        }
+        acc += c[i];
       }
     }
+    const uint64_t who = __ballot(cnt_b != 0);
+    const int src = who ? __ffsll((long long)who) - 1 : 0;
+    pick = __shfl(pick, src, 64);
+    above_b = __shfl(above_b, src, 64);
+    cnt_b = __shfl(cnt_b, src, 64);
+    rem -= above_b;
+    const uint64_t edge = lo + ((uint64_t)pick << sft);
+    if (cnt_b == rem || (!exact && cnt_b - rem <= slack) || sft == 0 || !who) return edge;
+    lo = edge;
+    const uint64_t top = edge + ((1ull << sft) - 1);
+    hi = top < hi ? top : hi;
+  }
+  return lo;
+}
+
+// One wave: keeps the keys >= t of L[0..n) at the front of L, in order, and
+// returns their number.  In place: four chunks of 64 are read before any of
+// them is written, and the writes never pass the reads.
+__device__ __forceinline__ uint32_t wave_compact(uint64_t* L, uint32_t n, uint64_t t) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t out = 0;
+  for (uint32_t j = 0; j < n; j += 256) {
+    uint64_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t jj = j + 64 * i + lane;
+      v[i] = jj < n ? L[jj] : 0;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t jj = j + 64 * i + lane;
+      const bool kp = jj < n && v[i] >= t;
+      const uint64_t bk = __ballot(kp);
+      if (kp) L[out + __popcll(bk & below)] = v[i];
+      out += (uint32_t)__popcll(bk);
+    }
+    wave_lds_sync();
+  }
+  return out;
+}
+
+template <int KS, int HI, int KF = 0>
+__global__ __launch_bounds__(kStreamWaves * 64) void index_topk_rows(IndexParams a) {
+  using Tile = RowTile<KS, HI, KF, kStreamRows>;
+  constexpr int RB = Tile::RB, RPL = Tile::RPL, EB = stream_eb<KS>();
+  constexpr int ROUND = kStreamWaves * 16 * EB;  // entries per round
+  __shared__ uint64_t s_list[kStreamRows][kStreamCap];
+  __shared__ uint32_t s_h[kStreamWaves][256];
+  __shared__ uint64_t s_tau[kStreamRows];   // tau (every listed key is at or above it) ...
+  __shared__ uint64_t s_max[kStreamRows];   // ... and the largest listed key
+  __shared__ float s_tauf[kStreamRows];    // tau's score ...
+  __shared__ uint32_t s_etau[kStreamRows]; // ... and the largest entry it admits at that score
+  __shared__ uint32_t s_n[kStreamRows];     // listed keys
+  __shared__ uint32_t s_add[kStreamRows];   // keys the round lists
+  __shared__ uint32_t s_base[kStreamRows];  // where the round's keys go
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int gps = (a.Tq + kStreamRows - 1) / kStreamRows;  // row groups per sequence
+  const int b = blockIdx.x / gps;
+  const int t0 = (blockIdx.x % gps) * kStreamRows;
+  const int nrows = min(kStreamRows, a.Tq - t0);
+  const int r0 = b * a.Tq + t0;
+  const int64_t e_base = a.csa_off[b];
+  const int64_t nseq = a.csa_off[b + 1] - e_base;
+  const uint32_t k = (uint32_t)a.k;
+  if (threadIdx.x < kStreamRows) {
+    s_tau[threadIdx.x] = 0;
+    s_max[threadIdx.x] = 0;
+    s_tauf[threadIdx.x] = -__builtin_inff();
+    s_etau[threadIdx.x] = 0xFFFFFFFFu;
+    s_n[threadIdx.x] = 0;
+    s_add[threadIdx.x] = 0;
+  }
+  // visible entries of each row (rows past nrows see none); the block's most
+  uint32_t nv_lane = 0;
+  if (lane < nrows) nv_lane = (uint32_t)row_visible(a, r0 + lane, nseq);
+  uint32_t nv_max = nv_lane;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nv_max = max(nv_max, (uint32_t)__shfl_xor(nv_max, o, 64));
+  // this lane's rows: row(rb, q, grp)
+  uint32_t nv_r[RB][RPL];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int q = 0; q < RPL; ++q) nv_r[rb][q] = (uint32_t)__shfl(nv_lane, Tile::row(rb, q, grp), 64);
+  Tile T;
+  T.load(a, r0, nrows, col, grp);
+  const char* seq = reinterpret_cast<const char*>(a.ikey) + e_base * KeyRegs<KS, KF, EB>::kRowBytes;
+  const uint32_t nseq32 = (uint32_t)nseq;
+  // two key buffers: a round scores one while the next round's keys load into the other
+  KeyRegs<KS, KF, EB> K0, K1;
+  if (nv_max > 0) K0.load_rows(seq, (uint32_t)wave * 16 * EB, nseq32, col, grp);
+  lds_barrier();
+  // A round: score the current keys (the next round's load in flight),
+  // count the keys to list per row (s_add), then -- after a barrier -- the
+  // owner wave of each row shrinks its list if the round's keys would not fit,
+  // and records where they go (s_base); after a second barrier every lane
+  // writes its keys.  The keys are tested against tau as it stood when the
+  // round began: a shrink in between may leave some of them below the new
+  // tau (extra candidates, which the final selection drops).
+  auto round = [&](KeyRegs<KS, KF, EB>& cur, KeyRegs<KS, KF, EB>& nxt, uint32_t base) {
+    float tf[RB][RPL];
+    uint32_t et[RB][RPL];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int q = 0; q < RPL; ++q) {
+        tf[rb][q] = s_tauf[Tile::row(rb, q, grp)];
+        et[rb][q] = s_etau[Tile::row(rb, q, grp)];
+      }
+    const uint32_t e0 = base + (uint32_t)wave * 16 * EB;
+    // unconditional (the addresses are clamped into the sequence, and the
+    // filter drops entries no row sees): branches here would make the
+    // compiler wait for the loads in flight
+    nxt.load_rows(seq, e0 + ROUND, nseq32, col, grp);
+    float sc[EB][RB][RPL];
+    T.template scores<EB>(cur, sc);
+    // listed: keys >= tau, i.e. a score above tau's, or equal to it with an
+    // entry at most tau's (NaN scores pass).  The float test !(s < tau's
+    // score) passes a superset; the exact test runs only when a lane of the
+    // wave passes it.  bits[rb][q]: the lane's listed entries u of row(rb, q).
+    uint32_t bits[RB][RPL];
+    bool pass_any = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int q = 0; q < RPL; ++q) {
+        bits[rb][q] = 0;
+#pragma unroll
+        for (int u = 0; u < EB; ++u) pass_any |= !(sc[u][rb][q] < tf[rb][q]);
+      }
+    if (__ballot(pass_any)) {
+#pragma unroll
+      for (int u = 0; u < EB; ++u) {
+        const uint32_t e = e0 + (uint32_t)(u * 16 + col);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int q = 0; q < RPL; ++q) {
+            const float s = sc[u][rb][q];
+            const bool keep = (!(s < tf[rb][q])) & ((s != tf[rb][q]) | (e <= et[rb][q])) & (e < nv_r[rb][q]);
+            bits[rb][q] |= (uint32_t)keep << u;
+          }
+      }
+    }
+    uint32_t any = 0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int q = 0; q < RPL; ++q) any |= bits[rb][q];
+    const bool wave_any = __ballot(any != 0) != 0;
+    // the lane's place among the round's keys of each of its rows (one LDS
+    // atomic per row, all issued before any result is used)
+    uint32_t slot[RB][RPL];
+    if (wave_any) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int q = 0; q < RPL; ++q)
+          slot[rb][q] = atomicAdd(&s_add[Tile::row(rb, q, grp)], (uint32_t)__popc(bits[rb][q]));
+    }
+    lds_barrier();  // the round's counts are complete
+    // a list is shrunk when the round's keys would overflow it, and every
+    // 4th round when it is more than three quarters full (rows fill at
+    // similar rates, so their shrinks tend to fall in the same rounds and the
+    // waves wait for each other less)
+    const bool trim = ((base / ROUND) & 3) == 3;
+    for (int r = wave; r < nrows; r += kStreamWaves) {
+      const uint32_t add = s_add[r];
+      uint32_t n = s_n[r];
+      if ((add != 0 && n + add > (uint32_t)kStreamCap) ||
+          (trim && n > k + k / 4 && n + add > (uint32_t)(kStreamCap - ROUND / 2))) {
+        uint64_t* L = s_list[r];
+        uint64_t t = wave_threshold(L, n, k, k / 4, false, s_h[wave], s_tau[r], s_max[r]);
+        // no key has the pattern of -0 (score_key maps it to +0's): the next key up admits the same set
+        if ((uint32_t)(t >> 32) == 0x7FFFFFFFu) t = 0x8000000000000000ull;
+        wave_lds_sync();
+        n = wave_compact(L, n, t);
+        if (lane == 0) {
+          const uint32_t kt = (uint32_t)(t >> 32);
+          s_tau[r] = t;
+          s_tauf[r] = kt ? __uint_as_float((kt & 0x80000000u) ? (kt & 0x7FFFFFFFu) : ~kt) : -__builtin_inff();
+          s_etau[r] = ~(uint32_t)t;
+        }
+      }
+      if (lane == 0) {
+        s_base[r] = n;
+        s_n[r] = n + add;
+        s_add[r] = 0;
+      }
+    }
+    lds_barrier();  // lists shrunk, places of the round's keys known
+    if (wave_any) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) slot[rb][q] += s_base[Tile::row(rb, q, grp)];
+      uint64_t kmax[RB][RPL];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) kmax[rb][q] = 0;
+#pragma unroll
+      for (int u = 0; u < EB; ++u) {
+        const uint32_t e = e0 + (uint32_t)(u * 16 + col);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int q = 0; q < RPL; ++q)
+            if (bits[rb][q] & (1u << u)) {
+              const int qr = Tile::row(rb, q, grp);
+              const uint32_t sl = slot[rb][q] + (uint32_t)__popc(bits[rb][q] & ((1u << u) - 1u));
+              const uint64_t key = ((uint64_t)score_key(sc[u][rb][q]) << 32) | (uint64_t)(~e);
+              kmax[rb][q] = key > kmax[rb][q] ? key : kmax[rb][q];
+              if (sl < (uint32_t)kStreamCap) s_list[qr][sl] = key;
+            }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int q = 0; q < RPL; ++q)
+          if (bits[rb][q]) atomicMax(&s_max[Tile::row(rb, q, grp)], kmax[rb][q]);
+    }
+  };
+  for (uint32_t base = 0; base < nv_max; base += 2 * ROUND) {
+    round(K0, K1, base);
+    if (base + ROUND >= nv_max) break;
+    round(K1, K0, base + ROUND);
+  }
+  lds_barrier();  // the last round's keys are listed
+  // the exact k-th key of each row, the chosen entries sorted by entry
+  for (int r = wave; r < nrows; r += kStreamWaves) {
+    uint64_t* L = s_list[r];
+    int32_t* out = a.idx + (int64_t)(r0 + r) * a.k;
+    const uint32_t n = min(s_n[r], (uint32_t)kStreamCap);
+    uint32_t nc = n;
+    if (n > k) {
+      const uint64_t t = wave_threshold(L, n, k, 0, true, s_h[wave], s_tau[r], s_max[r]);
+      wave_lds_sync();
+      nc = wave_compact(L, n, t);  // == k
+    }
+    wave_lds_sync();
+    // entries of the chosen keys behind them in the same list, padded to a power of two, sorted
+    uint32_t* E = reinterpret_cast<uint32_t*>(L + kStreamMaxK);
+    uint32_t P = 1;
+    while (P < nc) P <<= 1;
+    for (uint32_t j = (uint32_t)lane; j < P; j += 64) E[j] = j < nc ? ~(uint32_t)L[j] : 0xFFFFFFFFu;
+    for (uint32_t size = 2; size <= P; size <<= 1)
+      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+        wave_lds_sync();
+        for (uint32_t i = (uint32_t)lane; i < P / 2; i += 64) {
+          const uint32_t x0 = 2 * stride * (i / stride) + (i % stride), x1 = x0 + stride;
+          const uint32_t va = E[x0], vb = E[x1];
+          if ((va > vb) == ((x0 & size) == 0)) {
+            E[x0] = vb;
+            E[x1] = va;
+          }
+        }
+      }
+    wave_lds_sync();
+    for (uint32_t j = (uint32_t)lane; j < k; j += 64) out[j] = j < nc ? (int32_t)E[j] : -1;
   }
 }
 
@@ -296,7 +747,6 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
 // index order.
 constexpr int kRowThreads = 1024;
 constexpr int kRowLoads = 8;    // score loads in flight per thread and pass
-constexpr int kRowBitmapWords = kRowMaxEntries / 32;
 
 __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
   __shared__ uint32_t h1[4096];
@@ -593,6 +1043,48 @@ int launch_index_score(const void* p, const float* omega, const void* ikey, cons
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 
+// The scores and the selection of lca_csa_index_topk in one launch for calls
+// with many rows per sequence and no scores requested (index_topk_rows).
+// Returns false, launching nothing, where that kernel does not apply.
+bool index_topk_stream_applies(int B, int Tq, int HI, int dI, int k, int64_t maxN, int dtype) {
+  const bool keys = dtype == LCA_BF16 || dtype == LCA_BF16_FP8KEY || dtype == LCA_BF16_MXFP4KEY;
+  return keys && rows_mode(Tq, maxN) && k <= kStreamMaxK && (HI == 1 || HI == 2 || HI == 4) && dI % 32 == 0 &&
+         dI <= 256 &&
+         (int64_t)B * ((Tq + kStreamRows - 1) / kStreamRows) <= INT32_MAX;
+}
+
+int launch_index_topk_stream(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
+                             const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w, int64_t maxN,
+                             int32_t* idx, void* ws, int dtype, hipStream_t stream) {
+  IndexParams a = make_params(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, idx, nullptr, ws);
+  const int kf = dtype == LCA_BF16_FP8KEY ? 1 : dtype == LCA_BF16_MXFP4KEY ? 2 : 0;
+  const dim3 g((unsigned)(B * ((Tq + kStreamRows - 1) / kStreamRows)));
+  const dim3 blk(kStreamWaves * 64);
+#define LCA_STREAM2(KSv, F8)                                                                      \
+  switch (HI) {                                                                                   \
+    case 1: hipLaunchKernelGGL((index_topk_rows<KSv, 1, F8>), g, blk, 0, stream, a); break;      \
+    case 2: hipLaunchKernelGGL((index_topk_rows<KSv, 2, F8>), g, blk, 0, stream, a); break;      \
+    default: hipLaunchKernelGGL((index_topk_rows<KSv, 4, F8>), g, blk, 0, stream, a); break;     \
+  }
+#define LCA_STREAM(KSv)    \
+  if (kf == 1) {           \
+    LCA_STREAM2(KSv, 1)    \
+  } else if (kf == 2) {    \
+    LCA_STREAM2(KSv, 2)    \
+  } else {                 \
+    LCA_STREAM2(KSv, 0)    \
+  }
+  switch (dI / 32) {
+    case 1: LCA_STREAM(1) break;
+    case 2: LCA_STREAM(2) break;
+    case 4: LCA_STREAM(4) break;
+    default: LCA_STREAM(8) break;
+  }
+#undef LCA_STREAM
+#undef LCA_STREAM2
+  return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+}
+
 int launch_compress(const lca_compress_stream* streams, int n, const int64_t* tok_off, const int64_t* done_len,
                     int B, float eps, int dtype, hipStream_t stream);
 
@@ -844,6 +1336,9 @@ int launch_index_topk_noalloc(const void* p, const float* omega, const void* ike
                        reinterpret_cast<uint32_t*>(ws), words);
     if (hipPeekAtLastError() != hipSuccess) return LCA_ERR_HIP;
   }
+  if (!scores && index_topk_stream_applies(B, Tq, HI, dI, k, maxN, dtype))
+    return launch_index_topk_stream(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, idx, ws, dtype,
+                                    stream);
   int rc = launch_index_score(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, scores, ws, dtype, stream);
   if (rc != LCA_OK) return rc;
   return launch_topk_select(csa_off, q_pos, B, Tq, k, m, w, maxN, idx, scores, ws, stream);

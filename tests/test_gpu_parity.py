@@ -687,6 +687,10 @@ def test_topk_crowded_zero_ties(path):
         ws = layer.index_workspace(tq, maxN, "cuda")
         idx = ops.csa_index_topk(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
                                  maxN, ws, scores=s_gpu)
+        # no scores requested: the streaming selection (no score stored), the same lists
+        idx_s = ops.csa_index_topk(raw["p"], raw["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w,
+                                   maxN, ws)
+        assert torch.equal(idx_s, idx), "streaming selection differs from the stored-scores path"
         out = None
     torch.cuda.synchronize()
     ikey = f64(caches.ikey)
@@ -1007,9 +1011,13 @@ def test_many_rows_topk_equals_single_rows():
     scores = torch.full((rows, max_csa), float("nan"), dtype=torch.float32, device="cuda")
     idx = ops.csa_index_topk(d["p"], d["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa, ws,
                              scores=scores)
+    # no scores requested: the streaming selection (no score stored), the same lists
+    idx_s = ops.csa_index_topk(d["p"], d["omega"], caches.ikey, caches.csa_off, q_pos, cfg.k, cfg.m, cfg.w, max_csa,
+                               ws)
     ws1 = torch.zeros(ops.csa_index_topk_workspace(1, max_csa, cfg.k), dtype=torch.uint8, device="cuda")
     sc1 = torch.full((1, max_csa), float("nan"), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
+    assert torch.equal(idx_s, idx), "streaming selection differs from the stored-scores path"
     for r in range(rows):
         nv = ocmp.n_visible(int(q_pos[r].item()), cfg.m, cfg.w)
         i1 = ops.csa_index_topk(d["p"][r:r + 1].contiguous(), d["omega"][r:r + 1].contiguous(), caches.ikey,
