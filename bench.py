@@ -58,8 +58,8 @@ TRAFFIC = {
                   "long_context_attention_20_amd/csrc/lca_attn_block.h",
                   "long_context_attention_20_amd/csrc/lca_common.h",
                   "long_context_attention_20_amd/csrc/lca_topk.h"],
-        "sha1": "891598b042815fbab2b8b438d1ffe49bf70bc4db",
-        "fetch_kib": 6388.5, "write_kib": 16694.6, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha1": "c78c11b81ce07fde177f26a46ec0331cec1a1ca4",
+        "fetch_kib": 6378.8, "write_kib": 16694.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 

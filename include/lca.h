@@ -203,7 +203,9 @@ int lca_csa_index_topk(const void* p, const float* omega, const void* ikey, cons
  * library runs on holds its own copy until the process ends).  The call
  * allocates nothing.  A call whose workspace (lca_csa_index_topk_workspace of
  * the same arguments) exceeds that size returns LCA_ERR_WORKSPACE and
- * launches nothing.  Every call on a GPU shares that GPU's array: calls that
+ * launches nothing -- except a call that the streaming selection takes
+ * (scores NULL and the many-row bounds of lca_csa_index_topk), which needs
+ * no workspace at all and runs at any size.  Every call on a GPU shares that GPU's array: calls that
  * overlap on one GPU (on different streams, or from different threads) race
  * and must not be issued.  The array keeps the last call's contents; the
  * first call on a device, and every call whose (B*Tq, max_entries, k)

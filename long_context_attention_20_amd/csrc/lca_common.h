@@ -252,6 +252,27 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---------------------------------------------------------------- LDS ordering
+// The lanes of one wave exchange data through LDS (each lane writes words that
+// other lanes then update or read): the hardware keeps a wave's LDS
+// operations in order, and the fence keeps the compiler from moving a lane's
+// LDS access across this point or forwarding its own earlier store to a later
+// load (which would miss the other lanes' writes).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// A block barrier that orders LDS only: global loads in flight (a prefetch,
+// loads straight into LDS) stay in flight, where __syncthreads would wait for
+// every one of them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- launch status
 // Implemented in lca_abi.hip: records a message for lca_last_error().
 void set_error(const char* fmt, ...);

@@ -339,26 +339,6 @@ constexpr int kStreamRound = kStreamWaves * 16 * 4;  // the largest round
 constexpr int kStreamMaxK = 512;
 constexpr int kStreamCap = kStreamMaxK + kStreamMaxK / 4 + kStreamRound;  // keys per row list
 
-// The lanes of one wave exchange data through LDS (each lane clears or
-// writes words that other lanes then update or read): the hardware keeps a
-// wave's LDS operations in order, and the fence keeps the compiler from
-// moving a lane's LDS access across this point or forwarding its own earlier
-// store to a later load (which would miss the other lanes' writes).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// A block barrier that orders LDS only: the waves of the streaming selection
-// share nothing else, and a full barrier would also wait for every global
-// load in flight (the next round's keys).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // f(L[j]) for this lane's j < n (j = lane, lane + 64, ...), four LDS reads in
 // flight at a time.
 template <class F>
@@ -935,12 +915,14 @@ static IndexParams make_params(const void* p, const float* omega, const void* ik
   IndexParams a{};
   a.p = p; a.omega = omega; a.ikey = ikey; a.csa_off = csa_off; a.q_pos = q_pos;
   a.Tq = Tq; a.HI = HI; a.dI = dI; a.k = k; a.m = m; a.w = w; a.max_entries = maxN;
-  a.scores = scores ? const_cast<float*>(scores) : reinterpret_cast<float*>(base + L.scores);
-  a.hist = reinterpret_cast<uint32_t*>(base + L.hist);
-  a.ctr = reinterpret_cast<unsigned long long*>(base + L.ctr);
-  a.done = reinterpret_cast<uint32_t*>(base + L.done);
-  a.sel = reinterpret_cast<int32_t*>(base + L.sel);
-  a.cand = reinterpret_cast<uint64_t*>(base + L.cand);
+  // (no workspace: the streaming selection, which reads none of these)
+  auto at = [&](size_t off) { return base ? base + off : nullptr; };
+  a.scores = scores ? const_cast<float*>(scores) : reinterpret_cast<float*>(at(L.scores));
+  a.hist = reinterpret_cast<uint32_t*>(at(L.hist));
+  a.ctr = reinterpret_cast<unsigned long long*>(at(L.ctr));
+  a.done = reinterpret_cast<uint32_t*>(at(L.done));
+  a.sel = reinterpret_cast<int32_t*>(at(L.sel));
+  a.cand = reinterpret_cast<uint64_t*>(at(L.cand));
   a.idx = idx;
   a.chunk = (int)score_chunk(rows, maxN);
   a.nstripe = hist_stripes(rows, maxN);
@@ -1300,6 +1282,11 @@ __global__ __launch_bounds__(256) void zero_words(uint32_t* p, int64_t n) {
 int launch_index_topk_noalloc(const void* p, const float* omega, const void* ikey, const int64_t* csa_off,
                               const int32_t* q_pos, int B, int Tq, int HI, int dI, int k, int m, int w,
                               int64_t maxN, int32_t* idx, float* scores, int dtype, hipStream_t stream) {
+  // many rows and no scores requested: the streaming selection, which keeps
+  // its state in LDS and needs no workspace
+  if (!scores && index_topk_stream_applies(B, Tq, HI, dI, k, maxN, dtype))
+    return launch_index_topk_stream(p, omega, ikey, csa_off, q_pos, B, Tq, HI, dI, k, m, w, maxN, idx, nullptr, dtype,
+                                    stream);
   const int rows = B * Tq;
   const size_t need = index_topk_workspace(rows, maxN, k);
   if (need > kScratchBytes) {

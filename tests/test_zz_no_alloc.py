@@ -37,12 +37,12 @@ def _setup(cfg):
     return d, caches, q_pos, max_csa
 
 
-def _run(cfg, d, caches, q_pos, max_csa, noalloc):
+def _run(cfg, d, caches, q_pos, max_csa, noalloc, keep_scores=True):
     L = _lib()
     rows = q_pos.numel()
     B = caches.csa_off.numel() - 1
     idx = torch.full((rows, cfg.k), -7, dtype=torch.int32, device="cuda")
-    sc = torch.full((rows, max_csa), float("nan"), dtype=torch.float32, device="cuda")
+    sc = torch.full((rows, max_csa), float("nan"), dtype=torch.float32, device="cuda") if keep_scores else None
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     args = (_p(d["p"]), _p(d["omega"]), _p(caches.ikey), _p(caches.csa_off), _p(q_pos), B, rows // B, cfg.HI, cfg.dI,
             cfg.k, cfg.m, cfg.w, max_csa)
@@ -95,3 +95,21 @@ def test_noalloc_rejects_oversized():
     assert rc == L.LCA_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.all(idx == -7), "a rejected call launched work"
+
+
+def test_noalloc_many_rows_without_workspace():
+    """A prefill-like call (40 rows of a sequence, no scores requested) whose
+    workspace would exceed the static array: the streaming selection takes
+    it without any workspace, with the indices of the workspace call, on two
+    calls in a row (the second with fewer rows)."""
+    L = _lib()
+    cap = L.lib.lca_csa_index_topk_noalloc_max_bytes()
+    for n, (tq, lens) in enumerate(((40, (200000,)), (33, (120000,)))):
+        cfg = li.small(f"noalloc_rows{n}", 144, lens, tq=tq, H=16, D=64, k=512)
+        d, caches, q_pos, max_csa = _setup(cfg)
+        need = L.lib.lca_csa_index_topk_workspace(q_pos.numel(), max_csa, cfg.k)
+        print(f"[noalloc rows] call {n}: rows={q_pos.numel()} max_entries={max_csa} workspace={need} bytes", flush=True)
+        assert need > cap
+        got, _ = _run(cfg, d, caches, q_pos, max_csa, noalloc=True, keep_scores=False)
+        ref, _ = _run(cfg, d, caches, q_pos, max_csa, noalloc=False, keep_scores=True)
+        assert torch.equal(got, ref), f"call {n}: indices differ from the workspace call"
