@@ -15,8 +15,9 @@ Decode step (one query row per sequence, or a few), three calls on one stream:
                   the sparse attention over it; the HCA entry the step
                   completes, when it completes one
     swa_merge     sink + merge of every partial
-Prefill chunks (many rows per sequence) run kv_compress, csa_index_score,
-csa_topk_select and hybrid_attn_merge.
+Prefill chunks (many rows per sequence) run kv_compress, csa_index_topk (the
+scores and a streaming exact top-k in one launch, no score stored) and
+hybrid_attn_merge.
 """
 from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
