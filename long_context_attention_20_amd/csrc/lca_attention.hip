@@ -47,14 +47,14 @@ constexpr int kRowsBlockRows = 128;  // (query, head) rows per block
 constexpr int kRowsStreams = 2;      // gathered streams (queries) per block at most
 constexpr int kRowsIdx = 1024;       // gathered slots per stream and split
 
-// LDS rows of the row-tiled kernel are 1 KiB with no padding; the 16-byte
-// chunk c of tile row r sits at chunk c ^ rows_swz(r).  The swizzle keeps
-// both read patterns free of bank conflicts, for 32 banks (8 lanes per cycle
-// of a 16-byte read, 16 of an 8-byte one) and for 64 (16 and 32): the K-row
-// reads (16 rows, one chunk each) see rows_swz(r) distinct mod 16 over 16
-// consecutive rows and mod 8 over 8 aligned ones; the transposed V reads (4 or
-// 8 rows, two neighbouring chunks each) see rows_swz(r) >> 1 distinct over 4
-// or 8 aligned rows.
+// LDS rows of the row-tiled kernel: the 1 KiB key row in order, padded to
+// 1056 bytes.  With the pad, consecutive rows start 32 bytes further along
+// the banks, which keeps both read patterns free of bank conflicts on gfx950
+// (measured: SQ_LDS_BANK_CONFLICT 0 per launch, against 1.8e8 cycles for 1 KiB
+// rows with the 16-byte chunks XOR-swizzled per row): the K-row reads (16
+// rows, one 16-byte chunk each) and the transposed V reads (4 or 8 rows, two
+// neighbouring 8-byte halves each).
+constexpr int kRowsPitch = 528;  // bf16 elements per LDS row
 // One wave moves 64 x 16 bytes from global memory straight into LDS: lane
 // l's 16 bytes at its own address gsrc land at LDS byte offset lds + 16 l
 // (lds uniform).  Issued as assembly so that the compiler does not make later
@@ -65,10 +65,6 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, const void* lds_dst)
   const uint32_t lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(lds) : "memory", "m0");
-}
-
-__device__ __forceinline__ int rows_swz(int r) {
-  return (((r >> 2) & 1) << 3) | ((r & 3) << 1) | (((r >> 2) ^ (r >> 3)) & 1);
 }
 
 // Wave-uniform 64-bit value in scalar registers.
@@ -85,7 +81,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int D = 512;
   constexpr int KS = D / 32;      // k-steps of S over D
   constexpr int DB = D / 16;      // 16-dim blocks of O
-  constexpr int PITCH = D;        // bf16 elements per LDS row (chunks swizzled, no padding)
+  constexpr int PITCH = kRowsPitch;  // bf16 elements per LDS row (padded)
   constexpr int TILE_ELEMS = kRowsTile * PITCH;
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kRowsStreams][2][TILE_ELEMS];
   __shared__ int32_t sidx[kRowsStreams][kRowsIdx];
@@ -243,15 +239,15 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
         } else {
           ent = kc < bhi ? kc : blo;
         }
-        // lane l fills LDS chunk l with the row's chunk l ^ rows_swz(row)
-        const uint16_t* src = kvp + (first + ent) * D + ((lane ^ rows_swz(row)) * 8);
+        // lane l fills the row's chunk l
+        const uint16_t* src = kvp + (first + ent) * D + lane * 8;
         lds_dma16(src, tile + row * PITCH);
       }
     };
     // window rows: RMS over D of the raw row, then the rotary turn by the
     // token's position, rounded to bf16, in place (the wave that loaded a row
-    // normalises it once its loads have landed; LDS chunk l of the row holds
-    // its channels 8 (l ^ rows_swz(row)) ..)
+    // normalises it once its loads have landed; lane l holds the row's
+    // channels 8 l ..)
     auto norm_rows = [&](int64_t tt) {
       uint16_t* tile = tiles[0][(tt - tb) & 1];
       for (int v = 0; v < rpw; ++v) {
@@ -269,7 +265,7 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
         for (int e = 0; e < 8; ++e) f[e] *= inv;
         if (ROPE) {
           const int64_t kc = blo + tt * kRowsTile + row;  // the token position load_tile read
-          rope_turn<8>(f, (lane ^ rows_swz(row)) * 8, D, a.rope, (double)(kc < bhi ? kc : blo));
+          rope_turn<8>(f, lane * 8, D, a.rope, (double)(kc < bhi ? kc : blo));
         }
         *reinterpret_cast<uint4*>(rowp) = BF16::pack(f);
       }
@@ -292,18 +288,12 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
       if (wave_on && vm != 0) {  // uniform per wave
         // ---- S^T for tile rows 0..15 (p0) and 16..31 (p1)
         f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
-        // rows c16 and 16 + c16 (same swizzle), logical chunk 4 ks + g: with
-        // ks = 4j + i the physical chunk is 16j + ((4i + g) ^ swz), four
-        // per-lane offsets and an immediate.  The swizzle goes through an empty
-        // asm so that the offsets are formed here, not held over the loop.
-        int sk = rows_swz(c16);
-        asm volatile("" : "+v"(sk));
-        int koff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) koff[i] = c16 * PITCH + ((4 * i + g) ^ sk) * 8;
+        // rows c16 and 16 + c16, chunk 4 ks + g: one per-lane offset and an
+        // immediate
+        const uint16_t* kp = tile + c16 * PITCH + g * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint16_t* k0p = tile + koff[ks & 3] + (ks >> 2) * 128;
+          const uint16_t* k0p = kp + ks * 32;
           const uint4 a0 = *reinterpret_cast<const uint4*>(k0p);
           const uint4 a1 = *reinterpret_cast<const uint4*>(k0p + 16 * PITCH);
           p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), qb[ks], p0, 0, 0, 0);
@@ -346,21 +336,13 @@ __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)
           // ---- O^T += V^T . P^T: lane c16 of group g reads rows 4g + c16/4 (and
           // 16 + ...) at columns 16*db + 4*(c16%4); the transpose read returns
           // dim 16*db + c16 of tile rows 4g..4g+3 (and 16+4g..)
-          // (logical chunk 2 db + bit 1 of c16, half c16 & 1; rows 4g + c16/4
-          // and 16 + 4g + c16/4 share the swizzle)
-          // (with db = 8j + i the physical chunk is 16j + ((2i + hh) ^ swz):
-          // eight per-lane offsets and an immediate)
-          const int tr_r = 4 * g + (c16 >> 2);
-          int st = rows_swz(tr_r);
-          asm volatile("" : "+v"(st));
-          const int hh = (c16 >> 1) & 1;
-          int toff[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) toff[i] = tr_r * PITCH + 4 * (c16 & 1) + ((2 * i + hh) ^ st) * 8;
+          // (chunk 2 db + bit 1 of c16, half c16 & 1: one per-lane offset and
+          // an immediate)
+          const uint16_t* vp = tile + (4 * g + (c16 >> 2)) * PITCH + 8 * ((c16 >> 1) & 1) + 4 * (c16 & 1);
 #pragma unroll
           for (int db = 0; db < DB; db += 2) {
-            const uint16_t* t0 = tile + toff[db & 7] + (db >> 3) * 128;
-            const uint16_t* t1 = tile + toff[(db + 1) & 7] + ((db + 1) >> 3) * 128;
+            const uint16_t* t0 = vp + db * 16;
+            const uint16_t* t1 = vp + (db + 1) * 16;
             const s4_t v00 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)t0);
             const s4_t v01 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(t0 + 16 * PITCH));
             const s4_t v10 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)t1);
