@@ -354,6 +354,14 @@ __device__ __forceinline__ void lds_walk(const uint64_t* L, uint32_t n, F f) {
   }
 }
 
+// 64-bit lane exchange within a 16-lane DPP row (lanes with no source read 0)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = dpp_u32<CTRL, 0xF>((uint32_t)x), hi = dpp_u32<CTRL, 0xF>((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 // One wave: a key T such that at least `need` of the n listed keys L[0..n)
 // are >= T, and exactly `need` (exact) or at most need + slack.  Requires
 // n >= need >= 1, distinct keys and lo <= every key <= hi.  h: the wave's
@@ -552,11 +560,26 @@ __global__ __launch_bounds__(kStreamWaves * 64) void index_topk_rows(IndexParams
     // atomic per row, all issued before any result is used)
     uint32_t slot[RB][RPL];
     if (wave_any) {
+      // the 16 lanes of a lane group share their rows: a prefix over the
+      // group (DPP within the 16-lane row) and one LDS atomic per group and
+      // row (sixteen lanes adding to one word in one instruction serialise)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int q = 0; q < RPL; ++q)
-          slot[rb][q] = atomicAdd(&s_add[Tile::row(rb, q, grp)], (uint32_t)__popc(bits[rb][q]));
+        for (int q = 0; q < RPL; ++q) {
+          const uint32_t c = (uint32_t)__popc(bits[rb][q]);
+          uint32_t incl = c;
+          incl += dpp_u32<0x111, 0xF>(incl);  // row_shr:1
+          incl += dpp_u32<0x112, 0xF>(incl);  // row_shr:2
+          incl += dpp_u32<0x114, 0xF>(incl);  // row_shr:4
+          incl += dpp_u32<0x118, 0xF>(incl);  // row_shr:8
+          // the group's last lane holds its total
+          uint32_t at = 0;
+          if (col == 15 && incl) at = atomicAdd(&s_add[Tile::row(rb, q, grp)], incl);
+          const uint32_t a0 = __builtin_amdgcn_readlane(at, 15), a1 = __builtin_amdgcn_readlane(at, 31);
+          const uint32_t a2 = __builtin_amdgcn_readlane(at, 47), a3 = __builtin_amdgcn_readlane(at, 63);
+          slot[rb][q] = (grp & 2 ? (grp & 1 ? a3 : a2) : (grp & 1 ? a1 : a0)) + incl - c;
+        }
     }
     lds_barrier();  // the round's counts are complete
     // a list is shrunk when the round's keys would overflow it, and every
@@ -614,11 +637,19 @@ __global__ __launch_bounds__(kStreamWaves * 64) void index_topk_rows(IndexParams
               if (sl < (uint32_t)kStreamCap) s_list[qr][sl] = key;
             }
       }
+      // the group's largest key of each row (a prefix maximum over the 16
+      // lanes ends in the last one) and one LDS atomic per group and row
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int q = 0; q < RPL; ++q)
-          if (bits[rb][q]) atomicMax(&s_max[Tile::row(rb, q, grp)], kmax[rb][q]);
+        for (int q = 0; q < RPL; ++q) {
+          uint64_t m = kmax[rb][q];
+          m = max_u64(m, dpp_u64<0x111>(m));  // row_shr:1
+          m = max_u64(m, dpp_u64<0x112>(m));  // row_shr:2
+          m = max_u64(m, dpp_u64<0x114>(m));  // row_shr:4
+          m = max_u64(m, dpp_u64<0x118>(m));  // row_shr:8
+          if (col == 15 && m) atomicMax(&s_max[Tile::row(rb, q, grp)], m);
+        }
     }
   };
   for (uint32_t base = 0; base < nv_max; base += 2 * ROUND) {
