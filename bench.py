@@ -228,14 +228,15 @@ class Position:
 
 
 class Runner:
-    def __init__(self, cfg, R, dev, split_csa=0, split_hca=0, front=None):
+    def __init__(self, cfg, R, dev, split_csa=0, split_hca=0, front=None, half_partials=True):
         import torch
         from long_context_attention_20_amd import HybridAttention, ops
         self.torch, self.ops = torch, ops
         self.cfg = cfg
         a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
                             split_csa=split_csa or None, split_hca=split_hca or None, ikey=cfg.ikey,
-                            rope=cfg.rope, rope_base=cfg.rope_base, dual=cfg.dual, sepv=cfg.sepv)
+                            rope=cfg.rope, rope_base=cfg.rope_base, dual=cfg.dual, sepv=cfg.sepv,
+                            half_partials=half_partials)
         self.attn = a
         self.layers = [LayerState(cfg, r, a, dev) for r in range(R)]
         rows = cfg.B * cfg.tq
@@ -642,6 +643,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
     ap.add_argument("--split-csa", type=int, default=0, help="entry splits of the sparse attention (0: default)")
     ap.add_argument("--split-hca", type=int, default=0, help="entry splits of the HCA attention (0: default)")
+    ap.add_argument("--half-partials", type=int, default=1,
+                    help="1: the decode step's attention partials in fp16 (default), 0: fp32")
     ap.add_argument("--front", type=int, default=-1,
                     help="1: decode step in front form (HCA and window beside the scores), 0: HCA and window "
                          "beside the sparse blocks; -1: the layer's default for the workload")
@@ -675,7 +678,8 @@ def main():
     sb = step_bytes(cfg)
     R = args.layers or max(1, -(-2 * MALL_BYTES // sb))
     t0 = time.perf_counter()
-    run = Runner(cfg, R, dev, args.split_csa, args.split_hca, front=None if args.front < 0 else bool(args.front))
+    run = Runner(cfg, R, dev, args.split_csa, args.split_hca, front=None if args.front < 0 else bool(args.front),
+                 half_partials=bool(args.half_partials))
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     print(f"[bench] {cfg.name}: {R} layers built in {setup_s:.1f} s; {sb / 1e6:.2f} MB/step; "

@@ -368,7 +368,7 @@ typedef struct lca_attn_source {
   int32_t m2, w2;        /* DENSE: stride and window of the entries */
   int32_t W;             /* WINDOW: window length, >= 1 */
   int32_t n_split;       /* key-range parts */
-  float* o_part;         /* fp32 [n_split, B*Tq, H, D] */
+  void* o_part;          /* fp32 [n_split, B*Tq, H, D]; fp16 with o_half */
   float* lse;            /* fp32 [n_split, B*Tq, H] */
   /* LCA_SRC_TOPK only (zero otherwise): */
   void* ws;              /* index workspace of the preceding score call */
@@ -410,15 +410,28 @@ typedef struct lca_attn_source {
                                tokens (RMS-normalised and turned on load as the window
                                keys).  Such calls take the per-row kernel, also with
                                many query rows per sequence */
+  int32_t o_half;           /* 0: o_part is fp32.  1: o_part holds IEEE fp16 values (lse
+                               stays fp32), half the bytes the partials write and the
+                               merge reads.  A partial is a convex combination of value
+                               rows, so each of its elements is at most the largest
+                               value element in magnitude: the caller guarantees that
+                               bound is below 65504 (RMS-normalised entries and window
+                               tokens are at most sqrt(D) times their norm weight);
+                               fp16 then rounds each element to 2^-11 of itself, a
+                               quarter of a bf16 output's rounding.  Only calls of
+                               dtype LCA_BF16 with H a multiple of 16 and few query rows
+                               per sequence (the matrix-core kernel that writes one
+                               partial per block); elsewhere LCA_ERR_UNSUPPORTED */
 } lca_attn_source;
 
 int lca_hybrid_attn(const lca_attn_source* srcs, int n_src, const void* q, const int32_t* q_pos, int B, int Tq,
                     int H, int D, float scale, float eps, int dtype, void* stream);
 
 typedef struct lca_partial {
-  const float* o;   /* [n_split, B*Tq, H, D] */
+  const void* o;    /* [n_split, B*Tq, H, D], fp32 (fp16 with o_half) */
   const float* lse; /* [n_split, B*Tq, H]    */
   int32_t n_split;
+  int32_t o_half;   /* 1: o holds fp16 values, as an lca_attn_source with o_half wrote them */
 } lca_partial;
 
 size_t lca_swa_merge_workspace(int n_rows, int H, int D);

@@ -45,7 +45,8 @@ class CompressStream(ctypes.Structure):
 
 
 class Partial(ctypes.Structure):
-    _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("n_split", ctypes.c_int32)]
+    _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("n_split", ctypes.c_int32),
+                ("o_half", ctypes.c_int32)]
 
 
 class AttnSource(ctypes.Structure):
@@ -57,6 +58,7 @@ class AttnSource(ctypes.Structure):
         ("scores", ctypes.c_void_p), ("idx_out", ctypes.c_void_p),
         ("done_len", ctypes.c_void_p), ("part", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
         ("rope_base", ctypes.c_float), ("tiles_per_split", ctypes.c_int32), ("v", ctypes.c_void_p),
+        ("o_half", ctypes.c_int32),
     ]
 
 

@@ -339,7 +339,7 @@ int lca_csa_index_topk_noalloc(const void* p, const float* omega, const void* ik
 }
 
 static int check_attn(const char* what, const void* q, const void* kv, const void* off, const void* lst,
-                      int B, int Tq, int H, int D, float scale, float eps, int n_split, const float* o,
+                      int B, int Tq, int H, int D, float scale, float eps, int n_split, const void* o,
                       const float* lse, int dtype) {
   LCA_REQUIRE(q && kv && off && lst && o && lse, LCA_ERR_INVALID_ARG, "%s: a required pointer is NULL", what);
   LCA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1, LCA_ERR_INVALID_ARG, "%s: B=%d Tq=%d H=%d", what, B, Tq, H);
@@ -428,6 +428,10 @@ static int check_hybrid(const lca_attn_source* srcs, int n_src, const void* q, c
                 x.part);
     LCA_REQUIRE(x.tiles_per_split >= 0, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: tiles_per_split=%d < 0", i,
                 x.tiles_per_split);
+    LCA_REQUIRE(x.o_half == 0 || x.o_half == 1, LCA_ERR_INVALID_ARG, "hybrid_attn: source %d: o_half=%d", i,
+                x.o_half);
+    LCA_REQUIRE(x.o_half == 0 || (dtype == LCA_BF16 && H % 16 == 0), LCA_ERR_UNSUPPORTED,
+                "hybrid_attn: source %d: fp16 partials need dtype bf16 and H a multiple of 16", i);
     LCA_REQUIRE(x.rope_dims == srcs[0].rope_dims && x.rope_base == srcs[0].rope_base, LCA_ERR_INVALID_ARG,
                 "hybrid_attn: source %d: every source of a call gives the same rope_dims and rope_base", i);
     if (x.tiles_per_split > 0 && (x.kind == LCA_SRC_GATHER || x.kind == LCA_SRC_TOPK))
@@ -520,7 +524,8 @@ int lca_swa_merge(const void* q, const void* x, const int64_t* tok_off, const in
   LCA_REQUIRE(n_parts == 0 || parts != nullptr, LCA_ERR_INVALID_ARG, "swa_merge: parts is NULL");
   int slots = W > 0 ? 1 : 0;
   for (int p = 0; p < n_parts; ++p) {
-    LCA_REQUIRE(parts[p].o && parts[p].lse && parts[p].n_split >= 1 && parts[p].n_split <= 256,
+    LCA_REQUIRE(parts[p].o && parts[p].lse && parts[p].n_split >= 1 && parts[p].n_split <= 256 &&
+                    (parts[p].o_half == 0 || parts[p].o_half == 1),
                 LCA_ERR_INVALID_ARG, "swa_merge: part %d is invalid", p);
     slots += parts[p].n_split;
   }

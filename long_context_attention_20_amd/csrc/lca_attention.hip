@@ -507,9 +507,10 @@ __global__ __launch_bounds__(64) void attn_valu(AttnParams a) {
 constexpr int kMaxParts = 8;
 constexpr int kMaxSlots = 512;
 struct MergeParams {
-  const float* o[kMaxParts];
+  const void* o[kMaxParts];     // fp32, or fp16 where o_half
   const float* lse[kMaxParts];
   int n_split[kMaxParts];
+  int o_half[kMaxParts];
   int n_parts;
   int n_slots;
   const float* sink;
@@ -519,88 +520,174 @@ struct MergeParams {
 
 // One block per (row, head, 256-dim part): 256 threads = 4 slot groups x 64
 // lanes; a lane owns 4 consecutive dims (or fewer for D = 64), a slot group
-// every fourth slot.  The slots' addresses are resolved once, one thread per
-// slot, into LDS; then every wave loads all the slots' lse values and its own
-// slots' partials in one batch (one memory round trip), computes the slot
-// weights itself, and the groups' sums meet in LDS.
+// (wave) every fourth slot.  The block first resolves every slot's addresses
+// (one thread per slot) into LDS tables; every later load is then a global
+// one (the pointers are cast to the global address space: a generic load
+// would count against the LDS wait, so that each table read would also wait
+// for every partial requested before it).  Every wave reads all the slots'
+// lse values and its own slots' partials and lse in one batch (one memory
+// round trip), computes the slot weights itself, and the groups' sums meet
+// in LDS.
 constexpr int kMergeGroups = 4;
-constexpr int kMergeSlotsPerWave = 32;  // partial loads in flight per lane and batch
 
-template <typename ET, int DPL>
+// The block's slot tables: slot s (slots list the parts in order, split t
+// of part p) -> the address of its partial's (row, head) row at element
+// `first` (bit 0 set for fp16 partials; addresses are at least 4-byte
+// aligned) and of its lse.  The parts are walked with compile-time indices:
+// a part chosen per thread would index the kernel arguments at run time,
+// which the compiler serves from a copy in scratch memory.
+template <int NT>  // threads of the block
+__device__ __forceinline__ void merge_tables(const MergeParams& a, int64_t RH, int64_t rh, int first,
+                                             uint64_t* s_o, const float** s_l) {
+  int beg = 0;
+#pragma unroll
+  for (int p = 0; p < kMaxParts; ++p) {
+    if (p < a.n_parts) {  // uniform
+      const int n = a.n_split[p];
+      const int esz = a.o_half[p] ? 2 : 4;
+      for (int t = threadIdx.x; t < n; t += NT) {
+        const int64_t e = (int64_t)t * RH + rh;
+        s_o[beg + t] = (uint64_t)(uintptr_t)(static_cast<const char*>(a.o[p]) + (e * a.D + first) * esz) |
+                       (uint64_t)(a.o_half[p] ? 1 : 0);
+        s_l[beg + t] = a.lse[p] + e;
+      }
+      beg += n;
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T gload(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)(p);
+}
+
+// PH: the partials' types -- 0 every part fp32, 1 every part fp16, 2 some
+// of each (the type chosen per slot with a branch, which makes the compiler
+// wait for each slot's load: for the rare mixed call only).
+// SPW: slots per wave and batch (16 for calls of at most 64 slots, whose
+// lse values then take one load per lane; else 32): every load of a batch is
+// issued, whether its slot exists or not, so the batch fits the call.
+template <typename ET, int DPL, int PH, int SPW>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
+  constexpr int LLOC = SPW == 16 ? 1 : kMaxSlots / 64;  // lse words per lane
   __shared__ float red[kMergeGroups][64 * DPL];
-  __shared__ const float* s_o[kMaxSlots];
+  __shared__ uint64_t s_o[kMaxSlots];
   __shared__ const float* s_l[kMaxSlots];
-  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t RH = (int64_t)a.rows * a.H;
   const int parts_d = (a.D + 64 * DPL - 1) / (64 * DPL);
   const int64_t rh = blockIdx.x / parts_d;
   const int dpart = (blockIdx.x % parts_d) * 64 * DPL;
   const int h = (int)(rh % a.H);
-  for (int i = threadIdx.x; i < a.n_slots; i += blockDim.x) {
-    int p = 0, t = i;
-    while (p + 1 < a.n_parts && t >= a.n_split[p]) { t -= a.n_split[p]; ++p; }
-    s_o[i] = a.o[p] + ((int64_t)t * RH + rh) * a.D + dpart;
-    s_l[i] = a.lse[p] + (int64_t)t * RH + rh;
-  }
+  const int ns = a.n_slots;
+  merge_tables<256>(a, RH, rh, dpart, s_o, s_l);
   __syncthreads();
-  const int nmine = (a.n_slots - grp + kMergeGroups - 1) / kMergeGroups;
+  // the lse of every slot (lane l: slots l, l + 64, ...); loads are
+  // unconditional (a slot beyond the list reads slot 0 and is not used), so
+  // that each batch is straight-line code with every load in flight at once
+  float l_loc[LLOC];
+#pragma unroll
+  for (int i = 0; i < LLOC; ++i) {
+    const int sl = lane + 64 * i;
+    l_loc[i] = gload(s_l[sl < ns ? sl : 0]);
+  }
+  const int nmine = (ns - grp + kMergeGroups - 1) / kMergeGroups;
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   float lse_tot = -INFINITY;
-  for (int base = 0; base == 0 || base < nmine; base += kMergeSlotsPerWave) {
-    // lse of every slot (lane l: slots l, l + 64, ...; first batch only) and
-    // this group's partials, all in flight together
-    float l_loc[kMaxSlots / 64];
-    if (base == 0) {
+  // one batch of this wave's slots; the first is peeled off the loop (a
+  // loop entered with the lse loads in flight would wait for them first)
+  auto batch = [&](const int base) {
+    // this wave's slots grp + 4 j: the lane's DPL elements, fp32 words or
+    // fp16 pairs (converted where they are used)
+    constexpr int WPL = PH == 1 ? (DPL + 1) / 2 : DPL;  // 4-byte words per lane and slot
+    uint32_t w[SPW][WPL];
+    float lw[SPW];
 #pragma unroll
-      for (int i = 0; i < kMaxSlots / 64; ++i) {
-        const int sidx = lane + 64 * i;
-        l_loc[i] = sidx < a.n_slots ? *s_l[sidx] : -INFINITY;
-      }
-    }
-    float v[kMergeSlotsPerWave][DPL];
-    float lw[kMergeSlotsPerWave];
-#pragma unroll
-    for (int u = 0; u < kMergeSlotsPerWave; ++u) {
+    for (int u = 0; u < SPW; ++u) {
       const int j = base + u;
-      const bool ok = j < nmine;
-      const int sidx = ok ? grp + kMergeGroups * j : 0;
-      lw[u] = ok ? *s_l[sidx] : -INFINITY;
-      const float* op = (ok ? s_o[sidx] : s_o[0]) + lane * DPL;
-      if constexpr (DPL == 4) {
-        const float4 x = ok ? *reinterpret_cast<const float4*>(op) : make_float4(0.f, 0.f, 0.f, 0.f);
-        v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
-      } else {
+      const int sidx = j < nmine ? grp + kMergeGroups * j : 0;
+      const uint64_t ad = s_o[sidx];
+      lw[u] = gload(s_l[sidx]);
+      const char* bp = reinterpret_cast<const char*>((uintptr_t)(ad & ~(uint64_t)1));
+      if constexpr (PH == 0) {
+        if constexpr (DPL == 4) {
+          const u32x4 x = gload(reinterpret_cast<const u32x4*>(bp + lane * 16));
+          w[u][0] = x[0]; w[u][1] = x[1]; w[u][2] = x[2]; w[u][3] = x[3];
+        } else {
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) v[u][i] = ok ? op[i] : 0.f;
+          for (int i = 0; i < DPL; ++i) w[u][i] = gload(reinterpret_cast<const uint32_t*>(bp) + lane * DPL + i);
+        }
+      } else if constexpr (PH == 1) {
+        if constexpr (DPL == 4) {
+          const u32x2 x = gload(reinterpret_cast<const u32x2*>(bp + lane * 8));
+          w[u][0] = x[0]; w[u][1] = x[1];
+        } else {
+          // DPL 1: the word holding the lane's element and its neighbour's
+          w[u][0] = gload(reinterpret_cast<const uint32_t*>(bp + ((lane * DPL * 2) & ~3)));
+        }
+      } else {
+        if (ad & 1) {
+#pragma unroll
+          for (int i = 0; i < DPL; ++i)
+            w[u][i] = gload(reinterpret_cast<const uint16_t*>(bp) + lane * DPL + i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) w[u][i] = gload(reinterpret_cast<const uint32_t*>(bp) + lane * DPL + i);
+        }
       }
     }
     if (base == 0) {
       // total log-sum-exp over every slot and the sink (each wave alike)
+#pragma unroll
+      for (int i = 0; i < LLOC; ++i)
+        if (lane + 64 * i >= ns) l_loc[i] = -INFINITY;
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kMaxSlots / 64; ++i) mx = fmaxf(mx, l_loc[i]);
+      for (int i = 0; i < LLOC; ++i) mx = fmaxf(mx, l_loc[i]);
       mx = wave_max(mx, 64);
       if (a.sink) mx = fmaxf(mx, a.sink[h]);
       float den = 0.f;
       if (mx != -INFINITY) {
 #pragma unroll
-        for (int i = 0; i < kMaxSlots / 64; ++i) den += l_loc[i] == -INFINITY ? 0.f : expf(l_loc[i] - mx);
+        for (int i = 0; i < LLOC; ++i) den += l_loc[i] == -INFINITY ? 0.f : expf(l_loc[i] - mx);
       }
       den = wave_sum(den, 64);
       if (a.sink && mx != -INFINITY) den += expf(a.sink[h] - mx);
       lse_tot = mx != -INFINITY ? mx + logf(den) : -INFINITY;
     }
 #pragma unroll
-    for (int u = 0; u < kMergeSlotsPerWave; ++u) {
+    for (int u = 0; u < SPW; ++u) {
+      const int j = base + u;
+      if (j >= nmine) continue;  // uniform
       const bool use = lw[u] != -INFINITY && lse_tot != -INFINITY;
       const float wgt = use ? expf(lw[u] - lse_tot) : 0.f;
+      float v[DPL];
+      if constexpr (PH == 0) {
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wgt, v[u][i], acc[i]);
+        for (int i = 0; i < DPL; ++i) v[i] = __uint_as_float(w[u][i]);
+      } else if constexpr (PH == 1) {
+        if constexpr (DPL == 1) {
+          v[0] = (float)__builtin_bit_cast(f16x2_t, w[u][0])[lane & 1];
+        } else {
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) v[i] = (float)__builtin_bit_cast(f16x2_t, w[u][i / 2])[i & 1];
+        }
+      } else {
+        const uint32_t sidx = grp + kMergeGroups * j;
+        const bool hf = s_o[sidx] & 1;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i)
+          v[i] = hf ? (float)__builtin_bit_cast(_Float16, (uint16_t)w[u][i]) : __uint_as_float(w[u][i]);
+      }
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
     }
-  }
+  };
+  batch(0);
+  for (int base = SPW; base < nmine; base += SPW) batch(base);
 #pragma unroll
   for (int i = 0; i < DPL; ++i) red[grp][lane * DPL + i] = acc[i];
   __syncthreads();
@@ -655,16 +742,19 @@ __global__ __launch_bounds__(64 * kRowsWaves) void merge_rows_kernel(MergeParams
     if (s < a.n_slots) {  // uniform
       int t;
       const int p = slot_part(s, &t);
-      const float* op = a.o[p] + ((int64_t)t * RH + rh) * a.D + lane * DPL;
-      if constexpr (DPL % 4 == 0) {
+      const int64_t e0 = ((int64_t)t * RH + rh) * a.D + lane * DPL;
+      // fp32 or fp16 partials without a branch (as merge_kernel): fp16
+      // elements are read as 4-byte words of pairs (the second half of the
+      // lane's fp32-sized reads repeats the first)
+      const bool hf = a.o_half[p] != 0;
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(static_cast<const char*>(a.o[p]) + e0 * (hf ? 2 : 4));
+      uint32_t w[DPL];
 #pragma unroll
-        for (int i = 0; i < DPL; i += 4) {
-          const float4 x = *reinterpret_cast<const float4*>(op + i);
-          v[s][i] = x.x; v[s][i + 1] = x.y; v[s][i + 2] = x.z; v[s][i + 3] = x.w;
-        }
-      } else {
+      for (int i = 0; i < DPL; ++i) w[i] = wp[hf ? (i % (DPL / 2)) : i];
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) v[s][i] = op[i];
+      for (int i = 0; i < DPL; ++i) {
+        const f16x2_t hx = __builtin_bit_cast(f16x2_t, w[i / 2]);
+        v[s][i] = hf ? (float)hx[i & 1] : __uint_as_float(w[i]);
       }
     }
   }
@@ -806,6 +896,7 @@ static int merge_sources(const lca_attn_source* srcs, int n_src, int rows, int H
     parts[i].o = srcs[i].o_part;
     parts[i].lse = srcs[i].lse;
     parts[i].n_split = srcs[i].n_split;
+    parts[i].o_half = srcs[i].o_half;
   }
   return launch_merge(parts, n_src, nullptr, nullptr, mr->sink, rows, H, D, mr->out, dtype, stream);
 }
@@ -857,9 +948,15 @@ static int launch_attention_impl(const lca_attn_source* srcs, int n_src, const v
   int splits = 0, topk = -1;
   for (int i = 0; i < n_src; ++i) {
     const lca_attn_source& in = srcs[i];
+    if (in.o_half) {
+      set_error("attention: fp16 partials (o_half) are written by the few-rows kernel only, not by the "
+                "row-tiled one (%d query rows per sequence)", Tq);
+      return LCA_ERR_UNSUPPORTED;
+    }
     AttnSrc& d = a.s[i];
     d.kv = in.kv; d.off = in.off; d.idx = in.idx; d.kind = in.kind; d.k = in.k; d.m2 = in.m2; d.w2 = in.w2;
-    d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
+    d.W = in.W; d.n_split = in.n_split; d.o_part = static_cast<float*>(in.o_part); d.lse = in.lse;
+    d.o_half = in.o_half; d.idx_out = nullptr;
     d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split; d.v = in.v;
     d.block_begin = splits;
     splits += in.n_split;
@@ -926,6 +1023,11 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
   a.rope = make_rope_tab(srcs[0].rope_dims, srcs[0].rope_base);
   apply_diag(&a);
   const bool mfma = dtype == LCA_BF16 && H % 16 == 0;
+  for (int i = 0; i < n_src; ++i)
+    if (srcs[i].o_half && !mfma) {
+      set_error("attention: fp16 partials (o_half) need dtype bf16 and H a multiple of 16 (H=%d)", H);
+      return LCA_ERR_UNSUPPORTED;
+    }
   int blocks = 0;
   int topk = -1;          // the TOPK source
   bool fused_topk = false;  // selected inside the attention blocks
@@ -934,7 +1036,8 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
     const lca_attn_source& in = srcs[i];
     AttnSrc& d = a.s[i];
     d.kv = in.kv; d.off = in.off; d.idx = in.idx; d.kind = in.kind; d.k = in.k; d.m2 = in.m2; d.w2 = in.w2;
-    d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
+    d.W = in.W; d.n_split = in.n_split; d.o_part = static_cast<float*>(in.o_part); d.lse = in.lse;
+    d.o_half = in.o_half; d.idx_out = nullptr;
     d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split; d.v = in.v;
     if (in.v) opt |= kOptValues;
     d.block_begin = blocks;
@@ -1061,7 +1164,8 @@ int setup_attention_front(const lca_attn_source* srcs, int n_src, const void* q,
     if (in.kind != LCA_SRC_DENSE && in.kind != LCA_SRC_WINDOW) return LCA_ERR_UNSUPPORTED;
     AttnSrc& d = a->s[i];
     d.kv = in.kv; d.off = in.off; d.idx = nullptr; d.kind = in.kind; d.k = 0; d.m2 = in.m2; d.w2 = in.w2;
-    d.W = in.W; d.n_split = in.n_split; d.o_part = in.o_part; d.lse = in.lse; d.idx_out = nullptr;
+    d.W = in.W; d.n_split = in.n_split; d.o_part = static_cast<float*>(in.o_part); d.lse = in.lse;
+    d.o_half = in.o_half; d.idx_out = nullptr;
     d.done_len = in.done_len; d.part = in.part; d.tps = in.tiles_per_split; d.v = nullptr;
     d.block_begin = blocks;
     blocks += in.n_split;
@@ -1078,9 +1182,11 @@ int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, cons
   MergeParams a{};
   int np = 0, ns = 0;
   for (int p = 0; p < n_parts; ++p) {
-    a.o[np] = parts[p].o; a.lse[np] = parts[p].lse; a.n_split[np] = parts[p].n_split; ns += parts[p].n_split; ++np;
+    a.o[np] = parts[p].o; a.lse[np] = parts[p].lse; a.n_split[np] = parts[p].n_split;
+    a.o_half[np] = parts[p].o_half;
+    ns += parts[p].n_split; ++np;
   }
-  if (win_o) { a.o[np] = win_o; a.lse[np] = win_lse; a.n_split[np] = 1; ns += 1; ++np; }
+  if (win_o) { a.o[np] = win_o; a.lse[np] = win_lse; a.n_split[np] = 1; a.o_half[np] = 0; ns += 1; ++np; }
   if (ns > kMaxSlots) {
     set_error("merge: %d partial slots, at most %d", ns, kMaxSlots);
     return LCA_ERR_UNSUPPORTED;
@@ -1113,16 +1219,26 @@ int launch_merge(const lca_partial* parts, int n_parts, const float* win_o, cons
     return LCA_ERR_UNSUPPORTED;
   }
   dim3 grid((unsigned)nblk);
-#define LCA_MERGE(ETy)                                                                            \
-  switch (D) {                                                                                    \
-    case 64: hipLaunchKernelGGL((merge_kernel<ETy, 1>), grid, dim3(256), 0, stream, a); break;   \
-    case 128: hipLaunchKernelGGL((merge_kernel<ETy, 2>), grid, dim3(256), 0, stream, a); break;  \
-    case 256:                                                                                     \
-    case 512: hipLaunchKernelGGL((merge_kernel<ETy, 4>), grid, dim3(256), 0, stream, a); break;  \
-    default: set_error("merge: D=%d not supported", D); return LCA_ERR_UNSUPPORTED;             \
+  int n_half = 0;
+  for (int p = 0; p < np; ++p) n_half += a.o_half[p] ? 1 : 0;
+  const int ph = n_half == 0 ? 0 : n_half == np ? 1 : 2;
+  const bool few = ns <= 64;  // 16 slots per wave and batch
+#define LCA_MERGE_PH(ETy, PH)                                                                             \
+  switch (D) {                                                                                           \
+    case 64: hipLaunchKernelGGL((merge_kernel<ETy, 1, PH, 32>), grid, dim3(256), 0, stream, a); break;   \
+    case 128: hipLaunchKernelGGL((merge_kernel<ETy, 2, PH, 32>), grid, dim3(256), 0, stream, a); break;  \
+    case 256:                                                                                            \
+    case 512:                                                                                            \
+      if (few) hipLaunchKernelGGL((merge_kernel<ETy, 4, PH, 16>), grid, dim3(256), 0, stream, a);        \
+      else hipLaunchKernelGGL((merge_kernel<ETy, 4, PH, 32>), grid, dim3(256), 0, stream, a);            \
+      break;                                                                                             \
+    default: set_error("merge: D=%d not supported", D); return LCA_ERR_UNSUPPORTED;                    \
   }
+#define LCA_MERGE(ETy)                                                         \
+  if (ph == 0) { LCA_MERGE_PH(ETy, 0) } else if (ph == 1) { LCA_MERGE_PH(ETy, 1) } else { LCA_MERGE_PH(ETy, 2) }
   if (dtype == LCA_BF16) { LCA_MERGE(BF16) } else { LCA_MERGE(F32) }
 #undef LCA_MERGE
+#undef LCA_MERGE_PH
   return hipPeekAtLastError() == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 

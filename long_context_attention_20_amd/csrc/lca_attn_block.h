@@ -56,7 +56,7 @@ struct AttnSrc {
   int W;                // WINDOW length
   int n_split;
   int block_begin;
-  float* o_part;        // [n_split, rows, H, D]
+  float* o_part;        // [n_split, rows, H, D], fp32 (fp16 with o_half)
   float* lse;           // [n_split, rows, H]
   // DENSE: part 1 keeps the entries complete within the first done_len[b]
   // tokens of sequence b, part 2 the entries completed after them (0: all)
@@ -64,6 +64,7 @@ struct AttnSrc {
   int part;
   int tps;              // > 0: 32-key tiles per split (a fixed partition); 0: from n_split
   const void* v;        // values, rows laid out as kv; null: the keys are the values
+  int o_half;           // 1: o_part holds fp16 values
 };
 
 constexpr int kMaxSrc = 3;
@@ -802,7 +803,15 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     const float4 v = *reinterpret_cast<const float4*>(ox + (kAttnHeads + hh) * XP + d);
     float o4[4] = {u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w};
     if ((OPT & kOptRope) && a.rope.dims) rope_turn<4>(o4, d, D, a.rope, -(double)qpos_r);  // -i on the output
-    __builtin_nontemporal_store(f32x4{o4[0], o4[1], o4[2], o4[3]}, reinterpret_cast<f32x4*>(op + (int64_t)i * 4));
+    if (S.o_half) {
+      // fp16 (round to nearest even), 8 bytes per lane
+      const f16x4 hv = {(_Float16)o4[0], (_Float16)o4[1], (_Float16)o4[2], (_Float16)o4[3]};
+      __builtin_nontemporal_store(hv, reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(S.o_part) +
+                                                               ((((int64_t)split * a.rows + r) * a.H + hbase) * D +
+                                                                (int64_t)i * 4)));
+    } else {
+      __builtin_nontemporal_store(f32x4{o4[0], o4[1], o4[2], o4[3]}, reinterpret_cast<f32x4*>(op + (int64_t)i * 4));
+    }
   }
   if (threadIdx.x < nh) {
     float M, f0, f1, lsum;

@@ -147,17 +147,56 @@ __device__ __forceinline__ void hist_flush(const uint32_t* lh, uint32_t* gh) {
 template <int KS, int KF = 0>
 __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, int cx, int64_t lim, uint32_t* lh) {
   const int b = r / a.Tq;
+  // the sequence's entry range and the row's position, requested together
   const int64_t e_base = a.csa_off[b];
-  const int64_t nv = row_visible(a, r, a.csa_off[b + 1] - e_base);
+  const int64_t e_end = a.csa_off[b + 1];
+  const int qi = a.q_pos[r];
+  // (an empty use of the three values here keeps the compiler from sinking
+  // one load below the division that needs the other: one wait for both)
+  asm volatile("" : : "s"(e_base), "s"(e_end), "s"(qi));
+  int64_t nv = n_windows((int64_t)qi + 1, a.m, a.w);
+  nv = min(min(nv, e_end - e_base), a.max_entries);  // as row_visible
   const int64_t c0 = (int64_t)cx * a.chunk;
   const int64_t c1 = min(min(c0 + a.chunk, nv), lim);
   if (cx == 0) clear_row_state(a, r);
   if (c0 >= c1) return;
   const bool do_hist = nv > a.k && !a.no_hist;
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  const char* K = reinterpret_cast<const char*>(a.ikey);
+  const int64_t rowb = key_row_bytes(a, KF);
+  float* S = a.scores + (int64_t)r * a.max_entries;
+  constexpr int U = 8;  // tiles in flight per wave
+  const int64_t ntile = (c1 - c0 + 15) / 16;
+  const int nw = (int)(blockDim.x >> 6);
+  // The key rows of a batch of U tiles (16 entries each; lane (col, grp)
+  // takes entry col's slices for lane group grp).  The wave's first batch is
+  // requested right after the query operand and the head weights, before the
+  // LDS histogram is cleared and the block synchronises, so that its memory
+  // latency overlaps them.
+  uint4 kv[U][KS];
+  uint2 k8[U][KS];
+  float sc[U];
+  uint32_t k4[U][KS];
+  float ms[U][KS];
+  auto load_batch = [&](int64_t t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t e = c0 + (t0 + u) * 16 + col;
+      if (e >= c1) e = c1 - 1;  // clamp: stays inside the visible entries
+      const char* row = K + (e_base + e) * rowb;
+      if constexpr (KF == 1) {
+        load_fp8_slices<KS>(row, grp, k8[u]);
+        sc[u] = *reinterpret_cast<const float*>(row + a.dI);
+      } else if constexpr (KF == 2) {
+        load_mx_slices<KS>(row, grp, a.dI, k4[u], ms[u]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
+      }
+    }
+  };
   // A operand: head `col` (zero beyond HI), dims 32*ks + 8*grp .. +7
   bf16x8_t A[KS];
   {
@@ -176,35 +215,12 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
     const int h = grp * 4 + i;
     om[i] = h < a.HI ? a.omega[(int64_t)r * a.HI + h] : 0.f;
   }
+  int64_t t0 = wave * U;
+  if (t0 < ntile) load_batch(t0);
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0;
   __syncthreads();
 
-  const char* K = reinterpret_cast<const char*>(a.ikey);
-  const int64_t rowb = key_row_bytes(a, KF);
-  float* S = a.scores + (int64_t)r * a.max_entries;
-  constexpr int U = 8;  // tiles in flight per wave
-  const int64_t ntile = (c1 - c0 + 15) / 16;
-  const int nw = (int)(blockDim.x >> 6);
-  for (int64_t t0 = wave * U; t0 < ntile; t0 += nw * U) {
-    uint4 kv[U][KS];
-    uint2 k8[U][KS];
-    float sc[U];
-    uint32_t k4[U][KS];
-    float ms[U][KS];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t e = c0 + (t0 + u) * 16 + col;
-      if (e >= c1) e = c1 - 1;  // clamp: stays inside the visible entries
-      const char* row = K + (e_base + e) * rowb;
-      if constexpr (KF == 1) {
-        load_fp8_slices<KS>(row, grp, k8[u]);
-        sc[u] = *reinterpret_cast<const float*>(row + a.dI);
-      } else if constexpr (KF == 2) {
-        load_mx_slices<KS>(row, grp, a.dI, k4[u], ms[u]);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kv[u][ks] = *reinterpret_cast<const uint4*>(row + (ks * 32 + grp * 8) * 2);
-      }
-    }
+  while (t0 < ntile) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // C[head][entry] = P[head][:] . K[entry][:]; lane (col, grp) holds the
@@ -228,6 +244,8 @@ __device__ __forceinline__ void score_chunk_mfma(const IndexParams& a, int r, in
         if (do_hist) hist_add(lh, part);
       }
     }
+    t0 += nw * U;
+    if (t0 < ntile) load_batch(t0);
   }
   __syncthreads();
   if (do_hist) hist_flush(lh, a.hist + ((int64_t)r * a.nstripe + cx % a.nstripe) * kHistBins);

@@ -228,9 +228,13 @@ def csa_topk_select(csa_off, q_pos, k: int, m: int, w: int, max_entries: int, ws
 
 # ---------------------------------------------------------------- attention partials
 
-def _parts_out(rows, H, D, n_split, device, o_part, lse):
+def _parts_out(rows, H, D, n_split, device, o_part, lse, half=False):
+    """Partial buffers: o_part fp32, or fp16 (half: the fp16 partials of the
+    matrix-core decode kernel); lse fp32."""
     if o_part is None:
-        o_part = torch.empty((n_split, rows, H, D), dtype=torch.float32, device=device)
+        o_part = torch.empty((n_split, rows, H, D), dtype=torch.float16 if half else torch.float32, device=device)
+    if o_part.dtype not in (torch.float32, torch.float16):
+        raise TypeError("o_part must be float32 or float16")
     if lse is None:
         lse = torch.empty((n_split, rows, H), dtype=torch.float32, device=device)
     return o_part, lse
@@ -320,7 +324,7 @@ def _attn_sources(q, q_pos, sources: Sequence[dict]):
                 raise ValueError(f"idx_out must be [{rows}, {k}]")
             ws_bytes, max_entries = ws.numel() * ws.element_size(), int(s["max_entries"])
         ns = int(s["n_split"])
-        o_part, lse = _parts_out(rows, H, D, ns, q.device, s.get("o_part"), s.get("lse"))
+        o_part, lse = _parts_out(rows, H, D, ns, q.device, s.get("o_part"), s.get("lse"), bool(s.get("o_half")))
         _dev(o_part, lse)
         done_len, part = s.get("done_len"), int(s.get("part", 0))
         if part:
@@ -335,7 +339,8 @@ def _attn_sources(q, q_pos, sources: Sequence[dict]):
                             int(s.get("m2", 1)), int(s.get("w2", 1)), int(s.get("W", 0)), ns, o_part.data_ptr(),
                             lse.data_ptr(), _addr(ws), ws_bytes or 0, max_entries or 0, _addr(scores), _addr(idx_out),
                             _addr(done_len) if part else None, part, int(s.get("rope", 0)),
-                            float(s.get("rope_base", 10000.0)), int(s.get("tiles_per_split", 0)), _addr(v))
+                            float(s.get("rope_base", 10000.0)), int(s.get("tiles_per_split", 0)), _addr(v),
+                            int(o_part.dtype == torch.float16))
         outs.append((o_part, lse))
     return arr, outs, B
 
@@ -345,7 +350,9 @@ def hybrid_attn(q, q_pos, sources: Sequence[dict], scale: float, eps: float):
     kind ("gather", "dense", "window" or "topk"), kv, off and n_split, plus
     idx (gather), m2 and w2 (dense), W (window), and optionally o_part / lse,
     tiles_per_split (a fixed partition of each row's keys), rope / rope_base
-    (the rotary embedding of the call: the same in every source) and, for a dense
+    (the rotary embedding of the call: the same in every source), o_half
+    (fp16 partials, allocated when o_part is not given; a given o_part's
+    dtype, float32 or float16, decides) and, for a dense
     source, part (1: the entries complete within the first done_len[b]
     tokens; 2: those completed after them) with done_len (int64 [B]).
     A "topk" source selects the sparse branch's entries from the scores a
@@ -382,7 +389,8 @@ def swa_merge_workspace(n_rows: int, H: int, D: int) -> int:
 
 def swa_merge(q, x, tok_off, q_pos, sink, parts, W: int, scale: float, eps: float, ws: torch.Tensor,
               out=None):
-    """parts: list of (o_part, lse) pairs.  Returns out [B*Tq, H, D] (q's dtype).
+    """parts: list of (o_part, lse) pairs (o_part float32 or float16).
+    Returns out [B*Tq, H, D] (q's dtype).
     With W = 0 only the partials and the sink are merged (x, tok_off, q_pos
     and ws may be None)."""
     _dev(q, x, tok_off, q_pos, sink, ws, out)
@@ -397,7 +405,9 @@ def swa_merge(q, x, tok_off, q_pos, sink, parts, W: int, scale: float, eps: floa
     arr = (Partial * max(1, len(parts)))()
     for i, (o, l) in enumerate(parts):
         _dev(o, l)
-        arr[i] = Partial(o.data_ptr(), l.data_ptr(), o.shape[0])
+        if o.dtype not in (torch.float32, torch.float16):
+            raise TypeError("partials must be float32 or float16")
+        arr[i] = Partial(o.data_ptr(), l.data_ptr(), o.shape[0], int(o.dtype == torch.float16))
     if out is None:
         out = torch.empty_like(q)
     if sink is not None and sink.dtype != torch.float32:

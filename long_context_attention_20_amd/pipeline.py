@@ -58,8 +58,12 @@ class HybridAttention:
                  w2: int = 128, W: int = 128, eps: float = 1e-6, scale: Optional[float] = None,
                  split_csa: Optional[int] = None, split_hca: Optional[int] = None, ikey: str = "bf16",
                  rope: int = 0, rope_base: float = 10000.0, dual: bool = False, sepv: bool = False,
-                 batch_invariant: bool = False, max_context: int = 1 << 20):
+                 batch_invariant: bool = False, max_context: int = 1 << 20, half_partials: bool = True):
         self.H, self.D, self.HI, self.dI, self.k = H, D, HI, dI, k
+        # half_partials: decode_step keeps the attention partials it merges
+        # as fp16 (bf16 inputs, H a multiple of 16); every partial is a convex
+        # combination of RMS-normalised value rows, far inside fp16's range
+        self.half_partials = bool(half_partials)
         # partial rotary embedding on the last `rope` dims of each head (0:
         # none): compressed entries are stored turned by the position of
         # their window's last token, queries and window tokens turn by their
@@ -370,7 +374,9 @@ class HybridAttention:
         if not self.batch_invariant:
             sc = self.split_csa or sc
             sh = self.split_hca or sh
-        part = lambda n: (torch.empty((n, rows, self.H, self.D), dtype=f32, device=device),
+        # fp16 partials (o_half) where the decode kernel writes them
+        odt = torch.float16 if (self.half_partials and dtype == torch.bfloat16 and self.H % 16 == 0) else f32
+        part = lambda n: (torch.empty((n, rows, self.H, self.D), dtype=odt, device=device),  # noqa: E731
                           torch.empty((n, rows, self.H), dtype=f32, device=device))
         return dict(
             sc=sc, sh=sh, sw=sw, max_csa=max(1, max_csa), max_hca=max_hca, front=front,

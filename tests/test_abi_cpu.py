@@ -288,3 +288,29 @@ def test_fp8_key_rows_rejects(L):
     rc = lib.lca_csa_index_score_append(P, P, P, P, P, 1, 1, 4, 64, 512, 4, 8, 1000, idx, None, 0, P, P,
                                         1e-6, None, P, lib.lca_csa_index_topk_workspace(1, 1000, 512), 2, None)
     assert rc == L.LCA_ERR_INVALID_ARG
+
+
+def test_half_partials_rejects(L):
+    """fp16 partials (o_half): 0 or 1 only; an fp32 call, or H not a multiple
+    of 16, cannot take them (the kernel that writes them is the bf16
+    matrix-core one); the merge checks the flag of every part."""
+    lib = L.lib
+    P = ctypes.c_void_p(256)
+    src = (L.AttnSource * 1)()
+
+    def gather(o_half):
+        src[0] = L.AttnSource(L.LCA_SRC_GATHER, 256, 256, 256, 64, 1, 1, 0, 2, 256, 256, None, 0, 0, None, None)
+        src[0].o_half = o_half
+
+    def call(dtype=1, H=64):
+        return lib.lca_hybrid_attn(src, 1, P, P, 1, 1, H, 512, 0.04, 1e-6, dtype, None)
+    gather(2)
+    assert call() == L.LCA_ERR_INVALID_ARG
+    gather(1)
+    assert call(dtype=0) == L.LCA_ERR_UNSUPPORTED      # fp32 call
+    assert call(H=24) == L.LCA_ERR_UNSUPPORTED         # generic (VALU) path
+    parts = (L.Partial * 1)()
+    parts[0] = L.Partial(256, 256, 1, 2)
+    need = lib.lca_swa_merge_workspace(1, 64, 512)
+    assert lib.lca_swa_merge(P, P, P, P, P, parts, 1, 1, 1, 64, 512, 128, 0.04, 1e-6, P, P, need, 1, None) == \
+        L.LCA_ERR_INVALID_ARG
