@@ -21,6 +21,7 @@ namespace lca {
 template <int D, bool TOPK, int FC = 1, int OPT = 0>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma(AttnParams a) {
   __shared__ __attribute__((aligned(16))) char lds_raw[AttnLds<D, TOPK>::kBytes];
+  warm_kernargs<sizeof(AttnParams)>();
   attn_block<D, TOPK, FC, OPT>(a, blockIdx.x, lds_raw);
 }
 
@@ -569,6 +570,7 @@ __device__ __forceinline__ T gload(const T* p) {
 // issued, whether its slot exists or not, so the batch fits the call.
 template <typename ET, int DPL, int PH, int SPW>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams a) {
+  warm_kernargs<sizeof(MergeParams)>();
   constexpr int LLOC = SPW == 16 ? 1 : kMaxSlots / 64;  // lse words per lane
   __shared__ float red[kMergeGroups][64 * DPL];
   __shared__ uint64_t s_o[kMaxSlots];
@@ -941,6 +943,7 @@ static int launch_attention_impl(const lca_attn_source* srcs, int n_src, const v
     return merge_sources(srcs, n_src, B * Tq, H, D, mr, dtype, stream);
   }
   AttnParams a{};
+  a.topk_src = -1;
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
   a.rope = make_rope_tab(srcs[0].rope_dims, srcs[0].rope_base);
@@ -1018,6 +1021,7 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
                                     int B, int Tq, int H, int D, float scale, float eps, int dtype,
                                     hipStream_t stream) {
   AttnParams a{};
+  a.topk_src = -1;
   a.q = q; a.q_pos = q_pos; a.Tq = Tq; a.H = H; a.D = D; a.rows = B * Tq;
   a.scale = scale; a.eps = eps; a.n_src = n_src;
   a.rope = make_rope_tab(srcs[0].rope_dims, srcs[0].rope_base);
@@ -1048,6 +1052,7 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
       fused_topk = mfma && in.max_entries <= kBitmapEntries && !topk_rows_mode(Tq, in.max_entries);
       if (fused_topk) {
         d.idx_out = in.idx_out;
+        a.topk_src = i;
       } else {
         // the selection's own launches, then the gathered source
         d.kind = SRC_GATHER;
@@ -1154,6 +1159,7 @@ int setup_attention_front(const lca_attn_source* srcs, int n_src, const void* q,
                           int H, int D, float scale, float eps, AttnParams* a, int64_t* nblk) {
   if (D != 512 || H % 16 != 0 || n_src < 1 || n_src > kMaxSrc) return LCA_ERR_UNSUPPORTED;
   *a = AttnParams{};
+  a->topk_src = -1;
   a->q = q; a->q_pos = q_pos; a->Tq = Tq; a->H = H; a->D = D; a->rows = B * Tq;
   a->scale = scale; a->eps = eps; a->n_src = n_src;
   a->rope = make_rope_tab(srcs[0].rope_dims, srcs[0].rope_base);

@@ -80,6 +80,7 @@ struct AttnParams {
   AttnSrc s[kMaxSrc];
   TopkWs tw;            // the index workspace of a TOPK source
   int filter;           // 1: the TOPK blocks filter the scores themselves
+  int topk_src;         // the TOPK source (selected inside the blocks), or -1
   int tbpr;             // TOPK blocks per row (n_split * n_hb)
   // row-tiled path: every block takes all sources (one split each) and
   // writes the merged output with the sink (bf16 [rows, H, D]) instead of
@@ -286,6 +287,19 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     if (si == k) S = a.s[k];
   const int kind = S.kind;
   const bool gather = kind == SRC_GATHER || kind == SRC_TOPK;
+  // a TOPK block's filter (or selection) inputs first: they depend on the
+  // kernel arguments alone, and the block's critical path starts with them
+  SelectPrefetch<kAttnThreads> pf;
+  FilterPrefetch<kAttnThreads, kFilterPer, FC> fpf;
+  if constexpr (TOPK) {
+    if (si == a.topk_src) {  // (kind == SRC_TOPK, from the kernel arguments alone)
+      if (a.filter)
+        filter_prefetch(a.tw, r, split * a.n_hb + hb, a.tbpr, fpf);
+      else
+        topk_prefetch(a.tw, r, pf);
+      trace_stamp(a, 15);
+    }
+  }
   uint32_t tflags = (uint32_t)kind | ((uint32_t)(r & 0xFFFFF) << 12);
   __shared__ uint32_t s_timeout;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -307,10 +321,15 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   // value is not needed, so that no branch makes the compiler wait for it)
   // The block-uniform values are scalar loads (their own counter: waiting for
   // them does not wait for the vector loads behind them).
-  const int b = r / a.Tq;
+  // (r through an empty assembly statement: the row-only loads below then
+  // cannot be hoisted above a TOPK block's prefetch, whose loads would wait
+  // behind them)
+  int r_row = r;
+  asm volatile("" : "+s"(r_row));
+  const int b = r_row / a.Tq;
   const int64_t* offp = S.off + b;
   const int64_t off0 = scalar_load(offp), off1 = scalar_load(offp + 1);
-  const int32_t* qpp = a.q_pos ? a.q_pos + r : reinterpret_cast<const int32_t*>(offp);
+  const int32_t* qpp = a.q_pos ? a.q_pos + r_row : reinterpret_cast<const int32_t*>(offp);
   const int32_t qpos_ld = scalar_load(qpp);
   const int64_t* dlp = S.done_len ? S.done_len + b : offp;
   const int64_t dlen_ld = scalar_load(dlp);
@@ -343,17 +362,6 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     for (int u = 0; u < kIdxPer; ++u) {
       const int64_t i = (int64_t)threadIdx.x + u * kAttnThreads;
       jraw[u] = ip[i < last ? i : last];
-    }
-  }
-  SelectPrefetch<kAttnThreads> pf;
-  FilterPrefetch<kAttnThreads, kFilterPer, FC> fpf;
-  if constexpr (TOPK) {
-    if (kind == SRC_TOPK) {
-      if (a.filter)
-        filter_prefetch(a.tw, r, split * a.n_hb + hb, a.tbpr, fpf);
-      else
-        topk_prefetch(a.tw, r, pf);
-      trace_stamp(a, 15);
     }
   }
   // --- the key count and the block's key range

@@ -86,6 +86,20 @@ __device__ __forceinline__ void stg16(void* base, int64_t byte_off, uint4 v) {
 
 // ---------------------------------------------------------------- reductions
 // Butterfly over `width` lanes (a power of two <= 64) of one wavefront.
+// Every 64-byte line of the kernel's argument block (its first BYTES bytes)
+// requested at once at the kernel's start: the argument reads that follow
+// then hit the scalar cache, where the compiler would otherwise request the
+// lines one dependent wait at a time, each a memory round trip.
+template <int BYTES>
+__device__ __forceinline__ void warm_kernargs() {
+  const __attribute__((address_space(4))) uint32_t* kp =
+      (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t x = 0;
+#pragma unroll
+  for (int o = 0; o < BYTES; o += 64) x ^= kp[o / 4];
+  asm volatile("" : : "s"(x));
+}
+
 __device__ __forceinline__ float wave_sum(float v, int width) {
   for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;

@@ -39,6 +39,7 @@ namespace lca {
 template <int KS, int KF = 0>
 __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
   __shared__ uint32_t lh[kHistBins];
+  warm_kernargs<sizeof(IndexParams)>();
   score_chunk_mfma<KS, KF>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
 }
 
@@ -54,6 +55,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_multi(IndexParams a) 
 template <int KS, int TQ, int KF>
 __global__ __launch_bounds__(kIdxThreads) void index_score_append(IndexParams a, AppendIdx ap, CompressParams cp) {
   extern __shared__ uint32_t dyn[];  // max(histograms, compression) words
+  warm_kernargs<sizeof(IndexParams) + sizeof(AppendIdx) + sizeof(CompressParams)>();
   const int blk = blockIdx.x;
   if (blk < ap.ncb) {
     // 8-token batches and no prefetching keep the register budget of the
