@@ -79,6 +79,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 // the plain one within its register budget).
 template <bool MERGE, bool ROPE>
 __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_rows_mfma(AttnParams a) {
+  warm_kernargs<sizeof(AttnParams)>();
   constexpr int D = 512;
   constexpr int KS = D / 32;      // k-steps of S over D
   constexpr int DB = D / 16;      // 16-dim blocks of O
@@ -726,6 +727,7 @@ constexpr int kRowsWaves = 4;  // (row, head) pairs per block
 
 template <typename ET, int DPL>
 __global__ __launch_bounds__(64 * kRowsWaves) void merge_rows_kernel(MergeParams a) {
+  warm_kernargs<sizeof(MergeParams)>();
   const int lane = threadIdx.x & 63;
   const int64_t RH = (int64_t)a.rows * a.H;
   const int64_t rh = (int64_t)blockIdx.x * kRowsWaves + (threadIdx.x >> 6);

@@ -30,6 +30,7 @@ constexpr int kCompressThreads = 512;
 
 template <typename ET, int NV>
 __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressParams P) {
+  warm_kernargs<sizeof(CompressParams)>();
   extern __shared__ float lds[];
   compress_block<ET, NV>(P, (int)blockIdx.x, lds);
 }

@@ -38,6 +38,7 @@ template <int KS, int TQ, int KF>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_front(AttnParams a,
                                                                                                       FrontParams f) {
   __shared__ __attribute__((aligned(16))) char lds_raw[AttnLds<512, false>::kBytes];
+  warm_kernargs<sizeof(AttnParams) + sizeof(FrontParams)>();
   const int bid = blockIdx.x;
   if (bid < f.n_attn) {
     attn_block<512, false, 1>(a, bid, lds_raw);

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_score_mfma(IndexParams a) {
 
 template <int KS, int TQ, int KF = 0>
 __global__ __launch_bounds__(kIdxThreads) void index_score_multi(IndexParams a) {
+  warm_kernargs<sizeof(IndexParams)>();
   __shared__ uint32_t lh[TQ * kHistBins];
   score_chunk_multi<KS, TQ, KF>(a, blockIdx.y, blockIdx.x, INT64_MAX, lh);
 }
@@ -267,6 +268,7 @@ struct RowTile {
 
 template <int KS, int HI, int KF = 0>
 __global__ __launch_bounds__(256) void index_score_rows(IndexParams a) {
+  warm_kernargs<sizeof(IndexParams)>();
   using Tile = RowTile<KS, HI, KF, kRowsPerBlock>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -450,6 +452,7 @@ __device__ __forceinline__ uint32_t wave_compact(uint64_t* L, uint32_t n, uint64
 
 template <int KS, int HI, int KF = 0>
 __global__ __launch_bounds__(kStreamWaves * 64) void index_topk_rows(IndexParams a) {
+  warm_kernargs<sizeof(IndexParams)>();
   using Tile = RowTile<KS, HI, KF, kStreamRows>;
   constexpr int RB = Tile::RB, RPL = Tile::RPL, EB = stream_eb<KS>();
   constexpr int ROUND = kStreamWaves * 16 * EB;  // entries per round
@@ -704,6 +707,7 @@ __device__ __forceinline__ TopkWs topk_view(const IndexParams& a) {
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_filter(IndexParams a) {
+  warm_kernargs<sizeof(IndexParams)>();
   __shared__ FilterShared F;
   const int r = blockIdx.y;
   const int cb = blockIdx.x;
@@ -721,6 +725,7 @@ constexpr int kFinThreads = 1024;
 
 constexpr uint32_t kFinCandLds = 8192;  // candidates beyond the prefetched ones kept in LDS
 __global__ __launch_bounds__(kFinThreads) void topk_finalize(IndexParams a) {
+  warm_kernargs<sizeof(IndexParams)>();
   __shared__ SelectLds L;
   __shared__ SelectShared S;
   __shared__ uint64_t cl[kFinCandLds];
@@ -762,6 +767,7 @@ constexpr int kRowThreads = 1024;
 constexpr int kRowLoads = 8;    // score loads in flight per thread and pass
 
 __global__ __launch_bounds__(kRowThreads) void topk_rows(IndexParams a) {
+  warm_kernargs<sizeof(IndexParams)>();
   __shared__ uint32_t h1[4096];
   __shared__ uint32_t h2[kH2Bins];
   __shared__ uint32_t bitmap[kRowBitmapWords];
