@@ -58,8 +58,8 @@ TRAFFIC = {
                   "long_context_attention_20_amd/csrc/lca_attn_block.h",
                   "long_context_attention_20_amd/csrc/lca_common.h",
                   "long_context_attention_20_amd/csrc/lca_topk.h"],
-        "sha1": "c78c11b81ce07fde177f26a46ec0331cec1a1ca4",
-        "fetch_kib": 6378.8, "write_kib": 16694.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha1": "d717fa6f693e4cb729c094cdb13bdc4bfccb39cf",
+        "fetch_kib": 6387.3, "write_kib": 9012.7, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 

@@ -874,6 +874,11 @@ void diag_set_topk_wait(uint32_t extra, uint32_t ticks) {
   g_wait_extra.store(extra);
   g_wait_ticks.store(ticks ? ticks : kDefaultWaitTicks);
 }
+// The start delay of the dense and window blocks of a launch whose sparse
+// blocks filter the scores themselves (100 MHz ticks), for at most kHoldRows
+// query rows.
+constexpr uint32_t kHoldTicks = 125;
+constexpr int kHoldRows = 8;
 static void apply_diag(AttnParams* a) {
   a->wait_extra = g_wait_extra.load();
   a->wait_ticks = g_wait_ticks.load();
@@ -1102,6 +1107,12 @@ static int launch_attention_sources(const lca_attn_source* srcs, int n_src, cons
       // block more than one
       fc = !opt && D == 512 && (int64_t)a.tbpr * kAttnThreads * kFilterPer < in.max_entries ? 2 : 1;
       a.filter = nblk <= resident_blocks(D, fc, opt) ? 1 : 0;
+      // with few query rows, the dense and window blocks start their loads
+      // a little after the sparse blocks' filter loads, which lead the
+      // launch's critical path (measured: Pro 1M decode 46.2-46.7 -> 44.7-45.2
+      // us per step at 1.0-1.5 us, Flash decode 8 x 128K 61.1-61.6 -> 59.5;
+      // 64 rows of varlen decode lose 1-4 us, so they start at once)
+      if (a.filter && rows <= kHoldRows) a.hold_ticks = kHoldTicks;
       if (!a.filter)
         rc = launch_topk_filter(in.off, q_pos, B, Tq, in.k, in.m2, in.w2, in.max_entries, in.scores, in.ws, stream);
     } else {

@@ -97,6 +97,9 @@ struct AttnParams {
   // at most wait_ticks of the 100 MHz constant clock
   uint32_t wait_extra;
   uint32_t wait_ticks;
+  // dense and window blocks start this many ticks of the 100 MHz clock late
+  // (a launch whose sparse blocks filter the scores: their loads go first)
+  uint32_t hold_ticks;
   // diagnostics: per-block phase stamps (kTraceWords per block), or NULL
   uint64_t* trace;
   int64_t trace_words;
@@ -298,6 +301,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       else
         topk_prefetch(a.tw, r, pf);
       trace_stamp(a, 15);
+    }
+    if (a.hold_ticks && (kind == SRC_DENSE || kind == SRC_WINDOW)) {  // (a bounded wait)
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__builtin_amdgcn_s_memrealtime() - t0 < a.hold_ticks) __builtin_amdgcn_s_sleep(2);
     }
   }
   uint32_t tflags = (uint32_t)kind | ((uint32_t)(r & 0xFFFFF) << 12);
