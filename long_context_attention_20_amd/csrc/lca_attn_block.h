@@ -229,6 +229,7 @@ constexpr int kAttnHeads = 32;      // query heads per block
 // embedding, separate values.  Their code stays out of the plain kernel,
 // whose register budget it would strain.
 constexpr int kOptRope = 1;
+constexpr int kQRotPairs = 64;  // rotated pairs of the query-angle table
 constexpr int kOptValues = 2;
 
 // LDS of the block (besides a few small arrays it declares itself): the
@@ -269,6 +270,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   // token's position and the turns per position, per pair (rope_turn_near)
   __shared__ float2 s_rot[(OPT & kOptRope) ? D / 2 : 1];
   __shared__ float s_turns[(OPT & kOptRope) ? D / 2 : 1];
+  // the query position's angles, cosine and sine per rotated pair (for
+  // rotations over at most 2 * kQRotPairs dims): the query turns by them and
+  // the partial turns back by their conjugates
+  __shared__ float2 s_qrot[(OPT & kOptRope) ? kQRotPairs : 1];
   // 1-D grid, XCD-aware: workgroups go to the 8 XCDs round-robin by linear
   // id, so the n_hb head blocks of one (row, split) unit take ids 8 apart and
   // share an XCD's L2 for the keys they all read
@@ -373,6 +378,15 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
   }
   // --- the key count and the block's key range
   const int32_t qpos_r = ((kind != SRC_GATHER || ((OPT & kOptRope) && a.rope.dims)) && a.q_pos) ? qpos_ld : 0;
+  const bool qtab = (OPT & kOptRope) && a.rope.dims > 0 && a.rope.dims <= 2 * kQRotPairs;  // uniform
+  if constexpr ((OPT & kOptRope) != 0) {
+    // (read after the barriers that precede the query's normalisation)
+    if (qtab && (int)threadIdx.x < a.rope.dims / 2) {
+      float sn, cs;
+      rope_sincos((double)qpos_r, threadIdx.x, a.rope, &sn, &cs);
+      s_qrot[threadIdx.x] = make_float2(cs, sn);
+    }
+  }
   const int64_t dlen = (kind == SRC_DENSE && S.part != 0) ? dlen_ld : 0;
   const int64_t nseq = off1 - off0;
   int64_t first = off0;
@@ -633,7 +647,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
       BF16::unpack(qraw[ks], f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= inv;
-      if ((OPT & kOptRope) && a.rope.dims) rope_turn<8>(f, d0 + ks * 32 + g * 8, D, a.rope, (double)qpos_r);
+      if ((OPT & kOptRope) && a.rope.dims) {
+        if (qtab)
+          rope_turn_tab<8>(f, d0 + ks * 32 + g * 8, D, a.rope.dims, s_qrot, false);
+        else
+          rope_turn<8>(f, d0 + ks * 32 + g * 8, D, a.rope, (double)qpos_r);
+      }
       qb[ks] = __builtin_bit_cast(bf16x8_t, BF16::pack(f));
     }
   }
@@ -817,7 +836,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& a, const int bid, c
     const float4 u = *reinterpret_cast<const float4*>(ox + hh * XP + d);
     const float4 v = *reinterpret_cast<const float4*>(ox + (kAttnHeads + hh) * XP + d);
     float o4[4] = {u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w};
-    if ((OPT & kOptRope) && a.rope.dims) rope_turn<4>(o4, d, D, a.rope, -(double)qpos_r);  // -i on the output
+    if ((OPT & kOptRope) && a.rope.dims) {  // -i on the output
+      if (qtab)
+        rope_turn_tab<4>(o4, d, D, a.rope.dims, s_qrot, true);
+      else
+        rope_turn<4>(o4, d, D, a.rope, -(double)qpos_r);
+    }
     if (S.o_half) {
       // fp16 (round to nearest even), 8 bytes per lane
       const f16x4 hv = {(_Float16)o4[0], (_Float16)o4[1], (_Float16)o4[2], (_Float16)o4[3]};

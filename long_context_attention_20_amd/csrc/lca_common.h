@@ -262,6 +262,28 @@ __device__ __forceinline__ void rope_turn(float (&v)[N], int ch0, int C, const R
   }
 }
 
+// Channels [ch0, ch0 + N) of a C-channel vector (ch0 and N even) turned by
+// the angles of a table (tab[p]: cosine and sine of the angle of pair p, as
+// rope_sincos gives them), or by minus those angles (back: the sine negated,
+// which is rope_sincos of the negated position exactly, its reduction being
+// odd in the position).
+template <int N>
+__device__ __forceinline__ void rope_turn_tab(float (&v)[N], int ch0, int C, int dims, const float2* tab, bool back) {
+  static_assert(N % 2 == 0, "pairs");
+  const int lo = C - dims;
+#pragma unroll
+  for (int k = 0; k < N; k += 2) {
+    const int c = ch0 + k;
+    if (dims > 0 && c >= lo) {
+      const float2 t = tab[(c - lo) >> 1];
+      const float cs = t.x, sn = back ? -t.y : t.y;
+      const float x0 = v[k], x1 = v[k + 1];
+      v[k] = x0 * cs - x1 * sn;
+      v[k + 1] = x0 * sn + x1 * cs;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- ordering
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
 // -0 is folded into +0 so that the two zeros tie, as they compare equal.

@@ -249,6 +249,11 @@ class HybridAttention:
             # branch then runs row-tiled): one partial per source
             return (1, 1, 1)
         tiles = [max(1, (n + 31) // 32) for n in (n_csa, n_hca, n_win)]
+        if self.rope:
+            # a window tile is RMS-normalised and turned by the rotary
+            # embedding as it is staged: measured about four times an HCA
+            # tile, so the window takes more splits
+            tiles[2] *= 4
         budget = max(3, 256 // max(1, rows * hg))
         sc_min = -(-n_scores // (self.FILTER_PASS_SCORES * hg)) if select else 1
         for floor in (sc_min, 1):  # a floor that does not fit the budget is dropped
