@@ -58,8 +58,8 @@ TRAFFIC = {
                   "long_context_attention_20_amd/csrc/lca_attn_block.h",
                   "long_context_attention_20_amd/csrc/lca_common.h",
                   "long_context_attention_20_amd/csrc/lca_topk.h"],
-        "sha1": "d717fa6f693e4cb729c094cdb13bdc4bfccb39cf",
-        "fetch_kib": 6387.3, "write_kib": 9012.7, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sha1": "e362f2287aa9db536844baaae2d523b5d404c0bc",
+        "fetch_kib": 6388.1, "write_kib": 9013.3, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
