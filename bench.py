@@ -228,7 +228,7 @@ class Position:
 
 
 class Runner:
-    def __init__(self, cfg, R, dev, split_csa=0, split_hca=0, front=None, half_partials=True):
+    def __init__(self, cfg, R, dev, split_csa=0, split_hca=0, front=None, half_partials=True, batch_invariant=False):
         import torch
         from long_context_attention_20_amd import HybridAttention, ops
         self.torch, self.ops = torch, ops
@@ -236,7 +236,8 @@ class Runner:
         a = HybridAttention(cfg.H, cfg.D, cfg.HI, cfg.dI, cfg.k, cfg.m, cfg.w, cfg.m2, cfg.w2, cfg.W, cfg.eps,
                             split_csa=split_csa or None, split_hca=split_hca or None, ikey=cfg.ikey,
                             rope=cfg.rope, rope_base=cfg.rope_base, dual=cfg.dual, sepv=cfg.sepv,
-                            half_partials=half_partials)
+                            half_partials=half_partials, batch_invariant=batch_invariant,
+                            max_context=max(cfg.lens))
         self.attn = a
         self.layers = [LayerState(cfg, r, a, dev) for r in range(R)]
         rows = cfg.B * cfg.tq
@@ -643,6 +644,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget (0 disables)")
     ap.add_argument("--split-csa", type=int, default=0, help="entry splits of the sparse attention (0: default)")
     ap.add_argument("--split-hca", type=int, default=0, help="entry splits of the HCA attention (0: default)")
+    ap.add_argument("--batch-invariant", type=int, default=0,
+                    help="1: batch-invariant decode (fixed key ranges per split, HybridAttention(batch_invariant=True))")
     ap.add_argument("--half-partials", type=int, default=1,
                     help="1: the decode step's attention partials in fp16 (default), 0: fp32")
     ap.add_argument("--front", type=int, default=-1,
@@ -679,7 +682,7 @@ def main():
     R = args.layers or max(1, -(-2 * MALL_BYTES // sb))
     t0 = time.perf_counter()
     run = Runner(cfg, R, dev, args.split_csa, args.split_hca, front=None if args.front < 0 else bool(args.front),
-                 half_partials=bool(args.half_partials))
+                 half_partials=bool(args.half_partials), batch_invariant=bool(args.batch_invariant))
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     print(f"[bench] {cfg.name}: {R} layers built in {setup_s:.1f} s; {sb / 1e6:.2f} MB/step; "
