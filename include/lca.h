@@ -273,7 +273,8 @@ int lca_csa_topk_select(const int64_t* csa_off, const int32_t* q_pos, int B, int
  * scale * qhat . key.  The key list of a query is cut into n_split parts; part
  * s writes the softmax-normalised output and natural-log log-sum-exp of its
  * keys:
- *     o_part[s, r, h, :]  fp32, [n_split, B*Tq, H, D]
+ *     o_part[s, r, h, :]  fp32, [n_split, B*Tq, H, D]  (fp16 for an
+ *                         lca_hybrid_attn source with o_half)
  *     lse[s, r, h]        fp32, [n_split, B*Tq, H]
  * An empty part writes o = 0 and lse = -inf.  lca_swa_merge combines parts.
  * Supported: D in {64, 128, 256, 512}; any H (H a multiple of 16 uses the
