@@ -69,8 +69,11 @@ struct PoolState {
       float M = fmaxf(mx[e], o.mx[e]);
       float fa = (mx[e] == -INFINITY) ? 0.f : __expf(mx[e] - M);
       float fb = (o.mx[e] == -INFINITY) ? 0.f : __expf(o.mx[e] - M);
-      se[e] = se[e] * fa + o.se[e] * fb;
-      sn[e] = sn[e] * fa + o.sn[e] * fb;
+      // (one fused multiply-add, written out: left to the compiler, the
+      // contraction of a*b + c*d can differ between the kernels that inline
+      // this, and so would the pooled entries)
+      se[e] = fmaf(se[e], fa, o.se[e] * fb);
+      sn[e] = fmaf(sn[e], fa, o.sn[e] * fb);
       mx[e] = M;
     }
   }

@@ -456,6 +456,48 @@ def test_index_score_append_equals_separate(rmsnorm_idx):
                 assert abs(s_ref[j] - kth) <= 1e-6 * max(1.0, abs(kth)) + 2 * bound[j], f"row {b}: {j} not a near tie"
 
 
+def test_index_score_append_many_new_tokens():
+    """csa_index_score_append with hundreds of new tokens per sequence
+    (several HCA entries, runs of CSA entries, indexer keys pooled by the
+    append blocks in rounds of their row groups, and a sequence with no
+    earlier entries): every cache is bit-identical to kv_compress's from the
+    same state, the indexer keys included (the two kernels pool with the same
+    written-out fused multiply-adds)."""
+    from long_context_attention_20_amd import ops
+    cfg = li.small("append", 111, (4001, 2600, 777, 4096, 650), H=64, D=512, k=256)
+    raw = li.make_raw(cfg)
+    d, layer, caches, full, done, done_h, bufs = _decode_setup(cfg, raw)
+    done_h = [max(L - 700, 0) for L in cfg.lens]
+    tabs = ((caches.kv_csa, caches.csa_off_h, cfg.m, cfg.w), (caches.ikey, caches.csa_off_h, cfg.m, cfg.w),
+            (caches.kv_hca, caches.hca_off_h, cfg.m2, cfg.w2))
+
+    def wipe():
+        for b, L in enumerate(cfg.lens):
+            for t, off, m, w in tabs:
+                n0, n1 = ocmp.n_entries(done_h[b], m, w), ocmp.n_entries(L, m, w)
+                assert n1 - n0 >= (4 if m == cfg.m2 else 100) or L < 700
+                t[int(off[b]) + n0:int(off[b]) + n1] = 0
+
+    wipe()
+    done = torch.tensor(done_h, dtype=torch.int64, device="cuda")
+    streams = layer.compress_streams(caches, d, done_h)
+    idx_st = [s for s in streams if s["out"] is caches.ikey][0]
+    kv_st = [s for s in streams if s["out"] is not caches.ikey]
+    ws = layer.index_workspace(cfg.B, bufs["max_csa"], "cuda")
+    print(f"[append many] lens={cfg.lens} done={done_h}", flush=True)
+    ops.csa_index_score_append(d["p"], d["omega"], caches.ikey, caches.csa_off, d["q_pos"], cfg.k, cfg.m, cfg.w,
+                               bufs["max_csa"], ws, idx_st, kv_st, d["tok_off"], done, cfg.eps)
+    torch.cuda.synchronize()
+    fused = (caches.kv_csa.clone(), caches.ikey.clone(), caches.kv_hca.clone())
+    wipe()
+    ops.kv_compress([idx_st], d["tok_off"], done, cfg.eps)
+    ops.kv_compress(kv_st, d["tok_off"], done, cfg.eps)
+    torch.cuda.synchronize()
+    for got, ref, name in zip(fused, (caches.kv_csa, caches.ikey, caches.kv_hca), ("kv_csa", "ikey", "kv_hca")):
+        assert torch.equal(got, ref), f"{name}: fused append of many tokens differs from kv_compress"
+    assert torch.equal(fused[1], full[1])
+
+
 @pytest.mark.parametrize("p", [4986, 4987, 4991, 4863])
 def test_decode_step_at_earlier_position(p):
     """A decode step at token position p of a one-sequence cache built for
